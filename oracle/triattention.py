@@ -1,0 +1,338 @@
+"""Float64 CPU oracle of TriAttention's KV-cache compression step.
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, obviously-correct statement of what
+the compression pass computes.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it; the HIP library never does, and this
+module imports nothing from the HIP library or its binding.  It shares no code, tables or
+constants with the GPU path.
+
+Sources (web pages about the paper "TriAttention: Efficient Long Reasoning with
+Trigonometric KV Compression", Mao et al.), cited below by tag:
+
+  [Review]   "TriAttention: Trigonometric KV Compression for Efficient Long Reasoning"
+             (alanhou.org paper review): sections "Core Mechanism", "Key Concepts".
+  [Abstract] "TriAttention: Efficient Long Reasoning with Trigonometric KV Compression"
+             (chatpaper.ai abstract page), English abstract.
+  [DevTo]    "TriAttention: How a Geometric Trick Cuts LLM Memory Use by 10x Without Losing
+             Accuracy" (dev.to): sections "Why Existing KV Cache Compression Breaks in
+             Production", "The Core Idea: Q/K Concentration in Pre-RoPE Space", "Solving
+             the Memory Fragmentation Problem", "What the Numbers Look Like".
+  [Project]  "TriAttention: trigonometric KV cache compression for long reasoning"
+             (hysenlabs.com project page): sections "Pre-RoPE centres decide which keys
+             are worth keeping", "The KV budget is a runtime knob that chat sessions
+             should raise", "Calibration statistics are tied to a specific model".
+
+The scoring contract (the pages give its parts; the exact additive form is the build's
+documented reading of them).  For a pre-RoPE key k with RoPE bands k_f, f = 0..F-1
+(F = d/2, theta_f = base^(-2f/d)), calibrated query statistics E[q_f] (complex centre) and
+E|q_f| with concentration R_f = |E[q_f]| / E|q_f|, and future offsets Delta in D giving the
+distance d = query_pos - key_pos + Delta:
+
+    score(k) = mean_Delta sum_f |E[q_f]| |k_f| cos(d theta_f + arg E[q_f] - arg k_f)
+             + sum_f (1 - R_f) E|q_f| |k_f|
+
+Scores are reduced over the query heads of a GQA group (max or mean), the top-B keys of
+each KV head are kept with the most recent window always kept, and the survivors are
+packed forward into dense or paged storage.
+
+Parity status: every function here is pinned by the CPU tests (exact-centre RoPE
+identity, R = 0 limit, hand values, invariants, brute-force top-B, calibration closed
+forms, compaction invariants and the pages' memory ratios).  None is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "rope_theta",
+    "split_bands",
+    "concentration",
+    "score_keys",
+    "score_magnitude_bound",
+    "select_top_b",
+    "compact_dense",
+    "compact_paged_sequence",
+    "calibrate",
+    "unit_heads",
+]
+
+
+# ---------------------------------------------------------------------------------------
+# RoPE frequency bands
+# ---------------------------------------------------------------------------------------
+
+def rope_theta(base: float, head_dim: int) -> np.ndarray:
+    """theta_f = base^(-2f/d) for f = 0 .. d/2-1, in float64.
+
+    RoPE rotates each frequency pair by an angle proportional to position
+    ([Review] "Key Concepts", trigonometric distance preference).
+    """
+    if head_dim % 2:
+        raise ValueError("head_dim must be even")
+    f = np.arange(head_dim // 2, dtype=np.float64)
+    return np.float64(base) ** (-2.0 * f / head_dim)
+
+
+def split_bands(x, layout: str = "half") -> np.ndarray:
+    """The complex RoPE bands x_f of vectors x[..., d] (exact float64 upcast).
+
+    layout "half":        x_f = x[f] + i x[f + d/2]   (rotate-half pairing)
+    layout "interleaved": x_f = x[2f] + i x[2f + 1]
+    The pages do not say which pairing the models use; both are supported.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    if layout == "half":
+        return x[..., : d // 2] + 1j * x[..., d // 2:]
+    if layout == "interleaved":
+        return x[..., 0::2] + 1j * x[..., 1::2]
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+# ---------------------------------------------------------------------------------------
+# Calibration ([Review] "Key Concepts": the centre is the mean pre-RoPE query over a
+# calibration set; [Project] "Calibration statistics are tied to a specific model")
+# ---------------------------------------------------------------------------------------
+
+def calibrate(q, layout: str = "half"):
+    """Per-band query statistics from pre-RoPE query samples.
+
+    q: [N, n_layer, n_qh, d].  Returns (center [n_layer, n_qh, F] complex128,
+    mean_abs [n_layer, n_qh, F] float64): E[q_f] = mean_n q_{n,f} and
+    E|q_f| = mean_n |q_{n,f}|.
+    """
+    qb = split_bands(q, layout)
+    center = qb.mean(axis=0)
+    mean_abs = np.abs(qb).mean(axis=0)
+    return center, mean_abs
+
+
+def concentration(center, mean_abs) -> np.ndarray:
+    """R_f = |E[q_f]| / E|q_f| ([DevTo] "The Core Idea": a measured concentration metric).
+
+    A band with E|q_f| = 0 has no query energy at all; R_f is read as 0 there (0/0 -> 0).
+    No clamp is applied: statistics with R_f > 1 are used as given.
+    """
+    center = np.asarray(center, dtype=np.complex128)
+    mean_abs = np.asarray(mean_abs, dtype=np.float64)
+    mag = np.abs(center)
+    out = np.zeros(np.broadcast(mag, mean_abs).shape, dtype=np.float64)
+    np.divide(mag, mean_abs, out=out, where=mean_abs > 0)
+    return out
+
+
+# ---------------------------------------------------------------------------------------
+# Scoring
+# ---------------------------------------------------------------------------------------
+
+def _trig_term(k_bands, key_pos, query_pos, center_h, theta, offsets):
+    """mean_Delta sum_f |E q_f| |k_f| cos(d theta_f + arg E q_f - arg k_f), d = Q - p + Delta.
+
+    The dot product of fixed centres after RoPE is a cosine series in the relative
+    distance ([Review] "Core Mechanism" and "Key Concepts"; [Abstract]); it is evaluated
+    at each future query position Q + Delta and averaged over the offsets.
+    """
+    q_abs = np.abs(center_h)                                  # |E[q_f]|        [F]
+    q_arg = np.arctan2(center_h.imag, center_h.real)          # arg E[q_f]      [F]
+    k_abs = np.abs(k_bands)                                   # |k_f|           [L, F]
+    k_arg = np.arctan2(k_bands.imag, k_bands.real)            # arg k_f         [L, F]
+    total = np.zeros(k_bands.shape[0], dtype=np.float64)
+    for delta in offsets:
+        dist = (np.float64(query_pos) - key_pos.astype(np.float64)) + np.float64(delta)
+        phase = dist[:, None] * theta[None, :] + q_arg[None, :] - k_arg
+        total += np.sum(q_abs[None, :] * k_abs * np.cos(phase), axis=1)
+    return total / len(offsets)
+
+
+def _norm_term(k_bands, center_h, mean_abs_h):
+    """sum_f (1 - R_f) E|q_f| |k_f|.
+
+    Norms carry importance ([Review] "Key Concepts", norm as importance signal); weakly
+    concentrated heads lean on this norm-only signal in proportion to 1 - R_f ([DevTo]
+    "The Core Idea").  For a band with E|q_f| = 0 the product is read as 0.
+    """
+    R = concentration(center_h, mean_abs_h)
+    coef = (1.0 - R) * np.asarray(mean_abs_h, dtype=np.float64)
+    return np.sum(coef[None, :] * np.abs(k_bands), axis=1)
+
+
+def score_keys(keys, center, mean_abs, *, base: float, offsets, key_pos=None,
+               query_pos=None, layout: str = "half", reduce: str = "max",
+               return_heads: bool = False):
+    """Score every cached key of one (layer, KV head) unit.
+
+    keys:     [L, d] pre-RoPE keys (any float dtype; upcast exactly to float64)
+    center:   [G, F] complex E[q_f] of the G query heads of the group
+              (or [G, F, 2] real/imaginary pairs)
+    mean_abs: [G, F] E|q_f|
+    key_pos:  [L] RoPE positions of the keys (default: slot index 0..L-1)
+    query_pos: position of the newest query (default: L - 1)
+    reduce:   "max" or "mean" over the G query heads of the group
+
+    Returns float64 scores [L] (and the per-head scores [G, L] if return_heads).
+    The series is position-aware: the keys are scored at their positions relative to
+    the queries that will read them ([Review] "Framework Shift").
+    """
+    keys = np.asarray(keys, dtype=np.float64)
+    L, d = keys.shape
+    center = _as_complex(center)
+    mean_abs = np.asarray(mean_abs, dtype=np.float64)
+    if center.ndim == 1:
+        center = center[None, :]
+        mean_abs = mean_abs[None, :]
+    if key_pos is None:
+        key_pos = np.arange(L, dtype=np.int64)
+    key_pos = np.asarray(key_pos, dtype=np.int64)
+    if query_pos is None:
+        query_pos = L - 1
+    theta = rope_theta(base, d)
+    kb = split_bands(keys, layout)
+
+    heads = []
+    for h in range(center.shape[0]):
+        trig = _trig_term(kb, key_pos, query_pos, center[h], theta, offsets)
+        norm = _norm_term(kb, center[h], mean_abs[h])
+        heads.append(trig + norm)
+    heads = np.stack(heads, axis=0) if heads else np.zeros((0, L))
+    scores = _reduce_heads(heads, reduce)
+    if return_heads:
+        return scores, heads
+    return scores
+
+
+def score_magnitude_bound(keys, center, mean_abs, *, layout: str = "half",
+                          reduce: str = "max") -> np.ndarray:
+    """S_j = sum_f |k_f| (|E q_f| + |(1 - R_f) E|q_f||), reduced over heads like the score.
+
+    |score_j| <= S_j for every key; it is the scale against which score errors are
+    measured (a plain |error| / |score| is unbounded where a signed score crosses 0).
+    """
+    keys = np.asarray(keys, dtype=np.float64)
+    center = _as_complex(center)
+    mean_abs = np.asarray(mean_abs, dtype=np.float64)
+    if center.ndim == 1:
+        center = center[None, :]
+        mean_abs = mean_abs[None, :]
+    k_abs = np.abs(split_bands(keys, layout))
+    heads = []
+    for h in range(center.shape[0]):
+        R = concentration(center[h], mean_abs[h])
+        coef = np.abs(center[h]) + np.abs((1.0 - R) * mean_abs[h])
+        heads.append(np.sum(coef[None, :] * k_abs, axis=1))
+    return _reduce_heads(np.stack(heads, axis=0), reduce)
+
+
+def _reduce_heads(heads, reduce):
+    if reduce == "max":
+        return np.max(heads, axis=0)
+    if reduce == "mean":
+        return np.mean(heads, axis=0)
+    raise ValueError(f"unknown reduce {reduce!r}")
+
+
+def _as_complex(c):
+    c = np.asarray(c)
+    if np.iscomplexobj(c):
+        return c.astype(np.complex128)
+    c = c.astype(np.float64)
+    if c.shape[-1] != 2:
+        raise ValueError("real center arrays must end in a (re, im) axis of size 2")
+    return c[..., 0] + 1j * c[..., 1]
+
+
+def unit_heads(center, mean_abs, layer: int, kv_head: int, group: int):
+    """Statistics of the query heads that read KV head ``kv_head``.
+
+    center [n_layer, n_qh, F(,2)], mean_abs [n_layer, n_qh, F].  Query head h reads
+    KV head h // group (contiguous GQA groups).
+    """
+    hs = slice(kv_head * group, (kv_head + 1) * group)
+    return _as_complex(np.asarray(center)[layer, hs]), np.asarray(mean_abs, np.float64)[layer, hs]
+
+
+# ---------------------------------------------------------------------------------------
+# Selection ([Review] "Core Mechanism": keep only the top-scoring keys; [Project] "The KV
+# budget is a runtime knob": the budget bounds the whole kept cache; [DevTo] "What the
+# Numbers Look Like": a 3,072-token budget for 32K-token generations)
+# ---------------------------------------------------------------------------------------
+
+def select_top_b(scores, length: int, budget: int, window: int) -> np.ndarray:
+    """Kept slot indices of one unit, ascending.
+
+    If length <= budget every slot is kept.  Otherwise the last W' = min(window, budget)
+    slots are always kept, and the remaining B - W' slots are the best of the other
+    candidates ranked by (score descending, slot ascending); a NaN score ranks as -inf.
+    """
+    if budget < 1 or window < 0:
+        raise ValueError("budget must be >= 1 and window >= 0")
+    L = int(length)
+    if L <= budget:
+        return np.arange(L, dtype=np.int64)
+    w = min(window, budget)
+    n_cand = L - w
+    s = np.asarray(scores, dtype=np.float64)[:n_cand].copy()
+    s[np.isnan(s)] = -np.inf
+    slots = np.arange(n_cand, dtype=np.int64)
+    order = np.lexsort((slots, -s))        # last key is primary: -score asc, then slot asc
+    top = slots[order[: budget - w]]
+    return np.sort(np.concatenate([top, np.arange(n_cand, L, dtype=np.int64)]))
+
+
+# ---------------------------------------------------------------------------------------
+# Compaction ([DevTo] "Solving the Memory Fragmentation Problem": survivors are moved
+# forward into as few blocks as possible so the emptied tail blocks can be reclaimed;
+# "Why Existing KV Cache Compression Breaks in Production": a paged allocator can only
+# free a block that is completely empty)
+# ---------------------------------------------------------------------------------------
+
+def compact_dense(k, v, kept, pos=None):
+    """Dense compaction of one unit: rows kept[i] move to slot i (bit copy).
+
+    Returns (k_out, v_out or None, pos_out) where pos_out[i] is the RoPE position of the
+    row now in slot i (the slot index itself when ``pos`` is None).
+    """
+    kept = np.asarray(kept, dtype=np.int64)
+    k_out = np.asarray(k)[kept]
+    v_out = None if v is None else np.asarray(v)[kept]
+    pos_out = kept.copy() if pos is None else np.asarray(pos)[kept]
+    return k_out, v_out, pos_out
+
+
+def compact_paged_sequence(pool_k, pool_v, block_table_row, length: int, kept_by_unit,
+                           page: int = 16):
+    """Forward-pack one sequence of a paged cache.
+
+    pool_k, pool_v: [n_pages, n_layer, n_kvh, page, d] (copies are returned, inputs are
+      not modified; pool_v may be None)
+    block_table_row: [max_pages] page ids of the sequence (slot j lives in page
+      block_table_row[j // page], row j % page)
+    kept_by_unit: dict {(layer, kv_head): kept slots (ascending)}; every unit of the
+      sequence keeps the same number of rows.
+
+    Returns (pool_k', pool_v', freed_pages, new_len): row kept[i] of each unit is moved to
+    slot i, new_len = number kept, and the pages past ceil(new_len / page) that held the
+    sequence before are returned as freed (each is now empty).
+    """
+    bt = np.asarray(block_table_row, dtype=np.int64)
+    out_k = np.array(pool_k, copy=True)
+    out_v = None if pool_v is None else np.array(pool_v, copy=True)
+    counts = {len(np.asarray(v)) for v in kept_by_unit.values()}
+    if len(counts) > 1:
+        raise ValueError("every unit of a sequence must keep the same number of rows")
+    new_len = counts.pop() if counts else min(int(length), 0)
+    for (layer, head), kept in kept_by_unit.items():
+        kept = np.asarray(kept, dtype=np.int64)
+        src_page, src_row = bt[kept // page], kept % page
+        dst = np.arange(len(kept), dtype=np.int64)
+        dst_page, dst_row = bt[dst // page], dst % page
+        # gather from the pre-compaction snapshot, then scatter forward
+        rows_k = np.asarray(pool_k)[src_page, layer, head, src_row]
+        out_k[dst_page, layer, head, dst_row] = rows_k
+        if out_v is not None:
+            rows_v = np.asarray(pool_v)[src_page, layer, head, src_row]
+            out_v[dst_page, layer, head, dst_row] = rows_v
+    used_before = -(-int(length) // page)
+    used_after = -(-int(new_len) // page)
+    freed = bt[used_after:used_before].copy()
+    return out_k, out_v, freed, int(new_len)

@@ -1,0 +1,200 @@
+"""Planted mistakes in the oracle (on the CPU) must each be caught by some pin.
+
+Every mutation below is a plausible slip in the oracle (a dropped term, a wrong sign, a
+transposed operand, a wrong index or pairing).  The mutation is applied with monkeypatch
+to the oracle module only; the pins of test_oracle_pins / test_oracle_golden are then run
+and at least one of them must fail.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import triattention as T
+
+import test_oracle_golden as golden
+import test_oracle_pins as pins
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _pin_calls():
+    calls = []
+    for layout in ("half", "interleaved"):
+        for d, base, qpos, offs in [(128, 1e4, 2047, [1, 2, 4, 8, 16]), (16, 500.0, 37, [1, 3, 9])]:
+            calls.append(lambda layout=layout, d=d, base=base, qpos=qpos, offs=offs:
+                         pins.test_p1_exact_centre_identity(layout, d, base, qpos, offs))
+        calls.append(lambda layout=layout: pins.test_p2_zero_centre_is_pure_norm(layout))
+        calls.append(lambda layout=layout: pins.test_p6_identical_samples(layout))
+    calls += [
+        pins.test_p2_partial_concentration_norm_coefficient,
+        pins.test_p3_theta_hand_values,
+        lambda: pins.test_p3_single_band_345(7),
+        pins.test_p3_zero_distance_quarter_turn,
+        pins.test_p3_offsets_are_averaged,
+        pins.test_p4_shift_invariance,
+        pins.test_p4_key_scaling,
+        pins.test_p4_mean_fold_linearity,
+        pins.test_p4_identical_heads_and_max,
+        pins.test_p4_zero_key_scores_zero,
+        pins.test_p4_r_above_one_not_clamped,
+        pins.test_p5_edge_cases,
+        pins.test_p6_rotating_samples_have_zero_centre,
+        pins.test_p6_scaling_and_permutation,
+        pins.test_p7_dense_rows_are_bit_copies,
+        pins.test_p7_paged_forward_packing,
+    ]
+    calls += [lambda t=t: pins.test_p5_select_matches_brute_force(t) for t in range(60)]
+    with open(golden.GOLDEN) as fh:
+        import json
+        for case in json.load(fh)["cases"]:
+            calls.append(lambda case=case: golden.test_printed_memory_ratios(case))
+    return calls
+
+
+def _some_pin_fails():
+    for call in _pin_calls():
+        try:
+            call()
+        except (AssertionError, ValueError, IndexError):
+            return True
+    return False
+
+
+# ---- mutated pieces (each plants one mistake) ------------------------------------------
+
+def _theta_wrong_exponent(base, head_dim):
+    f = np.arange(head_dim // 2, dtype=np.float64)
+    return np.float64(base) ** (-1.0 * f / head_dim)
+
+
+def _bands_swapped(x, layout="half"):
+    other = {"half": "interleaved", "interleaved": "half"}[layout]
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    if other == "half":
+        return x[..., : d // 2] + 1j * x[..., d // 2:]
+    return x[..., 0::2] + 1j * x[..., 1::2]
+
+
+def _bands_conjugated(x, layout="half"):
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    if layout == "half":
+        return x[..., : d // 2] - 1j * x[..., d // 2:]
+    return x[..., 0::2] - 1j * x[..., 1::2]
+
+
+def _trig(kind):
+    def trig(k_bands, key_pos, query_pos, center_h, theta, offsets):
+        q_abs = np.abs(center_h)
+        q_arg = np.arctan2(center_h.imag, center_h.real)
+        if kind == "atan2_transposed":
+            q_arg = np.arctan2(center_h.real, center_h.imag)
+        k_abs = np.abs(k_bands)
+        k_arg = np.arctan2(k_bands.imag, k_bands.real)
+        total = np.zeros(k_bands.shape[0])
+        for delta in offsets:
+            if kind == "distance_sign":
+                dist = key_pos.astype(float) - query_pos - delta
+            elif kind == "offset_dropped":
+                dist = query_pos - key_pos.astype(float)
+            else:
+                dist = query_pos - key_pos.astype(float) + delta
+            phase = dist[:, None] * theta[None, :] + q_arg[None, :] - k_arg
+            if kind == "arg_sign":
+                phase = dist[:, None] * theta[None, :] - q_arg[None, :] + k_arg
+            total += np.sum(q_abs[None, :] * k_abs * np.cos(phase), axis=1)
+        if kind == "sum_not_mean":
+            return total
+        return total / len(offsets)
+    return trig
+
+
+def _norm(kind):
+    def norm(k_bands, center_h, mean_abs_h):
+        R = T.concentration(center_h, mean_abs_h)
+        if kind == "dropped":
+            return np.zeros(k_bands.shape[0])
+        coef = (R if kind == "R_not_1mR" else 1.0 - R) * mean_abs_h
+        if kind == "no_mean_abs":
+            coef = 1.0 - R
+        return np.sum(coef[None, :] * np.abs(k_bands), axis=1)
+    return norm
+
+
+def _select(kind):
+    orig = T.select_top_b
+
+    def sel(scores, length, budget, window):
+        L = int(length)
+        if L <= budget:
+            return np.arange(L)
+        w = min(window, budget)
+        if kind == "window_not_forced":
+            w = 0
+        n_cand = L - w
+        s = np.asarray(scores, dtype=float)[:n_cand].copy()
+        s[np.isnan(s)] = -np.inf
+        slots = np.arange(n_cand)
+        if kind == "ties_high_slot":
+            order = np.lexsort((-slots, -s))
+        elif kind == "ascending_scores":
+            order = np.lexsort((slots, s))
+        else:
+            order = np.lexsort((slots, -s))
+        take = budget - w
+        if kind == "off_by_one":
+            take -= 1
+        top = slots[order[:take]]
+        return np.sort(np.concatenate([top, np.arange(n_cand, L)]))
+    return sel if kind else orig
+
+
+def _calib_abs_of_mean(q, layout="half"):
+    qb = T.split_bands(q, layout)
+    c = qb.mean(axis=0)
+    return c, np.abs(c)
+
+
+def _compact_freed_off_by_one(pool_k, pool_v, bt, length, kept_by_unit, page=16):
+    out = T.__dict__["_orig_compact"](pool_k, pool_v, bt, length, kept_by_unit, page)
+    k, v, freed, new_len = out
+    return k, v, freed[1:], new_len
+
+
+MUTATIONS = {
+    "theta_exponent": ("rope_theta", _theta_wrong_exponent),
+    "bands_pairing": ("split_bands", _bands_swapped),
+    "bands_conjugated": ("split_bands", _bands_conjugated),
+    "distance_sign": ("_trig_term", _trig("distance_sign")),
+    "offset_dropped": ("_trig_term", _trig("offset_dropped")),
+    "arg_sign": ("_trig_term", _trig("arg_sign")),
+    "atan2_transposed": ("_trig_term", _trig("atan2_transposed")),
+    "sum_not_mean": ("_trig_term", _trig("sum_not_mean")),
+    "norm_dropped": ("_norm_term", _norm("dropped")),
+    "norm_R_not_1mR": ("_norm_term", _norm("R_not_1mR")),
+    "norm_no_mean_abs": ("_norm_term", _norm("no_mean_abs")),
+    "select_window_not_forced": ("select_top_b", _select("window_not_forced")),
+    "select_ties_high_slot": ("select_top_b", _select("ties_high_slot")),
+    "select_ascending": ("select_top_b", _select("ascending_scores")),
+    "select_off_by_one": ("select_top_b", _select("off_by_one")),
+    "calibrate_abs_of_mean": ("calibrate", _calib_abs_of_mean),
+    "compact_freed_off_by_one": ("compact_paged_sequence", _compact_freed_off_by_one),
+}
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert not _some_pin_fails()
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, repl = MUTATIONS[name]
+    monkeypatch.setitem(T.__dict__, "_orig_compact", T.compact_paged_sequence)
+    monkeypatch.setattr(T, attr, repl)
+    if hasattr(oracle, attr):
+        monkeypatch.setattr(oracle, attr, repl)
+    assert _some_pin_fails(), f"planted mistake {name!r} was not caught by any pin"

@@ -1,0 +1,402 @@
+"""Pins of the float64 oracle against facts fixed outside the oracle itself.
+
+Each test states what it pins.  Nothing here calls the HIP library.
+  P1  exact-centre identity: with E[q] = q the trig series equals the mean over the
+      offsets of the post-RoPE dot product, computed with textbook 2x2 rotations
+  P2  R = 0 limit: zero centre leaves the pure norm term
+  P3  single-band hand values (3-4-5 triangle) and theta_f hand values
+  P4  invariants: position shift, key scaling, mean-fold linearity, identical heads, k = 0
+  P5  brute-force top-B on tiny inputs (all subsets), plus window / budget edge cases
+  P6  calibration closed forms
+  P7  compaction invariants
+"""
+
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import triattention as T
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+# ---------------------------------------------------------------------------------------
+# helpers that are independent of the oracle's formula
+# ---------------------------------------------------------------------------------------
+
+def rope_rotate(x, position, base, layout):
+    """Textbook RoPE: rotate each frequency pair of x by position * theta_f with an
+    explicit 2x2 rotation matrix.  theta_f = base ** (-2 f / d) written out per f."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    out = np.empty_like(x)
+    for f in range(d // 2):
+        theta = base ** (-(2.0 * f) / d)
+        ang = position * theta
+        c, s = math.cos(ang), math.sin(ang)
+        if layout == "half":
+            i0, i1 = f, f + d // 2
+        else:
+            i0, i1 = 2 * f, 2 * f + 1
+        rot = np.array([[c, -s], [s, c]])
+        out[..., [i0, i1]] = np.stack([x[..., i0], x[..., i1]], -1) @ rot.T
+    return out
+
+
+def bands_of(x, layout):
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    if layout == "half":
+        re, im = x[..., : d // 2], x[..., d // 2:]
+    else:
+        re, im = x[..., 0::2], x[..., 1::2]
+    return np.stack([re, im], axis=-1)          # [..., F, 2] real pairs
+
+
+# ---------------------------------------------------------------------------------------
+# P1 exact-centre identity
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("layout", ["half", "interleaved"])
+@pytest.mark.parametrize("d,base,qpos,offsets", [
+    (128, 1e4, 2047, [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024]),
+    (128, 1e6, 131071, [2 ** i for i in range(15)]),
+    (16, 500.0, 37, [1, 3, 9]),
+])
+def test_p1_exact_centre_identity(layout, d, base, qpos, offsets):
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal(d)
+    L = 24
+    keys = rng.standard_normal((L, d)) * rng.uniform(0.2, 3.0, (L, 1))
+    key_pos = np.sort(rng.choice(qpos + 1, size=L, replace=False))
+    key_pos[-1] = qpos
+    center = bands_of(q, layout)[None]                                   # E[q] = q
+    mag = np.hypot(center[..., 0], center[..., 1])                       # E|q_f| = |q_f|
+    got = oracle.score_keys(keys, center, mag, base=base, offsets=offsets,
+                            key_pos=key_pos, query_pos=qpos, layout=layout)
+    want = np.zeros(L)
+    for delta in offsets:
+        rq = rope_rotate(q, qpos + delta, base, layout)
+        for j in range(L):
+            want[j] += rope_rotate(keys[j], key_pos[j], base, layout) @ rq
+    want /= len(offsets)
+    bound = oracle.score_magnitude_bound(keys, center, mag, layout=layout)
+    assert np.all(np.abs(got - want) <= 1e-9 * bound)
+
+
+# ---------------------------------------------------------------------------------------
+# P2 R = 0 limit
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("layout", ["half", "interleaved"])
+def test_p2_zero_centre_is_pure_norm(layout):
+    rng = np.random.default_rng(3)
+    d, L = 128, 50
+    keys = rng.standard_normal((L, d))
+    mean_abs = rng.uniform(0.1, 2.0, (1, d // 2))
+    center = np.zeros((1, d // 2, 2))
+    got = oracle.score_keys(keys, center, mean_abs, base=1e4, offsets=[1, 2, 4], layout=layout)
+    kb = bands_of(keys, layout)
+    k_abs = np.hypot(kb[..., 0], kb[..., 1])
+    want = (k_abs * mean_abs[0][None, :]).sum(axis=1)
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=0)
+
+
+def test_p2_partial_concentration_norm_coefficient():
+    # one band (d = 2, theta_0 = 1), E q = 0.6 (arg 0) against E|q| = 2: R = 0.3, so the
+    # norm coefficient is (1 - 0.3) * 2 = 1.4.  k = 2i (|k| = 2, arg pi/2), distance Delta:
+    # trig = 0.6 * 2 * cos(Delta - pi/2) = 1.2 sin(Delta);  norm = 1.4 * 2
+    keys = np.array([[0.0, 2.0]])
+    center = np.array([[[0.6, 0.0]]])
+    mean_abs = np.array([[2.0]])
+    delta = 5
+    got = oracle.score_keys(keys, center, mean_abs, base=10.0, offsets=[delta],
+                            key_pos=[0], query_pos=0)
+    want = 1.2 * math.sin(delta) + 2.8
+    assert abs(got[0] - want) < 1e-14
+
+
+# ---------------------------------------------------------------------------------------
+# P3 hand values
+# ---------------------------------------------------------------------------------------
+
+def test_p3_theta_hand_values():
+    th = oracle.rope_theta(10000.0, 4)
+    assert th[0] == 1.0
+    assert abs(th[1] - 0.01) < 1e-18
+    th = oracle.rope_theta(1e6, 128)
+    assert abs(th[32] - 1e-3) < 1e-18            # 1e6 ** (-64/128) = 1e-3
+    assert abs(th[63] - 1e6 ** (-126 / 128)) < 1e-20
+
+
+@pytest.mark.parametrize("delta", [1, 7, 1000, 147455])
+def test_p3_single_band_345(delta):
+    # d = 2 (one band), theta_0 = 1.  E q = 2i (|Eq| = 2, E|q| = 2, R = 1, no norm term),
+    # k = 3 + 4i (|k| = 5, arg k = phi with cos phi = 0.6, sin phi = 0.8).
+    # score = 10 cos(delta + pi/2 - phi) = 10 (sin(phi) cos(delta) - cos(phi) sin(delta))
+    #       = 8 cos(delta) - 6 sin(delta)
+    keys = np.array([[3.0, 4.0]])
+    center = np.array([[[0.0, 2.0]]])
+    got = oracle.score_keys(keys, center, np.array([[2.0]]), base=10.0, offsets=[delta],
+                            key_pos=[0], query_pos=0)
+    want = 8.0 * math.cos(delta) - 6.0 * math.sin(delta)
+    # the phase argument is ~delta in size: allow a few ulps of it, times |Eq||k| = 10
+    assert abs(got[0] - want) < 10 * 4 * np.spacing(float(delta) + 4.0)
+
+
+def test_p3_zero_distance_quarter_turn():
+    # E q = i, k = 1, distance 0: cos(pi/2) = 0
+    keys = np.array([[1.0, 0.0]])
+    got = oracle.score_keys(keys, np.array([[[0.0, 1.0]]]), np.array([[1.0]]), base=10.0,
+                            offsets=[0], key_pos=[0], query_pos=0)
+    assert abs(got[0]) < 1e-15
+
+
+def test_p3_offsets_are_averaged():
+    # E q = 1, k = 1, theta_0 = 1, Q = p: each offset contributes cos(Delta); the score is
+    # their mean, not their sum
+    keys = np.array([[1.0, 0.0]])
+    c = np.array([[[1.0, 0.0]]])
+    m = np.array([[1.0]])
+    one = oracle.score_keys(keys, c, m, base=10.0, offsets=[0], key_pos=[0], query_pos=0)
+    two = oracle.score_keys(keys, c, m, base=10.0, offsets=[0, 2], key_pos=[0], query_pos=0)
+    assert abs(one[0] - 1.0) < 1e-15
+    assert abs(two[0] - 0.5 * (1.0 + (1.0 - 2.0 * math.sin(1.0) ** 2))) < 1e-15   # cos 2 = 1 - 2 sin^2 1
+
+
+# ---------------------------------------------------------------------------------------
+# P4 invariants
+# ---------------------------------------------------------------------------------------
+
+def _random_unit(rng, G=3, L=40, d=32):
+    keys = rng.standard_normal((L, d)) + rng.standard_normal(d)
+    center = rng.standard_normal((G, d // 2, 2))
+    mag = np.hypot(center[..., 0], center[..., 1])
+    mean_abs = mag * rng.uniform(1.0, 3.0, mag.shape)
+    return keys, center, mean_abs
+
+
+def test_p4_shift_invariance():
+    rng = np.random.default_rng(11)
+    keys, center, mean_abs = _random_unit(rng)
+    pos = np.arange(keys.shape[0])
+    kw = dict(base=1e4, offsets=[1, 4, 16, 64])
+    a = oracle.score_keys(keys, center, mean_abs, key_pos=pos, query_pos=39, **kw)
+    b = oracle.score_keys(keys, center, mean_abs, key_pos=pos + 100003, query_pos=39 + 100003, **kw)
+    S = oracle.score_magnitude_bound(keys, center, mean_abs)
+    assert np.all(np.abs(a - b) <= 1e-9 * S)
+
+
+def test_p4_key_scaling():
+    rng = np.random.default_rng(12)
+    keys, center, mean_abs = _random_unit(rng)
+    kw = dict(base=1e4, offsets=[1, 2, 3])
+    a = oracle.score_keys(keys, center, mean_abs, **kw)
+    b = oracle.score_keys(2.5 * keys, center, mean_abs, **kw)
+    np.testing.assert_allclose(b, 2.5 * a, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(oracle.select_top_b(a, 40, 12, 4), oracle.select_top_b(b, 40, 12, 4))
+
+
+def test_p4_mean_fold_linearity():
+    # mean over heads == one head whose E q is the head-mean of E q and whose norm
+    # coefficient E|q| - |E q| is the head-mean of the heads' coefficients
+    rng = np.random.default_rng(13)
+    keys, center, mean_abs = _random_unit(rng, G=4)
+    cq = center[..., 0] + 1j * center[..., 1]
+    c_bar = cq.mean(axis=0)
+    n_bar = (mean_abs - np.abs(cq)).mean(axis=0)
+    m_bar = np.abs(c_bar) + n_bar
+    kw = dict(base=1e4, offsets=[1, 2, 4, 8])
+    a = oracle.score_keys(keys, center, mean_abs, reduce="mean", **kw)
+    b = oracle.score_keys(keys, c_bar[None], m_bar[None], reduce="max", **kw)
+    S = oracle.score_magnitude_bound(keys, center, mean_abs, reduce="mean")
+    assert np.all(np.abs(a - b) <= 1e-12 * S)
+
+
+def test_p4_identical_heads_and_max():
+    rng = np.random.default_rng(14)
+    keys, center, mean_abs = _random_unit(rng, G=1)
+    kw = dict(base=1e4, offsets=[1, 2, 4])
+    one = oracle.score_keys(keys, center, mean_abs, **kw)
+    c3 = np.repeat(center, 3, axis=0)
+    m3 = np.repeat(mean_abs, 3, axis=0)
+    np.testing.assert_allclose(oracle.score_keys(keys, c3, m3, reduce="max", **kw), one, rtol=1e-14)
+    np.testing.assert_allclose(oracle.score_keys(keys, c3, m3, reduce="mean", **kw), one, rtol=1e-13)
+    # max over distinct heads equals the elementwise max of single-head scores
+    keys, center, mean_abs = _random_unit(rng, G=3)
+    s, heads = oracle.score_keys(keys, center, mean_abs, return_heads=True, **kw)
+    for h in range(3):
+        single = oracle.score_keys(keys, center[h:h + 1], mean_abs[h:h + 1], **kw)
+        np.testing.assert_array_equal(heads[h], single)
+    np.testing.assert_array_equal(s, heads.max(axis=0))
+
+
+def test_p4_zero_key_scores_zero():
+    rng = np.random.default_rng(15)
+    keys, center, mean_abs = _random_unit(rng)
+    keys[5] = 0.0
+    s = oracle.score_keys(keys, center, mean_abs, base=1e4, offsets=[1, 2])
+    assert s[5] == 0.0
+
+
+def test_p4_bound_dominates_score():
+    rng = np.random.default_rng(16)
+    keys, center, mean_abs = _random_unit(rng, G=4, L=200)
+    mean_abs[1] *= 0.5                       # some R > 1 bands too
+    for reduce in ("max", "mean"):
+        s = oracle.score_keys(keys, center, mean_abs, base=1e6, offsets=[1, 2, 4], reduce=reduce)
+        S = oracle.score_magnitude_bound(keys, center, mean_abs, reduce=reduce)
+        assert np.all(np.abs(s) <= S * (1 + 1e-12))
+
+
+def test_p4_r_above_one_not_clamped():
+    # E|q| < |E q| gives a negative norm coefficient, used as written
+    keys = np.array([[0.0, 1.0]])                      # |k| = 1
+    center = np.array([[[2.0, 0.0]]])                  # |Eq| = 2
+    mean_abs = np.array([[1.0]])                       # R = 2
+    got = oracle.score_keys(keys, center, mean_abs, base=10.0, offsets=[0], key_pos=[0], query_pos=0)
+    # trig: 2 * 1 * cos(0 + 0 - pi/2) = 0 ; norm: (1 - 2) * 1 * 1 = -1
+    assert abs(got[0] - (-1.0)) < 1e-15
+
+
+# ---------------------------------------------------------------------------------------
+# P5 selection vs brute force
+# ---------------------------------------------------------------------------------------
+
+def brute_force_kept(scores, L, B, W):
+    """All subsets: keep the window, then among the candidate subsets of the right size
+    take the one whose descending score vector is largest, ties to the smallest slots."""
+    if L <= B:
+        return list(range(L))
+    w = min(W, B)
+    cand = list(range(L - w))
+    s = [(-math.inf if math.isnan(x) else x) for x in scores]
+    best = None
+    for sub in itertools.combinations(cand, B - w):
+        key = (tuple(sorted((s[j] for j in sub), reverse=True)), tuple(-j for j in sub))
+        if best is None or key > best[0]:
+            best = (key, sub)
+    return sorted(list(best[1]) + list(range(L - w, L)))
+
+
+@pytest.mark.parametrize("trial", range(60))
+def test_p5_select_matches_brute_force(trial):
+    rng = np.random.default_rng(1000 + trial)
+    L = int(rng.integers(1, 12))
+    B = int(rng.integers(1, 12))
+    W = int(rng.integers(0, 6))
+    kind = trial % 4
+    if kind == 0:
+        s = rng.standard_normal(L)
+    elif kind == 1:
+        s = rng.integers(-2, 3, L).astype(float)          # many ties
+    elif kind == 2:
+        s = rng.standard_normal(L)
+        s[rng.integers(0, L)] = np.nan
+        s[rng.integers(0, L)] = -np.inf
+    else:
+        s = np.zeros(L)
+        s[rng.integers(0, L)] = -0.0
+    got = oracle.select_top_b(s, L, B, W)
+    assert list(got) == brute_force_kept(list(s), L, B, W)
+
+
+def test_p5_edge_cases():
+    s = np.arange(10.0)[::-1]          # slot 0 best
+    assert list(oracle.select_top_b(s, 10, 10, 3)) == list(range(10))      # L <= B
+    assert list(oracle.select_top_b(s, 10, 4, 8)) == [6, 7, 8, 9]          # W >= B: window only
+    assert list(oracle.select_top_b(s, 10, 4, 0)) == [0, 1, 2, 3]          # W = 0
+    assert list(oracle.select_top_b(s, 10, 9, 2)) == [0, 1, 2, 3, 4, 5, 6, 8, 9]   # B = L - 1
+    assert list(oracle.select_top_b(np.zeros(6), 6, 3, 1)) == [0, 1, 5]    # ties -> low slots
+    assert list(oracle.select_top_b(np.full(6, np.nan), 6, 3, 1)) == [0, 1, 5]
+
+
+# ---------------------------------------------------------------------------------------
+# P6 calibration closed forms
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("layout", ["half", "interleaved"])
+def test_p6_identical_samples(layout):
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((2, 3, 16))
+    samples = np.broadcast_to(q, (7, 2, 3, 16))
+    center, mean_abs = oracle.calibrate(samples, layout)
+    qb = bands_of(q, layout)
+    np.testing.assert_allclose(center.real, qb[..., 0], rtol=1e-15)
+    np.testing.assert_allclose(center.imag, qb[..., 1], rtol=1e-15)
+    np.testing.assert_allclose(mean_abs, np.hypot(qb[..., 0], qb[..., 1]), rtol=1e-15)
+    np.testing.assert_allclose(oracle.concentration(center, mean_abs), 1.0, rtol=1e-15)
+
+
+def test_p6_rotating_samples_have_zero_centre():
+    N, r = 12, 1.7
+    ang = 2 * np.pi * np.arange(N) / N + 0.3
+    q = np.zeros((N, 1, 1, 4))
+    q[:, 0, 0, 0] = r * np.cos(ang)       # band 0 (half layout: re = x[0], im = x[2])
+    q[:, 0, 0, 2] = r * np.sin(ang)
+    q[:, 0, 0, 1] = 2.0                   # band 1 constant: centre 2 + 0i
+    center, mean_abs = oracle.calibrate(q, "half")
+    assert abs(center[0, 0, 0]) < 1e-15
+    assert abs(mean_abs[0, 0, 0] - r) < 1e-15
+    assert abs(center[0, 0, 1] - 2.0) < 1e-15
+    assert oracle.concentration(center, mean_abs)[0, 0, 0] < 1e-15
+
+
+def test_p6_scaling_and_permutation():
+    rng = np.random.default_rng(22)
+    q = rng.standard_normal((9, 2, 2, 8))
+    c1, m1 = oracle.calibrate(q)
+    c2, m2 = oracle.calibrate(3.0 * q[rng.permutation(9)])
+    np.testing.assert_allclose(c2, 3.0 * c1, rtol=1e-13)
+    np.testing.assert_allclose(m2, 3.0 * m1, rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------------------
+# P7 compaction invariants
+# ---------------------------------------------------------------------------------------
+
+def test_p7_dense_rows_are_bit_copies():
+    rng = np.random.default_rng(31)
+    k = rng.standard_normal((50, 8)).astype(np.float32)
+    v = rng.standard_normal((50, 8)).astype(np.float32)
+    kept = np.sort(rng.choice(50, 13, replace=False))
+    ko, vo, po = oracle.compact_dense(k, v, kept)
+    assert ko.tobytes() == b"".join(k[j].tobytes() for j in kept)
+    assert vo.tobytes() == b"".join(v[j].tobytes() for j in kept)
+    assert list(po) == list(kept)
+    pos = rng.integers(0, 10 ** 6, 50)
+    _, _, po = oracle.compact_dense(k, None, kept, pos=pos)
+    assert list(po) == list(pos[kept])
+
+
+def test_p7_paged_forward_packing():
+    rng = np.random.default_rng(32)
+    page, n_layer, n_kvh, d = 4, 2, 3, 5
+    L, B, W = 37, 14, 3
+    n_used = -(-L // page)
+    n_pages = n_used + 5
+    pool = rng.standard_normal((n_pages, n_layer, n_kvh, page, d))
+    pool_v = rng.standard_normal((n_pages, n_layer, n_kvh, page, d))
+    bt = rng.permutation(n_pages)[:n_used]
+    kept = {}
+    for l in range(n_layer):
+        for h in range(n_kvh):
+            kept[(l, h)] = oracle.select_top_b(rng.standard_normal(L), L, B, W)
+    pk, pv, freed, new_len = oracle.compact_paged_sequence(pool, pool_v, bt, L, kept, page)
+    assert new_len == min(B, L)
+    kept_pages = bt[: -(-new_len // page)]
+    assert set(freed) | set(kept_pages) == set(bt)
+    assert not (set(freed) & set(kept_pages))
+    assert len(set(freed)) == len(freed)
+    for (l, h), kk in kept.items():
+        for i, j in enumerate(kk):
+            got = pk[bt[i // page], l, h, i % page]
+            src = pool[bt[j // page], l, h, j % page]
+            assert got.tobytes() == src.tobytes()
+            assert pv[bt[i // page], l, h, i % page].tobytes() == pool_v[bt[j // page], l, h, j % page].tobytes()
+    # pages outside the sequence are untouched
+    others = sorted(set(range(n_pages)) - set(bt))
+    assert pk[others].tobytes() == pool[others].tobytes()
