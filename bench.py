@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Throughput of the TriAttention KV-cache compression pass on one MI355X.
+
+One step = one pass of the whole hot path over the resident synthetic cache:
+tri_score_keys -> tri_select_topb -> tri_compact_kv (dense, out of place), for every
+(layer, KV head) of the 32K-context GQA workload (36 layers x 8 KV heads x 32768 keys,
+bf16, 4 query heads per KV head, B = 2048, window 128).  Inputs are generated on the
+device before timing; the timed region is bracketed by torch.cuda.synchronize().
+
+Prints one JSON line with the metric (keys scored+selected+compacted per second), the
+roofline of the dominant kernel (scoring: algorithmic bytes = 256 B per key read, over its
+average HIP-event duration) and the CPU oracle timed on a bounded sample of units.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import multiprocessing as mp
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "Gkeys/s scored+selected+compacted at 32K ctx; % of HBM roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic.json")
+SCORE_SRC = os.path.join(ROOT, "kv_cache_compression_tri_amd", "csrc", "score.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="workload name (default: the 32K GQA pass)")
+    ap.add_argument("--cpu-units", type=int, default=0,
+                    help="units for the oracle baseline (0 = two per host core, capped at 32)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample)
+# ---------------------------------------------------------------------------------------
+
+def _oracle_unit(job):
+    """Score + select + compact one unit with the float64 oracle; returns seconds spent."""
+    import numpy as np
+    import oracle
+    name, s, l, h = job
+    from kv_cache_compression_tri_amd import synth
+    from kv_cache_compression_tri_amd.synth import workloads as W
+    w = W.WORKLOADS[name]
+    hp = W.make_params(w)
+    unit = W.unit_index(w, s, l, h)
+    L = int(hp.lengths[s])
+    keys = synth.rows_as_float(w.seed, synth.TAG_K, unit, L, hp.mu_k[l, h], hp.sigma, w.sink, w.dtype)
+    vals = synth.rows(w.seed, synth.TAG_V, unit, L, np.zeros(128, np.float32), np.ones(128, np.float32),
+                      False, w.dtype)
+    keys_raw = synth.rows(w.seed, synth.TAG_K, unit, L, hp.mu_k[l, h], hp.sigma, w.sink, w.dtype)
+    center, mean_abs = oracle.unit_heads(hp.center, hp.mean_abs, l, h, w.group)
+    t0 = time.perf_counter()
+    sc = oracle.score_keys(keys, center, mean_abs, base=w.base, offsets=w.offsets, layout=w.layout,
+                           reduce=w.reduce)
+    kept = oracle.select_top_b(sc, L, w.budget, w.window)
+    oracle.compact_dense(keys_raw, vals, kept)
+    return time.perf_counter() - t0, L
+
+
+def cpu_baseline(name, n_units):
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    from kv_cache_compression_tri_amd.synth import workloads as W
+    import numpy as np
+    w = W.WORKLOADS[name]
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    if n_units <= 0:
+        n_units = min(32, 2 * cores)
+    rng = np.random.default_rng(2024)
+    picks = rng.choice(w.n_units, size=min(n_units, w.n_units), replace=False)
+    jobs = [(name,) + tuple(int(x) for x in W.unit_coords(w, int(u))) for u in picks]
+    workers = min(cores, len(jobs))
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers, initializer=_pool_init) as pool:
+        res = pool.map(_oracle_unit, jobs)
+    wall = time.perf_counter() - t0
+    busy = sum(r[0] for r in res)
+    keys = sum(r[1] for r in res)
+    # rate over the oracle's own work, run on `workers` cores in parallel
+    rate = keys / (busy / workers) / 1e9
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": rate,
+        "unit": "Gkeys/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": (f"{len(jobs)} random units of {name} ({keys} keys; score+select+compact per unit, "
+                   f"float64 numpy, one single-threaded process per core; wall {wall:.1f} s, "
+                   f"oracle time {busy:.1f} core-s) on {cpu}"),
+    }
+
+
+def _pool_init():
+    os.environ["OMP_NUM_THREADS"] = "1"
+
+
+# ---------------------------------------------------------------------------------------
+# traffic counters recorded for the current scoring kernel
+# ---------------------------------------------------------------------------------------
+
+def recorded_traffic(name):
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+        with open(SCORE_SRC, "rb") as fh:
+            digest = hashlib.sha256(fh.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(name)
+    if not entry or entry.get("score_hip_sha256") != digest:
+        return None
+    return entry.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(units are independent, so N GPUs would each run this pass on their share)",
+              file=sys.stderr)
+        return 2
+    import torch
+    import kv_cache_compression_tri_amd as tri
+    from kv_cache_compression_tri_amd.synth import device as SD
+    from kv_cache_compression_tri_amd.synth import workloads as W
+
+    name = args.workload or W.BENCH_WORKLOAD
+    w = W.WORKLOADS[name]
+    if w.paged:
+        print("bench.py times the dense workloads (paged compaction is in place)", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    dw = SD.build(w)
+    kv = dw.kv()
+    dev = dw.k.device
+    units = w.n_units
+    keys_per_step = int(sum(int(x) for x in dw.hp.lengths)) * w.n_layer * w.n_kvh
+    scores = torch.empty((w.n_seq, w.n_layer, w.n_kvh, w.max_len), dtype=torch.float32, device=dev)
+    kept = torch.empty((w.n_seq, w.n_layer, w.n_kvh, w.budget), dtype=torch.int32, device=dev)
+    kept_n = torch.empty((w.n_seq,), dtype=torch.int32, device=dev)
+    k_out = torch.empty((w.n_seq, w.n_layer, w.n_kvh, w.budget, w.head_dim), dtype=dw.k.dtype, device=dev)
+    v_out = torch.empty_like(k_out) if dw.v is not None else None
+    pos_out = torch.empty((w.n_seq, w.n_layer, w.n_kvh, w.budget), dtype=torch.int32, device=dev)
+    new_len = torch.empty((w.n_seq,), dtype=torch.int32, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        tri.tri_score_keys(kv, dw.center, dw.mean_abs, rope_base=w.base, offsets=w.offsets, group=w.group,
+                           reduce=w.reduce, rope_layout=w.layout, scores=scores)
+        if ev is not None:
+            ev[1].record()
+        tri.tri_select_topb(scores, kv, w.budget, w.window, kept=kept, kept_n=kept_n)
+        if ev is not None:
+            ev[2].record()
+        tri.tri_compact_kv(kv, kept, kept_n, w.budget, k_out=k_out, v_out=v_out, pos_out=pos_out,
+                           new_len=new_len)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms = (t1 - t0) * 1e3 / args.steps
+    score_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    select_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    compact_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+    elt = 2 if w.dtype == "bf16" else 4
+    score_bytes = keys_per_step * w.head_dim * elt                       # every key read once
+    kept_rows = units * min(w.budget, w.max_len)
+    compact_bytes = kept_rows * w.head_dim * elt * (2 if w.with_values else 1) * 2   # read + write
+    pass_bytes = score_bytes + compact_bytes
+    achieved = score_bytes / (score_ms * 1e-3) / 1e9
+    value = keys_per_step / (ms * 1e-3) / 1e9
+    traffic = recorded_traffic(name)
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "Gkeys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": name,
+            "n_seq": w.n_seq, "n_layer": w.n_layer, "n_kv_heads": w.n_kvh, "group": w.group,
+            "context": w.max_len, "head_dim": w.head_dim, "kv_dtype": w.dtype, "budget": w.budget,
+            "window": w.window, "offsets": len(w.offsets), "reduce": w.reduce,
+            "keys_per_step": keys_per_step, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "score_kernel",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": score_bytes,
+            "avg_launch_ms": score_ms,
+        },
+        "pass": {
+            "algorithmic_bytes": pass_bytes,
+            "hbm_frac": pass_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "score_ms": score_ms, "select_ms": select_ms, "compact_ms": compact_ms,
+        },
+    }
+    del dw, kv, scores, kept, kept_n, k_out, v_out, pos_out, new_len
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(name, args.cpu_units)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,202 @@
+/*
+ * tri.h - C ABI of the TriAttention KV-cache compression pass for AMD Instinct MI355X
+ * (gfx950).  One shared library, libtri.so; every entry point is extern "C" and takes
+ * plain pointers and sizes.
+ *
+ * Sources (web pages about "TriAttention: Efficient Long Reasoning with Trigonometric KV
+ * Compression", Mao et al.):
+ *   [Review]  "TriAttention: Trigonometric KV Compression for Efficient Long Reasoning"
+ *             (alanhou.org review): sections "Core Mechanism", "Key Concepts".
+ *   [DevTo]   "TriAttention: How a Geometric Trick Cuts LLM Memory Use by 10x Without
+ *             Losing Accuracy" (dev.to): sections "Why Existing KV Cache Compression
+ *             Breaks in Production", "The Core Idea: Q/K Concentration in Pre-RoPE Space",
+ *             "Solving the Memory Fragmentation Problem", "What the Numbers Look Like".
+ *   [Project] "TriAttention: trigonometric KV cache compression for long reasoning"
+ *             (hysenlabs.com): sections "Pre-RoPE centres decide which keys are worth
+ *             keeping", "The KV budget is a runtime knob that chat sessions should
+ *             raise", "Calibration statistics are tied to a specific model".
+ *
+ * The pass, per unit = (sequence, layer, KV head) holding L cached pre-RoPE keys:
+ *   1. tri_score_keys   score every key from calibrated query statistics
+ *   2. tri_select_topb  keep the top-B keys (the recent window always kept)
+ *   3. tri_compact_kv   pack the survivors forward (dense out-of-place or paged in place)
+ * and, once per model, tri_calibrate_stats builds the statistics from query samples.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller unless a parameter says
+ *     "host".  The library never frees or retains them, allocates no device memory, and
+ *     keeps no state between calls (re-entrant; calls on different streams may overlap as
+ *     long as their output buffers are disjoint).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are asynchronous: they
+ *     return once their kernels are enqueued.  Argument errors are reported synchronously
+ *     before anything is launched; a device fault shows at the caller's next
+ *     synchronisation (and as TRI_EHIP from the next call that sees it).
+ *   - Workspace: if `ws_bytes != NULL` and `ws == NULL`, the call writes the bytes it needs
+ *     to *ws_bytes and returns TRI_OK without launching.  If both are non-NULL, *ws_bytes
+ *     is the capacity of `ws` (device memory, 256-byte aligned).  If `ws_bytes == NULL`
+ *     the call runs without workspace and fails with TRI_EWORKSPACE if it needs one.
+ *   - Return values are tri_status codes; tri_last_error() gives the text of the last
+ *     failure on the calling thread.
+ *   - Supported set: head_dim == 128 (F = 64 RoPE bands), dtype TRI_F32 or TRI_BF16, page
+ *     size 16, group (query heads per KV head) 1..8, up to 64 future offsets, per-unit
+ *     length up to 1,048,576 keys.  Other valid values return TRI_ENOTSUP.
+ */
+#ifndef TRI_H_
+#define TRI_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tri_status {
+  TRI_OK = 0,
+  TRI_EINVAL = -1,     /* bad argument or shape                       */
+  TRI_ENOTSUP = -2,    /* valid but outside the supported set          */
+  TRI_EWORKSPACE = -3, /* workspace missing or too small               */
+  TRI_EHIP = -4        /* HIP launch or runtime error                  */
+} tri_status;
+
+typedef enum tri_dtype { TRI_F32 = 0, TRI_BF16 = 1 } tri_dtype;
+
+/* Pairing of the RoPE frequency bands inside a head vector x[0..d):
+ *   TRI_ROPE_HALF:        band f = (x[f], x[f + d/2])   (rotate-half pairing)
+ *   TRI_ROPE_INTERLEAVED: band f = (x[2f], x[2f + 1])
+ * The pages do not fix the pairing; it must match the model's RoPE. */
+typedef enum tri_rope_layout { TRI_ROPE_HALF = 0, TRI_ROPE_INTERLEAVED = 1 } tri_rope_layout;
+
+/* Reduction of the per-query-head scores over the G query heads reading one KV head. */
+typedef enum tri_reduce { TRI_REDUCE_MAX = 0, TRI_REDUCE_MEAN = 1 } tri_reduce;
+
+typedef enum tri_kv_layout { TRI_DENSE = 0, TRI_PAGED = 1 } tri_kv_layout;
+
+/* Description of a pre-RoPE KV cache (all pointers device, caller-owned).
+ *   dense: k, v are [n_seq][n_layer][n_kvh][max_len][head_dim]; slot j of unit (s,l,h) is
+ *          row j; the unit holds seq_len[s] <= max_len keys.
+ *   paged: k, v are pools [n_pages][n_layer][n_kvh][page][head_dim]; slot j of sequence s
+ *          lives in page block_table[s * max_pages + j / page], row j % page.  Every page
+ *          holds all layers and KV heads of its 16 tokens, so it can be freed only when it
+ *          is empty for all of them ([DevTo] "Why Existing KV Cache Compression Breaks in
+ *          Production").  max_len is ignored; the per-unit slot capacity is
+ *          max_pages * page.
+ *   seq_len: [n_seq] int32 number of cached keys per sequence.
+ *   pos:     optional [n_seq][n_layer][n_kvh][slots] int32 RoPE positions of the cached
+ *            keys (slots = max_len dense, max_pages * page paged); NULL means the position
+ *            of slot j is j.  tri_score_keys supports only pos == NULL (TRI_ENOTSUP
+ *            otherwise); tri_compact_kv gathers pos when given. */
+typedef struct tri_kv {
+  int32_t layout;   /* tri_kv_layout */
+  int32_t dtype;    /* tri_dtype of k and v */
+  int32_t n_seq;
+  int32_t n_layer;
+  int32_t n_kvh;
+  int32_t head_dim;
+  int64_t max_len;
+  const int32_t *seq_len;
+  void *k;
+  void *v;          /* may be NULL (keys only) */
+  int32_t page;
+  int32_t max_pages;
+  const int32_t *block_table;
+  const int32_t *pos;
+} tri_kv;
+
+/* Scoring configuration.
+ *   rope_base: RoPE base; theta_f = rope_base^(-2f/head_dim).
+ *   offsets:   HOST array of n_offsets future query offsets Delta >= 0 (the score is the
+ *              mean over these offsets of the predicted logit at query_pos + Delta).
+ *   group:     G, query heads per KV head; query head hq reads KV head hq / G. */
+typedef struct tri_score_cfg {
+  double rope_base;
+  int32_t rope_layout;      /* tri_rope_layout */
+  int32_t n_offsets;
+  const int32_t *offsets;   /* host */
+  int32_t group;
+  int32_t reduce;           /* tri_reduce */
+} tri_score_cfg;
+
+/* Calibration of the query statistics ([Review] "Key Concepts": the centre is the mean of
+ * the pre-RoPE queries over a calibration set; [Project] "Calibration statistics are tied
+ * to a specific model").
+ *   q:        [n][n_layer][n_qh][head_dim] pre-RoPE query samples (dtype TRI_F32/TRI_BF16)
+ *   center:   out [n_layer][n_qh][head_dim/2][2] float32, E[q_f] = mean_n q_{n,f} (re, im)
+ *   mean_abs: out [n_layer][n_qh][head_dim/2] float32, E|q_f| = mean_n |q_{n,f}|
+ * Sums are accumulated in float64.  n >= 1.  Needs no workspace. */
+int tri_calibrate_stats(const void *q, int32_t dtype, int64_t n, int32_t n_layer, int32_t n_qh,
+                        int32_t head_dim, int32_t rope_layout, float *center, float *mean_abs,
+                        void *ws, size_t *ws_bytes, void *stream);
+
+/* Score every cached key ([Review] "Core Mechanism" and "Key Concepts": a trigonometric
+ * series in the query-key distance set by the pre-RoPE centres, plus norms; [DevTo] "The
+ * Core Idea": weakly concentrated heads blend in a norm signal weighted by the measured
+ * concentration).  For unit (s, l, h), key slot j with band values k_f and position p_j,
+ * and each query head hq of the group with statistics c_f = center[l][hq][f] (complex)
+ * and m_f = mean_abs[l][hq][f]:
+ *
+ *   R_f     = |c_f| / m_f                         (R_f = 0 where m_f = 0)
+ *   s_hq(j) = mean_{Delta in offsets} sum_f |c_f| |k_f| cos((Q - p_j + Delta) theta_f
+ *                                                       + arg c_f - arg k_f)
+ *           + sum_f (1 - R_f) m_f |k_f|
+ *   score(j) = max_hq s_hq(j)  (TRI_REDUCE_MAX)   or   mean_hq s_hq(j)  (TRI_REDUCE_MEAN)
+ *
+ * with Q = query_pos[s] (int64; NULL means seq_len[s] - 1).
+ *   center:   [n_layer][n_kvh * group][head_dim/2][2] float32
+ *   mean_abs: [n_layer][n_kvh * group][head_dim/2] float32
+ *   scores:   out float32 [n_seq][n_layer][n_kvh][slots] (slots = max_len dense,
+ *             max_pages * page paged); entries at j >= seq_len[s] are not written.
+ * Computed in float32 from float64-derived phase tables; needs no workspace. */
+int tri_score_keys(const tri_score_cfg *cfg, const float *center, const float *mean_abs,
+                   const tri_kv *kv, const int64_t *query_pos, float *scores, void *ws,
+                   size_t *ws_bytes, void *stream);
+
+/* Top-B selection per unit ([Review] "Core Mechanism": keep only the top-scoring keys;
+ * [Project] "The KV budget is a runtime knob": the budget bounds the whole kept cache).
+ * With L = seq_len[s]:
+ *   L <= budget: every slot is kept.
+ *   otherwise:   the last W' = min(window, budget) slots are kept, plus the best
+ *                budget - W' of the other slots ranked by (score descending, slot
+ *                ascending); a NaN score ranks as -inf and -0.0 equals +0.0.
+ *   scores: [n_seq][n_layer][n_kvh][slots] float32 as written by tri_score_keys
+ *   kept:   out int32 [n_seq][n_layer][n_kvh][budget], kept slots in ascending order;
+ *           entries past the kept count are set to -1
+ *   kept_n: out int32 [n_seq], min(budget, seq_len[s]) (same for every unit of s)
+ * Needs no workspace. */
+int tri_select_topb(const float *scores, const tri_kv *kv, int32_t budget, int32_t window,
+                    int32_t *kept, int32_t *kept_n, void *ws, size_t *ws_bytes, void *stream);
+
+/* Forward-packing compaction ([DevTo] "Solving the Memory Fragmentation Problem": the
+ * survivors are moved into as few blocks as possible so that the emptied tail blocks can
+ * be reclaimed).  Row kept[i] of each unit moves to slot i, i < kept_n[s] (bit copy).
+ *   dense: k_out (and v_out iff kv->v != NULL) are [n_seq][n_layer][n_kvh][budget][d],
+ *          written out of place; freed / n_freed must be NULL.
+ *   paged: k_out = v_out = NULL (in place through the block tables; kv->k and kv->v are
+ *          modified).  Because every unit of a sequence keeps kept_n[s] rows, pages
+ *          block_table[s][ceil(kept_n/page) .. ceil(seq_len/page)) become empty for every
+ *          layer and head; they are written to freed[s * max_pages + 0 ..] with their
+ *          count in n_freed[s] (both optional, both or neither).  Rows of the last kept
+ *          page past kept_n are left as they were.  The block table is not modified.
+ *   pos_out: optional out int32 [n_seq][n_layer][n_kvh][budget], RoPE position of the row
+ *            now in slot i (kv->pos gathered, or kept[i] when kv->pos == NULL).
+ *   new_len: optional out int32 [n_seq], = kept_n.
+ * kept must be ascending per unit (as written by tri_select_topb); the in-place order of
+ * the paged path relies on kept[i] >= i. */
+int tri_compact_kv(const tri_kv *kv, const int32_t *kept, const int32_t *kept_n, int32_t budget,
+                   void *k_out, void *v_out, int32_t *pos_out, int32_t *freed, int32_t *n_freed,
+                   int32_t *new_len, void *stream);
+
+/* Text of the last failure on the calling thread ("" if none).  Owned by the library;
+ * valid until the next call on this thread. */
+const char *tri_last_error(void);
+
+/* ABI version of this header: major * 10000 + minor * 100 + patch. */
+int tri_version(void);
+
+#define TRI_VERSION 10000
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRI_H_ */

@@ -1,0 +1,272 @@
+"""TriAttention KV-cache compression pass for AMD Instinct MI355X (gfx950).
+
+Thin Python binding of libtri.so with the same entry-point names as include/tri.h.  It only
+marshals arguments (torch tensors -> device pointers, the current HIP stream, output
+allocation); every step of the pass runs in the library's HIP kernels.  If the library is
+not built, every call raises.
+
+    kv = KVCache.dense(k, v, seq_len)                       # or KVCache.paged(...)
+    scores = tri_score_keys(kv, center, mean_abs, rope_base=1e6, offsets=[1, 2, 4], group=4)
+    kept, kept_n = tri_select_topb(scores, kv, budget=2048, window=128)
+    out = tri_compact_kv(kv, kept, kept_n, budget=2048)
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+from . import _abi
+from ._abi import TriError  # noqa: F401
+
+__all__ = [
+    "KVCache",
+    "TriError",
+    "tri_calibrate_stats",
+    "tri_score_keys",
+    "tri_select_topb",
+    "tri_compact_kv",
+    "tri_version",
+    "compress",
+]
+
+_LAYOUTS = {"half": _abi.TRI_ROPE_HALF, "interleaved": _abi.TRI_ROPE_INTERLEAVED}
+_REDUCE = {"max": _abi.TRI_REDUCE_MAX, "mean": _abi.TRI_REDUCE_MEAN}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return _abi.TRI_BF16
+    if t.dtype == torch.float32:
+        return _abi.TRI_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+@dataclass
+class KVCache:
+    """A pre-RoPE KV cache in device memory (see tri_kv in include/tri.h).
+
+    dense: k, v [n_seq, n_layer, n_kvh, max_len, head_dim]
+    paged: k, v pools [n_pages, n_layer, n_kvh, page, head_dim] with block_table
+           [n_seq, max_pages] (int32) mapping slot j of sequence s to page
+           block_table[s, j // page], row j % page
+    seq_len: int32 [n_seq] on the device; pos: optional int32 RoPE positions
+    """
+
+    k: object
+    v: object
+    seq_len: object
+    layout: str = "dense"
+    block_table: object = None
+    pos: object = None
+
+    @classmethod
+    def dense(cls, k, v, seq_len, pos=None):
+        return cls(k, v, seq_len, "dense", None, pos)
+
+    @classmethod
+    def paged(cls, k_pool, v_pool, block_table, seq_len, pos=None):
+        return cls(k_pool, v_pool, seq_len, "paged", block_table, pos)
+
+    @property
+    def n_seq(self) -> int:
+        return int(self.seq_len.shape[0])
+
+    @property
+    def slots(self) -> int:
+        if self.layout == "dense":
+            return int(self.k.shape[3])
+        return int(self.block_table.shape[1]) * int(self.k.shape[3])
+
+    def descriptor(self) -> _abi.TriKV:
+        torch = _torch()
+        _dev(self.k, "k")
+        _dev(self.v, "v")
+        _dev(self.seq_len, "seq_len", torch.int32)
+        _dev(self.pos, "pos", torch.int32)
+        if self.v is not None and (self.v.shape != self.k.shape or self.v.dtype != self.k.dtype):
+            raise ValueError("v must match k in shape and dtype")
+        d = _abi.TriKV()
+        d.dtype = _dtype_code(self.k)
+        d.head_dim = int(self.k.shape[-1])
+        d.n_layer = int(self.k.shape[1])
+        d.n_kvh = int(self.k.shape[2])
+        d.n_seq = self.n_seq
+        d.seq_len = self.seq_len.data_ptr()
+        d.k = self.k.data_ptr()
+        d.v = None if self.v is None else self.v.data_ptr()
+        d.pos = None if self.pos is None else self.pos.data_ptr()
+        if self.layout == "dense":
+            if self.k.dim() != 5 or int(self.k.shape[0]) != self.n_seq:
+                raise ValueError("dense k must be [n_seq, n_layer, n_kvh, max_len, head_dim]")
+            d.layout = _abi.TRI_DENSE
+            d.max_len = int(self.k.shape[3])
+        elif self.layout == "paged":
+            _dev(self.block_table, "block_table", torch.int32)
+            if self.k.dim() != 5 or self.block_table.dim() != 2 or int(self.block_table.shape[0]) != self.n_seq:
+                raise ValueError("paged k must be [n_pages, n_layer, n_kvh, page, head_dim] with "
+                                 "block_table [n_seq, max_pages]")
+            d.layout = _abi.TRI_PAGED
+            d.page = int(self.k.shape[3])
+            d.max_pages = int(self.block_table.shape[1])
+            d.block_table = self.block_table.data_ptr()
+        else:
+            raise ValueError(f"unknown layout {self.layout!r}")
+        if self.pos is not None and self.pos.numel() != self.n_seq * d.n_layer * d.n_kvh * self.slots:
+            raise ValueError("pos must be [n_seq, n_layer, n_kvh, slots]")
+        return d
+
+
+def tri_version() -> int:
+    return _abi.lib().tri_version()
+
+
+def tri_calibrate_stats(q, rope_layout: str = "half", center=None, mean_abs=None, stream=None):
+    """Query statistics from pre-RoPE samples q [n, n_layer, n_qh, head_dim].
+
+    Returns (center [n_layer, n_qh, F, 2] float32, mean_abs [n_layer, n_qh, F] float32).
+    """
+    torch = _torch()
+    L = _abi.lib()
+    _dev(q, "q")
+    if q.dim() != 4:
+        raise ValueError("q must be [n, n_layer, n_qh, head_dim]")
+    n, n_layer, n_qh, d = (int(x) for x in q.shape)
+    if center is None:
+        center = torch.empty((n_layer, n_qh, d // 2, 2), dtype=torch.float32, device=q.device)
+    if mean_abs is None:
+        mean_abs = torch.empty((n_layer, n_qh, d // 2), dtype=torch.float32, device=q.device)
+    _dev(center, "center", torch.float32)
+    _dev(mean_abs, "mean_abs", torch.float32)
+    _abi.check(L.tri_calibrate_stats(_ptr(q), _dtype_code(q), n, n_layer, n_qh, d, _LAYOUTS[rope_layout],
+                                     _ptr(center), _ptr(mean_abs), None, None, _stream(stream)))
+    return center, mean_abs
+
+
+def _score_cfg(rope_base, offsets, group, reduce, rope_layout):
+    offs = (ctypes.c_int32 * len(offsets))(*[int(o) for o in offsets])
+    cfg = _abi.TriScoreCfg()
+    cfg.rope_base = float(rope_base)
+    cfg.rope_layout = _LAYOUTS[rope_layout]
+    cfg.n_offsets = len(offsets)
+    cfg.offsets = ctypes.cast(offs, ctypes.POINTER(ctypes.c_int32))
+    cfg.group = int(group)
+    cfg.reduce = _REDUCE[reduce]
+    return cfg, offs
+
+
+def tri_score_keys(kv: KVCache, center, mean_abs, *, rope_base: float, offsets: Sequence[int],
+                   group: int, reduce: str = "max", rope_layout: str = "half", query_pos=None,
+                   scores=None, stream=None):
+    """Score every cached key; returns float32 scores [n_seq, n_layer, n_kvh, slots]."""
+    torch = _torch()
+    L = _abi.lib()
+    desc = kv.descriptor()
+    _dev(center, "center", torch.float32)
+    _dev(mean_abs, "mean_abs", torch.float32)
+    _dev(query_pos, "query_pos", torch.int64)
+    if scores is None:
+        scores = torch.empty((kv.n_seq, desc.n_layer, desc.n_kvh, kv.slots), dtype=torch.float32,
+                             device=kv.k.device)
+    _dev(scores, "scores", torch.float32)
+    cfg, _keep = _score_cfg(rope_base, offsets, group, reduce, rope_layout)
+    _abi.check(L.tri_score_keys(ctypes.byref(cfg), _ptr(center), _ptr(mean_abs), ctypes.byref(desc),
+                                _ptr(query_pos), _ptr(scores), None, None, _stream(stream)))
+    return scores
+
+
+def tri_select_topb(scores, kv: KVCache, budget: int, window: int, kept=None, kept_n=None, stream=None):
+    """Top-B per unit; returns (kept int32 [n_seq, n_layer, n_kvh, budget], kept_n int32 [n_seq])."""
+    torch = _torch()
+    L = _abi.lib()
+    desc = kv.descriptor()
+    _dev(scores, "scores", torch.float32)
+    if kept is None:
+        kept = torch.empty((kv.n_seq, desc.n_layer, desc.n_kvh, budget), dtype=torch.int32, device=scores.device)
+    if kept_n is None:
+        kept_n = torch.empty((kv.n_seq,), dtype=torch.int32, device=scores.device)
+    _dev(kept, "kept", torch.int32)
+    _dev(kept_n, "kept_n", torch.int32)
+    _abi.check(L.tri_select_topb(_ptr(scores), ctypes.byref(desc), int(budget), int(window), _ptr(kept),
+                                 _ptr(kept_n), None, None, _stream(stream)))
+    return kept, kept_n
+
+
+def tri_compact_kv(kv: KVCache, kept, kept_n, budget: int, k_out=None, v_out=None, pos_out=None,
+                   freed=None, n_freed=None, new_len=None, want_pos=True, want_freed=True, stream=None):
+    """Forward-pack the survivors.  Returns a dict with the outputs that were written.
+
+    dense: k_out / v_out [n_seq, n_layer, n_kvh, budget, d] (allocated if not given)
+    paged: in place; freed [n_seq, max_pages] and n_freed [n_seq] list the emptied pages
+    """
+    torch = _torch()
+    L = _abi.lib()
+    desc = kv.descriptor()
+    dev = kv.k.device
+    _dev(kept, "kept", torch.int32)
+    _dev(kept_n, "kept_n", torch.int32)
+    shape_u = (kv.n_seq, desc.n_layer, desc.n_kvh)
+    if kv.layout == "dense":
+        if k_out is None:
+            k_out = torch.empty(shape_u + (budget, desc.head_dim), dtype=kv.k.dtype, device=dev)
+        if kv.v is not None and v_out is None:
+            v_out = torch.empty_like(k_out)
+    elif want_freed:
+        if freed is None:
+            freed = torch.empty((kv.n_seq, desc.max_pages), dtype=torch.int32, device=dev)
+        if n_freed is None:
+            n_freed = torch.empty((kv.n_seq,), dtype=torch.int32, device=dev)
+    if want_pos and pos_out is None:
+        pos_out = torch.empty(shape_u + (budget,), dtype=torch.int32, device=dev)
+    if new_len is None:
+        new_len = torch.empty((kv.n_seq,), dtype=torch.int32, device=dev)
+    for t, name in ((k_out, "k_out"), (v_out, "v_out")):
+        _dev(t, name, kv.k.dtype)
+    for t, name in ((pos_out, "pos_out"), (freed, "freed"), (n_freed, "n_freed"), (new_len, "new_len")):
+        _dev(t, name, torch.int32)
+    _abi.check(L.tri_compact_kv(ctypes.byref(desc), _ptr(kept), _ptr(kept_n), int(budget), _ptr(k_out),
+                                _ptr(v_out), _ptr(pos_out), _ptr(freed), _ptr(n_freed), _ptr(new_len),
+                                _stream(stream)))
+    return {"k_out": k_out, "v_out": v_out, "pos_out": pos_out, "freed": freed, "n_freed": n_freed,
+            "new_len": new_len}
+
+
+def compress(kv: KVCache, center, mean_abs, *, rope_base, offsets, group, budget, window,
+             reduce="max", rope_layout="half", query_pos=None, stream=None):
+    """Score, select and compact in one call (convenience; not part of the C ABI)."""
+    scores = tri_score_keys(kv, center, mean_abs, rope_base=rope_base, offsets=offsets, group=group,
+                            reduce=reduce, rope_layout=rope_layout, query_pos=query_pos, stream=stream)
+    kept, kept_n = tri_select_topb(scores, kv, budget, window, stream=stream)
+    out = tri_compact_kv(kv, kept, kept_n, budget, stream=stream)
+    out.update(scores=scores, kept=kept, kept_n=kept_n)
+    return out

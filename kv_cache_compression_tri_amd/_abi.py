@@ -1,0 +1,96 @@
+"""ctypes declarations of libtri.so (mirrors include/tri.h).  Loading fails loudly."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_double, c_int, c_int32, c_int64, c_size_t, c_void_p
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "lib", "libtri.so")
+
+TRI_OK, TRI_EINVAL, TRI_ENOTSUP, TRI_EWORKSPACE, TRI_EHIP = 0, -1, -2, -3, -4
+TRI_F32, TRI_BF16 = 0, 1
+TRI_ROPE_HALF, TRI_ROPE_INTERLEAVED = 0, 1
+TRI_REDUCE_MAX, TRI_REDUCE_MEAN = 0, 1
+TRI_DENSE, TRI_PAGED = 0, 1
+
+EXPORTED = (
+    "tri_calibrate_stats",
+    "tri_score_keys",
+    "tri_select_topb",
+    "tri_compact_kv",
+    "tri_last_error",
+    "tri_version",
+)
+
+
+class TriKV(ctypes.Structure):
+    _fields_ = [
+        ("layout", c_int32),
+        ("dtype", c_int32),
+        ("n_seq", c_int32),
+        ("n_layer", c_int32),
+        ("n_kvh", c_int32),
+        ("head_dim", c_int32),
+        ("max_len", c_int64),
+        ("seq_len", c_void_p),
+        ("k", c_void_p),
+        ("v", c_void_p),
+        ("page", c_int32),
+        ("max_pages", c_int32),
+        ("block_table", c_void_p),
+        ("pos", c_void_p),
+    ]
+
+
+class TriScoreCfg(ctypes.Structure):
+    _fields_ = [
+        ("rope_base", c_double),
+        ("rope_layout", c_int32),
+        ("n_offsets", c_int32),
+        ("offsets", POINTER(c_int32)),
+        ("group", c_int32),
+        ("reduce", c_int32),
+    ]
+
+
+class TriError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"libtri error {code}: {message}")
+        self.code = code
+
+
+_LIB = None
+
+
+def lib(path: str = LIB_PATH):
+    """Load libtri.so once; raise if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build the HIP library first (python -m kv_cache_compression_tri_amd.build)")
+    L = ctypes.CDLL(path)
+    L.tri_calibrate_stats.argtypes = [c_void_p, c_int32, c_int64, c_int32, c_int32, c_int32, c_int32,
+                                      c_void_p, c_void_p, c_void_p, POINTER(c_size_t), c_void_p]
+    L.tri_score_keys.argtypes = [POINTER(TriScoreCfg), c_void_p, c_void_p, POINTER(TriKV), c_void_p,
+                                 c_void_p, c_void_p, POINTER(c_size_t), c_void_p]
+    L.tri_select_topb.argtypes = [c_void_p, POINTER(TriKV), c_int32, c_int32, c_void_p, c_void_p,
+                                  c_void_p, POINTER(c_size_t), c_void_p]
+    L.tri_compact_kv.argtypes = [POINTER(TriKV), c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+                                 c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+    L.tri_last_error.argtypes = []
+    L.tri_last_error.restype = c_char_p
+    L.tri_version.argtypes = []
+    for name in ("tri_calibrate_stats", "tri_score_keys", "tri_select_topb", "tri_compact_kv", "tri_version"):
+        getattr(L, name).restype = c_int
+    _LIB = L
+    return L
+
+
+def check(rc: int) -> None:
+    if rc != TRI_OK:
+        msg = lib().tri_last_error()
+        raise TriError(rc, msg.decode() if msg else "")

@@ -1,0 +1,263 @@
+// C ABI of libtri.so: argument validation, float64 coefficient preparation and kernel
+// dispatch for the TriAttention KV-cache compression pass.  The entry points and their
+// contracts are declared and documented in include/tri.h.
+#include "tri.h"
+#include "tri_internal.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(TRI_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t slots_of(const tri_kv* kv) {
+  return kv->layout == TRI_PAGED ? int64_t(kv->max_pages) * kv->page : kv->max_len;
+}
+
+int check_dims(int32_t head_dim) {
+  if (head_dim < 2 || (head_dim & 1)) return fail(TRI_EINVAL, "head_dim must be even and >= 2 (got %d)", head_dim);
+  if (head_dim != tri::kHeadDim) return fail(TRI_ENOTSUP, "head_dim %d is not supported (only 128)", head_dim);
+  return TRI_OK;
+}
+
+int check_kv(const tri_kv* kv, bool need_k) {
+  if (!kv) return fail(TRI_EINVAL, "kv descriptor is NULL");
+  if (kv->layout != TRI_DENSE && kv->layout != TRI_PAGED) return fail(TRI_EINVAL, "unknown kv layout %d", kv->layout);
+  if (kv->dtype != TRI_F32 && kv->dtype != TRI_BF16) return fail(TRI_EINVAL, "unknown dtype %d", kv->dtype);
+  if (kv->n_seq < 1 || kv->n_layer < 1 || kv->n_kvh < 1)
+    return fail(TRI_EINVAL, "n_seq, n_layer and n_kvh must be >= 1");
+  if (int rc = check_dims(kv->head_dim)) return rc;
+  if (!kv->seq_len) return fail(TRI_EINVAL, "seq_len is NULL");
+  if (need_k && !kv->k) return fail(TRI_EINVAL, "k is NULL");
+  if (kv->layout == TRI_DENSE) {
+    if (kv->max_len < 1) return fail(TRI_EINVAL, "max_len must be >= 1");
+  } else {
+    if (kv->page < 1 || kv->max_pages < 1) return fail(TRI_EINVAL, "page and max_pages must be >= 1");
+    if (kv->page != tri::kPage) return fail(TRI_ENOTSUP, "page size %d is not supported (only 16)", kv->page);
+    if (!kv->block_table) return fail(TRI_EINVAL, "block_table is NULL");
+  }
+  if (slots_of(kv) > tri::kMaxUnitLen)
+    return fail(TRI_ENOTSUP, "per-unit capacity %lld exceeds %lld slots", (long long)slots_of(kv),
+                (long long)tri::kMaxUnitLen);
+  const int64_t units = int64_t(kv->n_seq) * kv->n_layer * kv->n_kvh;
+  if (units > 0x7FFFFFFF) return fail(TRI_ENOTSUP, "too many units (%lld)", (long long)units);
+  return TRI_OK;
+}
+
+// 1: size query answered; 0: proceed; <0: error.
+int workspace(void* ws, size_t* ws_bytes, size_t need) {
+  if (ws_bytes && !ws) {
+    *ws_bytes = need;
+    return 1;
+  }
+  if (need == 0) return 0;
+  if (!ws || !ws_bytes) return fail(TRI_EWORKSPACE, "workspace of %zu bytes required", need);
+  if (*ws_bytes < need) return fail(TRI_EWORKSPACE, "workspace of %zu bytes required (%zu given)", need, *ws_bytes);
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tri_last_error(void) { return g_error.c_str(); }
+
+int tri_version(void) { return TRI_VERSION; }
+
+int tri_calibrate_stats(const void* q, int32_t dtype, int64_t n, int32_t n_layer, int32_t n_qh,
+                        int32_t head_dim, int32_t rope_layout, float* center, float* mean_abs,
+                        void* ws, size_t* ws_bytes, void* stream) {
+  try {
+    g_error.clear();
+    if (!q || !center || !mean_abs) return fail(TRI_EINVAL, "q, center and mean_abs must be non-NULL");
+    if (dtype != TRI_F32 && dtype != TRI_BF16) return fail(TRI_EINVAL, "unknown dtype %d", dtype);
+    if (rope_layout != TRI_ROPE_HALF && rope_layout != TRI_ROPE_INTERLEAVED)
+      return fail(TRI_EINVAL, "unknown rope layout %d", rope_layout);
+    if (n < 1 || n_layer < 1 || n_qh < 1) return fail(TRI_EINVAL, "n, n_layer and n_qh must be >= 1");
+    if (int rc = check_dims(head_dim)) return rc;
+    if (int64_t(n_layer) * n_qh > 0x7FFFFFFF) return fail(TRI_ENOTSUP, "too many heads");
+    if (int rc = workspace(ws, ws_bytes, 0)) return rc > 0 ? TRI_OK : rc;
+    tri::CalibParams p{};
+    p.q = q;
+    p.n = n;
+    p.n_layer = n_layer;
+    p.n_qh = n_qh;
+    p.center = center;
+    p.mean_abs = mean_abs;
+    (void)hipGetLastError();
+    hipError_t e = tri::launch_calib(p, dtype == TRI_BF16, rope_layout == TRI_ROPE_INTERLEAVED,
+                                     static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TRI_OK : hip_fail(e, "calibration launch");
+  } catch (...) {
+    return fail(TRI_EHIP, "unexpected host exception in tri_calibrate_stats");
+  }
+}
+
+int tri_score_keys(const tri_score_cfg* cfg, const float* center, const float* mean_abs,
+                   const tri_kv* kv, const int64_t* query_pos, float* scores, void* ws,
+                   size_t* ws_bytes, void* stream) {
+  try {
+    g_error.clear();
+    if (!cfg) return fail(TRI_EINVAL, "cfg is NULL");
+    if (int rc = check_kv(kv, true)) return rc;
+    if (!std::isfinite(cfg->rope_base) || cfg->rope_base <= 0.0)
+      return fail(TRI_EINVAL, "rope_base must be finite and > 0");
+    if (cfg->rope_layout != TRI_ROPE_HALF && cfg->rope_layout != TRI_ROPE_INTERLEAVED)
+      return fail(TRI_EINVAL, "unknown rope layout %d", cfg->rope_layout);
+    if (cfg->reduce != TRI_REDUCE_MAX && cfg->reduce != TRI_REDUCE_MEAN)
+      return fail(TRI_EINVAL, "unknown reduce %d", cfg->reduce);
+    if (cfg->group < 1) return fail(TRI_EINVAL, "group must be >= 1");
+    if (cfg->group > tri::kMaxGroup) return fail(TRI_ENOTSUP, "group %d > %d", cfg->group, tri::kMaxGroup);
+    if (cfg->n_offsets < 1 || !cfg->offsets) return fail(TRI_EINVAL, "at least one offset is required");
+    if (cfg->n_offsets > tri::kMaxOffsets)
+      return fail(TRI_ENOTSUP, "%d offsets > %d", cfg->n_offsets, tri::kMaxOffsets);
+    for (int i = 0; i < cfg->n_offsets; ++i)
+      if (cfg->offsets[i] < 0) return fail(TRI_EINVAL, "offsets must be >= 0");
+    if (!center || !mean_abs || !scores) return fail(TRI_EINVAL, "center, mean_abs and scores must be non-NULL");
+    if (kv->pos) return fail(TRI_ENOTSUP, "explicit key positions are not supported by tri_score_keys");
+    if (int rc = workspace(ws, ws_bytes, 0)) return rc > 0 ? TRI_OK : rc;
+
+    tri::ScoreParams p{};
+    // theta_f = base^(-2f/d) and C_f = mean over offsets of e^{i Delta theta_f}, in float64
+    for (int f = 0; f < tri::kBands; ++f) {
+      const double th = std::pow(cfg->rope_base, -2.0 * f / double(tri::kHeadDim));
+      double cr = 0.0, ci = 0.0;
+      for (int i = 0; i < cfg->n_offsets; ++i) {
+        const double a = double(cfg->offsets[i]) * th;
+        cr += std::cos(a);
+        ci += std::sin(a);
+      }
+      p.theta[f] = th;
+      p.c_re[f] = cr / cfg->n_offsets;
+      p.c_im[f] = ci / cfg->n_offsets;
+    }
+    const int64_t slots = slots_of(kv);
+    const int64_t units = int64_t(kv->n_seq) * kv->n_layer * kv->n_kvh;
+    p.k = kv->k;
+    p.seq_len = kv->seq_len;
+    p.query_pos = query_pos;
+    p.block_table = kv->layout == TRI_PAGED ? kv->block_table : nullptr;
+    p.center = center;
+    p.mean_abs = mean_abs;
+    p.scores = scores;
+    p.max_len = kv->max_len;
+    p.score_stride = slots;
+    p.n_layer = kv->n_layer;
+    p.n_kvh = kv->n_kvh;
+    p.group = cfg->group;
+    p.max_pages = kv->max_pages;
+    p.reduce_mean = cfg->reduce == TRI_REDUCE_MEAN;
+    p.chunks_per_span = 8;  // 1024 keys per wave work item
+    const int64_t span = int64_t(p.chunks_per_span) * tri::kChunk;
+    p.spans_per_unit = int32_t((slots + span - 1) / span);
+    p.n_items = units * p.spans_per_unit;
+    int64_t grid = (p.n_items + tri::kScoreWaves - 1) / tri::kScoreWaves;
+    if (grid > 4096) grid = 4096;
+    const int g_eff = p.reduce_mean ? 1 : cfg->group;
+    (void)hipGetLastError();
+    hipError_t e = tri::launch_score(p, g_eff, kv->dtype == TRI_BF16,
+                                     cfg->rope_layout == TRI_ROPE_INTERLEAVED,
+                                     kv->layout == TRI_PAGED, int(grid), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TRI_OK : hip_fail(e, "score launch");
+  } catch (...) {
+    return fail(TRI_EHIP, "unexpected host exception in tri_score_keys");
+  }
+}
+
+int tri_select_topb(const float* scores, const tri_kv* kv, int32_t budget, int32_t window,
+                    int32_t* kept, int32_t* kept_n, void* ws, size_t* ws_bytes, void* stream) {
+  try {
+    g_error.clear();
+    if (int rc = check_kv(kv, false)) return rc;
+    if (budget < 1) return fail(TRI_EINVAL, "budget must be >= 1");
+    if (window < 0) return fail(TRI_EINVAL, "window must be >= 0");
+    if (!scores || !kept || !kept_n) return fail(TRI_EINVAL, "scores, kept and kept_n must be non-NULL");
+    if (int rc = workspace(ws, ws_bytes, 0)) return rc > 0 ? TRI_OK : rc;
+    tri::SelectParams p{};
+    p.scores = scores;
+    p.score_stride = slots_of(kv);
+    p.seq_len = kv->seq_len;
+    p.kept = kept;
+    p.kept_n = kept_n;
+    p.budget = budget;
+    p.window = window;
+    p.units_per_seq = kv->n_layer * kv->n_kvh;
+    const int64_t units = int64_t(kv->n_seq) * p.units_per_seq;
+    (void)hipGetLastError();
+    hipError_t e = tri::launch_select(p, units, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TRI_OK : hip_fail(e, "select launch");
+  } catch (...) {
+    return fail(TRI_EHIP, "unexpected host exception in tri_select_topb");
+  }
+}
+
+int tri_compact_kv(const tri_kv* kv, const int32_t* kept, const int32_t* kept_n, int32_t budget,
+                   void* k_out, void* v_out, int32_t* pos_out, int32_t* freed, int32_t* n_freed,
+                   int32_t* new_len, void* stream) {
+  try {
+    g_error.clear();
+    if (int rc = check_kv(kv, true)) return rc;
+    if (!kept || !kept_n) return fail(TRI_EINVAL, "kept and kept_n must be non-NULL");
+    if (budget < 1) return fail(TRI_EINVAL, "budget must be >= 1");
+    const bool paged = kv->layout == TRI_PAGED;
+    const bool with_v = kv->v != nullptr;
+    if (paged) {
+      if (k_out || v_out) return fail(TRI_ENOTSUP, "paged compaction is in place: k_out and v_out must be NULL");
+      if ((freed == nullptr) != (n_freed == nullptr))
+        return fail(TRI_EINVAL, "freed and n_freed must both be given or both be NULL");
+    } else {
+      if (!k_out) return fail(TRI_EINVAL, "dense compaction needs k_out");
+      if (with_v != (v_out != nullptr)) return fail(TRI_EINVAL, "v_out must be given exactly when kv->v is");
+      if (freed || n_freed) return fail(TRI_EINVAL, "freed / n_freed apply to the paged layout only");
+    }
+    tri::CompactParams p{};
+    p.k = kv->k;
+    p.v = kv->v;
+    p.k_out = k_out;
+    p.v_out = v_out;
+    p.kept = kept;
+    p.kept_n = kept_n;
+    p.seq_len = kv->seq_len;
+    p.block_table = paged ? kv->block_table : nullptr;
+    p.pos = kv->pos;
+    p.pos_out = pos_out;
+    p.freed = freed;
+    p.n_freed = n_freed;
+    p.new_len = new_len;
+    p.max_len = kv->max_len;
+    p.pos_stride = slots_of(kv);
+    p.budget = budget;
+    p.units_per_seq = kv->n_layer * kv->n_kvh;
+    p.n_layer = kv->n_layer;
+    p.n_kvh = kv->n_kvh;
+    p.max_pages = kv->max_pages;
+    p.chunks_per_unit = (budget + 63) / 64;
+    const int64_t units = int64_t(kv->n_seq) * p.units_per_seq;
+    if (!paged && units * p.chunks_per_unit > 0x7FFFFFFF) return fail(TRI_ENOTSUP, "grid too large");
+    (void)hipGetLastError();
+    hipError_t e = tri::launch_compact(p, units, kv->dtype == TRI_BF16, paged, with_v,
+                                       static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TRI_OK : hip_fail(e, "compaction launch");
+  } catch (...) {
+    return fail(TRI_EHIP, "unexpected host exception in tri_compact_kv");
+  }
+}
+
+}  // extern "C"

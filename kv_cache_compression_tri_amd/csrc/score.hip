@@ -1,0 +1,338 @@
+// Key-scoring kernel of the TriAttention compression pass (gfx950).
+//
+// What it computes (per unit = sequence s, layer l, KV head h; key slot j at position p_j;
+// query heads hq of the group with centre c_f = E[q_f] and m_f = E|q_f|):
+//
+//   s_hq(j) = mean_Delta sum_f |c_f||k_f| cos((Q - p_j + Delta) theta_f + arg c_f - arg k_f)
+//           + sum_f (1 - R_f) m_f |k_f|,          R_f = |c_f| / m_f
+//
+// The first term is the cosine series in the query-key distance that fixed pre-RoPE
+// centres produce after RoPE ("TriAttention: Trigonometric KV Compression for Efficient
+// Long Reasoning", sections "Core Mechanism" and "Key Concepts"); the second blends in a
+// norm-only signal weighted by the measured concentration ("TriAttention: How a Geometric
+// Trick Cuts LLM Memory Use by 10x Without Losing Accuracy", section "The Core Idea: Q/K
+// Concentration in Pre-RoPE Space").
+//
+// Evaluation (exact algebraic rewrite, no per-key transcendental except |k_f|):
+//   |c||k| cos(d theta + arg c - arg k) = Re(c conj(k) e^{i d theta}), so
+//   s_hq(j) = sum_f Re( W_f e^{-i (p_j - p_a) theta_f} conj(k_f) ) + N_f |k_f|
+//   with W_f = c_f C_f e^{i (Q - p_a) theta_f},  C_f = mean_Delta e^{i Delta theta_f},
+//   N_f = m_f - |c_f| (= (1 - R_f) m_f), and p_a an anchor slot.
+// W is built in float64 per anchor and rounded to float32; e^{-i r theta_f} for the offset
+// r = p_j - p_a < kChunk comes from an LDS table computed in float64.  Large phases never
+// go through a float32 sin/cos.  For the mean reduction W and N are averaged over the
+// group first (both terms are linear in them).
+//
+// Mapping: 8 lanes per key, lane g of a key owns bands 8g..8g+7, so the 8 lanes of a key
+// read its row as two coalesced 128-byte lines (half layout) and a wave scores 8 keys per
+// step.  Per-lane partial sums are combined with three DPP steps inside each 8-lane group.
+// A wave owns a span of keys of one unit; the anchored weights live in registers and are
+// rotated by e^{-i kChunk theta_f} at each chunk boundary.  Scores of 8 steps are gathered
+// into one lane each and written as one coalesced 256-byte store.
+#include "tri_internal.h"
+
+namespace tri {
+namespace {
+
+template <bool BF16>
+struct Frag {
+  uint4 d[BF16 ? 2 : 4];
+};
+
+__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// (re, im) of band b (0..7) of the lane's fragment.
+template <bool BF16, bool IL>
+__device__ __forceinline__ void band_of(const Frag<BF16>& fr, int b, float& re, float& im) {
+  if constexpr (BF16) {
+    if constexpr (!IL) {
+      const uint32_t wr = word(fr.d[0], b >> 1), wi = word(fr.d[1], b >> 1);
+      re = (b & 1) ? bf16_hi(wr) : bf16_lo(wr);
+      im = (b & 1) ? bf16_hi(wi) : bf16_lo(wi);
+    } else {
+      const uint32_t w = word(fr.d[b >> 2], b & 3);
+      re = bf16_lo(w);
+      im = bf16_hi(w);
+    }
+  } else {
+    if constexpr (!IL) {
+      re = __uint_as_float(word(fr.d[b >> 2], b & 3));
+      im = __uint_as_float(word(fr.d[2 + (b >> 2)], b & 3));
+    } else {
+      re = __uint_as_float(word(fr.d[b >> 1], 2 * (b & 1)));
+      im = __uint_as_float(word(fr.d[b >> 1], 2 * (b & 1) + 1));
+    }
+  }
+}
+
+// Load the lane's 8 bands of one key row.
+template <bool BF16, bool IL>
+__device__ __forceinline__ void load_frag(const char* row, int g, Frag<BF16>& fr) {
+  if constexpr (BF16) {
+    if constexpr (!IL) {
+      fr.d[0] = *reinterpret_cast<const uint4*>(row + g * 16);
+      fr.d[1] = *reinterpret_cast<const uint4*>(row + 128 + g * 16);
+    } else {
+      fr.d[0] = *reinterpret_cast<const uint4*>(row + g * 32);
+      fr.d[1] = *reinterpret_cast<const uint4*>(row + g * 32 + 16);
+    }
+  } else {
+    if constexpr (!IL) {
+      fr.d[0] = *reinterpret_cast<const uint4*>(row + g * 32);
+      fr.d[1] = *reinterpret_cast<const uint4*>(row + g * 32 + 16);
+      fr.d[2] = *reinterpret_cast<const uint4*>(row + 256 + g * 32);
+      fr.d[3] = *reinterpret_cast<const uint4*>(row + 256 + g * 32 + 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fr.d[i] = *reinterpret_cast<const uint4*>(row + g * 64 + 16 * i);
+    }
+  }
+}
+
+// Sum over the 8 lanes of a key (lanes 8k..8k+7): two quad swaps and a half-row mirror.
+__device__ __forceinline__ float sum8(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  return v;
+}
+
+// float64 weight of query head hq, band f at anchor A = C_f e^{i(Q - p_a) theta_f}.
+__device__ __forceinline__ void head_weight(const ScoreParams& P, int l, int hq, int n_qh, int f,
+                                            double ar, double ai, double& wr, double& wi,
+                                            double& nc) {
+  const int64_t idx = (int64_t(l) * n_qh + hq) * kBands + f;
+  const float2 c = reinterpret_cast<const float2*>(P.center)[idx];
+  const float m = P.mean_abs[idx];
+  const double cr = c.x, ci = c.y;
+  wr = cr * ar - ci * ai;
+  wi = cr * ai + ci * ar;
+  // (1 - R_f) m_f = m_f - |c_f|; a band with m_f = 0 carries no norm term
+  nc = (m > 0.0f) ? double(m) - sqrt(cr * cr + ci * ci) : 0.0;
+}
+
+template <int GE, bool BF16, bool IL, bool PAGED>
+__global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScoreParams P) {
+  constexpr int NW = kScoreWaves;
+  constexpr int STEPS = kChunk / 8;            // 8 keys per wave step
+  constexpr int PF = GE <= 4 ? 4 : 2;          // steps of loads in flight
+  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int ROW = kHeadDim * ESZ;
+  static_assert(STEPS % PF == 0 && STEPS % 8 == 0, "chunk geometry");
+
+  __shared__ float4 tab[kChunk * kBands / 2];  // e^{-i r theta_f}, r < kChunk, float32 pairs
+  __shared__ float2 stepc[kBands];             // e^{-i kChunk theta_f}
+  __shared__ double2 anc[NW][kBands];          // per-wave anchors (float64)
+
+  const int tid = threadIdx.x;
+  // ---- phase table: float64 recurrences from one sincos per run, rounded once ----------
+  {
+    constexpr int RL = kChunk / NW;
+    const int f = tid & 63, run = tid >> 6;
+    const double th = P.theta[f];
+    double s1, c1, zr, zi;
+    sincos(-th, &s1, &c1);
+    sincos(-double(run * RL) * th, &zi, &zr);
+    float2* t2 = reinterpret_cast<float2*>(tab);
+    const int g = f >> 3, r = (f & 7) >> 1, e = f & 1;
+    for (int m = 0; m < RL; ++m) {
+      const int j = run * RL + m;
+      t2[((((j >> 3) * 4 + r) * 64) + ((j & 7) * 8 + g)) * 2 + e] = make_float2(float(zr), float(zi));
+      const double nr = zr * c1 - zi * s1;
+      zi = zr * s1 + zi * c1;
+      zr = nr;
+    }
+    if (tid < kBands) {
+      double ss, cc;
+      sincos(-double(kChunk) * th, &ss, &cc);
+      stepc[tid] = make_float2(float(cc), float(ss));
+    }
+  }
+  __syncthreads();
+
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kk = lane >> 3;   // key of the step
+  const int g = lane & 7;     // band group
+  const int ups = P.n_layer * P.n_kvh;
+  const int n_qh = P.n_kvh * P.group;
+  const int S = P.chunks_per_span * kChunk;
+
+  for (int64_t item = int64_t(blockIdx.x) * NW + wave; item < P.n_items;
+       item += int64_t(gridDim.x) * NW) {
+    const int64_t unit = item / P.spans_per_unit;
+    const int span = int(item - unit * P.spans_per_unit);
+    const int s = int(unit / ups);
+    const int rem = int(unit - int64_t(s) * ups);
+    const int l = rem / P.n_kvh;
+    const int h = rem - l * P.n_kvh;
+    const int L = min(max(P.seq_len[s], 0), int(P.score_stride));
+    const int p0 = span * S;
+    if (p0 >= L) continue;
+    const int64_t Q = P.query_pos ? P.query_pos[s] : int64_t(L) - 1;
+    const int nkeys = min(S, L - p0);
+    const int n_steps = (nkeys + 7) >> 3;
+
+    {  // anchor of this span, one band per lane
+      const double ang = double(Q - p0) * P.theta[lane];
+      double sa, ca;
+      sincos(ang, &sa, &ca);
+      const double cr = P.c_re[lane], ci = P.c_im[lane];
+      anc[wave][lane] = make_double2(cr * ca - ci * sa, cr * sa + ci * ca);
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    float wr[GE][8], wn[GE][8], nn[GE][8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int f = g * 8 + b;
+      const double2 A = anc[wave][f];
+      if (P.reduce_mean) {
+        double sr = 0.0, si = 0.0, sn = 0.0;
+        for (int hh = 0; hh < P.group; ++hh) {
+          double r0, i0, n0;
+          head_weight(P, l, h * P.group + hh, n_qh, f, A.x, A.y, r0, i0, n0);
+          sr += r0;
+          si += i0;
+          sn += n0;
+        }
+        const double inv = 1.0 / double(P.group);
+        wr[0][b] = float(sr * inv);
+        wn[0][b] = float(-si * inv);
+        nn[0][b] = float(sn * inv);
+      } else {
+#pragma unroll
+        for (int hh = 0; hh < GE; ++hh) {
+          double r0, i0, n0;
+          head_weight(P, l, h * P.group + hh, n_qh, f, A.x, A.y, r0, i0, n0);
+          wr[hh][b] = float(r0);
+          wn[hh][b] = float(-i0);
+          nn[hh][b] = float(n0);
+        }
+      }
+    }
+
+    const char* kunit = static_cast<const char*>(P.k) + (PAGED ? 0 : unit * P.max_len * ROW);
+    const int32_t* bt = PAGED ? P.block_table + int64_t(s) * P.max_pages : nullptr;
+    auto load_step = [&](int n, Frag<BF16>& fr) {
+      const int key0 = p0 + 8 * n;   // wave-uniform
+      if (n < n_steps && key0 + kk < p0 + nkeys) {
+        const char* row;
+        if constexpr (PAGED) {
+          const int64_t page = bt[key0 >> 4];
+          row = kunit + ((((page * P.n_layer + l) * P.n_kvh + h) * kPage) + (key0 & 15) + kk) * ROW;
+        } else {
+          row = kunit + int64_t(key0 + kk) * ROW;
+        }
+        load_frag<BF16, IL>(row, g, fr);
+      } else {
+#pragma unroll
+        for (int i = 0; i < (BF16 ? 2 : 4); ++i) fr.d[i] = make_uint4(0, 0, 0, 0);
+      }
+    };
+
+    Frag<BF16> ring[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) load_step(i, ring[i]);
+
+    float* out = P.scores + unit * P.score_stride + p0;
+    float keep = 0.0f;
+    int n = 0;
+    for (int c = 0; n < n_steps; ++c) {
+      if (c > 0) {  // next chunk: W <- W e^{-i kChunk theta_f}
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const float2 R = stepc[g * 8 + b];
+#pragma unroll
+          for (int hh = 0; hh < GE; ++hh) {
+            const float a = wr[hh][b], q = wn[hh][b];
+            wr[hh][b] = fmaf(a, R.x, q * R.y);
+            wn[hh][b] = fmaf(q, R.x, -(a * R.y));
+          }
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < STEPS; ++it) {
+        if (n < n_steps) {
+          const Frag<BF16> cur = ring[it % PF];
+          load_step(n + PF, ring[it % PF]);
+          const float4* tp = tab + it * 4 * 64 + lane;
+          const float4 t4[4] = {tp[0], tp[64], tp[128], tp[192]};
+          float acc[GE];
+#pragma unroll
+          for (int hh = 0; hh < GE; ++hh) acc[hh] = 0.0f;
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+            float a, q;
+            band_of<BF16, IL>(cur, b, a, q);
+            const float tc = (b & 1) ? t4[b >> 1].z : t4[b >> 1].x;
+            const float ts = (b & 1) ? t4[b >> 1].w : t4[b >> 1].y;
+            const float xr = fmaf(tc, a, ts * q);     // Re(e^{-i r theta} conj(k))
+            const float xi = fmaf(ts, a, -(tc * q));  // Im(...)
+            const float nk = __builtin_amdgcn_sqrtf(fmaf(a, a, q * q));
+#pragma unroll
+            for (int hh = 0; hh < GE; ++hh) {
+              acc[hh] = fmaf(wr[hh][b], xr, acc[hh]);
+              acc[hh] = fmaf(wn[hh][b], xi, acc[hh]);
+              acc[hh] = fmaf(nn[hh][b], nk, acc[hh]);
+            }
+          }
+          float sc = sum8(acc[0]);
+#pragma unroll
+          for (int hh = 1; hh < GE; ++hh) sc = fmaxf(sc, sum8(acc[hh]));
+          if ((it & 7) == g) keep = sc;
+          if ((it & 7) == 7 || n == n_steps - 1) {
+            // lane (kk, g) holds the score of step (n & ~7) + g, key kk
+            const int step = (n & ~7) + g;
+            const int key = 8 * step + kk;
+            if (step <= n && key < nkeys) out[key] = keep;
+          }
+          ++n;
+        }
+      }
+    }
+  }
+}
+
+template <int GE>
+hipError_t launch_ge(const ScoreParams& p, bool bf16, bool il, bool paged, int grid, hipStream_t st) {
+  const dim3 blk(kScoreWaves * 64), grd(grid);
+#define TRI_SCORE_CASE(B, I, PG)                                                     \
+  if (bf16 == B && il == I && paged == PG) {                                         \
+    hipLaunchKernelGGL((score_kernel<GE, B, I, PG>), grd, blk, 0, st, p);           \
+    return hipGetLastError();                                                        \
+  }
+  TRI_SCORE_CASE(true, false, false)
+  TRI_SCORE_CASE(true, false, true)
+  TRI_SCORE_CASE(true, true, false)
+  TRI_SCORE_CASE(true, true, true)
+  TRI_SCORE_CASE(false, false, false)
+  TRI_SCORE_CASE(false, false, true)
+  TRI_SCORE_CASE(false, true, false)
+  TRI_SCORE_CASE(false, true, true)
+#undef TRI_SCORE_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_score(const ScoreParams& p, int G_eff, bool bf16, bool interleaved, bool paged,
+                        int grid, hipStream_t stream) {
+  switch (G_eff) {
+    case 1: return launch_ge<1>(p, bf16, interleaved, paged, grid, stream);
+    case 2: return launch_ge<2>(p, bf16, interleaved, paged, grid, stream);
+    case 3: return launch_ge<3>(p, bf16, interleaved, paged, grid, stream);
+    case 4: return launch_ge<4>(p, bf16, interleaved, paged, grid, stream);
+    case 5: return launch_ge<5>(p, bf16, interleaved, paged, grid, stream);
+    case 6: return launch_ge<6>(p, bf16, interleaved, paged, grid, stream);
+    case 7: return launch_ge<7>(p, bf16, interleaved, paged, grid, stream);
+    case 8: return launch_ge<8>(p, bf16, interleaved, paged, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace tri

@@ -1,0 +1,90 @@
+// Internal launch descriptors shared by the host API and the kernels of libtri.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tri {
+
+constexpr int kHeadDim = 128;
+constexpr int kBands = 64;          // F = head_dim / 2 RoPE frequency bands
+constexpr int kPage = 16;           // paged-cache block size (tokens)
+constexpr int kMaxGroup = 8;        // query heads per KV head
+constexpr int kMaxOffsets = 64;
+constexpr int64_t kMaxUnitLen = 1 << 20;
+
+// Score kernel geometry: 8 lanes per key (8 bands each), 8 keys per wave per step, phase
+// table of kChunk consecutive offsets in LDS, weights re-anchored every kChunk keys.
+constexpr int kChunk = 128;
+constexpr int kScoreWaves = 4;      // waves per workgroup
+
+struct ScoreParams {
+  const void* k;
+  const int32_t* seq_len;
+  const int64_t* query_pos;
+  const int32_t* block_table;
+  const float* center;       // [n_layer][n_qh][64][2]
+  const float* mean_abs;     // [n_layer][n_qh][64]
+  float* scores;
+  int64_t max_len;           // dense token stride
+  int64_t score_stride;      // slots per unit in `scores`
+  int64_t n_items;           // units * spans_per_unit
+  int32_t n_layer, n_kvh, group, max_pages;
+  int32_t spans_per_unit;
+  int32_t chunks_per_span;
+  int32_t reduce_mean;
+  double theta[kBands];      // theta_f, float64
+  double c_re[kBands];       // C_f = mean over offsets of exp(i Delta theta_f), float64
+  double c_im[kBands];
+};
+
+struct SelectParams {
+  const float* scores;
+  int64_t score_stride;
+  const int32_t* seq_len;
+  int32_t* kept;
+  int32_t* kept_n;
+  int32_t budget;
+  int32_t window;
+  int32_t units_per_seq;
+};
+
+struct CompactParams {
+  const void* k;             // dense source or paged pool
+  const void* v;
+  void* k_out;               // dense only
+  void* v_out;
+  const int32_t* kept;
+  const int32_t* kept_n;
+  const int32_t* seq_len;
+  const int32_t* block_table;
+  const int32_t* pos;
+  int32_t* pos_out;
+  int32_t* freed;
+  int32_t* n_freed;
+  int32_t* new_len;
+  int64_t max_len;           // dense token stride
+  int64_t pos_stride;        // slots per unit of `pos`
+  int32_t budget;
+  int32_t units_per_seq;
+  int32_t n_layer, n_kvh, max_pages;
+  int32_t chunks_per_unit;   // dense: ceil(budget / 64)
+};
+
+struct CalibParams {
+  const void* q;
+  int64_t n;
+  int32_t n_layer, n_qh;
+  float* center;
+  float* mean_abs;
+};
+
+// launchers (return hipError_t of the launch)
+hipError_t launch_score(const ScoreParams& p, int G_eff, bool bf16, bool interleaved, bool paged,
+                        int grid, hipStream_t stream);
+hipError_t launch_select(const SelectParams& p, int64_t n_units, hipStream_t stream);
+hipError_t launch_compact(const CompactParams& p, int64_t n_units, bool bf16, bool paged,
+                          bool with_v, hipStream_t stream);
+hipError_t launch_calib(const CalibParams& p, bool bf16, bool interleaved, hipStream_t stream);
+
+}  // namespace tri

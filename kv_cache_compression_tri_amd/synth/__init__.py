@@ -1,0 +1,105 @@
+"""Seeded synthetic inputs for the compression pass (test and benchmark infrastructure).
+
+This module holds no step of the compression method.  It defines one counter-based
+generator of key/value elements, implemented twice from the same published definitions:
+here in numpy (host, for the oracle's inputs and small cases) and in ``csrc/synth.hip``
+(device, for the full-size caches).  Both produce bit-identical values:
+
+* hash:   SplitMix64's output function ``mix64`` (Steele, Lea & Flood, "Fast splittable
+          pseudorandom number generators", OOPSLA 2014), applied to the counter
+          ``key + n * 0x9E3779B97F4A7C15`` (the SplitMix64 stream read at index n).
+* normal: Irwin-Hall sum of twelve 16-bit uniforms minus 6 (a classic N(0, 1)
+          approximation with unit variance), formed as an exact integer numerator times
+          2^-16, so it is exact in float32.
+* value:  ``x = mu[col] + sigma[col] * n`` in float32 with each operation rounded once
+          (no fused multiply-add), times 20 on a sink row, then rounded to bfloat16 with
+          round-to-nearest-even (or kept as float32).
+
+Element (unit, row, col) of stream ``tag`` under ``seed`` uses counter
+``c = unit << 27 | row << 7 | col`` (row < 2^20, col < 128) and the three hashes at
+SplitMix64 indices 3c+1, 3c+2, 3c+3 of the stream keyed by ``mix64(seed << 8 | tag)``.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+GAMMA = 0x9E3779B97F4A7C15
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+_U64 = np.uint64
+
+TAG_K = 0
+TAG_V = 1
+SINK_SCALE = np.float32(20.0)
+MAX_ROWS = 1 << 20
+
+
+def mix64(z):
+    """SplitMix64 output function on uint64 arrays (wrapping arithmetic)."""
+    z = np.asarray(z, dtype=np.uint64)
+    z = (z ^ (z >> _U64(30))) * _M1
+    z = (z ^ (z >> _U64(27))) * _M2
+    return z ^ (z >> _U64(31))
+
+
+def stream_key(seed: int, tag: int) -> np.uint64:
+    if not (0 <= seed < (1 << 56)) or not (0 <= tag < 256):
+        raise ValueError("seed must be in [0, 2^56) and tag in [0, 256)")
+    return mix64(np.array([(seed << 8) | tag], dtype=np.uint64))[0]
+
+
+def normals(seed: int, tag: int, unit: int, rows, cols=128) -> np.ndarray:
+    """Irwin-Hall(12) - 6 variates for element counters (unit, rows[i], col), float32 [R, cols]."""
+    rows = np.asarray(rows, dtype=np.uint64).reshape(-1, 1)
+    col = np.arange(cols, dtype=np.uint64).reshape(1, -1)
+    if rows.size and int(rows.max()) >= MAX_ROWS:
+        raise ValueError("row index out of the counter's range")
+    c = (_U64(unit) << _U64(27)) | (rows << _U64(7)) | col
+    key = stream_key(seed, tag)
+    s = np.zeros(c.shape, dtype=np.int64)
+    with np.errstate(over="ignore"):
+        for i in range(3):
+            h = mix64(key + (_U64(3) * c + _U64(i + 1)) * _U64(GAMMA))
+            for w in range(4):
+                s += ((h >> _U64(16 * w)) & _U64(0xFFFF)).astype(np.int64)
+    m = (s - 393210).astype(np.float32)
+    return m * np.float32(2.0 ** -16)
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """Round float32 to bfloat16 (round to nearest, ties to even); returns uint16 bits."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def rows(seed: int, tag: int, unit: int, n_rows: int, mu, sigma, sink: bool,
+         dtype: str = "bf16", row_start: int = 0) -> np.ndarray:
+    """Rows row_start .. row_start+n_rows-1 of one unit.
+
+    Returns float32 [n_rows, 128] for dtype "f32" and uint16 bfloat16 bits for "bf16".
+    """
+    r = np.arange(row_start, row_start + n_rows, dtype=np.uint64)
+    n = normals(seed, tag, unit, r, len(mu))
+    mu = np.asarray(mu, dtype=np.float32)[None, :]
+    sigma = np.asarray(sigma, dtype=np.float32)[None, :]
+    x = mu + sigma * n                       # two float32 roundings, as on the device
+    if sink and row_start == 0 and n_rows > 0:
+        x[0] = SINK_SCALE * x[0]
+    if dtype == "f32":
+        return x.astype(np.float32)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def rows_as_float(seed, tag, unit, n_rows, mu, sigma, sink, dtype="bf16", row_start=0):
+    """Same rows as ``rows`` but always as float32 values (bf16 widened exactly)."""
+    r = rows(seed, tag, unit, n_rows, mu, sigma, sink, dtype, row_start)
+    return r if dtype == "f32" else bf16_bits_to_f32(r)

@@ -1,0 +1,186 @@
+"""C-ABI contract checks that need no GPU.
+
+The library must load, export every function declared in include/tri.h, and reject bad
+arguments before it makes any HIP call (the fake device pointers used here are never
+dereferenced: every call below fails validation or is a workspace-size query).
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from kv_cache_compression_tri_amd import _abi
+from kv_cache_compression_tri_amd.synth import device as synth_device
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tri.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_abi.LIB_PATH), reason="libtri.so not built")
+
+FAKE = ctypes.c_void_p(0x10000)
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(tri_\w+)\s*\(", text, flags=re.M))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == set(_abi.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(_abi.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _abi.LIB_PATH], capture_output=True, text=True).stdout
+    defined = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert declared_functions() <= defined
+
+
+def test_version_matches_header():
+    m = re.search(r"#define TRI_VERSION (\d+)", open(HEADER).read())
+    assert _abi.lib().tri_version() == int(m.group(1))
+
+
+def _kv(**over):
+    d = _abi.TriKV()
+    d.layout, d.dtype, d.n_seq, d.n_layer, d.n_kvh, d.head_dim = _abi.TRI_DENSE, _abi.TRI_BF16, 1, 2, 2, 128
+    d.max_len = 4096
+    d.seq_len = FAKE.value
+    d.k = FAKE.value
+    d.v = FAKE.value
+    d.page, d.max_pages, d.block_table, d.pos = 16, 256, FAKE.value, None
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d
+
+
+def _cfg(**over):
+    offs = (ctypes.c_int32 * 3)(1, 2, 4)
+    c = _abi.TriScoreCfg()
+    c.rope_base, c.rope_layout, c.n_offsets, c.group, c.reduce = 1e6, 0, 3, 4, 0
+    c.offsets = ctypes.cast(offs, ctypes.POINTER(ctypes.c_int32))
+    for k, v in over.items():
+        setattr(c, k, v)
+    return c, offs
+
+
+def _score(cfg=None, kv=None, center=FAKE, scores=FAKE, ws_query=False):
+    L = _abi.lib()
+    size = ctypes.c_size_t(123)
+    rc = L.tri_score_keys(None if cfg is None else ctypes.byref(cfg), center, FAKE,
+                          None if kv is None else ctypes.byref(kv), None, scores, None,
+                          ctypes.byref(size) if ws_query else None, None)
+    return rc, size.value
+
+
+def test_score_keys_validation():
+    c, _o = _cfg()
+    assert _score(None, _kv())[0] == _abi.TRI_EINVAL
+    assert _score(c, None)[0] == _abi.TRI_EINVAL
+    assert _score(c, _kv(head_dim=64))[0] == _abi.TRI_ENOTSUP
+    assert _score(c, _kv(head_dim=127))[0] == _abi.TRI_EINVAL
+    assert _score(c, _kv(dtype=7))[0] == _abi.TRI_EINVAL
+    assert _score(c, _kv(layout=5))[0] == _abi.TRI_EINVAL
+    assert _score(c, _kv(n_layer=0))[0] == _abi.TRI_EINVAL
+    assert _score(c, _kv(seq_len=None))[0] == _abi.TRI_EINVAL
+    assert _score(c, _kv(k=None))[0] == _abi.TRI_EINVAL
+    assert _score(c, _kv(max_len=0))[0] == _abi.TRI_EINVAL
+    assert _score(c, _kv(max_len=(1 << 20) + 1))[0] == _abi.TRI_ENOTSUP
+    assert _score(c, _kv(pos=FAKE.value))[0] == _abi.TRI_ENOTSUP
+    assert _score(c, _kv(layout=_abi.TRI_PAGED, page=32))[0] == _abi.TRI_ENOTSUP
+    assert _score(c, _kv(layout=_abi.TRI_PAGED, block_table=None))[0] == _abi.TRI_EINVAL
+    assert _score(c, _kv(), center=None)[0] == _abi.TRI_EINVAL
+    assert _score(c, _kv(), scores=None)[0] == _abi.TRI_EINVAL
+    for over, code in [(dict(group=0), _abi.TRI_EINVAL), (dict(group=9), _abi.TRI_ENOTSUP),
+                       (dict(n_offsets=0), _abi.TRI_EINVAL), (dict(rope_base=0.0), _abi.TRI_EINVAL),
+                       (dict(rope_base=float("nan")), _abi.TRI_EINVAL), (dict(reduce=3), _abi.TRI_EINVAL),
+                       (dict(rope_layout=2), _abi.TRI_EINVAL)]:
+        cc, _k = _cfg(**over)
+        assert _score(cc, _kv())[0] == code, over
+    many = (ctypes.c_int32 * 65)(*range(65))
+    cc, _k = _cfg(n_offsets=65, offsets=ctypes.cast(many, ctypes.POINTER(ctypes.c_int32)))
+    assert _score(cc, _kv())[0] == _abi.TRI_ENOTSUP
+    neg = (ctypes.c_int32 * 2)(1, -3)
+    cc, _k = _cfg(n_offsets=2, offsets=ctypes.cast(neg, ctypes.POINTER(ctypes.c_int32)))
+    assert _score(cc, _kv())[0] == _abi.TRI_EINVAL
+
+
+def test_score_keys_workspace_query_launches_nothing():
+    c, _o = _cfg()
+    rc, size = _score(c, _kv(), ws_query=True)
+    assert rc == _abi.TRI_OK and size == 0
+    rc, size = _score(c, _kv(layout=_abi.TRI_PAGED), ws_query=True)
+    assert rc == _abi.TRI_OK and size == 0
+
+
+def test_last_error_text():
+    c, _o = _cfg(group=9)
+    assert _score(c, _kv())[0] == _abi.TRI_ENOTSUP
+    assert b"group" in _abi.lib().tri_last_error()
+
+
+def test_select_validation():
+    L = _abi.lib()
+    size = ctypes.c_size_t(7)
+
+    def sel(kv=None, budget=16, window=4, kept=FAKE, ws=False):
+        return L.tri_select_topb(FAKE, ctypes.byref(kv or _kv()), budget, window, kept, FAKE, None,
+                                 ctypes.byref(size) if ws else None, None)
+    assert sel(budget=0) == _abi.TRI_EINVAL
+    assert sel(window=-1) == _abi.TRI_EINVAL
+    assert sel(kept=None) == _abi.TRI_EINVAL
+    assert sel(kv=_kv(head_dim=96)) == _abi.TRI_ENOTSUP
+    assert sel(ws=True) == _abi.TRI_OK and size.value == 0
+
+
+def test_compact_validation():
+    L = _abi.lib()
+
+    def comp(kv, k_out=FAKE, v_out=FAKE, freed=None, n_freed=None, budget=8):
+        return L.tri_compact_kv(ctypes.byref(kv), FAKE, FAKE, budget, k_out, v_out, None, freed, n_freed,
+                                None, None)
+    assert comp(_kv(), k_out=None) == _abi.TRI_EINVAL
+    assert comp(_kv(), v_out=None) == _abi.TRI_EINVAL
+    assert comp(_kv(v=None)) == _abi.TRI_EINVAL
+    assert comp(_kv(), freed=FAKE, n_freed=FAKE) == _abi.TRI_EINVAL
+    assert comp(_kv(), budget=0) == _abi.TRI_EINVAL
+    paged = _kv(layout=_abi.TRI_PAGED)
+    assert comp(paged) == _abi.TRI_ENOTSUP
+    assert comp(paged, k_out=None, v_out=None, freed=FAKE) == _abi.TRI_EINVAL
+    assert L.tri_compact_kv(ctypes.byref(paged), None, FAKE, 8, None, None, None, None, None, None,
+                            None) == _abi.TRI_EINVAL
+
+
+def test_calibrate_validation():
+    L = _abi.lib()
+    size = ctypes.c_size_t(5)
+
+    def cal(n=10, dtype=0, head_dim=128, layout=0, q=FAKE, ws=False):
+        return L.tri_calibrate_stats(q, dtype, n, 2, 4, head_dim, layout, FAKE, FAKE, None,
+                                     ctypes.byref(size) if ws else None, None)
+    assert cal(n=0) == _abi.TRI_EINVAL
+    assert cal(dtype=3) == _abi.TRI_EINVAL
+    assert cal(layout=9) == _abi.TRI_EINVAL
+    assert cal(head_dim=96) == _abi.TRI_ENOTSUP
+    assert cal(q=None) == _abi.TRI_EINVAL
+    assert cal(ws=True) == _abi.TRI_OK and size.value == 0
+
+
+def test_synth_library_exports_and_rejects_bad_arguments():
+    L = synth_device.lib()
+    for name in synth_device.SYNTH_EXPORTS:
+        assert hasattr(L, name)
+    assert L.tri_synth_fill_dense(None, 1, 1, 16, 1, FAKE, FAKE, 0, 0, 0, None) == -1
+    assert L.tri_synth_fill_dense(FAKE, 1, 1, (1 << 20) + 1, 1, FAKE, FAKE, 0, 0, 0, None) == -1
+    assert L.tri_synth_fill_paged(FAKE, 1, 1, 1, 1, 16, 0, FAKE, FAKE, FAKE, FAKE, 0, 0, 0, None) == -1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(_abi, "_LIB", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _abi.lib(os.path.join(ROOT, "no_such_dir", "libtri.so"))

@@ -1,0 +1,99 @@
+"""Host side of the seeded input generator and the workload parameters (no GPU)."""
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_compression_tri_amd import synth
+from kv_cache_compression_tri_amd.synth import workloads as W
+
+
+def test_mix64_known_values():
+    # SplitMix64 seeded with 0: first outputs are mix64(k * gamma), published reference values
+    g = np.uint64(synth.GAMMA)
+    with np.errstate(over="ignore"):
+        outs = synth.mix64(np.array([g, g * np.uint64(2), g * np.uint64(3)], dtype=np.uint64))
+    assert [int(x) for x in outs] == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+def test_normals_moments_and_range():
+    n = synth.normals(7, 0, 3, np.arange(4000), 128).ravel()
+    assert abs(n.mean()) < 0.01
+    assert abs(n.var() - 1.0) < 0.02
+    assert n.min() >= -6.0 and n.max() <= 6.0
+    assert n.dtype == np.float32
+    # exact multiples of 2^-16
+    assert np.all((n * 65536.0) == np.round(n * 65536.0))
+
+
+def test_normals_deterministic_and_stream_separated():
+    a = synth.normals(1, 0, 5, np.arange(64))
+    b = synth.normals(1, 0, 5, np.arange(64))
+    assert np.array_equal(a, b)
+    c = synth.normals(1, 1, 5, np.arange(64))
+    d = synth.normals(2, 0, 5, np.arange(64))
+    e = synth.normals(1, 0, 6, np.arange(64))
+    for other in (c, d, e):
+        assert abs(np.corrcoef(a.ravel(), other.ravel())[0, 1]) < 0.05
+    # a row range starting mid-unit equals the same rows of the full range
+    full = synth.normals(1, 0, 5, np.arange(100))
+    assert np.array_equal(full[40:60], synth.normals(1, 0, 5, np.arange(40, 60)))
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(100000).astype(np.float32) * 10
+    # add exact ties: values halfway between two bf16 numbers
+    ties = (np.arange(1, 2000, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
+    x = np.concatenate([x, ties, -ties])
+    ours = synth.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    assert np.array_equal(synth.bf16_bits_to_f32(ours), torch.from_numpy(ours.view(np.int16)).view(torch.bfloat16).float().numpy())
+
+
+def test_rows_sink_and_center():
+    mu = np.linspace(-1, 1, 128).astype(np.float32)
+    sig = np.full(128, 0.3, np.float32)
+    r = synth.rows(3, 0, 2, 8, mu, sig, sink=True, dtype="f32")
+    n = synth.normals(3, 0, 2, np.arange(8))
+    np.testing.assert_array_equal(r[1:], mu + sig * n[1:])
+    np.testing.assert_array_equal(r[0], np.float32(20) * (mu + sig * n[0]))
+    rb = synth.rows(3, 0, 2, 8, mu, sig, sink=True, dtype="bf16")
+    assert np.array_equal(rb, synth.f32_to_bf16_bits(r))
+
+
+@pytest.mark.parametrize("name", sorted(W.WORKLOADS))
+def test_workload_params(name):
+    w = W.WORKLOADS[name]
+    hp = W.make_params(w)
+    F = w.head_dim // 2
+    assert hp.center.shape == (w.n_layer, w.n_qh, F, 2) and hp.center.dtype == np.float32
+    assert hp.mean_abs.shape == (w.n_layer, w.n_qh, F)
+    assert hp.mu_k.shape == (w.n_layer, w.n_kvh, w.head_dim)
+    assert int(hp.low_r.sum()) == int(round(w.low_r_frac * w.n_layer * w.n_kvh))
+    mag = np.hypot(hp.center[..., 0].astype(np.float64), hp.center[..., 1].astype(np.float64))
+    R = mag / hp.mean_abs
+    low = np.repeat(hp.low_r, w.group, axis=1)
+    if low.any():
+        assert np.allclose(R[low], 0.3, rtol=1e-6)
+    assert np.allclose(R[~low], 1 / 1.1, rtol=1e-6)
+    if w.paged:
+        lo, hi = w.len_range
+        assert hp.lengths.min() >= lo and hp.lengths.max() <= hi
+        pages = -(-hp.lengths.astype(np.int64) // w.page)
+        assert hp.n_pages == pages.sum()
+        used = np.concatenate([hp.block_table[s, : pages[s]] for s in range(w.n_seq)])
+        assert np.array_equal(np.sort(used), np.arange(hp.n_pages))
+    else:
+        assert np.all(hp.lengths == w.max_len)
+    # deterministic
+    hp2 = W.make_params(w)
+    assert np.array_equal(hp.center, hp2.center) and np.array_equal(hp.mu_k, hp2.mu_k)
+
+
+def test_heteroscedastic_sigma_by_band():
+    w = W.WORKLOADS["long_128k_bf16"]
+    s = W.make_params(w).sigma
+    assert np.all(s[:32] == np.float32(0.1)) and np.all(s[64:96] == np.float32(0.1))
+    assert np.all(s[32:64] == np.float32(1.0)) and np.all(s[96:] == np.float32(1.0))
