@@ -41,7 +41,25 @@ def parse():
     ap.add_argument("--cpu-units", type=int, default=0,
                     help="units for the oracle baseline (0 = two per host core, capped at 32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB mebibytes (calibrates HBM counters)")
     return ap.parse_args()
+
+
+def copy_bandwidth(mib, reps=5):
+    """Plain device-to-device copy of `mib` MiB; returns (bytes moved per copy, GB/s)."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    return 2 * n, 2 * n / dt / 1e9
 
 
 # ---------------------------------------------------------------------------------------
@@ -149,6 +167,11 @@ def main():
               file=sys.stderr)
         return 2
     import torch
+    if args.copy_probe:
+        moved, gbs = copy_bandwidth(args.copy_probe)
+        print(json.dumps({"copy_probe_bytes_read": moved // 2, "copy_probe_bytes_written": moved // 2,
+                          "copy_GBps": gbs}), flush=True)
+        return 0
     import kv_cache_compression_tri_amd as tri
     from kv_cache_compression_tri_amd.synth import device as SD
     from kv_cache_compression_tri_amd.synth import workloads as W
@@ -252,6 +275,9 @@ def main():
     }
     del dw, kv, scores, kept, kept_n, k_out, v_out, pos_out, new_len
     torch.cuda.empty_cache()
+    _, copy_gbs = copy_bandwidth(1024)
+    line["pass"]["copy_GBps"] = copy_gbs
+    line["pass"]["frac_of_copy"] = pass_bytes / (ms * 1e-3) / 1e9 / copy_gbs
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(name, args.cpu_units)
     print(json.dumps(line), flush=True)

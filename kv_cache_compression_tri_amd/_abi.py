@@ -72,6 +72,8 @@ def lib(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build the HIP library first (python -m kv_cache_compression_tri_amd.build)")
+    # torch ships its own HIP runtime; load it first so libtri.so binds to the same one
+    import torch  # noqa: F401
     L = ctypes.CDLL(path)
     L.tri_calibrate_stats.argtypes = [c_void_p, c_int32, c_int64, c_int32, c_int32, c_int32, c_int32,
                                       c_void_p, c_void_p, c_void_p, POINTER(c_size_t), c_void_p]

@@ -27,6 +27,18 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(TRI_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Compute units of the current device (cached per device id).
+int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
+
 int64_t slots_of(const tri_kv* kv) {
   return kv->layout == TRI_PAGED ? int64_t(kv->max_pages) * kv->page : kv->max_len;
 }
@@ -164,12 +176,14 @@ int tri_score_keys(const tri_score_cfg* cfg, const float* center, const float* m
     p.group = cfg->group;
     p.max_pages = kv->max_pages;
     p.reduce_mean = cfg->reduce == TRI_REDUCE_MEAN;
-    p.chunks_per_span = 8;  // 1024 keys per wave work item
+    p.chunks_per_span = tri::kSpanChunks;
     const int64_t span = int64_t(p.chunks_per_span) * tri::kChunk;
     p.spans_per_unit = int32_t((slots + span - 1) / span);
     p.n_items = units * p.spans_per_unit;
+    // persistent grid: one workgroup per CU builds the 128 KB phase table once
     int64_t grid = (p.n_items + tri::kScoreWaves - 1) / tri::kScoreWaves;
-    if (grid > 4096) grid = 4096;
+    const int64_t resident = int64_t(cu_count());
+    if (grid > resident) grid = resident;
     const int g_eff = p.reduce_mean ? 1 : cfg->group;
     (void)hipGetLastError();
     hipError_t e = tri::launch_score(p, g_eff, kv->dtype == TRI_BF16,

@@ -13,22 +13,27 @@
 // Trick Cuts LLM Memory Use by 10x Without Losing Accuracy", section "The Core Idea: Q/K
 // Concentration in Pre-RoPE Space").
 //
-// Evaluation (exact algebraic rewrite, no per-key transcendental except |k_f|):
-//   |c||k| cos(d theta + arg c - arg k) = Re(c conj(k) e^{i d theta}), so
-//   s_hq(j) = sum_f Re( W_f e^{-i (p_j - p_a) theta_f} conj(k_f) ) + N_f |k_f|
-//   with W_f = c_f C_f e^{i (Q - p_a) theta_f},  C_f = mean_Delta e^{i Delta theta_f},
-//   N_f = m_f - |c_f| (= (1 - R_f) m_f), and p_a an anchor slot.
-// W is built in float64 per anchor and rounded to float32; e^{-i r theta_f} for the offset
-// r = p_j - p_a < kChunk comes from an LDS table computed in float64.  Large phases never
-// go through a float32 sin/cos.  For the mean reduction W and N are averaged over the
-// group first (both terms are linear in them).
+// Evaluation (exact algebraic rewrite; the only per-key transcendental is |k_f|):
+//   |c||k| cos(d theta + arg c - arg k) = Re(c conj(k) e^{i d theta}), so with an anchor
+//   slot p_a and r = p_j - p_a,
+//     s_hq(j) = sum_f Re( W_f x_f ) + N_f |k_f|,   x_f = e^{-i r theta_f} conj(k_f),
+//     W_f = c_f C_f e^{i (Q - p_a) theta_f},  C_f = mean_Delta e^{i Delta theta_f},
+//     N_f = m_f - |c_f|  (= (1 - R_f) m_f).
+// The anchor phase is formed in float64 per span; e^{-i r theta_f} (r < kChunk) comes from
+// an LDS table built in float64 and rounded once to float32.  Large phases never go through
+// a float32 sin/cos.  At each chunk boundary the weights rotate by e^{-i kChunk theta_f}.
+// For the mean reduction W and N are averaged over the group first (both terms are linear
+// in them).  bf16 keys are widened exactly to float32 (one shift or mask per element); all
+// arithmetic is float32.
 //
-// Mapping: 8 lanes per key, lane g of a key owns bands 8g..8g+7, so the 8 lanes of a key
-// read its row as two coalesced 128-byte lines (half layout) and a wave scores 8 keys per
-// step.  Per-lane partial sums are combined with three DPP steps inside each 8-lane group.
-// A wave owns a span of keys of one unit; the anchored weights live in registers and are
-// rotated by e^{-i kChunk theta_f} at each chunk boundary.  Scores of 8 steps are gathered
-// into one lane each and written as one coalesced 256-byte store.
+// Mapping: 8 lanes per key; lane g of a key owns bands 8g..8g+7, so the 8 lanes of a key
+// read its row as coalesced 16-byte pieces and a wave scores 8 keys per step.  Per-lane
+// partial sums are combined with three DPP steps inside each 8-lane group.  Each wave owns
+// one span of one unit at a time; the weights live in registers.  Key rows are addressed
+// from a wave-uniform (scalar) base plus a per-lane constant offset.  Scores of 8 steps are
+// gathered into one lane each and written as one coalesced 256-byte store.  The grid is
+// persistent (one workgroup of kScoreWaves waves per CU), so the 128 KB phase table is
+// built once per CU.
 #include "tri_internal.h"
 
 namespace tri {
@@ -49,46 +54,22 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 template <bool BF16, bool IL>
 __device__ __forceinline__ void band_of(const Frag<BF16>& fr, int b, float& re, float& im) {
   if constexpr (BF16) {
-    if constexpr (!IL) {
-      const uint32_t wr = word(fr.d[0], b >> 1), wi = word(fr.d[1], b >> 1);
-      re = (b & 1) ? bf16_hi(wr) : bf16_lo(wr);
-      im = (b & 1) ? bf16_hi(wi) : bf16_lo(wi);
-    } else {
+    if constexpr (IL) {
       const uint32_t w = word(fr.d[b >> 2], b & 3);
       re = bf16_lo(w);
       im = bf16_hi(w);
+    } else {
+      const uint32_t wr = word(fr.d[0], b >> 1), wi = word(fr.d[1], b >> 1);
+      re = (b & 1) ? bf16_hi(wr) : bf16_lo(wr);
+      im = (b & 1) ? bf16_hi(wi) : bf16_lo(wi);
     }
   } else {
-    if constexpr (!IL) {
-      re = __uint_as_float(word(fr.d[b >> 2], b & 3));
-      im = __uint_as_float(word(fr.d[2 + (b >> 2)], b & 3));
-    } else {
+    if constexpr (IL) {
       re = __uint_as_float(word(fr.d[b >> 1], 2 * (b & 1)));
       im = __uint_as_float(word(fr.d[b >> 1], 2 * (b & 1) + 1));
-    }
-  }
-}
-
-// Load the lane's 8 bands of one key row.
-template <bool BF16, bool IL>
-__device__ __forceinline__ void load_frag(const char* row, int g, Frag<BF16>& fr) {
-  if constexpr (BF16) {
-    if constexpr (!IL) {
-      fr.d[0] = *reinterpret_cast<const uint4*>(row + g * 16);
-      fr.d[1] = *reinterpret_cast<const uint4*>(row + 128 + g * 16);
     } else {
-      fr.d[0] = *reinterpret_cast<const uint4*>(row + g * 32);
-      fr.d[1] = *reinterpret_cast<const uint4*>(row + g * 32 + 16);
-    }
-  } else {
-    if constexpr (!IL) {
-      fr.d[0] = *reinterpret_cast<const uint4*>(row + g * 32);
-      fr.d[1] = *reinterpret_cast<const uint4*>(row + g * 32 + 16);
-      fr.d[2] = *reinterpret_cast<const uint4*>(row + 256 + g * 32);
-      fr.d[3] = *reinterpret_cast<const uint4*>(row + 256 + g * 32 + 16);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fr.d[i] = *reinterpret_cast<const uint4*>(row + g * 64 + 16 * i);
+      re = __uint_as_float(word(fr.d[b >> 2], b & 3));
+      im = __uint_as_float(word(fr.d[2 + (b >> 2)], b & 3));
     }
   }
 }
@@ -101,47 +82,54 @@ __device__ __forceinline__ float sum8(float v) {
   return v;
 }
 
-// float64 weight of query head hq, band f at anchor A = C_f e^{i(Q - p_a) theta_f}.
-__device__ __forceinline__ void head_weight(const ScoreParams& P, int l, int hq, int n_qh, int f,
-                                            double ar, double ai, double& wr, double& wi,
-                                            double& nc) {
-  const int64_t idx = (int64_t(l) * n_qh + hq) * kBands + f;
+// Weight of query head row `row` (= layer * n_qh + hq), band f at anchor
+// A = C_f e^{i(Q - p_a) theta_f}.
+__device__ __forceinline__ void head_weight(const ScoreParams& P, int64_t row, int f, float ar, float ai,
+                                            float& wr, float& wi, float& nc) {
+  const int64_t idx = row * kBands + f;
   const float2 c = reinterpret_cast<const float2*>(P.center)[idx];
   const float m = P.mean_abs[idx];
-  const double cr = c.x, ci = c.y;
-  wr = cr * ar - ci * ai;
-  wi = cr * ai + ci * ar;
+  wr = c.x * ar - c.y * ai;
+  wi = c.x * ai + c.y * ar;
   // (1 - R_f) m_f = m_f - |c_f|; a band with m_f = 0 carries no norm term
-  nc = (m > 0.0f) ? double(m) - sqrt(cr * cr + ci * ci) : 0.0;
+  nc = (m > 0.0f) ? m - __builtin_sqrtf(c.x * c.x + c.y * c.y) : 0.0f;
+}
+
+// LDS phase table: entry (r, f), r < kChunk, holds (c, s) = e^{-i r theta_f} as float32.
+// Step it = r / 8, key kk = r % 8, band group g = f / 8 and band b = f % 8 are arranged so
+// that the 64 lanes of a step read 64 consecutive 16-byte slots per instruction (one slot
+// holds bands 2m and 2m+1 of the lane's key).
+__device__ __forceinline__ int tab_slot(int r, int f) {
+  const int it = r >> 3, kk = r & 7, g = f >> 3, b = f & 7;
+  return ((it * 4 + (b >> 1)) * 64 + kk * 8 + g) * 2 + (b & 1);   // float2 index
 }
 
 template <int GE, bool BF16, bool IL, bool PAGED>
 __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScoreParams P) {
   constexpr int NW = kScoreWaves;
+  constexpr int NT = NW * 64;
   constexpr int STEPS = kChunk / 8;            // 8 keys per wave step
   constexpr int PF = GE <= 4 ? 4 : 2;          // steps of loads in flight
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int ROW = kHeadDim * ESZ;
   static_assert(STEPS % PF == 0 && STEPS % 8 == 0, "chunk geometry");
 
-  __shared__ float4 tab[kChunk * kBands / 2];  // e^{-i r theta_f}, r < kChunk, float32 pairs
+  __shared__ float4 tab[kChunk * kBands / 2];
   __shared__ float2 stepc[kBands];             // e^{-i kChunk theta_f}
-  __shared__ double2 anc[NW][kBands];          // per-wave anchors (float64)
+  __shared__ float2 anc[NW][kBands];           // per-wave anchors
 
   const int tid = threadIdx.x;
-  // ---- phase table: float64 recurrences from one sincos per run, rounded once ----------
+  // ---- phase table: float64 recurrence per (band, run of offsets), rounded once -------
   {
-    constexpr int RL = kChunk / NW;
+    constexpr int RL = kChunk * kBands / NT;   // offsets per thread
     const int f = tid & 63, run = tid >> 6;
     const double th = P.theta[f];
     double s1, c1, zr, zi;
     sincos(-th, &s1, &c1);
     sincos(-double(run * RL) * th, &zi, &zr);
     float2* t2 = reinterpret_cast<float2*>(tab);
-    const int g = f >> 3, r = (f & 7) >> 1, e = f & 1;
     for (int m = 0; m < RL; ++m) {
-      const int j = run * RL + m;
-      t2[((((j >> 3) * 4 + r) * 64) + ((j & 7) * 8 + g)) * 2 + e] = make_float2(float(zr), float(zi));
+      t2[tab_slot(run * RL + m, f)] = make_float2(float(zr), float(zi));
       const double nr = zr * c1 - zi * s1;
       zi = zr * s1 + zi * c1;
       zr = nr;
@@ -161,92 +149,119 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
   const int ups = P.n_layer * P.n_kvh;
   const int n_qh = P.n_kvh * P.group;
   const int S = P.chunks_per_span * kChunk;
+  // per-lane constant byte offsets of the lane's pieces inside a step's 8 rows
+  uint32_t off[BF16 ? 2 : 4];
+  if constexpr (BF16) {
+    off[0] = kk * ROW + (IL ? g * 32 : g * 16);
+    off[1] = kk * ROW + (IL ? g * 32 + 16 : 128 + g * 16);
+  } else {
+    off[0] = kk * ROW + (IL ? g * 64 : g * 32);
+    off[1] = off[0] + 16;
+    off[2] = kk * ROW + (IL ? g * 64 + 32 : 256 + g * 32);
+    off[3] = off[2] + 16;
+  }
 
-  for (int64_t item = int64_t(blockIdx.x) * NW + wave; item < P.n_items;
-       item += int64_t(gridDim.x) * NW) {
+  // Each wave takes a contiguous, equal share of the spans; consecutive spans of one unit
+  // form one segment, so the weights carry over (rotated chunk by chunk) and the loads
+  // stream without a break.
+  const int64_t n_waves = int64_t(gridDim.x) * NW;
+  const int64_t w_id = int64_t(blockIdx.x) * NW + wave;
+  const int64_t i_end = (w_id + 1) * P.n_items / n_waves;
+  int64_t item = w_id * P.n_items / n_waves;
+  while (item < i_end) {
     const int64_t unit = item / P.spans_per_unit;
-    const int span = int(item - unit * P.spans_per_unit);
+    const int64_t unit_end = min(i_end, (unit + 1) * P.spans_per_unit);
+    const int span0 = int(item - unit * P.spans_per_unit);
+    const int span1 = int(unit_end - unit * P.spans_per_unit);
+    item = unit_end;
     const int s = int(unit / ups);
     const int rem = int(unit - int64_t(s) * ups);
     const int l = rem / P.n_kvh;
     const int h = rem - l * P.n_kvh;
     const int L = min(max(P.seq_len[s], 0), int(P.score_stride));
-    const int p0 = span * S;
+    const int p0 = span0 * S;
     if (p0 >= L) continue;
-    const int64_t Q = P.query_pos ? P.query_pos[s] : int64_t(L) - 1;
-    const int nkeys = min(S, L - p0);
+    const int nkeys = min(span1 * S, L) - p0;
     const int n_steps = (nkeys + 7) >> 3;
+    const int64_t Q = P.query_pos ? P.query_pos[s] : int64_t(L) - 1;
 
-    {  // anchor of this span, one band per lane
-      const double ang = double(Q - p0) * P.theta[lane];
-      double sa, ca;
-      sincos(ang, &sa, &ca);
-      const double cr = P.c_re[lane], ci = P.c_im[lane];
-      anc[wave][lane] = make_double2(cr * ca - ci * sa, cr * sa + ci * ca);
-    }
-    __builtin_amdgcn_wave_barrier();
-
-    float wr[GE][8], wn[GE][8], nn[GE][8];
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const int f = g * 8 + b;
-      const double2 A = anc[wave][f];
-      if (P.reduce_mean) {
-        double sr = 0.0, si = 0.0, sn = 0.0;
-        for (int hh = 0; hh < P.group; ++hh) {
-          double r0, i0, n0;
-          head_weight(P, l, h * P.group + hh, n_qh, f, A.x, A.y, r0, i0, n0);
-          sr += r0;
-          si += i0;
-          sn += n0;
-        }
-        const double inv = 1.0 / double(P.group);
-        wr[0][b] = float(sr * inv);
-        wn[0][b] = float(-si * inv);
-        nn[0][b] = float(sn * inv);
-      } else {
-#pragma unroll
-        for (int hh = 0; hh < GE; ++hh) {
-          double r0, i0, n0;
-          head_weight(P, l, h * P.group + hh, n_qh, f, A.x, A.y, r0, i0, n0);
-          wr[hh][b] = float(r0);
-          wn[hh][b] = float(-i0);
-          nn[hh][b] = float(n0);
-        }
-      }
-    }
-
-    const char* kunit = static_cast<const char*>(P.k) + (PAGED ? 0 : unit * P.max_len * ROW);
+    // ---- key stream: raw buffer loads; reads past the segment return zero ------------
+    const char* kbase = static_cast<const char*>(P.k);
     const int32_t* bt = PAGED ? P.block_table + int64_t(s) * P.max_pages : nullptr;
     auto load_step = [&](int n, Frag<BF16>& fr) {
-      const int key0 = p0 + 8 * n;   // wave-uniform
-      if (n < n_steps && key0 + kk < p0 + nkeys) {
-        const char* row;
-        if constexpr (PAGED) {
-          const int64_t page = bt[key0 >> 4];
-          row = kunit + ((((page * P.n_layer + l) * P.n_kvh + h) * kPage) + (key0 & 15) + kk) * ROW;
-        } else {
-          row = kunit + int64_t(key0 + kk) * ROW;
-        }
-        load_frag<BF16, IL>(row, g, fr);
+      if (n >= n_steps) return;
+      const int key0 = p0 + 8 * n;
+      const char* base;
+      if constexpr (PAGED) {
+        const int64_t page = bt[key0 >> 4];
+        base = kbase + ((((page * P.n_layer + l) * P.n_kvh + h) * kPage) + (key0 & 15)) * ROW;
       } else {
-#pragma unroll
-        for (int i = 0; i < (BF16 ? 2 : 4); ++i) fr.d[i] = make_uint4(0, 0, 0, 0);
+        base = kbase + (unit * P.max_len + key0) * ROW;
       }
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, min(8, nkeys - 8 * n) * ROW, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < (BF16 ? 2 : 4); ++i)
+        fr.d[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], 0, 0));
     };
-
     Frag<BF16> ring[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) load_step(i, ring[i]);
 
+    {  // anchor of this segment (float64), one band per lane
+      const double ang = double(Q - p0) * P.theta[lane];
+      double sa, ca;
+      sincos(ang, &sa, &ca);
+      const double cr = P.c_re[lane], ci = P.c_im[lane];
+      anc[wave][lane] = make_float2(float(cr * ca - ci * sa), float(cr * sa + ci * ca));
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    float wr[GE][8], wn[GE][8], nn[GE][8];
+    const int64_t hrow0 = int64_t(l) * n_qh + int64_t(h) * P.group;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int f = g * 8 + b;
+      const float2 A = anc[wave][f];
+      if (P.reduce_mean) {
+        float sr = 0.0f, si = 0.0f, sn = 0.0f;
+        for (int hh = 0; hh < P.group; ++hh) {
+          float r0, i0, n0;
+          head_weight(P, hrow0 + hh, f, A.x, A.y, r0, i0, n0);
+          sr += r0;
+          si += i0;
+          sn += n0;
+        }
+        const float inv = 1.0f / float(P.group);
+        wr[0][b] = sr * inv;
+        wn[0][b] = -si * inv;
+        nn[0][b] = sn * inv;
+      } else {
+#pragma unroll
+        for (int hh = 0; hh < GE; ++hh) {
+          float r0, i0, n0;
+          head_weight(P, hrow0 + hh, f, A.x, A.y, r0, i0, n0);
+          wr[hh][b] = r0;
+          wn[hh][b] = -i0;
+          nn[hh][b] = n0;
+        }
+      }
+    }
+
     float* out = P.scores + unit * P.score_stride + p0;
+    const int lane_key = 8 * g + kk;   // key this lane stores within a group of 8 steps
     float keep = 0.0f;
     int n = 0;
     for (int c = 0; n < n_steps; ++c) {
+      // The table is read-only, so its per-step reads are invariant across chunks; an opaque
+      // base keeps them inside their step instead of being hoisted (and held in registers)
+      // for all steps of the chunk.
+      int tz = lane;
+      asm volatile("" : "+v"(tz));
       if (c > 0) {  // next chunk: W <- W e^{-i kChunk theta_f}
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
-          const float2 R = stepc[g * 8 + b];
+          const float2 R = stepc[(tz & 7) * 8 + b];
 #pragma unroll
           for (int hh = 0; hh < GE; ++hh) {
             const float a = wr[hh][b], q = wn[hh][b];
@@ -258,21 +273,20 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
 #pragma unroll
       for (int it = 0; it < STEPS; ++it) {
         if (n < n_steps) {
-          const Frag<BF16> cur = ring[it % PF];
-          load_step(n + PF, ring[it % PF]);
-          const float4* tp = tab + it * 4 * 64 + lane;
-          const float4 t4[4] = {tp[0], tp[64], tp[128], tp[192]};
+          Frag<BF16>& cur = ring[it % PF];
           float acc[GE];
 #pragma unroll
           for (int hh = 0; hh < GE; ++hh) acc[hh] = 0.0f;
+          const float4* tp = tab + it * 4 * 64 + tz;
+          const float4 t4[4] = {tp[0], tp[64], tp[128], tp[192]};
 #pragma unroll
           for (int b = 0; b < 8; ++b) {
             float a, q;
             band_of<BF16, IL>(cur, b, a, q);
             const float tc = (b & 1) ? t4[b >> 1].z : t4[b >> 1].x;
             const float ts = (b & 1) ? t4[b >> 1].w : t4[b >> 1].y;
-            const float xr = fmaf(tc, a, ts * q);     // Re(e^{-i r theta} conj(k))
-            const float xi = fmaf(ts, a, -(tc * q));  // Im(...)
+            const float xr = fmaf(tc, a, ts * q);      // Re(e^{-i r theta} conj(k))
+            const float xi = fmaf(ts, a, -(tc * q));   // Im(...)
             const float nk = __builtin_amdgcn_sqrtf(fmaf(a, a, q * q));
 #pragma unroll
             for (int hh = 0; hh < GE; ++hh) {
@@ -281,17 +295,20 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
               acc[hh] = fmaf(nn[hh][b], nk, acc[hh]);
             }
           }
+          // the slot is free again: fetch the step PF ahead into it
+          load_step(n + PF, cur);
           float sc = sum8(acc[0]);
 #pragma unroll
           for (int hh = 1; hh < GE; ++hh) sc = fmaxf(sc, sum8(acc[hh]));
           if ((it & 7) == g) keep = sc;
           if ((it & 7) == 7 || n == n_steps - 1) {
             // lane (kk, g) holds the score of step (n & ~7) + g, key kk
-            const int step = (n & ~7) + g;
-            const int key = 8 * step + kk;
-            if (step <= n && key < nkeys) out[key] = keep;
+            const int key = 8 * (n & ~7) + lane_key;
+            if (g <= (n & 7) && key < nkeys) out[key] = keep;
           }
           ++n;
+          // keep each step's table reads and arithmetic inside its own step
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }

@@ -14,9 +14,11 @@ constexpr int kMaxOffsets = 64;
 constexpr int64_t kMaxUnitLen = 1 << 20;
 
 // Score kernel geometry: 8 lanes per key (8 bands each), 8 keys per wave per step, phase
-// table of kChunk consecutive offsets in LDS, weights re-anchored every kChunk keys.
-constexpr int kChunk = 128;
-constexpr int kScoreWaves = 4;      // waves per workgroup
+// table of kChunk consecutive offsets in LDS, weights re-anchored every kChunk keys, a wave
+// work item of kSpanChunks chunks, one persistent workgroup of kScoreWaves waves per CU.
+constexpr int kChunk = 256;
+constexpr int kSpanChunks = 2;
+constexpr int kScoreWaves = 8;      // waves per workgroup
 
 struct ScoreParams {
   const void* k;
