@@ -25,9 +25,10 @@ namespace {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kTilesPerSeg = 64;   // groups per segment = kTilesPerSeg * waves = threads
 constexpr int kSample = 4096;
 constexpr int kBandCap = 8192;
+constexpr int kBatchTiles = 16;                        // tiles of keys held in registers
+constexpr int kBatch = kBatchTiles * kSelThreads;      // 16384 slots per batch
 
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t b = __float_as_uint(x);
@@ -107,7 +108,7 @@ struct SelShared {
   uint32_t pick[2];
   uint32_t band_n;
   uint32_t wsum_a[kSelWaves], wsum_b[kSelWaves];
-  uint32_t grp_a[kSelThreads], grp_b[kSelThreads];
+  uint32_t grp_a[kBatchTiles * kSelWaves], grp_b[kBatchTiles * kSelWaves];
   uint32_t band_u[kBandCap];      // sample keys, then band keys
   uint32_t band_slot[kBandCap];
 };
@@ -183,6 +184,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectParams 
   const int ncand = L - w;
   const int need = B - w;
 
+  // keys of one batch of slots, one per tile, kept in registers (loaded in one burst)
+  uint32_t u[kBatchTiles];
+  auto load_batch = [&](int b0) {
+#pragma unroll
+    for (int t = 0; t < kBatchTiles; ++t) {
+      const int slot = b0 + t * kSelThreads + tid;
+      u[t] = slot < ncand ? order_key(sc[slot]) : 0u;
+    }
+  };
+
   uint32_t tau = 0xFFFFFFFFu, need_eq = 0u;
   if (need > 0) {
     // ---- 1. bracket the target rank with two sample quantiles -------------------------
@@ -209,21 +220,24 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectParams 
     if (tid == 0) sh.band_n = 0u;
     __syncthreads();
     uint32_t my_above = 0u;
-    const int span = (ncand + kSelThreads - 1) / kSelThreads * kSelThreads;
-    for (int j = tid; j < span; j += kSelThreads) {
-      const bool in = j < ncand;
-      const uint32_t u = in ? order_key(sc[j]) : 0u;
-      my_above += (in && u > v_hi) ? 1u : 0u;
-      const bool band = in && u >= v_lo && u <= v_hi;
-      const uint64_t m = __ballot(band);
-      if (m) {
-        uint32_t base = 0u;
-        if (lane == 0) base = atomicAdd(&sh.band_n, uint32_t(__popcll(m)));
-        base = __shfl(base, 0);
-        const uint32_t at = base + lanes_below(m);
-        if (band && at < uint32_t(kBandCap)) {
-          sh.band_u[at] = u;
-          sh.band_slot[at] = uint32_t(j);
+    for (int b0 = 0; b0 < ncand; b0 += kBatch) {
+      load_batch(b0);
+#pragma unroll
+      for (int t = 0; t < kBatchTiles; ++t) {
+        const int j = b0 + t * kSelThreads + tid;
+        const bool in = j < ncand;
+        my_above += (in && u[t] > v_hi) ? 1u : 0u;
+        const bool band = in && u[t] >= v_lo && u[t] <= v_hi;
+        const uint64_t m = __ballot(band);
+        if (m) {
+          uint32_t base = 0u;
+          if (lane == 0) base = atomicAdd(&sh.band_n, uint32_t(__popcll(m)));
+          base = __shfl(base, 0);
+          const uint32_t at = base + lanes_below(m);
+          if (band && at < uint32_t(kBandCap)) {
+            sh.band_u[at] = u[t];
+            sh.band_slot[at] = uint32_t(j);
+          }
         }
       }
     }
@@ -244,56 +258,52 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectParams 
     }
   }
 
-  // ---- ordered write: slot order = (tile, wave, lane) ----------------------------------
+  // ---- ordered write: slot order = (tile, wave, lane) within each batch -----------------
   uint32_t carry_a = 0u, carry_b = 0u;
-  for (int seg = 0; seg < L; seg += kTilesPerSeg * kSelThreads) {
-    const int tiles = min(kTilesPerSeg, (L - seg + kSelThreads - 1) / kSelThreads);
-    for (int t = 0; t < kTilesPerSeg; ++t) {
-      bool a = false, b = false;
-      if (t < tiles) {
-        const int slot = seg + t * kSelThreads + tid;
-        if (slot < L) {
-          if (slot >= ncand) {
-            a = true;
-          } else if (need > 0) {
-            const uint32_t u = order_key(sc[slot]);
-            a = u > tau;
-            b = u == tau;
-          }
+  for (int b0 = 0; b0 < L; b0 += kBatch) {
+    load_batch(b0);
+    auto classify = [&](int t, bool& a, bool& b) {
+      const int slot = b0 + t * kSelThreads + tid;
+      a = false;
+      b = false;
+      if (slot < L) {
+        if (slot >= ncand) {
+          a = true;                       // recent window
+        } else if (need > 0) {
+          a = u[t] > tau;
+          b = u[t] == tau;
         }
       }
+    };
+#pragma unroll
+    for (int t = 0; t < kBatchTiles; ++t) {
+      bool a, b;
+      classify(t, a, b);
       const uint64_t ma = __ballot(a), mb = __ballot(b);
       if (lane == 0) {
         sh.grp_a[t * kSelWaves + wave] = uint32_t(__popcll(ma));
         sh.grp_b[t * kSelWaves + wave] = uint32_t(__popcll(mb));
       }
-      if (t >= tiles) break;
     }
     __syncthreads();
-    uint32_t ga = sh.grp_a[tid], gb = sh.grp_b[tid], ta, tb;
-    if (tid >= tiles * kSelWaves) ga = gb = 0u;
+    constexpr int kGroups = kBatchTiles * kSelWaves;
+    uint32_t ga = tid < kGroups ? sh.grp_a[tid] : 0u, gb = tid < kGroups ? sh.grp_b[tid] : 0u, ta, tb;
     block_scan2(ga, gb, ta, tb, sh.wsum_a, sh.wsum_b, lane, wave);
     __syncthreads();
-    sh.grp_a[tid] = ga + carry_a;
-    sh.grp_b[tid] = gb + carry_b;
+    if (tid < kGroups) {
+      sh.grp_a[tid] = ga + carry_a;
+      sh.grp_b[tid] = gb + carry_b;
+    }
     __syncthreads();
-    for (int t = 0; t < tiles; ++t) {
-      const int slot = seg + t * kSelThreads + tid;
-      bool a = false, b = false;
-      if (slot < L) {
-        if (slot >= ncand) {
-          a = true;
-        } else if (need > 0) {
-          const uint32_t u = order_key(sc[slot]);
-          a = u > tau;
-          b = u == tau;
-        }
-      }
+#pragma unroll
+    for (int t = 0; t < kBatchTiles; ++t) {
+      bool a, b;
+      classify(t, a, b);
       const uint64_t ma = __ballot(a), mb = __ballot(b);
       const uint32_t ra = sh.grp_a[t * kSelWaves + wave] + lanes_below(ma);
       const uint32_t rb = sh.grp_b[t * kSelWaves + wave] + lanes_below(mb);
       const uint32_t at = ra + min(rb, need_eq);
-      if ((a || (b && rb < need_eq)) && at < uint32_t(B)) out[at] = slot;
+      if ((a || (b && rb < need_eq)) && at < uint32_t(B)) out[at] = b0 + t * kSelThreads + tid;
     }
     carry_a += ta;
     carry_b += tb;
