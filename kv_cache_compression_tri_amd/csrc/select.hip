@@ -7,164 +7,108 @@
 // "TriAttention: trigonometric KV cache compression for long reasoning", section "The KV
 // budget is a runtime knob ...": the budget bounds the whole kept cache).
 //
-// Scores map to order-preserving 32-bit keys (NaN and -inf to the lowest key, -0 to +0).
-// The exact threshold key tau of the need-th best candidate is found in three steps:
-//   1. a strided sample of 4096 candidates is brought to LDS and two sample quantiles that
-//      bracket the target rank with a wide safety margin are found (radix select in LDS);
-//   2. one pass over the unit counts the candidates above the bracket and appends the
-//      ones inside it (typically ~3% of the unit) to LDS with ballot compaction;
-//   3. a radix select inside that band gives tau and how many keys equal to tau are taken.
-// If the bracket misses the target or the band overflows LDS (e.g. massive ties), the
-// kernel falls back to radix passes over the whole unit in global memory.  The ordered
-// write uses one ballot + mbcnt per wave per tile and a workgroup scan of the per-wave
-// counts, so the output is ascending without a sort; ties at tau go to the lowest slots.
+// Scores map to order-preserving 32-bit keys (NaN and -inf to the lowest candidate key, -0
+// to +0).  Each wave owns a contiguous range of slots, four consecutive slots per lane, and
+// keeps the keys of up to 4096 slots in registers, so a unit of up to 32768 slots is read
+// from memory once; longer units re-read their scores on every sweep.  The threshold is
+// found by refining linear histograms instead of sorting:
+//   level 1: 2048 bins spanning [min, max] of the candidate keys;
+//   level k+1: 2048 sub-bins of the bin that holds the target rank;
+// until either the whole target bin is kept (its lower edge becomes the threshold: keep
+// key >= T) or the bins are single key values (at most three levels, because the key span
+// has 32 bits and each level resolves 11).  In the second case only some of the keys equal
+// to the threshold are kept: the lowest slots among them, found with one more sweep.
+// The ordered write counts the kept slots per wave, turns the counts into offsets, and
+// writes each wave's kept slots in order from ballots (mbcnt ranks), without a sort.
 #include "tri_internal.h"
 
 namespace tri {
 namespace {
 
-constexpr int kSelThreads = 1024;
+constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kSample = 4096;
-constexpr int kBandCap = 8192;
-constexpr int kBatchTiles = 16;                        // tiles of keys held in registers
-constexpr int kBatch = kBatchTiles * kSelThreads;      // 16384 slots per batch
+constexpr int kVec = 4;                       // consecutive slots per lane in a tile
+constexpr int kTile = 64 * kVec;              // slots per wave tile
+constexpr int kBatchTiles = 16;               // tiles of keys a wave holds in registers
+constexpr int kBinBits = 11;
+constexpr int kBins = 1 << kBinBits;
+constexpr int kLevels = 3;                    // ceil(32 / kBinBits)
+constexpr uint32_t kKeyNone = 0u;             // slot outside the wave's range
+constexpr uint32_t kKeyWindow = 0xFFFFFFFFu;  // recent-window slot, always kept
 
-__device__ __forceinline__ uint32_t order_key(float x) {
-  uint32_t b = __float_as_uint(x);
-  if (x != x) return 0x007FFFFFu;              // NaN ranks as -inf
-  if (b == 0x80000000u) b = 0u;                // -0 == +0
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+// Candidate keys lie in [0x007FFFFF, 0xFF800000], strictly between the two sentinels.
+__device__ __forceinline__ uint32_t order_key(uint32_t b) {
+  const float x = __uint_as_float(b);
+  if (b == 0x80000000u) b = 0u;                              // -0 ranks as +0
+  const uint32_t k = b ^ (uint32_t(int32_t(b) >> 31) | 0x80000000u);
+  return x != x ? 0x007FFFFFu : k;                           // NaN ranks as -inf
 }
 
-__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+// acc + number of set bits of m in lanes below this one
+__device__ __forceinline__ uint32_t mbcnt(uint64_t m, uint32_t acc) {
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), acc));
 }
 
-// Add 1 to hist[bin] for every active lane, merging the two most common bins of the wave.
-__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool active, int lane) {
-#pragma unroll
-  for (int round = 0; round < 2; ++round) {
-    const uint64_t m = __ballot(active);
-    if (m == 0) return;
-    const int leader = __ffsll((unsigned long long)m) - 1;
-    const uint32_t b0 = __shfl(bin, leader);
-    const bool same = active && bin == b0;
-    const uint64_t sm = __ballot(same);
-    if (lane == leader) atomicAdd(&hist[b0], uint32_t(__popcll(sm)));
-    active = active && !same;
-  }
-  if (active) atomicAdd(&hist[bin], 1u);
-}
-
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t t = __shfl_up(v, d, 64);
-    if (lane >= d) v += t;
-  }
+// Inclusive prefix sum over the 64 lanes: row shifts inside 16-lane rows, then row
+// broadcasts of lane 15 and lane 31 into the rows above.
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x111, 0xF, 0xF, true));   // row_shr:1
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x112, 0xF, 0xF, true));   // row_shr:2
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x114, 0xF, 0xF, true));   // row_shr:4
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x118, 0xF, 0xF, true));   // row_shr:8
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x143, 0xC, 0xF, false));  // row_bcast:31
   return v;
 }
 
-__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* wsum, int lane, int wave) {
-  v = wave_incl_scan(v, lane);
-  if (lane == 63) wsum[wave] = v;
-  __syncthreads();
-  uint32_t t = 0;
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
 #pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) t += wsum[w];
-  __syncthreads();
-  return t;
+  for (int d = 32; d >= 1; d >>= 1) v = min(v, uint32_t(__shfl_xor(int(v), d, 64)));
+  return v;
 }
 
-// Exclusive scan of (a, b) across the workgroup; totals returned in ta, tb.
-__device__ __forceinline__ void block_scan2(uint32_t& a, uint32_t& b, uint32_t& ta, uint32_t& tb,
-                                            uint32_t* wa, uint32_t* wb, int lane, int wave) {
-  const uint32_t ia = wave_incl_scan(a, lane), ib = wave_incl_scan(b, lane);
-  if (lane == 63) {
-    wa[wave] = ia;
-    wb[wave] = ib;
-  }
-  __syncthreads();
-  uint32_t pa = 0, pb = 0;
-  ta = 0;
-  tb = 0;
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 #pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    const uint32_t x = wa[w], y = wb[w];
-    if (w < wave) {
-      pa += x;
-      pb += y;
-    }
-    ta += x;
-    tb += y;
-  }
-  a = pa + ia - a;
-  b = pb + ib - b;
+  for (int d = 32; d >= 1; d >>= 1) v = max(v, uint32_t(__shfl_xor(int(v), d, 64)));
+  return v;
 }
 
 struct SelShared {
-  uint32_t hist[256];
-  uint32_t pick[2];
-  uint32_t band_n;
-  uint32_t wsum_a[kSelWaves], wsum_b[kSelWaves];
-  uint32_t grp_a[kBatchTiles * kSelWaves], grp_b[kBatchTiles * kSelWaves];
-  uint32_t band_u[kBandCap];      // sample keys, then band keys
-  uint32_t band_slot[kBandCap];
+  alignas(16) uint32_t hist[kLevels][kBins];
+  uint32_t wmin[kSelWaves], wmax[kSelWaves];
+  uint32_t wties[kSelWaves], wkeep[kSelWaves];
+  int32_t jstar;
 };
 
-// After all radix levels: the rank-th largest value (1-based) and the count above it.
-// `fetch(i)` gives element i (i < n) and `in(i)` whether it takes part.
-template <typename Fetch>
-__device__ __forceinline__ void radix_select(Fetch fetch, int n, uint32_t rank, SelShared& sh,
-                                             int tid, int lane, int wave, uint32_t& tau,
-                                             uint32_t& above) {
-  uint32_t prefix = 0u, pmask = 0u, remaining = rank, gt = 0u;
-  const int span = (n + kSelThreads - 1) / kSelThreads * kSelThreads;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) sh.hist[tid] = 0u;
-    __syncthreads();
-    for (int i = tid; i < span; i += kSelThreads) {
-      bool act = i < n;
-      const uint32_t u = act ? fetch(i) : 0u;
-      act = act && (u & pmask) == prefix;
-      hist_add(sh.hist, (u >> shift) & 255u, act, lane);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // lane holds bins 4*lane .. 4*lane+3; count the values in higher bins
-      uint32_t hb[4];
+// The bin holding the rank-th largest (1-based) histogram entry, the number of entries in
+// higher bins and in the bin itself.  Every lane of the calling wave gets the same result.
+// Lane l first sums bins [kBins - 32(l+1), kBins - 32l), so lanes ascending walk the bins
+// descending; the 16-byte reads are rotated per lane to spread them over the LDS banks.
+__device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t rank, int lane, uint32_t& tbin,
+                                         uint32_t& above, uint32_t& cnt) {
+  const uint4* hv = reinterpret_cast<const uint4*>(hist + kBins - 32 * (lane + 1));
+  uint32_t lsum = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hb[i] = sh.hist[4 * lane + i];
-      const uint32_t lsum = hb[0] + hb[1] + hb[2] + hb[3];
-      const uint32_t rev = wave_incl_scan(__shfl(lsum, 63 - lane), lane);
-      const uint32_t incl = __shfl(rev, 63 - lane);   // sum over lanes >= lane
-      uint32_t abv = incl - lsum;                      // sum over lanes > lane
-      if (abv < remaining && remaining <= incl) {
-#pragma unroll
-        for (int i = 3; i >= 0; --i) {
-          if (abv + hb[i] >= remaining) {
-            sh.pick[0] = uint32_t(4 * lane + i);
-            sh.pick[1] = abv;
-            break;
-          }
-          abv += hb[i];
-        }
-      }
-    }
-    __syncthreads();
-    const uint32_t digit = sh.pick[0], a = sh.pick[1];
-    remaining -= a;
-    gt += a;
-    prefix |= digit << shift;
-    pmask |= 255u << shift;
-    __syncthreads();
+  for (int c = 0; c < 8; ++c) {
+    const uint4 q = hv[(c + lane) & 7];
+    lsum += (q.x + q.y) + (q.z + q.w);
   }
-  tau = prefix;
-  above = gt;
+  const uint32_t incl = wave_incl_sum(lsum);
+  const uint64_t hit = __ballot(incl >= rank);
+  const int fl = hit ? __ffsll((unsigned long long)hit) - 1 : 63;
+  const uint32_t abv = uint32_t(__builtin_amdgcn_readlane(int(incl - lsum), fl));
+  const int top = kBins - 1 - 32 * fl;
+  const uint32_t v = lane < 32 ? hist[top - lane] : 0u;
+  const uint32_t incl2 = abv + wave_incl_sum(v);
+  const uint64_t hit2 = __ballot(lane < 32 && incl2 >= rank);
+  const int k = hit2 ? __ffsll((unsigned long long)hit2) - 1 : 31;
+  cnt = uint32_t(__builtin_amdgcn_readlane(int(v), k));
+  above = uint32_t(__builtin_amdgcn_readlane(int(incl2), k)) - cnt;
+  tbin = uint32_t(top - k);
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectParams P) {
+template <bool kStream>
+__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(const SelectParams P) {
   __shared__ SelShared sh;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -181,140 +125,209 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectParams 
     return;
   }
   const int w = min(P.window, B);
-  const int ncand = L - w;
-  const int need = B - w;
+  const int ncand = L - w;                 // >= 1 because L > B >= w
+  const uint32_t need = uint32_t(B - w);   // candidates to keep
 
-  // keys of one batch of slots, one per tile, kept in registers (loaded in one burst)
-  uint32_t u[kBatchTiles];
-  auto load_batch = [&](int b0) {
+  // this wave's slots [r0, r1), in tiles of 64 lanes x 4 consecutive slots
+  const int per_wave = (L + kSelWaves * kTile - 1) / (kSelWaves * kTile) * kTile;
+  const int r0 = min(L, wave * per_wave), r1 = min(L, r0 + per_wave);
+  const int n_tiles = (r1 - r0 + kTile - 1) / kTile;
+  const int cand_end = min(r1, ncand);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sc), (short)0, L * 4, 0x00020000);
+
+  uint32_t u[kBatchTiles][kVec];
+  auto load = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < kBatchTiles; ++t) {
-      const int slot = b0 + t * kSelThreads + tid;
-      u[t] = slot < ncand ? order_key(sc[slot]) : 0u;
-    }
-  };
-
-  uint32_t tau = 0xFFFFFFFFu, need_eq = 0u;
-  if (need > 0) {
-    // ---- 1. bracket the target rank with two sample quantiles -------------------------
-    uint32_t v_lo = 0u, v_hi = 0xFFFFFFFFu;
-    if (ncand > kBandCap) {
-      for (int i = tid; i < kSample; i += kSelThreads) {
-        const int j = int((int64_t(i) * ncand) / kSample);
-        sh.band_u[i] = order_key(sc[j]);
+      if (t0 + t < n_tiles) {
+        const int j = r0 + (t0 + t) * kTile + lane * kVec;
+        const uint4 q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, j * 4, 0, 0));
+        u[t][0] = q.x;
+        u[t][1] = q.y;
+        u[t][2] = q.z;
+        u[t][3] = q.w;
       }
-      __syncthreads();
-      const double p = double(need) / double(ncand);
-      const double r = p * kSample;
-      const double sd = sqrt(r * (1.0 - p));
-      const int margin = int(4.0 * sd) + 16;
-      const int r_hi = int(r) - margin;        // ranks are 0-based, descending
-      const int r_lo = int(r) + margin;
-      auto fs = [&](int i) { return sh.band_u[i]; };
-      uint32_t ab;
-      if (r_hi >= 0) radix_select(fs, kSample, uint32_t(r_hi + 1), sh, tid, lane, wave, v_hi, ab);
-      if (r_lo < kSample) radix_select(fs, kSample, uint32_t(r_lo + 1), sh, tid, lane, wave, v_lo, ab);
-      __syncthreads();
     }
-    // ---- 2. count above the bracket, collect the band ----------------------------------
-    if (tid == 0) sh.band_n = 0u;
-    __syncthreads();
-    uint32_t my_above = 0u;
-    for (int b0 = 0; b0 < ncand; b0 += kBatch) {
-      load_batch(b0);
 #pragma unroll
-      for (int t = 0; t < kBatchTiles; ++t) {
-        const int j = b0 + t * kSelThreads + tid;
-        const bool in = j < ncand;
-        my_above += (in && u[t] > v_hi) ? 1u : 0u;
-        const bool band = in && u[t] >= v_lo && u[t] <= v_hi;
-        const uint64_t m = __ballot(band);
-        if (m) {
-          uint32_t base = 0u;
-          if (lane == 0) base = atomicAdd(&sh.band_n, uint32_t(__popcll(m)));
-          base = __shfl(base, 0);
-          const uint32_t at = base + lanes_below(m);
-          if (band && at < uint32_t(kBandCap)) {
-            sh.band_u[at] = u[t];
-            sh.band_slot[at] = uint32_t(j);
+    for (int t = 0; t < kBatchTiles; ++t) {
+      const int jt = r0 + (t0 + t) * kTile;
+      if (t0 + t < n_tiles) {
+        if (jt + kTile <= cand_end) {
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) u[t][e] = order_key(u[t][e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) {
+            const int j = jt + lane * kVec + e;
+            u[t][e] = j >= r1 ? kKeyNone : j >= ncand ? kKeyWindow : order_key(u[t][e]);
           }
         }
       }
     }
-    const uint32_t above = block_sum(my_above, sh.wsum_a, lane, wave);
-    const uint32_t band_n = sh.band_n;
-    if (above < uint32_t(need) && uint32_t(need) <= above + band_n && band_n <= uint32_t(kBandCap)) {
-      // ---- 3. exact select inside the band -------------------------------------------
-      uint32_t ab;
-      auto fb = [&](int i) { return sh.band_u[i]; };
-      radix_select(fb, int(band_n), uint32_t(need) - above, sh, tid, lane, wave, tau, ab);
-      need_eq = uint32_t(need) - above - ab;
+  };
+  // body(t, jt) runs for every tile of the wave with keys u[t][*] of slots jt + 4*lane + e;
+  // the scheduling barrier keeps the tiles in order so that ballots do not pile up in SGPRs
+  auto sweep = [&](auto&& body) __attribute__((always_inline)) {
+    if constexpr (kStream) {
+      for (int t0 = 0; t0 < n_tiles; t0 += kBatchTiles) {
+        load(t0);
+#pragma unroll
+        for (int t = 0; t < kBatchTiles; ++t) {
+          if (t0 + t < n_tiles) body(t, r0 + (t0 + t) * kTile);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     } else {
-      // ---- fallback: radix passes over the whole unit --------------------------------
-      uint32_t ab;
-      auto fg = [&](int i) { return order_key(sc[i]); };
-      radix_select(fg, ncand, uint32_t(need), sh, tid, lane, wave, tau, ab);
-      need_eq = uint32_t(need) - ab;
+#pragma unroll
+      for (int t = 0; t < kBatchTiles; ++t) {
+        if (t < n_tiles) body(t, r0 + t * kTile);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  if constexpr (!kStream) load(0);
+
+  // kept: key > tau, or key == tau and slot <= jstar (jstar = -1 when all ties at tau are
+  // kept, i.e. the threshold is key >= tau + 1)
+  uint32_t tau = kKeyWindow - 1u;
+  int jstar = -1;
+  bool partial = false;
+  if (need > 0) {
+    // ---- range of the candidate keys (sentinels wrap out of the min and the max) --------
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    sweep([&](int t, int) __attribute__((always_inline)) {
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) {
+        mn = min(mn, u[t][e] - 1u);
+        mx = max(mx, u[t][e] + 1u);
+      }
+    });
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (lane == 0) {
+      sh.wmin[wave] = mn;
+      sh.wmax[wave] = mx;
+    }
+    for (int i = tid; i < kLevels * kBins; i += kSelThreads) (&sh.hist[0][0])[i] = 0u;
+    __syncthreads();
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int i = 0; i < kSelWaves; ++i) {
+      lo = min(lo, sh.wmin[i]);
+      hi = max(hi, sh.wmax[i]);
+    }
+    lo += 1u;
+    hi -= 1u;
+
+    // ---- histogram refinement ------------------------------------------------------------
+    uint32_t base = lo, span = hi - lo, rank = need;   // in range: key - base <= span
+    const int bitlen = 32 - __clz(int(span));
+    int shift = bitlen > kBinBits ? bitlen - kBinBits : 0;
+    for (int lev = 0; lev < kLevels; ++lev) {
+      uint32_t* hist = sh.hist[lev];
+      sweep([&](int t, int) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+          const uint32_t d = u[t][e] - base;
+          if (d <= span) atomicAdd(&hist[d >> shift], 1u);
+        }
+      });
+      __syncthreads();
+      uint32_t tbin, above, cnt;
+      find_bin(hist, rank, lane, tbin, above, cnt);
+      rank -= above;
+      const uint32_t edge = base + (tbin << shift);
+      if (rank == cnt) {             // the whole bin is kept
+        tau = edge - 1u;
+        break;
+      }
+      if (shift == 0) {              // keys equal to edge: only the first `rank` are kept
+        tau = edge;
+        partial = true;
+        break;
+      }
+      base = edge;
+      span = (1u << shift) - 1u;
+      shift = shift > kBinBits ? shift - kBinBits : 0;
+    }
+
+    if (partial) {
+      // ---- slot of the rank-th key equal to tau, in slot order -------------------------
+      uint32_t ct = 0;
+      sweep([&](int t, int) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) ct += uint32_t(__popcll(__ballot(u[t][e] == tau)));
+      });
+      if (lane == 0) sh.wties[wave] = ct;
+      __syncthreads();
+      uint32_t run = 0;
+      for (int i = 0; i < wave; ++i) run += sh.wties[i];
+      if (run < rank && rank <= run + ct) {
+        sweep([&](int t, int jt) __attribute__((always_inline)) {
+          uint64_t m[kVec];
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) m[e] = __ballot(u[t][e] == tau);
+          uint32_t r = run;
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) r = mbcnt(m[e], r);
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) {
+            const bool f = u[t][e] == tau;
+            if (f && r == rank - 1u) sh.jstar = jt + lane * kVec + e;
+            r += f ? 1u : 0u;
+          }
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) run += uint32_t(__popcll(m[e]));
+        });
+      }
+      __syncthreads();
+      jstar = sh.jstar;
     }
   }
 
-  // ---- ordered write: slot order = (tile, wave, lane) within each batch -----------------
-  uint32_t carry_a = 0u, carry_b = 0u;
-  for (int b0 = 0; b0 < L; b0 += kBatch) {
-    load_batch(b0);
-    auto classify = [&](int t, bool& a, bool& b) {
-      const int slot = b0 + t * kSelThreads + tid;
-      a = false;
-      b = false;
-      if (slot < L) {
-        if (slot >= ncand) {
-          a = true;                       // recent window
-        } else if (need > 0) {
-          a = u[t] > tau;
-          b = u[t] == tau;
-        }
-      }
-    };
+  // ---- ordered write --------------------------------------------------------------------
+  auto keep = [&](uint32_t k, int j) __attribute__((always_inline)) {
+    return k > tau || (k == tau && j <= jstar);
+  };
+  uint32_t ck = 0;
+  sweep([&](int t, int jt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < kBatchTiles; ++t) {
-      bool a, b;
-      classify(t, a, b);
-      const uint64_t ma = __ballot(a), mb = __ballot(b);
-      if (lane == 0) {
-        sh.grp_a[t * kSelWaves + wave] = uint32_t(__popcll(ma));
-        sh.grp_b[t * kSelWaves + wave] = uint32_t(__popcll(mb));
-      }
-    }
-    __syncthreads();
-    constexpr int kGroups = kBatchTiles * kSelWaves;
-    uint32_t ga = tid < kGroups ? sh.grp_a[tid] : 0u, gb = tid < kGroups ? sh.grp_b[tid] : 0u, ta, tb;
-    block_scan2(ga, gb, ta, tb, sh.wsum_a, sh.wsum_b, lane, wave);
-    __syncthreads();
-    if (tid < kGroups) {
-      sh.grp_a[tid] = ga + carry_a;
-      sh.grp_b[tid] = gb + carry_b;
-    }
-    __syncthreads();
+    for (int e = 0; e < kVec; ++e) ck += uint32_t(__popcll(__ballot(keep(u[t][e], jt + lane * kVec + e))));
+  });
+  if (lane == 0) sh.wkeep[wave] = ck;
+  __syncthreads();
+  uint32_t run = 0;
+  for (int i = 0; i < wave; ++i) run += sh.wkeep[i];
+  sweep([&](int t, int jt) __attribute__((always_inline)) {
+    bool f[kVec];
+    uint64_t m[kVec];
 #pragma unroll
-    for (int t = 0; t < kBatchTiles; ++t) {
-      bool a, b;
-      classify(t, a, b);
-      const uint64_t ma = __ballot(a), mb = __ballot(b);
-      const uint32_t ra = sh.grp_a[t * kSelWaves + wave] + lanes_below(ma);
-      const uint32_t rb = sh.grp_b[t * kSelWaves + wave] + lanes_below(mb);
-      const uint32_t at = ra + min(rb, need_eq);
-      if ((a || (b && rb < need_eq)) && at < uint32_t(B)) out[at] = b0 + t * kSelThreads + tid;
+    for (int e = 0; e < kVec; ++e) {
+      f[e] = keep(u[t][e], jt + lane * kVec + e);
+      m[e] = __ballot(f[e]);
     }
-    carry_a += ta;
-    carry_b += tb;
-    __syncthreads();
-  }
+    uint32_t r = run;
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) r = mbcnt(m[e], r);
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+      if (f[e] && r < uint32_t(B)) out[r] = jt + lane * kVec + e;
+      r += f[e] ? 1u : 0u;
+    }
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) run += uint32_t(__popcll(m[e]));
+  });
 }
 
 }  // namespace
 
 hipError_t launch_select(const SelectParams& p, int64_t n_units, hipStream_t stream) {
-  hipLaunchKernelGGL(select_kernel, dim3(unsigned(n_units)), dim3(kSelThreads), 0, stream, p);
+  // units longer than the register-resident capacity re-read their scores on every sweep
+  if (p.score_stride <= int64_t(kSelWaves) * kBatchTiles * kTile)
+    hipLaunchKernelGGL(select_kernel<false>, dim3(unsigned(n_units)), dim3(kSelThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(select_kernel<true>, dim3(unsigned(n_units)), dim3(kSelThreads), 0, stream, p);
   return hipGetLastError();
 }
 

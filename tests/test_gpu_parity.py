@@ -265,6 +265,8 @@ def test_select_edge_cases():
         rng.standard_normal(1001).astype(np.float32),                 # B = L - 1
         np.full(2000, np.nan, np.float32),                            # all NaN
         (rng.standard_normal(4000) * 1e-30).astype(np.float32),       # tiny magnitudes
+        (rng.standard_normal(3000) * 1e-40).astype(np.float32),       # subnormals
+        np.exp(rng.standard_normal(3000) * 20).astype(np.float32),    # wide dynamic range
         np.float32([5.0]),                                            # L = 1
     ]
     log("select edge cases B=1000 W=100")
@@ -274,6 +276,20 @@ def test_select_edge_cases():
     _select_case(cases, 1000, 2000)
     _select_case(cases, 1, 0)
     _select_case(cases, 1, 1)
+
+
+def test_select_register_resident_boundary():
+    # units of up to 32768 slots keep their keys in registers; longer ones stream
+    rng = np.random.default_rng(7)
+    heavy = rng.integers(0, 100, 32768).astype(np.float32)        # ties at the threshold
+    normal = rng.standard_normal(32768).astype(np.float32)
+    ragged = rng.standard_normal(24577).astype(np.float32)
+    ragged[rng.choice(24577, 3000, replace=False)] = 0.5
+    log("select resident units (32768, 32768, 24577), B=2048 W=128")
+    _select_case([heavy, normal, ragged], 2048, 128)
+    log("select streamed units (32769, 40000), B=2048 W=128")
+    _select_case([rng.standard_normal(32769).astype(np.float32),
+                  rng.integers(-5, 5, 40000).astype(np.float32)], 2048, 128)
 
 
 def test_select_long_unit_multiple_segments():
