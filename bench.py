@@ -2,10 +2,14 @@
 """Throughput of the TriAttention KV-cache compression pass on one MI355X.
 
 One step = one pass of the whole hot path over the resident synthetic cache:
-tri_score_keys -> tri_select_topb -> tri_compact_kv (dense, out of place), for every
-(layer, KV head) of the 32K-context GQA workload (36 layers x 8 KV heads x 32768 keys,
-bf16, 4 query heads per KV head, B = 2048, window 128).  Inputs are generated on the
-device before timing; the timed region is bracketed by torch.cuda.synchronize().
+tri_score_keys -> tri_select_topb -> tri_compact_kv, for every (layer, KV head).  The
+default workload is the 32K-context GQA pass (36 layers x 8 KV heads x 32768 keys, bf16,
+4 query heads per KV head, B = 2048, window 128, dense out-of-place compaction);
+--workload picks another one (the paged workload compacts in place, so its pools are
+regenerated before every step, outside the timed region, and each step is timed on its
+own; the single-head float32 workload has no values and is scored and selected only).
+Inputs are generated on the device before timing; the timed region is bracketed by
+torch.cuda.synchronize().
 
 Prints one JSON line with the metric (keys scored+selected+compacted per second), the
 roofline of the dominant kernel (scoring: algorithmic bytes = 256 B per key read, over its
@@ -86,7 +90,8 @@ def _oracle_unit(job):
     sc = oracle.score_keys(keys, center, mean_abs, base=w.base, offsets=w.offsets, layout=w.layout,
                            reduce=w.reduce)
     kept = oracle.select_top_b(sc, L, w.budget, w.window)
-    oracle.compact_dense(keys_raw, vals, kept)
+    if w.with_values:
+        oracle.compact_dense(keys_raw, vals, kept)
     return time.perf_counter() - t0, L
 
 
@@ -177,10 +182,10 @@ def main():
     from kv_cache_compression_tri_amd.synth import workloads as W
 
     name = args.workload or W.BENCH_WORKLOAD
-    w = W.WORKLOADS[name]
-    if w.paged:
-        print("bench.py times the dense workloads (paged compaction is in place)", file=sys.stderr)
+    if name not in W.WORKLOADS:
+        print(f"unknown workload {name!r}; choose from {sorted(W.WORKLOADS)}", file=sys.stderr)
         return 2
+    w = W.WORKLOADS[name]
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
@@ -189,14 +194,23 @@ def main():
     kv = dw.kv()
     dev = dw.k.device
     units = w.n_units
-    keys_per_step = int(sum(int(x) for x in dw.hp.lengths)) * w.n_layer * w.n_kvh
-    scores = torch.empty((w.n_seq, w.n_layer, w.n_kvh, w.max_len), dtype=torch.float32, device=dev)
+    lengths = [int(x) for x in dw.hp.lengths]
+    keys_per_step = sum(lengths) * w.n_layer * w.n_kvh
+    slots = kv.slots
+    compacts = w.with_values          # the single-head f32 case is scoring + selection only
+    scores = torch.empty((w.n_seq, w.n_layer, w.n_kvh, slots), dtype=torch.float32, device=dev)
     kept = torch.empty((w.n_seq, w.n_layer, w.n_kvh, w.budget), dtype=torch.int32, device=dev)
     kept_n = torch.empty((w.n_seq,), dtype=torch.int32, device=dev)
-    k_out = torch.empty((w.n_seq, w.n_layer, w.n_kvh, w.budget, w.head_dim), dtype=dw.k.dtype, device=dev)
-    v_out = torch.empty_like(k_out) if dw.v is not None else None
     pos_out = torch.empty((w.n_seq, w.n_layer, w.n_kvh, w.budget), dtype=torch.int32, device=dev)
     new_len = torch.empty((w.n_seq,), dtype=torch.int32, device=dev)
+    if w.paged:                       # in place: freed page list instead of output tensors
+        k_out = v_out = None
+        freed = torch.empty((w.n_seq, w.max_pages), dtype=torch.int32, device=dev)
+        n_freed = torch.empty((w.n_seq,), dtype=torch.int32, device=dev)
+    else:
+        k_out = torch.empty((w.n_seq, w.n_layer, w.n_kvh, w.budget, w.head_dim), dtype=dw.k.dtype, device=dev)
+        v_out = torch.empty_like(k_out) if dw.v is not None else None
+        freed = n_freed = None
 
     def step(ev=None):
         if ev is not None:
@@ -208,30 +222,48 @@ def main():
         tri.tri_select_topb(scores, kv, w.budget, w.window, kept=kept, kept_n=kept_n)
         if ev is not None:
             ev[2].record()
-        tri.tri_compact_kv(kv, kept, kept_n, w.budget, k_out=k_out, v_out=v_out, pos_out=pos_out,
-                           new_len=new_len)
+        if compacts:
+            tri.tri_compact_kv(kv, kept, kept_n, w.budget, k_out=k_out, v_out=v_out, pos_out=pos_out,
+                               freed=freed, n_freed=n_freed, new_len=new_len)
         if ev is not None:
             ev[3].record()
 
+    def regenerate():
+        # in-place (paged) compaction rewrites the pools: restore them outside the timed region
+        if w.paged:
+            SD.fill(w, dw.hp, dw.k, dw.v, dw.seq_len, dw.block_table)
+
     for _ in range(args.warmup):
+        regenerate()
         step()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    if w.paged:
+        ms_total = 0.0
+        for i in range(args.steps):
+            regenerate()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            step(events[i])
+            torch.cuda.synchronize()
+            ms_total += (time.perf_counter() - t0) * 1e3
+        ms = ms_total / args.steps
+    else:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(events[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms = (t1 - t0) * 1e3 / args.steps
 
-    ms = (t1 - t0) * 1e3 / args.steps
     score_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
     select_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
     compact_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
     elt = 2 if w.dtype == "bf16" else 4
     score_bytes = keys_per_step * w.head_dim * elt                       # every key read once
-    kept_rows = units * min(w.budget, w.max_len)
-    compact_bytes = kept_rows * w.head_dim * elt * (2 if w.with_values else 1) * 2   # read + write
+    kept_rows = w.n_layer * w.n_kvh * sum(min(w.budget, L) for L in lengths)
+    compact_bytes = kept_rows * w.head_dim * elt * 2 * 2 if compacts else 0   # K and V, read + write
     pass_bytes = score_bytes + compact_bytes
     achieved = score_bytes / (score_ms * 1e-3) / 1e9
     value = keys_per_step / (ms * 1e-3) / 1e9
@@ -254,6 +286,7 @@ def main():
             "n_seq": w.n_seq, "n_layer": w.n_layer, "n_kv_heads": w.n_kvh, "group": w.group,
             "context": w.max_len, "head_dim": w.head_dim, "kv_dtype": w.dtype, "budget": w.budget,
             "window": w.window, "offsets": len(w.offsets), "reduce": w.reduce,
+            "layout": "paged" if w.paged else "dense", "compaction": compacts,
             "keys_per_step": keys_per_step, "parallelism": "single GPU",
         },
         "roofline": {
@@ -273,7 +306,7 @@ def main():
             "score_ms": score_ms, "select_ms": select_ms, "compact_ms": compact_ms,
         },
     }
-    del dw, kv, scores, kept, kept_n, k_out, v_out, pos_out, new_len
+    del dw, kv, scores, kept, kept_n, k_out, v_out, pos_out, new_len, freed, n_freed
     torch.cuda.empty_cache()
     _, copy_gbs = copy_bandwidth(1024)
     line["pass"]["copy_GBps"] = copy_gbs

@@ -61,6 +61,13 @@ def _dev(t, name, dtype=None):
     return t
 
 
+def _shape(t, name, shape):
+    """Require an exact shape: the kernels index these buffers with the descriptor's sizes."""
+    if t is not None and tuple(int(x) for x in t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -168,6 +175,8 @@ def tri_calibrate_stats(q, rope_layout: str = "half", center=None, mean_abs=None
         mean_abs = torch.empty((n_layer, n_qh, d // 2), dtype=torch.float32, device=q.device)
     _dev(center, "center", torch.float32)
     _dev(mean_abs, "mean_abs", torch.float32)
+    _shape(center, "center", (n_layer, n_qh, d // 2, 2))
+    _shape(mean_abs, "mean_abs", (n_layer, n_qh, d // 2))
     _abi.check(L.tri_calibrate_stats(_ptr(q), _dtype_code(q), n, n_layer, n_qh, d, _LAYOUTS[rope_layout],
                                      _ptr(center), _ptr(mean_abs), None, None, _stream(stream)))
     return center, mean_abs
@@ -199,6 +208,11 @@ def tri_score_keys(kv: KVCache, center, mean_abs, *, rope_base: float, offsets: 
         scores = torch.empty((kv.n_seq, desc.n_layer, desc.n_kvh, kv.slots), dtype=torch.float32,
                              device=kv.k.device)
     _dev(scores, "scores", torch.float32)
+    n_qh = desc.n_kvh * int(group)
+    _shape(center, "center", (desc.n_layer, n_qh, desc.head_dim // 2, 2))
+    _shape(mean_abs, "mean_abs", (desc.n_layer, n_qh, desc.head_dim // 2))
+    _shape(query_pos, "query_pos", (kv.n_seq,))
+    _shape(scores, "scores", (kv.n_seq, desc.n_layer, desc.n_kvh, kv.slots))
     cfg, _keep = _score_cfg(rope_base, offsets, group, reduce, rope_layout)
     _abi.check(L.tri_score_keys(ctypes.byref(cfg), _ptr(center), _ptr(mean_abs), ctypes.byref(desc),
                                 _ptr(query_pos), _ptr(scores), None, None, _stream(stream)))
@@ -217,6 +231,9 @@ def tri_select_topb(scores, kv: KVCache, budget: int, window: int, kept=None, ke
         kept_n = torch.empty((kv.n_seq,), dtype=torch.int32, device=scores.device)
     _dev(kept, "kept", torch.int32)
     _dev(kept_n, "kept_n", torch.int32)
+    _shape(scores, "scores", (kv.n_seq, desc.n_layer, desc.n_kvh, kv.slots))
+    _shape(kept, "kept", (kv.n_seq, desc.n_layer, desc.n_kvh, int(budget)))
+    _shape(kept_n, "kept_n", (kv.n_seq,))
     _abi.check(L.tri_select_topb(_ptr(scores), ctypes.byref(desc), int(budget), int(window), _ptr(kept),
                                  _ptr(kept_n), None, None, _stream(stream)))
     return kept, kept_n
@@ -254,6 +271,15 @@ def tri_compact_kv(kv: KVCache, kept, kept_n, budget: int, k_out=None, v_out=Non
         _dev(t, name, kv.k.dtype)
     for t, name in ((pos_out, "pos_out"), (freed, "freed"), (n_freed, "n_freed"), (new_len, "new_len")):
         _dev(t, name, torch.int32)
+    _shape(kept, "kept", shape_u + (int(budget),))
+    _shape(kept_n, "kept_n", (kv.n_seq,))
+    _shape(k_out, "k_out", shape_u + (int(budget), desc.head_dim))
+    _shape(v_out, "v_out", shape_u + (int(budget), desc.head_dim))
+    _shape(pos_out, "pos_out", shape_u + (int(budget),))
+    if kv.layout == "paged":
+        _shape(freed, "freed", (kv.n_seq, desc.max_pages))
+    _shape(n_freed, "n_freed", (kv.n_seq,))
+    _shape(new_len, "new_len", (kv.n_seq,))
     _abi.check(L.tri_compact_kv(ctypes.byref(desc), _ptr(kept), _ptr(kept_n), int(budget), _ptr(k_out),
                                 _ptr(v_out), _ptr(pos_out), _ptr(freed), _ptr(n_freed), _ptr(new_len),
                                 _stream(stream)))

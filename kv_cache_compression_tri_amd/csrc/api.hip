@@ -176,14 +176,15 @@ int tri_score_keys(const tri_score_cfg* cfg, const float* center, const float* m
     p.group = cfg->group;
     p.max_pages = kv->max_pages;
     p.reduce_mean = cfg->reduce == TRI_REDUCE_MEAN;
-    p.chunks_per_span = tri::kSpanChunks;
-    const int64_t span = int64_t(p.chunks_per_span) * tri::kChunk;
-    p.spans_per_unit = int32_t((slots + span - 1) / span);
-    p.n_items = units * p.spans_per_unit;
-    // persistent grid: one workgroup per CU builds the 128 KB phase table once
-    int64_t grid = (p.n_items + tri::kScoreWaves - 1) / tri::kScoreWaves;
+    p.n_seq = kv->n_seq;
+    // persistent grid: one workgroup per CU builds the 128 KB phase table once; fewer
+    // workgroups when there are not kMinWaveSteps steps per wave even at full length
+    const int64_t max_steps = units * ((slots + 7) / 8);
+    const int64_t waves = (max_steps + tri::kMinWaveSteps - 1) / tri::kMinWaveSteps;
+    int64_t grid = (waves + tri::kScoreWaves - 1) / tri::kScoreWaves;
     const int64_t resident = int64_t(cu_count());
     if (grid > resident) grid = resident;
+    if (grid < 1) grid = 1;
     const int g_eff = p.reduce_mean ? 1 : cfg->group;
     (void)hipGetLastError();
     hipError_t e = tri::launch_score(p, g_eff, kv->dtype == TRI_BF16,

@@ -29,11 +29,12 @@
 // Mapping: 8 lanes per key; lane g of a key owns bands 8g..8g+7, so the 8 lanes of a key
 // read its row as coalesced 16-byte pieces and a wave scores 8 keys per step.  Per-lane
 // partial sums are combined with three DPP steps inside each 8-lane group.  Each wave owns
-// one span of one unit at a time; the weights live in registers.  Key rows are addressed
-// from a wave-uniform (scalar) base plus a per-lane constant offset.  Scores of 8 steps are
-// gathered into one lane each and written as one coalesced 256-byte store.  The grid is
-// persistent (one workgroup of kScoreWaves waves per CU), so the 128 KB phase table is
-// built once per CU.
+// an equal, contiguous share of all 8-key steps of all units and walks it unit by unit; the
+// weights of the current unit live in registers.  Key rows are fetched with raw buffer
+// loads from a wave-uniform base plus a per-lane constant offset, a few steps ahead, into a
+// ring of registers.  Scores of 8 steps are gathered into one lane each and written as one
+// coalesced 256-byte store.  The grid is persistent (one workgroup of kScoreWaves waves per
+// CU), so the 128 KB phase table is built once per CU.
 #include "tri_internal.h"
 
 namespace tri {
@@ -72,6 +73,13 @@ __device__ __forceinline__ void band_of(const Frag<BF16>& fr, int b, float& re, 
       im = __uint_as_float(word(fr.d[2 + (b >> 2)], b & 3));
     }
   }
+}
+
+// A wave-uniform 64-bit value held in scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v)));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v) >> 32));
+  return int64_t((uint64_t(hi) << 32) | lo);
 }
 
 // Sum over the 8 lanes of a key (lanes 8k..8k+7): two quad swaps and a half-row mirror.
@@ -148,7 +156,6 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
   const int g = lane & 7;     // band group
   const int ups = P.n_layer * P.n_kvh;
   const int n_qh = P.n_kvh * P.group;
-  const int S = P.chunks_per_span * kChunk;
   // per-lane constant byte offsets of the lane's pieces inside a step's 8 rows
   uint32_t off[BF16 ? 2 : 4];
   if constexpr (BF16) {
@@ -161,28 +168,70 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
     off[3] = off[2] + 16;
   }
 
-  // Each wave takes a contiguous, equal share of the spans; consecutive spans of one unit
-  // form one segment, so the weights carry over (rotated chunk by chunk) and the loads
-  // stream without a break.
+  // Work division: the units' keys, in (sequence, layer, head) order and in 8-key steps
+  // (a unit of L keys has ceil(L / 8) steps), are split into one contiguous, equal share
+  // per wave, so ragged lengths do not unbalance the grid.  Consecutive steps of one unit
+  // form a segment: the weights carry over (rotated chunk by chunk) and the loads stream
+  // without a break.  seq_len lives on the device, so each wave sums it itself.
+  auto unit_steps = [&](int sq) -> int64_t {
+    return (int64_t(min(max(P.seq_len[sq], 0), int(P.score_stride))) + 7) >> 3;
+  };
+  int64_t total = 0;
+  for (int s0 = 0; s0 < P.n_seq; s0 += 64) {
+    int64_t c = s0 + lane < P.n_seq ? unit_steps(s0 + lane) : 0;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
+    total += uniform64(c);
+  }
+  total *= ups;
   const int64_t n_waves = int64_t(gridDim.x) * NW;
   const int64_t w_id = int64_t(blockIdx.x) * NW + wave;
-  const int64_t i_end = (w_id + 1) * P.n_items / n_waves;
-  int64_t item = w_id * P.n_items / n_waves;
-  while (item < i_end) {
-    const int64_t unit = item / P.spans_per_unit;
-    const int64_t unit_end = min(i_end, (unit + 1) * P.spans_per_unit);
-    const int span0 = int(item - unit * P.spans_per_unit);
-    const int span1 = int(unit_end - unit * P.spans_per_unit);
-    item = unit_end;
-    const int s = int(unit / ups);
-    const int rem = int(unit - int64_t(s) * ups);
-    const int l = rem / P.n_kvh;
-    const int h = rem - l * P.n_kvh;
+  const int64_t share = total / n_waves, extra = total % n_waves;
+  const int64_t g0 = w_id * share + min(w_id, extra);
+  const int64_t g1 = g0 + share + (w_id < extra ? 1 : 0);
+  // sequence holding step g0, and the global index of that sequence's first step
+  int s = 0;
+  int64_t seq_base = 0;
+  if (g0 < g1) {
+    for (int s0 = 0; s0 < P.n_seq; s0 += 64) {
+      const int64_t c = s0 + lane < P.n_seq ? unit_steps(s0 + lane) * ups : 0;
+      int64_t incl = c;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int64_t t = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += t;
+      }
+      const uint64_t hit = __ballot(seq_base + incl > g0);
+      if (hit) {
+        const int ln = __ffsll((unsigned long long)hit) - 1;
+        s = s0 + ln;
+        seq_base += uniform64(__shfl(incl - c, ln, 64));
+        break;
+      }
+      seq_base += uniform64(__shfl(incl, 63, 64));
+    }
+  }
+  int64_t gs = g0;
+  while (gs < g1 && s < P.n_seq) {
+    const int64_t spu = unit_steps(s);
+    const int64_t rel = gs - seq_base;
+    if (rel >= spu * ups) {            // past the end of sequence s (or s is empty)
+      seq_base += spu * ups;
+      ++s;
+      continue;
+    }
+    const int u_in = int(rel / spu);
+    const int st0 = int(rel - int64_t(u_in) * spu);
+    const int64_t seg_end = min(g1, seq_base + (int64_t(u_in) + 1) * spu);
+    const int seg_steps = int(seg_end - gs);
+    gs = seg_end;
+    const int64_t unit = int64_t(s) * ups + u_in;
+    const int l = u_in / P.n_kvh;
+    const int h = u_in - l * P.n_kvh;
     const int L = min(max(P.seq_len[s], 0), int(P.score_stride));
-    const int p0 = span0 * S;
-    if (p0 >= L) continue;
-    const int nkeys = min(span1 * S, L) - p0;
-    const int n_steps = (nkeys + 7) >> 3;
+    const int p0 = 8 * st0;
+    const int nkeys = min(L - p0, 8 * seg_steps);
+    const int n_steps = seg_steps;
     const int64_t Q = P.query_pos ? P.query_pos[s] : int64_t(L) - 1;
 
     // ---- key stream: raw buffer loads; reads past the segment return zero ------------

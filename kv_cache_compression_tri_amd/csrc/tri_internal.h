@@ -14,11 +14,12 @@ constexpr int kMaxOffsets = 64;
 constexpr int64_t kMaxUnitLen = 1 << 20;
 
 // Score kernel geometry: 8 lanes per key (8 bands each), 8 keys per wave per step, phase
-// table of kChunk consecutive offsets in LDS, weights re-anchored every kChunk keys, a wave
-// work item of kSpanChunks chunks, one persistent workgroup of kScoreWaves waves per CU.
+// table of kChunk consecutive offsets in LDS, weights re-anchored every kChunk keys, one
+// persistent workgroup of kScoreWaves waves per CU, at least kMinWaveSteps 8-key steps per
+// wave (so that the per-segment set-up stays small next to the streaming).
 constexpr int kChunk = 256;
-constexpr int kSpanChunks = 2;
 constexpr int kScoreWaves = 8;      // waves per workgroup
+constexpr int kMinWaveSteps = 32;
 
 struct ScoreParams {
   const void* k;
@@ -30,10 +31,7 @@ struct ScoreParams {
   float* scores;
   int64_t max_len;           // dense token stride
   int64_t score_stride;      // slots per unit in `scores`
-  int64_t n_items;           // units * spans_per_unit
-  int32_t n_layer, n_kvh, group, max_pages;
-  int32_t spans_per_unit;
-  int32_t chunks_per_span;
+  int32_t n_seq, n_layer, n_kvh, group, max_pages;
   int32_t reduce_mean;
   double theta[kBands];      // theta_f, float64
   double c_re[kBands];       // C_f = mean over offsets of exp(i Delta theta_f), float64

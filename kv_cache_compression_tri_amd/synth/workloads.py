@@ -161,8 +161,8 @@ def make_params(w: Workload, lengths=None) -> HostParams:
     if lengths is None:
         lengths = np.full(w.n_seq, w.max_len, dtype=np.int32)
     lengths = np.asarray(lengths, dtype=np.int32)
-    if lengths.shape != (w.n_seq,) or lengths.min() < 1 or lengths.max() > w.max_len:
-        raise ValueError("lengths must be n_seq values in [1, max_len]")
+    if lengths.shape != (w.n_seq,) or lengths.min() < 0 or lengths.max() > w.max_len:
+        raise ValueError("lengths must be n_seq values in [0, max_len]")
     return HostParams(mu_k, center, mean_abs, low, sigma, lengths)
 
 

@@ -142,6 +142,9 @@ SMALL_DENSE = {
                                    window=1, low_r_frac=0.5), [2049]),
     "g6_max_half_bf16_short": (dict(n_seq=3, n_layer=1, n_kvh=1, group=6, max_len=900, budget=64,
                                     window=16), [900, 1, 65]),
+    # empty sequences between non-empty ones: the score grid divides only real keys
+    "g4_max_half_bf16_empty_seqs": (dict(n_seq=5, n_layer=2, n_kvh=2, group=4, max_len=2600, budget=300,
+                                         window=32), [0, 2600, 0, 0, 1031]),
 }
 
 
@@ -458,3 +461,32 @@ def test_full_paged_ragged64_bf16():
     total_before = int(sum(-(-int(L) // 16) for L in hp.lengths))
     total_after = int(sum(-(-min(int(L), w.budget) // 16) for L in hp.lengths))
     assert int(nf.sum()) == total_before - total_after
+
+
+# ---------------------------------------------------------------------------------------
+# binding: buffers whose shape does not match the descriptor are rejected before launch
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.gpu
+def test_binding_rejects_mismatched_shapes():
+    import torch
+    lengths = torch.tensor([100, 80], dtype=torch.int32, device="cuda")
+    k = torch.zeros((2, 3, 2, 128, 128), dtype=torch.bfloat16, device="cuda")
+    kv = tri.KVCache.dense(k, k.clone(), lengths)
+    center = torch.zeros((3, 4, 64, 2), dtype=torch.float32, device="cuda")
+    mean_abs = torch.zeros((3, 4, 64), dtype=torch.float32, device="cuda")
+    kw = dict(rope_base=1e4, offsets=(1, 2), group=2)
+    bad = [
+        lambda: tri.tri_score_keys(kv, center[:2], mean_abs, **kw),
+        lambda: tri.tri_score_keys(kv, center, mean_abs, scores=torch.empty((2, 3, 2, 100), device="cuda"), **kw),
+        lambda: tri.tri_select_topb(torch.empty((2, 3, 2, 64), device="cuda"), kv, 16, 4),
+        lambda: tri.tri_select_topb(torch.empty((2, 3, 2, 128), device="cuda"), kv, 16, 4,
+                                    kept=torch.empty((2, 3, 2, 8), dtype=torch.int32, device="cuda")),
+        lambda: tri.tri_compact_kv(kv, torch.zeros((2, 3, 2, 16), dtype=torch.int32, device="cuda"),
+                                   torch.zeros((2,), dtype=torch.int32, device="cuda"), 16,
+                                   k_out=torch.empty((2, 3, 2, 8, 128), dtype=torch.bfloat16, device="cuda")),
+    ]
+    for i, fn in enumerate(bad):
+        with pytest.raises(ValueError):
+            fn()
+    torch.cuda.synchronize()
