@@ -8,9 +8,9 @@
 // budget is a runtime knob ...": the budget bounds the whole kept cache).
 //
 // Scores map to order-preserving 32-bit keys (NaN and -inf to the lowest candidate key, -0
-// to +0).  Each wave owns a contiguous range of slots, four consecutive slots per lane, and
-// keeps the keys of up to 4096 slots in registers, so a unit of up to 32768 slots is read
-// from memory once; longer units re-read their scores on every sweep.  The threshold is
+// to +0).  Each wave of a 1024-thread workgroup owns a contiguous range of slots, four
+// consecutive slots per lane; a unit of up to 32768 slots is read from memory once into
+// registers (2048 slots per wave), longer units re-read their scores on every sweep.  The threshold is
 // found by refining linear histograms instead of sorting:
 //   level 1: 2048 bins spanning [min, max] of the candidate keys;
 //   level k+1: 2048 sub-bins of the bin that holds the target rank;
@@ -25,11 +25,14 @@
 namespace tri {
 namespace {
 
-constexpr int kSelThreads = 512;
-constexpr int kSelWaves = kSelThreads / 64;
+// Workgroup sizes: a unit that fits in registers (up to kResident slots) uses kResThreads
+// threads holding kResident / kResThreads keys each; longer units stream their scores
+// with kStreamThreads threads.
+constexpr int kResThreads = 1024;
+constexpr int kStreamThreads = 1024;
 constexpr int kVec = 4;                       // consecutive slots per lane in a tile
 constexpr int kTile = 64 * kVec;              // slots per wave tile
-constexpr int kBatchTiles = 16;               // tiles of keys a wave holds in registers
+constexpr int kResident = 32768;              // slots a workgroup holds in registers
 constexpr int kBinBits = 11;
 constexpr int kBins = 1 << kBinBits;
 constexpr int kLevels = 3;                    // ceil(32 / kBinBits)
@@ -73,10 +76,11 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
   return v;
 }
 
+template <int NW>
 struct SelShared {
   alignas(16) uint32_t hist[kLevels][kBins];
-  uint32_t wmin[kSelWaves], wmax[kSelWaves];
-  uint32_t wties[kSelWaves], wkeep[kSelWaves];
+  uint32_t wmin[NW], wmax[NW];
+  uint32_t wties[NW], wkeep[NW];
   int32_t jstar;
 };
 
@@ -107,9 +111,12 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t rank, in
   tbin = uint32_t(top - k);
 }
 
-template <bool kStream>
-__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(const SelectParams P) {
-  __shared__ SelShared sh;
+template <bool kStream, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(const SelectParams P) {
+  constexpr int kSelThreads = NT;
+  constexpr int kSelWaves = NT / 64;
+  constexpr int kBatchTiles = kResident / (NT * kVec);   // tiles of keys a wave holds in registers
+  __shared__ SelShared<kSelWaves> sh;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t unit = blockIdx.x;
@@ -324,10 +331,11 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(4))
 
 hipError_t launch_select(const SelectParams& p, int64_t n_units, hipStream_t stream) {
   // units longer than the register-resident capacity re-read their scores on every sweep
-  if (p.score_stride <= int64_t(kSelWaves) * kBatchTiles * kTile)
-    hipLaunchKernelGGL(select_kernel<false>, dim3(unsigned(n_units)), dim3(kSelThreads), 0, stream, p);
+  if (p.score_stride <= kResident)
+    hipLaunchKernelGGL((select_kernel<false, kResThreads>), dim3(unsigned(n_units)), dim3(kResThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(select_kernel<true>, dim3(unsigned(n_units)), dim3(kSelThreads), 0, stream, p);
+    hipLaunchKernelGGL((select_kernel<true, kStreamThreads>), dim3(unsigned(n_units)), dim3(kStreamThreads), 0,
+                       stream, p);
   return hipGetLastError();
 }
 
