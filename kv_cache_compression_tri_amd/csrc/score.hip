@@ -40,6 +40,11 @@
 namespace tri {
 namespace {
 
+// Block-table entries are read through the constant address space: the table is read-only
+// during the kernel and its addresses are wave-uniform, so these become scalar loads (they
+// do not pass through the vector memory counter that tracks the key stream).
+typedef __attribute__((address_space(4))) const int32_t* const_i32_ptr;
+
 template <bool BF16>
 struct Frag {
   uint4 d[BF16 ? 2 : 4];
@@ -236,13 +241,17 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
 
     // ---- key stream: raw buffer loads; reads past the segment return zero ------------
     const char* kbase = static_cast<const char*>(P.k);
-    const int32_t* bt = PAGED ? P.block_table + int64_t(s) * P.max_pages : nullptr;
+    const_i32_ptr bt = PAGED ? (const_i32_ptr)(P.block_table + int64_t(s) * P.max_pages) : nullptr;
+    // paged: page of step n, read one step before the step's load is issued
+    auto page_of = [&](int n) -> int32_t { return bt[(p0 + 8 * min(n, n_steps - 1)) >> 4]; };
+    int32_t pg_next = PAGED ? page_of(0) : 0;   // widened only where it is used
     auto load_step = [&](int n, Frag<BF16>& fr) {
       if (n >= n_steps) return;
       const int key0 = p0 + 8 * n;
       const char* base;
       if constexpr (PAGED) {
-        const int64_t page = bt[key0 >> 4];
+        const int64_t page = pg_next;
+        pg_next = page_of(n + 1);
         base = kbase + ((((page * P.n_layer + l) * P.n_kvh + h) * kPage) + (key0 & 15)) * ROW;
       } else {
         base = kbase + (unit * P.max_len + key0) * ROW;
