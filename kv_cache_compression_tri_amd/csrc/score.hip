@@ -19,7 +19,7 @@
 //     s_hq(j) = sum_f Re( W_f x_f ) + N_f |k_f|,   x_f = e^{-i r theta_f} conj(k_f),
 //     W_f = c_f C_f e^{i (Q - p_a) theta_f},  C_f = mean_Delta e^{i Delta theta_f},
 //     N_f = m_f - |c_f|  (= (1 - R_f) m_f).
-// The anchor phase is formed in float64 per span; e^{-i r theta_f} (r < kChunk) comes from
+// The anchor phase is formed in float64 per segment; e^{-i r theta_f} (r < kChunk) comes from
 // an LDS table built in float64 and rounded once to float32.  Large phases never go through
 // a float32 sin/cos.  At each chunk boundary the weights rotate by e^{-i kChunk theta_f}.
 // For the mean reduction W and N are averaged over the group first (both terms are linear
