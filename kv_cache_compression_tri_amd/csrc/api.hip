@@ -4,6 +4,7 @@
 #include "tri.h"
 #include "tri_internal.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -27,15 +28,19 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(TRI_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Compute units of the current device (cached per device id).
+// Compute units of the current device (cached per device id; calls may come from several
+// host threads at once).
 int cu_count() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-  if (dev < 64) cache[dev] = n;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
