@@ -490,3 +490,59 @@ def test_binding_rejects_mismatched_shapes():
         with pytest.raises(ValueError):
             fn()
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------------------
+# adversarial keys through the whole pass: exact score ties (zero keys score exactly 0 at any
+# position), near-ties (one row repeated at many positions) and a NaN row
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.gpu
+def test_zero_duplicated_and_nan_key_rows():
+    w = W.scaled(BASE, name="adversarial", n_seq=1, n_layer=1, n_kvh=2, group=4, max_len=1500,
+                 budget=300, window=16)
+    hp = W.make_params(w)
+    L = w.max_len
+    raw = np.stack([P.host_rows(w, hp, 0, 0, h, as_float=False) for h in range(w.n_kvh)])  # [2, L, 128] bf16 bits
+    rng = np.random.default_rng(11)
+    live = np.zeros(L, bool)
+    live[rng.choice(L, 150, replace=False)] = True
+    raw[0, ~live] = 0                          # head 0: mostly zero keys, so the threshold sits in a tie at 0
+    raw[0, 300] = 0x7FC0                       # and a NaN key row (scores as -inf)
+    raw[1, 100:200] = raw[1, 50:51]            # head 1: one row repeated at 100 positions
+    raw[1, 700:1000:3] = raw[1, 699:700]
+    log("adversarial rows: zero keys (exact ties at the threshold), repeated rows, a NaN row; B=300 W=16")
+    k = torch.from_numpy(raw.view(np.int16).reshape(1, 1, 2, L, 128).copy()).cuda().view(torch.bfloat16)
+    v = torch.from_numpy(raw[::-1].copy().view(np.int16).reshape(1, 1, 2, L, 128)).cuda().view(torch.bfloat16)
+    lengths = torch.tensor([L], dtype=torch.int32, device="cuda")
+    kv = tri.KVCache.dense(k, v, lengths)
+    center = torch.from_numpy(hp.center).cuda()
+    mean_abs = torch.from_numpy(hp.mean_abs).cuda()
+    sc = tri.tri_score_keys(kv, center, mean_abs, rope_base=w.base, offsets=w.offsets, group=w.group)
+    kept, kept_n = tri.tri_select_topb(sc, kv, w.budget, w.window)
+    out = tri.tri_compact_kv(kv, kept, kept_n, w.budget)
+    torch.cuda.synchronize()
+    sc_h, kept_h = sc.cpu().numpy()[0, 0], kept.cpu().numpy()[0, 0]
+    k_out, v_out = bits(out["k_out"])[0, 0], bits(out["v_out"])[0, 0]
+    for h in range(w.n_kvh):
+        keys = synth.bf16_bits_to_f32(raw[h])
+        center_h, mean_abs_h = oracle.unit_heads(hp.center, hp.mean_abs, 0, h, w.group)
+        orc = oracle.score_keys(keys, center_h, mean_abs_h, base=w.base, offsets=w.offsets)
+        S = oracle.score_magnitude_bound(keys, center_h, mean_abs_h)
+        bad = ~np.isfinite(orc)
+        assert np.array_equal(~np.isfinite(sc_h[h, :L]), bad), "non-finite scores differ from the oracle's"
+        fin = ~bad
+        assert np.all(np.abs(sc_h[h, :L][fin] - orc[fin]) <= P.SCORE_TOL * S[fin])
+        want = oracle.select_top_b(sc_h[h, :L].astype(np.float64), L, w.budget, w.window)
+        assert np.array_equal(kept_h[h, : len(want)], want)
+        if h == 0:
+            zero = (raw[0] == 0).all(axis=1)
+            assert np.all(sc_h[0, :L][zero] == 0.0), "zero keys must score exactly 0"
+            cand = np.arange(L - w.window)
+            kept_zero = np.intersect1d(want, cand[zero[: L - w.window]])
+            assert 0 < kept_zero.size < zero[: L - w.window].sum(), "the threshold must fall inside the zero tie"
+            assert 300 not in set(want.tolist()), "a NaN-scored key must rank last"
+            # both selections agree exactly here: ties are exact in both score sets
+            assert np.array_equal(want, oracle.select_top_b(orc, L, w.budget, w.window))
+        assert np.array_equal(k_out[h, : len(want)], raw[h].view(np.int16)[want])
+        assert np.array_equal(v_out[h, : len(want)], raw[::-1][h].view(np.int16)[want])
