@@ -257,6 +257,7 @@ def main():
         t1 = time.perf_counter()
         ms = (t1 - t0) * 1e3 / args.steps
 
+    step_ms = sorted(e[0].elapsed_time(e[3]) for e in events)       # per-step GPU time (events)
     score_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
     select_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
     compact_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
@@ -304,6 +305,9 @@ def main():
             "algorithmic_bytes": pass_bytes,
             "hbm_frac": pass_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "score_ms": score_ms, "select_ms": select_ms, "compact_ms": compact_ms,
+            "step_event_ms": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0],
+                              "p90": step_ms[min(len(step_ms) - 1, int(0.9 * len(step_ms)))]},
+            "algorithmic_GBps": pass_bytes / (ms * 1e-3) / 1e9,
         },
     }
     del dw, kv, scores, kept, kept_n, k_out, v_out, pos_out, new_len, freed, n_freed

@@ -7,6 +7,7 @@ imports, links or calls anything here, and nothing here imports the product path
 
 from .triattention import (  # noqa: F401
     rope_theta,
+    rope_apply,
     split_bands,
     concentration,
     score_keys,

@@ -46,6 +46,7 @@ import numpy as np
 
 __all__ = [
     "rope_theta",
+    "rope_apply",
     "split_bands",
     "concentration",
     "score_keys",
@@ -72,6 +73,33 @@ def rope_theta(base: float, head_dim: int) -> np.ndarray:
         raise ValueError("head_dim must be even")
     f = np.arange(head_dim // 2, dtype=np.float64)
     return np.float64(base) ** (-2.0 * f / head_dim)
+
+
+def rope_apply(x, positions, *, base: float, layout: str = "half", inverse: bool = False) -> np.ndarray:
+    """Rotate every RoPE pair of the vectors x[L, d] by the angle p_j theta_f (float64).
+
+    RoPE turns each frequency pair by an angle proportional to the token's position
+    ([Review] "Key Concepts"): the pair (a, b) of a vector at position p becomes
+    (a cos(p theta_f) - b sin(p theta_f), a sin(p theta_f) + b cos(p theta_f)).
+    inverse=True turns by the opposite angle, which undoes the rotation.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    L, d = x.shape
+    ang = np.asarray(positions, dtype=np.float64).reshape(L, 1) * rope_theta(base, d)[None, :]
+    if inverse:
+        ang = -ang
+    c, s = np.cos(ang), np.sin(ang)
+    if layout == "half":
+        ia, ib = np.arange(d // 2), np.arange(d // 2, d)
+    elif layout == "interleaved":
+        ia, ib = np.arange(0, d, 2), np.arange(1, d, 2)
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
+    a, b = x[:, ia], x[:, ib]
+    out = np.empty_like(x)
+    out[:, ia] = a * c - b * s
+    out[:, ib] = a * s + b * c
+    return out
 
 
 def split_bands(x, layout: str = "half") -> np.ndarray:
@@ -159,10 +187,14 @@ def _norm_term(k_bands, center_h, mean_abs_h):
 
 def score_keys(keys, center, mean_abs, *, base: float, offsets, key_pos=None,
                query_pos=None, layout: str = "half", reduce: str = "max",
-               return_heads: bool = False):
+               return_heads: bool = False, key_space: str = "pre"):
     """Score every cached key of one (layer, KV head) unit.
 
-    keys:     [L, d] pre-RoPE keys (any float dtype; upcast exactly to float64)
+    keys:     [L, d] cached keys (any float dtype; upcast exactly to float64): pre-RoPE
+              (key_space "pre"), or already rotated by RoPE at key_pos (key_space
+              "post"), in which case they are turned back to pre-RoPE first: the score
+              is defined on pre-RoPE keys ([Review] "Framework Shift"; [DevTo] "The Core
+              Idea: Q/K Concentration in Pre-RoPE Space")
     center:   [G, F] complex E[q_f] of the G query heads of the group
               (or [G, F, 2] real/imaginary pairs)
     mean_abs: [G, F] E|q_f|
@@ -186,6 +218,10 @@ def score_keys(keys, center, mean_abs, *, base: float, offsets, key_pos=None,
     key_pos = np.asarray(key_pos, dtype=np.int64)
     if query_pos is None:
         query_pos = L - 1
+    if key_space == "post":
+        keys = rope_apply(keys, key_pos, base=base, layout=layout, inverse=True)
+    elif key_space != "pre":
+        raise ValueError(f"unknown key_space {key_space!r}")
     theta = rope_theta(base, d)
     kb = split_bands(keys, layout)
 

@@ -27,6 +27,9 @@ def _pin_calls():
             calls.append(lambda layout=layout, d=d, base=base, qpos=qpos, offs=offs:
                          pins.test_p1_exact_centre_identity(layout, d, base, qpos, offs))
         calls.append(lambda layout=layout: pins.test_p2_zero_centre_is_pure_norm(layout))
+        calls.append(lambda layout=layout: pins.test_p9_rope_apply_is_textbook_rope(layout))
+        calls.append(lambda layout=layout: pins.test_p9_post_rope_keys_score_like_pre_rope_keys(layout, "max"))
+        calls.append(lambda layout=layout: pins.test_p9_post_rope_exact_centre_identity(layout))
         calls.append(lambda layout=layout: pins.test_p6_identical_samples(layout))
     calls += [
         pins.test_p2_partial_concentration_norm_coefficient,
@@ -153,6 +156,17 @@ def _select(kind):
     return sel if kind else orig
 
 
+_rope_apply = T.rope_apply
+
+
+def _rope_inverse_ignored(x, positions, *, base, layout="half", inverse=False):
+    return _rope_apply(x, positions, base=base, layout=layout, inverse=False)
+
+
+def _rope_sin_sign(x, positions, *, base, layout="half", inverse=False):
+    return _rope_apply(x, -np.asarray(positions), base=base, layout=layout, inverse=inverse)
+
+
 def _calib_abs_of_mean(q, layout="half"):
     qb = T.split_bands(q, layout)
     c = qb.mean(axis=0)
@@ -183,6 +197,8 @@ MUTATIONS = {
     "select_off_by_one": ("select_top_b", _select("off_by_one")),
     "calibrate_abs_of_mean": ("calibrate", _calib_abs_of_mean),
     "compact_freed_off_by_one": ("compact_paged_sequence", _compact_freed_off_by_one),
+    "rope_inverse_ignored": ("rope_apply", _rope_inverse_ignored),
+    "rope_angle_sign": ("rope_apply", _rope_sin_sign),
 }
 
 

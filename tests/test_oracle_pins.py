@@ -9,6 +9,8 @@ Each test states what it pins.  Nothing here calls the HIP library.
   P5  brute-force top-B on tiny inputs (all subsets), plus window / budget edge cases
   P6  calibration closed forms
   P7  compaction invariants
+  P9  keys cached after RoPE: the oracle's rotation equals textbook RoPE, undoes itself,
+      and scoring rotated keys equals scoring the pre-RoPE keys
 """
 
 import itertools
@@ -400,3 +402,61 @@ def test_p7_paged_forward_packing():
     # pages outside the sequence are untouched
     others = sorted(set(range(n_pages)) - set(bt))
     assert pk[others].tobytes() == pool[others].tobytes()
+
+
+# ---------------------------------------------------------------------------------------
+# P9 keys cached after RoPE
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("layout", ["half", "interleaved"])
+def test_p9_rope_apply_is_textbook_rope(layout):
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((9, 128))
+    pos = np.array([0, 1, 2, 17, 255, 4096, 32767, 131071, 147455])
+    got = oracle.rope_apply(x, pos, base=1e6, layout=layout)
+    want = np.stack([rope_rotate(x[i], int(pos[i]), 1e6, layout) for i in range(len(pos))])
+    # the two compute theta_f with different rounding; the angle error grows with p
+    tol = 1e-14 * (pos[:, None] + 1.0)
+    assert np.all(np.abs(got - want) <= tol)
+    back = oracle.rope_apply(got, pos, base=1e6, layout=layout, inverse=True)
+    assert np.all(np.abs(back - x) <= tol)
+    assert np.array_equal(oracle.rope_apply(x[:1], [0], base=1e6, layout=layout), x[:1])
+
+
+@pytest.mark.parametrize("layout", ["half", "interleaved"])
+@pytest.mark.parametrize("reduce", ["max", "mean"])
+def test_p9_post_rope_keys_score_like_pre_rope_keys(layout, reduce):
+    rng = np.random.default_rng(22)
+    d, G, L, qpos, base = 128, 3, 40, 50000, 1e6
+    offsets = [2 ** i for i in range(13)]
+    keys = rng.standard_normal((L, d)) + rng.standard_normal(d)
+    key_pos = np.sort(rng.choice(qpos + 1, size=L, replace=False))
+    center = rng.standard_normal((G, d // 2, 2))
+    mean_abs = np.hypot(center[..., 0], center[..., 1]) * rng.uniform(1.0, 3.0, (G, d // 2))
+    rotated = np.stack([rope_rotate(keys[i], int(key_pos[i]), base, layout) for i in range(L)])
+    pre = oracle.score_keys(keys, center, mean_abs, base=base, offsets=offsets, key_pos=key_pos,
+                            query_pos=qpos, layout=layout, reduce=reduce)
+    post = oracle.score_keys(rotated, center, mean_abs, base=base, offsets=offsets, key_pos=key_pos,
+                             query_pos=qpos, layout=layout, reduce=reduce, key_space="post")
+    S = oracle.score_magnitude_bound(keys, center, mean_abs, layout=layout, reduce=reduce)
+    assert np.all(np.abs(post - pre) <= 1e-9 * S)
+
+
+@pytest.mark.parametrize("layout", ["half", "interleaved"])
+def test_p9_post_rope_exact_centre_identity(layout):
+    # with E[q] = q the score of a rotated key is the mean over the offsets of the dot
+    # product of the rotated query with the key exactly as cached
+    rng = np.random.default_rng(23)
+    d, L, qpos, base = 128, 16, 9000, 1e4
+    offsets = [1, 2, 4, 8, 16, 32]
+    q = rng.standard_normal(d)
+    cached = rng.standard_normal((L, d))
+    key_pos = np.sort(rng.choice(qpos + 1, size=L, replace=False))
+    center = bands_of(q, layout)[None]
+    mag = np.hypot(center[..., 0], center[..., 1])
+    got = oracle.score_keys(cached, center, mag, base=base, offsets=offsets, key_pos=key_pos,
+                            query_pos=qpos, layout=layout, key_space="post")
+    want = np.array([np.mean([rope_rotate(q, qpos + o, base, layout) @ cached[j] for o in offsets])
+                     for j in range(L)])
+    S = oracle.score_magnitude_bound(cached, center, mag, layout=layout)
+    assert np.all(np.abs(got - want) <= 1e-9 * S)
