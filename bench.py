@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 METRIC = "Gkeys/s scored+selected+compacted at 32K ctx; % of HBM roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic.json")
-SCORE_SRC = os.path.join(ROOT, "kv_cache_compression_tri_amd", "csrc", "score.hip")
+SCORE_SRC = os.path.join(ROOT, "kv_cache_compression_tri_amd", "csrc", "score_kernel.h")
 
 
 def parse():
@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None, help="workload name (default: the 32K GQA pass)")
+    ap.add_argument("--key-space", choices=("pre", "post"), default="pre",
+                    help="score the cache as pre-RoPE keys (default) or as keys already rotated by RoPE")
     ap.add_argument("--cpu-units", type=int, default=0,
                     help="units for the oracle baseline (0 = two per host core, capped at 32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -74,7 +76,7 @@ def _oracle_unit(job):
     """Score + select + compact one unit with the float64 oracle; returns seconds spent."""
     import numpy as np
     import oracle
-    name, s, l, h = job
+    name, key_space, s, l, h = job
     from kv_cache_compression_tri_amd import synth
     from kv_cache_compression_tri_amd.synth import workloads as W
     w = W.WORKLOADS[name]
@@ -88,14 +90,14 @@ def _oracle_unit(job):
     center, mean_abs = oracle.unit_heads(hp.center, hp.mean_abs, l, h, w.group)
     t0 = time.perf_counter()
     sc = oracle.score_keys(keys, center, mean_abs, base=w.base, offsets=w.offsets, layout=w.layout,
-                           reduce=w.reduce)
+                           reduce=w.reduce, key_space=key_space)
     kept = oracle.select_top_b(sc, L, w.budget, w.window)
     if w.with_values:
         oracle.compact_dense(keys_raw, vals, kept)
     return time.perf_counter() - t0, L
 
 
-def cpu_baseline(name, n_units):
+def cpu_baseline(name, n_units, key_space="pre"):
     os.environ.setdefault("OMP_NUM_THREADS", "1")
     from kv_cache_compression_tri_amd.synth import workloads as W
     import numpy as np
@@ -109,7 +111,7 @@ def cpu_baseline(name, n_units):
         n_units = min(32, 2 * cores)
     rng = np.random.default_rng(2024)
     picks = rng.choice(w.n_units, size=min(n_units, w.n_units), replace=False)
-    jobs = [(name,) + tuple(int(x) for x in W.unit_coords(w, int(u))) for u in picks]
+    jobs = [(name, key_space) + tuple(int(x) for x in W.unit_coords(w, int(u))) for u in picks]
     workers = min(cores, len(jobs))
     ctx = mp.get_context("spawn")
     t0 = time.perf_counter()
@@ -157,7 +159,7 @@ def recorded_traffic(name):
     except (OSError, ValueError):
         return None
     entry = rec.get(name)
-    if not entry or entry.get("score_hip_sha256") != digest:
+    if not entry or entry.get("score_kernel_sha256") != digest:
         return None
     return entry.get("bytes_per_launch")
 
@@ -216,7 +218,7 @@ def main():
         if ev is not None:
             ev[0].record()
         tri.tri_score_keys(kv, dw.center, dw.mean_abs, rope_base=w.base, offsets=w.offsets, group=w.group,
-                           reduce=w.reduce, rope_layout=w.layout, scores=scores)
+                           reduce=w.reduce, rope_layout=w.layout, scores=scores, key_space=args.key_space)
         if ev is not None:
             ev[1].record()
         tri.tri_select_topb(scores, kv, w.budget, w.window, kept=kept, kept_n=kept_n)
@@ -268,7 +270,7 @@ def main():
     pass_bytes = score_bytes + compact_bytes
     achieved = score_bytes / (score_ms * 1e-3) / 1e9
     value = keys_per_step / (ms * 1e-3) / 1e9
-    traffic = recorded_traffic(name)
+    traffic = recorded_traffic(name) if args.key_space == "pre" else None
     line = {
         "metric": METRIC,
         "value": value,
@@ -287,7 +289,7 @@ def main():
             "n_seq": w.n_seq, "n_layer": w.n_layer, "n_kv_heads": w.n_kvh, "group": w.group,
             "context": w.max_len, "head_dim": w.head_dim, "kv_dtype": w.dtype, "budget": w.budget,
             "window": w.window, "offsets": len(w.offsets), "reduce": w.reduce,
-            "layout": "paged" if w.paged else "dense", "compaction": compacts,
+            "layout": "paged" if w.paged else "dense", "compaction": compacts, "key_space": args.key_space,
             "keys_per_step": keys_per_step, "parallelism": "single GPU",
         },
         "roofline": {
@@ -316,7 +318,7 @@ def main():
     line["pass"]["copy_GBps"] = copy_gbs
     line["pass"]["frac_of_copy"] = pass_bytes / (ms * 1e-3) / 1e9 / copy_gbs
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(name, args.cpu_units)
+        line["cpu_baseline"] = cpu_baseline(name, args.cpu_units, args.key_space)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -72,6 +72,13 @@ typedef enum tri_reduce { TRI_REDUCE_MAX = 0, TRI_REDUCE_MEAN = 1 } tri_reduce;
 
 typedef enum tri_kv_layout { TRI_DENSE = 0, TRI_PAGED = 1 } tri_kv_layout;
 
+/* What the cache holds.  The score is defined on pre-RoPE keys ([DevTo] "The Core Idea:
+ * Q/K Concentration in Pre-RoPE Space"; [Review] "Framework Shift").  A serving cache may
+ * instead hold keys already rotated by RoPE at their positions; with
+ * TRI_KEYS_POST_ROPE the same score is computed from those keys (slot j rotated at
+ * position j) without rotating them back. */
+typedef enum tri_key_space { TRI_KEYS_PRE_ROPE = 0, TRI_KEYS_POST_ROPE = 1 } tri_key_space;
+
 /* Description of a pre-RoPE KV cache (all pointers device, caller-owned).
  *   dense: k, v are [n_seq][n_layer][n_kvh][max_len][head_dim]; slot j of unit (s,l,h) is
  *          row j; the unit holds seq_len[s] <= max_len keys.
@@ -115,6 +122,7 @@ typedef struct tri_score_cfg {
   const int32_t *offsets;   /* host */
   int32_t group;
   int32_t reduce;           /* tri_reduce */
+  int32_t key_space;        /* tri_key_space (0 = pre-RoPE keys) */
 } tri_score_cfg;
 
 /* Calibration of the query statistics ([Review] "Key Concepts": the centre is the mean of
@@ -141,7 +149,11 @@ int tri_calibrate_stats(const void *q, int32_t dtype, int64_t n, int32_t n_layer
  *           + sum_f (1 - R_f) m_f |k_f|
  *   score(j) = max_hq s_hq(j)  (TRI_REDUCE_MAX)   or   mean_hq s_hq(j)  (TRI_REDUCE_MEAN)
  *
- * with Q = query_pos[s] (int64; NULL means seq_len[s] - 1).
+ * with Q = query_pos[s] (int64; NULL means seq_len[s] - 1).  With cfg->key_space ==
+ * TRI_KEYS_POST_ROPE the cached vector of slot j is k'_f = k_f e^{i j theta_f} (RoPE
+ * applied at position j) and the score is that of k_f; since
+ * conj(k_f) e^{-i p_j theta_f} = conj(k'_f), it is evaluated as
+ * sum_f Re(c_f C_f e^{i Q theta_f} conj(k'_f)) + (1 - R_f) m_f |k'_f|.
  *   center:   [n_layer][n_kvh * group][head_dim/2][2] float32
  *   mean_abs: [n_layer][n_kvh * group][head_dim/2] float32
  *   scores:   out float32 [n_seq][n_layer][n_kvh][slots] (slots = max_len dense,
@@ -193,7 +205,7 @@ const char *tri_last_error(void);
 /* ABI version of this header: major * 10000 + minor * 100 + patch. */
 int tri_version(void);
 
-#define TRI_VERSION 10000
+#define TRI_VERSION 10100
 
 #ifdef __cplusplus
 }

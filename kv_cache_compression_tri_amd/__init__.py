@@ -182,7 +182,10 @@ def tri_calibrate_stats(q, rope_layout: str = "half", center=None, mean_abs=None
     return center, mean_abs
 
 
-def _score_cfg(rope_base, offsets, group, reduce, rope_layout):
+_KEY_SPACES = {"pre": _abi.TRI_KEYS_PRE_ROPE, "post": _abi.TRI_KEYS_POST_ROPE}
+
+
+def _score_cfg(rope_base, offsets, group, reduce, rope_layout, key_space="pre"):
     offs = (ctypes.c_int32 * len(offsets))(*[int(o) for o in offsets])
     cfg = _abi.TriScoreCfg()
     cfg.rope_base = float(rope_base)
@@ -191,13 +194,16 @@ def _score_cfg(rope_base, offsets, group, reduce, rope_layout):
     cfg.offsets = ctypes.cast(offs, ctypes.POINTER(ctypes.c_int32))
     cfg.group = int(group)
     cfg.reduce = _REDUCE[reduce]
+    cfg.key_space = _KEY_SPACES[key_space]
     return cfg, offs
 
 
 def tri_score_keys(kv: KVCache, center, mean_abs, *, rope_base: float, offsets: Sequence[int],
                    group: int, reduce: str = "max", rope_layout: str = "half", query_pos=None,
-                   scores=None, stream=None):
-    """Score every cached key; returns float32 scores [n_seq, n_layer, n_kvh, slots]."""
+                   scores=None, stream=None, key_space: str = "pre"):
+    """Score every cached key; returns float32 scores [n_seq, n_layer, n_kvh, slots].
+
+    key_space "post": the cache holds keys already rotated by RoPE at their slot index."""
     torch = _torch()
     L = _abi.lib()
     desc = kv.descriptor()
@@ -213,7 +219,7 @@ def tri_score_keys(kv: KVCache, center, mean_abs, *, rope_base: float, offsets: 
     _shape(mean_abs, "mean_abs", (desc.n_layer, n_qh, desc.head_dim // 2))
     _shape(query_pos, "query_pos", (kv.n_seq,))
     _shape(scores, "scores", (kv.n_seq, desc.n_layer, desc.n_kvh, kv.slots))
-    cfg, _keep = _score_cfg(rope_base, offsets, group, reduce, rope_layout)
+    cfg, _keep = _score_cfg(rope_base, offsets, group, reduce, rope_layout, key_space)
     _abi.check(L.tri_score_keys(ctypes.byref(cfg), _ptr(center), _ptr(mean_abs), ctypes.byref(desc),
                                 _ptr(query_pos), _ptr(scores), None, None, _stream(stream)))
     return scores
@@ -288,10 +294,11 @@ def tri_compact_kv(kv: KVCache, kept, kept_n, budget: int, k_out=None, v_out=Non
 
 
 def compress(kv: KVCache, center, mean_abs, *, rope_base, offsets, group, budget, window,
-             reduce="max", rope_layout="half", query_pos=None, stream=None):
+             reduce="max", rope_layout="half", query_pos=None, stream=None, key_space="pre"):
     """Score, select and compact in one call (convenience; not part of the C ABI)."""
     scores = tri_score_keys(kv, center, mean_abs, rope_base=rope_base, offsets=offsets, group=group,
-                            reduce=reduce, rope_layout=rope_layout, query_pos=query_pos, stream=stream)
+                            reduce=reduce, rope_layout=rope_layout, query_pos=query_pos, stream=stream,
+                            key_space=key_space)
     kept, kept_n = tri_select_topb(scores, kv, budget, window, stream=stream)
     out = tri_compact_kv(kv, kept, kept_n, budget, stream=stream)
     out.update(scores=scores, kept=kept, kept_n=kept_n)

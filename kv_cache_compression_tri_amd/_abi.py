@@ -14,6 +14,7 @@ TRI_F32, TRI_BF16 = 0, 1
 TRI_ROPE_HALF, TRI_ROPE_INTERLEAVED = 0, 1
 TRI_REDUCE_MAX, TRI_REDUCE_MEAN = 0, 1
 TRI_DENSE, TRI_PAGED = 0, 1
+TRI_KEYS_PRE_ROPE, TRI_KEYS_POST_ROPE = 0, 1
 
 EXPORTED = (
     "tri_calibrate_stats",
@@ -52,6 +53,7 @@ class TriScoreCfg(ctypes.Structure):
         ("offsets", POINTER(c_int32)),
         ("group", c_int32),
         ("reduce", c_int32),
+        ("key_space", c_int32),
     ]
 
 

@@ -22,7 +22,7 @@ ARCH = os.environ.get("TRI_OFFLOAD_ARCH", "gfx950")
 LIBS = {
     "libtri.so": {
         "dir": os.path.join(PKG, "csrc"),
-        "sources": ["api.hip", "score.hip", "select.hip", "compact.hip", "calib.hip"],
+        "sources": ["api.hip", "score.hip", "score_post.hip", "select.hip", "compact.hip", "calib.hip"],
         "includes": [os.path.join(ROOT, "include"), os.path.join(PKG, "csrc")],
     },
     "libtri_synth.so": {

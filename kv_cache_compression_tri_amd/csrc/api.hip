@@ -140,6 +140,8 @@ int tri_score_keys(const tri_score_cfg* cfg, const float* center, const float* m
       return fail(TRI_EINVAL, "unknown rope layout %d", cfg->rope_layout);
     if (cfg->reduce != TRI_REDUCE_MAX && cfg->reduce != TRI_REDUCE_MEAN)
       return fail(TRI_EINVAL, "unknown reduce %d", cfg->reduce);
+    if (cfg->key_space != TRI_KEYS_PRE_ROPE && cfg->key_space != TRI_KEYS_POST_ROPE)
+      return fail(TRI_EINVAL, "unknown key space %d", cfg->key_space);
     if (cfg->group < 1) return fail(TRI_EINVAL, "group must be >= 1");
     if (cfg->group > tri::kMaxGroup) return fail(TRI_ENOTSUP, "group %d > %d", cfg->group, tri::kMaxGroup);
     if (cfg->n_offsets < 1 || !cfg->offsets) return fail(TRI_EINVAL, "at least one offset is required");
@@ -194,7 +196,8 @@ int tri_score_keys(const tri_score_cfg* cfg, const float* center, const float* m
     (void)hipGetLastError();
     hipError_t e = tri::launch_score(p, g_eff, kv->dtype == TRI_BF16,
                                      cfg->rope_layout == TRI_ROPE_INTERLEAVED,
-                                     kv->layout == TRI_PAGED, int(grid), static_cast<hipStream_t>(stream));
+                                     kv->layout == TRI_PAGED, cfg->key_space == TRI_KEYS_POST_ROPE, int(grid),
+                                     static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TRI_OK : hip_fail(e, "score launch");
   } catch (...) {
     return fail(TRI_EHIP, "unexpected host exception in tri_score_keys");

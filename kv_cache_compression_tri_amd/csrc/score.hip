@@ -1,413 +1,12 @@
-// Key-scoring kernel of the TriAttention compression pass (gfx950).
-//
-// What it computes (per unit = sequence s, layer l, KV head h; key slot j at position p_j;
-// query heads hq of the group with centre c_f = E[q_f] and m_f = E|q_f|):
-//
-//   s_hq(j) = mean_Delta sum_f |c_f||k_f| cos((Q - p_j + Delta) theta_f + arg c_f - arg k_f)
-//           + sum_f (1 - R_f) m_f |k_f|,          R_f = |c_f| / m_f
-//
-// The first term is the cosine series in the query-key distance that fixed pre-RoPE
-// centres produce after RoPE ("TriAttention: Trigonometric KV Compression for Efficient
-// Long Reasoning", sections "Core Mechanism" and "Key Concepts"); the second blends in a
-// norm-only signal weighted by the measured concentration ("TriAttention: How a Geometric
-// Trick Cuts LLM Memory Use by 10x Without Losing Accuracy", section "The Core Idea: Q/K
-// Concentration in Pre-RoPE Space").
-//
-// Evaluation (exact algebraic rewrite; the only per-key transcendental is |k_f|):
-//   |c||k| cos(d theta + arg c - arg k) = Re(c conj(k) e^{i d theta}), so with an anchor
-//   slot p_a and r = p_j - p_a,
-//     s_hq(j) = sum_f Re( W_f x_f ) + N_f |k_f|,   x_f = e^{-i r theta_f} conj(k_f),
-//     W_f = c_f C_f e^{i (Q - p_a) theta_f},  C_f = mean_Delta e^{i Delta theta_f},
-//     N_f = m_f - |c_f|  (= (1 - R_f) m_f).
-// The anchor phase is formed in float64 per segment; e^{-i r theta_f} (r < kChunk) comes from
-// an LDS table built in float64 and rounded once to float32.  Large phases never go through
-// a float32 sin/cos.  At each chunk boundary the weights rotate by e^{-i kChunk theta_f}.
-// For the mean reduction W and N are averaged over the group first (both terms are linear
-// in them).  bf16 keys are widened exactly to float32 (one shift or mask per element); all
-// arithmetic is float32.
-//
-// Mapping: 8 lanes per key; lane g of a key owns bands 8g..8g+7, so the 8 lanes of a key
-// read its row as coalesced 16-byte pieces and a wave scores 8 keys per step.  Per-lane
-// partial sums are combined with three DPP steps inside each 8-lane group.  Each wave owns
-// an equal, contiguous share of all 8-key steps of all units and walks it unit by unit; the
-// weights of the current unit live in registers.  Key rows are fetched with raw buffer
-// loads from a wave-uniform base plus a per-lane constant offset, a few steps ahead, into a
-// ring of registers.  Scores of 8 steps are gathered into one lane each and written as one
-// coalesced 256-byte store.  The grid is persistent (one workgroup of kScoreWaves waves per
-// CU), so the 128 KB phase table is built once per CU.
-#include "tri_internal.h"
+// Key scoring for caches that hold pre-RoPE keys (the kernel is in score_kernel.h).
+#include "score_kernel.h"
 
 namespace tri {
-namespace {
-
-// Block-table entries are read through the constant address space: the table is read-only
-// during the kernel and its addresses are wave-uniform, so these become scalar loads (they
-// do not pass through the vector memory counter that tracks the key stream).
-typedef __attribute__((address_space(4))) const int32_t* const_i32_ptr;
-
-template <bool BF16>
-struct Frag {
-  uint4 d[BF16 ? 2 : 4];
-};
-
-__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
-  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
-}
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// (re, im) of band b (0..7) of the lane's fragment.
-template <bool BF16, bool IL>
-__device__ __forceinline__ void band_of(const Frag<BF16>& fr, int b, float& re, float& im) {
-  if constexpr (BF16) {
-    if constexpr (IL) {
-      const uint32_t w = word(fr.d[b >> 2], b & 3);
-      re = bf16_lo(w);
-      im = bf16_hi(w);
-    } else {
-      const uint32_t wr = word(fr.d[0], b >> 1), wi = word(fr.d[1], b >> 1);
-      re = (b & 1) ? bf16_hi(wr) : bf16_lo(wr);
-      im = (b & 1) ? bf16_hi(wi) : bf16_lo(wi);
-    }
-  } else {
-    if constexpr (IL) {
-      re = __uint_as_float(word(fr.d[b >> 1], 2 * (b & 1)));
-      im = __uint_as_float(word(fr.d[b >> 1], 2 * (b & 1) + 1));
-    } else {
-      re = __uint_as_float(word(fr.d[b >> 2], b & 3));
-      im = __uint_as_float(word(fr.d[2 + (b >> 2)], b & 3));
-    }
-  }
-}
-
-// A wave-uniform 64-bit value held in scalar registers.
-__device__ __forceinline__ int64_t uniform64(int64_t v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v)));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v) >> 32));
-  return int64_t((uint64_t(hi) << 32) | lo);
-}
-
-// Sum over the 8 lanes of a key (lanes 8k..8k+7): two quad swaps and a half-row mirror.
-__device__ __forceinline__ float sum8(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
-  return v;
-}
-
-// Weight of query head row `row` (= layer * n_qh + hq), band f at anchor
-// A = C_f e^{i(Q - p_a) theta_f}.
-__device__ __forceinline__ void head_weight(const ScoreParams& P, int64_t row, int f, float ar, float ai,
-                                            float& wr, float& wi, float& nc) {
-  const int64_t idx = row * kBands + f;
-  const float2 c = reinterpret_cast<const float2*>(P.center)[idx];
-  const float m = P.mean_abs[idx];
-  wr = c.x * ar - c.y * ai;
-  wi = c.x * ai + c.y * ar;
-  // (1 - R_f) m_f = m_f - |c_f|; a band with m_f = 0 carries no norm term
-  nc = (m > 0.0f) ? m - __builtin_sqrtf(c.x * c.x + c.y * c.y) : 0.0f;
-}
-
-// LDS phase table: entry (r, f), r < kChunk, holds (c, s) = e^{-i r theta_f} as float32.
-// Step it = r / 8, key kk = r % 8, band group g = f / 8 and band b = f % 8 are arranged so
-// that the 64 lanes of a step read 64 consecutive 16-byte slots per instruction (one slot
-// holds bands 2m and 2m+1 of the lane's key).
-__device__ __forceinline__ int tab_slot(int r, int f) {
-  const int it = r >> 3, kk = r & 7, g = f >> 3, b = f & 7;
-  return ((it * 4 + (b >> 1)) * 64 + kk * 8 + g) * 2 + (b & 1);   // float2 index
-}
-
-template <int GE, bool BF16, bool IL, bool PAGED>
-__global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScoreParams P) {
-  constexpr int NW = kScoreWaves;
-  constexpr int NT = NW * 64;
-  constexpr int STEPS = kChunk / 8;            // 8 keys per wave step
-  constexpr int PF = GE <= 4 ? 4 : 2;          // steps of loads in flight
-  constexpr int ESZ = BF16 ? 2 : 4;
-  constexpr int ROW = kHeadDim * ESZ;
-  static_assert(STEPS % PF == 0 && STEPS % 8 == 0, "chunk geometry");
-
-  __shared__ float4 tab[kChunk * kBands / 2];
-  __shared__ float2 stepc[kBands];             // e^{-i kChunk theta_f}
-  __shared__ float2 anc[NW][kBands];           // per-wave anchors
-
-  const int tid = threadIdx.x;
-  // ---- phase table: float64 recurrence per (band, run of offsets), rounded once -------
-  {
-    constexpr int RL = kChunk * kBands / NT;   // offsets per thread
-    const int f = tid & 63, run = tid >> 6;
-    const double th = P.theta[f];
-    double s1, c1, zr, zi;
-    sincos(-th, &s1, &c1);
-    sincos(-double(run * RL) * th, &zi, &zr);
-    float2* t2 = reinterpret_cast<float2*>(tab);
-    for (int m = 0; m < RL; ++m) {
-      t2[tab_slot(run * RL + m, f)] = make_float2(float(zr), float(zi));
-      const double nr = zr * c1 - zi * s1;
-      zi = zr * s1 + zi * c1;
-      zr = nr;
-    }
-    if (tid < kBands) {
-      double ss, cc;
-      sincos(-double(kChunk) * th, &ss, &cc);
-      stepc[tid] = make_float2(float(cc), float(ss));
-    }
-  }
-  __syncthreads();
-
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kk = lane >> 3;   // key of the step
-  const int g = lane & 7;     // band group
-  const int ups = P.n_layer * P.n_kvh;
-  const int n_qh = P.n_kvh * P.group;
-  // per-lane constant byte offsets of the lane's pieces inside a step's 8 rows
-  uint32_t off[BF16 ? 2 : 4];
-  if constexpr (BF16) {
-    off[0] = kk * ROW + (IL ? g * 32 : g * 16);
-    off[1] = kk * ROW + (IL ? g * 32 + 16 : 128 + g * 16);
-  } else {
-    off[0] = kk * ROW + (IL ? g * 64 : g * 32);
-    off[1] = off[0] + 16;
-    off[2] = kk * ROW + (IL ? g * 64 + 32 : 256 + g * 32);
-    off[3] = off[2] + 16;
-  }
-
-  // Work division: the units' keys, in (sequence, layer, head) order and in 8-key steps
-  // (a unit of L keys has ceil(L / 8) steps), are split into one contiguous, equal share
-  // per wave, so ragged lengths do not unbalance the grid.  Consecutive steps of one unit
-  // form a segment: the weights carry over (rotated chunk by chunk) and the loads stream
-  // without a break.  seq_len lives on the device, so each wave sums it itself.
-  auto unit_steps = [&](int sq) -> int64_t {
-    return (int64_t(min(max(P.seq_len[sq], 0), int(P.score_stride))) + 7) >> 3;
-  };
-  int64_t total = 0;
-  for (int s0 = 0; s0 < P.n_seq; s0 += 64) {
-    int64_t c = s0 + lane < P.n_seq ? unit_steps(s0 + lane) : 0;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
-    total += uniform64(c);
-  }
-  total *= ups;
-  const int64_t n_waves = int64_t(gridDim.x) * NW;
-  const int64_t w_id = int64_t(blockIdx.x) * NW + wave;
-  const int64_t share = total / n_waves, extra = total % n_waves;
-  const int64_t g0 = w_id * share + min(w_id, extra);
-  const int64_t g1 = g0 + share + (w_id < extra ? 1 : 0);
-  // sequence holding step g0, and the global index of that sequence's first step
-  int s = 0;
-  int64_t seq_base = 0;
-  if (g0 < g1) {
-    for (int s0 = 0; s0 < P.n_seq; s0 += 64) {
-      const int64_t c = s0 + lane < P.n_seq ? unit_steps(s0 + lane) * ups : 0;
-      int64_t incl = c;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int64_t t = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += t;
-      }
-      const uint64_t hit = __ballot(seq_base + incl > g0);
-      if (hit) {
-        const int ln = __ffsll((unsigned long long)hit) - 1;
-        s = s0 + ln;
-        seq_base += uniform64(__shfl(incl - c, ln, 64));
-        break;
-      }
-      seq_base += uniform64(__shfl(incl, 63, 64));
-    }
-  }
-  int64_t gs = g0;
-  while (gs < g1 && s < P.n_seq) {
-    const int64_t spu = unit_steps(s);
-    const int64_t rel = gs - seq_base;
-    if (rel >= spu * ups) {            // past the end of sequence s (or s is empty)
-      seq_base += spu * ups;
-      ++s;
-      continue;
-    }
-    const int u_in = int(rel / spu);
-    const int st0 = int(rel - int64_t(u_in) * spu);
-    const int64_t seg_end = min(g1, seq_base + (int64_t(u_in) + 1) * spu);
-    const int seg_steps = int(seg_end - gs);
-    gs = seg_end;
-    const int64_t unit = int64_t(s) * ups + u_in;
-    const int l = u_in / P.n_kvh;
-    const int h = u_in - l * P.n_kvh;
-    const int L = min(max(P.seq_len[s], 0), int(P.score_stride));
-    const int p0 = 8 * st0;
-    const int nkeys = min(L - p0, 8 * seg_steps);
-    const int n_steps = seg_steps;
-    const int64_t Q = P.query_pos ? P.query_pos[s] : int64_t(L) - 1;
-
-    // ---- key stream: raw buffer loads; reads past the segment return zero ------------
-    const char* kbase = static_cast<const char*>(P.k);
-    const_i32_ptr bt = PAGED ? (const_i32_ptr)(P.block_table + int64_t(s) * P.max_pages) : nullptr;
-    // paged: page of step n, read one step before the step's load is issued
-    auto page_of = [&](int n) -> int32_t { return bt[(p0 + 8 * min(n, n_steps - 1)) >> 4]; };
-    int32_t pg_next = PAGED ? page_of(0) : 0;   // widened only where it is used
-    auto load_step = [&](int n, Frag<BF16>& fr) {
-      if (n >= n_steps) return;
-      const int key0 = p0 + 8 * n;
-      const char* base;
-      if constexpr (PAGED) {
-        const int64_t page = pg_next;
-        pg_next = page_of(n + 1);
-        base = kbase + ((((page * P.n_layer + l) * P.n_kvh + h) * kPage) + (key0 & 15)) * ROW;
-      } else {
-        base = kbase + (unit * P.max_len + key0) * ROW;
-      }
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, min(8, nkeys - 8 * n) * ROW, 0x00020000);
-#pragma unroll
-      for (int i = 0; i < (BF16 ? 2 : 4); ++i)
-        fr.d[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], 0, 0));
-    };
-    Frag<BF16> ring[PF];
-#pragma unroll
-    for (int i = 0; i < PF; ++i) load_step(i, ring[i]);
-
-    {  // anchor of this segment (float64), one band per lane
-      const double ang = double(Q - p0) * P.theta[lane];
-      double sa, ca;
-      sincos(ang, &sa, &ca);
-      const double cr = P.c_re[lane], ci = P.c_im[lane];
-      anc[wave][lane] = make_float2(float(cr * ca - ci * sa), float(cr * sa + ci * ca));
-    }
-    __builtin_amdgcn_wave_barrier();
-
-    float wr[GE][8], wn[GE][8], nn[GE][8];
-    const int64_t hrow0 = int64_t(l) * n_qh + int64_t(h) * P.group;
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const int f = g * 8 + b;
-      const float2 A = anc[wave][f];
-      if (P.reduce_mean) {
-        float sr = 0.0f, si = 0.0f, sn = 0.0f;
-        for (int hh = 0; hh < P.group; ++hh) {
-          float r0, i0, n0;
-          head_weight(P, hrow0 + hh, f, A.x, A.y, r0, i0, n0);
-          sr += r0;
-          si += i0;
-          sn += n0;
-        }
-        const float inv = 1.0f / float(P.group);
-        wr[0][b] = sr * inv;
-        wn[0][b] = -si * inv;
-        nn[0][b] = sn * inv;
-      } else {
-#pragma unroll
-        for (int hh = 0; hh < GE; ++hh) {
-          float r0, i0, n0;
-          head_weight(P, hrow0 + hh, f, A.x, A.y, r0, i0, n0);
-          wr[hh][b] = r0;
-          wn[hh][b] = -i0;
-          nn[hh][b] = n0;
-        }
-      }
-    }
-
-    float* out = P.scores + unit * P.score_stride + p0;
-    const int lane_key = 8 * g + kk;   // key this lane stores within a group of 8 steps
-    float keep = 0.0f;
-    int n = 0;
-    for (int c = 0; n < n_steps; ++c) {
-      // The table is read-only, so its per-step reads are invariant across chunks; an opaque
-      // base keeps them inside their step instead of being hoisted (and held in registers)
-      // for all steps of the chunk.
-      int tz = lane;
-      asm volatile("" : "+v"(tz));
-      if (c > 0) {  // next chunk: W <- W e^{-i kChunk theta_f}
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          const float2 R = stepc[(tz & 7) * 8 + b];
-#pragma unroll
-          for (int hh = 0; hh < GE; ++hh) {
-            const float a = wr[hh][b], q = wn[hh][b];
-            wr[hh][b] = fmaf(a, R.x, q * R.y);
-            wn[hh][b] = fmaf(q, R.x, -(a * R.y));
-          }
-        }
-      }
-#pragma unroll
-      for (int it = 0; it < STEPS; ++it) {
-        if (n < n_steps) {
-          Frag<BF16>& cur = ring[it % PF];
-          float acc[GE];
-#pragma unroll
-          for (int hh = 0; hh < GE; ++hh) acc[hh] = 0.0f;
-          const float4* tp = tab + it * 4 * 64 + tz;
-          const float4 t4[4] = {tp[0], tp[64], tp[128], tp[192]};
-#pragma unroll
-          for (int b = 0; b < 8; ++b) {
-            float a, q;
-            band_of<BF16, IL>(cur, b, a, q);
-            const float tc = (b & 1) ? t4[b >> 1].z : t4[b >> 1].x;
-            const float ts = (b & 1) ? t4[b >> 1].w : t4[b >> 1].y;
-            const float xr = fmaf(tc, a, ts * q);      // Re(e^{-i r theta} conj(k))
-            const float xi = fmaf(ts, a, -(tc * q));   // Im(...)
-            const float nk = __builtin_amdgcn_sqrtf(fmaf(a, a, q * q));
-#pragma unroll
-            for (int hh = 0; hh < GE; ++hh) {
-              acc[hh] = fmaf(wr[hh][b], xr, acc[hh]);
-              acc[hh] = fmaf(wn[hh][b], xi, acc[hh]);
-              acc[hh] = fmaf(nn[hh][b], nk, acc[hh]);
-            }
-          }
-          // the slot is free again: fetch the step PF ahead into it
-          load_step(n + PF, cur);
-          float sc = sum8(acc[0]);
-#pragma unroll
-          for (int hh = 1; hh < GE; ++hh) sc = fmaxf(sc, sum8(acc[hh]));
-          if ((it & 7) == g) keep = sc;
-          if ((it & 7) == 7 || n == n_steps - 1) {
-            // lane (kk, g) holds the score of step (n & ~7) + g, key kk
-            const int key = 8 * (n & ~7) + lane_key;
-            if (g <= (n & 7) && key < nkeys) out[key] = keep;
-          }
-          ++n;
-          // keep each step's table reads and arithmetic inside its own step
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    }
-  }
-}
-
-template <int GE>
-hipError_t launch_ge(const ScoreParams& p, bool bf16, bool il, bool paged, int grid, hipStream_t st) {
-  const dim3 blk(kScoreWaves * 64), grd(grid);
-#define TRI_SCORE_CASE(B, I, PG)                                                     \
-  if (bf16 == B && il == I && paged == PG) {                                         \
-    hipLaunchKernelGGL((score_kernel<GE, B, I, PG>), grd, blk, 0, st, p);           \
-    return hipGetLastError();                                                        \
-  }
-  TRI_SCORE_CASE(true, false, false)
-  TRI_SCORE_CASE(true, false, true)
-  TRI_SCORE_CASE(true, true, false)
-  TRI_SCORE_CASE(true, true, true)
-  TRI_SCORE_CASE(false, false, false)
-  TRI_SCORE_CASE(false, false, true)
-  TRI_SCORE_CASE(false, true, false)
-  TRI_SCORE_CASE(false, true, true)
-#undef TRI_SCORE_CASE
-  return hipErrorInvalidValue;
-}
-
-}  // namespace
 
 hipError_t launch_score(const ScoreParams& p, int G_eff, bool bf16, bool interleaved, bool paged,
-                        int grid, hipStream_t stream) {
-  switch (G_eff) {
-    case 1: return launch_ge<1>(p, bf16, interleaved, paged, grid, stream);
-    case 2: return launch_ge<2>(p, bf16, interleaved, paged, grid, stream);
-    case 3: return launch_ge<3>(p, bf16, interleaved, paged, grid, stream);
-    case 4: return launch_ge<4>(p, bf16, interleaved, paged, grid, stream);
-    case 5: return launch_ge<5>(p, bf16, interleaved, paged, grid, stream);
-    case 6: return launch_ge<6>(p, bf16, interleaved, paged, grid, stream);
-    case 7: return launch_ge<7>(p, bf16, interleaved, paged, grid, stream);
-    case 8: return launch_ge<8>(p, bf16, interleaved, paged, grid, stream);
-    default: return hipErrorInvalidValue;
-  }
+                        bool post, int grid, hipStream_t stream) {
+  if (post) return launch_score_post(p, G_eff, bf16, interleaved, paged, grid, stream);
+  return launch_groups<false>(p, G_eff, bf16, interleaved, paged, grid, stream);
 }
 
 }  // namespace tri

@@ -81,7 +81,9 @@ struct CalibParams {
 
 // launchers (return hipError_t of the launch)
 hipError_t launch_score(const ScoreParams& p, int G_eff, bool bf16, bool interleaved, bool paged,
-                        int grid, hipStream_t stream);
+                        bool post, int grid, hipStream_t stream);
+hipError_t launch_score_post(const ScoreParams& p, int G_eff, bool bf16, bool interleaved, bool paged,
+                             int grid, hipStream_t stream);
 hipError_t launch_select(const SelectParams& p, int64_t n_units, hipStream_t stream);
 hipError_t launch_compact(const CompactParams& p, int64_t n_units, bool bf16, bool paged,
                           bool with_v, hipStream_t stream);

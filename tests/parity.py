@@ -33,10 +33,10 @@ def host_rows(w, hp, s, layer, kv_head, tag=synth.TAG_K, as_float=True):
     return fn(w.seed, tag, unit, L, mu, sig, sink, w.dtype)
 
 
-def oracle_scores(w, hp, s, layer, kv_head, keys):
+def oracle_scores(w, hp, s, layer, kv_head, keys, key_space="pre"):
     center, mean_abs = oracle.unit_heads(hp.center, hp.mean_abs, layer, kv_head, w.group)
     sc = oracle.score_keys(keys, center, mean_abs, base=w.base, offsets=w.offsets,
-                           layout=w.layout, reduce=w.reduce)
+                           layout=w.layout, reduce=w.reduce, key_space=key_space)
     S = oracle.score_magnitude_bound(keys, center, mean_abs, layout=w.layout, reduce=w.reduce)
     return sc, S
 

@@ -99,7 +99,8 @@ def test_score_keys_validation():
     for over, code in [(dict(group=0), _abi.TRI_EINVAL), (dict(group=9), _abi.TRI_ENOTSUP),
                        (dict(n_offsets=0), _abi.TRI_EINVAL), (dict(rope_base=0.0), _abi.TRI_EINVAL),
                        (dict(rope_base=float("nan")), _abi.TRI_EINVAL), (dict(reduce=3), _abi.TRI_EINVAL),
-                       (dict(rope_layout=2), _abi.TRI_EINVAL)]:
+                       (dict(rope_layout=2), _abi.TRI_EINVAL), (dict(key_space=2), _abi.TRI_EINVAL),
+                       (dict(key_space=-1), _abi.TRI_EINVAL)]:
         cc, _k = _cfg(**over)
         assert _score(cc, _kv())[0] == code, over
     many = (ctypes.c_int32 * 65)(*range(65))

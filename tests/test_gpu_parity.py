@@ -44,11 +44,11 @@ def bits(t):
     return t.cpu().numpy()
 
 
-def run_pass(dw):
+def run_pass(dw, key_space="pre"):
     w = dw.w
     kv = dw.kv()
     scores = tri.tri_score_keys(kv, dw.center, dw.mean_abs, rope_base=w.base, offsets=w.offsets,
-                                group=w.group, reduce=w.reduce, rope_layout=w.layout)
+                                group=w.group, reduce=w.reduce, rope_layout=w.layout, key_space=key_space)
     kept, kept_n = tri.tri_select_topb(scores, kv, w.budget, w.window)
     out = tri.tri_compact_kv(kv, kept, kept_n, w.budget)
     torch.cuda.synchronize()
@@ -168,14 +168,15 @@ def test_small_dense_parity(name):
 # small paged case: every unit, in-place packing, freed pages
 # ---------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("lengths", [[5000, 70, 1300, 1024], [1025, 4096, 16, 2047]])
-def test_small_paged_parity(lengths):
+@pytest.mark.parametrize("lengths,key_space", [([5000, 70, 1300, 1024], "pre"), ([1025, 4096, 16, 2047], "pre"),
+                                               ([3000, 17, 4096, 900], "post")])
+def test_small_paged_parity(lengths, key_space):
     w = W.scaled(W.WORKLOADS["paged_ragged64_bf16"], n_seq=4, n_layer=2, n_kvh=2, max_len=5120,
                  len_range=(16, 5120))
-    log(f"small paged lengths={lengths}")
+    log(f"small paged lengths={lengths} keys {key_space}-RoPE")
     dw = SD.build(w, hp=W.make_params(w, lengths=lengths))
     k_before, v_before = bits(dw.k), bits(dw.v)
-    sc, kept, kept_n, out = host_outputs(*run_pass(dw))
+    sc, kept, kept_n, out = host_outputs(*run_pass(dw, key_space))
     k_after, v_after = bits(dw.k), bits(dw.v)
     bt = dw.hp.block_table
     exp_k, exp_v = k_before.copy(), v_before.copy()
@@ -185,7 +186,7 @@ def test_small_paged_parity(lengths):
         for l in range(w.n_layer):
             for h in range(w.n_kvh):
                 keys = P.host_rows(w, dw.hp, s, l, h)
-                orc, S = P.oracle_scores(w, dw.hp, s, l, h, keys)
+                orc, S = P.oracle_scores(w, dw.hp, s, l, h, keys, key_space)
                 P.check_scores(sc[s, l, h, :L], orc, S)
                 P.check_kept(kept[s, l, h], sc[s, l, h], orc, S, L, w.budget, w.window)
                 kept_units[(l, h)] = kept[s, l, h, : min(L, w.budget)]
@@ -329,12 +330,12 @@ def test_calibration_parity(dtype, layout):
 # full-size workloads, sampled units
 # ---------------------------------------------------------------------------------------
 
-def _full_dense(name, units):
+def _full_dense(name, units, key_space="pre"):
     w = W.WORKLOADS[name]
     log(f"full size {name}: building")
     dw = SD.build(w)
-    log(f"full size {name}: running the pass")
-    scores, kept, kept_n, out = run_pass(dw)
+    log(f"full size {name}: running the pass (keys {key_space}-RoPE)")
+    scores, kept, kept_n, out = run_pass(dw, key_space)
     kn = kept_n.cpu().numpy()
     worst = 0.0
     for u in units:
@@ -348,7 +349,7 @@ def _full_dense(name, units):
              "new_len": out["new_len"][s:s + 1].cpu().numpy()}
         # re-index the sampled unit as unit (0, 0, 0) of a one-unit view
         sub = SD.DeviceWorkload(w, dw.hp, None, None, None, None, None, None)
-        worst = max(worst, _check_sampled(sub, s, l, h, sc_h, kp_h, kn[s:s + 1], o))
+        worst = max(worst, _check_sampled(sub, s, l, h, sc_h, kp_h, kn[s:s + 1], o, key_space))
     # the generator itself: device K rows of the sampled units equal the host rows
     for u in units[:2]:
         s, l, h = W.unit_coords(w, u)
@@ -357,11 +358,11 @@ def _full_dense(name, units):
     log(f"  max score error / bound = {worst:.3e}")
 
 
-def _check_sampled(dw, s, l, h, sc_h, kp_h, kn_h, o):
+def _check_sampled(dw, s, l, h, sc_h, kp_h, kn_h, o, key_space="pre"):
     w, hp = dw.w, dw.hp
     L = int(hp.lengths[s])
     keys = P.host_rows(w, hp, s, l, h)
-    orc, S = P.oracle_scores(w, hp, s, l, h, keys)
+    orc, S = P.oracle_scores(w, hp, s, l, h, keys, key_space)
     worst, _ = P.check_scores(sc_h[0, 0, 0, :L], orc, S)
     P.check_kept(kp_h[0, 0, 0], sc_h[0, 0, 0], orc, S, L, w.budget, w.window)
     n = min(L, w.budget)
@@ -546,3 +547,64 @@ def test_zero_duplicated_and_nan_key_rows():
             assert np.array_equal(want, oracle.select_top_b(orc, L, w.budget, w.window))
         assert np.array_equal(k_out[h, : len(want)], raw[h].view(np.int16)[want])
         assert np.array_equal(v_out[h, : len(want)], raw[::-1][h].view(np.int16)[want])
+
+
+
+# ---------------------------------------------------------------------------------------
+# keys cached after RoPE
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,layout,group,reduce", [("bf16", "half", 4, "max"), ("f32", "interleaved", 3, "mean"),
+                                                       ("bf16", "interleaved", 7, "max")])
+def test_post_rope_small_dense(dtype, layout, group, reduce):
+    # a post-RoPE cache built on the host: the generator's keys rotated by RoPE at their
+    # slots in float64 (the oracle's rotation), then stored in the cache dtype
+    w = W.scaled(BASE, name="post_rope", n_seq=2, n_layer=2, n_kvh=2, group=group, reduce=reduce, dtype=dtype,
+                 layout=layout, max_len=2600, budget=500, window=32)
+    lengths = [2600, 1111]
+    hp = W.make_params(w, lengths=lengths)
+    log(f"post-RoPE small dense {dtype} {layout} G={group} {reduce}")
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    k = torch.zeros((2, 2, 2, w.max_len, 128), dtype=tdt)
+    cached = {}
+    for s in range(2):
+        L = lengths[s]
+        for l in range(2):
+            for h in range(2):
+                pre = P.host_rows(w, hp, s, l, h)
+                post = oracle.rope_apply(pre, np.arange(L), base=w.base, layout=layout).astype(np.float32)
+                if dtype == "bf16":
+                    b = synth.f32_to_bf16_bits(post)
+                    cached[(s, l, h)] = synth.bf16_bits_to_f32(b)
+                    k[s, l, h, :L] = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16)
+                else:
+                    cached[(s, l, h)] = post
+                    k[s, l, h, :L] = torch.from_numpy(post)
+    k = k.cuda()
+    kv = tri.KVCache.dense(k, None, torch.tensor(lengths, dtype=torch.int32, device="cuda"))
+    center, mean_abs = torch.from_numpy(hp.center).cuda(), torch.from_numpy(hp.mean_abs).cuda()
+    out = tri.compress(kv, center, mean_abs, rope_base=w.base, offsets=w.offsets, group=group, budget=w.budget,
+                       window=w.window, reduce=reduce, rope_layout=layout, key_space="post")
+    torch.cuda.synchronize()
+    sc, kp, kn = out["scores"].cpu().numpy(), out["kept"].cpu().numpy(), out["kept_n"].cpu().numpy()
+    ko = out["k_out"].cpu().float().numpy()
+    worst = 0.0
+    for (s, l, h), keys in cached.items():
+        L = lengths[s]
+        orc, S = P.oracle_scores(w, hp, s, l, h, keys, "post")
+        e, _ = P.check_scores(sc[s, l, h, :L], orc, S)
+        worst = max(worst, e)
+        P.check_kept(kp[s, l, h], sc[s, l, h], orc, S, L, w.budget, w.window)
+        n = min(L, w.budget)
+        assert kn[s] == n
+        assert np.array_equal(ko[s, l, h, :n], keys[kp[s, l, h, :n]])
+    log(f"  max score error / bound = {worst:.3e}")
+
+
+def test_full_gqa8b_32k_bf16_post_rope():
+    # the full-size cache read as a post-RoPE cache (the synthetic keys stand for rotated keys)
+    w = W.WORKLOADS["gqa8b_32k_bf16"]
+    hp = W.make_params(w)
+    rng = np.random.default_rng(105)
+    units = [0, w.n_units - 1] + _low_r_units(w, hp, 1) + [int(x) for x in rng.choice(w.n_units, 1, replace=False)]
+    _full_dense("gqa8b_32k_bf16", units, key_space="post")
