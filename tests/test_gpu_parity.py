@@ -608,3 +608,27 @@ def test_full_gqa8b_32k_bf16_post_rope():
     rng = np.random.default_rng(105)
     units = [0, w.n_units - 1] + _low_r_units(w, hp, 1) + [int(x) for x in rng.choice(w.n_units, 1, replace=False)]
     _full_dense("gqa8b_32k_bf16", units, key_space="post")
+
+
+# ---------------------------------------------------------------------------------------
+# calls enqueued on a non-default stream give the default stream's results
+# ---------------------------------------------------------------------------------------
+
+def test_side_stream_matches_default_stream():
+    w = W.scaled(BASE, name="streams", n_seq=2, n_layer=2, n_kvh=2, max_len=2000, budget=300, window=32)
+    dw = SD.build(w, hp=W.make_params(w, lengths=[2000, 1234]))
+    log("same pass on the default stream and on a side stream")
+    ref = run_pass(dw)
+    side = torch.cuda.Stream()
+    kv = dw.kv()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        sc = tri.tri_score_keys(kv, dw.center, dw.mean_abs, rope_base=w.base, offsets=w.offsets,
+                                group=w.group, reduce=w.reduce, stream=side)
+        kept, kept_n = tri.tri_select_topb(sc, kv, w.budget, w.window, stream=side)
+        out = tri.tri_compact_kv(kv, kept, kept_n, w.budget, stream=side)
+    side.synchronize()
+    assert torch.equal(sc.view(torch.int32), ref[0].view(torch.int32))
+    assert torch.equal(kept, ref[1]) and torch.equal(kept_n, ref[2])
+    assert torch.equal(out["k_out"].view(torch.int16), ref[3]["k_out"].view(torch.int16))
+    assert torch.equal(out["v_out"].view(torch.int16), ref[3]["v_out"].view(torch.int16))
