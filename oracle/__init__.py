@@ -8,6 +8,7 @@ imports, links or calls anything here, and nothing here imports the product path
 from .triattention import (  # noqa: F401
     rope_theta,
     rope_apply,
+    decode_fp8_e4m3,
     split_bands,
     concentration,
     score_keys,

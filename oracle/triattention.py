@@ -45,6 +45,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
+    "decode_fp8_e4m3",
     "rope_theta",
     "rope_apply",
     "split_bands",
@@ -57,6 +58,27 @@ __all__ = [
     "calibrate",
     "unit_heads",
 ]
+
+
+# ---------------------------------------------------------------------------------------
+# fp8 keys (OCP 8-bit floating point, E4M3 "fn" encoding)
+# ---------------------------------------------------------------------------------------
+
+def decode_fp8_e4m3(codes) -> np.ndarray:
+    """Exact float64 values of OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3
+    mantissa bits; exponent field 0 is subnormal; S.1111.111 is NaN; there is no infinity).
+
+    A cache may hold its keys as such codes times a positive scale, which composes the
+    compression with KV quantisation ([Project], the project's news entries).
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    out = sign * val
+    out[(c & 0x7F) == 0x7F] = np.nan
+    return out
 
 
 # ---------------------------------------------------------------------------------------

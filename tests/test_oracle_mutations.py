@@ -48,6 +48,7 @@ def _pin_calls():
         pins.test_p6_scaling_and_permutation,
         pins.test_p7_dense_rows_are_bit_copies,
         pins.test_p7_paged_forward_packing,
+        pins.test_p10_fp8_e4m3_values_fixed_by_the_format,
     ]
     calls += [lambda t=t: pins.test_p5_select_matches_brute_force(t) for t in range(60)]
     with open(golden.GOLDEN) as fh:
@@ -167,6 +168,20 @@ def _rope_sin_sign(x, positions, *, base, layout="half", inverse=False):
     return _rope_apply(x, -np.asarray(positions), base=base, layout=layout, inverse=inverse)
 
 
+def _fp8_bias_8(codes):
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    out = T.__dict__["_orig_decode_fp8"](c) / 2.0
+    out[(c & 0x78) == 0] *= 2.0          # subnormals unchanged, normals off by the bias
+    return out
+
+
+def _fp8_no_subnormals(codes):
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    out = T.__dict__["_orig_decode_fp8"](c)
+    out[(c & 0x78) == 0] = 0.0
+    return out
+
+
 def _calib_abs_of_mean(q, layout="half"):
     qb = T.split_bands(q, layout)
     c = qb.mean(axis=0)
@@ -199,6 +214,8 @@ MUTATIONS = {
     "compact_freed_off_by_one": ("compact_paged_sequence", _compact_freed_off_by_one),
     "rope_inverse_ignored": ("rope_apply", _rope_inverse_ignored),
     "rope_angle_sign": ("rope_apply", _rope_sin_sign),
+    "fp8_exponent_bias": ("decode_fp8_e4m3", _fp8_bias_8),
+    "fp8_no_subnormals": ("decode_fp8_e4m3", _fp8_no_subnormals),
 }
 
 
@@ -210,6 +227,7 @@ def test_unmutated_oracle_passes_every_pin():
 def test_mutation_is_caught(name, monkeypatch):
     attr, repl = MUTATIONS[name]
     monkeypatch.setitem(T.__dict__, "_orig_compact", T.compact_paged_sequence)
+    monkeypatch.setitem(T.__dict__, "_orig_decode_fp8", T.decode_fp8_e4m3)
     monkeypatch.setattr(T, attr, repl)
     if hasattr(oracle, attr):
         monkeypatch.setattr(oracle, attr, repl)

@@ -11,6 +11,7 @@ Each test states what it pins.  Nothing here calls the HIP library.
   P7  compaction invariants
   P9  keys cached after RoPE: the oracle's rotation equals textbook RoPE, undoes itself,
       and scoring rotated keys equals scoring the pre-RoPE keys
+  P10 fp8 (OCP E4M3) key codes: values the format definition fixes
 """
 
 import itertools
@@ -460,3 +461,28 @@ def test_p9_post_rope_exact_centre_identity(layout):
                      for j in range(L)])
     S = oracle.score_magnitude_bound(cached, center, mag, layout=layout)
     assert np.all(np.abs(got - want) <= 1e-9 * S)
+
+
+# ---------------------------------------------------------------------------------------
+# P10 fp8 (OCP E4M3) key codes
+# ---------------------------------------------------------------------------------------
+
+def test_p10_fp8_e4m3_values_fixed_by_the_format():
+    v = oracle.decode_fp8_e4m3
+    # zero, smallest subnormal 2^-9, largest subnormal 7 * 2^-9, smallest normal 2^-6, one,
+    # the largest finite value 448, its negation, and the NaN codes
+    assert v([0x00])[0] == 0.0 and math.copysign(1.0, v([0x80])[0]) == -1.0
+    assert v([0x01])[0] == 2.0 ** -9
+    assert v([0x07])[0] == 7 * 2.0 ** -9
+    assert v([0x08])[0] == 2.0 ** -6
+    assert v([0x38])[0] == 1.0 and v([0xB8])[0] == -1.0
+    assert v([0x7E])[0] == 448.0 and v([0xFE])[0] == -448.0
+    assert np.isnan(v([0x7F, 0xFF])).all()
+    assert v([0x3C])[0] == 1.5 and v([0x40])[0] == 2.0 and v([0x46])[0] == 3.5 and v([0x4B])[0] == 5.5
+    # every other code is finite, and the positive codes increase with the code
+    c = np.arange(256)
+    fin = (c & 0x7F) != 0x7F
+    assert np.isfinite(v(c[fin])).all()
+    pos = v(np.arange(0x00, 0x7F))
+    assert np.all(np.diff(pos) > 0)
+    assert np.array_equal(v(np.arange(0x80, 0xFF)), -pos)
