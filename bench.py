@@ -12,8 +12,8 @@ Inputs are generated on the device before timing; the timed region is bracketed 
 torch.cuda.synchronize().
 
 Prints one JSON line with the metric (keys scored+selected+compacted per second), the
-roofline of the dominant kernel (scoring: algorithmic bytes = 256 B per key read, over its
-average HIP-event duration) and the CPU oracle timed on a bounded sample of units.
+roofline of the dominant kernel (scoring: algorithmic bytes = one key row per key read,
+256 B for bf16, 128 B for fp8, 512 B for float32, over its average HIP-event duration) and the CPU oracle timed on a bounded sample of units.
 """
 
 from __future__ import annotations
@@ -83,10 +83,13 @@ def _oracle_unit(job):
     hp = W.make_params(w)
     unit = W.unit_index(w, s, l, h)
     L = int(hp.lengths[s])
-    keys = synth.rows_as_float(w.seed, synth.TAG_K, unit, L, hp.mu_k[l, h], hp.sigma, w.sink, w.dtype)
+    scale = float(hp.k_scale[l, h])
+    keys = synth.rows_as_float(w.seed, synth.TAG_K, unit, L, hp.mu_k[l, h], hp.sigma, w.sink, w.dtype,
+                               scale=scale)
     vals = synth.rows(w.seed, synth.TAG_V, unit, L, np.zeros(128, np.float32), np.ones(128, np.float32),
                       False, w.dtype)
-    keys_raw = synth.rows(w.seed, synth.TAG_K, unit, L, hp.mu_k[l, h], hp.sigma, w.sink, w.dtype)
+    keys_raw = synth.rows(w.seed, synth.TAG_K, unit, L, hp.mu_k[l, h], hp.sigma, w.sink, w.dtype,
+                          scale=scale)
     center, mean_abs = oracle.unit_heads(hp.center, hp.mean_abs, l, h, w.group)
     t0 = time.perf_counter()
     sc = oracle.score_keys(keys, center, mean_abs, base=w.base, offsets=w.offsets, layout=w.layout,
@@ -263,7 +266,7 @@ def main():
     score_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
     select_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
     compact_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
-    elt = 2 if w.dtype == "bf16" else 4
+    elt = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
     score_bytes = keys_per_step * w.head_dim * elt                       # every key read once
     kept_rows = w.n_layer * w.n_kvh * sum(min(w.budget, L) for L in lengths)
     compact_bytes = kept_rows * w.head_dim * elt * 2 * 2 if compacts else 0   # K and V, read + write

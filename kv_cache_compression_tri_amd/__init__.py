@@ -46,7 +46,9 @@ def _dtype_code(t) -> int:
         return _abi.TRI_BF16
     if t.dtype == torch.float32:
         return _abi.TRI_F32
-    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    if t.dtype == torch.float8_e4m3fn:
+        return _abi.TRI_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16 or float8_e4m3fn)")
 
 
 def _dev(t, name, dtype=None):
@@ -88,6 +90,8 @@ class KVCache:
            [n_seq, max_pages] (int32) mapping slot j of sequence s to page
            block_table[s, j // page], row j % page
     seq_len: int32 [n_seq] on the device; pos: optional int32 RoPE positions
+    k_scale: fp8 (torch.float8_e4m3fn, OCP E4M3) caches only, optional float32
+             [n_layer, n_kvh]: key = decoded code * k_scale[l, h]
     """
 
     k: object
@@ -96,14 +100,15 @@ class KVCache:
     layout: str = "dense"
     block_table: object = None
     pos: object = None
+    k_scale: object = None
 
     @classmethod
-    def dense(cls, k, v, seq_len, pos=None):
-        return cls(k, v, seq_len, "dense", None, pos)
+    def dense(cls, k, v, seq_len, pos=None, k_scale=None):
+        return cls(k, v, seq_len, "dense", None, pos, k_scale)
 
     @classmethod
-    def paged(cls, k_pool, v_pool, block_table, seq_len, pos=None):
-        return cls(k_pool, v_pool, seq_len, "paged", block_table, pos)
+    def paged(cls, k_pool, v_pool, block_table, seq_len, pos=None, k_scale=None):
+        return cls(k_pool, v_pool, seq_len, "paged", block_table, pos, k_scale)
 
     @property
     def n_seq(self) -> int:
@@ -133,6 +138,12 @@ class KVCache:
         d.k = self.k.data_ptr()
         d.v = None if self.v is None else self.v.data_ptr()
         d.pos = None if self.pos is None else self.pos.data_ptr()
+        if self.k_scale is not None:
+            if d.dtype != _abi.TRI_FP8_E4M3:
+                raise ValueError("k_scale is only valid with float8_e4m3fn keys")
+            _dev(self.k_scale, "k_scale", torch.float32)
+            _shape(self.k_scale, "k_scale", (d.n_layer, d.n_kvh))
+            d.k_scale = self.k_scale.data_ptr()
         if self.layout == "dense":
             if self.k.dim() != 5 or int(self.k.shape[0]) != self.n_seq:
                 raise ValueError("dense k must be [n_seq, n_layer, n_kvh, max_len, head_dim]")

@@ -22,7 +22,8 @@ ARCH = os.environ.get("TRI_OFFLOAD_ARCH", "gfx950")
 LIBS = {
     "libtri.so": {
         "dir": os.path.join(PKG, "csrc"),
-        "sources": ["api.hip", "score.hip", "score_post.hip", "select.hip", "compact.hip", "calib.hip"],
+        "sources": ["api.hip", "score.hip", "score_post.hip", "score_fp8.hip", "score_post_fp8.hip",
+                    "select.hip", "compact.hip", "calib.hip"],
         "includes": [os.path.join(ROOT, "include"), os.path.join(PKG, "csrc")],
     },
     "libtri_synth.so": {
@@ -75,7 +76,8 @@ def build(verbose: bool = False, jobs: int = 8, extra_flags=()) -> dict:
         objs = [o for (lb, o, _) in jobs_list if lb == lib]
         target = os.path.join(LIB_DIR, lib)
         tmp = target + ".tmp"
-        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs],
+             verbose)
         os.replace(tmp, target)
         out[lib] = target
     return out

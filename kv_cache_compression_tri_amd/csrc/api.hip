@@ -48,6 +48,8 @@ int64_t slots_of(const tri_kv* kv) {
   return kv->layout == TRI_PAGED ? int64_t(kv->max_pages) * kv->page : kv->max_len;
 }
 
+int elem_bytes(int32_t dtype) { return dtype == TRI_F32 ? 4 : (dtype == TRI_BF16 ? 2 : 1); }
+
 int check_dims(int32_t head_dim) {
   if (head_dim < 2 || (head_dim & 1)) return fail(TRI_EINVAL, "head_dim must be even and >= 2 (got %d)", head_dim);
   if (head_dim != tri::kHeadDim) return fail(TRI_ENOTSUP, "head_dim %d is not supported (only 128)", head_dim);
@@ -57,7 +59,9 @@ int check_dims(int32_t head_dim) {
 int check_kv(const tri_kv* kv, bool need_k) {
   if (!kv) return fail(TRI_EINVAL, "kv descriptor is NULL");
   if (kv->layout != TRI_DENSE && kv->layout != TRI_PAGED) return fail(TRI_EINVAL, "unknown kv layout %d", kv->layout);
-  if (kv->dtype != TRI_F32 && kv->dtype != TRI_BF16) return fail(TRI_EINVAL, "unknown dtype %d", kv->dtype);
+  if (kv->dtype != TRI_F32 && kv->dtype != TRI_BF16 && kv->dtype != TRI_FP8_E4M3)
+    return fail(TRI_EINVAL, "unknown dtype %d", kv->dtype);
+  if (kv->k_scale && kv->dtype != TRI_FP8_E4M3) return fail(TRI_EINVAL, "k_scale is only valid with fp8 keys");
   if (kv->n_seq < 1 || kv->n_layer < 1 || kv->n_kvh < 1)
     return fail(TRI_EINVAL, "n_seq, n_layer and n_kvh must be >= 1");
   if (int rc = check_dims(kv->head_dim)) return rc;
@@ -104,6 +108,7 @@ int tri_calibrate_stats(const void* q, int32_t dtype, int64_t n, int32_t n_layer
   try {
     g_error.clear();
     if (!q || !center || !mean_abs) return fail(TRI_EINVAL, "q, center and mean_abs must be non-NULL");
+    if (dtype == TRI_FP8_E4M3) return fail(TRI_ENOTSUP, "calibration takes float32 or bfloat16 queries");
     if (dtype != TRI_F32 && dtype != TRI_BF16) return fail(TRI_EINVAL, "unknown dtype %d", dtype);
     if (rope_layout != TRI_ROPE_HALF && rope_layout != TRI_ROPE_INTERLEAVED)
       return fail(TRI_EINVAL, "unknown rope layout %d", rope_layout);
@@ -175,6 +180,7 @@ int tri_score_keys(const tri_score_cfg* cfg, const float* center, const float* m
     p.block_table = kv->layout == TRI_PAGED ? kv->block_table : nullptr;
     p.center = center;
     p.mean_abs = mean_abs;
+    p.k_scale = kv->k_scale;
     p.scores = scores;
     p.max_len = kv->max_len;
     p.score_stride = slots;
@@ -194,7 +200,7 @@ int tri_score_keys(const tri_score_cfg* cfg, const float* center, const float* m
     if (grid < 1) grid = 1;
     const int g_eff = p.reduce_mean ? 1 : cfg->group;
     (void)hipGetLastError();
-    hipError_t e = tri::launch_score(p, g_eff, kv->dtype == TRI_BF16,
+    hipError_t e = tri::launch_score(p, g_eff, kv->dtype,
                                      cfg->rope_layout == TRI_ROPE_INTERLEAVED,
                                      kv->layout == TRI_PAGED, cfg->key_space == TRI_KEYS_POST_ROPE, int(grid),
                                      static_cast<hipStream_t>(stream));
@@ -275,7 +281,7 @@ int tri_compact_kv(const tri_kv* kv, const int32_t* kept, const int32_t* kept_n,
     const int64_t units = int64_t(kv->n_seq) * p.units_per_seq;
     if (!paged && units * p.chunks_per_unit > 0x7FFFFFFF) return fail(TRI_ENOTSUP, "grid too large");
     (void)hipGetLastError();
-    hipError_t e = tri::launch_compact(p, units, kv->dtype == TRI_BF16, paged, with_v,
+    hipError_t e = tri::launch_compact(p, units, elem_bytes(kv->dtype), paged, with_v,
                                        static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TRI_OK : hip_fail(e, "compaction launch");
   } catch (...) {

@@ -6,8 +6,8 @@
 // and "Why Existing KV Cache Compression Breaks in Production": a paged allocator can only
 // free a block that is completely empty).
 //
-// Dense (out of place): one workgroup per (unit, 64 output rows); 16 lanes copy one bf16
-// row (256 bytes) with 16-byte loads and stores.
+// Dense (out of place): one workgroup per (unit, 64 output rows); ROW/16 lanes copy one
+// row (128 B fp8, 256 B bf16, 512 B float32) with 16-byte loads and stores.
 //
 // Paged (in place): one workgroup per unit walks its destination slots in chunks of 64,
 // in increasing order; each chunk loads all of its source rows into registers, waits for
@@ -24,10 +24,10 @@ namespace {
 constexpr int kCopyThreads = 256;
 constexpr int kRowsPerChunk = 64;
 
-template <bool BF16>
+template <int ESZ>
 __global__ __launch_bounds__(kCopyThreads) void compact_dense_kernel(const CompactParams P,
                                                                       bool with_v) {
-  constexpr int ROW = kHeadDim * (BF16 ? 2 : 4);
+  constexpr int ROW = kHeadDim * ESZ;
   constexpr int TPR = ROW / 16;                  // lanes per row
   constexpr int RPP = kCopyThreads / TPR;        // rows per pass
   const int64_t unit = blockIdx.x / P.chunks_per_unit;
@@ -58,10 +58,10 @@ __global__ __launch_bounds__(kCopyThreads) void compact_dense_kernel(const Compa
   }
 }
 
-template <bool BF16>
+template <int ESZ>
 __global__ __launch_bounds__(kCopyThreads) void compact_paged_kernel(const CompactParams P,
                                                                       bool with_v) {
-  constexpr int ROW = kHeadDim * (BF16 ? 2 : 4);
+  constexpr int ROW = kHeadDim * ESZ;
   constexpr int TPR = ROW / 16;
   constexpr int RPP = kCopyThreads / TPR;
   constexpr int PASSES = kRowsPerChunk / RPP;
@@ -126,22 +126,26 @@ __global__ __launch_bounds__(kCopyThreads) void compact_paged_kernel(const Compa
   }
 }
 
+template <int ESZ>
+void launch_compact_esz(const CompactParams& p, int64_t n_units, bool paged, bool with_v,
+                        hipStream_t stream) {
+  const dim3 blk(kCopyThreads);
+  if (paged)
+    hipLaunchKernelGGL(compact_paged_kernel<ESZ>, dim3(unsigned(n_units)), blk, 0, stream, p, with_v);
+  else
+    hipLaunchKernelGGL(compact_dense_kernel<ESZ>, dim3(unsigned(n_units * p.chunks_per_unit)), blk, 0,
+                       stream, p, with_v);
+}
+
 }  // namespace
 
-hipError_t launch_compact(const CompactParams& p, int64_t n_units, bool bf16, bool paged,
+hipError_t launch_compact(const CompactParams& p, int64_t n_units, int elem_bytes, bool paged,
                           bool with_v, hipStream_t stream) {
-  const dim3 blk(kCopyThreads);
-  if (paged) {
-    if (bf16)
-      hipLaunchKernelGGL(compact_paged_kernel<true>, dim3(unsigned(n_units)), blk, 0, stream, p, with_v);
-    else
-      hipLaunchKernelGGL(compact_paged_kernel<false>, dim3(unsigned(n_units)), blk, 0, stream, p, with_v);
-  } else {
-    const int64_t grid = n_units * p.chunks_per_unit;
-    if (bf16)
-      hipLaunchKernelGGL(compact_dense_kernel<true>, dim3(unsigned(grid)), blk, 0, stream, p, with_v);
-    else
-      hipLaunchKernelGGL(compact_dense_kernel<false>, dim3(unsigned(grid)), blk, 0, stream, p, with_v);
+  switch (elem_bytes) {
+    case 1: launch_compact_esz<1>(p, n_units, paged, with_v, stream); break;
+    case 2: launch_compact_esz<2>(p, n_units, paged, with_v, stream); break;
+    case 4: launch_compact_esz<4>(p, n_units, paged, with_v, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -1,12 +1,17 @@
-// Key scoring for caches that hold pre-RoPE keys (the kernel is in score_kernel.h).
+// Key scoring, pre-RoPE float32 / bfloat16 keys, and the dispatch over the instantiating
+// translation units (the kernel is in score_kernel.h).
 #include "score_kernel.h"
 
 namespace tri {
 
-hipError_t launch_score(const ScoreParams& p, int G_eff, bool bf16, bool interleaved, bool paged,
+hipError_t launch_score(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
                         bool post, int grid, hipStream_t stream) {
-  if (post) return launch_score_post(p, G_eff, bf16, interleaved, paged, grid, stream);
-  return launch_groups<false>(p, G_eff, bf16, interleaved, paged, grid, stream);
+  if (dtype == 2)
+    return post ? launch_score_post_fp8(p, G_eff, interleaved, paged, grid, stream)
+                : launch_score_fp8(p, G_eff, interleaved, paged, grid, stream);
+  if (post) return launch_score_post(p, G_eff, dtype, interleaved, paged, grid, stream);
+  return dtype == 1 ? launch_groups<1, false>(p, G_eff, interleaved, paged, grid, stream)
+                    : launch_groups<0, false>(p, G_eff, interleaved, paged, grid, stream);
 }
 
 }  // namespace tri

@@ -1,0 +1,11 @@
+// Key scoring for fp8 (OCP E4M3) caches of pre-RoPE keys (the kernel is in score_kernel.h).
+#include "score_kernel.h"
+
+namespace tri {
+
+hipError_t launch_score_fp8(const ScoreParams& p, int G_eff, bool interleaved, bool paged, int grid,
+                            hipStream_t stream) {
+  return launch_groups<2, false>(p, G_eff, interleaved, paged, grid, stream);
+}
+
+}  // namespace tri

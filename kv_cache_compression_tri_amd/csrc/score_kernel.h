@@ -1,6 +1,6 @@
 // Key-scoring kernel of the TriAttention compression pass (gfx950), shared by the
-// translation units that instantiate it (score.hip: pre-RoPE keys, score_post.hip: keys
-// cached after RoPE).
+// translation units that instantiate it (score.hip / score_post.hip: pre-RoPE keys / keys
+// cached after RoPE, float32 or bfloat16; score_fp8.hip / score_post_fp8.hip: fp8 codes).
 //
 // What it computes (per unit = sequence s, layer l, KV head h; key slot j at position p_j;
 // query heads hq of the group with centre c_f = E[q_f] and m_f = E|q_f|):
@@ -25,8 +25,10 @@
 // an LDS table built in float64 and rounded once to float32.  Large phases never go through
 // a float32 sin/cos.  At each chunk boundary the weights rotate by e^{-i kChunk theta_f}.
 // For the mean reduction W and N are averaged over the group first (both terms are linear
-// in them).  bf16 keys are widened exactly to float32 (one shift or mask per element); all
-// arithmetic is float32.
+// in them).  bf16 keys are widened exactly to float32 (one shift or mask per element) and
+// fp8 (OCP E4M3) codes are converted exactly, two per instruction; all arithmetic is
+// float32.  A per-(layer, KV head) key scale (stored key = true key / scale) multiplies W
+// and N once per segment, since both terms are linear in the key.
 //
 // Mapping: 8 lanes per key; lane g of a key owns bands 8g..8g+7, so the 8 lanes of a key
 // read its row as coalesced 16-byte pieces and a wave scores 8 keys per step.  Per-lane
@@ -53,9 +55,11 @@ namespace {
 // do not pass through the vector memory counter that tracks the key stream).
 typedef __attribute__((address_space(4))) const int32_t* const_i32_ptr;
 
-template <bool BF16>
+// Element types of the key cache: DT 0 = float32, 1 = bfloat16, 2 = fp8 (OCP E4M3 codes).
+// A step fragment holds a lane's 8 bands of one key: 64 B (f32), 32 B (bf16), 16 B (fp8).
+template <int DT>
 struct Frag {
-  uint4 d[BF16 ? 2 : 4];
+  uint4 d[DT == 0 ? 4 : (DT == 1 ? 2 : 1)];
 };
 
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
@@ -65,9 +69,24 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // (re, im) of band b (0..7) of the lane's fragment.
-template <bool BF16, bool IL>
-__device__ __forceinline__ void band_of(const Frag<BF16>& fr, int b, float& re, float& im) {
-  if constexpr (BF16) {
+template <int DT, bool IL>
+__device__ __forceinline__ void band_of(const Frag<DT>& fr, int b, float& re, float& im) {
+  if constexpr (DT == 2) {
+    // exact E4M3 -> float32 conversion of two codes at a time (bytes 0,1 or 2,3 of a word;
+    // b is a constant once the band loop is unrolled, so each branch folds away)
+    if constexpr (IL) {       // bytes (re_b, im_b) sit next to each other
+      const int w = int(word(fr.d[0], b >> 1));
+      const auto v = (b & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true) : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+      re = v[0];
+      im = v[1];
+    } else {                  // re codes in words x, y; im codes in words z, w
+      const int wr = int(word(fr.d[0], b >> 2)), wi = int(word(fr.d[0], 2 + (b >> 2)));
+      const auto vr = (b & 2) ? __builtin_amdgcn_cvt_pk_f32_fp8(wr, true) : __builtin_amdgcn_cvt_pk_f32_fp8(wr, false);
+      const auto vi = (b & 2) ? __builtin_amdgcn_cvt_pk_f32_fp8(wi, true) : __builtin_amdgcn_cvt_pk_f32_fp8(wi, false);
+      re = vr[b & 1];
+      im = vi[b & 1];
+    }
+  } else if constexpr (DT == 1) {
     if constexpr (IL) {
       const uint32_t w = word(fr.d[b >> 2], b & 3);
       re = bf16_lo(w);
@@ -125,13 +144,13 @@ __device__ __forceinline__ int tab_slot(int r, int f) {
   return ((it * 4 + (b >> 1)) * 64 + kk * 8 + g) * 2 + (b & 1);   // float2 index
 }
 
-template <int GE, bool BF16, bool IL, bool PAGED, bool POST>
+template <int GE, int DT, bool IL, bool PAGED, bool POST>
 __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScoreParams P) {
   constexpr int NW = kScoreWaves;
   constexpr int NT = NW * 64;
   constexpr int STEPS = kChunk / 8;            // 8 keys per wave step
   constexpr int PF = GE <= 4 ? 4 : 2;          // steps of loads in flight
-  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int ESZ = DT == 0 ? 4 : (DT == 1 ? 2 : 1);
   constexpr int ROW = kHeadDim * ESZ;
   static_assert(STEPS % PF == 0 && STEPS % 8 == 0, "chunk geometry");
 
@@ -170,8 +189,11 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
   const int ups = P.n_layer * P.n_kvh;
   const int n_qh = P.n_kvh * P.group;
   // per-lane constant byte offsets of the lane's pieces inside a step's 8 rows
-  uint32_t off[BF16 ? 2 : 4];
-  if constexpr (BF16) {
+  uint32_t off[DT == 0 ? 4 : 2];
+  if constexpr (DT == 2) {
+    off[0] = kk * ROW + (IL ? g * 16 : g * 8);          // interleaved: one 16-byte piece
+    off[1] = kk * ROW + 64 + g * 8;                      // half: re codes, then im codes
+  } else if constexpr (DT == 1) {
     off[0] = kk * ROW + (IL ? g * 32 : g * 16);
     off[1] = kk * ROW + (IL ? g * 32 + 16 : 128 + g * 16);
   } else {
@@ -253,7 +275,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
     // paged: page of step n, read one step before the step's load is issued
     auto page_of = [&](int n) -> int32_t { return bt[(p0 + 8 * min(n, n_steps - 1)) >> 4]; };
     int32_t pg_next = PAGED ? page_of(0) : 0;   // widened only where it is used
-    auto load_step = [&](int n, Frag<BF16>& fr) {
+    auto load_step = [&](int n, Frag<DT>& fr) {
       if (n >= n_steps) return;
       const int key0 = p0 + 8 * n;
       const char* base;
@@ -266,11 +288,19 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
       }
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, min(8, nkeys - 8 * n) * ROW, 0x00020000);
+      if constexpr (DT == 2 && !IL) {
+        const uint2 re = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off[0], 0, 0));
+        const uint2 im = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off[1], 0, 0));
+        fr.d[0] = make_uint4(re.x, re.y, im.x, im.y);
+      } else if constexpr (DT == 2) {
+        fr.d[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[0], 0, 0));
+      } else {
 #pragma unroll
-      for (int i = 0; i < (BF16 ? 2 : 4); ++i)
-        fr.d[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], 0, 0));
+        for (int i = 0; i < (DT == 1 ? 2 : 4); ++i)
+          fr.d[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], 0, 0));
+      }
     };
-    Frag<BF16> ring[PF];
+    Frag<DT> ring[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) load_step(i, ring[i]);
 
@@ -314,6 +344,18 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
       }
     }
 
+    if (P.k_scale) {   // stored key = true key / scale: the score is linear in the key
+      const float ks = P.k_scale[int64_t(l) * P.n_kvh + h];
+#pragma unroll
+      for (int hh = 0; hh < GE; ++hh)
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          wr[hh][b] *= ks;
+          wn[hh][b] *= ks;
+          nn[hh][b] *= ks;
+        }
+    }
+
     float* out = P.scores + unit * P.score_stride + p0;
     const int lane_key = 8 * g + kk;   // key this lane stores within a group of 8 steps
     float keep = 0.0f;
@@ -339,7 +381,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
 #pragma unroll
       for (int it = 0; it < STEPS; ++it) {
         if (n < n_steps) {
-          Frag<BF16>& cur = ring[it % PF];
+          Frag<DT>& cur = ring[it % PF];
           float acc[GE];
 #pragma unroll
           for (int hh = 0; hh < GE; ++hh) acc[hh] = 0.0f;
@@ -347,7 +389,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
 #pragma unroll
             for (int b = 0; b < 8; ++b) {
               float a, q;
-              band_of<BF16, IL>(cur, b, a, q);
+              band_of<DT, IL>(cur, b, a, q);
               const float nk = __builtin_amdgcn_sqrtf(fmaf(a, a, q * q));
 #pragma unroll
               for (int hh = 0; hh < GE; ++hh) {        // x = conj(k'): Re(W x) = Wr a + Wi q
@@ -362,7 +404,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
 #pragma unroll
           for (int b = 0; b < 8; ++b) {
             float a, q;
-            band_of<BF16, IL>(cur, b, a, q);
+            band_of<DT, IL>(cur, b, a, q);
             const float tc = (b & 1) ? t4[b >> 1].z : t4[b >> 1].x;
             const float ts = (b & 1) ? t4[b >> 1].w : t4[b >> 1].y;
             const float xr = fmaf(tc, a, ts * q);      // Re(e^{-i r theta} conj(k))
@@ -396,38 +438,34 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
   }
 }
 
-template <int GE, bool POST>
-hipError_t launch_ge(const ScoreParams& p, bool bf16, bool il, bool paged, int grid, hipStream_t st) {
+template <int GE, int DT, bool POST>
+hipError_t launch_ge(const ScoreParams& p, bool il, bool paged, int grid, hipStream_t st) {
   const dim3 blk(kScoreWaves * 64), grd(grid);
-#define TRI_SCORE_CASE(B, I, PG)                                                     \
-  if (bf16 == B && il == I && paged == PG) {                                         \
-    hipLaunchKernelGGL((score_kernel<GE, B, I, PG, POST>), grd, blk, 0, st, p);     \
+#define TRI_SCORE_CASE(I, PG)                                                        \
+  if (il == I && paged == PG) {                                                      \
+    hipLaunchKernelGGL((score_kernel<GE, DT, I, PG, POST>), grd, blk, 0, st, p);    \
     return hipGetLastError();                                                        \
   }
-  TRI_SCORE_CASE(true, false, false)
-  TRI_SCORE_CASE(true, false, true)
-  TRI_SCORE_CASE(true, true, false)
-  TRI_SCORE_CASE(true, true, true)
-  TRI_SCORE_CASE(false, false, false)
-  TRI_SCORE_CASE(false, false, true)
-  TRI_SCORE_CASE(false, true, false)
-  TRI_SCORE_CASE(false, true, true)
+  TRI_SCORE_CASE(false, false)
+  TRI_SCORE_CASE(false, true)
+  TRI_SCORE_CASE(true, false)
+  TRI_SCORE_CASE(true, true)
 #undef TRI_SCORE_CASE
   return hipErrorInvalidValue;
 }
 
-template <bool POST>
-hipError_t launch_groups(const ScoreParams& p, int G_eff, bool bf16, bool interleaved, bool paged,
-                         int grid, hipStream_t stream) {
+template <int DT, bool POST>
+hipError_t launch_groups(const ScoreParams& p, int G_eff, bool interleaved, bool paged, int grid,
+                         hipStream_t stream) {
   switch (G_eff) {
-    case 1: return launch_ge<1, POST>(p, bf16, interleaved, paged, grid, stream);
-    case 2: return launch_ge<2, POST>(p, bf16, interleaved, paged, grid, stream);
-    case 3: return launch_ge<3, POST>(p, bf16, interleaved, paged, grid, stream);
-    case 4: return launch_ge<4, POST>(p, bf16, interleaved, paged, grid, stream);
-    case 5: return launch_ge<5, POST>(p, bf16, interleaved, paged, grid, stream);
-    case 6: return launch_ge<6, POST>(p, bf16, interleaved, paged, grid, stream);
-    case 7: return launch_ge<7, POST>(p, bf16, interleaved, paged, grid, stream);
-    case 8: return launch_ge<8, POST>(p, bf16, interleaved, paged, grid, stream);
+    case 1: return launch_ge<1, DT, POST>(p, interleaved, paged, grid, stream);
+    case 2: return launch_ge<2, DT, POST>(p, interleaved, paged, grid, stream);
+    case 3: return launch_ge<3, DT, POST>(p, interleaved, paged, grid, stream);
+    case 4: return launch_ge<4, DT, POST>(p, interleaved, paged, grid, stream);
+    case 5: return launch_ge<5, DT, POST>(p, interleaved, paged, grid, stream);
+    case 6: return launch_ge<6, DT, POST>(p, interleaved, paged, grid, stream);
+    case 7: return launch_ge<7, DT, POST>(p, interleaved, paged, grid, stream);
+    case 8: return launch_ge<8, DT, POST>(p, interleaved, paged, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -13,7 +13,8 @@ here in numpy (host, for the oracle's inputs and small cases) and in ``csrc/synt
           2^-16, so it is exact in float32.
 * value:  ``x = mu[col] + sigma[col] * n`` in float32 with each operation rounded once
           (no fused multiply-add), times 20 on a sink row, then rounded to bfloat16 with
-          round-to-nearest-even (or kept as float32).
+          round-to-nearest-even, kept as float32, or (fp8) multiplied by a power-of-two
+          inverse scale and encoded as OCP E4M3 (round to nearest even, saturating at 448).
 
 Element (unit, row, col) of stream ``tag`` under ``seed`` uses counter
 ``c = unit << 27 | row << 7 | col`` (row < 2^20, col < 128) and the three hashes at
@@ -79,11 +80,51 @@ def bf16_bits_to_f32(b) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def f32_to_fp8_e4m3(x) -> np.ndarray:
+    """OCP E4M3 codes of float32 values: round to nearest even on the float32 bits,
+    subnormal steps of 2^-9 below 2^-6, saturation at +-448, NaN -> S.1111.111."""
+    x = np.asarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.int64)
+    sign = (u >> 24) & 0x80
+    a = u & 0x7FFFFFFF
+    e0 = (a >> 23) - 127
+    r = (a >> 20) & 7
+    rem = a & 0xFFFFF
+    r = r + ((rem > 0x80000) | ((rem == 0x80000) & ((r & 1) == 1))).astype(np.int64)
+    carry = r == 8
+    r = np.where(carry, 0, r)
+    e = e0 + carry
+    normal = np.where(e > 8, 0x7E, ((e + 7) << 3) | r)
+    normal = np.minimum(normal, 0x7E)
+    with np.errstate(over="ignore", invalid="ignore"):
+        sub = np.rint(np.abs(x) * np.float32(512.0)).astype(np.float64)
+    sub = np.where(e0 < -6, sub, 0).astype(np.int64)
+    code = np.where(e0 >= -6, normal, sub)
+    code = np.where(a > 0x7F800000, 0x7F, code)
+    return (sign | code).astype(np.uint8)
+
+
+def fp8_e4m3_to_f32(c) -> np.ndarray:
+    """Exact float32 values of OCP E4M3 codes (built from their bit fields)."""
+    c = np.asarray(c, dtype=np.uint8).astype(np.uint32)
+    sign = (c & 0x80) << 24
+    e = (c >> 3) & 0xF
+    m = c & 7
+    # normal: float32 exponent e - 7 + 127, mantissa m in its top 3 bits
+    normal = sign | ((e + 120) << 23) | (m << 20)
+    out = normal.view(np.float32).copy()
+    sub = e == 0
+    out[sub] = (m[sub].astype(np.float32) * np.float32(2.0 ** -9)) * np.where(c[sub] & 0x80, -1.0, 1.0).astype(np.float32)
+    out[(c & 0x7F) == 0x7F] = np.nan
+    return out
+
+
 def rows(seed: int, tag: int, unit: int, n_rows: int, mu, sigma, sink: bool,
-         dtype: str = "bf16", row_start: int = 0) -> np.ndarray:
+         dtype: str = "bf16", row_start: int = 0, scale: float = 1.0) -> np.ndarray:
     """Rows row_start .. row_start+n_rows-1 of one unit.
 
-    Returns float32 [n_rows, 128] for dtype "f32" and uint16 bfloat16 bits for "bf16".
+    Returns float32 [n_rows, 128] for dtype "f32", uint16 bfloat16 bits for "bf16" and
+    uint8 E4M3 codes of x / scale (scale a power of two) for "fp8".
     """
     r = np.arange(row_start, row_start + n_rows, dtype=np.uint64)
     n = normals(seed, tag, unit, r, len(mu))
@@ -96,10 +137,17 @@ def rows(seed: int, tag: int, unit: int, n_rows: int, mu, sigma, sink: bool,
         return x.astype(np.float32)
     if dtype == "bf16":
         return f32_to_bf16_bits(x)
+    if dtype == "fp8":
+        return f32_to_fp8_e4m3(x * np.float32(1.0 / scale))
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
-def rows_as_float(seed, tag, unit, n_rows, mu, sigma, sink, dtype="bf16", row_start=0):
-    """Same rows as ``rows`` but always as float32 values (bf16 widened exactly)."""
-    r = rows(seed, tag, unit, n_rows, mu, sigma, sink, dtype, row_start)
-    return r if dtype == "f32" else bf16_bits_to_f32(r)
+def rows_as_float(seed, tag, unit, n_rows, mu, sigma, sink, dtype="bf16", row_start=0, scale=1.0):
+    """Same rows as ``rows`` but always as float32 values (bf16 widened exactly, fp8 codes
+    decoded exactly and multiplied by their scale)."""
+    r = rows(seed, tag, unit, n_rows, mu, sigma, sink, dtype, row_start, scale)
+    if dtype == "f32":
+        return r
+    if dtype == "fp8":
+        return fp8_e4m3_to_f32(r) * np.float32(scale)
+    return bf16_bits_to_f32(r)

@@ -7,7 +7,9 @@
 //   normal = (sum of twelve 16-bit fields of the hashes at n = 3c+1, 3c+2, 3c+3) - 393210,
 //            times 2^-16 (Irwin-Hall(12) - 6, exact in float32)
 //   value  = mu[col] + sigma[col] * normal, each float32 operation rounded once (no FMA),
-//            times 20 on a sink row (row 0), then RNE to bfloat16 or kept as float32
+//            times 20 on a sink row (row 0), then RNE to bfloat16, kept as float32, or
+//            (fp8) times a power-of-two inverse scale and encoded as OCP E4M3 with
+//            round-to-nearest-even, saturating at +-448
 //   counter c = unit << 27 | row << 7 | col
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -45,16 +47,49 @@ __device__ __forceinline__ uint16_t to_bf16(float x) {
   return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-// 8 consecutive columns per thread.
-template <bool BF16>
+// OCP E4M3: round to nearest even on the float32 bits; normal codes for |x| >= 2^-6,
+// subnormal steps of 2^-9 below; magnitudes rounding past 448 saturate to 448; NaN -> S.1111.111
+__device__ __forceinline__ uint32_t to_fp8_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;
+  int e = int(a >> 23) - 127;
+  uint32_t code;
+  if (e >= -6) {
+    uint32_t r = (a >> 20) & 7u;
+    const uint32_t rem = a & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
+    if (r == 8u) {
+      r = 0u;
+      ++e;
+    }
+    code = e > 8 ? 0x7Eu : ((uint32_t(e + 7) << 3) | r);
+    if (code > 0x7Eu) code = 0x7Eu;
+  } else {
+    code = uint32_t(rintf(__uint_as_float(a) * 512.0f));   // exact scaling, then RNE: 0..8
+  }
+  return sign | code;
+}
+
+// 8 consecutive columns per thread; DT 0 = float32, 1 = bfloat16, 2 = fp8 E4M3.
+template <int DT>
 __device__ __forceinline__ void write8(void* dst, uint64_t key, uint64_t unit, uint32_t row,
                                        uint32_t col0, const float* mu, const float* sigma,
-                                       bool sink_row) {
+                                       bool sink_row, float inv_scale) {
   float v[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e)
     v[e] = element(key, unit, row, col0 + e, mu[col0 + e], sigma[col0 + e], sink_row);
-  if (BF16) {
+  if (DT == 2) {
+    uint32_t c[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = to_fp8_e4m3(__fmul_rn(v[e], inv_scale));
+    uint2 w;
+    w.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    w.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    *reinterpret_cast<uint2*>(dst) = w;
+  } else if (DT == 1) {
     uint4 w;
     w.x = uint32_t(to_bf16(v[0])) | (uint32_t(to_bf16(v[1])) << 16);
     w.y = uint32_t(to_bf16(v[2])) | (uint32_t(to_bf16(v[3])) << 16);
@@ -68,12 +103,12 @@ __device__ __forceinline__ void write8(void* dst, uint64_t key, uint64_t unit, u
   }
 }
 
-template <bool BF16>
+template <int DT>
 __global__ void fill_dense_kernel(void* out, int64_t n_units, int64_t max_len, int32_t n_model_units,
                                   const float* __restrict__ mu, const float* __restrict__ sigma,
-                                  int32_t sink, uint64_t key) {
+                                  int32_t sink, uint64_t key, const float* __restrict__ inv_scale) {
   const int64_t total = n_units * max_len * 16;  // 16 groups of 8 columns per row
-  const size_t esz = BF16 ? 2 : 4;
+  const size_t esz = DT == 2 ? 1 : (DT == 1 ? 2 : 4);
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
        i += int64_t(gridDim.x) * blockDim.x) {
     const uint32_t cg = uint32_t(i & 15);
@@ -82,21 +117,22 @@ __global__ void fill_dense_kernel(void* out, int64_t n_units, int64_t max_len, i
     const int64_t unit = r / max_len;
     const float* m = mu + int64_t(unit % n_model_units) * 128;
     char* dst = static_cast<char*>(out) + (r * 128 + cg * 8) * esz;
-    write8<BF16>(dst, key, uint64_t(unit), row, cg * 8, m, sigma, sink && row == 0);
+    const float isc = inv_scale ? inv_scale[unit % n_model_units] : 1.0f;
+    write8<DT>(dst, key, uint64_t(unit), row, cg * 8, m, sigma, sink && row == 0, isc);
   }
 }
 
-template <bool BF16>
+template <int DT>
 __global__ void fill_paged_kernel(void* pool, int32_t n_seq, int32_t n_layer, int32_t n_kvh,
                                   int32_t page, int32_t max_pages,
                                   const int32_t* __restrict__ block_table,
                                   const int32_t* __restrict__ seq_len,
                                   const float* __restrict__ mu, const float* __restrict__ sigma,
-                                  int32_t sink, uint64_t key) {
+                                  int32_t sink, uint64_t key, const float* __restrict__ inv_scale) {
   // one work index per (seq, page slot, layer, head, row-in-page, column group)
   const int64_t per_page = int64_t(n_layer) * n_kvh * page * 16;
   const int64_t total = int64_t(n_seq) * max_pages * per_page;
-  const size_t esz = BF16 ? 2 : 4;
+  const size_t esz = DT == 2 ? 1 : (DT == 1 ? 2 : 4);
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
        i += int64_t(gridDim.x) * blockDim.x) {
     const uint32_t cg = uint32_t(i & 15);
@@ -115,8 +151,9 @@ __global__ void fill_paged_kernel(void* pool, int32_t n_seq, int32_t n_layer, in
     const uint64_t unit = (uint64_t(s) * n_layer + l) * n_kvh + h;
     const float* m = mu + (int64_t(l) * n_kvh + h) * 128;
     const int64_t elem = (((pg * n_layer + l) * n_kvh + h) * page + prow) * 128 + cg * 8;
-    write8<BF16>(static_cast<char*>(pool) + elem * esz, key, unit, uint32_t(slot), cg * 8, m,
-                 sigma, sink && slot == 0);
+    const float isc = inv_scale ? inv_scale[int64_t(l) * n_kvh + h] : 1.0f;
+    write8<DT>(static_cast<char*>(pool) + elem * esz, key, unit, uint32_t(slot), cg * 8, m,
+               sigma, sink && slot == 0, isc);
   }
 }
 
@@ -137,48 +174,58 @@ int grid_for(int64_t work) {
 
 extern "C" {
 
-// Fill a dense [n_units][max_len][128] cache (dtype 0 = float32, 1 = bfloat16).
+// Fill a dense [n_units][max_len][128] cache (dtype 0 = float32, 1 = bfloat16, 2 = fp8 E4M3).
 // mu: device [n_model_units][128] float32 (unit u uses row u % n_model_units);
-// sigma: device [128] float32.  Returns 0, -1 on a bad argument, -4 on a HIP error.
+// sigma: device [128] float32; inv_scale: fp8 only, device [n_model_units] float32 powers of
+// two (NULL = 1).  Returns 0, -1 on a bad argument, -4 on a HIP error.
 int tri_synth_fill_dense(void* out, int32_t dtype, int64_t n_units, int64_t max_len,
                          int32_t n_model_units, const float* mu, const float* sigma,
-                         int32_t sink, uint64_t seed, uint32_t tag, void* stream) {
+                         int32_t sink, uint64_t seed, uint32_t tag, const float* inv_scale,
+                         void* stream) {
   if (!out || !mu || !sigma || n_units <= 0 || max_len <= 0 || max_len > (1 << 20) ||
-      n_model_units <= 0 || (dtype != 0 && dtype != 1) || seed >= (1ull << 56) || tag > 255)
+      n_model_units <= 0 || dtype < 0 || dtype > 2 || seed >= (1ull << 56) || tag > 255)
     return -1;
   const uint64_t key = host_mix64((seed << 8) | tag);
   const int grid = grid_for(n_units * max_len * 16);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dtype == 1)
-    hipLaunchKernelGGL(fill_dense_kernel<true>, dim3(grid), dim3(256), 0, st, out, n_units,
-                       max_len, n_model_units, mu, sigma, sink, key);
+  if (dtype == 2)
+    hipLaunchKernelGGL(fill_dense_kernel<2>, dim3(grid), dim3(256), 0, st, out, n_units, max_len,
+                       n_model_units, mu, sigma, sink, key, inv_scale);
+  else if (dtype == 1)
+    hipLaunchKernelGGL(fill_dense_kernel<1>, dim3(grid), dim3(256), 0, st, out, n_units, max_len,
+                       n_model_units, mu, sigma, sink, key, inv_scale);
   else
-    hipLaunchKernelGGL(fill_dense_kernel<false>, dim3(grid), dim3(256), 0, st, out, n_units,
-                       max_len, n_model_units, mu, sigma, sink, key);
+    hipLaunchKernelGGL(fill_dense_kernel<0>, dim3(grid), dim3(256), 0, st, out, n_units, max_len,
+                       n_model_units, mu, sigma, sink, key, inv_scale);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 // Fill a paged pool [n_pages][n_layer][n_kvh][page][128] through per-sequence block tables
 // (device [n_seq][max_pages]) for slots < seq_len[s] (device [n_seq]).  mu: device
-// [n_layer][n_kvh][128]; unit index of (s, l, h) is (s * n_layer + l) * n_kvh + h.
+// [n_layer][n_kvh][128]; unit index of (s, l, h) is (s * n_layer + l) * n_kvh + h;
+// inv_scale: fp8 only, device [n_layer][n_kvh] (NULL = 1).
 int tri_synth_fill_paged(void* pool, int32_t dtype, int32_t n_seq, int32_t n_layer, int32_t n_kvh,
                          int32_t page, int32_t max_pages, const int32_t* block_table,
                          const int32_t* seq_len, const float* mu, const float* sigma,
-                         int32_t sink, uint64_t seed, uint32_t tag, void* stream) {
+                         int32_t sink, uint64_t seed, uint32_t tag, const float* inv_scale,
+                         void* stream) {
   if (!pool || !block_table || !seq_len || !mu || !sigma || n_seq <= 0 || n_layer <= 0 ||
       n_kvh <= 0 || page <= 0 || max_pages <= 0 || int64_t(page) * max_pages > (1 << 20) ||
-      (dtype != 0 && dtype != 1) || seed >= (1ull << 56) || tag > 255)
+      dtype < 0 || dtype > 2 || seed >= (1ull << 56) || tag > 255)
     return -1;
   const uint64_t key = host_mix64((seed << 8) | tag);
   const int64_t work = int64_t(n_seq) * max_pages * n_layer * n_kvh * page * 16;
   const int grid = grid_for(work);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dtype == 1)
-    hipLaunchKernelGGL(fill_paged_kernel<true>, dim3(grid), dim3(256), 0, st, pool, n_seq,
-                       n_layer, n_kvh, page, max_pages, block_table, seq_len, mu, sigma, sink, key);
+  if (dtype == 2)
+    hipLaunchKernelGGL(fill_paged_kernel<2>, dim3(grid), dim3(256), 0, st, pool, n_seq, n_layer, n_kvh,
+                       page, max_pages, block_table, seq_len, mu, sigma, sink, key, inv_scale);
+  else if (dtype == 1)
+    hipLaunchKernelGGL(fill_paged_kernel<1>, dim3(grid), dim3(256), 0, st, pool, n_seq, n_layer, n_kvh,
+                       page, max_pages, block_table, seq_len, mu, sigma, sink, key, inv_scale);
   else
-    hipLaunchKernelGGL(fill_paged_kernel<false>, dim3(grid), dim3(256), 0, st, pool, n_seq,
-                       n_layer, n_kvh, page, max_pages, block_table, seq_len, mu, sigma, sink, key);
+    hipLaunchKernelGGL(fill_paged_kernel<0>, dim3(grid), dim3(256), 0, st, pool, n_seq, n_layer, n_kvh,
+                       page, max_pages, block_table, seq_len, mu, sigma, sink, key, inv_scale);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

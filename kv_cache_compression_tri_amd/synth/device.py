@@ -26,10 +26,10 @@ def lib():
             raise RuntimeError(f"{SYNTH_LIB} is missing: build with python -m kv_cache_compression_tri_amd.build")
         L = ctypes.CDLL(SYNTH_LIB)
         L.tri_synth_fill_dense.argtypes = [c_void_p, c_int32, c_int64, c_int64, c_int32, c_void_p, c_void_p,
-                                           c_int32, c_uint64, c_uint32, c_void_p]
+                                           c_int32, c_uint64, c_uint32, c_void_p, c_void_p]
         L.tri_synth_fill_paged.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                                            c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_uint64, c_uint32,
-                                           c_void_p]
+                                           c_void_p, c_void_p]
         L.tri_synth_fill_dense.restype = ctypes.c_int
         L.tri_synth_fill_paged.restype = ctypes.c_int
         _LIB = L
@@ -56,37 +56,41 @@ class DeviceWorkload:
     block_table: object
     center: object
     mean_abs: object
+    k_scale: object = None     # device [n_layer, n_kvh] float32 for fp8 caches
 
     def kv(self):
         from .. import KVCache
         if self.w.paged:
-            return KVCache.paged(self.k, self.v, self.block_table, self.seq_len)
-        return KVCache.dense(self.k, self.v, self.seq_len)
+            return KVCache.paged(self.k, self.v, self.block_table, self.seq_len, k_scale=self.k_scale)
+        return KVCache.dense(self.k, self.v, self.seq_len, k_scale=self.k_scale)
 
 
 def fill(w: Workload, hp: HostParams, k, v, seq_len, block_table):
     """(Re)generate K (and V) in place from the workload's seed."""
     import torch
     dev = k.device
-    dtype_code = 1 if w.dtype == "bf16" else 0
+    dtype_code = {"f32": 0, "bf16": 1, "fp8": 2}[w.dtype]
     mu_k = torch.from_numpy(np.ascontiguousarray(hp.mu_k.reshape(-1, w.head_dim))).to(dev)
     sig_k = torch.from_numpy(hp.sigma).to(dev)
     mu_v = torch.zeros_like(mu_k)
     sig_v = torch.ones_like(sig_k)
+    inv_k = torch.from_numpy((1.0 / hp.k_scale).astype(np.float32).reshape(-1)).to(dev)
     st = _stream()
     L = lib()
-    jobs = [(k, mu_k, sig_k, int(w.sink), TAG_K)]
+    jobs = [(k, mu_k, sig_k, int(w.sink), TAG_K, inv_k)]
     if v is not None:
-        jobs.append((v, mu_v, sig_v, 0, TAG_V))
-    for t, mu, sig, sink, tag in jobs:
+        jobs.append((v, mu_v, sig_v, 0, TAG_V, None))
+    for t, mu, sig, sink, tag, inv in jobs:
+        inv_p = c_void_p(inv.data_ptr()) if inv is not None else None
         if w.paged:
             rc = L.tri_synth_fill_paged(c_void_p(t.data_ptr()), dtype_code, w.n_seq, w.n_layer, w.n_kvh, w.page,
                                         w.max_pages, c_void_p(block_table.data_ptr()), c_void_p(seq_len.data_ptr()),
-                                        c_void_p(mu.data_ptr()), c_void_p(sig.data_ptr()), sink, w.seed, tag, st)
+                                        c_void_p(mu.data_ptr()), c_void_p(sig.data_ptr()), sink, w.seed, tag, inv_p,
+                                        st)
         else:
             rc = L.tri_synth_fill_dense(c_void_p(t.data_ptr()), dtype_code, w.n_units, w.max_len,
                                         w.n_layer * w.n_kvh, c_void_p(mu.data_ptr()), c_void_p(sig.data_ptr()),
-                                        sink, w.seed, tag, st)
+                                        sink, w.seed, tag, inv_p, st)
         _check(rc, "synthetic fill")
     # keep the parameter tensors alive until the fills have run
     torch.cuda.current_stream().synchronize()
@@ -96,7 +100,7 @@ def build(w: Workload, device="cuda", hp: HostParams = None) -> DeviceWorkload:
     """Allocate and generate the workload's cache and statistics on the device."""
     import torch
     hp = hp or make_params(w)
-    tdtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    tdtype = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.float8_e4m3fn}[w.dtype]
     seq_len = torch.from_numpy(hp.lengths).to(device)
     if w.paged:
         shape = (hp.n_pages, w.n_layer, w.n_kvh, w.page, w.head_dim)
@@ -109,4 +113,5 @@ def build(w: Workload, device="cuda", hp: HostParams = None) -> DeviceWorkload:
     fill(w, hp, k, v, seq_len, block_table)
     center = torch.from_numpy(hp.center).to(device)
     mean_abs = torch.from_numpy(hp.mean_abs).to(device)
-    return DeviceWorkload(w, hp, k, v, seq_len, block_table, center, mean_abs)
+    k_scale = torch.from_numpy(hp.k_scale).to(device) if w.dtype == "fp8" else None
+    return DeviceWorkload(w, hp, k, v, seq_len, block_table, center, mean_abs, k_scale)

@@ -1,4 +1,4 @@
-"""The five synthetic workloads of the compression pass and their host-side parameters.
+"""The synthetic workloads of the compression pass and their host-side parameters.
 
 A workload fixes the cache shapes, the RoPE base, the future offsets, the budget and the
 window, and the seed from which every input is drawn.  Host parameters (key centres,
@@ -35,7 +35,7 @@ class Workload:
     n_kvh: int
     group: int
     max_len: int
-    dtype: str                 # "f32" | "bf16"
+    dtype: str                 # "f32" | "bf16" | "fp8" (OCP E4M3 codes times a per-head scale)
     base: float
     offsets: tuple
     budget: int
@@ -92,6 +92,11 @@ WORKLOADS = {
         "paged_ragged64_bf16", n_seq=64, n_layer=36, n_kvh=8, group=4, max_len=32768,
         dtype="bf16", base=1e6, offsets=geometric_offsets(12), budget=1024, window=128,
         reduce="max", seed=4, paged=True, len_range=(4096, 32768)),
+    # the 32K GQA step on an fp8 (OCP E4M3) cache with per-(layer, KV head) key scales
+    "gqa8b_32k_fp8": Workload(
+        "gqa8b_32k_fp8", n_seq=1, n_layer=36, n_kvh=8, group=4, max_len=32768,
+        dtype="fp8", base=1e6, offsets=geometric_offsets(12), budget=2048, window=128,
+        reduce="max", seed=5),
 }
 
 BENCH_WORKLOAD = "gqa8b_32k_bf16"
@@ -112,6 +117,16 @@ class HostParams:
     lengths: np.ndarray       # [n_seq] int32
     block_table: np.ndarray = field(default=None)   # [n_seq, max_pages] int32 (paged)
     n_pages: int = 0
+    k_scale: np.ndarray = field(default=None)       # [n_layer, n_kvh] float32 (fp8 keys)
+
+
+def key_scales(w) -> np.ndarray:
+    """Per-(layer, KV head) key scales of an fp8 cache: powers of two (1 and 1/2 in a
+    checkerboard), so that encoding x / scale is exact before rounding; 1 otherwise."""
+    if w.dtype != "fp8":
+        return np.ones((w.n_layer, w.n_kvh), dtype=np.float32)
+    lh = np.add.outer(np.arange(w.n_layer), np.arange(w.n_kvh))
+    return np.where(lh % 2 == 0, 1.0, 0.5).astype(np.float32)
 
 
 def make_params(w: Workload, lengths=None) -> HostParams:
@@ -157,13 +172,13 @@ def make_params(w: Workload, lengths=None) -> HostParams:
         for s in range(w.n_seq):
             bt[s, : pages_per[s]] = perm[off: off + pages_per[s]]
             off += pages_per[s]
-        return HostParams(mu_k, center, mean_abs, low, sigma, lengths, bt, n_pages)
+        return HostParams(mu_k, center, mean_abs, low, sigma, lengths, bt, n_pages, key_scales(w))
     if lengths is None:
         lengths = np.full(w.n_seq, w.max_len, dtype=np.int32)
     lengths = np.asarray(lengths, dtype=np.int32)
     if lengths.shape != (w.n_seq,) or lengths.min() < 0 or lengths.max() > w.max_len:
         raise ValueError("lengths must be n_seq values in [0, max_len]")
-    return HostParams(mu_k, center, mean_abs, low, sigma, lengths)
+    return HostParams(mu_k, center, mean_abs, low, sigma, lengths, k_scale=key_scales(w))
 
 
 def unit_index(w: Workload, s: int, layer: int, kv_head: int) -> int:

@@ -22,15 +22,29 @@ from kv_cache_compression_tri_amd.synth import workloads as W
 SCORE_TOL = 2e-3
 
 
+# numpy view of a cache element's raw bits
+BITS_VIEW = {"f32": np.int32, "bf16": np.int16, "fp8": np.uint8}
+
+
 def host_rows(w, hp, s, layer, kv_head, tag=synth.TAG_K, as_float=True):
+    """One unit's rows from the host generator: float32 values (fp8 keys decoded and
+    multiplied by their head's scale) or the raw stored elements."""
     unit = W.unit_index(w, s, layer, kv_head)
     L = int(hp.lengths[s])
+    scale = 1.0
     if tag == synth.TAG_K:
         mu, sig, sink = hp.mu_k[layer, kv_head], hp.sigma, w.sink
+        if w.dtype == "fp8":
+            scale = float(hp.k_scale[layer, kv_head])
     else:
         mu, sig, sink = np.zeros(w.head_dim, np.float32), np.ones(w.head_dim, np.float32), False
     fn = synth.rows_as_float if as_float else synth.rows
-    return fn(w.seed, tag, unit, L, mu, sig, sink, w.dtype)
+    return fn(w.seed, tag, unit, L, mu, sig, sink, w.dtype, scale=scale)
+
+
+def host_bits(w, hp, s, layer, kv_head, tag=synth.TAG_K):
+    """Raw stored elements of one unit, viewed as the integer type of the cache element."""
+    return host_rows(w, hp, s, layer, kv_head, tag, as_float=False).view(BITS_VIEW[w.dtype])
 
 
 def oracle_scores(w, hp, s, layer, kv_head, keys, key_space="pre"):

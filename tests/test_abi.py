@@ -85,6 +85,9 @@ def test_score_keys_validation():
     assert _score(c, _kv(head_dim=64))[0] == _abi.TRI_ENOTSUP
     assert _score(c, _kv(head_dim=127))[0] == _abi.TRI_EINVAL
     assert _score(c, _kv(dtype=7))[0] == _abi.TRI_EINVAL
+    assert _score(c, _kv(k_scale=FAKE.value))[0] == _abi.TRI_EINVAL          # scale needs fp8 keys
+    assert _score(c, _kv(dtype=_abi.TRI_FP8_E4M3), ws_query=True) == (_abi.TRI_OK, 0)
+    assert _score(c, _kv(dtype=_abi.TRI_FP8_E4M3, k_scale=FAKE.value), ws_query=True) == (_abi.TRI_OK, 0)
     assert _score(c, _kv(layout=5))[0] == _abi.TRI_EINVAL
     assert _score(c, _kv(n_layer=0))[0] == _abi.TRI_EINVAL
     assert _score(c, _kv(seq_len=None))[0] == _abi.TRI_EINVAL
@@ -166,6 +169,7 @@ def test_calibrate_validation():
                                      ctypes.byref(size) if ws else None, None)
     assert cal(n=0) == _abi.TRI_EINVAL
     assert cal(dtype=3) == _abi.TRI_EINVAL
+    assert cal(dtype=_abi.TRI_FP8_E4M3) == _abi.TRI_ENOTSUP                 # queries are f32 / bf16
     assert cal(layout=9) == _abi.TRI_EINVAL
     assert cal(head_dim=96) == _abi.TRI_ENOTSUP
     assert cal(q=None) == _abi.TRI_EINVAL
@@ -176,9 +180,10 @@ def test_synth_library_exports_and_rejects_bad_arguments():
     L = synth_device.lib()
     for name in synth_device.SYNTH_EXPORTS:
         assert hasattr(L, name)
-    assert L.tri_synth_fill_dense(None, 1, 1, 16, 1, FAKE, FAKE, 0, 0, 0, None) == -1
-    assert L.tri_synth_fill_dense(FAKE, 1, 1, (1 << 20) + 1, 1, FAKE, FAKE, 0, 0, 0, None) == -1
-    assert L.tri_synth_fill_paged(FAKE, 1, 1, 1, 1, 16, 0, FAKE, FAKE, FAKE, FAKE, 0, 0, 0, None) == -1
+    assert L.tri_synth_fill_dense(None, 1, 1, 16, 1, FAKE, FAKE, 0, 0, 0, None, None) == -1
+    assert L.tri_synth_fill_dense(FAKE, 1, 1, (1 << 20) + 1, 1, FAKE, FAKE, 0, 0, 0, None, None) == -1
+    assert L.tri_synth_fill_dense(FAKE, 3, 1, 16, 1, FAKE, FAKE, 0, 0, 0, None, None) == -1    # dtype
+    assert L.tri_synth_fill_paged(FAKE, 1, 1, 1, 1, 16, 0, FAKE, FAKE, FAKE, FAKE, 0, 0, 0, None, None) == -1
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

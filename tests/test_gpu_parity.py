@@ -41,6 +41,8 @@ def bits(t):
         return t.view(torch.int16).cpu().numpy()
     if t.dtype == torch.float32:
         return t.view(torch.int32).cpu().numpy()
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).cpu().numpy()
     return t.cpu().numpy()
 
 
@@ -66,15 +68,10 @@ def check_dense_unit(dw, s, l, h, sc_h, kept_h, kept_n_h, out_h):
     n = min(L, w.budget)
     assert kept_n_h[s] == n
     kk = kept_h[s, l, h, :n]
-    kbits = P.host_rows(w, hp, s, l, h, as_float=False)
-    if w.dtype == "f32":
-        kbits = kbits.view(np.int32)
-    else:
-        kbits = kbits.view(np.int16)
+    kbits = P.host_bits(w, hp, s, l, h)
     assert np.array_equal(out_h["k_out"][s, l, h, :n], kbits[kk]), "compacted K rows differ"
     if w.with_values:
-        vbits = P.host_rows(w, hp, s, l, h, tag=synth.TAG_V, as_float=False)
-        vbits = vbits.view(np.int32) if w.dtype == "f32" else vbits.view(np.int16)
+        vbits = P.host_bits(w, hp, s, l, h, tag=synth.TAG_V)
         assert np.array_equal(out_h["v_out"][s, l, h, :n], vbits[kk]), "compacted V rows differ"
     assert np.array_equal(out_h["pos_out"][s, l, h, :n], kk)
     assert out_h["new_len"][s] == n
@@ -90,7 +87,7 @@ def host_outputs(scores, kept, kept_n, out):
 # generator: device == host, bit for bit
 # ---------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8"])
 def test_device_generator_matches_host(dtype):
     w = W.scaled(W.WORKLOADS["gqa8b_32k_bf16"], n_seq=2, n_layer=2, n_kvh=2, max_len=300, dtype=dtype)
     log(f"generator dense {dtype}")
@@ -99,11 +96,8 @@ def test_device_generator_matches_host(dtype):
     for s in range(2):
         for l in range(2):
             for h in range(2):
-                hk = P.host_rows(w, dw.hp, s, l, h, as_float=False)
-                hv = P.host_rows(w, dw.hp, s, l, h, tag=synth.TAG_V, as_float=False)
-                view = np.int32 if dtype == "f32" else np.int16
-                assert np.array_equal(kb[s, l, h], hk.view(view))
-                assert np.array_equal(vb[s, l, h], hv.view(view))
+                assert np.array_equal(kb[s, l, h], P.host_bits(w, dw.hp, s, l, h))
+                assert np.array_equal(vb[s, l, h], P.host_bits(w, dw.hp, s, l, h, tag=synth.TAG_V))
     wp = W.scaled(W.WORKLOADS["paged_ragged64_bf16"], n_seq=3, n_layer=2, n_kvh=2, max_len=700,
                   len_range=(10, 700), dtype=dtype)
     log(f"generator paged {dtype}")
@@ -114,10 +108,8 @@ def test_device_generator_matches_host(dtype):
         L = int(dp.hp.lengths[s])
         for l in range(2):
             for h in range(2):
-                hk = P.host_rows(wp, dp.hp, s, l, h, as_float=False)
-                view = np.int32 if dtype == "f32" else np.int16
                 got = np.stack([pk[bt[s, j // 16], l, h, j % 16] for j in range(L)])
-                assert np.array_equal(got, hk.view(view))
+                assert np.array_equal(got, P.host_bits(wp, dp.hp, s, l, h))
 
 
 # ---------------------------------------------------------------------------------------
@@ -145,6 +137,14 @@ SMALL_DENSE = {
     # empty sequences between non-empty ones: the score grid divides only real keys
     "g4_max_half_bf16_empty_seqs": (dict(n_seq=5, n_layer=2, n_kvh=2, group=4, max_len=2600, budget=300,
                                          window=32), [0, 2600, 0, 0, 1031]),
+    # fp8 (OCP E4M3) keys with per-(layer, KV head) scales 1 and 1/2
+    "g4_max_half_fp8": (dict(n_seq=2, n_layer=2, n_kvh=2, group=4, dtype="fp8", max_len=2600, budget=500,
+                             window=32), [2600, 1111]),
+    "g8_max_interleaved_fp8": (dict(n_seq=1, n_layer=1, n_kvh=2, group=8, dtype="fp8", layout="interleaved",
+                                    max_len=1300, budget=200, window=16), [1300]),
+    "g2_mean_half_fp8_wide": (dict(n_seq=2, n_layer=1, n_kvh=3, group=2, dtype="fp8", reduce="mean",
+                                   max_len=1100, budget=1024, window=8, sigma_low=0.01, sigma_high=2.0),
+                              [1100, 57]),
 }
 
 
@@ -174,6 +174,8 @@ def test_small_dense_parity(name):
     ([3000, 17, 4096, 900], "post", {}),
     ([2222, 4000, 1, 513], "pre", dict(dtype="f32", layout="interleaved", group=2)),
     ([700, 4100, 1500, 33], "post", dict(layout="interleaved", group=3, reduce="mean")),
+    ([3000, 17, 4096, 900], "pre", dict(dtype="fp8")),
+    ([1200, 4111, 64, 2000], "post", dict(dtype="fp8", layout="interleaved", group=5)),
 ])
 def test_small_paged_parity(lengths, key_space, extra):
     w = W.scaled(W.WORKLOADS["paged_ragged64_bf16"], n_seq=4, n_layer=2, n_kvh=2, max_len=5120,
@@ -358,8 +360,7 @@ def _full_dense(name, units, key_space="pre"):
     # the generator itself: device K rows of the sampled units equal the host rows
     for u in units[:2]:
         s, l, h = W.unit_coords(w, u)
-        hk = P.host_rows(w, dw.hp, s, l, h, as_float=False)
-        assert np.array_equal(bits(dw.k[s, l, h]), hk.view(np.int32 if w.dtype == "f32" else np.int16))
+        assert np.array_equal(bits(dw.k[s, l, h]), P.host_bits(w, dw.hp, s, l, h))
     log(f"  max score error / bound = {worst:.3e}")
 
 
@@ -373,10 +374,9 @@ def _check_sampled(dw, s, l, h, sc_h, kp_h, kn_h, o, key_space="pre"):
     n = min(L, w.budget)
     assert kn_h[0] == n and o["new_len"][0] == n
     kk = kp_h[0, 0, 0, :n]
-    view = np.int32 if w.dtype == "f32" else np.int16
-    assert np.array_equal(o["k_out"][0, 0, 0, :n], P.host_rows(w, hp, s, l, h, as_float=False).view(view)[kk])
+    assert np.array_equal(o["k_out"][0, 0, 0, :n], P.host_bits(w, hp, s, l, h)[kk])
     if o["v_out"] is not None:
-        hv = P.host_rows(w, hp, s, l, h, tag=synth.TAG_V, as_float=False).view(view)
+        hv = P.host_bits(w, hp, s, l, h, tag=synth.TAG_V)
         assert np.array_equal(o["v_out"][0, 0, 0, :n], hv[kk])
     assert np.array_equal(o["pos_out"][0, 0, 0, :n], kk)
     return worst
@@ -560,18 +560,19 @@ def test_zero_duplicated_and_nan_key_rows():
 # ---------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype,layout,group,reduce", [("bf16", "half", 4, "max"), ("f32", "interleaved", 3, "mean"),
-                                                       ("bf16", "interleaved", 7, "max")])
+                                                       ("bf16", "interleaved", 7, "max"), ("fp8", "half", 4, "max")])
 def test_post_rope_small_dense(dtype, layout, group, reduce):
     # a post-RoPE cache built on the host: the generator's keys rotated by RoPE at their
-    # slots in float64 (the oracle's rotation), then stored in the cache dtype
+    # slots in float64 (the oracle's rotation), then stored in the cache dtype (fp8: the
+    # codes of key / scale, with the head's power-of-two scale)
     w = W.scaled(BASE, name="post_rope", n_seq=2, n_layer=2, n_kvh=2, group=group, reduce=reduce, dtype=dtype,
                  layout=layout, max_len=2600, budget=500, window=32)
     lengths = [2600, 1111]
     hp = W.make_params(w, lengths=lengths)
     log(f"post-RoPE small dense {dtype} {layout} G={group} {reduce}")
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.float8_e4m3fn}[dtype]
     k = torch.zeros((2, 2, 2, w.max_len, 128), dtype=tdt)
-    cached = {}
+    cached, stored = {}, {}
     for s in range(2):
         L = lengths[s]
         for l in range(2):
@@ -579,20 +580,26 @@ def test_post_rope_small_dense(dtype, layout, group, reduce):
                 pre = P.host_rows(w, hp, s, l, h)
                 post = oracle.rope_apply(pre, np.arange(L), base=w.base, layout=layout).astype(np.float32)
                 if dtype == "bf16":
-                    b = synth.f32_to_bf16_bits(post)
-                    cached[(s, l, h)] = synth.bf16_bits_to_f32(b)
-                    k[s, l, h, :L] = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16)
+                    raw = synth.f32_to_bf16_bits(post).view(np.int16)
+                    cached[(s, l, h)] = synth.bf16_bits_to_f32(raw.view(np.uint16))
+                elif dtype == "fp8":
+                    sc_lh = np.float32(hp.k_scale[l, h])
+                    raw = synth.f32_to_fp8_e4m3(post / sc_lh)
+                    cached[(s, l, h)] = synth.fp8_e4m3_to_f32(raw) * sc_lh
                 else:
+                    raw = post.view(np.int32)
                     cached[(s, l, h)] = post
-                    k[s, l, h, :L] = torch.from_numpy(post)
+                stored[(s, l, h)] = raw
+                k[s, l, h, :L] = torch.from_numpy(raw.copy()).view(tdt)
     k = k.cuda()
-    kv = tri.KVCache.dense(k, None, torch.tensor(lengths, dtype=torch.int32, device="cuda"))
+    k_scale = torch.from_numpy(hp.k_scale).cuda() if dtype == "fp8" else None
+    kv = tri.KVCache.dense(k, None, torch.tensor(lengths, dtype=torch.int32, device="cuda"), k_scale=k_scale)
     center, mean_abs = torch.from_numpy(hp.center).cuda(), torch.from_numpy(hp.mean_abs).cuda()
     out = tri.compress(kv, center, mean_abs, rope_base=w.base, offsets=w.offsets, group=group, budget=w.budget,
                        window=w.window, reduce=reduce, rope_layout=layout, key_space="post")
     torch.cuda.synchronize()
     sc, kp, kn = out["scores"].cpu().numpy(), out["kept"].cpu().numpy(), out["kept_n"].cpu().numpy()
-    ko = out["k_out"].cpu().float().numpy()
+    ko = bits(out["k_out"])
     worst = 0.0
     for (s, l, h), keys in cached.items():
         L = lengths[s]
@@ -602,7 +609,7 @@ def test_post_rope_small_dense(dtype, layout, group, reduce):
         P.check_kept(kp[s, l, h], sc[s, l, h], orc, S, L, w.budget, w.window)
         n = min(L, w.budget)
         assert kn[s] == n
-        assert np.array_equal(ko[s, l, h, :n], keys[kp[s, l, h, :n]])
+        assert np.array_equal(ko[s, l, h, :n], stored[(s, l, h)][kp[s, l, h, :n]])
     log(f"  max score error / bound = {worst:.3e}")
 
 
@@ -613,6 +620,14 @@ def test_full_gqa8b_32k_bf16_post_rope():
     rng = np.random.default_rng(105)
     units = [0, w.n_units - 1] + _low_r_units(w, hp, 1) + [int(x) for x in rng.choice(w.n_units, 1, replace=False)]
     _full_dense("gqa8b_32k_bf16", units, key_space="post")
+
+
+def test_full_gqa8b_32k_fp8():
+    w = W.WORKLOADS["gqa8b_32k_fp8"]
+    hp = W.make_params(w)
+    rng = np.random.default_rng(106)
+    units = [0, 1, w.n_units - 1] + _low_r_units(w, hp, 1) + [int(x) for x in rng.choice(w.n_units, 2, replace=False)]
+    _full_dense("gqa8b_32k_fp8", units)
 
 
 # ---------------------------------------------------------------------------------------

@@ -97,3 +97,67 @@ def test_heteroscedastic_sigma_by_band():
     s = W.make_params(w).sigma
     assert np.all(s[:32] == np.float32(0.1)) and np.all(s[64:96] == np.float32(0.1))
     assert np.all(s[32:64] == np.float32(1.0)) and np.all(s[96:] == np.float32(1.0))
+
+
+# ---------------------------------------------------------------------------------------
+# fp8 (OCP E4M3) encoding of the generator
+# ---------------------------------------------------------------------------------------
+
+def _fp8_nearest_even(x):
+    """Brute force: the finite E4M3 value nearest to x (ties to the even code), or the
+    saturated code when |x| rounds past 448."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = synth.fp8_e4m3_to_f32(codes).astype(np.float64)
+    out = []
+    for v in np.asarray(x, dtype=np.float64):
+        if abs(v) >= 464.0:                     # past the midpoint of 448 and 480
+            out.append(0x7E | (0x80 if v < 0 else 0))
+            continue
+        d = np.abs(vals - v)
+        best = np.nonzero(d == d.min())[0]
+        cand = codes[best]
+        if len(cand) > 1:
+            # +0 and -0 tie for zero: the sign of x decides; otherwise the even mantissa wins
+            same_sign = [c for c in cand if ((c & 0x80) != 0) == (np.signbit(v))]
+            cand = same_sign or list(cand)
+            even = [c for c in cand if (c & 1) == 0]
+            cand = even or cand
+        out.append(int(cand[0]))
+    return np.array(out, dtype=np.uint8)
+
+
+def test_fp8_encoder_is_round_to_nearest_even():
+    rng = np.random.default_rng(31)
+    x = np.concatenate([
+        rng.standard_normal(3000) * 10.0,
+        rng.standard_normal(1000) * 2.0 ** -7,                 # subnormal range
+        np.exp(rng.uniform(-12, 6.5, 2000)) * rng.choice([-1, 1], 2000),
+    ]).astype(np.float32)
+    assert np.array_equal(synth.f32_to_fp8_e4m3(x), _fp8_nearest_even(x))
+
+
+def test_fp8_encoder_ties_saturation_and_specials():
+    enc = lambda v: int(synth.f32_to_fp8_e4m3(np.float32([v]))[0])
+    assert enc(1.0625) == 0x38 and enc(1.1875) == 0x3A          # ties go to the even mantissa
+    assert enc(2.0 ** -10) == 0x00 and enc(3 * 2.0 ** -10) == 0x02   # subnormal ties
+    assert enc(7.5 * 2.0 ** -9) == 0x08                          # rounds up into the normals
+    assert enc(448.0) == 0x7E and enc(463.9) == 0x7E and enc(464.0) == 0x7E and enc(1e9) == 0x7E
+    assert enc(float("inf")) == 0x7E and enc(-float("inf")) == 0xFE
+    assert enc(float("nan")) & 0x7F == 0x7F
+    assert enc(-0.0) == 0x80 and enc(0.0) == 0x00
+
+
+def test_fp8_rows_are_codes_of_scaled_values():
+    w = W.scaled(W.WORKLOADS["gqa8b_32k_bf16"], dtype="fp8", n_layer=2, n_kvh=2, max_len=64)
+    hp = W.make_params(w)
+    assert set(np.unique(hp.k_scale)) == {0.5, 1.0}
+    for l in range(2):
+        for h in range(2):
+            unit = W.unit_index(w, 0, l, h)
+            sc = float(hp.k_scale[l, h])
+            codes = synth.rows(w.seed, synth.TAG_K, unit, 64, hp.mu_k[l, h], hp.sigma, True, "fp8", scale=sc)
+            x = synth.rows(w.seed, synth.TAG_K, unit, 64, hp.mu_k[l, h], hp.sigma, True, "f32")
+            assert codes.dtype == np.uint8
+            assert np.array_equal(codes, synth.f32_to_fp8_e4m3(x / np.float32(sc)))
+            vals = synth.rows_as_float(w.seed, synth.TAG_K, unit, 64, hp.mu_k[l, h], hp.sigma, True, "fp8", scale=sc)
+            assert np.array_equal(vals, synth.fp8_e4m3_to_f32(codes) * np.float32(sc))
