@@ -13,7 +13,8 @@ torch.cuda.synchronize().
 
 Prints one JSON line with the metric (keys scored+selected+compacted per second), the
 roofline of the dominant kernel (scoring: algorithmic bytes = one key row per key read,
-256 B for bf16, 128 B for fp8, 512 B for float32, over its average HIP-event duration) and the CPU oracle timed on a bounded sample of units.
+256 B for bf16, 128 B for fp8 and int8, 512 B for float32, over its average HIP-event
+duration) and the CPU oracle timed on a bounded sample of units.
 """
 
 from __future__ import annotations
@@ -266,7 +267,7 @@ def main():
     score_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
     select_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
     compact_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
-    elt = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
+    elt = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}[w.dtype]
     score_bytes = keys_per_step * w.head_dim * elt                       # every key read once
     kept_rows = w.n_layer * w.n_kvh * sum(min(w.budget, L) for L in lengths)
     compact_bytes = kept_rows * w.head_dim * elt * 2 * 2 if compacts else 0   # K and V, read + write

@@ -37,8 +37,8 @@
  *     the call runs without workspace and fails with TRI_EWORKSPACE if it needs one.
  *   - Return values are tri_status codes; tri_last_error() gives the text of the last
  *     failure on the calling thread.
- *   - Supported set: head_dim == 128 (F = 64 RoPE bands), dtype TRI_F32, TRI_BF16 or
- *     TRI_FP8_E4M3 (tri_calibrate_stats: TRI_F32 or TRI_BF16), page
+ *   - Supported set: head_dim == 128 (F = 64 RoPE bands), dtype TRI_F32, TRI_BF16,
+ *     TRI_FP8_E4M3 or TRI_INT8 (tri_calibrate_stats: TRI_F32 or TRI_BF16), page
  *     size 16, group (query heads per KV head) 1..8, up to 64 future offsets, per-unit
  *     length up to 1,048,576 keys.  Other valid values return TRI_ENOTSUP.
  */
@@ -60,12 +60,14 @@ typedef enum tri_status {
   TRI_EHIP = -4        /* HIP launch or runtime error                  */
 } tri_status;
 
-/* Element type of k and v.  TRI_FP8_E4M3 is the OCP 8-bit float E4M3 (1 sign bit, 4
- * exponent bits with bias 7, 3 mantissa bits, subnormals, no infinities, S.1111.111 = NaN,
- * largest finite 448), one byte per element; it lets the pass run on a quantised KV cache
+/* Element type of k and v.  The two 8-bit types let the pass run on a quantised KV cache
  * ([Project] "The same compression idea now runs on four different backends": the method
- * composes with KV quantisation).  The key codes may carry a scale (tri_kv.k_scale). */
-typedef enum tri_dtype { TRI_F32 = 0, TRI_BF16 = 1, TRI_FP8_E4M3 = 2 } tri_dtype;
+ * composes with KV quantisation); their key codes may carry a scale (tri_kv.k_scale).
+ *   TRI_FP8_E4M3: the OCP 8-bit float E4M3 (1 sign bit, 4 exponent bits with bias 7, 3
+ *                 mantissa bits, subnormals, no infinities, S.1111.111 = NaN, largest
+ *                 finite 448), one byte per element.
+ *   TRI_INT8:     two's-complement signed bytes (symmetric quantisation: value = code). */
+typedef enum tri_dtype { TRI_F32 = 0, TRI_BF16 = 1, TRI_FP8_E4M3 = 2, TRI_INT8 = 3 } tri_dtype;
 
 /* Pairing of the RoPE frequency bands inside a head vector x[0..d):
  *   TRI_ROPE_HALF:        band f = (x[f], x[f + d/2])   (rotate-half pairing)
@@ -99,8 +101,8 @@ typedef enum tri_key_space { TRI_KEYS_PRE_ROPE = 0, TRI_KEYS_POST_ROPE = 1 } tri
  *            keys (slots = max_len dense, max_pages * page paged); NULL means the position
  *            of slot j is j.  tri_score_keys supports only pos == NULL (TRI_ENOTSUP
  *            otherwise); tri_compact_kv gathers pos when given.
- *   k_scale: optional device [n_layer][n_kvh] float32, dtype TRI_FP8_E4M3 only (must be
- *            NULL otherwise): the key of head (l, h) is its decoded code times
+ *   k_scale: optional device [n_layer][n_kvh] float32, dtype TRI_FP8_E4M3 or TRI_INT8 only
+ *            (must be NULL otherwise): the key of head (l, h) is its decoded code times
  *            k_scale[l * n_kvh + h] (NULL = 1).  Scores are computed from the scaled keys;
  *            compaction copies codes unchanged, so the scale still applies to k_out.
  *            Values must be finite and > 0. */
@@ -119,7 +121,7 @@ typedef struct tri_kv {
   int32_t max_pages;
   const int32_t *block_table;
   const int32_t *pos;
-  const float *k_scale;   /* TRI_FP8_E4M3 only, optional: [n_layer][n_kvh] float32 */
+  const float *k_scale;   /* 8-bit dtypes only, optional: [n_layer][n_kvh] float32 */
 } tri_kv;
 
 /* Scoring configuration.
@@ -217,7 +219,7 @@ const char *tri_last_error(void);
 /* ABI version of this header: major * 10000 + minor * 100 + patch. */
 int tri_version(void);
 
-#define TRI_VERSION 10200
+#define TRI_VERSION 10300
 
 #ifdef __cplusplus
 }

@@ -48,7 +48,9 @@ def _dtype_code(t) -> int:
         return _abi.TRI_F32
     if t.dtype == torch.float8_e4m3fn:
         return _abi.TRI_FP8_E4M3
-    raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16 or float8_e4m3fn)")
+    if t.dtype == torch.int8:
+        return _abi.TRI_INT8
+    raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16, float8_e4m3fn or int8)")
 
 
 def _dev(t, name, dtype=None):
@@ -90,8 +92,8 @@ class KVCache:
            [n_seq, max_pages] (int32) mapping slot j of sequence s to page
            block_table[s, j // page], row j % page
     seq_len: int32 [n_seq] on the device; pos: optional int32 RoPE positions
-    k_scale: fp8 (torch.float8_e4m3fn, OCP E4M3) caches only, optional float32
-             [n_layer, n_kvh]: key = decoded code * k_scale[l, h]
+    k_scale: 8-bit caches only (torch.float8_e4m3fn = OCP E4M3, or torch.int8), optional
+             float32 [n_layer, n_kvh]: key = decoded code * k_scale[l, h]
     """
 
     k: object
@@ -139,8 +141,8 @@ class KVCache:
         d.v = None if self.v is None else self.v.data_ptr()
         d.pos = None if self.pos is None else self.pos.data_ptr()
         if self.k_scale is not None:
-            if d.dtype != _abi.TRI_FP8_E4M3:
-                raise ValueError("k_scale is only valid with float8_e4m3fn keys")
+            if d.dtype not in (_abi.TRI_FP8_E4M3, _abi.TRI_INT8):
+                raise ValueError("k_scale is only valid with 8-bit (float8_e4m3fn or int8) keys")
             _dev(self.k_scale, "k_scale", torch.float32)
             _shape(self.k_scale, "k_scale", (d.n_layer, d.n_kvh))
             d.k_scale = self.k_scale.data_ptr()

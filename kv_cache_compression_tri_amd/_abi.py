@@ -10,7 +10,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "lib", "libtri.so")
 
 TRI_OK, TRI_EINVAL, TRI_ENOTSUP, TRI_EWORKSPACE, TRI_EHIP = 0, -1, -2, -3, -4
-TRI_F32, TRI_BF16, TRI_FP8_E4M3 = 0, 1, 2
+TRI_F32, TRI_BF16, TRI_FP8_E4M3, TRI_INT8 = 0, 1, 2, 3
 TRI_ROPE_HALF, TRI_ROPE_INTERLEAVED = 0, 1
 TRI_REDUCE_MAX, TRI_REDUCE_MEAN = 0, 1
 TRI_DENSE, TRI_PAGED = 0, 1

@@ -22,7 +22,7 @@ ARCH = os.environ.get("TRI_OFFLOAD_ARCH", "gfx950")
 LIBS = {
     "libtri.so": {
         "dir": os.path.join(PKG, "csrc"),
-        "sources": ["api.hip", "score.hip", "score_post.hip", "score_fp8.hip", "score_post_fp8.hip",
+        "sources": ["api.hip", "score.hip", "score_post.hip", "score_8bit.hip", "score_post_8bit.hip",
                     "select.hip", "compact.hip", "calib.hip"],
         "includes": [os.path.join(ROOT, "include"), os.path.join(PKG, "csrc")],
     },

@@ -59,9 +59,10 @@ int check_dims(int32_t head_dim) {
 int check_kv(const tri_kv* kv, bool need_k) {
   if (!kv) return fail(TRI_EINVAL, "kv descriptor is NULL");
   if (kv->layout != TRI_DENSE && kv->layout != TRI_PAGED) return fail(TRI_EINVAL, "unknown kv layout %d", kv->layout);
-  if (kv->dtype != TRI_F32 && kv->dtype != TRI_BF16 && kv->dtype != TRI_FP8_E4M3)
+  if (kv->dtype != TRI_F32 && kv->dtype != TRI_BF16 && kv->dtype != TRI_FP8_E4M3 && kv->dtype != TRI_INT8)
     return fail(TRI_EINVAL, "unknown dtype %d", kv->dtype);
-  if (kv->k_scale && kv->dtype != TRI_FP8_E4M3) return fail(TRI_EINVAL, "k_scale is only valid with fp8 keys");
+  if (kv->k_scale && kv->dtype != TRI_FP8_E4M3 && kv->dtype != TRI_INT8)
+    return fail(TRI_EINVAL, "k_scale is only valid with 8-bit keys");
   if (kv->n_seq < 1 || kv->n_layer < 1 || kv->n_kvh < 1)
     return fail(TRI_EINVAL, "n_seq, n_layer and n_kvh must be >= 1");
   if (int rc = check_dims(kv->head_dim)) return rc;
@@ -108,7 +109,8 @@ int tri_calibrate_stats(const void* q, int32_t dtype, int64_t n, int32_t n_layer
   try {
     g_error.clear();
     if (!q || !center || !mean_abs) return fail(TRI_EINVAL, "q, center and mean_abs must be non-NULL");
-    if (dtype == TRI_FP8_E4M3) return fail(TRI_ENOTSUP, "calibration takes float32 or bfloat16 queries");
+    if (dtype == TRI_FP8_E4M3 || dtype == TRI_INT8)
+      return fail(TRI_ENOTSUP, "calibration takes float32 or bfloat16 queries");
     if (dtype != TRI_F32 && dtype != TRI_BF16) return fail(TRI_EINVAL, "unknown dtype %d", dtype);
     if (rope_layout != TRI_ROPE_HALF && rope_layout != TRI_ROPE_INTERLEAVED)
       return fail(TRI_EINVAL, "unknown rope layout %d", rope_layout);

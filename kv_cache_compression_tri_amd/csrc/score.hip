@@ -6,9 +6,9 @@ namespace tri {
 
 hipError_t launch_score(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
                         bool post, int grid, hipStream_t stream) {
-  if (dtype == 2)
-    return post ? launch_score_post_fp8(p, G_eff, interleaved, paged, grid, stream)
-                : launch_score_fp8(p, G_eff, interleaved, paged, grid, stream);
+  if (dtype >= 2)
+    return post ? launch_score_post_8bit(p, G_eff, dtype, interleaved, paged, grid, stream)
+                : launch_score_8bit(p, G_eff, dtype, interleaved, paged, grid, stream);
   if (post) return launch_score_post(p, G_eff, dtype, interleaved, paged, grid, stream);
   return dtype == 1 ? launch_groups<1, false>(p, G_eff, interleaved, paged, grid, stream)
                     : launch_groups<0, false>(p, G_eff, interleaved, paged, grid, stream);

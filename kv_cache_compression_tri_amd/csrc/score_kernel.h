@@ -1,6 +1,7 @@
 // Key-scoring kernel of the TriAttention compression pass (gfx950), shared by the
 // translation units that instantiate it (score.hip / score_post.hip: pre-RoPE keys / keys
-// cached after RoPE, float32 or bfloat16; score_fp8.hip / score_post_fp8.hip: fp8 codes).
+// cached after RoPE, float32 or bfloat16; score_8bit.hip / score_post_8bit.hip: fp8 and
+// int8 codes).
 //
 // What it computes (per unit = sequence s, layer l, KV head h; key slot j at position p_j;
 // query heads hq of the group with centre c_f = E[q_f] and m_f = E|q_f|):
@@ -25,9 +26,9 @@
 // an LDS table built in float64 and rounded once to float32.  Large phases never go through
 // a float32 sin/cos.  At each chunk boundary the weights rotate by e^{-i kChunk theta_f}.
 // For the mean reduction W and N are averaged over the group first (both terms are linear
-// in them).  bf16 keys are widened exactly to float32 (one shift or mask per element) and
-// fp8 (OCP E4M3) codes are converted exactly, two per instruction; all arithmetic is
-// float32.  A per-(layer, KV head) key scale (stored key = true key / scale) multiplies W
+// in them).  bf16 keys are widened exactly to float32 (one shift or mask per element),
+// fp8 (OCP E4M3) codes are converted exactly, two per instruction, and int8 codes one per
+// instruction; all arithmetic is float32.  A per-(layer, KV head) key scale (stored key = true key / scale) multiplies W
 // and N once per segment, since both terms are linear in the key.
 //
 // Mapping: 8 lanes per key; lane g of a key owns bands 8g..8g+7, so the 8 lanes of a key
@@ -55,8 +56,9 @@ namespace {
 // do not pass through the vector memory counter that tracks the key stream).
 typedef __attribute__((address_space(4))) const int32_t* const_i32_ptr;
 
-// Element types of the key cache: DT 0 = float32, 1 = bfloat16, 2 = fp8 (OCP E4M3 codes).
-// A step fragment holds a lane's 8 bands of one key: 64 B (f32), 32 B (bf16), 16 B (fp8).
+// Element types of the key cache: DT 0 = float32, 1 = bfloat16, 2 = fp8 (OCP E4M3 codes),
+// 3 = int8.  A step fragment holds a lane's 8 bands of one key: 64 B (f32), 32 B (bf16),
+// 16 B (8-bit).
 template <int DT>
 struct Frag {
   uint4 d[DT == 0 ? 4 : (DT == 1 ? 2 : 1)];
@@ -69,9 +71,21 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // (re, im) of band b (0..7) of the lane's fragment.
+// Signed byte i (0..3) of a word as float32 (exact; one SDWA conversion).
+__device__ __forceinline__ float i8_at(uint32_t w, int i) { return float(int8_t(w >> (8 * i))); }
+
 template <int DT, bool IL>
 __device__ __forceinline__ void band_of(const Frag<DT>& fr, int b, float& re, float& im) {
-  if constexpr (DT == 2) {
+  if constexpr (DT == 3) {
+    if constexpr (IL) {       // bytes (re_b, im_b) sit next to each other
+      const uint32_t w = word(fr.d[0], b >> 1);
+      re = i8_at(w, 2 * (b & 1));
+      im = i8_at(w, 2 * (b & 1) + 1);
+    } else {                  // re codes in words x, y; im codes in words z, w
+      re = i8_at(word(fr.d[0], b >> 2), b & 3);
+      im = i8_at(word(fr.d[0], 2 + (b >> 2)), b & 3);
+    }
+  } else if constexpr (DT == 2) {
     // exact E4M3 -> float32 conversion of two codes at a time (bytes 0,1 or 2,3 of a word;
     // b is a constant once the band loop is unrolled, so each branch folds away)
     if constexpr (IL) {       // bytes (re_b, im_b) sit next to each other
@@ -151,6 +165,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
   constexpr int STEPS = kChunk / 8;            // 8 keys per wave step
   constexpr int PF = GE <= 4 ? 4 : 2;          // steps of loads in flight
   constexpr int ESZ = DT == 0 ? 4 : (DT == 1 ? 2 : 1);
+  constexpr bool B8 = DT >= 2;                 // one byte per element
   constexpr int ROW = kHeadDim * ESZ;
   static_assert(STEPS % PF == 0 && STEPS % 8 == 0, "chunk geometry");
 
@@ -190,7 +205,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
   const int n_qh = P.n_kvh * P.group;
   // per-lane constant byte offsets of the lane's pieces inside a step's 8 rows
   uint32_t off[DT == 0 ? 4 : 2];
-  if constexpr (DT == 2) {
+  if constexpr (B8) {
     off[0] = kk * ROW + (IL ? g * 16 : g * 8);          // interleaved: one 16-byte piece
     off[1] = kk * ROW + 64 + g * 8;                      // half: re codes, then im codes
   } else if constexpr (DT == 1) {
@@ -288,11 +303,11 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
       }
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, min(8, nkeys - 8 * n) * ROW, 0x00020000);
-      if constexpr (DT == 2 && !IL) {
+      if constexpr (B8 && !IL) {
         const uint2 re = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off[0], 0, 0));
         const uint2 im = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off[1], 0, 0));
         fr.d[0] = make_uint4(re.x, re.y, im.x, im.y);
-      } else if constexpr (DT == 2) {
+      } else if constexpr (B8) {
         fr.d[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[0], 0, 0));
       } else {
 #pragma unroll

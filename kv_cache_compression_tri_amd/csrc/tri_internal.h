@@ -28,7 +28,7 @@ struct ScoreParams {
   const int32_t* block_table;
   const float* center;       // [n_layer][n_qh][64][2]
   const float* mean_abs;     // [n_layer][n_qh][64]
-  const float* k_scale;      // optional [n_layer][n_kvh]: true key = stored key * scale
+  const float* k_scale;      // optional [n_layer][n_kvh] (8-bit keys): key = code * scale
   float* scores;
   int64_t max_len;           // dense token stride
   int64_t score_stride;      // slots per unit in `scores`
@@ -85,10 +85,10 @@ hipError_t launch_score(const ScoreParams& p, int G_eff, int dtype, bool interle
                         bool post, int grid, hipStream_t stream);
 hipError_t launch_score_post(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
                              int grid, hipStream_t stream);
-hipError_t launch_score_fp8(const ScoreParams& p, int G_eff, bool interleaved, bool paged, int grid,
-                            hipStream_t stream);
-hipError_t launch_score_post_fp8(const ScoreParams& p, int G_eff, bool interleaved, bool paged, int grid,
-                                 hipStream_t stream);
+hipError_t launch_score_8bit(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
+                             int grid, hipStream_t stream);
+hipError_t launch_score_post_8bit(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
+                                  int grid, hipStream_t stream);
 hipError_t launch_select(const SelectParams& p, int64_t n_units, hipStream_t stream);
 hipError_t launch_compact(const CompactParams& p, int64_t n_units, int elem_bytes, bool paged,
                           bool with_v, hipStream_t stream);

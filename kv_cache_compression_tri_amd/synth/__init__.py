@@ -13,8 +13,9 @@ here in numpy (host, for the oracle's inputs and small cases) and in ``csrc/synt
           2^-16, so it is exact in float32.
 * value:  ``x = mu[col] + sigma[col] * n`` in float32 with each operation rounded once
           (no fused multiply-add), times 20 on a sink row, then rounded to bfloat16 with
-          round-to-nearest-even, kept as float32, or (fp8) multiplied by a power-of-two
-          inverse scale and encoded as OCP E4M3 (round to nearest even, saturating at 448).
+          round-to-nearest-even, kept as float32, or (fp8, int8) multiplied by a power-of-two
+          inverse scale and encoded as OCP E4M3 (round to nearest even, saturating at 448)
+          or as int8 (round to nearest even, clamped to [-127, 127]).
 
 Element (unit, row, col) of stream ``tag`` under ``seed`` uses counter
 ``c = unit << 27 | row << 7 | col`` (row < 2^20, col < 128) and the three hashes at
@@ -104,6 +105,12 @@ def f32_to_fp8_e4m3(x) -> np.ndarray:
     return (sign | code).astype(np.uint8)
 
 
+def f32_to_int8(x) -> np.ndarray:
+    """Symmetric int8 codes of float32 values: round to nearest even, clamp to [-127, 127]."""
+    x = np.asarray(x, dtype=np.float32)
+    return np.clip(np.rint(x), -127, 127).astype(np.int8)
+
+
 def fp8_e4m3_to_f32(c) -> np.ndarray:
     """Exact float32 values of OCP E4M3 codes (built from their bit fields)."""
     c = np.asarray(c, dtype=np.uint8).astype(np.uint32)
@@ -123,8 +130,9 @@ def rows(seed: int, tag: int, unit: int, n_rows: int, mu, sigma, sink: bool,
          dtype: str = "bf16", row_start: int = 0, scale: float = 1.0) -> np.ndarray:
     """Rows row_start .. row_start+n_rows-1 of one unit.
 
-    Returns float32 [n_rows, 128] for dtype "f32", uint16 bfloat16 bits for "bf16" and
-    uint8 E4M3 codes of x / scale (scale a power of two) for "fp8".
+    Returns float32 [n_rows, 128] for dtype "f32", uint16 bfloat16 bits for "bf16",
+    uint8 E4M3 codes of x / scale for "fp8" and int8 codes of x / scale for "int8" (scale a
+    power of two, so x / scale is exact before rounding).
     """
     r = np.arange(row_start, row_start + n_rows, dtype=np.uint64)
     n = normals(seed, tag, unit, r, len(mu))
@@ -139,15 +147,19 @@ def rows(seed: int, tag: int, unit: int, n_rows: int, mu, sigma, sink: bool,
         return f32_to_bf16_bits(x)
     if dtype == "fp8":
         return f32_to_fp8_e4m3(x * np.float32(1.0 / scale))
+    if dtype == "int8":
+        return f32_to_int8(x * np.float32(1.0 / scale))
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
 def rows_as_float(seed, tag, unit, n_rows, mu, sigma, sink, dtype="bf16", row_start=0, scale=1.0):
     """Same rows as ``rows`` but always as float32 values (bf16 widened exactly, fp8 codes
-    decoded exactly and multiplied by their scale)."""
+    decoded exactly and multiplied by their scale; int8 codes times their scale)."""
     r = rows(seed, tag, unit, n_rows, mu, sigma, sink, dtype, row_start, scale)
     if dtype == "f32":
         return r
     if dtype == "fp8":
         return fp8_e4m3_to_f32(r) * np.float32(scale)
+    if dtype == "int8":
+        return r.astype(np.float32) * np.float32(scale)
     return bf16_bits_to_f32(r)

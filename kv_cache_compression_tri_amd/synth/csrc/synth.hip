@@ -8,8 +8,9 @@
 //            times 2^-16 (Irwin-Hall(12) - 6, exact in float32)
 //   value  = mu[col] + sigma[col] * normal, each float32 operation rounded once (no FMA),
 //            times 20 on a sink row (row 0), then RNE to bfloat16, kept as float32, or
-//            (fp8) times a power-of-two inverse scale and encoded as OCP E4M3 with
-//            round-to-nearest-even, saturating at +-448
+//            (fp8, int8) times a power-of-two inverse scale and encoded as OCP E4M3 with
+//            round-to-nearest-even, saturating at +-448, or as int8 with round-to-nearest-
+//            even, clamped to [-127, 127]
 //   counter c = unit << 27 | row << 7 | col
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -72,7 +73,13 @@ __device__ __forceinline__ uint32_t to_fp8_e4m3(float x) {
   return sign | code;
 }
 
-// 8 consecutive columns per thread; DT 0 = float32, 1 = bfloat16, 2 = fp8 E4M3.
+// int8: round to nearest even, clamp to [-127, 127]
+__device__ __forceinline__ uint32_t to_int8(float x) {
+  const float r = fminf(fmaxf(rintf(x), -127.0f), 127.0f);
+  return uint32_t(int32_t(r)) & 0xFFu;
+}
+
+// 8 consecutive columns per thread; DT 0 = float32, 1 = bfloat16, 2 = fp8 E4M3, 3 = int8.
 template <int DT>
 __device__ __forceinline__ void write8(void* dst, uint64_t key, uint64_t unit, uint32_t row,
                                        uint32_t col0, const float* mu, const float* sigma,
@@ -81,10 +88,11 @@ __device__ __forceinline__ void write8(void* dst, uint64_t key, uint64_t unit, u
 #pragma unroll
   for (int e = 0; e < 8; ++e)
     v[e] = element(key, unit, row, col0 + e, mu[col0 + e], sigma[col0 + e], sink_row);
-  if (DT == 2) {
+  if (DT >= 2) {
     uint32_t c[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) c[e] = to_fp8_e4m3(__fmul_rn(v[e], inv_scale));
+    for (int e = 0; e < 8; ++e)
+      c[e] = DT == 2 ? to_fp8_e4m3(__fmul_rn(v[e], inv_scale)) : to_int8(__fmul_rn(v[e], inv_scale));
     uint2 w;
     w.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
     w.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
@@ -108,7 +116,7 @@ __global__ void fill_dense_kernel(void* out, int64_t n_units, int64_t max_len, i
                                   const float* __restrict__ mu, const float* __restrict__ sigma,
                                   int32_t sink, uint64_t key, const float* __restrict__ inv_scale) {
   const int64_t total = n_units * max_len * 16;  // 16 groups of 8 columns per row
-  const size_t esz = DT == 2 ? 1 : (DT == 1 ? 2 : 4);
+  const size_t esz = DT >= 2 ? 1 : (DT == 1 ? 2 : 4);
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
        i += int64_t(gridDim.x) * blockDim.x) {
     const uint32_t cg = uint32_t(i & 15);
@@ -132,7 +140,7 @@ __global__ void fill_paged_kernel(void* pool, int32_t n_seq, int32_t n_layer, in
   // one work index per (seq, page slot, layer, head, row-in-page, column group)
   const int64_t per_page = int64_t(n_layer) * n_kvh * page * 16;
   const int64_t total = int64_t(n_seq) * max_pages * per_page;
-  const size_t esz = DT == 2 ? 1 : (DT == 1 ? 2 : 4);
+  const size_t esz = DT >= 2 ? 1 : (DT == 1 ? 2 : 4);
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
        i += int64_t(gridDim.x) * blockDim.x) {
     const uint32_t cg = uint32_t(i & 15);
@@ -174,21 +182,25 @@ int grid_for(int64_t work) {
 
 extern "C" {
 
-// Fill a dense [n_units][max_len][128] cache (dtype 0 = float32, 1 = bfloat16, 2 = fp8 E4M3).
+// Fill a dense [n_units][max_len][128] cache (dtype 0 = float32, 1 = bfloat16, 2 = fp8 E4M3,
+// 3 = int8).
 // mu: device [n_model_units][128] float32 (unit u uses row u % n_model_units);
-// sigma: device [128] float32; inv_scale: fp8 only, device [n_model_units] float32 powers of
+// sigma: device [128] float32; inv_scale: 8-bit only, device [n_model_units] float32 powers of
 // two (NULL = 1).  Returns 0, -1 on a bad argument, -4 on a HIP error.
 int tri_synth_fill_dense(void* out, int32_t dtype, int64_t n_units, int64_t max_len,
                          int32_t n_model_units, const float* mu, const float* sigma,
                          int32_t sink, uint64_t seed, uint32_t tag, const float* inv_scale,
                          void* stream) {
   if (!out || !mu || !sigma || n_units <= 0 || max_len <= 0 || max_len > (1 << 20) ||
-      n_model_units <= 0 || dtype < 0 || dtype > 2 || seed >= (1ull << 56) || tag > 255)
+      n_model_units <= 0 || dtype < 0 || dtype > 3 || seed >= (1ull << 56) || tag > 255)
     return -1;
   const uint64_t key = host_mix64((seed << 8) | tag);
   const int grid = grid_for(n_units * max_len * 16);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dtype == 2)
+  if (dtype == 3)
+    hipLaunchKernelGGL(fill_dense_kernel<3>, dim3(grid), dim3(256), 0, st, out, n_units, max_len,
+                       n_model_units, mu, sigma, sink, key, inv_scale);
+  else if (dtype == 2)
     hipLaunchKernelGGL(fill_dense_kernel<2>, dim3(grid), dim3(256), 0, st, out, n_units, max_len,
                        n_model_units, mu, sigma, sink, key, inv_scale);
   else if (dtype == 1)
@@ -203,7 +215,7 @@ int tri_synth_fill_dense(void* out, int32_t dtype, int64_t n_units, int64_t max_
 // Fill a paged pool [n_pages][n_layer][n_kvh][page][128] through per-sequence block tables
 // (device [n_seq][max_pages]) for slots < seq_len[s] (device [n_seq]).  mu: device
 // [n_layer][n_kvh][128]; unit index of (s, l, h) is (s * n_layer + l) * n_kvh + h;
-// inv_scale: fp8 only, device [n_layer][n_kvh] (NULL = 1).
+// inv_scale: 8-bit only, device [n_layer][n_kvh] (NULL = 1).
 int tri_synth_fill_paged(void* pool, int32_t dtype, int32_t n_seq, int32_t n_layer, int32_t n_kvh,
                          int32_t page, int32_t max_pages, const int32_t* block_table,
                          const int32_t* seq_len, const float* mu, const float* sigma,
@@ -211,13 +223,16 @@ int tri_synth_fill_paged(void* pool, int32_t dtype, int32_t n_seq, int32_t n_lay
                          void* stream) {
   if (!pool || !block_table || !seq_len || !mu || !sigma || n_seq <= 0 || n_layer <= 0 ||
       n_kvh <= 0 || page <= 0 || max_pages <= 0 || int64_t(page) * max_pages > (1 << 20) ||
-      dtype < 0 || dtype > 2 || seed >= (1ull << 56) || tag > 255)
+      dtype < 0 || dtype > 3 || seed >= (1ull << 56) || tag > 255)
     return -1;
   const uint64_t key = host_mix64((seed << 8) | tag);
   const int64_t work = int64_t(n_seq) * max_pages * n_layer * n_kvh * page * 16;
   const int grid = grid_for(work);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dtype == 2)
+  if (dtype == 3)
+    hipLaunchKernelGGL(fill_paged_kernel<3>, dim3(grid), dim3(256), 0, st, pool, n_seq, n_layer, n_kvh,
+                       page, max_pages, block_table, seq_len, mu, sigma, sink, key, inv_scale);
+  else if (dtype == 2)
     hipLaunchKernelGGL(fill_paged_kernel<2>, dim3(grid), dim3(256), 0, st, pool, n_seq, n_layer, n_kvh,
                        page, max_pages, block_table, seq_len, mu, sigma, sink, key, inv_scale);
   else if (dtype == 1)

@@ -56,7 +56,7 @@ class DeviceWorkload:
     block_table: object
     center: object
     mean_abs: object
-    k_scale: object = None     # device [n_layer, n_kvh] float32 for fp8 caches
+    k_scale: object = None     # device [n_layer, n_kvh] float32 for 8-bit caches
 
     def kv(self):
         from .. import KVCache
@@ -69,7 +69,7 @@ def fill(w: Workload, hp: HostParams, k, v, seq_len, block_table):
     """(Re)generate K (and V) in place from the workload's seed."""
     import torch
     dev = k.device
-    dtype_code = {"f32": 0, "bf16": 1, "fp8": 2}[w.dtype]
+    dtype_code = {"f32": 0, "bf16": 1, "fp8": 2, "int8": 3}[w.dtype]
     mu_k = torch.from_numpy(np.ascontiguousarray(hp.mu_k.reshape(-1, w.head_dim))).to(dev)
     sig_k = torch.from_numpy(hp.sigma).to(dev)
     mu_v = torch.zeros_like(mu_k)
@@ -100,7 +100,7 @@ def build(w: Workload, device="cuda", hp: HostParams = None) -> DeviceWorkload:
     """Allocate and generate the workload's cache and statistics on the device."""
     import torch
     hp = hp or make_params(w)
-    tdtype = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.float8_e4m3fn}[w.dtype]
+    tdtype = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.float8_e4m3fn, "int8": torch.int8}[w.dtype]
     seq_len = torch.from_numpy(hp.lengths).to(device)
     if w.paged:
         shape = (hp.n_pages, w.n_layer, w.n_kvh, w.page, w.head_dim)
@@ -113,5 +113,5 @@ def build(w: Workload, device="cuda", hp: HostParams = None) -> DeviceWorkload:
     fill(w, hp, k, v, seq_len, block_table)
     center = torch.from_numpy(hp.center).to(device)
     mean_abs = torch.from_numpy(hp.mean_abs).to(device)
-    k_scale = torch.from_numpy(hp.k_scale).to(device) if w.dtype == "fp8" else None
+    k_scale = torch.from_numpy(hp.k_scale).to(device) if w.dtype in ("fp8", "int8") else None
     return DeviceWorkload(w, hp, k, v, seq_len, block_table, center, mean_abs, k_scale)

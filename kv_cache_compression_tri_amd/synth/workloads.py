@@ -35,7 +35,7 @@ class Workload:
     n_kvh: int
     group: int
     max_len: int
-    dtype: str                 # "f32" | "bf16" | "fp8" (OCP E4M3 codes times a per-head scale)
+    dtype: str                 # "f32" | "bf16" | "fp8" | "int8" (8-bit codes times a per-head scale)
     base: float
     offsets: tuple
     budget: int
@@ -97,6 +97,11 @@ WORKLOADS = {
         "gqa8b_32k_fp8", n_seq=1, n_layer=36, n_kvh=8, group=4, max_len=32768,
         dtype="fp8", base=1e6, offsets=geometric_offsets(12), budget=2048, window=128,
         reduce="max", seed=5),
+    # the 32K GQA step on an int8 cache with per-(layer, KV head) key scales
+    "gqa8b_32k_int8": Workload(
+        "gqa8b_32k_int8", n_seq=1, n_layer=36, n_kvh=8, group=4, max_len=32768,
+        dtype="int8", base=1e6, offsets=geometric_offsets(12), budget=2048, window=128,
+        reduce="max", seed=6),
 }
 
 BENCH_WORKLOAD = "gqa8b_32k_bf16"
@@ -117,16 +122,18 @@ class HostParams:
     lengths: np.ndarray       # [n_seq] int32
     block_table: np.ndarray = field(default=None)   # [n_seq, max_pages] int32 (paged)
     n_pages: int = 0
-    k_scale: np.ndarray = field(default=None)       # [n_layer, n_kvh] float32 (fp8 keys)
+    k_scale: np.ndarray = field(default=None)       # [n_layer, n_kvh] float32 (8-bit keys)
 
 
 def key_scales(w) -> np.ndarray:
-    """Per-(layer, KV head) key scales of an fp8 cache: powers of two (1 and 1/2 in a
-    checkerboard), so that encoding x / scale is exact before rounding; 1 otherwise."""
-    if w.dtype != "fp8":
+    """Per-(layer, KV head) key scales of an 8-bit cache: powers of two in a checkerboard,
+    so that encoding x / scale is exact before rounding (fp8: 1 and 1/2; int8: 1/16 and 1/8,
+    which puts typical keys at codes of a few tens); 1 otherwise."""
+    if w.dtype not in ("fp8", "int8"):
         return np.ones((w.n_layer, w.n_kvh), dtype=np.float32)
     lh = np.add.outer(np.arange(w.n_layer), np.arange(w.n_kvh))
-    return np.where(lh % 2 == 0, 1.0, 0.5).astype(np.float32)
+    hi, lo = (1.0, 0.5) if w.dtype == "fp8" else (1.0 / 16, 1.0 / 8)
+    return np.where(lh % 2 == 0, hi, lo).astype(np.float32)
 
 
 def make_params(w: Workload, lengths=None) -> HostParams:

@@ -23,7 +23,7 @@ SCORE_TOL = 2e-3
 
 
 # numpy view of a cache element's raw bits
-BITS_VIEW = {"f32": np.int32, "bf16": np.int16, "fp8": np.uint8}
+BITS_VIEW = {"f32": np.int32, "bf16": np.int16, "fp8": np.uint8, "int8": np.int8}
 
 
 def host_rows(w, hp, s, layer, kv_head, tag=synth.TAG_K, as_float=True):
@@ -34,7 +34,7 @@ def host_rows(w, hp, s, layer, kv_head, tag=synth.TAG_K, as_float=True):
     scale = 1.0
     if tag == synth.TAG_K:
         mu, sig, sink = hp.mu_k[layer, kv_head], hp.sigma, w.sink
-        if w.dtype == "fp8":
+        if w.dtype in ("fp8", "int8"):
             scale = float(hp.k_scale[layer, kv_head])
     else:
         mu, sig, sink = np.zeros(w.head_dim, np.float32), np.ones(w.head_dim, np.float32), False

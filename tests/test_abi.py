@@ -88,6 +88,8 @@ def test_score_keys_validation():
     assert _score(c, _kv(k_scale=FAKE.value))[0] == _abi.TRI_EINVAL          # scale needs fp8 keys
     assert _score(c, _kv(dtype=_abi.TRI_FP8_E4M3), ws_query=True) == (_abi.TRI_OK, 0)
     assert _score(c, _kv(dtype=_abi.TRI_FP8_E4M3, k_scale=FAKE.value), ws_query=True) == (_abi.TRI_OK, 0)
+    assert _score(c, _kv(dtype=_abi.TRI_INT8, k_scale=FAKE.value), ws_query=True) == (_abi.TRI_OK, 0)
+    assert _score(c, _kv(dtype=_abi.TRI_INT8 + 1))[0] == _abi.TRI_EINVAL
     assert _score(c, _kv(layout=5))[0] == _abi.TRI_EINVAL
     assert _score(c, _kv(n_layer=0))[0] == _abi.TRI_EINVAL
     assert _score(c, _kv(seq_len=None))[0] == _abi.TRI_EINVAL
@@ -168,8 +170,9 @@ def test_calibrate_validation():
         return L.tri_calibrate_stats(q, dtype, n, 2, 4, head_dim, layout, FAKE, FAKE, None,
                                      ctypes.byref(size) if ws else None, None)
     assert cal(n=0) == _abi.TRI_EINVAL
-    assert cal(dtype=3) == _abi.TRI_EINVAL
+    assert cal(dtype=4) == _abi.TRI_EINVAL
     assert cal(dtype=_abi.TRI_FP8_E4M3) == _abi.TRI_ENOTSUP                 # queries are f32 / bf16
+    assert cal(dtype=_abi.TRI_INT8) == _abi.TRI_ENOTSUP
     assert cal(layout=9) == _abi.TRI_EINVAL
     assert cal(head_dim=96) == _abi.TRI_ENOTSUP
     assert cal(q=None) == _abi.TRI_EINVAL
@@ -182,7 +185,7 @@ def test_synth_library_exports_and_rejects_bad_arguments():
         assert hasattr(L, name)
     assert L.tri_synth_fill_dense(None, 1, 1, 16, 1, FAKE, FAKE, 0, 0, 0, None, None) == -1
     assert L.tri_synth_fill_dense(FAKE, 1, 1, (1 << 20) + 1, 1, FAKE, FAKE, 0, 0, 0, None, None) == -1
-    assert L.tri_synth_fill_dense(FAKE, 3, 1, 16, 1, FAKE, FAKE, 0, 0, 0, None, None) == -1    # dtype
+    assert L.tri_synth_fill_dense(FAKE, 4, 1, 16, 1, FAKE, FAKE, 0, 0, 0, None, None) == -1    # dtype
     assert L.tri_synth_fill_paged(FAKE, 1, 1, 1, 1, 16, 0, FAKE, FAKE, FAKE, FAKE, 0, 0, 0, None, None) == -1
 
 

@@ -87,7 +87,7 @@ def host_outputs(scores, kept, kept_n, out):
 # generator: device == host, bit for bit
 # ---------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8", "int8"])
 def test_device_generator_matches_host(dtype):
     w = W.scaled(W.WORKLOADS["gqa8b_32k_bf16"], n_seq=2, n_layer=2, n_kvh=2, max_len=300, dtype=dtype)
     log(f"generator dense {dtype}")
@@ -145,6 +145,11 @@ SMALL_DENSE = {
     "g2_mean_half_fp8_wide": (dict(n_seq=2, n_layer=1, n_kvh=3, group=2, dtype="fp8", reduce="mean",
                                    max_len=1100, budget=1024, window=8, sigma_low=0.01, sigma_high=2.0),
                               [1100, 57]),
+    # int8 keys with per-(layer, KV head) scales 1/16 and 1/8
+    "g4_max_half_int8": (dict(n_seq=2, n_layer=2, n_kvh=2, group=4, dtype="int8", max_len=2300, budget=400,
+                              window=64), [2300, 700]),
+    "g7_max_interleaved_int8": (dict(n_seq=1, n_layer=2, n_kvh=1, group=7, dtype="int8", layout="interleaved",
+                                     max_len=1800, budget=256, window=0), [1800]),
 }
 
 
@@ -176,6 +181,7 @@ def test_small_dense_parity(name):
     ([700, 4100, 1500, 33], "post", dict(layout="interleaved", group=3, reduce="mean")),
     ([3000, 17, 4096, 900], "pre", dict(dtype="fp8")),
     ([1200, 4111, 64, 2000], "post", dict(dtype="fp8", layout="interleaved", group=5)),
+    ([2500, 33, 4096, 1000], "pre", dict(dtype="int8", layout="interleaved", reduce="mean")),
 ])
 def test_small_paged_parity(lengths, key_space, extra):
     w = W.scaled(W.WORKLOADS["paged_ragged64_bf16"], n_seq=4, n_layer=2, n_kvh=2, max_len=5120,
@@ -560,7 +566,8 @@ def test_zero_duplicated_and_nan_key_rows():
 # ---------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype,layout,group,reduce", [("bf16", "half", 4, "max"), ("f32", "interleaved", 3, "mean"),
-                                                       ("bf16", "interleaved", 7, "max"), ("fp8", "half", 4, "max")])
+                                                       ("bf16", "interleaved", 7, "max"), ("fp8", "half", 4, "max"),
+                                                       ("int8", "interleaved", 2, "mean")])
 def test_post_rope_small_dense(dtype, layout, group, reduce):
     # a post-RoPE cache built on the host: the generator's keys rotated by RoPE at their
     # slots in float64 (the oracle's rotation), then stored in the cache dtype (fp8: the
@@ -570,7 +577,7 @@ def test_post_rope_small_dense(dtype, layout, group, reduce):
     lengths = [2600, 1111]
     hp = W.make_params(w, lengths=lengths)
     log(f"post-RoPE small dense {dtype} {layout} G={group} {reduce}")
-    tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.float8_e4m3fn}[dtype]
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.float8_e4m3fn, "int8": torch.int8}[dtype]
     k = torch.zeros((2, 2, 2, w.max_len, 128), dtype=tdt)
     cached, stored = {}, {}
     for s in range(2):
@@ -586,13 +593,17 @@ def test_post_rope_small_dense(dtype, layout, group, reduce):
                     sc_lh = np.float32(hp.k_scale[l, h])
                     raw = synth.f32_to_fp8_e4m3(post / sc_lh)
                     cached[(s, l, h)] = synth.fp8_e4m3_to_f32(raw) * sc_lh
+                elif dtype == "int8":
+                    sc_lh = np.float32(hp.k_scale[l, h])
+                    raw = synth.f32_to_int8(post / sc_lh)
+                    cached[(s, l, h)] = raw.astype(np.float32) * sc_lh
                 else:
                     raw = post.view(np.int32)
                     cached[(s, l, h)] = post
                 stored[(s, l, h)] = raw
                 k[s, l, h, :L] = torch.from_numpy(raw.copy()).view(tdt)
     k = k.cuda()
-    k_scale = torch.from_numpy(hp.k_scale).cuda() if dtype == "fp8" else None
+    k_scale = torch.from_numpy(hp.k_scale).cuda() if dtype in ("fp8", "int8") else None
     kv = tri.KVCache.dense(k, None, torch.tensor(lengths, dtype=torch.int32, device="cuda"), k_scale=k_scale)
     center, mean_abs = torch.from_numpy(hp.center).cuda(), torch.from_numpy(hp.mean_abs).cuda()
     out = tri.compress(kv, center, mean_abs, rope_base=w.base, offsets=w.offsets, group=group, budget=w.budget,
@@ -628,6 +639,14 @@ def test_full_gqa8b_32k_fp8():
     rng = np.random.default_rng(106)
     units = [0, 1, w.n_units - 1] + _low_r_units(w, hp, 1) + [int(x) for x in rng.choice(w.n_units, 2, replace=False)]
     _full_dense("gqa8b_32k_fp8", units)
+
+
+def test_full_gqa8b_32k_int8():
+    w = W.WORKLOADS["gqa8b_32k_int8"]
+    hp = W.make_params(w)
+    rng = np.random.default_rng(107)
+    units = [0, 1, w.n_units - 1] + _low_r_units(w, hp, 1) + [int(x) for x in rng.choice(w.n_units, 2, replace=False)]
+    _full_dense("gqa8b_32k_int8", units)
 
 
 # ---------------------------------------------------------------------------------------

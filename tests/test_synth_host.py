@@ -161,3 +161,46 @@ def test_fp8_rows_are_codes_of_scaled_values():
             assert np.array_equal(codes, synth.f32_to_fp8_e4m3(x / np.float32(sc)))
             vals = synth.rows_as_float(w.seed, synth.TAG_K, unit, 64, hp.mu_k[l, h], hp.sigma, True, "fp8", scale=sc)
             assert np.array_equal(vals, synth.fp8_e4m3_to_f32(codes) * np.float32(sc))
+
+
+# ---------------------------------------------------------------------------------------
+# int8 encoding of the generator
+# ---------------------------------------------------------------------------------------
+
+def _int8_nearest_even(x):
+    """Brute force: the nearest of the codes -127..127, ties to the even code."""
+    codes = np.arange(-127, 128)
+    out = []
+    for v in np.asarray(x, dtype=np.float64):
+        d = np.abs(codes - v)
+        cand = codes[d == d.min()]
+        even = [c for c in cand if c % 2 == 0]
+        out.append(int(even[0] if even else cand[0]))
+    return np.array(out, dtype=np.int8)
+
+
+def test_int8_encoder_is_round_to_nearest_even_and_clamps():
+    rng = np.random.default_rng(32)
+    x = np.concatenate([rng.standard_normal(3000) * 40.0, rng.uniform(-3, 3, 1000),
+                        np.arange(-130, 131) + 0.5, [127.4, 127.5, 200.0, -127.5, -1e9, 1e9]]).astype(np.float32)
+    assert np.array_equal(synth.f32_to_int8(x), _int8_nearest_even(x))
+    enc = lambda v: int(synth.f32_to_int8(np.float32([v]))[0])
+    assert enc(0.5) == 0 and enc(1.5) == 2 and enc(2.5) == 2 and enc(-0.5) == 0 and enc(-1.5) == -2
+    assert enc(126.5) == 126 and enc(127.5) == 127 and enc(300.0) == 127 and enc(-300.0) == -127
+
+
+def test_int8_rows_are_codes_of_scaled_values():
+    w = W.scaled(W.WORKLOADS["gqa8b_32k_bf16"], dtype="int8", n_layer=2, n_kvh=2, max_len=64)
+    hp = W.make_params(w)
+    assert set(np.unique(hp.k_scale)) == {1.0 / 16, 1.0 / 8}
+    for l in range(2):
+        for h in range(2):
+            unit = W.unit_index(w, 0, l, h)
+            sc = float(hp.k_scale[l, h])
+            codes = synth.rows(w.seed, synth.TAG_K, unit, 64, hp.mu_k[l, h], hp.sigma, True, "int8", scale=sc)
+            x = synth.rows(w.seed, synth.TAG_K, unit, 64, hp.mu_k[l, h], hp.sigma, True, "f32")
+            assert codes.dtype == np.int8
+            assert np.array_equal(codes, synth.f32_to_int8(x / np.float32(sc)))
+            assert np.abs(codes[1:]).max() < 127          # only the sink row may clamp
+            vals = synth.rows_as_float(w.seed, synth.TAG_K, unit, 64, hp.mu_k[l, h], hp.sigma, True, "int8", scale=sc)
+            assert np.array_equal(vals, codes.astype(np.float32) * np.float32(sc))
