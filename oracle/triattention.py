@@ -31,6 +31,14 @@ distance d = query_pos - key_pos + Delta:
     score(k) = mean_Delta sum_f |E[q_f]| |k_f| cos(d theta_f + arg E[q_f] - arg k_f)
              + sum_f (1 - R_f) E|q_f| |k_f|
 
+A second, multiplicative form follows [Review] "Core Mechanism" (a trigonometric series
+in the distance, then scaled by ||Q|| ||K||): the series keeps only the phases,
+
+    score_mult(k) = mean_Delta sum_f cos(d theta_f + arg E[q_f] - arg k_f) * ||E q|| * ||k||
+
+with ||E q|| the L2 norm of the query centre and ||k|| that of the key (bands where E[q_f]
+or k_f is 0 have no phase and contribute 0 to the series).
+
 Scores are reduced over the query heads of a GQA group (max or mean), the top-B keys of
 each KV head are kept with the most recent window always kept, and the survivors are
 packed forward into dense or paged storage.
@@ -195,6 +203,30 @@ def _trig_term(k_bands, key_pos, query_pos, center_h, theta, offsets):
     return total / len(offsets)
 
 
+def _trig_unit_term(k_bands, key_pos, query_pos, center_h, theta, offsets):
+    """mean_Delta sum_f cos(d theta_f + arg E q_f - arg k_f), d = Q - p + Delta (phases only).
+
+    The series of [Review] "Core Mechanism" ("score(d) = cos(d theta_1) + cos(d theta_2) +
+    ...") before its norm weighting: each band contributes the cosine of its phase
+    difference at the distance, with unit amplitude.  A band whose centre or key part is 0
+    has no phase and contributes 0.
+    """
+    q_arg = np.arctan2(center_h.imag, center_h.real)          # arg E[q_f]      [F]
+    k_arg = np.arctan2(k_bands.imag, k_bands.real)            # arg k_f         [L, F]
+    live = (np.abs(center_h)[None, :] > 0) & (np.abs(k_bands) > 0)
+    total = np.zeros(k_bands.shape[0], dtype=np.float64)
+    for delta in offsets:
+        dist = (np.float64(query_pos) - key_pos.astype(np.float64)) + np.float64(delta)
+        phase = dist[:, None] * theta[None, :] + q_arg[None, :] - k_arg
+        total += np.sum(np.where(live, np.cos(phase), 0.0), axis=1)
+    return total / len(offsets)
+
+
+def _l2_norm(bands):
+    """||x|| = sqrt(sum_f |x_f|^2) over the bands of each row (the vector's L2 norm)."""
+    return np.sqrt(np.sum(np.abs(bands) ** 2, axis=-1))
+
+
 def _norm_term(k_bands, center_h, mean_abs_h):
     """sum_f (1 - R_f) E|q_f| |k_f|.
 
@@ -209,7 +241,7 @@ def _norm_term(k_bands, center_h, mean_abs_h):
 
 def score_keys(keys, center, mean_abs, *, base: float, offsets, key_pos=None,
                query_pos=None, layout: str = "half", reduce: str = "max",
-               return_heads: bool = False, key_space: str = "pre"):
+               return_heads: bool = False, key_space: str = "pre", form: str = "additive"):
     """Score every cached key of one (layer, KV head) unit.
 
     keys:     [L, d] cached keys (any float dtype; upcast exactly to float64): pre-RoPE
@@ -223,6 +255,9 @@ def score_keys(keys, center, mean_abs, *, base: float, offsets, key_pos=None,
     key_pos:  [L] RoPE positions of the keys (default: slot index 0..L-1)
     query_pos: position of the newest query (default: L - 1)
     reduce:   "max" or "mean" over the G query heads of the group
+    form:     "additive" (the trig series of centre/key band pairs plus the
+              concentration-weighted norm term) or "multiplicative" (the phase-only
+              series times ||E q|| ||k||, [Review] "Core Mechanism"; mean_abs is unused)
 
     Returns float64 scores [L] (and the per-head scores [G, L] if return_heads).
     The series is position-aware: the keys are scored at their positions relative to
@@ -247,8 +282,14 @@ def score_keys(keys, center, mean_abs, *, base: float, offsets, key_pos=None,
     theta = rope_theta(base, d)
     kb = split_bands(keys, layout)
 
+    if form not in ("additive", "multiplicative"):
+        raise ValueError(f"unknown score form {form!r}")
     heads = []
     for h in range(center.shape[0]):
+        if form == "multiplicative":
+            series = _trig_unit_term(kb, key_pos, query_pos, center[h], theta, offsets)
+            heads.append(series * _l2_norm(center[h][None, :])[0] * _l2_norm(kb))
+            continue
         trig = _trig_term(kb, key_pos, query_pos, center[h], theta, offsets)
         norm = _norm_term(kb, center[h], mean_abs[h])
         heads.append(trig + norm)
@@ -260,12 +301,24 @@ def score_keys(keys, center, mean_abs, *, base: float, offsets, key_pos=None,
 
 
 def score_magnitude_bound(keys, center, mean_abs, *, layout: str = "half",
-                          reduce: str = "max") -> np.ndarray:
-    """S_j = sum_f |k_f| (|E q_f| + |(1 - R_f) E|q_f||), reduced over heads like the score.
+                          reduce: str = "max", form: str = "additive") -> np.ndarray:
+    """S_j = sum_f |k_f| (|E q_f| + |(1 - R_f) E|q_f||), reduced over heads like the score
+    (multiplicative form: n_j ||E q|| ||k_j||, n_j = bands where both parts are non-zero).
 
     |score_j| <= S_j for every key; it is the scale against which score errors are
     measured (a plain |error| / |score| is unbounded where a signed score crosses 0).
     """
+    if form == "multiplicative":
+        kb = split_bands(np.asarray(keys, dtype=np.float64), layout)
+        center = _as_complex(center)
+        if center.ndim == 1:
+            center = center[None, :]
+        k_norm = np.sqrt(np.sum(np.abs(kb) ** 2, axis=1))
+        heads = []
+        for h in range(center.shape[0]):
+            live = (np.abs(center[h])[None, :] > 0) & (np.abs(kb) > 0)
+            heads.append(live.sum(axis=1) * np.sqrt(np.sum(np.abs(center[h]) ** 2)) * k_norm)
+        return _reduce_heads(np.stack(heads, axis=0), reduce)
     keys = np.asarray(keys, dtype=np.float64)
     center = _as_complex(center)
     mean_abs = np.asarray(mean_abs, dtype=np.float64)

@@ -49,7 +49,12 @@ def _pin_calls():
         pins.test_p7_dense_rows_are_bit_copies,
         pins.test_p7_paged_forward_packing,
         pins.test_p10_fp8_e4m3_values_fixed_by_the_format,
+        pins.test_p11_hand_value_two_bands,
+        pins.test_p11_band_magnitudes_enter_only_through_the_key_norm,
     ]
+    for layout in ("half", "interleaved"):
+        calls.append(lambda layout=layout: pins.test_p11_aligned_phases_closed_form(layout))
+        calls.append(lambda layout=layout: pins.test_p11_single_band_centre_matches_amplitude_series(layout))
     calls += [lambda t=t: pins.test_p5_select_matches_brute_force(t) for t in range(60)]
     with open(golden.GOLDEN) as fh:
         import json
@@ -194,6 +199,22 @@ def _compact_freed_off_by_one(pool_k, pool_v, bt, length, kept_by_unit, page=16)
     return k, v, freed[1:], new_len
 
 
+def _unit_series_amplitude_kept(k_bands, key_pos, query_pos, center_h, theta, offsets):
+    # slip: the key magnitudes stay inside the phase-only series
+    out = T.__dict__["_orig_unit"](k_bands, key_pos, query_pos, center_h, theta, offsets)
+    return out * np.sqrt(np.sum(np.abs(k_bands) ** 2, axis=1)) / np.sqrt(k_bands.shape[1])
+
+
+def _unit_series_phase_sign(k_bands, key_pos, query_pos, center_h, theta, offsets):
+    # slip: the key's phase enters with the wrong sign
+    return T.__dict__["_orig_unit"](np.conj(k_bands), key_pos, query_pos, center_h, theta, offsets)
+
+
+def _l2_as_l1(bands):
+    # slip: the norm of the vector taken as the sum of band magnitudes
+    return np.sum(np.abs(bands), axis=-1)
+
+
 MUTATIONS = {
     "theta_exponent": ("rope_theta", _theta_wrong_exponent),
     "bands_pairing": ("split_bands", _bands_swapped),
@@ -216,6 +237,9 @@ MUTATIONS = {
     "rope_angle_sign": ("rope_apply", _rope_sin_sign),
     "fp8_exponent_bias": ("decode_fp8_e4m3", _fp8_bias_8),
     "fp8_no_subnormals": ("decode_fp8_e4m3", _fp8_no_subnormals),
+    "mult_amplitude_kept": ("_trig_unit_term", _unit_series_amplitude_kept),
+    "mult_phase_sign": ("_trig_unit_term", _unit_series_phase_sign),
+    "mult_norm_l1": ("_l2_norm", _l2_as_l1),
 }
 
 
@@ -228,6 +252,7 @@ def test_mutation_is_caught(name, monkeypatch):
     attr, repl = MUTATIONS[name]
     monkeypatch.setitem(T.__dict__, "_orig_compact", T.compact_paged_sequence)
     monkeypatch.setitem(T.__dict__, "_orig_decode_fp8", T.decode_fp8_e4m3)
+    monkeypatch.setitem(T.__dict__, "_orig_unit", T._trig_unit_term)
     monkeypatch.setattr(T, attr, repl)
     if hasattr(oracle, attr):
         monkeypatch.setattr(oracle, attr, repl)

@@ -12,6 +12,8 @@ Each test states what it pins.  Nothing here calls the HIP library.
   P9  keys cached after RoPE: the oracle's rotation equals textbook RoPE, undoes itself,
       and scoring rotated keys equals scoring the pre-RoPE keys
   P10 fp8 (OCP E4M3) key codes: values the format definition fixes
+  P11 multiplicative form: hand value, aligned-phase closed form, the single-band
+      identity with the amplitude series, and scaling by the key norm
 """
 
 import itertools
@@ -486,3 +488,89 @@ def test_p10_fp8_e4m3_values_fixed_by_the_format():
     pos = v(np.arange(0x00, 0x7F))
     assert np.all(np.diff(pos) > 0)
     assert np.array_equal(v(np.arange(0x80, 0xFF)), -pos)
+
+
+# ---------------------------------------------------------------------------------------
+# P11 multiplicative form: phase-only series times ||E q|| ||k||
+# ---------------------------------------------------------------------------------------
+
+def _bands_to_vector(bands, layout):
+    """Real head vector [.., d] from complex bands [.., F] (written out per layout)."""
+    F = bands.shape[-1]
+    x = np.empty(bands.shape[:-1] + (2 * F,))
+    if layout == "half":
+        x[..., :F], x[..., F:] = bands.real, bands.imag
+    else:
+        x[..., 0::2], x[..., 1::2] = bands.real, bands.imag
+    return x
+
+
+def test_p11_hand_value_two_bands():
+    # d = 4: bands f = 0, 1 with theta = 1 and base^-1/2; one offset; Q - p = 3 for key 0
+    base, qpos, delta = 100.0, 3, 2
+    c = np.array([[3.0 + 4.0j, 0.0 - 2.0j]])                 # |c| = 5, 2 -> ||c|| = sqrt(29)
+    kb = np.array([[1.0 + 1.0j, -2.0 + 0.0j]])                # |k| = sqrt2, 2 -> ||k|| = sqrt6
+    keys = _bands_to_vector(kb, "half")
+    got = oracle.score_keys(keys, c, np.abs(c), base=base, offsets=[delta], query_pos=qpos,
+                            form="multiplicative")[0]
+    dist = qpos - 0 + delta
+    th = [1.0, base ** -0.5]
+    want = (math.cos(dist * th[0] + math.atan2(4, 3) - math.atan2(1, 1))
+            + math.cos(dist * th[1] + math.atan2(-2, 0) - math.atan2(0, -2))) * math.sqrt(29) * math.sqrt(6)
+    assert abs(got - want) <= 1e-12 * abs(want)
+
+
+@pytest.mark.parametrize("layout", ["half", "interleaved"])
+def test_p11_aligned_phases_closed_form(layout):
+    # key bands rotated so every band's phase difference is 0 at the one offset: the series
+    # counts the live bands, so the score is n_live * ||c|| * ||k||
+    rng = np.random.default_rng(41)
+    d, base, qpos, delta, L = 128, 1e4, 900, 8, 6
+    F = d // 2
+    c = rng.standard_normal(F) + 1j * rng.standard_normal(F)
+    pos = np.array([0, 1, 5, 100, 640, 900])
+    theta = np.array([base ** (-(2.0 * f) / d) for f in range(F)])
+    r = rng.uniform(0.2, 3.0, (L, F))
+    r[2, 10:20] = 0.0                                        # dead key bands: no phase
+    kb = r * np.exp(1j * (np.angle(c)[None, :] + (qpos - pos[:, None] + delta) * theta[None, :]))
+    keys = _bands_to_vector(kb, layout)
+    got = oracle.score_keys(keys, c, np.abs(c), base=base, offsets=[delta], key_pos=pos, query_pos=qpos,
+                            layout=layout, form="multiplicative")
+    n_live = (r > 0).sum(axis=1)
+    want = n_live * np.sqrt(np.sum(np.abs(c) ** 2)) * np.sqrt(np.sum(r ** 2, axis=1))
+    assert np.allclose(got, want, rtol=1e-9, atol=0)
+
+
+@pytest.mark.parametrize("layout", ["half", "interleaved"])
+def test_p11_single_band_centre_matches_amplitude_series(layout):
+    # with one live centre band f0 the phase-only series times |c| |k_f0| is the amplitude
+    # series of the additive form (pinned by P1); R = 1 leaves that form no norm term
+    rng = np.random.default_rng(42)
+    d, base, qpos, L = 128, 1e6, 3000, 30
+    offsets = [2 ** i for i in range(9)]
+    F, f0 = d // 2, 23
+    c = np.zeros(F, complex)
+    c[f0] = 1.7 - 0.4j
+    keys = rng.standard_normal((L, d))
+    kb = (keys[:, :F] + 1j * keys[:, F:]) if layout == "half" else (keys[:, 0::2] + 1j * keys[:, 1::2])
+    mult = oracle.score_keys(keys, c, np.abs(c), base=base, offsets=offsets, query_pos=qpos, layout=layout,
+                             form="multiplicative")
+    add = oracle.score_keys(keys, c, np.abs(c), base=base, offsets=offsets, query_pos=qpos, layout=layout)
+    k_norm = np.sqrt(np.sum(keys ** 2, axis=1))
+    assert np.allclose(mult * np.abs(kb[:, f0]), add * k_norm, rtol=1e-9, atol=1e-12)
+
+
+def test_p11_band_magnitudes_enter_only_through_the_key_norm():
+    rng = np.random.default_rng(43)
+    d, L = 128, 12
+    c = rng.standard_normal((2, d // 2, 2))
+    keys = rng.standard_normal((L, d))
+    kw = dict(base=1e4, offsets=[1, 2, 4, 8], reduce="mean", form="multiplicative")
+    s0 = oracle.score_keys(keys, c, np.ones((2, d // 2)), **kw)
+    scaled = keys.copy()
+    scaled[:, [3, 3 + 64, 40, 40 + 64]] *= 5.0                  # two bands, phases unchanged
+    s1 = oracle.score_keys(scaled, c, np.ones((2, d // 2)), **kw)
+    ratio = np.sqrt(np.sum(scaled ** 2, axis=1)) / np.sqrt(np.sum(keys ** 2, axis=1))
+    assert np.allclose(s1, s0 * ratio, rtol=1e-10, atol=1e-12)
+    S = oracle.score_magnitude_bound(keys, c, np.ones((2, d // 2)), reduce="mean", form="multiplicative")
+    assert np.all(np.abs(s0) <= S)
