@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None, help="workload name (default: the 32K GQA pass)")
+    ap.add_argument("--form", choices=("additive", "multiplicative"), default="additive",
+                    help="score form: additive (default) or the phase-only series times the norms")
     ap.add_argument("--key-space", choices=("pre", "post"), default="pre",
                     help="score the cache as pre-RoPE keys (default) or as keys already rotated by RoPE")
     ap.add_argument("--cpu-units", type=int, default=0,
@@ -77,7 +79,7 @@ def _oracle_unit(job):
     """Score + select + compact one unit with the float64 oracle; returns seconds spent."""
     import numpy as np
     import oracle
-    name, key_space, s, l, h = job
+    name, key_space, form, s, l, h = job
     from kv_cache_compression_tri_amd import synth
     from kv_cache_compression_tri_amd.synth import workloads as W
     w = W.WORKLOADS[name]
@@ -94,14 +96,14 @@ def _oracle_unit(job):
     center, mean_abs = oracle.unit_heads(hp.center, hp.mean_abs, l, h, w.group)
     t0 = time.perf_counter()
     sc = oracle.score_keys(keys, center, mean_abs, base=w.base, offsets=w.offsets, layout=w.layout,
-                           reduce=w.reduce, key_space=key_space)
+                           reduce=w.reduce, key_space=key_space, form=form)
     kept = oracle.select_top_b(sc, L, w.budget, w.window)
     if w.with_values:
         oracle.compact_dense(keys_raw, vals, kept)
     return time.perf_counter() - t0, L
 
 
-def cpu_baseline(name, n_units, key_space="pre"):
+def cpu_baseline(name, n_units, key_space="pre", form="additive"):
     os.environ.setdefault("OMP_NUM_THREADS", "1")
     from kv_cache_compression_tri_amd.synth import workloads as W
     import numpy as np
@@ -115,7 +117,7 @@ def cpu_baseline(name, n_units, key_space="pre"):
         n_units = min(32, 2 * cores)
     rng = np.random.default_rng(2024)
     picks = rng.choice(w.n_units, size=min(n_units, w.n_units), replace=False)
-    jobs = [(name, key_space) + tuple(int(x) for x in W.unit_coords(w, int(u))) for u in picks]
+    jobs = [(name, key_space, form) + tuple(int(x) for x in W.unit_coords(w, int(u))) for u in picks]
     workers = min(cores, len(jobs))
     ctx = mp.get_context("spawn")
     t0 = time.perf_counter()
@@ -222,7 +224,8 @@ def main():
         if ev is not None:
             ev[0].record()
         tri.tri_score_keys(kv, dw.center, dw.mean_abs, rope_base=w.base, offsets=w.offsets, group=w.group,
-                           reduce=w.reduce, rope_layout=w.layout, scores=scores, key_space=args.key_space)
+                           reduce=w.reduce, rope_layout=w.layout, scores=scores, key_space=args.key_space,
+                           form=args.form)
         if ev is not None:
             ev[1].record()
         tri.tri_select_topb(scores, kv, w.budget, w.window, kept=kept, kept_n=kept_n)
@@ -274,7 +277,7 @@ def main():
     pass_bytes = score_bytes + compact_bytes
     achieved = score_bytes / (score_ms * 1e-3) / 1e9
     value = keys_per_step / (ms * 1e-3) / 1e9
-    traffic = recorded_traffic(name) if args.key_space == "pre" else None
+    traffic = recorded_traffic(name) if (args.key_space == "pre" and args.form == "additive") else None
     line = {
         "metric": METRIC,
         "value": value,
@@ -294,6 +297,7 @@ def main():
             "context": w.max_len, "head_dim": w.head_dim, "kv_dtype": w.dtype, "budget": w.budget,
             "window": w.window, "offsets": len(w.offsets), "reduce": w.reduce,
             "layout": "paged" if w.paged else "dense", "compaction": compacts, "key_space": args.key_space,
+            "form": args.form,
             "keys_per_step": keys_per_step, "parallelism": "single GPU",
         },
         "roofline": {
@@ -322,7 +326,7 @@ def main():
     line["pass"]["copy_GBps"] = copy_gbs
     line["pass"]["frac_of_copy"] = pass_bytes / (ms * 1e-3) / 1e9 / copy_gbs
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(name, args.cpu_units, args.key_space)
+        line["cpu_baseline"] = cpu_baseline(name, args.cpu_units, args.key_space, args.form)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -87,6 +87,19 @@ typedef enum tri_kv_layout { TRI_DENSE = 0, TRI_PAGED = 1 } tri_kv_layout;
  * position j) without rotating them back. */
 typedef enum tri_key_space { TRI_KEYS_PRE_ROPE = 0, TRI_KEYS_POST_ROPE = 1 } tri_key_space;
 
+/* Form of the score.
+ *   TRI_SCORE_ADDITIVE (default): the offset-averaged cosine series of the centre/key band
+ *     pairs, sum_f |c_f||k_f| cos(d theta_f + arg c_f - arg k_f), plus the concentration-
+ *     weighted norm term sum_f (1 - R_f) E|q_f| |k_f| ([Review] "Key Concepts"; [DevTo] "The
+ *     Core Idea: Q/K Concentration in Pre-RoPE Space").
+ *   TRI_SCORE_MULTIPLICATIVE: the phase-only series sum_f cos(d theta_f + arg c_f - arg k_f)
+ *     (a band whose centre or key part is 0 contributes 0), offset-averaged, times ||c|| ||k||
+ *     ([Review] "Core Mechanism": a trigonometric series in the distance, then weighted by
+ *     the query and key norms).  ||c|| is the L2 norm of the query head's centre and ||k||
+ *     the key's; mean_abs is not read and may be NULL.  A key band with |k_f|^2 below the
+ *     float32 range (|k_f| < about 1e-19) counts as 0. */
+typedef enum tri_score_form { TRI_SCORE_ADDITIVE = 0, TRI_SCORE_MULTIPLICATIVE = 1 } tri_score_form;
+
 /* Description of a pre-RoPE KV cache (all pointers device, caller-owned).
  *   dense: k, v are [n_seq][n_layer][n_kvh][max_len][head_dim]; slot j of unit (s,l,h) is
  *          row j; the unit holds seq_len[s] <= max_len keys.
@@ -137,6 +150,7 @@ typedef struct tri_score_cfg {
   int32_t group;
   int32_t reduce;           /* tri_reduce */
   int32_t key_space;        /* tri_key_space (0 = pre-RoPE keys) */
+  int32_t form;             /* tri_score_form (0 = additive) */
 } tri_score_cfg;
 
 /* Calibration of the query statistics ([Review] "Key Concepts": the centre is the mean of
@@ -219,7 +233,7 @@ const char *tri_last_error(void);
 /* ABI version of this header: major * 10000 + minor * 100 + patch. */
 int tri_version(void);
 
-#define TRI_VERSION 10300
+#define TRI_VERSION 10400
 
 #ifdef __cplusplus
 }

@@ -196,9 +196,10 @@ def tri_calibrate_stats(q, rope_layout: str = "half", center=None, mean_abs=None
 
 
 _KEY_SPACES = {"pre": _abi.TRI_KEYS_PRE_ROPE, "post": _abi.TRI_KEYS_POST_ROPE}
+_FORMS = {"additive": _abi.TRI_SCORE_ADDITIVE, "multiplicative": _abi.TRI_SCORE_MULTIPLICATIVE}
 
 
-def _score_cfg(rope_base, offsets, group, reduce, rope_layout, key_space="pre"):
+def _score_cfg(rope_base, offsets, group, reduce, rope_layout, key_space="pre", form="additive"):
     offs = (ctypes.c_int32 * len(offsets))(*[int(o) for o in offsets])
     cfg = _abi.TriScoreCfg()
     cfg.rope_base = float(rope_base)
@@ -208,20 +209,23 @@ def _score_cfg(rope_base, offsets, group, reduce, rope_layout, key_space="pre"):
     cfg.group = int(group)
     cfg.reduce = _REDUCE[reduce]
     cfg.key_space = _KEY_SPACES[key_space]
+    cfg.form = _FORMS[form]
     return cfg, offs
 
 
 def tri_score_keys(kv: KVCache, center, mean_abs, *, rope_base: float, offsets: Sequence[int],
                    group: int, reduce: str = "max", rope_layout: str = "half", query_pos=None,
-                   scores=None, stream=None, key_space: str = "pre"):
+                   scores=None, stream=None, key_space: str = "pre", form: str = "additive"):
     """Score every cached key; returns float32 scores [n_seq, n_layer, n_kvh, slots].
 
-    key_space "post": the cache holds keys already rotated by RoPE at their slot index."""
+    key_space "post": the cache holds keys already rotated by RoPE at their slot index.
+    form "multiplicative": phase-only series times ||centre|| ||key|| (mean_abs may be None)."""
     torch = _torch()
     L = _abi.lib()
     desc = kv.descriptor()
     _dev(center, "center", torch.float32)
-    _dev(mean_abs, "mean_abs", torch.float32)
+    if mean_abs is not None or form != "multiplicative":
+        _dev(mean_abs, "mean_abs", torch.float32)
     _dev(query_pos, "query_pos", torch.int64)
     if scores is None:
         scores = torch.empty((kv.n_seq, desc.n_layer, desc.n_kvh, kv.slots), dtype=torch.float32,
@@ -232,7 +236,9 @@ def tri_score_keys(kv: KVCache, center, mean_abs, *, rope_base: float, offsets: 
     _shape(mean_abs, "mean_abs", (desc.n_layer, n_qh, desc.head_dim // 2))
     _shape(query_pos, "query_pos", (kv.n_seq,))
     _shape(scores, "scores", (kv.n_seq, desc.n_layer, desc.n_kvh, kv.slots))
-    cfg, _keep = _score_cfg(rope_base, offsets, group, reduce, rope_layout, key_space)
+    if mean_abs is None and form != "multiplicative":
+        raise ValueError("mean_abs is required for the additive form")
+    cfg, _keep = _score_cfg(rope_base, offsets, group, reduce, rope_layout, key_space, form)
     _abi.check(L.tri_score_keys(ctypes.byref(cfg), _ptr(center), _ptr(mean_abs), ctypes.byref(desc),
                                 _ptr(query_pos), _ptr(scores), None, None, _stream(stream)))
     return scores
@@ -307,11 +313,12 @@ def tri_compact_kv(kv: KVCache, kept, kept_n, budget: int, k_out=None, v_out=Non
 
 
 def compress(kv: KVCache, center, mean_abs, *, rope_base, offsets, group, budget, window,
-             reduce="max", rope_layout="half", query_pos=None, stream=None, key_space="pre"):
+             reduce="max", rope_layout="half", query_pos=None, stream=None, key_space="pre",
+             form="additive"):
     """Score, select and compact in one call (convenience; not part of the C ABI)."""
     scores = tri_score_keys(kv, center, mean_abs, rope_base=rope_base, offsets=offsets, group=group,
                             reduce=reduce, rope_layout=rope_layout, query_pos=query_pos, stream=stream,
-                            key_space=key_space)
+                            key_space=key_space, form=form)
     kept, kept_n = tri_select_topb(scores, kv, budget, window, stream=stream)
     out = tri_compact_kv(kv, kept, kept_n, budget, stream=stream)
     out.update(scores=scores, kept=kept, kept_n=kept_n)

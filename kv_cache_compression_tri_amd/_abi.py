@@ -15,6 +15,7 @@ TRI_ROPE_HALF, TRI_ROPE_INTERLEAVED = 0, 1
 TRI_REDUCE_MAX, TRI_REDUCE_MEAN = 0, 1
 TRI_DENSE, TRI_PAGED = 0, 1
 TRI_KEYS_PRE_ROPE, TRI_KEYS_POST_ROPE = 0, 1
+TRI_SCORE_ADDITIVE, TRI_SCORE_MULTIPLICATIVE = 0, 1
 
 EXPORTED = (
     "tri_calibrate_stats",
@@ -55,6 +56,7 @@ class TriScoreCfg(ctypes.Structure):
         ("group", c_int32),
         ("reduce", c_int32),
         ("key_space", c_int32),
+        ("form", c_int32),
     ]
 
 

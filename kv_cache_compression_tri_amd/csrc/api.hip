@@ -149,6 +149,9 @@ int tri_score_keys(const tri_score_cfg* cfg, const float* center, const float* m
       return fail(TRI_EINVAL, "unknown reduce %d", cfg->reduce);
     if (cfg->key_space != TRI_KEYS_PRE_ROPE && cfg->key_space != TRI_KEYS_POST_ROPE)
       return fail(TRI_EINVAL, "unknown key space %d", cfg->key_space);
+    if (cfg->form != TRI_SCORE_ADDITIVE && cfg->form != TRI_SCORE_MULTIPLICATIVE)
+      return fail(TRI_EINVAL, "unknown score form %d", cfg->form);
+    const bool mult = cfg->form == TRI_SCORE_MULTIPLICATIVE;
     if (cfg->group < 1) return fail(TRI_EINVAL, "group must be >= 1");
     if (cfg->group > tri::kMaxGroup) return fail(TRI_ENOTSUP, "group %d > %d", cfg->group, tri::kMaxGroup);
     if (cfg->n_offsets < 1 || !cfg->offsets) return fail(TRI_EINVAL, "at least one offset is required");
@@ -156,7 +159,8 @@ int tri_score_keys(const tri_score_cfg* cfg, const float* center, const float* m
       return fail(TRI_ENOTSUP, "%d offsets > %d", cfg->n_offsets, tri::kMaxOffsets);
     for (int i = 0; i < cfg->n_offsets; ++i)
       if (cfg->offsets[i] < 0) return fail(TRI_EINVAL, "offsets must be >= 0");
-    if (!center || !mean_abs || !scores) return fail(TRI_EINVAL, "center, mean_abs and scores must be non-NULL");
+    if (!center || !scores) return fail(TRI_EINVAL, "center and scores must be non-NULL");
+    if (!mean_abs && !mult) return fail(TRI_EINVAL, "mean_abs must be non-NULL for the additive form");
     if (kv->pos) return fail(TRI_ENOTSUP, "explicit key positions are not supported by tri_score_keys");
     if (int rc = workspace(ws, ws_bytes, 0)) return rc > 0 ? TRI_OK : rc;
 
@@ -204,7 +208,7 @@ int tri_score_keys(const tri_score_cfg* cfg, const float* center, const float* m
     (void)hipGetLastError();
     hipError_t e = tri::launch_score(p, g_eff, kv->dtype,
                                      cfg->rope_layout == TRI_ROPE_INTERLEAVED,
-                                     kv->layout == TRI_PAGED, cfg->key_space == TRI_KEYS_POST_ROPE, int(grid),
+                                     kv->layout == TRI_PAGED, cfg->key_space == TRI_KEYS_POST_ROPE, mult, int(grid),
                                      static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TRI_OK : hip_fail(e, "score launch");
   } catch (...) {

@@ -5,7 +5,14 @@
 namespace tri {
 
 hipError_t launch_score(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
-                        bool post, int grid, hipStream_t stream) {
+                        bool post, bool mult, int grid, hipStream_t stream) {
+  if (mult) {
+    if (dtype >= 2)
+      return post ? launch_score_post_mult_8bit(p, G_eff, dtype, interleaved, paged, grid, stream)
+                  : launch_score_mult_8bit(p, G_eff, dtype, interleaved, paged, grid, stream);
+    return post ? launch_score_post_mult(p, G_eff, dtype, interleaved, paged, grid, stream)
+                : launch_score_mult(p, G_eff, dtype, interleaved, paged, grid, stream);
+  }
   if (dtype >= 2)
     return post ? launch_score_post_8bit(p, G_eff, dtype, interleaved, paged, grid, stream)
                 : launch_score_8bit(p, G_eff, dtype, interleaved, paged, grid, stream);

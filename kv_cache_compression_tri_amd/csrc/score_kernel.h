@@ -1,7 +1,7 @@
 // Key-scoring kernel of the TriAttention compression pass (gfx950), shared by the
 // translation units that instantiate it (score.hip / score_post.hip: pre-RoPE keys / keys
 // cached after RoPE, float32 or bfloat16; score_8bit.hip / score_post_8bit.hip: fp8 and
-// int8 codes).
+// int8 codes; score_*mult*.hip: the same for the multiplicative form).
 //
 // What it computes (per unit = sequence s, layer l, KV head h; key slot j at position p_j;
 // query heads hq of the group with centre c_f = E[q_f] and m_f = E|q_f|):
@@ -40,6 +40,14 @@
 // ring of registers.  Scores of 8 steps are gathered into one lane each and written as one
 // coalesced 256-byte store.  The grid is persistent (one workgroup of kScoreWaves waves per
 // CU), so the 128 KB phase table is built once per CU.
+//
+// Multiplicative form (MULT; "TriAttention: Trigonometric KV Compression for Efficient Long
+// Reasoning", section "Core Mechanism": the series, then weighted by the query and key
+// norms): s_hq(j) = mean_Delta sum_f cos(d theta_f + arg c_f - arg k_f) ||c|| ||k_j||.  The
+// same rewrite applies to unit bands: W_f = (c_f / |c_f|) ||c|| C_f e^{i(Q - p_a) theta_f} and
+// x_f = e^{-i r theta_f} conj(k_f) / |k_f| (one v_rsq_f32 per band; a band with |k_f|^2 = 0
+// contributes 0), and the reduced score is multiplied by ||k_j|| = sqrt(sum_f |k_f|^2).  There
+// is no norm term.
 //
 // Keys cached after RoPE (POST): key j was stored as k'_f = k_f e^{i p_j theta_f}, so
 // c conj(k) e^{i(Q - p_j + Delta) theta} = c conj(k') e^{i(Q + Delta) theta}: the weights
@@ -158,7 +166,7 @@ __device__ __forceinline__ int tab_slot(int r, int f) {
   return ((it * 4 + (b >> 1)) * 64 + kk * 8 + g) * 2 + (b & 1);   // float2 index
 }
 
-template <int GE, int DT, bool IL, bool PAGED, bool POST>
+template <int GE, int DT, bool IL, bool PAGED, bool POST, bool MULT>
 __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScoreParams P) {
   constexpr int NW = kScoreWaves;
   constexpr int NT = NW * 64;
@@ -328,8 +336,60 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
     }
     __builtin_amdgcn_wave_barrier();
 
-    float wr[GE][8], wn[GE][8], nn[GE][8];
+    float wr[GE][8], wn[GE][8], nn[MULT ? 1 : GE][8];
     const int64_t hrow0 = int64_t(l) * n_qh + int64_t(h) * P.group;
+    if constexpr (MULT) {
+      // multiplicative form: the weight of band f is (c_f / |c_f|) ||c|| C_f A_f (a centre
+      // band of 0 has no phase and weighs 0); ||c|| sums |c_f|^2 over the 8 lanes of a key
+      // group, which hold the head's 64 bands
+      const float2* cbase = reinterpret_cast<const float2*>(P.center) + hrow0 * kBands + g * 8;
+      auto unit_weights = [&](int hh, float (&r)[8], float (&i)[8]) __attribute__((always_inline)) {
+        const float2* cr = cbase + int64_t(hh) * kBands;
+        float c2 = 0.0f;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) c2 = fmaf(cr[b].x, cr[b].x, fmaf(cr[b].y, cr[b].y, c2));
+        const float cn = __builtin_sqrtf(sum8(c2));
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const float2 c = cr[b], A = anc[wave][g * 8 + b];
+          const float m = __builtin_sqrtf(c.x * c.x + c.y * c.y);
+          const float sc = m > 0.0f ? cn / m : 0.0f;
+          r[b] = sc * (c.x * A.x - c.y * A.y);
+          i[b] = sc * (c.x * A.y + c.y * A.x);
+        }
+      };
+      if (P.reduce_mean) {
+        float sr[8], si[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) sr[b] = si[b] = 0.0f;
+        for (int hh = 0; hh < P.group; ++hh) {
+          float r[8], i[8];
+          unit_weights(hh, r, i);
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+            sr[b] += r[b];
+            si[b] += i[b];
+          }
+        }
+        const float inv = 1.0f / float(P.group);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          wr[0][b] = sr[b] * inv;
+          wn[0][b] = -si[b] * inv;
+        }
+      } else {
+#pragma unroll
+        for (int hh = 0; hh < GE; ++hh) {
+          float r[8], i[8];
+          unit_weights(hh, r, i);
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+            wr[hh][b] = r[b];
+            wn[hh][b] = -i[b];
+          }
+        }
+      }
+    } else {
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       const int f = g * 8 + b;
@@ -358,6 +418,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
         }
       }
     }
+    }
 
     if (P.k_scale) {   // stored key = true key / scale: the score is linear in the key
       const float ks = P.k_scale[int64_t(l) * P.n_kvh + h];
@@ -367,7 +428,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
         for (int b = 0; b < 8; ++b) {
           wr[hh][b] *= ks;
           wn[hh][b] *= ks;
-          nn[hh][b] *= ks;
+          if constexpr (!MULT) nn[hh][b] *= ks;
         }
     }
 
@@ -400,17 +461,25 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
           float acc[GE];
 #pragma unroll
           for (int hh = 0; hh < GE; ++hh) acc[hh] = 0.0f;
+          float k2sum = 0.0f;   // multiplicative form: sum_f |k_f|^2 of the lane's bands
           if constexpr (POST) {
 #pragma unroll
             for (int b = 0; b < 8; ++b) {
               float a, q;
               band_of<DT, IL>(cur, b, a, q);
-              const float nk = __builtin_amdgcn_sqrtf(fmaf(a, a, q * q));
+              if constexpr (MULT) {   // unit band: the series keeps phases only
+                const float k2 = fmaf(a, a, q * q);
+                k2sum += k2;
+                const float rinv = k2 > 0.0f ? __builtin_amdgcn_rsqf(k2) : 0.0f;
+                a *= rinv;
+                q *= rinv;
+              }
+              const float nk = MULT ? 0.0f : __builtin_amdgcn_sqrtf(fmaf(a, a, q * q));
 #pragma unroll
               for (int hh = 0; hh < GE; ++hh) {        // x = conj(k'): Re(W x) = Wr a + Wi q
                 acc[hh] = fmaf(wr[hh][b], a, acc[hh]);
                 acc[hh] = fmaf(wn[hh][b], -q, acc[hh]);
-                acc[hh] = fmaf(nn[hh][b], nk, acc[hh]);
+                if constexpr (!MULT) acc[hh] = fmaf(nn[hh][b], nk, acc[hh]);
               }
             }
           } else {
@@ -420,16 +489,23 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
           for (int b = 0; b < 8; ++b) {
             float a, q;
             band_of<DT, IL>(cur, b, a, q);
+            if constexpr (MULT) {   // unit band: the series keeps phases only
+              const float k2 = fmaf(a, a, q * q);
+              k2sum += k2;
+              const float rinv = k2 > 0.0f ? __builtin_amdgcn_rsqf(k2) : 0.0f;
+              a *= rinv;
+              q *= rinv;
+            }
             const float tc = (b & 1) ? t4[b >> 1].z : t4[b >> 1].x;
             const float ts = (b & 1) ? t4[b >> 1].w : t4[b >> 1].y;
             const float xr = fmaf(tc, a, ts * q);      // Re(e^{-i r theta} conj(k))
             const float xi = fmaf(ts, a, -(tc * q));   // Im(...)
-            const float nk = __builtin_amdgcn_sqrtf(fmaf(a, a, q * q));
+            const float nk = MULT ? 0.0f : __builtin_amdgcn_sqrtf(fmaf(a, a, q * q));
 #pragma unroll
             for (int hh = 0; hh < GE; ++hh) {
               acc[hh] = fmaf(wr[hh][b], xr, acc[hh]);
               acc[hh] = fmaf(wn[hh][b], xi, acc[hh]);
-              acc[hh] = fmaf(nn[hh][b], nk, acc[hh]);
+              if constexpr (!MULT) acc[hh] = fmaf(nn[hh][b], nk, acc[hh]);
             }
           }
           }
@@ -438,6 +514,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
           float sc = sum8(acc[0]);
 #pragma unroll
           for (int hh = 1; hh < GE; ++hh) sc = fmaxf(sc, sum8(acc[hh]));
+          if constexpr (MULT) sc *= __builtin_sqrtf(sum8(k2sum));   // times ||k|| (>= 0)
           if ((it & 7) == g) keep = sc;
           if ((it & 7) == 7 || n == n_steps - 1) {
             // lane (kk, g) holds the score of step (n & ~7) + g, key kk
@@ -453,13 +530,13 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
   }
 }
 
-template <int GE, int DT, bool POST>
+template <int GE, int DT, bool POST, bool MULT>
 hipError_t launch_ge(const ScoreParams& p, bool il, bool paged, int grid, hipStream_t st) {
   const dim3 blk(kScoreWaves * 64), grd(grid);
-#define TRI_SCORE_CASE(I, PG)                                                        \
-  if (il == I && paged == PG) {                                                      \
-    hipLaunchKernelGGL((score_kernel<GE, DT, I, PG, POST>), grd, blk, 0, st, p);    \
-    return hipGetLastError();                                                        \
+#define TRI_SCORE_CASE(I, PG)                                                              \
+  if (il == I && paged == PG) {                                                            \
+    hipLaunchKernelGGL((score_kernel<GE, DT, I, PG, POST, MULT>), grd, blk, 0, st, p);    \
+    return hipGetLastError();                                                              \
   }
   TRI_SCORE_CASE(false, false)
   TRI_SCORE_CASE(false, true)
@@ -469,18 +546,18 @@ hipError_t launch_ge(const ScoreParams& p, bool il, bool paged, int grid, hipStr
   return hipErrorInvalidValue;
 }
 
-template <int DT, bool POST>
+template <int DT, bool POST, bool MULT = false>
 hipError_t launch_groups(const ScoreParams& p, int G_eff, bool interleaved, bool paged, int grid,
                          hipStream_t stream) {
   switch (G_eff) {
-    case 1: return launch_ge<1, DT, POST>(p, interleaved, paged, grid, stream);
-    case 2: return launch_ge<2, DT, POST>(p, interleaved, paged, grid, stream);
-    case 3: return launch_ge<3, DT, POST>(p, interleaved, paged, grid, stream);
-    case 4: return launch_ge<4, DT, POST>(p, interleaved, paged, grid, stream);
-    case 5: return launch_ge<5, DT, POST>(p, interleaved, paged, grid, stream);
-    case 6: return launch_ge<6, DT, POST>(p, interleaved, paged, grid, stream);
-    case 7: return launch_ge<7, DT, POST>(p, interleaved, paged, grid, stream);
-    case 8: return launch_ge<8, DT, POST>(p, interleaved, paged, grid, stream);
+    case 1: return launch_ge<1, DT, POST, MULT>(p, interleaved, paged, grid, stream);
+    case 2: return launch_ge<2, DT, POST, MULT>(p, interleaved, paged, grid, stream);
+    case 3: return launch_ge<3, DT, POST, MULT>(p, interleaved, paged, grid, stream);
+    case 4: return launch_ge<4, DT, POST, MULT>(p, interleaved, paged, grid, stream);
+    case 5: return launch_ge<5, DT, POST, MULT>(p, interleaved, paged, grid, stream);
+    case 6: return launch_ge<6, DT, POST, MULT>(p, interleaved, paged, grid, stream);
+    case 7: return launch_ge<7, DT, POST, MULT>(p, interleaved, paged, grid, stream);
+    case 8: return launch_ge<8, DT, POST, MULT>(p, interleaved, paged, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,0 +1,13 @@
+// Multiplicative score form (phase-only cosine series times the centre and key norms) for
+// 8-bit (fp8 or int8) keys already rotated by RoPE (the kernel is in score_kernel.h).
+#include "score_kernel.h"
+
+namespace tri {
+
+hipError_t launch_score_post_mult_8bit(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged, int grid,
+                  hipStream_t stream) {
+  return dtype == 3 ? launch_groups<3, true, true>(p, G_eff, interleaved, paged, grid, stream)
+                    : launch_groups<2, true, true>(p, G_eff, interleaved, paged, grid, stream);
+}
+
+}  // namespace tri

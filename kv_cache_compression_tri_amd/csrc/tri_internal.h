@@ -82,7 +82,15 @@ struct CalibParams {
 
 // launchers (return hipError_t of the launch)
 hipError_t launch_score(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
-                        bool post, int grid, hipStream_t stream);
+                        bool post, bool mult, int grid, hipStream_t stream);
+hipError_t launch_score_mult(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
+                            int grid, hipStream_t stream);
+hipError_t launch_score_post_mult(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
+                                 int grid, hipStream_t stream);
+hipError_t launch_score_mult_8bit(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
+                                 int grid, hipStream_t stream);
+hipError_t launch_score_post_mult_8bit(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
+                                      int grid, hipStream_t stream);
 hipError_t launch_score_post(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
                              int grid, hipStream_t stream);
 hipError_t launch_score_8bit(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,

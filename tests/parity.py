@@ -4,7 +4,8 @@ The oracle's inputs are regenerated on the host from the workload seed (the host
 the counter-based generator), never read back from the GPU path.  Tolerances:
   * scores: |s_gpu - s_oracle| <= 2e-3 * S_j, S_j = sum_f |k_f| (|E q_f| + |(1-R_f) E|q_f||)
     reduced over the group like the score (a bound on |s_j|; the scores are computed in
-    float32 from bf16/f32 keys, the oracle in float64);
+    float32 from the stored keys, the oracle in float64); for the multiplicative form
+    S_j = n_j ||E q|| ||k_j|| (n_j = bands where centre and key parts are non-zero);
   * selection: exact against the oracle's selection applied to the GPU's own scores, and
     equal to the oracle's selection on oracle scores except for keys whose oracle score is
     within 2e-3 * S_j of the threshold score;
@@ -47,11 +48,11 @@ def host_bits(w, hp, s, layer, kv_head, tag=synth.TAG_K):
     return host_rows(w, hp, s, layer, kv_head, tag, as_float=False).view(BITS_VIEW[w.dtype])
 
 
-def oracle_scores(w, hp, s, layer, kv_head, keys, key_space="pre"):
+def oracle_scores(w, hp, s, layer, kv_head, keys, key_space="pre", form="additive"):
     center, mean_abs = oracle.unit_heads(hp.center, hp.mean_abs, layer, kv_head, w.group)
     sc = oracle.score_keys(keys, center, mean_abs, base=w.base, offsets=w.offsets,
-                           layout=w.layout, reduce=w.reduce, key_space=key_space)
-    S = oracle.score_magnitude_bound(keys, center, mean_abs, layout=w.layout, reduce=w.reduce)
+                           layout=w.layout, reduce=w.reduce, key_space=key_space, form=form)
+    S = oracle.score_magnitude_bound(keys, center, mean_abs, layout=w.layout, reduce=w.reduce, form=form)
     return sc, S
 
 

@@ -69,10 +69,10 @@ def _cfg(**over):
     return c, offs
 
 
-def _score(cfg=None, kv=None, center=FAKE, scores=FAKE, ws_query=False):
+def _score(cfg=None, kv=None, center=FAKE, scores=FAKE, ws_query=False, mean_abs=FAKE):
     L = _abi.lib()
     size = ctypes.c_size_t(123)
-    rc = L.tri_score_keys(None if cfg is None else ctypes.byref(cfg), center, FAKE,
+    rc = L.tri_score_keys(None if cfg is None else ctypes.byref(cfg), center, mean_abs,
                           None if kv is None else ctypes.byref(kv), None, scores, None,
                           ctypes.byref(size) if ws_query else None, None)
     return rc, size.value
@@ -85,7 +85,12 @@ def test_score_keys_validation():
     assert _score(c, _kv(head_dim=64))[0] == _abi.TRI_ENOTSUP
     assert _score(c, _kv(head_dim=127))[0] == _abi.TRI_EINVAL
     assert _score(c, _kv(dtype=7))[0] == _abi.TRI_EINVAL
-    assert _score(c, _kv(k_scale=FAKE.value))[0] == _abi.TRI_EINVAL          # scale needs fp8 keys
+    assert _score(c, _kv(k_scale=FAKE.value))[0] == _abi.TRI_EINVAL          # scale needs 8-bit keys
+    cm, _om = _cfg(form=_abi.TRI_SCORE_MULTIPLICATIVE)
+    cbad, _ob = _cfg(form=2)
+    assert _score(cbad, _kv())[0] == _abi.TRI_EINVAL
+    assert _score(cm, _kv(), ws_query=True, mean_abs=None) == (_abi.TRI_OK, 0)    # not read by that form
+    assert _score(c, _kv(), mean_abs=None)[0] == _abi.TRI_EINVAL
     assert _score(c, _kv(dtype=_abi.TRI_FP8_E4M3), ws_query=True) == (_abi.TRI_OK, 0)
     assert _score(c, _kv(dtype=_abi.TRI_FP8_E4M3, k_scale=FAKE.value), ws_query=True) == (_abi.TRI_OK, 0)
     assert _score(c, _kv(dtype=_abi.TRI_INT8, k_scale=FAKE.value), ws_query=True) == (_abi.TRI_OK, 0)

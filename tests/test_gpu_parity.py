@@ -46,23 +46,25 @@ def bits(t):
     return t.cpu().numpy()
 
 
-def run_pass(dw, key_space="pre"):
+def run_pass(dw, key_space="pre", form="additive"):
     w = dw.w
     kv = dw.kv()
-    scores = tri.tri_score_keys(kv, dw.center, dw.mean_abs, rope_base=w.base, offsets=w.offsets,
-                                group=w.group, reduce=w.reduce, rope_layout=w.layout, key_space=key_space)
+    mean_abs = None if form == "multiplicative" else dw.mean_abs    # not read by that form
+    scores = tri.tri_score_keys(kv, dw.center, mean_abs, rope_base=w.base, offsets=w.offsets,
+                                group=w.group, reduce=w.reduce, rope_layout=w.layout, key_space=key_space,
+                                form=form)
     kept, kept_n = tri.tri_select_topb(scores, kv, w.budget, w.window)
     out = tri.tri_compact_kv(kv, kept, kept_n, w.budget)
     torch.cuda.synchronize()
     return scores, kept, kept_n, out
 
 
-def check_dense_unit(dw, s, l, h, sc_h, kept_h, kept_n_h, out_h):
+def check_dense_unit(dw, s, l, h, sc_h, kept_h, kept_n_h, out_h, key_space="pre", form="additive"):
     """sc_h etc. are host copies; checks one unit of a dense workload."""
     w, hp = dw.w, dw.hp
     L = int(hp.lengths[s])
     keys = P.host_rows(w, hp, s, l, h)
-    orc, S = P.oracle_scores(w, hp, s, l, h, keys)
+    orc, S = P.oracle_scores(w, hp, s, l, h, keys, key_space, form)
     worst, rel = P.check_scores(sc_h[s, l, h, :L], orc, S)
     P.check_kept(kept_h[s, l, h], sc_h[s, l, h], orc, S, L, w.budget, w.window)
     n = min(L, w.budget)
@@ -647,6 +649,99 @@ def test_full_gqa8b_32k_int8():
     rng = np.random.default_rng(107)
     units = [0, 1, w.n_units - 1] + _low_r_units(w, hp, 1) + [int(x) for x in rng.choice(w.n_units, 2, replace=False)]
     _full_dense("gqa8b_32k_int8", units)
+
+
+# ---------------------------------------------------------------------------------------
+# multiplicative score form: phase-only series times the centre and key norms
+# ---------------------------------------------------------------------------------------
+
+MULT_DENSE = {
+    "g4_max_half_bf16": (dict(n_seq=2, n_layer=2, n_kvh=2, group=4, max_len=2700, budget=600, window=64),
+                         [2700, 1500], "pre"),
+    "g3_mean_interleaved_f32": (dict(n_seq=1, n_layer=2, n_kvh=2, group=3, reduce="mean", layout="interleaved",
+                                     dtype="f32", max_len=1700, budget=300, window=16), [1700], "pre"),
+    "g8_max_half_fp8": (dict(n_seq=1, n_layer=1, n_kvh=2, group=8, dtype="fp8", max_len=1300, budget=200,
+                             window=8), [1300], "pre"),
+    "g1_half_int8": (dict(n_seq=2, n_layer=1, n_kvh=2, group=1, dtype="int8", max_len=1100, budget=128,
+                          window=32), [1100, 450], "pre"),
+    "g4_max_half_bf16_post": (dict(n_seq=1, n_layer=2, n_kvh=2, group=4, max_len=2100, budget=500, window=32),
+                              [2100], "post"),
+    "g6_max_interleaved_bf16_post": (dict(n_seq=2, n_layer=1, n_kvh=1, group=6, layout="interleaved",
+                                          max_len=1500, budget=256, window=0), [1500, 999], "post"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MULT_DENSE))
+def test_multiplicative_small_dense(name):
+    over, lengths, key_space = MULT_DENSE[name]
+    w = W.scaled(BASE, name="mult_" + name, **over)
+    log(f"multiplicative small dense {name}: {over} lengths={lengths} keys {key_space}-RoPE")
+    dw = SD.build(w, hp=W.make_params(w, lengths=lengths))
+    sc, kept, kept_n, out = host_outputs(*run_pass(dw, key_space, "multiplicative"))
+    worst = 0.0
+    for s in range(w.n_seq):
+        for l in range(w.n_layer):
+            for h in range(w.n_kvh):
+                e, _ = check_dense_unit(dw, s, l, h, sc, kept, kept_n, out, key_space, "multiplicative")
+                worst = max(worst, e)
+    log(f"  max score error / bound = {worst:.3e}")
+
+
+def test_multiplicative_small_paged():
+    w = W.scaled(W.WORKLOADS["paged_ragged64_bf16"], n_seq=3, n_layer=2, n_kvh=2, max_len=4200,
+                 len_range=(16, 4200))
+    lengths = [4200, 40, 2049]
+    log(f"multiplicative small paged lengths={lengths}")
+    dw = SD.build(w, hp=W.make_params(w, lengths=lengths))
+    sc, kept, kept_n, out = host_outputs(*run_pass(dw, "pre", "multiplicative"))
+    for s in range(w.n_seq):
+        L = lengths[s]
+        for l in range(w.n_layer):
+            for h in range(w.n_kvh):
+                keys = P.host_rows(w, dw.hp, s, l, h)
+                orc, S = P.oracle_scores(w, dw.hp, s, l, h, keys, "pre", "multiplicative")
+                P.check_scores(sc[s, l, h, :L], orc, S)
+                P.check_kept(kept[s, l, h], sc[s, l, h], orc, S, L, w.budget, w.window)
+        assert kept_n[s] == min(L, w.budget)
+
+
+def test_multiplicative_zero_and_nan_key_rows():
+    # zero keys score exactly 0 (no live band, ||k|| = 0); a NaN key scores NaN
+    w = W.scaled(BASE, name="mult_adv", n_seq=1, n_layer=1, n_kvh=1, group=4, max_len=600, budget=100, window=8)
+    hp = W.make_params(w)
+    keys = P.host_rows(w, hp, 0, 0, 0).copy()
+    keys[[5, 77, 300]] = 0.0
+    keys[400, 9] = np.nan
+    k = torch.from_numpy(synth.f32_to_bf16_bits(keys).view(np.int16).reshape(1, 1, 1, 600, 128).copy())
+    k = k.cuda().view(torch.bfloat16)
+    kv = tri.KVCache.dense(k, None, torch.tensor([600], dtype=torch.int32, device="cuda"))
+    sc = tri.tri_score_keys(kv, torch.from_numpy(hp.center).cuda(), None, rope_base=w.base, offsets=w.offsets,
+                            group=4, form="multiplicative").cpu().numpy()[0, 0, 0]
+    assert np.all(sc[[5, 77, 300]] == 0.0) and np.isnan(sc[400])
+    ok = np.ones(600, bool)
+    ok[[5, 77, 300, 400]] = False          # checked above; their bound S is 0
+    orc, S = P.oracle_scores(w, hp, 0, 0, 0, synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(keys)), "pre",
+                             "multiplicative")
+    P.check_scores(sc[ok], orc[ok], S[ok])
+
+
+def test_full_gqa8b_32k_bf16_multiplicative():
+    w = W.WORKLOADS["gqa8b_32k_bf16"]
+    hp = W.make_params(w)
+    log("full size gqa8b_32k_bf16, multiplicative form: building")
+    dw = SD.build(w)
+    scores, kept, kept_n, out = run_pass(dw, "pre", "multiplicative")
+    rng = np.random.default_rng(108)
+    units = [0, w.n_units - 1] + _low_r_units(w, hp, 1) + [int(x) for x in rng.choice(w.n_units, 2, replace=False)]
+    for u in units:
+        s, l, h = W.unit_coords(w, u)
+        log(f"  unit {u} (seq {s}, layer {l}, head {h})")
+        L = int(hp.lengths[s])
+        keys = P.host_rows(w, hp, s, l, h)
+        orc, S = P.oracle_scores(w, hp, s, l, h, keys, "pre", "multiplicative")
+        sc_h = scores[s, l, h].cpu().numpy()
+        P.check_scores(sc_h[:L], orc, S)
+        P.check_kept(kept[s, l, h].cpu().numpy(), sc_h, orc, S, L, w.budget, w.window)
 
 
 # ---------------------------------------------------------------------------------------
