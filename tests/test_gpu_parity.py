@@ -745,6 +745,79 @@ def test_full_gqa8b_32k_bf16_multiplicative():
 
 
 # ---------------------------------------------------------------------------------------
+# explicit query positions, and the longest supported unit
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("key_space", ["pre", "post"])
+def test_explicit_query_positions(key_space):
+    # the newest query ahead of the cache (tokens generated since the last pass) and behind it
+    w = W.scaled(BASE, name="qpos", n_seq=3, n_layer=1, n_kvh=2, group=4, max_len=1500, budget=256, window=16)
+    lengths = [1500, 900, 1200]
+    qpos = [1500 + 3000, 950, 700]
+    hp = W.make_params(w, lengths=lengths)
+    log(f"explicit query positions {qpos} (lengths {lengths}), keys {key_space}-RoPE")
+    dw = SD.build(w, hp=hp)
+    kv = dw.kv()
+    q = torch.tensor(qpos, dtype=torch.int64, device="cuda")
+    sc = tri.tri_score_keys(kv, dw.center, dw.mean_abs, rope_base=w.base, offsets=w.offsets, group=w.group,
+                            reduce=w.reduce, query_pos=q, key_space=key_space)
+    kept, kept_n = tri.tri_select_topb(sc, kv, w.budget, w.window)
+    torch.cuda.synchronize()
+    sc, kept = sc.cpu().numpy(), kept.cpu().numpy()
+    for s in range(w.n_seq):
+        L = lengths[s]
+        for h in range(w.n_kvh):
+            keys = P.host_rows(w, hp, s, 0, h)
+            center, mean_abs = oracle.unit_heads(hp.center, hp.mean_abs, 0, h, w.group)
+            orc = oracle.score_keys(keys, center, mean_abs, base=w.base, offsets=w.offsets, query_pos=qpos[s],
+                                    layout=w.layout, reduce=w.reduce, key_space=key_space)
+            S = oracle.score_magnitude_bound(keys, center, mean_abs, layout=w.layout, reduce=w.reduce)
+            P.check_scores(sc[s, 0, h, :L], orc, S)
+            P.check_kept(kept[s, 0, h], sc[s, 0, h], orc, S, L, w.budget, w.window)
+
+
+def test_longest_supported_unit_sampled():
+    # one unit of 2^20 keys (the largest per-unit length the library accepts): float64
+    # anchors keep the phase exact at large positions; scores are checked on sampled row
+    # blocks, the selection exactly against the GPU's own scores and, outside the threshold
+    # band, against the sampled oracle scores
+    L = 1 << 20
+    w = W.scaled(BASE, name="max_unit", n_seq=1, n_layer=1, n_kvh=1, group=4, max_len=L, budget=4096,
+                 window=256, offsets=W.geometric_offsets(14))
+    hp = W.make_params(w)
+    log("longest unit: 1 x 1048576 keys, building")
+    dw = SD.build(w, hp=hp)
+    sc, kept, kept_n, _ = run_pass(dw)
+    sc, kept = sc.cpu().numpy()[0, 0, 0], kept.cpu().numpy()[0, 0, 0]
+    assert int(kept_n.cpu()[0]) == w.budget
+    exact = oracle.select_top_b(sc.astype(np.float64), L, w.budget, w.window)
+    assert np.array_equal(kept, exact)
+    center, mean_abs = oracle.unit_heads(hp.center, hp.mean_abs, 0, 0, w.group)
+    cand = L - w.window
+    tau = np.sort(sc[:cand])[::-1][w.budget - w.window - 1]
+    kept_set = set(kept.tolist())
+    worst = 0.0
+    for r0 in [0, 4096, 131072 - 32, 524288 + 7, 1000000, L - 1024, L - 300]:
+        n = min(256, L - r0)
+        rows = synth.rows_as_float(w.seed, synth.TAG_K, 0, n, hp.mu_k[0, 0], hp.sigma, w.sink, w.dtype, row_start=r0)
+        pos = np.arange(r0, r0 + n)
+        orc = oracle.score_keys(rows, center, mean_abs, base=w.base, offsets=w.offsets, key_pos=pos,
+                                query_pos=L - 1, layout=w.layout, reduce=w.reduce)
+        S = oracle.score_magnitude_bound(rows, center, mean_abs, layout=w.layout, reduce=w.reduce)
+        e, _ = P.check_scores(sc[r0:r0 + n], orc, S)
+        worst = max(worst, e)
+        for j in range(n):
+            p = r0 + j
+            if p >= cand:
+                assert p in kept_set                      # the window is always kept
+            elif orc[j] > tau + P.SCORE_TOL * S[j]:
+                assert p in kept_set
+            elif orc[j] < tau - P.SCORE_TOL * S[j]:
+                assert p not in kept_set
+    log(f"  max score error / bound over sampled blocks = {worst:.3e}")
+
+
+# ---------------------------------------------------------------------------------------
 # calls enqueued on a non-default stream give the default stream's results
 # ---------------------------------------------------------------------------------------
 
