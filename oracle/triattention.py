@@ -206,9 +206,9 @@ def _trig_term(k_bands, key_pos, query_pos, center_h, theta, offsets):
 def _trig_unit_term(k_bands, key_pos, query_pos, center_h, theta, offsets):
     """mean_Delta sum_f cos(d theta_f + arg E q_f - arg k_f), d = Q - p + Delta (phases only).
 
-    The series of [Review] "Core Mechanism" ("score(d) = cos(d theta_1) + cos(d theta_2) +
-    ...") before its norm weighting: each band contributes the cosine of its phase
-    difference at the distance, with unit amplitude.  A band whose centre or key part is 0
+    The review's series in the distance ([Review] "Core Mechanism": one cosine per frequency
+    band, summed, before the norm weighting): each band contributes the cosine of its
+    phase difference at the distance, with unit amplitude.  A band whose centre or key part is 0
     has no phase and contributes 0.
     """
     q_arg = np.arctan2(center_h.imag, center_h.real)          # arg E[q_f]      [F]
