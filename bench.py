@@ -137,14 +137,19 @@ def cpu_baseline(name, n_units, key_space="pre", form="additive"):
                     break
     except OSError:
         pass
+    hp = W.make_params(w)
+    pass_keys = int(np.sum(np.minimum(hp.lengths, w.max_len))) * w.n_layer * w.n_kvh
     return {
         "value": rate,
         "unit": "Gkeys/s",
         "cores": workers,
         "kind": "oracle",
+        "per_core_value": keys / busy / 1e9,
+        "full_pass_s": pass_keys / (rate * 1e9),
         "sample": (f"{len(jobs)} random units of {name} ({keys} keys; score+select+compact per unit, "
                    f"float64 numpy, one single-threaded process per core; wall {wall:.1f} s, "
-                   f"oracle time {busy:.1f} core-s) on {cpu}"),
+                   f"oracle time {busy:.1f} core-s) on {cpu}; full_pass_s extrapolates to all "
+                   f"{pass_keys} keys at this rate"),
     }
 
 
