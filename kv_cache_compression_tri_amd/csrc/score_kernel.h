@@ -144,19 +144,6 @@ __device__ __forceinline__ float sum8(float v) {
   return v;
 }
 
-// Weight of query head row `row` (= layer * n_qh + hq), band f at anchor
-// A = C_f e^{i(Q - p_a) theta_f}.
-__device__ __forceinline__ void head_weight(const ScoreParams& P, int64_t row, int f, float ar, float ai,
-                                            float& wr, float& wi, float& nc) {
-  const int64_t idx = row * kBands + f;
-  const float2 c = reinterpret_cast<const float2*>(P.center)[idx];
-  const float m = P.mean_abs[idx];
-  wr = c.x * ar - c.y * ai;
-  wi = c.x * ai + c.y * ar;
-  // (1 - R_f) m_f = m_f - |c_f|; a band with m_f = 0 carries no norm term
-  nc = (m > 0.0f) ? m - __builtin_sqrtf(c.x * c.x + c.y * c.y) : 0.0f;
-}
-
 // LDS phase table: entry (r, f), r < kChunk, holds (c, s) = e^{-i r theta_f} as float32.
 // Step it = r / 8, key kk = r % 8, band group g = f / 8 and band b = f % 8 are arranged so
 // that the 64 lanes of a step read 64 consecutive 16-byte slots per instruction (one slot
@@ -327,6 +314,55 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
 #pragma unroll
     for (int i = 0; i < PF; ++i) load_step(i, ring[i]);
 
+    float wr[GE][8], wn[GE][8], nn[MULT ? 1 : GE][8];
+    const int64_t hrow0 = int64_t(l) * n_qh + int64_t(h) * P.group;
+    if constexpr (!MULT) {
+      // per-head statistics of the lane's bands, loaded into the weight registers before the
+      // float64 anchor work so that their latency overlaps it (turned into weights below)
+      const float2* c2 = reinterpret_cast<const float2*>(P.center);
+      if (!P.reduce_mean) {
+#pragma unroll
+        for (int hh = 0; hh < GE; ++hh)
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+            const int64_t idx = (hrow0 + hh) * kBands + g * 8 + b;
+            const float2 c = c2[idx];
+            wr[hh][b] = c.x;
+            wn[hh][b] = c.y;
+            nn[hh][b] = P.mean_abs[idx];
+          }
+      } else {
+        // mean over the group: W and N are linear in the head statistics, so the centres
+        // and norm weights are averaged first and the anchor is applied once below
+#pragma unroll
+        for (int b = 0; b < 8; ++b) wr[0][b] = wn[0][b] = nn[0][b] = 0.0f;
+        for (int hh = 0; hh < P.group; ++hh) {
+          float2 c[8];
+          float m[8];
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+            const int64_t idx = (hrow0 + hh) * kBands + g * 8 + b;
+            c[b] = c2[idx];
+            m[b] = P.mean_abs[idx];
+          }
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+            wr[0][b] += c[b].x;
+            wn[0][b] += c[b].y;
+            // (1 - R_f) m_f = m_f - |c_f|; a band with m_f = 0 carries no norm term
+            nn[0][b] += (m[b] > 0.0f) ? m[b] - __builtin_sqrtf(c[b].x * c[b].x + c[b].y * c[b].y) : 0.0f;
+          }
+        }
+        const float inv = 1.0f / float(P.group);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          wr[0][b] *= inv;
+          wn[0][b] *= inv;
+          nn[0][b] *= inv;
+        }
+      }
+    }
+
     {  // anchor of this segment (float64), one band per lane; after RoPE the anchor is 0
       const double ang = double(POST ? Q : Q - p0) * P.theta[lane];
       double sa, ca;
@@ -336,8 +372,6 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
     }
     __builtin_amdgcn_wave_barrier();
 
-    float wr[GE][8], wn[GE][8], nn[MULT ? 1 : GE][8];
-    const int64_t hrow0 = int64_t(l) * n_qh + int64_t(h) * P.group;
     if constexpr (MULT) {
       // multiplicative form: the weight of band f is (c_f / |c_f|) ||c|| C_f A_f (a centre
       // band of 0 has no phase and weighs 0); ||c|| sums |c_f|^2 over the 8 lanes of a key
@@ -394,27 +428,17 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
     for (int b = 0; b < 8; ++b) {
       const int f = g * 8 + b;
       const float2 A = anc[wave][f];
-      if (P.reduce_mean) {
-        float sr = 0.0f, si = 0.0f, sn = 0.0f;
-        for (int hh = 0; hh < P.group; ++hh) {
-          float r0, i0, n0;
-          head_weight(P, hrow0 + hh, f, A.x, A.y, r0, i0, n0);
-          sr += r0;
-          si += i0;
-          sn += n0;
-        }
-        const float inv = 1.0f / float(P.group);
-        wr[0][b] = sr * inv;
-        wn[0][b] = -si * inv;
-        nn[0][b] = sn * inv;
+      if (P.reduce_mean) {   // group-mean centre (already averaged) times the anchor
+        const float cx = wr[0][b], cy = wn[0][b];
+        wr[0][b] = cx * A.x - cy * A.y;
+        wn[0][b] = -(cx * A.y + cy * A.x);
       } else {
 #pragma unroll
-        for (int hh = 0; hh < GE; ++hh) {
-          float r0, i0, n0;
-          head_weight(P, hrow0 + hh, f, A.x, A.y, r0, i0, n0);
-          wr[hh][b] = r0;
-          wn[hh][b] = -i0;
-          nn[hh][b] = n0;
+        for (int hh = 0; hh < GE; ++hh) {   // W = c A
+          const float cx = wr[hh][b], cy = wn[hh][b], m = nn[hh][b];
+          wr[hh][b] = cx * A.x - cy * A.y;
+          wn[hh][b] = -(cx * A.y + cy * A.x);
+          nn[hh][b] = (m > 0.0f) ? m - __builtin_sqrtf(cx * cx + cy * cy) : 0.0f;   // (1 - R_f) m_f
         }
       }
     }
