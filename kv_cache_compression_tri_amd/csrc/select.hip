@@ -144,18 +144,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void se
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sc), (short)0, L * 4, 0x00020000);
 
   uint32_t u[kBatchTiles][kVec];
-  auto load = [&](int t0) __attribute__((always_inline)) {
+  // raw scores of the tiles from t0 into r (no waiting here: the loads stay in flight)
+  auto issue = [&](int t0, uint32_t (&r)[kBatchTiles][kVec]) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < kBatchTiles; ++t) {
       if (t0 + t < n_tiles) {
         const int j = r0 + (t0 + t) * kTile + lane * kVec;
         const uint4 q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, j * 4, 0, 0));
-        u[t][0] = q.x;
-        u[t][1] = q.y;
-        u[t][2] = q.z;
-        u[t][3] = q.w;
+        r[t][0] = q.x;
+        r[t][1] = q.y;
+        r[t][2] = q.z;
+        r[t][3] = q.w;
       }
     }
+  };
+  // scores in u -> order keys, with the window and padding sentinels
+  auto to_keys = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < kBatchTiles; ++t) {
       const int jt = r0 + (t0 + t) * kTile;
@@ -174,11 +178,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void se
     }
   };
   // body(t, jt) runs for every tile of the wave with keys u[t][*] of slots jt + 4*lane + e;
-  // the scheduling barrier keeps the tiles in order so that ballots do not pile up in SGPRs
+  // the scheduling barrier keeps the tiles in order so that ballots do not pile up in SGPRs.
+  // Streaming: the next batch's loads are issued into a second buffer before the current
+  // batch is processed, so their latency overlaps the work instead of stalling each batch.
   auto sweep = [&](auto&& body) __attribute__((always_inline)) {
     if constexpr (kStream) {
+      uint32_t nxt[kBatchTiles][kVec];
+      issue(0, nxt);
       for (int t0 = 0; t0 < n_tiles; t0 += kBatchTiles) {
-        load(t0);
+#pragma unroll
+        for (int t = 0; t < kBatchTiles; ++t)
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) u[t][e] = nxt[t][e];
+        to_keys(t0);
+        if (t0 + kBatchTiles < n_tiles) issue(t0 + kBatchTiles, nxt);
 #pragma unroll
         for (int t = 0; t < kBatchTiles; ++t) {
           if (t0 + t < n_tiles) body(t, r0 + (t0 + t) * kTile);
@@ -193,7 +206,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void se
       }
     }
   };
-  if constexpr (!kStream) load(0);
+  if constexpr (!kStream) {
+    issue(0, u);
+    to_keys(0);
+  }
 
   // kept: key > tau, or key == tau and slot <= jstar (jstar = -1 when all ties at tau are
   // kept, i.e. the threshold is key >= tau + 1)
