@@ -198,3 +198,43 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(_abi, "_LIB", None)
     with pytest.raises(RuntimeError, match="missing"):
         _abi.lib(os.path.join(ROOT, "no_such_dir", "libtri.so"))
+
+
+def test_header_is_c99_and_struct_layouts_match_the_binding(tmp_path):
+    """include/tri.h compiles as strict C99, a C program links against libtri.so and calls it,
+    and the struct layouts the C compiler sees are the ones the ctypes binding uses."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "abi_check.c"
+    src.write_text(r'''
+#include <stddef.h>
+#include <stdio.h>
+#include "tri.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(tri_kv), offsetof(tri_kv, max_len), offsetof(tri_kv, block_table),
+         offsetof(tri_kv, pos), offsetof(tri_kv, k_scale), sizeof(tri_score_cfg));
+  printf("%zu %zu %zu %zu\n", offsetof(tri_score_cfg, offsets), offsetof(tri_score_cfg, group),
+         offsetof(tri_score_cfg, key_space), offsetof(tri_score_cfg, form));
+  printf("%d %d %d\n", tri_version(), tri_score_keys(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL),
+         TRI_VERSION);
+  return 0;
+}
+''')
+    lib_dir = os.path.dirname(_abi.LIB_PATH)
+    exe = tmp_path / "abi_check"
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", f"-I{os.path.join(ROOT, 'include')}",
+           str(src), "-o", str(exe), f"-L{lib_dir}", "-ltri", f"-Wl,-rpath,{lib_dir}",
+           "-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stderr
+    lines = [list(map(int, ln.split())) for ln in out.stdout.strip().splitlines()]
+    K, C = _abi.TriKV, _abi.TriScoreCfg
+    assert lines[0] == [ctypes.sizeof(K), K.max_len.offset, K.block_table.offset, K.pos.offset, K.k_scale.offset,
+                        ctypes.sizeof(C)]
+    assert lines[1] == [C.offsets.offset, C.group.offset, C.key_space.offset, C.form.offset]
+    assert lines[2][0] == lines[2][2] and lines[2][1] == _abi.TRI_EINVAL
