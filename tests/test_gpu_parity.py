@@ -745,6 +745,74 @@ def test_full_gqa8b_32k_bf16_multiplicative():
 
 
 # ---------------------------------------------------------------------------------------
+# seeded random combinations of every option, small enough for the oracle on every unit
+# ---------------------------------------------------------------------------------------
+
+def _random_case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    dtype = ["f32", "bf16", "fp8", "int8"][rng.integers(4)]
+    paged = bool(rng.integers(2))
+    group = int(rng.integers(1, 9))
+    over = dict(name=f"mix{seed}", n_seq=int(rng.integers(1, 4)), n_layer=int(rng.integers(1, 3)),
+                n_kvh=int(rng.integers(1, 3)), group=group, dtype=dtype,
+                layout=["half", "interleaved"][rng.integers(2)], reduce=["max", "mean"][rng.integers(2)],
+                max_len=int(rng.integers(300, 2600)), budget=int(16 * rng.integers(2, 40)),
+                window=int(rng.integers(0, 200)), base=float([1e4, 5e5, 1e6][rng.integers(3)]),
+                offsets=W.geometric_offsets(int(rng.integers(0, 15))), seed=int(50 + seed),
+                low_r_frac=float(rng.uniform(0, 0.5)), sink=bool(rng.integers(2)))
+    if paged:
+        w = W.scaled(W.WORKLOADS["paged_ragged64_bf16"], len_range=(1, over["max_len"]), **over)
+    else:
+        w = W.scaled(BASE, **over)
+    lengths = [int(x) for x in rng.integers(0, w.max_len + 1, w.n_seq)]
+    lengths[int(rng.integers(w.n_seq))] = w.max_len
+    key_space = ["pre", "post"][rng.integers(2)]
+    form = ["additive", "multiplicative"][rng.integers(2)]
+    return w, lengths, key_space, form
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_option_mix(seed):
+    w, lengths, key_space, form = _random_case(seed)
+    log(f"mix {seed}: {w.dtype} {'paged' if w.paged else 'dense'} {w.layout} G={w.group} {w.reduce} "
+        f"B={w.budget} W={w.window} |D|={len(w.offsets)} base={w.base:g} keys {key_space}-RoPE {form} "
+        f"lengths={lengths}")
+    dw = SD.build(w, hp=W.make_params(w, lengths=lengths))
+    k_before, v_before = bits(dw.k), bits(dw.v)
+    sc, kept, kept_n, out = host_outputs(*run_pass(dw, key_space, form))
+    exp_k, exp_v = k_before.copy(), v_before.copy()
+    for s in range(w.n_seq):
+        L = lengths[s]
+        n = min(L, w.budget)
+        assert kept_n[s] == n and out["new_len"][s] == n
+        kept_units = {}
+        for l in range(w.n_layer):
+            for h in range(w.n_kvh):
+                keys = P.host_rows(w, dw.hp, s, l, h)
+                orc, S = P.oracle_scores(w, dw.hp, s, l, h, keys, key_space, form)
+                live = S > 0
+                P.check_scores(sc[s, l, h, :L][live], orc[live], S[live])
+                assert np.all(sc[s, l, h, :L][~live] == 0.0)
+                P.check_kept(kept[s, l, h], sc[s, l, h], orc, S, L, w.budget, w.window)
+                kk = kept[s, l, h, :n]
+                assert np.array_equal(out["pos_out"][s, l, h, :n], kk)
+                if w.paged:
+                    kept_units[(l, h)] = kk
+                else:
+                    assert np.array_equal(out["k_out"][s, l, h, :n], P.host_bits(w, dw.hp, s, l, h)[kk])
+                    assert np.array_equal(out["v_out"][s, l, h, :n],
+                                          P.host_bits(w, dw.hp, s, l, h, tag=synth.TAG_V)[kk])
+        if w.paged:
+            ek, ev, freed, new_len = oracle.compact_paged_sequence(exp_k, exp_v, dw.hp.block_table[s], L,
+                                                                   kept_units, 16)
+            exp_k, exp_v = ek, ev
+            nf = int(out["n_freed"][s])
+            assert new_len == n and nf == len(freed) and np.array_equal(out["freed"][s, :nf], freed)
+    if w.paged:
+        assert np.array_equal(bits(dw.k), exp_k) and np.array_equal(bits(dw.v), exp_v)
+
+
+# ---------------------------------------------------------------------------------------
 # explicit query positions, and the longest supported unit
 # ---------------------------------------------------------------------------------------
 
