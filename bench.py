@@ -32,6 +32,20 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+# non-packed fp32 vector issue of MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (lane operations / s)
+PEAK_VALU_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+
+def score_lane_ops_per_key(group_eff: int, key_space: str, form: str) -> int:
+    """Vector lane operations the score needs per key, counting only the arithmetic of the
+    method (per band: rotation by the phase table 4 (pre-RoPE keys only), |k_f|^2 and its
+    square root 3, and per effective head 3 multiply-adds (multiplicative form: |k_f|^2 2,
+    reciprocal square root 1, unit scaling 2, and 2 per head)); unpacking, reductions and
+    addressing are overhead."""
+    rot = 4 if key_space == "pre" else 0
+    if form == "multiplicative":
+        return 64 * (rot + 5 + 2 * group_eff)
+    return 64 * (rot + 3 + 3 * group_eff)
 METRIC = "Gkeys/s scored+selected+compacted at 32K ctx; % of HBM roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic.json")
 SCORE_SRC = os.path.join(ROOT, "kv_cache_compression_tri_amd", "csrc", "score_kernel.h")
@@ -281,6 +295,8 @@ def main():
     compact_bytes = kept_rows * w.head_dim * elt * 2 * 2 if compacts else 0   # K and V, read + write
     pass_bytes = score_bytes + compact_bytes
     achieved = score_bytes / (score_ms * 1e-3) / 1e9
+    lane_ops = score_lane_ops_per_key(1 if w.reduce == "mean" else w.group, args.key_space, args.form)
+    alu_achieved = lane_ops * keys_per_step / (score_ms * 1e-3) / 1e12
     value = keys_per_step / (ms * 1e-3) / 1e9
     traffic = recorded_traffic(name) if (args.key_space == "pre" and args.form == "additive") else None
     line = {
@@ -315,6 +331,15 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": score_bytes,
             "avg_launch_ms": score_ms,
+        },
+        "alu": {
+            "bound": "alu",
+            "kernel": "score_kernel",
+            "lane_ops_per_key": lane_ops,
+            "achieved": alu_achieved,
+            "peak": PEAK_VALU_TLANEOPS,
+            "unit": "Tlane-op/s",
+            "frac": alu_achieved / PEAK_VALU_TLANEOPS,
         },
         "pass": {
             "algorithmic_bytes": pass_bytes,
