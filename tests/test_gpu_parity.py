@@ -886,6 +886,102 @@ def test_longest_supported_unit_sampled():
 
 
 # ---------------------------------------------------------------------------------------
+# the three calls captured in a HIP graph: the library allocates nothing and issues no
+# memsets, so a captured pass replays to the eager results
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_graph_capture_replays_match_eager(paged):
+    if paged:
+        w = W.scaled(W.WORKLOADS["paged_ragged64_bf16"], name="graph_paged", n_seq=3, n_layer=2, n_kvh=2,
+                     max_len=3000, len_range=(16, 3000), budget=512, window=32)
+        lengths = [3000, 700, 2049]
+    else:
+        w = W.scaled(BASE, name="graph_dense", n_seq=2, n_layer=2, n_kvh=2, max_len=2500, budget=400, window=32)
+        lengths = [2500, 1333]
+    log(f"graph capture, {'paged (in place)' if paged else 'dense'} lengths={lengths}")
+    dw = SD.build(w, hp=W.make_params(w, lengths=lengths))
+    kv = dw.kv()
+    dev = dw.k.device
+    slots = kv.slots
+    scores = torch.empty((w.n_seq, w.n_layer, w.n_kvh, slots), dtype=torch.float32, device=dev)
+    kept = torch.empty((w.n_seq, w.n_layer, w.n_kvh, w.budget), dtype=torch.int32, device=dev)
+    kept_n = torch.empty((w.n_seq,), dtype=torch.int32, device=dev)
+    pos_out = torch.empty((w.n_seq, w.n_layer, w.n_kvh, w.budget), dtype=torch.int32, device=dev)
+    new_len = torch.empty((w.n_seq,), dtype=torch.int32, device=dev)
+    if paged:
+        k_out = v_out = None
+        freed = torch.empty((w.n_seq, w.max_pages), dtype=torch.int32, device=dev)
+        n_freed = torch.empty((w.n_seq,), dtype=torch.int32, device=dev)
+    else:
+        k_out = torch.empty((w.n_seq, w.n_layer, w.n_kvh, w.budget, 128), dtype=dw.k.dtype, device=dev)
+        v_out = torch.empty_like(k_out)
+        freed = n_freed = None
+
+    def one_pass(stream):
+        tri.tri_score_keys(kv, dw.center, dw.mean_abs, rope_base=w.base, offsets=w.offsets, group=w.group,
+                           reduce=w.reduce, scores=scores, stream=stream)
+        tri.tri_select_topb(scores, kv, w.budget, w.window, kept=kept, kept_n=kept_n, stream=stream)
+        tri.tri_compact_kv(kv, kept, kept_n, w.budget, k_out=k_out, v_out=v_out, pos_out=pos_out, freed=freed,
+                           n_freed=n_freed, new_len=new_len, stream=stream)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        out = [scores.clone(), kept.clone(), kept_n.clone(), pos_out.clone(), new_len.clone()]
+        if paged:
+            out += [freed.clone(), n_freed.clone(), dw.k.clone(), dw.v.clone()]
+        else:
+            out += [k_out.clone(), v_out.clone()]
+        return out
+
+    def restore():
+        if paged:   # in-place compaction rewrote the pools
+            SD.fill(w, dw.hp, dw.k, dw.v, dw.seq_len, dw.block_table)
+        torch.cuda.synchronize()
+
+    restore()
+    one_pass(torch.cuda.current_stream())
+    ref = snapshot()
+    restore()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            one_pass(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        restore()
+        scores.fill_(-1.0)      # eager work between replays
+        kept.fill_(-7)
+        graph.replay()
+        got = snapshot()
+        for i, (a, b) in enumerate(zip(ref, got)):
+            if i == 0:   # only slots < seq_len hold scores
+                for s, L in enumerate(lengths):
+                    assert torch.equal(a[s, ..., :L], b[s, ..., :L]), f"replay {rep}: scores differ"
+            elif not paged and i >= 5:
+                for s, L in enumerate(lengths):
+                    n = min(L, w.budget)
+                    assert torch.equal(a[s, :, :, :n].view(torch.int16), b[s, :, :, :n].view(torch.int16))
+            elif paged and i == 5:
+                for s in range(w.n_seq):
+                    nf = int(ref[6][s])
+                    assert torch.equal(a[s, :nf], b[s, :nf])
+            elif i == 3:
+                for s, L in enumerate(lengths):
+                    n = min(L, w.budget)
+                    assert torch.equal(a[s, :, :, :n], b[s, :, :, :n])
+            else:
+                assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else
+                                   (a.view(torch.int16) if a.dtype == torch.bfloat16 else a),
+                                   b.view(torch.int32) if b.dtype == torch.float32 else
+                                   (b.view(torch.int16) if b.dtype == torch.bfloat16 else b)), \
+                    f"replay {rep}: output {i} differs"
+
+
+# ---------------------------------------------------------------------------------------
 # calls enqueued on a non-default stream give the default stream's results
 # ---------------------------------------------------------------------------------------
 
