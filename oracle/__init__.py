@@ -18,4 +18,5 @@ from .triattention import (  # noqa: F401
     compact_paged_sequence,
     calibrate,
     unit_heads,
+    decode_attention,
 )

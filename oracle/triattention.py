@@ -65,6 +65,7 @@ __all__ = [
     "compact_paged_sequence",
     "calibrate",
     "unit_heads",
+    "decode_attention",
 ]
 
 
@@ -447,3 +448,43 @@ def compact_paged_sequence(pool_k, pool_v, block_table_row, length: int, kept_by
     used_after = -(-int(new_len) // page)
     freed = bt[used_after:used_before].copy()
     return out_k, out_v, freed, int(new_len)
+
+
+# ---------------------------------------------------------------------------------------
+# The consumer of the compressed cache: RoPE at the kept keys' positions, then attention
+# ---------------------------------------------------------------------------------------
+
+def decode_attention(q, keys, values, *, base: float, key_pos, query_pos: int,
+                     layout: str = "half", key_space: str = "pre") -> np.ndarray:
+    """Attention of the newest token's query heads over a (compressed) cache.
+
+    After compression the surviving keys are rotated by RoPE at their own positions and
+    read by standard attention ([Review] "Core Mechanism": apply RoPE, then attention on
+    the compressed cache); compacted slots no longer equal positions, so the positions
+    come from the compaction's position output.
+
+    q:        [G, d] pre-RoPE query vectors of the query heads reading this KV head,
+              at position query_pos
+    keys:     [L, d] cached keys, pre-RoPE (key_space "pre", rotated here at key_pos) or
+              already rotated at their positions (key_space "post")
+    values:   [L, d]
+    key_pos:  [L] RoPE positions of the cached keys
+
+    Returns float64 [G, d]: softmax_j((R(Q) q) . (R(p_j) k_j) / sqrt(d)) weighted sum of the
+    values (zeros when L = 0).
+    """
+    q = np.atleast_2d(np.asarray(q, dtype=np.float64))
+    keys = np.asarray(keys, dtype=np.float64)
+    values = np.asarray(values, dtype=np.float64)
+    G, d = q.shape
+    L = keys.shape[0]
+    if L == 0:
+        return np.zeros((G, d))
+    key_pos = np.asarray(key_pos, dtype=np.int64)
+    q_rot = rope_apply(q, np.full(G, query_pos), base=base, layout=layout)
+    k_rot = keys if key_space == "post" else rope_apply(keys, key_pos, base=base, layout=layout)
+    logits = q_rot @ k_rot.T / np.sqrt(d)                                   # [G, L]
+    logits = logits - logits.max(axis=1, keepdims=True)
+    w = np.exp(logits)
+    w /= w.sum(axis=1, keepdims=True)
+    return w @ values

@@ -50,11 +50,15 @@ def _pin_calls():
         pins.test_p7_paged_forward_packing,
         pins.test_p10_fp8_e4m3_values_fixed_by_the_format,
         pins.test_p11_hand_value_two_bands,
+        pins.test_p12_one_key_returns_its_value,
+        pins.test_p12_equal_logits_average_the_values,
         pins.test_p11_band_magnitudes_enter_only_through_the_key_norm,
     ]
     for layout in ("half", "interleaved"):
         calls.append(lambda layout=layout: pins.test_p11_aligned_phases_closed_form(layout))
         calls.append(lambda layout=layout: pins.test_p11_single_band_centre_matches_amplitude_series(layout))
+        calls.append(lambda layout=layout: pins.test_p12_hand_weighting_three_to_one(layout))
+        calls.append(lambda layout=layout: pins.test_p12_relative_positions_and_post_rope_keys(layout))
     calls += [lambda t=t: pins.test_p5_select_matches_brute_force(t) for t in range(60)]
     with open(golden.GOLDEN) as fh:
         import json
@@ -210,6 +214,19 @@ def _unit_series_phase_sign(k_bands, key_pos, query_pos, center_h, theta, offset
     return T.__dict__["_orig_unit"](np.conj(k_bands), key_pos, query_pos, center_h, theta, offsets)
 
 
+def _attention_key_not_rotated(q, keys, values, *, base, key_pos, query_pos, layout="half", key_space="pre"):
+    # slip: the kept keys are used without RoPE at their positions
+    return T.__dict__["_orig_attn"](q, keys, values, base=base, key_pos=key_pos, query_pos=query_pos,
+                                     layout=layout, key_space="post")
+
+
+def _attention_no_scale(q, keys, values, *, base, key_pos, query_pos, layout="half", key_space="pre"):
+    # slip: logits not divided by sqrt(d)
+    return T.__dict__["_orig_attn"](np.asarray(q, dtype=np.float64) * np.sqrt(np.asarray(q).shape[-1]), keys,
+                                     values, base=base, key_pos=key_pos, query_pos=query_pos, layout=layout,
+                                     key_space=key_space)
+
+
 def _l2_as_l1(bands):
     # slip: the norm of the vector taken as the sum of band magnitudes
     return np.sum(np.abs(bands), axis=-1)
@@ -240,6 +257,8 @@ MUTATIONS = {
     "mult_amplitude_kept": ("_trig_unit_term", _unit_series_amplitude_kept),
     "mult_phase_sign": ("_trig_unit_term", _unit_series_phase_sign),
     "mult_norm_l1": ("_l2_norm", _l2_as_l1),
+    "attention_key_not_rotated": ("decode_attention", _attention_key_not_rotated),
+    "attention_no_scale": ("decode_attention", _attention_no_scale),
 }
 
 
@@ -253,6 +272,7 @@ def test_mutation_is_caught(name, monkeypatch):
     monkeypatch.setitem(T.__dict__, "_orig_compact", T.compact_paged_sequence)
     monkeypatch.setitem(T.__dict__, "_orig_decode_fp8", T.decode_fp8_e4m3)
     monkeypatch.setitem(T.__dict__, "_orig_unit", T._trig_unit_term)
+    monkeypatch.setitem(T.__dict__, "_orig_attn", T.decode_attention)
     monkeypatch.setattr(T, attr, repl)
     if hasattr(oracle, attr):
         monkeypatch.setattr(oracle, attr, repl)

@@ -14,6 +14,9 @@ Each test states what it pins.  Nothing here calls the HIP library.
   P10 fp8 (OCP E4M3) key codes: values the format definition fixes
   P11 multiplicative form: hand value, aligned-phase closed form, the single-band
       identity with the amplitude series, and scaling by the key norm
+  P12 attention over the compressed cache: one key returns its value, equal logits
+      average the values, a hand-made 3:1 weighting, the relative-position property
+      against textbook RoPE, and post-RoPE keys give the same result
 """
 
 import itertools
@@ -574,3 +577,66 @@ def test_p11_band_magnitudes_enter_only_through_the_key_norm():
     assert np.allclose(s1, s0 * ratio, rtol=1e-10, atol=1e-12)
     S = oracle.score_magnitude_bound(keys, c, np.ones((2, d // 2)), reduce="mean", form="multiplicative")
     assert np.all(np.abs(s0) <= S)
+
+
+# ---------------------------------------------------------------------------------------
+# P12 attention over the compressed cache (RoPE at the kept positions, then softmax)
+# ---------------------------------------------------------------------------------------
+
+def test_p12_one_key_returns_its_value():
+    rng = np.random.default_rng(51)
+    q, k, v = rng.standard_normal((3, 128)), rng.standard_normal((1, 128)), rng.standard_normal((1, 128))
+    out = oracle.decode_attention(q, k, v, base=1e6, key_pos=[777], query_pos=5000)
+    assert np.allclose(out, np.repeat(v, 3, axis=0), rtol=0, atol=1e-14)
+
+
+def test_p12_equal_logits_average_the_values():
+    rng = np.random.default_rng(52)
+    k = np.repeat(rng.standard_normal((1, 128)), 5, axis=0)
+    v = rng.standard_normal((5, 128))
+    out = oracle.decode_attention(rng.standard_normal((2, 128)), k, v, base=1e4, key_pos=[40] * 5, query_pos=90)
+    assert np.allclose(out, np.repeat(v.mean(axis=0, keepdims=True), 2, axis=0), atol=1e-13)
+    assert np.array_equal(oracle.decode_attention(np.ones((2, 128)), k[:0], v[:0], base=1e4, key_pos=[],
+                                                  query_pos=3), np.zeros((2, 128)))
+
+
+@pytest.mark.parametrize("layout", ["half", "interleaved"])
+def test_p12_hand_weighting_three_to_one(layout):
+    # at zero distance RoPE cancels: logits are q.k / sqrt(d); two keys along q whose logits
+    # differ by ln 3 get weights 3/4 and 1/4
+    d = 128
+    q = np.zeros((1, d))
+    q[0, 5] = 2.0
+    a = 1.0
+    b = a - math.log(3.0) * math.sqrt(d) / 2.0
+    k = np.zeros((2, d))
+    k[0, 5], k[1, 5] = a, b
+    v = np.stack([np.full(d, 4.0), np.full(d, -8.0)])
+    out = oracle.decode_attention(q, k, v, base=1e6, key_pos=[321, 321], query_pos=321, layout=layout)
+    assert np.allclose(out, 0.75 * 4.0 + 0.25 * -8.0, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("layout", ["half", "interleaved"])
+def test_p12_relative_positions_and_post_rope_keys(layout):
+    # logits depend on the query-key distance only (textbook RoPE), and keys cached after
+    # RoPE at their positions give the same attention
+    rng = np.random.default_rng(53)
+    d, L, base = 128, 40, 1e4
+    q = rng.standard_normal((2, d))
+    k = rng.standard_normal((L, d))
+    v = rng.standard_normal((L, d))
+    pos = np.sort(rng.choice(6000, L, replace=False))
+    Q = 7000
+    out = oracle.decode_attention(q, k, v, base=base, key_pos=pos, query_pos=Q, layout=layout)
+    shifted = oracle.decode_attention(q, k, v, base=base, key_pos=pos + 12345, query_pos=Q + 12345, layout=layout)
+    assert np.allclose(out, shifted, atol=1e-9)
+    # the same logits from explicit 2x2 rotations of the distance only (query at Q - p, key at 0)
+    logits = np.stack([[rope_rotate(q[h], Q - int(p), base, layout) @ k[j] for j, p in enumerate(pos)]
+                       for h in range(2)]) / np.sqrt(d)
+    w = np.exp(logits - logits.max(axis=1, keepdims=True))
+    want = (w / w.sum(axis=1, keepdims=True)) @ v
+    assert np.allclose(out, want, atol=1e-9)
+    k_post = np.stack([rope_rotate(k[j], int(pos[j]), base, layout) for j in range(L)])
+    post = oracle.decode_attention(q, k_post, v, base=base, key_pos=pos, query_pos=Q, layout=layout,
+                                   key_space="post")
+    assert np.allclose(out, post, atol=1e-9)
