@@ -228,12 +228,37 @@ int tri_compact_kv(const tri_kv *kv, const int32_t *kept, const int32_t *kept_n,
 
 /* Text of the last failure on the calling thread ("" if none).  Owned by the library;
  * valid until the next call on this thread. */
+/* Attention of the newest token over a compressed cache: the consumer of the compaction
+ * outputs.  After compression the kept keys are rotated by RoPE at their own positions and
+ * read by standard attention ([Review] "Core Mechanism"; [DevTo] "Solving the Memory
+ * Fragmentation Problem": packing keeps the survivors but not their slot indices).
+ *   kv:         the (compacted) cache: dense [n_seq][n_layer][n_kvh][max_len][head_dim] or
+ *               paged; seq_len = the lengths after compaction (new_len); dtype TRI_F32 or
+ *               TRI_BF16 (other dtypes: TRI_ENOTSUP); v is required.
+ *   layer0, n_layers: the layers [layer0, layer0 + n_layers) to process.
+ *   q:          device [n_seq][n_layers][n_kvh * group][head_dim] float32 pre-RoPE queries of
+ *               the newest token of each sequence.
+ *   query_pos:  device [n_seq] int64 position of that token.
+ *   pos:        device [n_seq][n_layer][n_kvh][pos_stride] int32 positions of the cached keys
+ *               (e.g. tri_compact_kv's pos_out with pos_stride = budget), or NULL for
+ *               position = slot; pos_stride >= the per-unit slot capacity when pos is given.
+ *   key_space:  TRI_KEYS_PRE_ROPE (keys rotated here at their positions) or
+ *               TRI_KEYS_POST_ROPE (keys already rotated).
+ *   group:      query heads per KV head (1..8).
+ *   out:        device [n_seq][n_layers][n_kvh * group][head_dim] float32:
+ *               softmax_j((R(Q) q) . (R(p_j) k_j) / sqrt(head_dim)) weighted sum of v_j over
+ *               the seq_len[s] cached keys (zeros when there are none).
+ * Errors as for the other calls; needs no workspace. */
+int tri_decode_attention(const tri_kv *kv, int32_t layer0, int32_t n_layers, const float *q,
+                         const int64_t *query_pos, const int32_t *pos, int64_t pos_stride, double rope_base,
+                         int32_t rope_layout, int32_t key_space, int32_t group, float *out, void *stream);
+
 const char *tri_last_error(void);
 
 /* ABI version of this header: major * 10000 + minor * 100 + patch. */
 int tri_version(void);
 
-#define TRI_VERSION 10400
+#define TRI_VERSION 10500
 
 #ifdef __cplusplus
 }

@@ -312,6 +312,37 @@ def tri_compact_kv(kv: KVCache, kept, kept_n, budget: int, k_out=None, v_out=Non
             "new_len": new_len}
 
 
+def tri_decode_attention(kv: KVCache, q, query_pos, *, rope_base: float, group: int, pos=None, layer0: int = 0,
+                         n_layers=None, rope_layout: str = "half", key_space: str = "pre", out=None, stream=None):
+    """Attention of the newest token over a (compressed) cache: keys rotated by RoPE at their
+    positions (pos, e.g. the compaction's pos_out [n_seq, n_layer, n_kvh, budget]; None = slot
+    index), softmax over kv.seq_len keys.  q: float32 [n_seq, n_layers, n_kvh * group, d]
+    pre-RoPE queries at query_pos (int64 [n_seq]).  Returns float32 out of q's shape."""
+    torch = _torch()
+    L = _abi.lib()
+    desc = kv.descriptor()
+    n_layers = desc.n_layer - layer0 if n_layers is None else int(n_layers)
+    shape_q = (kv.n_seq, n_layers, desc.n_kvh * int(group), desc.head_dim)
+    _dev(q, "q", torch.float32)
+    _shape(q, "q", shape_q)
+    _dev(query_pos, "query_pos", torch.int64)
+    _shape(query_pos, "query_pos", (kv.n_seq,))
+    pos_stride = 0
+    if pos is not None:
+        _dev(pos, "pos", torch.int32)
+        if pos.dim() != 4 or tuple(pos.shape[:3]) != (kv.n_seq, desc.n_layer, desc.n_kvh):
+            raise ValueError("pos must be [n_seq, n_layer, n_kvh, stride]")
+        pos_stride = int(pos.shape[3])
+    if out is None:
+        out = torch.empty(shape_q, dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32)
+    _shape(out, "out", shape_q)
+    _abi.check(L.tri_decode_attention(ctypes.byref(desc), int(layer0), n_layers, _ptr(q), _ptr(query_pos), _ptr(pos),
+                                      pos_stride, float(rope_base), _LAYOUTS[rope_layout], _KEY_SPACES[key_space],
+                                      int(group), _ptr(out), _stream(stream)))
+    return out
+
+
 def compress(kv: KVCache, center, mean_abs, *, rope_base, offsets, group, budget, window,
              reduce="max", rope_layout="half", query_pos=None, stream=None, key_space="pre",
              form="additive"):

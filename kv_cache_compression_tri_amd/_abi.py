@@ -24,6 +24,7 @@ EXPORTED = (
     "tri_compact_kv",
     "tri_last_error",
     "tri_version",
+    "tri_decode_attention",
 )
 
 
@@ -91,7 +92,10 @@ def lib(path: str = LIB_PATH):
     L.tri_last_error.argtypes = []
     L.tri_last_error.restype = c_char_p
     L.tri_version.argtypes = []
-    for name in ("tri_calibrate_stats", "tri_score_keys", "tri_select_topb", "tri_compact_kv", "tri_version"):
+    L.tri_decode_attention.argtypes = [POINTER(TriKV), c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_int64,
+                                       c_double, c_int32, c_int32, c_int32, c_void_p, c_void_p]
+    for name in ("tri_calibrate_stats", "tri_score_keys", "tri_select_topb", "tri_compact_kv", "tri_version",
+                 "tri_decode_attention"):
         getattr(L, name).restype = c_int
     _LIB = L
     return L

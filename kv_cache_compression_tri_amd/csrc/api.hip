@@ -101,6 +101,59 @@ extern "C" {
 
 const char* tri_last_error(void) { return g_error.c_str(); }
 
+int tri_decode_attention(const tri_kv* kv, int32_t layer0, int32_t n_layers, const float* q,
+                         const int64_t* query_pos, const int32_t* pos, int64_t pos_stride, double rope_base,
+                         int32_t rope_layout, int32_t key_space, int32_t group, float* out, void* stream) {
+  try {
+    g_error.clear();
+    if (int rc = check_kv(kv, true)) return rc;
+    if (kv->dtype != TRI_F32 && kv->dtype != TRI_BF16)
+      return fail(TRI_ENOTSUP, "attention reads float32 or bfloat16 caches");
+    if (!kv->v) return fail(TRI_EINVAL, "v is NULL");
+    if (!q || !query_pos || !out) return fail(TRI_EINVAL, "q, query_pos and out must be non-NULL");
+    if (n_layers < 1 || layer0 < 0 || int64_t(layer0) + n_layers > kv->n_layer)
+      return fail(TRI_EINVAL, "layers [%d, %d) outside [0, %d)", layer0, layer0 + n_layers, kv->n_layer);
+    if (group < 1) return fail(TRI_EINVAL, "group must be >= 1");
+    if (group > tri::kMaxGroup) return fail(TRI_ENOTSUP, "group %d > %d", group, tri::kMaxGroup);
+    if (!std::isfinite(rope_base) || rope_base <= 0.0) return fail(TRI_EINVAL, "rope_base must be finite and > 0");
+    if (rope_layout != TRI_ROPE_HALF && rope_layout != TRI_ROPE_INTERLEAVED)
+      return fail(TRI_EINVAL, "unknown rope layout %d", rope_layout);
+    if (key_space != TRI_KEYS_PRE_ROPE && key_space != TRI_KEYS_POST_ROPE)
+      return fail(TRI_EINVAL, "unknown key space %d", key_space);
+    const int64_t slots = slots_of(kv);
+    if (pos && pos_stride < slots) return fail(TRI_EINVAL, "pos_stride %lld < %lld slots", (long long)pos_stride,
+                                               (long long)slots);
+    tri::DecodeParams p{};
+    for (int f = 0; f < tri::kBands; ++f)
+      p.theta_turns[f] = std::pow(rope_base, -2.0 * f / double(tri::kHeadDim)) / (2.0 * M_PI);
+    p.k = kv->k;
+    p.v = kv->v;
+    p.seq_len = kv->seq_len;
+    p.block_table = kv->layout == TRI_PAGED ? kv->block_table : nullptr;
+    p.pos = pos;
+    p.query_pos = query_pos;
+    p.q = q;
+    p.out = out;
+    p.max_len = kv->max_len;
+    p.slots = slots;
+    p.pos_stride = pos ? pos_stride : 0;
+    p.n_seq = kv->n_seq;
+    p.n_layer = kv->n_layer;
+    p.n_kvh = kv->n_kvh;
+    p.group = group;
+    p.max_pages = kv->max_pages;
+    p.layer0 = layer0;
+    p.n_layers = n_layers;
+    (void)hipGetLastError();
+    hipError_t e = tri::launch_decode_attention(p, kv->dtype == TRI_BF16, rope_layout == TRI_ROPE_INTERLEAVED,
+                                                kv->layout == TRI_PAGED, key_space == TRI_KEYS_POST_ROPE,
+                                                static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TRI_OK : hip_fail(e, "attention launch");
+  } catch (...) {
+    return fail(TRI_EHIP, "unexpected host exception in tri_decode_attention");
+  }
+}
+
 int tri_version(void) { return TRI_VERSION; }
 
 int tri_calibrate_stats(const void* q, int32_t dtype, int64_t n, int32_t n_layer, int32_t n_qh,
@@ -161,7 +214,10 @@ int tri_score_keys(const tri_score_cfg* cfg, const float* center, const float* m
       if (cfg->offsets[i] < 0) return fail(TRI_EINVAL, "offsets must be >= 0");
     if (!center || !scores) return fail(TRI_EINVAL, "center and scores must be non-NULL");
     if (!mean_abs && !mult) return fail(TRI_EINVAL, "mean_abs must be non-NULL for the additive form");
-    if (kv->pos) return fail(TRI_ENOTSUP, "explicit key positions are not supported by tri_score_keys");
+    // keys at explicit positions: pre-RoPE keys are rotated at them (additive form); keys cached
+    // after RoPE already carry their rotation, so their positions are not needed
+    if (kv->pos && mult && cfg->key_space == TRI_KEYS_PRE_ROPE)
+      return fail(TRI_ENOTSUP, "explicit key positions with the multiplicative form are not supported");
     if (int rc = workspace(ws, ws_bytes, 0)) return rc > 0 ? TRI_OK : rc;
 
     tri::ScoreParams p{};
@@ -187,6 +243,7 @@ int tri_score_keys(const tri_score_cfg* cfg, const float* center, const float* m
     p.center = center;
     p.mean_abs = mean_abs;
     p.k_scale = kv->k_scale;
+    p.pos = cfg->key_space == TRI_KEYS_PRE_ROPE ? kv->pos : nullptr;
     p.scores = scores;
     p.max_len = kv->max_len;
     p.score_stride = slots;

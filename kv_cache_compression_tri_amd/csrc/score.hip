@@ -6,6 +6,7 @@ namespace tri {
 
 hipError_t launch_score(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
                         bool post, bool mult, int grid, hipStream_t stream) {
+  if (p.pos && !post) return launch_score_pos(p, G_eff, dtype, interleaved, paged, grid, stream);
   if (mult) {
     if (dtype >= 2)
       return post ? launch_score_post_mult_8bit(p, G_eff, dtype, interleaved, paged, grid, stream)

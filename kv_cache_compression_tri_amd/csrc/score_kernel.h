@@ -153,8 +153,10 @@ __device__ __forceinline__ int tab_slot(int r, int f) {
   return ((it * 4 + (b >> 1)) * 64 + kk * 8 + g) * 2 + (b & 1);   // float2 index
 }
 
-template <int GE, int DT, bool IL, bool PAGED, bool POST, bool MULT>
+template <int GE, int DT, bool IL, bool PAGED, bool POST, bool MULT, bool XP>
 __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScoreParams P) {
+  // XP: pre-RoPE keys at explicit positions (P.pos): each key is rotated by its own phase,
+  // formed like the anchor (float64 turns) and evaluated by v_cos / v_sin; no table
   constexpr int NW = kScoreWaves;
   constexpr int NT = NW * 64;
   constexpr int STEPS = kChunk / 8;            // 8 keys per wave step
@@ -164,13 +166,14 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
   constexpr int ROW = kHeadDim * ESZ;
   static_assert(STEPS % PF == 0 && STEPS % 8 == 0, "chunk geometry");
 
-  __shared__ float4 tab[POST ? 1 : kChunk * kBands / 2];
+  constexpr bool TABLE = !POST && !XP;          // consecutive positions: LDS phase table
+  __shared__ float4 tab[TABLE ? kChunk * kBands / 2 : 1];
   __shared__ float2 stepc[kBands];             // e^{-i kChunk theta_f}
   __shared__ float2 anc[NW][kBands];           // per-wave anchors
 
   const int tid = threadIdx.x;
   // ---- phase table: float64 recurrence per (band, run of offsets), rounded once -------
-  if constexpr (!POST) {
+  if constexpr (TABLE) {
     constexpr int RL = kChunk * kBands / NT;   // offsets per thread
     const int f = tid & 63, run = tid >> 6;
     const double th = P.theta[f];
@@ -196,6 +199,11 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kk = lane >> 3;   // key of the step
   const int g = lane & 7;     // band group
+  double th_turns[XP ? 8 : 1];   // XP: theta_f / (2 pi) of the lane's bands
+  if constexpr (XP) {
+#pragma unroll
+    for (int b = 0; b < 8; ++b) th_turns[b] = P.theta[g * 8 + b] * 0.15915494309189535;
+  }
   const int ups = P.n_layer * P.n_kvh;
   const int n_qh = P.n_kvh * P.group;
   // per-lane constant byte offsets of the lane's pieces inside a step's 8 rows
@@ -285,9 +293,14 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
     // paged: page of step n, read one step before the step's load is issued
     auto page_of = [&](int n) -> int32_t { return bt[(p0 + 8 * min(n, n_steps - 1)) >> 4]; };
     int32_t pg_next = PAGED ? page_of(0) : 0;   // widened only where it is used
-    auto load_step = [&](int n, Frag<DT>& fr) {
+    Frag<DT> ring[PF];
+    const int32_t* kpos = XP ? P.pos + unit * P.score_stride : nullptr;
+    int32_t pring[XP ? PF : 1];   // XP: position of the lane's key, fetched with the key
+    auto load_step = [&](int n, int sl) __attribute__((always_inline)) {
       if (n >= n_steps) return;
+      Frag<DT>& fr = ring[sl];
       const int key0 = p0 + 8 * n;
+      if constexpr (XP) pring[sl] = (key0 + kk < p0 + nkeys) ? kpos[key0 + kk] : 0;
       const char* base;
       if constexpr (PAGED) {
         const int64_t page = pg_next;
@@ -310,9 +323,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
           fr.d[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], 0, 0));
       }
     };
-    Frag<DT> ring[PF];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) load_step(i, ring[i]);
+    for (int i = 0; i < PF; ++i) load_step(i, i);
 
     float wr[GE][8], wn[GE][8], nn[MULT ? 1 : GE][8];
     const int64_t hrow0 = int64_t(l) * n_qh + int64_t(h) * P.group;
@@ -364,7 +376,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
     }
 
     {  // anchor of this segment (float64), one band per lane; after RoPE the anchor is 0
-      const double ang = double(POST ? Q : Q - p0) * P.theta[lane];
+      const double ang = double((POST || XP) ? Q : Q - p0) * P.theta[lane];
       double sa, ca;
       sincos(ang, &sa, &ca);
       const double cr = P.c_re[lane], ci = P.c_im[lane];
@@ -466,7 +478,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
       // for all steps of the chunk.
       int tz = lane;
       asm volatile("" : "+v"(tz));
-      if (!POST && c > 0) {  // next chunk: W <- W e^{-i kChunk theta_f}
+      if (TABLE && c > 0) {  // next chunk: W <- W e^{-i kChunk theta_f}
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
           const float2 R = stepc[(tz & 7) * 8 + b];
@@ -507,8 +519,23 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
               }
             }
           } else {
-          const float4* tp = tab + it * 4 * 64 + tz;
-          const float4 t4[4] = {tp[0], tp[64], tp[128], tp[192]};
+          float4 t4[4];
+          if constexpr (TABLE) {
+            const float4* tp = tab + it * 4 * 64 + tz;
+            t4[0] = tp[0];
+            t4[1] = tp[64];
+            t4[2] = tp[128];
+            t4[3] = tp[192];
+          } else {   // e^{-i p theta_f} of the key's own position p
+            const double pk = double(pring[it % PF]);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+              double turns = pk * th_turns[b];
+              turns -= __builtin_floor(turns);
+              const float cs = __builtin_amdgcn_cosf(float(turns)), sn = __builtin_amdgcn_sinf(float(turns));
+              if (b & 1) { t4[b >> 1].z = cs; t4[b >> 1].w = -sn; } else { t4[b >> 1].x = cs; t4[b >> 1].y = -sn; }
+            }
+          }
 #pragma unroll
           for (int b = 0; b < 8; ++b) {
             float a, q;
@@ -534,7 +561,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
           }
           }
           // the slot is free again: fetch the step PF ahead into it
-          load_step(n + PF, cur);
+          load_step(n + PF, it % PF);
           float sc = sum8(acc[0]);
 #pragma unroll
           for (int hh = 1; hh < GE; ++hh) sc = fmaxf(sc, sum8(acc[hh]));
@@ -554,12 +581,12 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
   }
 }
 
-template <int GE, int DT, bool POST, bool MULT>
+template <int GE, int DT, bool POST, bool MULT, bool XP>
 hipError_t launch_ge(const ScoreParams& p, bool il, bool paged, int grid, hipStream_t st) {
   const dim3 blk(kScoreWaves * 64), grd(grid);
 #define TRI_SCORE_CASE(I, PG)                                                              \
   if (il == I && paged == PG) {                                                            \
-    hipLaunchKernelGGL((score_kernel<GE, DT, I, PG, POST, MULT>), grd, blk, 0, st, p);    \
+    hipLaunchKernelGGL((score_kernel<GE, DT, I, PG, POST, MULT, XP>), grd, blk, 0, st, p);\
     return hipGetLastError();                                                              \
   }
   TRI_SCORE_CASE(false, false)
@@ -570,18 +597,18 @@ hipError_t launch_ge(const ScoreParams& p, bool il, bool paged, int grid, hipStr
   return hipErrorInvalidValue;
 }
 
-template <int DT, bool POST, bool MULT = false>
+template <int DT, bool POST, bool MULT = false, bool XP = false>
 hipError_t launch_groups(const ScoreParams& p, int G_eff, bool interleaved, bool paged, int grid,
                          hipStream_t stream) {
   switch (G_eff) {
-    case 1: return launch_ge<1, DT, POST, MULT>(p, interleaved, paged, grid, stream);
-    case 2: return launch_ge<2, DT, POST, MULT>(p, interleaved, paged, grid, stream);
-    case 3: return launch_ge<3, DT, POST, MULT>(p, interleaved, paged, grid, stream);
-    case 4: return launch_ge<4, DT, POST, MULT>(p, interleaved, paged, grid, stream);
-    case 5: return launch_ge<5, DT, POST, MULT>(p, interleaved, paged, grid, stream);
-    case 6: return launch_ge<6, DT, POST, MULT>(p, interleaved, paged, grid, stream);
-    case 7: return launch_ge<7, DT, POST, MULT>(p, interleaved, paged, grid, stream);
-    case 8: return launch_ge<8, DT, POST, MULT>(p, interleaved, paged, grid, stream);
+    case 1: return launch_ge<1, DT, POST, MULT, XP>(p, interleaved, paged, grid, stream);
+    case 2: return launch_ge<2, DT, POST, MULT, XP>(p, interleaved, paged, grid, stream);
+    case 3: return launch_ge<3, DT, POST, MULT, XP>(p, interleaved, paged, grid, stream);
+    case 4: return launch_ge<4, DT, POST, MULT, XP>(p, interleaved, paged, grid, stream);
+    case 5: return launch_ge<5, DT, POST, MULT, XP>(p, interleaved, paged, grid, stream);
+    case 6: return launch_ge<6, DT, POST, MULT, XP>(p, interleaved, paged, grid, stream);
+    case 7: return launch_ge<7, DT, POST, MULT, XP>(p, interleaved, paged, grid, stream);
+    case 8: return launch_ge<8, DT, POST, MULT, XP>(p, interleaved, paged, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -29,6 +29,7 @@ struct ScoreParams {
   const float* center;       // [n_layer][n_qh][64][2]
   const float* mean_abs;     // [n_layer][n_qh][64]
   const float* k_scale;      // optional [n_layer][n_kvh] (8-bit keys): key = code * scale
+  const int32_t* pos;        // optional [units][score_stride] key positions (pre-RoPE keys)
   float* scores;
   int64_t max_len;           // dense token stride
   int64_t score_stride;      // slots per unit in `scores`
@@ -83,6 +84,10 @@ struct CalibParams {
 // launchers (return hipError_t of the launch)
 hipError_t launch_score(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
                         bool post, bool mult, int grid, hipStream_t stream);
+hipError_t launch_score_pos(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged, int grid,
+                            hipStream_t stream);
+hipError_t launch_score_pos_8bit(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
+                                 int grid, hipStream_t stream);
 hipError_t launch_score_mult(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
                             int grid, hipStream_t stream);
 hipError_t launch_score_post_mult(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
@@ -97,6 +102,23 @@ hipError_t launch_score_8bit(const ScoreParams& p, int G_eff, int dtype, bool in
                              int grid, hipStream_t stream);
 hipError_t launch_score_post_8bit(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
                                   int grid, hipStream_t stream);
+// Attention of the newest query over a compressed cache (decode.hip).
+struct DecodeParams {
+  double theta_turns[kBands];   // theta_f / (2 pi), float64
+  const void* k;
+  const void* v;
+  const int32_t* seq_len;
+  const int32_t* block_table;
+  const int32_t* pos;           // [n_seq][n_layer][n_kvh][pos_stride] or NULL (position = slot)
+  const int64_t* query_pos;     // [n_seq]
+  const float* q;               // [n_seq][n_layers][n_qh][128]
+  float* out;                   // [n_seq][n_layers][n_qh][128]
+  int64_t max_len, slots, pos_stride;
+  int32_t n_seq, n_layer, n_kvh, group, max_pages, layer0, n_layers;
+};
+hipError_t launch_decode_attention(const DecodeParams& p, bool bf16, bool interleaved, bool paged, bool post,
+                                   hipStream_t stream);
+
 hipError_t launch_select(const SelectParams& p, int64_t n_units, hipStream_t stream);
 hipError_t launch_compact(const CompactParams& p, int64_t n_units, int elem_bytes, bool paged,
                           bool with_v, hipStream_t stream);

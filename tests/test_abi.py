@@ -101,7 +101,11 @@ def test_score_keys_validation():
     assert _score(c, _kv(k=None))[0] == _abi.TRI_EINVAL
     assert _score(c, _kv(max_len=0))[0] == _abi.TRI_EINVAL
     assert _score(c, _kv(max_len=(1 << 20) + 1))[0] == _abi.TRI_ENOTSUP
-    assert _score(c, _kv(pos=FAKE.value))[0] == _abi.TRI_ENOTSUP
+    assert _score(c, _kv(pos=FAKE.value), ws_query=True) == (_abi.TRI_OK, 0)   # keys at explicit positions
+    cmp, _omp = _cfg(form=_abi.TRI_SCORE_MULTIPLICATIVE)
+    assert _score(cmp, _kv(pos=FAKE.value))[0] == _abi.TRI_ENOTSUP
+    cpo, _opo = _cfg(key_space=_abi.TRI_KEYS_POST_ROPE, form=_abi.TRI_SCORE_MULTIPLICATIVE)
+    assert _score(cpo, _kv(pos=FAKE.value), ws_query=True) == (_abi.TRI_OK, 0)   # rotated keys need none
     assert _score(c, _kv(layout=_abi.TRI_PAGED, page=32))[0] == _abi.TRI_ENOTSUP
     assert _score(c, _kv(layout=_abi.TRI_PAGED, block_table=None))[0] == _abi.TRI_EINVAL
     assert _score(c, _kv(), center=None)[0] == _abi.TRI_EINVAL
@@ -238,3 +242,27 @@ int main(void) {
                         ctypes.sizeof(C)]
     assert lines[1] == [C.offsets.offset, C.group.offset, C.key_space.offset, C.form.offset]
     assert lines[2][0] == lines[2][2] and lines[2][1] == _abi.TRI_EINVAL
+
+
+def test_decode_attention_validation():
+    L = _abi.lib()
+    out = FAKE
+
+    def att(kv=None, layer0=0, n_layers=2, q=FAKE, qpos=FAKE, pos=None, stride=0, base=1e6, layout=0, ks=0,
+            group=4):
+        kv = _kv() if kv is None else kv
+        return L.tri_decode_attention(ctypes.byref(kv), layer0, n_layers, q, qpos, pos, stride, base, layout, ks,
+                                      group, out, None)
+    assert att(q=None) == _abi.TRI_EINVAL
+    assert att(qpos=None) == _abi.TRI_EINVAL
+    assert att(kv=_kv(v=None)) == _abi.TRI_EINVAL
+    assert att(kv=_kv(dtype=_abi.TRI_FP8_E4M3)) == _abi.TRI_ENOTSUP
+    assert att(layer0=1, n_layers=2) == _abi.TRI_EINVAL
+    assert att(n_layers=0) == _abi.TRI_EINVAL
+    assert att(group=9) == _abi.TRI_ENOTSUP
+    assert att(group=0) == _abi.TRI_EINVAL
+    assert att(base=0.0) == _abi.TRI_EINVAL
+    assert att(layout=2) == _abi.TRI_EINVAL
+    assert att(ks=5) == _abi.TRI_EINVAL
+    assert att(pos=FAKE, stride=100) == _abi.TRI_EINVAL        # stride below the 4096 slots
+    assert "pos_stride" in L.tri_last_error().decode()

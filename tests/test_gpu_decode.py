@@ -1,0 +1,306 @@
+"""GPU parity of the steps either side of compaction: attention over the compressed cache
+(RoPE at the kept keys' positions), scoring keys at explicit positions, and a decode loop on
+a synthetic token stream.
+
+The decode loop follows the pages' serving picture: prompts arrive in prefill chunks of at most
+1024 tokens (a chunk can overshoot the budget before compression runs, so the budget is a soft
+target), decoding appends one token per step, and every 128 decode steps the cache is
+compressed and packed forward in its pages, whose emptied tail pages go back to the pool.
+Oracle inputs are regenerated on the host from the generator's seed; the host tracks which
+positions each unit still holds.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import kv_cache_compression_tri_amd as tri
+from kv_cache_compression_tri_amd import synth
+from kv_cache_compression_tri_amd.synth import device as SD
+from kv_cache_compression_tri_amd.synth import workloads as W
+
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+ATT_TOL = 2e-3     # |out_gpu - out_oracle| <= ATT_TOL * max_j |v_j| (per query head)
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def check_attention(got, want, values):
+    scale = max(float(np.abs(values).max()), 1e-30) if values.size else 1.0
+    err = float(np.abs(got - want).max()) / scale
+    assert np.all(np.isfinite(got)), "non-finite attention output"
+    assert err <= ATT_TOL, f"attention error {err:.3e} of max |v| exceeds {ATT_TOL}"
+    return err
+
+
+def unit_rows(w, hp, s, l, h, n, tag=synth.TAG_K):
+    unit = W.unit_index(w, s, l, h)
+    if tag == synth.TAG_K:
+        return synth.rows(w.seed, tag, unit, n, hp.mu_k[l, h], hp.sigma, w.sink, w.dtype)
+    return synth.rows(w.seed, tag, unit, n, np.zeros(128, np.float32), np.ones(128, np.float32), False, w.dtype)
+
+
+def as_float(bits, dtype):
+    return bits if dtype == "f32" else synth.bf16_bits_to_f32(bits)
+
+
+# ---------------------------------------------------------------------------------------
+# attention over a cache
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,layout,key_space,group", [("bf16", "half", "pre", 4), ("f32", "interleaved", "pre", 7),
+                                                          ("bf16", "interleaved", "post", 2),
+                                                          ("f32", "half", "post", 8)])
+def test_attention_dense(dtype, layout, key_space, group):
+    w = W.scaled(W.WORKLOADS["gqa8b_32k_bf16"], name="att", n_seq=3, n_layer=2, n_kvh=2, group=group, dtype=dtype,
+                 layout=layout, max_len=1300)
+    lengths = [1300, 517, 0]
+    hp = W.make_params(w, lengths=lengths)
+    log(f"attention dense {dtype} {layout} keys {key_space}-RoPE G={group} lengths={lengths}")
+    dw = SD.build(w, hp=hp)
+    rng = np.random.default_rng(61)
+    n_qh = w.n_kvh * group
+    q = rng.standard_normal((w.n_seq, w.n_layer, n_qh, 128)).astype(np.float32)
+    qpos = np.array([1300 + 40, 517, 9], np.int64)
+    out = tri.tri_decode_attention(dw.kv(), torch.from_numpy(q).cuda(), torch.from_numpy(qpos).cuda(),
+                                   rope_base=w.base, group=group, rope_layout=layout, key_space=key_space)
+    out = out.cpu().numpy()
+    worst = 0.0
+    for s in range(w.n_seq):
+        L = lengths[s]
+        for l in range(w.n_layer):
+            for h in range(w.n_kvh):
+                k = as_float(unit_rows(w, hp, s, l, h, L), dtype)
+                v = as_float(unit_rows(w, hp, s, l, h, L, synth.TAG_V), dtype)
+                want = oracle.decode_attention(q[s, l, h * group:(h + 1) * group], k, v, base=w.base,
+                                               key_pos=np.arange(L), query_pos=int(qpos[s]), layout=layout,
+                                               key_space=key_space)
+                worst = max(worst, check_attention(out[s, l, h * group:(h + 1) * group], want, v))
+    log(f"  max attention error / max|v| = {worst:.3e}")
+
+
+def test_attention_over_a_compressed_cache():
+    # compress a dense cache, then attend over k_out / v_out with the kept keys' positions
+    w = W.scaled(W.WORKLOADS["gqa8b_32k_bf16"], name="att_comp", n_seq=2, n_layer=2, n_kvh=2, max_len=3000,
+                 budget=640, window=64)
+    lengths = [3000, 1900]
+    hp = W.make_params(w, lengths=lengths)
+    dw = SD.build(w, hp=hp)
+    kv = dw.kv()
+    res = tri.compress(kv, dw.center, dw.mean_abs, rope_base=w.base, offsets=w.offsets, group=w.group,
+                       budget=w.budget, window=w.window)
+    packed = tri.KVCache.dense(res["k_out"], res["v_out"], res["new_len"])
+    rng = np.random.default_rng(62)
+    q = rng.standard_normal((w.n_seq, w.n_layer, w.n_qh, 128)).astype(np.float32)
+    qpos = np.array(lengths, np.int64)            # the next token
+    out = tri.tri_decode_attention(packed, torch.from_numpy(q).cuda(), torch.from_numpy(qpos).cuda(),
+                                   rope_base=w.base, group=w.group, pos=res["pos_out"]).cpu().numpy()
+    kept = res["kept"].cpu().numpy()
+    worst = 0.0
+    for s in range(w.n_seq):
+        n = min(lengths[s], w.budget)
+        for l in range(w.n_layer):
+            for h in range(w.n_kvh):
+                kk = kept[s, l, h, :n]
+                k = as_float(unit_rows(w, hp, s, l, h, lengths[s]), w.dtype)[kk]
+                v = as_float(unit_rows(w, hp, s, l, h, lengths[s], synth.TAG_V), w.dtype)[kk]
+                want = oracle.decode_attention(q[s, l, h * w.group:(h + 1) * w.group], k, v, base=w.base,
+                                               key_pos=kk, query_pos=int(qpos[s]))
+                worst = max(worst, check_attention(out[s, l, h * w.group:(h + 1) * w.group], want, v))
+    log(f"attention over the compressed cache: max error / max|v| = {worst:.3e}")
+
+
+# ---------------------------------------------------------------------------------------
+# scoring keys at explicit positions
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,layout,group,reduce", [("bf16", "half", 4, "max"), ("f32", "interleaved", 3, "mean"),
+                                                       ("fp8", "half", 7, "max"), ("int8", "interleaved", 1, "max")])
+def test_scores_at_explicit_positions(dtype, layout, group, reduce):
+    w = W.scaled(W.WORKLOADS["gqa8b_32k_bf16"], name="xpos", n_seq=2, n_layer=1, n_kvh=2, group=group,
+                 reduce=reduce, dtype=dtype, layout=layout, max_len=1800, budget=300, window=16)
+    lengths = [1800, 1011]
+    hp = W.make_params(w, lengths=lengths)
+    dw = SD.build(w, hp=hp)
+    rng = np.random.default_rng(63)
+    # sparse, ascending positions far beyond the slot index (a cache compacted before)
+    pos = np.zeros((w.n_seq, w.n_layer, w.n_kvh, w.max_len), np.int32)
+    for s in range(w.n_seq):
+        for h in range(w.n_kvh):
+            pos[s, 0, h] = np.sort(rng.choice(200000, w.max_len, replace=False))
+    qpos = np.array([200500, 200017], np.int64)
+    log(f"scores at explicit positions {dtype} {layout} G={group} {reduce}")
+    kv = dw.kv()
+    kv.pos = torch.from_numpy(pos).cuda()
+    sc = tri.tri_score_keys(kv, dw.center, dw.mean_abs, rope_base=w.base, offsets=w.offsets, group=group,
+                            reduce=reduce, rope_layout=layout, query_pos=torch.from_numpy(qpos).cuda())
+    kept, _ = tri.tri_select_topb(sc, kv, w.budget, w.window)
+    sc, kept = sc.cpu().numpy(), kept.cpu().numpy()
+    for s in range(w.n_seq):
+        L = lengths[s]
+        for h in range(w.n_kvh):
+            keys = P.host_rows(w, hp, s, 0, h)
+            center, mean_abs = oracle.unit_heads(hp.center, hp.mean_abs, 0, h, group)
+            orc = oracle.score_keys(keys, center, mean_abs, base=w.base, offsets=w.offsets, key_pos=pos[s, 0, h, :L],
+                                    query_pos=int(qpos[s]), layout=layout, reduce=reduce)
+            S = oracle.score_magnitude_bound(keys, center, mean_abs, layout=layout, reduce=reduce)
+            P.check_scores(sc[s, 0, h, :L], orc, S)
+            P.check_kept(kept[s, 0, h], sc[s, 0, h], orc, S, L, w.budget, w.window)
+
+
+# ---------------------------------------------------------------------------------------
+# decode loop on a synthetic token stream
+# ---------------------------------------------------------------------------------------
+
+PREFILL_CHUNK = 1024
+TRIGGER = 128
+
+
+class PagedStream:
+    """A paged K/V pool fed token by token from the generator, with a host page allocator."""
+
+    def __init__(self, w, hp, total_tokens, max_pages):
+        self.w, self.hp = w, hp
+        n_pool = w.n_seq * max_pages
+        self.k = torch.zeros((n_pool, w.n_layer, w.n_kvh, 16, 128), dtype=torch.bfloat16, device="cuda")
+        self.v = torch.zeros_like(self.k)
+        self.free = list(range(n_pool))[::-1]
+        self.bt = np.full((w.n_seq, max_pages), -1, np.int32)
+        self.max_pages = max_pages
+        self.length = np.zeros(w.n_seq, np.int64)          # cached keys per sequence
+        self.next_pos = np.zeros(w.n_seq, np.int64)        # position of the next token
+        self.pos = torch.zeros((w.n_seq, w.n_layer, w.n_kvh, max_pages * 16), dtype=torch.int32, device="cuda")
+        self.held = {(s, l, h): np.zeros(0, np.int64) for s in range(w.n_seq) for l in range(w.n_layer)
+                     for h in range(w.n_kvh)}                # host: positions held, in slot order
+        # the stream's rows by absolute position, per unit
+        self.kbits = {u: unit_rows(w, hp, *u, total_tokens) for u in self.held}
+        self.vbits = {u: unit_rows(w, hp, *u, total_tokens, synth.TAG_V) for u in self.held}
+        self.peak = 0
+
+    def append(self, s, n):
+        L, t0 = int(self.length[s]), int(self.next_pos[s])
+        for pg in range(L // 16, -(-(L + n) // 16)):
+            if self.bt[s, pg] < 0:
+                self.bt[s, pg] = self.free.pop()
+        slots = np.arange(L, L + n)
+        pages = torch.from_numpy(self.bt[s, slots // 16].astype(np.int64)).cuda()
+        rows = torch.from_numpy((slots % 16).astype(np.int64)).cuda()
+        for (ss, l, h), held in self.held.items():
+            if ss != s:
+                continue
+            kb = torch.from_numpy(self.kbits[(s, l, h)][t0:t0 + n].view(np.int16).copy()).cuda().view(torch.bfloat16)
+            vb = torch.from_numpy(self.vbits[(s, l, h)][t0:t0 + n].view(np.int16).copy()).cuda().view(torch.bfloat16)
+            self.k[pages, l, h, rows] = kb
+            self.v[pages, l, h, rows] = vb
+            self.held[(s, l, h)] = np.concatenate([held, np.arange(t0, t0 + n)])
+        self.pos[s, :, :, L:L + n] = torch.arange(t0, t0 + n, dtype=torch.int32, device="cuda")
+        self.length[s] += n
+        self.next_pos[s] += n
+        self.peak = max(self.peak, int(self.length.max()))
+
+    def kv(self):
+        return tri.KVCache.paged(self.k, self.v, torch.from_numpy(self.bt).cuda(),
+                                 torch.from_numpy(self.length.astype(np.int32)).cuda(), pos=self.pos)
+
+    def compress(self, dw, budget, window):
+        w, hp = self.w, self.hp
+        kv = self.kv()
+        qpos = torch.from_numpy(self.next_pos - 1).cuda()     # the newest token's position
+        res = tri.compress(kv, dw.center, dw.mean_abs, rope_base=w.base, offsets=w.offsets, group=w.group,
+                           budget=budget, window=window, query_pos=qpos)
+        torch.cuda.synchronize()
+        sc, kept = res["scores"].cpu().numpy(), res["kept"].cpu().numpy()
+        new_len = res["new_len"].cpu().numpy()
+        n_freed, freed = res["n_freed"].cpu().numpy(), res["freed"].cpu().numpy()
+        for (s, l, h), held in self.held.items():
+            L = int(self.length[s])
+            keys = as_float(self.kbits[(s, l, h)][held], w.dtype)
+            center, mean_abs = oracle.unit_heads(hp.center, hp.mean_abs, l, h, w.group)
+            orc = oracle.score_keys(keys, center, mean_abs, base=w.base, offsets=w.offsets, key_pos=held,
+                                    query_pos=int(self.next_pos[s] - 1))
+            S = oracle.score_magnitude_bound(keys, center, mean_abs)
+            P.check_scores(sc[s, l, h, :L], orc, S)
+            P.check_kept(kept[s, l, h], sc[s, l, h], orc, S, L, budget, window)
+            n = min(L, budget)
+            self.held[(s, l, h)] = held[kept[s, l, h, :n]]
+        for s in range(w.n_seq):
+            L, n = int(self.length[s]), int(new_len[s])
+            assert n == min(L, budget)
+            used_after, used_before = -(-n // 16), -(-L // 16)
+            assert int(n_freed[s]) == used_before - used_after
+            assert np.array_equal(freed[s, :n_freed[s]], self.bt[s, used_after:used_before])
+            self.free.extend(int(x) for x in freed[s, :n_freed[s]])
+            self.bt[s, used_after:used_before] = -1
+            self.length[s] = n
+        self.pos[..., :budget] = res["pos_out"]
+        # the packed pages hold exactly the stream's rows of the kept positions
+        k_now = self.k.view(torch.int16).cpu().numpy()
+        for (s, l, h), held in self.held.items():
+            n = len(held)
+            slots = np.arange(n)
+            got = k_now[self.bt[s, slots // 16], l, h, slots % 16]
+            assert np.array_equal(got, self.kbits[(s, l, h)][held].view(np.int16)), "packed rows differ"
+            assert np.array_equal(self.pos[s, l, h, :n].cpu().numpy(), held)
+
+
+def test_decode_loop_on_a_synthetic_stream():
+    budget, window = 512, 64
+    prompts, decode_steps = [1500, 2300], 600
+    total = max(prompts) + decode_steps + 1
+    w = W.scaled(W.WORKLOADS["paged_ragged64_bf16"], name="stream", n_seq=2, n_layer=2, n_kvh=2, budget=budget,
+                 window=window, max_len=total, len_range=(1, total))
+    hp = W.make_params(w, lengths=[1, 1])
+    dw = SD.build(w, hp=hp)                      # statistics only; the pool is fed below
+    max_pages = -(-(budget + PREFILL_CHUNK + TRIGGER) // 16) + 2
+    st = PagedStream(w, hp, total, max_pages)
+    n_compress = 0
+    # prefill in chunks; a chunk can overshoot the budget before compression runs
+    for s, plen in enumerate(prompts):
+        done = 0
+        while done < plen:
+            c = min(PREFILL_CHUNK, plen - done)
+            st.append(s, c)
+            done += c
+            if st.length.max() > budget:
+                st.compress(dw, budget, window)
+                n_compress += 1
+    log(f"prefill done: lengths {st.length.tolist()}, {n_compress} compressions")
+    for step in range(1, decode_steps + 1):
+        for s in range(w.n_seq):
+            st.append(s, 1)
+        if step % TRIGGER == 0 and st.length.max() > budget:
+            st.compress(dw, budget, window)
+            n_compress += 1
+    log(f"decode done: lengths {st.length.tolist()}, {n_compress} compressions, peak {st.peak} keys, "
+        f"{len(st.free)} free pages")
+    assert st.peak <= budget + PREFILL_CHUNK + TRIGGER            # the soft budget
+    assert len(st.free) + int(sum(-(-int(L) // 16) for L in st.length)) == st.k.shape[0]   # no page leaks
+    # the consumer: attention of the newest token over the compressed paged cache
+    rng = np.random.default_rng(64)
+    q = rng.standard_normal((w.n_seq, w.n_layer, w.n_qh, 128)).astype(np.float32)
+    qpos = st.next_pos - 1
+    out = tri.tri_decode_attention(st.kv(), torch.from_numpy(q).cuda(), torch.from_numpy(qpos).cuda(),
+                                   rope_base=w.base, group=w.group, pos=st.pos).cpu().numpy()
+    worst = 0.0
+    for (s, l, h), held in st.held.items():
+        k = as_float(st.kbits[(s, l, h)][held], w.dtype)
+        v = as_float(st.vbits[(s, l, h)][held], w.dtype)
+        want = oracle.decode_attention(q[s, l, h * w.group:(h + 1) * w.group], k, v, base=w.base, key_pos=held,
+                                       query_pos=int(qpos[s]))
+        worst = max(worst, check_attention(out[s, l, h * w.group:(h + 1) * w.group], want, v))
+    log(f"  attention over the compressed stream: max error / max|v| = {worst:.3e}")
