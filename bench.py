@@ -59,6 +59,10 @@ def parse():
     ap.add_argument("--workload", default=None, help="workload name (default: the 32K GQA pass)")
     ap.add_argument("--form", choices=("additive", "multiplicative"), default="additive",
                     help="score form: additive (default) or the phase-only series times the norms")
+    ap.add_argument("--positions", action="store_true",
+                    help="give the cache explicit key positions (slot index), scored without the phase table")
+    ap.add_argument("--consumer", action="store_true",
+                    help="also time attention of a new token over the compressed cache (tri_decode_attention)")
     ap.add_argument("--key-space", choices=("pre", "post"), default="pre",
                     help="score the cache as pre-RoPE keys (default) or as keys already rotated by RoPE")
     ap.add_argument("--cpu-units", type=int, default=0,
@@ -191,6 +195,44 @@ def recorded_traffic(name):
 
 # ---------------------------------------------------------------------------------------
 
+def consumer(args, w, dw, kv, kept_n, new_len, k_out, v_out, pos_out, reps=20):
+    """Attention of a new token of every sequence over the cache the last pass compressed
+    (RoPE at the kept keys' positions).  Bytes: every kept key and value row read once."""
+    import numpy as np
+    import torch
+    import kv_cache_compression_tri_amd as tri
+    torch.cuda.synchronize()
+    if w.paged:
+        # the pools were packed in place; positions of the packed slots at the cache's stride
+        pos = torch.zeros((w.n_seq, w.n_layer, w.n_kvh, kv.slots), dtype=torch.int32, device=dw.k.device)
+        pos[..., :w.budget] = pos_out
+        cache = tri.KVCache.paged(dw.k, dw.v, dw.block_table, new_len, pos=pos)
+    else:
+        pos = pos_out
+        cache = tri.KVCache.dense(k_out, v_out, new_len)
+    rng = np.random.default_rng(7)
+    q = torch.from_numpy(rng.standard_normal((w.n_seq, w.n_layer, w.n_qh, w.head_dim)).astype(np.float32)).cuda()
+    qpos = dw.seq_len.to(torch.int64)
+    out = torch.empty_like(q)
+    run = lambda: tri.tri_decode_attention(cache, q, qpos, rope_base=w.base, group=w.group, pos=pos,
+                                           rope_layout=w.layout, key_space=args.key_space, out=out)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    rows = int(new_len.sum().item()) * w.n_layer * w.n_kvh
+    elt = {"f32": 4, "bf16": 2}[w.dtype]
+    nbytes = rows * w.head_dim * elt * 2
+    return {"kernel": "decode_attention_kernel", "ms": ms, "keys": rows, "bytes": nbytes,
+            "GBps": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -219,6 +261,10 @@ def main():
     torch.cuda.set_device(0)
     dw = SD.build(w)
     kv = dw.kv()
+    if args.positions:   # explicit positions (equal to the slot index, so the scores are unchanged)
+        n_slots = kv.slots
+        kv.pos = torch.arange(n_slots, dtype=torch.int32, device=dw.k.device).expand(
+            w.n_seq, w.n_layer, w.n_kvh, n_slots).contiguous()
     dev = dw.k.device
     units = w.n_units
     lengths = [int(x) for x in dw.hp.lengths]
@@ -298,7 +344,8 @@ def main():
     lane_ops = score_lane_ops_per_key(1 if w.reduce == "mean" else w.group, args.key_space, args.form)
     alu_achieved = lane_ops * keys_per_step / (score_ms * 1e-3) / 1e12
     value = keys_per_step / (ms * 1e-3) / 1e9
-    traffic = recorded_traffic(name) if (args.key_space == "pre" and args.form == "additive") else None
+    traffic = recorded_traffic(name) if (args.key_space == "pre" and args.form == "additive"
+                                         and not args.positions) else None
     line = {
         "metric": METRIC,
         "value": value,
@@ -318,7 +365,7 @@ def main():
             "context": w.max_len, "head_dim": w.head_dim, "kv_dtype": w.dtype, "budget": w.budget,
             "window": w.window, "offsets": len(w.offsets), "reduce": w.reduce,
             "layout": "paged" if w.paged else "dense", "compaction": compacts, "key_space": args.key_space,
-            "form": args.form,
+            "form": args.form, "explicit_positions": bool(args.positions),
             "keys_per_step": keys_per_step, "parallelism": "single GPU",
         },
         "roofline": {
@@ -350,11 +397,16 @@ def main():
             "algorithmic_GBps": pass_bytes / (ms * 1e-3) / 1e9,
         },
     }
+    cons = None
+    if args.consumer and compacts and w.dtype in ("f32", "bf16"):
+        cons = consumer(args, w, dw, kv, kept_n, new_len, k_out, v_out, pos_out)
     del dw, kv, scores, kept, kept_n, k_out, v_out, pos_out, new_len, freed, n_freed
     torch.cuda.empty_cache()
     _, copy_gbs = copy_bandwidth(1024)
     line["pass"]["copy_GBps"] = copy_gbs
     line["pass"]["frac_of_copy"] = pass_bytes / (ms * 1e-3) / 1e9 / copy_gbs
+    if cons is not None:
+        line["consumer"] = cons
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(name, args.cpu_units, args.key_space, args.form)
     print(json.dumps(line), flush=True)

@@ -14,17 +14,17 @@
 // as (Q - p) theta_f / 2pi in float64, reduced to a fraction of a turn, and evaluated by
 // v_sin_f32 / v_cos_f32 (which take turns), so large positions keep full accuracy.
 //
-// Mapping: one workgroup per (sequence, layer, KV head) with one wave per query head of the
-// group.  A wave reads 8 keys per step with 8 lanes per key (lane g owns bands 8g..8g+7 of
-// the key and dims 16g..16g+15 of its value), sums the key's logit with three DPP steps and
-// keeps an online softmax (running max, sum and 16 accumulated value dims) per key slot.  The
-// 8 key slots are merged with a log-sum-exp reduction at the end.
+// Mapping: one workgroup of 8 waves per (sequence, layer, KV head).  Wave w takes every 8th
+// step of 8 keys, with 8 lanes per key (lane g owns bands 8g..8g+7 of the key and dims
+// 16g..16g+15 of its value), and scores each key for all query heads of the group: the key's
+// phase and value row are formed once and serve every head.  The next step's rows are in
+// flight while a step is processed.  Each lane keeps an online softmax per head (running
+// max, sum and 16 accumulated value dims) for its key slot; slots are merged with a
+// log-sum-exp reduction across lanes, then across waves through LDS.
 #include "tri_internal.h"
 
 namespace tri {
 namespace {
-
-constexpr int kDecodeMaxGroup = 8;
 
 __device__ __forceinline__ float sum8d(float v) {
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
@@ -33,20 +33,34 @@ __device__ __forceinline__ float sum8d(float v) {
   return v;
 }
 
-template <bool BF16>
-__device__ __forceinline__ float elem(const char* row, int i) {
-  if constexpr (BF16) return __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(row)[i]) << 16);
-  else return reinterpret_cast<const float*>(row)[i];
+
+constexpr int kDecodeWaves = 8;
+
+__device__ __forceinline__ float bf16w(uint32_t w, int hi) {
+  return __uint_as_float(hi ? (w & 0xFFFF0000u) : (w << 16));
+}
+__device__ __forceinline__ uint32_t wd(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-template <bool BF16, bool IL, bool PAGED, bool POST>
-__global__ __launch_bounds__(kDecodeMaxGroup * 64) void decode_attention_kernel(const DecodeParams P) {
+// One workgroup per (sequence, layer, KV head, pass): wave w takes every 8th step of 8 keys
+// and scores each key for up to GE query heads hq0.. of the group (the key's phase and value
+// row serve every head); groups of more than GE heads take a second pass.
+template <int GE, bool BF16, bool IL, bool PAGED, bool POST>
+__global__ __launch_bounds__(kDecodeWaves * 64) void decode_attention_kernel(const DecodeParams P) {
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int ROW = kHeadDim * ESZ;
+  constexpr int NW = kDecodeWaves;
+  __shared__ float red_m[NW][GE], red_l[NW][GE];
+  __shared__ float red_acc[NW][GE][kHeadDim];
   const int lane = threadIdx.x & 63;
-  const int hq_in = threadIdx.x >> 6;                 // query head within the group
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kk = lane >> 3, g = lane & 7;             // key slot of the step, band group
   int64_t wg = blockIdx.x;
+  const int pass = int(wg % P.n_pass);
+  wg /= P.n_pass;
+  const int hq0 = pass * GE;                            // first head of this pass
+  const int nh = min(GE, P.group - hq0);
   const int h = int(wg % P.n_kvh);
   wg /= P.n_kvh;
   const int lr = int(wg % P.n_layers);
@@ -54,28 +68,33 @@ __global__ __launch_bounds__(kDecodeMaxGroup * 64) void decode_attention_kernel(
   const int l = P.layer0 + lr;
   const int L = min(max(P.seq_len[s], 0), int(P.slots));
   const int n_qh = P.n_kvh * P.group;
-  const int hq = h * P.group + hq_in;
-  const int64_t qrow = (int64_t(s) * P.n_layers + lr) * n_qh + hq;
-  const float* q = P.q + qrow * kHeadDim;
+  const int64_t qrow0 = (int64_t(s) * P.n_layers + lr) * n_qh + int64_t(h) * P.group + hq0;
   const int64_t Q = P.query_pos[s];
   const float scale = 0.08838834764831845f;            // 1 / sqrt(128)
 
-  // the lane's 8 query bands (pre-RoPE; POST: rotated to the query position here)
-  float qr[8], qi[8];
+  // the lane's 8 query bands of each head (pre-RoPE; POST: rotated to the query position)
+  float qr[GE][8], qi[GE][8];
+  double th[8];
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const int f = g * 8 + b;
-    const float re = IL ? q[2 * f] : q[f];
-    const float im = IL ? q[2 * f + 1] : q[f + kBands];
-    if constexpr (POST) {
-      double turns = double(Q) * P.theta_turns[f];
-      turns -= __builtin_floor(turns);
-      const float c = __builtin_amdgcn_cosf(float(turns)), sn = __builtin_amdgcn_sinf(float(turns));
-      qr[b] = re * c - im * sn;
-      qi[b] = re * sn + im * c;
-    } else {
-      qr[b] = re;
-      qi[b] = im;
+  for (int b = 0; b < 8; ++b) th[b] = P.theta_turns[g * 8 + b];
+#pragma unroll
+  for (int hh = 0; hh < GE; ++hh) {
+    const float* q = P.q + (qrow0 + min(hh, nh - 1)) * kHeadDim;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int f = g * 8 + b;
+      const float re = IL ? q[2 * f] : q[f];
+      const float im = IL ? q[2 * f + 1] : q[f + kBands];
+      if constexpr (POST) {
+        double turns = double(Q) * th[b];
+        turns -= __builtin_floor(turns);
+        const float c = __builtin_amdgcn_cosf(float(turns)), sn = __builtin_amdgcn_sinf(float(turns));
+        qr[hh][b] = re * c - im * sn;
+        qi[hh][b] = re * sn + im * c;
+      } else {
+        qr[hh][b] = re;
+        qi[hh][b] = im;
+      }
     }
   }
 
@@ -88,72 +107,167 @@ __global__ __launch_bounds__(kDecodeMaxGroup * 64) void decode_attention_kernel(
     if constexpr (PAGED) return ((((int64_t(bt[j >> 4]) * P.n_layer + l) * P.n_kvh + h) * kPage) + (j & 15)) * ROW;
     else return (unit * P.max_len + j) * ROW;
   };
-
-  float m = -INFINITY, lsum = 0.0f, acc[16];
-#pragma unroll
-  for (int d = 0; d < 16; ++d) acc[d] = 0.0f;
-  for (int j0 = 0; j0 < L; j0 += 8) {
+  // lane pieces: key bands 8g..8g+7 (re, im) and value dims 16g..16g+15
+  struct Step {
+    uint4 k[BF16 ? 2 : 4];
+    uint4 v[BF16 ? 2 : 4];
+    int32_t p;
+  };
+  auto fetch = [&](int j0, Step& st) __attribute__((always_inline)) {
     const int j = j0 + kk;
-    if (j < L) {   // lanes of a key slot past the end keep their state
-      const char* krow = kb + row_off(j);
-      const char* vrow = vb + row_off(j);
-      const int64_t p = kpos ? int64_t(kpos[j]) : int64_t(j);
-      float part = 0.0f;
+    if (j0 >= L) return;
+    const bool live = j < L;
+    const int jj = live ? j : L - 1;                   // clamped: dead slots are not used
+    const char* kr = kb + row_off(jj);
+    const char* vr = vb + row_off(jj);
+    if constexpr (BF16) {
+      st.k[0] = *reinterpret_cast<const uint4*>(kr + (IL ? 32 * g : 16 * g));
+      st.k[1] = *reinterpret_cast<const uint4*>(kr + (IL ? 32 * g + 16 : 128 + 16 * g));
+      st.v[0] = *reinterpret_cast<const uint4*>(vr + 32 * g);
+      st.v[1] = *reinterpret_cast<const uint4*>(vr + 32 * g + 16);
+    } else {
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const int f = g * 8 + b;
-        const float a = elem<BF16>(krow, IL ? 2 * f : f);
-        const float c = elem<BF16>(krow, IL ? 2 * f + 1 : f + kBands);
-        if constexpr (POST) {   // (R(Q) q) . k'
-          part = fmaf(qr[b], a, fmaf(qi[b], c, part));
-        } else {                // Re(q conj(k) e^{i (Q - p) theta})
-          double turns = double(Q - p) * P.theta_turns[f];
-          turns -= __builtin_floor(turns);
-          const float cs = __builtin_amdgcn_cosf(float(turns)), sn = __builtin_amdgcn_sinf(float(turns));
-          const float zr = fmaf(qr[b], a, qi[b] * c);
-          const float zi = fmaf(qi[b], a, -(qr[b] * c));
-          part = fmaf(zr, cs, fmaf(-zi, sn, part));
-        }
+      for (int i = 0; i < 2; ++i) {
+        st.k[i] = *reinterpret_cast<const uint4*>(kr + (IL ? 64 * g : 32 * g) + 16 * i);
+        st.k[2 + i] = *reinterpret_cast<const uint4*>(kr + (IL ? 64 * g + 32 : 256 + 32 * g) + 16 * i);
       }
-      const float logit = sum8d(part) * scale;
-      const float m_new = fmaxf(m, logit);
-      const float keep = __expf(m - m_new), w = __expf(logit - m_new);
-      lsum = fmaf(lsum, keep, w);
 #pragma unroll
-      for (int d = 0; d < 16; ++d) acc[d] = fmaf(acc[d], keep, w * elem<BF16>(vrow, 16 * g + d));
-      m = m_new;
+      for (int i = 0; i < 4; ++i) st.v[i] = *reinterpret_cast<const uint4*>(vr + 64 * g + 16 * i);
+    }
+    st.p = kpos ? kpos[jj] : jj;
+  };
+  auto key_band = [&](const Step& st, int b, float& a, float& c) __attribute__((always_inline)) {
+    if constexpr (BF16) {
+      if constexpr (IL) {
+        const uint32_t w = wd(st.k[b >> 2], b & 3);
+        a = bf16w(w, 0);
+        c = bf16w(w, 1);
+      } else {
+        const uint32_t wr = wd(st.k[0], b >> 1), wi = wd(st.k[1], b >> 1);
+        a = bf16w(wr, b & 1);
+        c = bf16w(wi, b & 1);
+      }
+    } else {
+      if constexpr (IL) {
+        a = __uint_as_float(wd(st.k[b >> 1], 2 * (b & 1)));
+        c = __uint_as_float(wd(st.k[b >> 1], 2 * (b & 1) + 1));
+      } else {
+        a = __uint_as_float(wd(st.k[b >> 2], b & 3));
+        c = __uint_as_float(wd(st.k[2 + (b >> 2)], b & 3));
+      }
+    }
+  };
+  auto value_dim = [&](const Step& st, int d) __attribute__((always_inline)) -> float {
+    if constexpr (BF16) return bf16w(wd(st.v[d >> 3], (d & 7) >> 1), d & 1);
+    else return __uint_as_float(wd(st.v[d >> 2], d & 3));
+  };
+
+  float m[GE], lsum[GE], acc[GE][16];
+#pragma unroll
+  for (int hh = 0; hh < GE; ++hh) {
+    m[hh] = -INFINITY;
+    lsum[hh] = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) acc[hh][d] = 0.0f;
+  }
+  auto process = [&](const Step& cur, int j0) __attribute__((always_inline)) {
+    const bool live = j0 + kk < L;
+    float part[GE];
+#pragma unroll
+    for (int hh = 0; hh < GE; ++hh) part[hh] = 0.0f;
+    const double dq = double(Q - int64_t(cur.p));
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      float a, c;
+      key_band(cur, b, a, c);
+      if constexpr (!POST) {   // u = k e^{-i (Q - p) theta}: then Re(q conj(k) e^{i..}) = Re(q conj(u))
+        double turns = dq * th[b];
+        turns -= __builtin_floor(turns);
+        const float cs = __builtin_amdgcn_cosf(float(turns)), sn = __builtin_amdgcn_sinf(float(turns));
+        const float ur = fmaf(a, cs, c * sn);
+        const float ui = fmaf(c, cs, -(a * sn));
+        a = ur;
+        c = ui;
+      }
+#pragma unroll
+      for (int hh = 0; hh < GE; ++hh) part[hh] = fmaf(qr[hh][b], a, fmaf(qi[hh][b], c, part[hh]));
+    }
+#pragma unroll
+    for (int hh = 0; hh < GE; ++hh) {
+      const float logit = live ? sum8d(part[hh]) * scale : -INFINITY;
+      const float m_new = fmaxf(m[hh], logit);
+      if (m_new == -INFINITY) continue;                 // nothing seen yet in this slot
+      const float keep = __expf(m[hh] - m_new), w = __expf(logit - m_new);
+      lsum[hh] = fmaf(lsum[hh], keep, w);
+#pragma unroll
+      for (int d = 0; d < 16; ++d) acc[hh][d] = fmaf(acc[hh][d], keep, w * value_dim(cur, d));
+      m[hh] = m_new;
+    }
+  };
+  // steps j0 = 8 wave + 8 NW t; two register buffers, the next step's loads in flight
+  constexpr int STRIDE = 8 * NW;
+  Step s0, s1;
+  int j0 = 8 * wave;
+  fetch(j0, s0);
+  while (j0 < L) {
+    fetch(j0 + STRIDE, s1);
+    process(s0, j0);
+    j0 += STRIDE;
+    if (j0 >= L) break;
+    fetch(j0 + STRIDE, s0);
+    process(s1, j0);
+    j0 += STRIDE;
+  }
+  // merge the 8 key slots of the wave (lanes kk * 8 + g, same g), then the waves through LDS
+#pragma unroll
+  for (int hh = 0; hh < GE; ++hh) {
+    float m_all = m[hh];
+#pragma unroll
+    for (int x = 8; x < 64; x <<= 1) m_all = fmaxf(m_all, __shfl_xor(m_all, x, 64));
+    const float f = (m[hh] == -INFINITY) ? 0.0f : __expf(m[hh] - m_all);
+    float ls = lsum[hh] * f;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) acc[hh][d] *= f;
+#pragma unroll
+    for (int x = 8; x < 64; x <<= 1) {
+      ls += __shfl_xor(ls, x, 64);
+#pragma unroll
+      for (int d = 0; d < 16; ++d) acc[hh][d] += __shfl_xor(acc[hh][d], x, 64);
+    }
+    if (lane == 0) {
+      red_m[wave][hh] = m_all;
+      red_l[wave][hh] = ls;
+    }
+    if (kk == 0) {
+#pragma unroll
+      for (int d = 0; d < 16; ++d) red_acc[wave][hh][16 * g + d] = acc[hh][d];
     }
   }
-  // merge the 8 key slots (lanes kk * 8 + g, same g): log-sum-exp
-  float m_all = m;
-#pragma unroll
-  for (int x = 8; x < 64; x <<= 1) m_all = fmaxf(m_all, __shfl_xor(m_all, x, 64));
-  const float f = (m == -INFINITY) ? 0.0f : __expf(m - m_all);
-  lsum *= f;
-#pragma unroll
-  for (int d = 0; d < 16; ++d) acc[d] *= f;
-#pragma unroll
-  for (int x = 8; x < 64; x <<= 1) {
-    lsum += __shfl_xor(lsum, x, 64);
-#pragma unroll
-    for (int d = 0; d < 16; ++d) acc[d] += __shfl_xor(acc[d], x, 64);
-  }
-  if (kk == 0) {
-    float* o = P.out + qrow * kHeadDim + 16 * g;
-    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;   // no keys: zeros
-#pragma unroll
-    for (int d = 0; d < 16; ++d) o[d] = acc[d] * inv;
+  __syncthreads();
+  // thread t: head t / 128 (when < G), dim t % 128
+  for (int t = threadIdx.x; t < nh * kHeadDim; t += NW * 64) {
+    const int hh = t / kHeadDim, d = t % kHeadDim;
+    float mt = -INFINITY;
+    for (int w = 0; w < NW; ++w) mt = fmaxf(mt, red_m[w][hh]);
+    float lt = 0.0f, at = 0.0f;
+    if (mt != -INFINITY)
+      for (int w = 0; w < NW; ++w) {
+        if (red_m[w][hh] == -INFINITY) continue;
+        const float f = __expf(red_m[w][hh] - mt);
+        lt = fmaf(red_l[w][hh], f, lt);
+        at = fmaf(red_acc[w][hh][d], f, at);
+      }
+    P.out[(qrow0 + hh) * kHeadDim + d] = lt > 0.0f ? at / lt : 0.0f;   // no keys: zeros
   }
 }
 
-}  // namespace
-
-hipError_t launch_decode_attention(const DecodeParams& p, bool bf16, bool interleaved, bool paged, bool post,
-                                   hipStream_t stream) {
-  const dim3 grid(unsigned(int64_t(p.n_seq) * p.n_layers * p.n_kvh)), block(p.group * 64);
+template <int GE>
+hipError_t launch_decode_ge(const DecodeParams& p, bool bf16, bool interleaved, bool paged, bool post,
+                            hipStream_t stream) {
+  const dim3 grid(unsigned(int64_t(p.n_seq) * p.n_layers * p.n_kvh * p.n_pass)), block(kDecodeWaves * 64);
 #define TRI_DECODE_CASE(B, I, PG, PO)                                                                  \
   if (bf16 == B && interleaved == I && paged == PG && post == PO) {                                    \
-    hipLaunchKernelGGL((decode_attention_kernel<B, I, PG, PO>), grid, block, 0, stream, p);          \
+    hipLaunchKernelGGL((decode_attention_kernel<GE, B, I, PG, PO>), grid, block, 0, stream, p);      \
     return hipGetLastError();                                                                          \
   }
   TRI_DECODE_CASE(true, false, false, false)
@@ -174,6 +288,16 @@ hipError_t launch_decode_attention(const DecodeParams& p, bool bf16, bool interl
   TRI_DECODE_CASE(false, true, true, true)
 #undef TRI_DECODE_CASE
   return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode_attention(const DecodeParams& p, bool bf16, bool interleaved, bool paged, bool post,
+                                   hipStream_t stream) {
+  // a wave holds 4 query heads; larger groups take a second pass over the keys
+  DecodeParams q = p;
+  q.n_pass = (p.group + 3) / 4;
+  return launch_decode_ge<4>(q, bf16, interleaved, paged, post, stream);
 }
 
 }  // namespace tri

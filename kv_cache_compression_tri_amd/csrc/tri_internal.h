@@ -115,6 +115,7 @@ struct DecodeParams {
   float* out;                   // [n_seq][n_layers][n_qh][128]
   int64_t max_len, slots, pos_stride;
   int32_t n_seq, n_layer, n_kvh, group, max_pages, layer0, n_layers;
+  int32_t n_pass;               // passes over the keys (4 query heads each); set by the launcher
 };
 hipError_t launch_decode_attention(const DecodeParams& p, bool bf16, bool interleaved, bool paged, bool post,
                                    hipStream_t stream);
