@@ -24,6 +24,18 @@ namespace {
 constexpr int kCopyThreads = 256;
 constexpr int kRowsPerChunk = 64;
 
+// Rows are moved exactly once, so the loads and stores carry the non-temporal hint (the
+// copy then streams instead of filling the caches with rows nobody reads again).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_row_piece(const char* p) {
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ void store_row_piece(char* p, const uint4& v) {
+  const u32x4 t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p));
+}
+
 template <int ESZ>
 __global__ __launch_bounds__(kCopyThreads) void compact_dense_kernel(const CompactParams P,
                                                                       bool with_v) {
@@ -48,11 +60,9 @@ __global__ __launch_bounds__(kCopyThreads) void compact_dense_kernel(const Compa
     if (src < 0 || src >= L) continue;   // not a slot of this unit
     const int64_t so = (unit * P.max_len + src) * ROW + part * 16;
     const int64_t dof = (unit * P.budget + i) * ROW + part * 16;
-    *reinterpret_cast<uint4*>(static_cast<char*>(P.k_out) + dof) =
-        *reinterpret_cast<const uint4*>(static_cast<const char*>(P.k) + so);
+    store_row_piece(static_cast<char*>(P.k_out) + dof, load_row_piece(static_cast<const char*>(P.k) + so));
     if (with_v)
-      *reinterpret_cast<uint4*>(static_cast<char*>(P.v_out) + dof) =
-          *reinterpret_cast<const uint4*>(static_cast<const char*>(P.v) + so);
+      store_row_piece(static_cast<char*>(P.v_out) + dof, load_row_piece(static_cast<const char*>(P.v) + so));
     if (P.pos_out && part == 0)
       P.pos_out[unit * P.budget + i] = P.pos ? P.pos[unit * P.pos_stride + src] : src;
   }
@@ -93,8 +103,8 @@ __global__ __launch_bounds__(kCopyThreads) void compact_paged_kernel(const Compa
         const int src = kp[i];
         if (src != i && src >= 0 && src < L) {
           const int64_t so = row_off(src);
-          kb[p] = *reinterpret_cast<const uint4*>(kpool + so);
-          if (with_v) vb[p] = *reinterpret_cast<const uint4*>(vpool + so);
+          kb[p] = load_row_piece(kpool + so);
+          if (with_v) vb[p] = load_row_piece(vpool + so);
           dst[p] = i;
         }
       }
@@ -106,8 +116,8 @@ __global__ __launch_bounds__(kCopyThreads) void compact_paged_kernel(const Compa
     for (int p = 0; p < PASSES; ++p) {
       if (dst[p] >= 0) {
         const int64_t d = row_off(dst[p]);
-        *reinterpret_cast<uint4*>(kpool + d) = kb[p];
-        if (with_v) *reinterpret_cast<uint4*>(vpool + d) = vb[p];
+        store_row_piece(kpool + d, kb[p]);
+        if (with_v) store_row_piece(vpool + d, vb[p]);
       }
     }
   }

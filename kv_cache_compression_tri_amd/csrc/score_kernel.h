@@ -64,6 +64,12 @@ namespace {
 // do not pass through the vector memory counter that tracks the key stream).
 typedef __attribute__((address_space(4))) const int32_t* const_i32_ptr;
 
+// Cache policy of the key-stream buffer loads: non-temporal (NT).  Every key row is read
+// exactly once, so the stream is marked as such instead of being kept in the caches; on
+// gfx950 this raises the sustained read rate of the stream (a plain streaming-read probe of
+// the same access pattern: about 6.1 TB/s without the bit, 6.9-7.0 TB/s with it).
+constexpr int kStreamPolicy = 2;
+
 // Element types of the key cache: DT 0 = float32, 1 = bfloat16, 2 = fp8 (OCP E4M3 codes),
 // 3 = int8.  A step fragment holds a lane's 8 bands of one key: 64 B (f32), 32 B (bf16),
 // 16 B (8-bit).
@@ -312,15 +318,15 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, min(8, nkeys - 8 * n) * ROW, 0x00020000);
       if constexpr (B8 && !IL) {
-        const uint2 re = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off[0], 0, 0));
-        const uint2 im = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off[1], 0, 0));
+        const uint2 re = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off[0], 0, kStreamPolicy));
+        const uint2 im = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off[1], 0, kStreamPolicy));
         fr.d[0] = make_uint4(re.x, re.y, im.x, im.y);
       } else if constexpr (B8) {
-        fr.d[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[0], 0, 0));
+        fr.d[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[0], 0, kStreamPolicy));
       } else {
 #pragma unroll
         for (int i = 0; i < (DT == 1 ? 2 : 4); ++i)
-          fr.d[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], 0, 0));
+          fr.d[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], 0, kStreamPolicy));
       }
     };
 #pragma unroll
@@ -570,7 +576,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
           if ((it & 7) == 7 || n == n_steps - 1) {
             // lane (kk, g) holds the score of step (n & ~7) + g, key kk
             const int key = 8 * (n & ~7) + lane_key;
-            if (g <= (n & 7) && key < nkeys) out[key] = keep;
+            // the scores are written once here and read once by the selection pass
+            if (g <= (n & 7) && key < nkeys) __builtin_nontemporal_store(keep, out + key);
           }
           ++n;
           // keep each step's table reads and arithmetic inside its own step
