@@ -7,7 +7,9 @@
 // free a block that is completely empty).
 //
 // Dense (out of place): one workgroup per (unit, 64 output rows); ROW/16 lanes copy one
-// row (128 B fp8, 256 B bf16, 512 B float32) with 16-byte loads and stores.
+// row (128 B fp8, 256 B bf16, 512 B float32) with 16-byte loads and stores.  A thread
+// first reads the kept indices of all its rows, then issues all its row loads, then all
+// its stores, so its loads are in flight together.
 //
 // Paged (in place): one workgroup per unit walks its destination slots in chunks of 64,
 // in increasing order; each chunk loads all of its source rows into registers, waits for
@@ -53,18 +55,33 @@ __global__ __launch_bounds__(kCopyThreads) void compact_dense_kernel(const Compa
   if (i0 >= n) return;
   const int32_t* kp = P.kept + unit * P.budget;
   const int part = tid % TPR;
-  for (int r = tid / TPR; r < kRowsPerChunk; r += RPP) {
-    const int i = i0 + r;
-    if (i >= n) break;
-    const int src = kp[i];
-    if (src < 0 || src >= L) continue;   // not a slot of this unit
-    const int64_t so = (unit * P.max_len + src) * ROW + part * 16;
-    const int64_t dof = (unit * P.budget + i) * ROW + part * 16;
-    store_row_piece(static_cast<char*>(P.k_out) + dof, load_row_piece(static_cast<const char*>(P.k) + so));
-    if (with_v)
-      store_row_piece(static_cast<char*>(P.v_out) + dof, load_row_piece(static_cast<const char*>(P.v) + so));
-    if (P.pos_out && part == 0)
-      P.pos_out[unit * P.budget + i] = P.pos ? P.pos[unit * P.pos_stride + src] : src;
+  constexpr int PASSES = kRowsPerChunk / RPP;
+  // all index loads of the chunk first, then all row loads, then all stores
+  int src[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int i = i0 + p * RPP + tid / TPR;
+    src[p] = i < n ? kp[i] : -1;
+  }
+  uint4 kb[PASSES], vb[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    if (src[p] >= 0 && src[p] < L) {
+      const int64_t so = (unit * P.max_len + src[p]) * ROW + part * 16;
+      kb[p] = load_row_piece(static_cast<const char*>(P.k) + so);
+      if (with_v) vb[p] = load_row_piece(static_cast<const char*>(P.v) + so);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int i = i0 + p * RPP + tid / TPR;
+    if (src[p] >= 0 && src[p] < L) {
+      const int64_t dof = (unit * P.budget + i) * ROW + part * 16;
+      store_row_piece(static_cast<char*>(P.k_out) + dof, kb[p]);
+      if (with_v) store_row_piece(static_cast<char*>(P.v_out) + dof, vb[p]);
+      if (P.pos_out && part == 0)
+        P.pos_out[unit * P.budget + i] = P.pos ? P.pos[unit * P.pos_stride + src[p]] : src[p];
+    }
   }
 }
 
