@@ -248,17 +248,25 @@ int tri_compact_kv(const tri_kv *kv, const int32_t *kept, const int32_t *kept_n,
  *   out:        device [n_seq][n_layers][n_kvh * group][head_dim] float32:
  *               softmax_j((R(Q) q) . (R(p_j) k_j) / sqrt(head_dim)) weighted sum of v_j over
  *               the seq_len[s] cached keys (zeros when there are none).
- * Errors as for the other calls; needs no workspace. */
+ *   ws, ws_bytes: optional workspace (convention above).  Without one (ws_bytes == NULL)
+ *               each (sequence, layer, KV head) is one workgroup.  With one, shapes with few
+ *               units split their slots over several workgroups and merge the partial softmax
+ *               states in a second kernel; the size query returns 0 when the shape is not
+ *               split.  A workspace smaller than the query's answer: TRI_EWORKSPACE.  The
+ *               results of the two paths agree to float32 rounding (the summation order
+ *               differs).
+ * Errors as for the other calls. */
 int tri_decode_attention(const tri_kv *kv, int32_t layer0, int32_t n_layers, const float *q,
                          const int64_t *query_pos, const int32_t *pos, int64_t pos_stride, double rope_base,
-                         int32_t rope_layout, int32_t key_space, int32_t group, float *out, void *stream);
+                         int32_t rope_layout, int32_t key_space, int32_t group, float *out, void *ws,
+                         size_t *ws_bytes, void *stream);
 
 const char *tri_last_error(void);
 
 /* ABI version of this header: major * 10000 + minor * 100 + patch. */
 int tri_version(void);
 
-#define TRI_VERSION 10500
+#define TRI_VERSION 10600
 
 #ifdef __cplusplus
 }

@@ -313,11 +313,14 @@ def tri_compact_kv(kv: KVCache, kept, kept_n, budget: int, k_out=None, v_out=Non
 
 
 def tri_decode_attention(kv: KVCache, q, query_pos, *, rope_base: float, group: int, pos=None, layer0: int = 0,
-                         n_layers=None, rope_layout: str = "half", key_space: str = "pre", out=None, stream=None):
+                         n_layers=None, rope_layout: str = "half", key_space: str = "pre", out=None, stream=None,
+                         workspace="auto"):
     """Attention of the newest token over a (compressed) cache: keys rotated by RoPE at their
     positions (pos, e.g. the compaction's pos_out [n_seq, n_layer, n_kvh, budget]; None = slot
     index), softmax over kv.seq_len keys.  q: float32 [n_seq, n_layers, n_kvh * group, d]
-    pre-RoPE queries at query_pos (int64 [n_seq]).  Returns float32 out of q's shape."""
+    pre-RoPE queries at query_pos (int64 [n_seq]).  Returns float32 out of q's shape.
+    workspace: "auto" (allocated here when the shape is split over several workgroups per
+    unit), None (one workgroup per unit, no workspace), or a device uint8 tensor."""
     torch = _torch()
     L = _abi.lib()
     desc = kv.descriptor()
@@ -337,9 +340,21 @@ def tri_decode_attention(kv: KVCache, q, query_pos, *, rope_base: float, group: 
         out = torch.empty(shape_q, dtype=torch.float32, device=q.device)
     _dev(out, "out", torch.float32)
     _shape(out, "out", shape_q)
-    _abi.check(L.tri_decode_attention(ctypes.byref(desc), int(layer0), n_layers, _ptr(q), _ptr(query_pos), _ptr(pos),
-                                      pos_stride, float(rope_base), _LAYOUTS[rope_layout], _KEY_SPACES[key_space],
-                                      int(group), _ptr(out), _stream(stream)))
+    args = (ctypes.byref(desc), int(layer0), n_layers, _ptr(q), _ptr(query_pos), _ptr(pos), pos_stride,
+            float(rope_base), _LAYOUTS[rope_layout], _KEY_SPACES[key_space], int(group), _ptr(out))
+    ws, nbytes, cap = None, None, ctypes.c_size_t(0)
+    if workspace is not None:
+        need = ctypes.c_size_t(0)
+        _abi.check(L.tri_decode_attention(*args, None, ctypes.byref(need), _stream(stream)))
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError("workspace must be 'auto', None or a device uint8 tensor")
+            workspace = (torch.empty((need.value,), dtype=torch.uint8, device=q.device) if need.value else None)
+        if workspace is not None:
+            _dev(workspace, "workspace", torch.uint8)
+            cap.value = workspace.numel()
+            ws, nbytes = _ptr(workspace), ctypes.byref(cap)
+    _abi.check(L.tri_decode_attention(*args, ws, nbytes, _stream(stream)))
     return out
 
 

@@ -103,7 +103,8 @@ const char* tri_last_error(void) { return g_error.c_str(); }
 
 int tri_decode_attention(const tri_kv* kv, int32_t layer0, int32_t n_layers, const float* q,
                          const int64_t* query_pos, const int32_t* pos, int64_t pos_stride, double rope_base,
-                         int32_t rope_layout, int32_t key_space, int32_t group, float* out, void* stream) {
+                         int32_t rope_layout, int32_t key_space, int32_t group, float* out, void* ws,
+                         size_t* ws_bytes, void* stream) {
   try {
     g_error.clear();
     if (int rc = check_kv(kv, true)) return rc;
@@ -123,7 +124,28 @@ int tri_decode_attention(const tri_kv* kv, int32_t layer0, int32_t n_layers, con
     const int64_t slots = slots_of(kv);
     if (pos && pos_stride < slots) return fail(TRI_EINVAL, "pos_stride %lld < %lld slots", (long long)pos_stride,
                                                (long long)slots);
+    // optional workspace: it lets few, long units split their slots over several workgroups
+    const int64_t unit_passes = int64_t(kv->n_seq) * n_layers * kv->n_kvh *
+                                ((group + tri::kDecodeHeadsPerPass - 1) / tri::kDecodeHeadsPerPass);
+    const int n_split = tri::decode_splits(unit_passes, slots);
+    const size_t need = size_t(tri::decode_workspace_bytes(unit_passes, n_split));
+    if (ws_bytes && !ws) {
+      *ws_bytes = need;
+      return TRI_OK;
+    }
+    const bool split = ws && ws_bytes && need > 0;
+    if (split && *ws_bytes < need)
+      return fail(TRI_EWORKSPACE, "workspace of %zu bytes required (%zu given)", need, *ws_bytes);
+    if (split && reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(TRI_EINVAL, "workspace must be 256-byte aligned");
+    if (unit_passes * (split ? n_split : 1) > 0x7FFFFFFF) return fail(TRI_ENOTSUP, "too many units");
     tri::DecodeParams p{};
+    p.n_split = split ? n_split : 1;
+    if (split) {
+      p.split_len = ((slots + n_split - 1) / n_split + 63) / 64 * 64;
+      const int64_t parts = unit_passes * n_split * tri::kDecodeHeadsPerPass;
+      p.part_ml = static_cast<float*>(ws);
+      p.part_acc = reinterpret_cast<float*>(static_cast<char*>(ws) + ((parts * 2 * 4 + 255) / 256) * 256);
+    }
     for (int f = 0; f < tri::kBands; ++f)
       p.theta_turns[f] = std::pow(rope_base, -2.0 * f / double(tri::kHeadDim)) / (2.0 * M_PI);
     p.k = kv->k;

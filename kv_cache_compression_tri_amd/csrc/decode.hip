@@ -14,13 +14,18 @@
 // as (Q - p) theta_f / 2pi in float64, reduced to a fraction of a turn, and evaluated by
 // v_sin_f32 / v_cos_f32 (which take turns), so large positions keep full accuracy.
 //
-// Mapping: one workgroup of 8 waves per (sequence, layer, KV head).  Wave w takes every 8th
-// step of 8 keys, with 8 lanes per key (lane g owns bands 8g..8g+7 of the key and dims
-// 16g..16g+15 of its value), and scores each key for all query heads of the group: the key's
-// phase and value row are formed once and serve every head.  The next step's rows are in
-// flight while a step is processed.  Each lane keeps an online softmax per head (running
-// max, sum and 16 accumulated value dims) for its key slot; slots are merged with a
-// log-sum-exp reduction across lanes, then across waves through LDS.
+// Mapping: one workgroup of 8 waves per (sequence, layer, KV head, slot split).  Wave w takes
+// every 8th step of 8 keys of its split, with 8 lanes per key (lane g owns bands 8g..8g+7 of
+// the key and dims 16g..16g+15 of its value), and scores each key for all query heads of the
+// group: the key's phase and value row are formed once and serve every head.  The next
+// steps' rows are in flight while a step is processed.  Each lane keeps an online softmax
+// per head (running max, sum and 16 accumulated value dims) for its key slot; slots are
+// merged with a log-sum-exp reduction across lanes, then across waves through LDS.  With
+// one split the workgroup writes the output; with several (so that few, long units still
+// fill the GPU) each writes its partial state (max, sum, unnormalised value sums) to the
+// caller's workspace and a second kernel merges the splits the same way.
+#include <algorithm>
+
 #include "tri_internal.h"
 
 namespace tri {
@@ -43,9 +48,10 @@ __device__ __forceinline__ uint32_t wd(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-// One workgroup per (sequence, layer, KV head, pass): wave w takes every 8th step of 8 keys
-// and scores each key for up to GE query heads hq0.. of the group (the key's phase and value
-// row serve every head); groups of more than GE heads take a second pass.
+// One workgroup per (sequence, layer, KV head, pass, split): wave w takes every 8th step of 8
+// keys of the split and scores each key for up to GE query heads hq0.. of the group (the
+// key's phase and value row serve every head); groups of more than GE heads take a second
+// pass.
 template <int GE, bool BF16, bool IL, bool PAGED, bool POST>
 __global__ __launch_bounds__(kDecodeWaves * 64) void decode_attention_kernel(const DecodeParams P) {
   constexpr int ESZ = BF16 ? 2 : 4;
@@ -57,6 +63,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_attention_kernel(con
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kk = lane >> 3, g = lane & 7;             // key slot of the step, band group
   int64_t wg = blockIdx.x;
+  const int split = int(wg % P.n_split);
+  wg /= P.n_split;
+  const int64_t unit_pass = wg;                         // (sequence, layer, KV head, pass)
   const int pass = int(wg % P.n_pass);
   wg /= P.n_pass;
   const int hq0 = pass * GE;                            // first head of this pass
@@ -66,7 +75,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_attention_kernel(con
   const int lr = int(wg % P.n_layers);
   const int s = int(wg / P.n_layers);
   const int l = P.layer0 + lr;
-  const int L = min(max(P.seq_len[s], 0), int(P.slots));
+  const int L_all = min(max(P.seq_len[s], 0), int(P.slots));
+  const int j_begin = int(min(int64_t(L_all), int64_t(split) * P.split_len));
+  const int L = int(min(int64_t(L_all), int64_t(j_begin) + P.split_len));   // end of this split's slots
   const int n_qh = P.n_kvh * P.group;
   const int64_t qrow0 = (int64_t(s) * P.n_layers + lr) * n_qh + int64_t(h) * P.group + hq0;
   const int64_t Q = P.query_pos[s];
@@ -204,19 +215,39 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_attention_kernel(con
       m[hh] = m_new;
     }
   };
-  // steps j0 = 8 wave + 8 NW t; two register buffers, the next step's loads in flight
+  // steps j0 = j_begin + 8 wave + 8 NW t; register buffers with the next steps' loads in
+  // flight (bfloat16: three buffers, two steps ahead; float32: two buffers, one step ahead)
   constexpr int STRIDE = 8 * NW;
-  Step s0, s1;
-  int j0 = 8 * wave;
-  fetch(j0, s0);
-  while (j0 < L) {
+  int j0 = j_begin + 8 * wave;
+  if constexpr (BF16) {
+    Step s0, s1, s2;
+    fetch(j0, s0);
     fetch(j0 + STRIDE, s1);
-    process(s0, j0);
-    j0 += STRIDE;
-    if (j0 >= L) break;
-    fetch(j0 + STRIDE, s0);
-    process(s1, j0);
-    j0 += STRIDE;
+    while (j0 < L) {
+      fetch(j0 + 2 * STRIDE, s2);
+      process(s0, j0);
+      j0 += STRIDE;
+      if (j0 >= L) break;
+      fetch(j0 + 2 * STRIDE, s0);
+      process(s1, j0);
+      j0 += STRIDE;
+      if (j0 >= L) break;
+      fetch(j0 + 2 * STRIDE, s1);
+      process(s2, j0);
+      j0 += STRIDE;
+    }
+  } else {
+    Step s0, s1;
+    fetch(j0, s0);
+    while (j0 < L) {
+      fetch(j0 + STRIDE, s1);
+      process(s0, j0);
+      j0 += STRIDE;
+      if (j0 >= L) break;
+      fetch(j0 + STRIDE, s0);
+      process(s1, j0);
+      j0 += STRIDE;
+    }
   }
   // merge the 8 key slots of the wave (lanes kk * 8 + g, same g), then the waves through LDS
 #pragma unroll
@@ -245,6 +276,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_attention_kernel(con
   }
   __syncthreads();
   // thread t: head t / 128 (when < G), dim t % 128
+  const int64_t part = unit_pass * P.n_split + split;
   for (int t = threadIdx.x; t < nh * kHeadDim; t += NW * 64) {
     const int hh = t / kHeadDim, d = t % kHeadDim;
     float mt = -INFINITY;
@@ -257,17 +289,62 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_attention_kernel(con
         lt = fmaf(red_l[w][hh], f, lt);
         at = fmaf(red_acc[w][hh][d], f, at);
       }
-    P.out[(qrow0 + hh) * kHeadDim + d] = lt > 0.0f ? at / lt : 0.0f;   // no keys: zeros
+    if (P.n_split == 1) {
+      P.out[(qrow0 + hh) * kHeadDim + d] = lt > 0.0f ? at / lt : 0.0f;   // no keys: zeros
+    } else {
+      P.part_acc[(part * GE + hh) * kHeadDim + d] = at;
+      if (d == 0) {
+        P.part_ml[(part * GE + hh) * 2] = mt;
+        P.part_ml[(part * GE + hh) * 2 + 1] = lt;
+      }
+    }
   }
+}
+
+// Merge of the splits: one 128-thread workgroup per (sequence, layer, KV head, pass, head of
+// the pass); thread d combines value dim d of every split by log-sum-exp.
+template <int GE>
+__global__ __launch_bounds__(kHeadDim) void decode_merge_kernel(const DecodeParams P) {
+  const int d = threadIdx.x;
+  int64_t wg = blockIdx.x;
+  const int hh = int(wg % GE);
+  wg /= GE;
+  const int64_t unit_pass = wg;
+  const int pass = int(wg % P.n_pass);
+  wg /= P.n_pass;
+  const int h = int(wg % P.n_kvh);
+  wg /= P.n_kvh;
+  const int lr = int(wg % P.n_layers);
+  const int s = int(wg / P.n_layers);
+  const int hq = pass * GE + hh;
+  if (hq >= P.group) return;
+  const int64_t qrow = (int64_t(s) * P.n_layers + lr) * (int64_t(P.n_kvh) * P.group) + int64_t(h) * P.group + hq;
+  const int64_t part0 = unit_pass * P.n_split;
+  float mt = -INFINITY;
+  for (int sp = 0; sp < P.n_split; ++sp) mt = fmaxf(mt, P.part_ml[((part0 + sp) * GE + hh) * 2]);
+  float lt = 0.0f, at = 0.0f;
+  if (mt != -INFINITY)
+    for (int sp = 0; sp < P.n_split; ++sp) {
+      const float m = P.part_ml[((part0 + sp) * GE + hh) * 2];
+      if (m == -INFINITY) continue;                     // a split with no keys
+      const float f = __expf(m - mt);
+      lt = fmaf(P.part_ml[((part0 + sp) * GE + hh) * 2 + 1], f, lt);
+      at = fmaf(P.part_acc[((part0 + sp) * GE + hh) * kHeadDim + d], f, at);
+    }
+  P.out[qrow * kHeadDim + d] = lt > 0.0f ? at / lt : 0.0f;
 }
 
 template <int GE>
 hipError_t launch_decode_ge(const DecodeParams& p, bool bf16, bool interleaved, bool paged, bool post,
                             hipStream_t stream) {
-  const dim3 grid(unsigned(int64_t(p.n_seq) * p.n_layers * p.n_kvh * p.n_pass)), block(kDecodeWaves * 64);
+  const int64_t unit_passes = int64_t(p.n_seq) * p.n_layers * p.n_kvh * p.n_pass;
+  const dim3 grid(unsigned(unit_passes * p.n_split)), block(kDecodeWaves * 64);
 #define TRI_DECODE_CASE(B, I, PG, PO)                                                                  \
   if (bf16 == B && interleaved == I && paged == PG && post == PO) {                                    \
     hipLaunchKernelGGL((decode_attention_kernel<GE, B, I, PG, PO>), grid, block, 0, stream, p);      \
+    if (p.n_split > 1)                                                                                 \
+      hipLaunchKernelGGL((decode_merge_kernel<GE>), dim3(unsigned(unit_passes * GE)), dim3(kHeadDim), 0, \
+                         stream, p);                                                                   \
     return hipGetLastError();                                                                          \
   }
   TRI_DECODE_CASE(true, false, false, false)
@@ -292,12 +369,35 @@ hipError_t launch_decode_ge(const DecodeParams& p, bool bf16, bool interleaved, 
 
 }  // namespace
 
+int64_t decode_workspace_bytes(int64_t unit_passes, int n_split) {
+  if (n_split <= 1) return 0;
+  const int64_t parts = unit_passes * n_split * kDecodeHeadsPerPass;
+  return ((parts * 2 * 4 + 255) / 256) * 256 + parts * kHeadDim * 4;
+}
+
+int decode_splits(int64_t unit_passes, int64_t slots) {
+  int best = 1;
+  double best_cost = 0.0;
+  for (int n = 1; n <= kDecodeMaxSplits; ++n) {
+    if (n > 1 && slots < int64_t(n) * kDecodeMinSplitLen) break;
+    const double rounds = double((unit_passes * n + kDecodeCUs - 1) / kDecodeCUs);
+    const double cost = rounds * (kDecodeGroupCost + double(slots) / n) + (n > 1 ? kDecodeMergeCost : 0);
+    if (n == 1 || cost < best_cost) {
+      best = n;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 hipError_t launch_decode_attention(const DecodeParams& p, bool bf16, bool interleaved, bool paged, bool post,
                                    hipStream_t stream) {
-  // a wave holds 4 query heads; larger groups take a second pass over the keys
+  // a wave holds kDecodeHeadsPerPass query heads; larger groups take more passes over the keys
   DecodeParams q = p;
-  q.n_pass = (p.group + 3) / 4;
-  return launch_decode_ge<4>(q, bf16, interleaved, paged, post, stream);
+  q.n_pass = (p.group + kDecodeHeadsPerPass - 1) / kDecodeHeadsPerPass;
+  if (q.n_split < 1) q.n_split = 1;
+  if (q.n_split == 1) q.split_len = q.slots;
+  return launch_decode_ge<kDecodeHeadsPerPass>(q, bf16, interleaved, paged, post, stream);
 }
 
 }  // namespace tri

@@ -116,7 +116,29 @@ struct DecodeParams {
   int64_t max_len, slots, pos_stride;
   int32_t n_seq, n_layer, n_kvh, group, max_pages, layer0, n_layers;
   int32_t n_pass;               // passes over the keys (4 query heads each); set by the launcher
+  // Split over the key slots: n_split workgroups per (sequence, layer, KV head, pass), each
+  // over split_len slots, write partial softmax states that a second kernel merges.
+  // n_split == 1: one workgroup writes out directly (no workspace).
+  int32_t n_split;
+  int64_t split_len;            // multiple of 64
+  float* part_ml;               // [units * n_pass][n_split][4][2]   (running max, sum)
+  float* part_acc;              // [units * n_pass][n_split][4][128] (unnormalised value sums)
 };
+// Slot splits for the attention kernel.  Its workgroups hold more than 128 VGPRs per lane,
+// so a CU runs one at a time and the kernel takes ceil(groups / kDecodeCUs) rounds.  The
+// split count minimises rounds x (per-workgroup cost + slots per split), plus the merge
+// kernel when split; costs in slot-equivalents, fitted to same-process timings on MI355X
+// (256 CUs): about 190 slots of fixed work per workgroup, about 260 for the merge.
+constexpr int kDecodeCUs = 256;
+constexpr int kDecodeGroupCost = 192;
+constexpr int kDecodeMergeCost = 256;
+constexpr int kDecodeMinSplitLen = 64;
+constexpr int kDecodeMaxSplits = 16;
+constexpr int kDecodeHeadsPerPass = 4;
+// slot splits the attention kernel uses for this many (sequence, layer, KV head, pass)
+// groups, and the workspace they need (0 for one split)
+int decode_splits(int64_t unit_passes, int64_t slots);
+int64_t decode_workspace_bytes(int64_t unit_passes, int n_split);
 hipError_t launch_decode_attention(const DecodeParams& p, bool bf16, bool interleaved, bool paged, bool post,
                                    hipStream_t stream);
 

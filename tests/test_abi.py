@@ -252,7 +252,7 @@ def test_decode_attention_validation():
             group=4):
         kv = _kv() if kv is None else kv
         return L.tri_decode_attention(ctypes.byref(kv), layer0, n_layers, q, qpos, pos, stride, base, layout, ks,
-                                      group, out, None)
+                                      group, out, None, None, None)
     assert att(q=None) == _abi.TRI_EINVAL
     assert att(qpos=None) == _abi.TRI_EINVAL
     assert att(kv=_kv(v=None)) == _abi.TRI_EINVAL
@@ -266,3 +266,29 @@ def test_decode_attention_validation():
     assert att(ks=5) == _abi.TRI_EINVAL
     assert att(pos=FAKE, stride=100) == _abi.TRI_EINVAL        # stride below the 4096 slots
     assert "pos_stride" in L.tri_last_error().decode()
+
+
+def test_decode_attention_workspace():
+    """The optional workspace: size query, too small, misaligned; no launch in any case."""
+    L = _abi.lib()
+
+    def att(kv, group, ws, nbytes):
+        return L.tri_decode_attention(ctypes.byref(kv), 0, kv.n_layer, FAKE, FAKE, None, 0, 1e6, 0, 0, group,
+                                      FAKE, ws, nbytes, None)
+    # 1 x 2 x 2 units, 4096 slots: 4 (sequence, layer, head) groups of <= 4 query heads fit in one round
+    # of 256 workgroups at any split count, so they take the most splits (16); per split and head 2
+    # floats of (max, sum), padded to 256 bytes, and 128 floats of value sums
+    n = ctypes.c_size_t(0)
+    assert att(_kv(), 4, None, ctypes.byref(n)) == _abi.TRI_OK
+    assert n.value == 4 * 16 * 4 * 2 * 4 + 4 * 16 * 4 * 128 * 4
+    assert att(_kv(), 8, None, ctypes.byref(n)) == _abi.TRI_OK      # 8 heads: two passes
+    assert n.value == 8 * 16 * 4 * 2 * 4 + 8 * 16 * 4 * 128 * 4
+    assert att(_kv(max_len=512), 4, None, ctypes.byref(n)) == _abi.TRI_OK   # 512 slots: 8 splits of 64
+    assert n.value == 4 * 8 * 4 * 2 * 4 + 4 * 8 * 4 * 128 * 4
+    assert att(_kv(n_seq=128), 4, None, ctypes.byref(n)) == _abi.TRI_OK    # 512 groups: not split
+    assert n.value == 0
+    small = ctypes.c_size_t(1000)
+    assert att(_kv(), 4, FAKE, ctypes.byref(small)) == _abi.TRI_EWORKSPACE
+    big = ctypes.c_size_t(1 << 20)
+    assert att(_kv(), 4, ctypes.c_void_p(FAKE.value + 8), ctypes.byref(big)) == _abi.TRI_EINVAL
+    assert "aligned" in L.tri_last_error().decode()

@@ -63,22 +63,26 @@ def as_float(bits, dtype):
 # attention over a cache
 # ---------------------------------------------------------------------------------------
 
+@pytest.mark.parametrize("workspace", ["auto", None])
 @pytest.mark.parametrize("dtype,layout,key_space,group", [("bf16", "half", "pre", 4), ("f32", "interleaved", "pre", 7),
                                                           ("bf16", "interleaved", "post", 2),
                                                           ("f32", "half", "post", 8)])
-def test_attention_dense(dtype, layout, key_space, group):
+def test_attention_dense(dtype, layout, key_space, group, workspace):
+    # workspace "auto": the units split their 1300 slots over 10-16 workgroups each (splits past
+    # a unit's length, and a unit with no keys, included); None: one workgroup per unit
     w = W.scaled(W.WORKLOADS["gqa8b_32k_bf16"], name="att", n_seq=3, n_layer=2, n_kvh=2, group=group, dtype=dtype,
                  layout=layout, max_len=1300)
     lengths = [1300, 517, 0]
     hp = W.make_params(w, lengths=lengths)
-    log(f"attention dense {dtype} {layout} keys {key_space}-RoPE G={group} lengths={lengths}")
+    log(f"attention dense {dtype} {layout} keys {key_space}-RoPE G={group} lengths={lengths} workspace={workspace}")
     dw = SD.build(w, hp=hp)
     rng = np.random.default_rng(61)
     n_qh = w.n_kvh * group
     q = rng.standard_normal((w.n_seq, w.n_layer, n_qh, 128)).astype(np.float32)
     qpos = np.array([1300 + 40, 517, 9], np.int64)
     out = tri.tri_decode_attention(dw.kv(), torch.from_numpy(q).cuda(), torch.from_numpy(qpos).cuda(),
-                                   rope_base=w.base, group=group, rope_layout=layout, key_space=key_space)
+                                   rope_base=w.base, group=group, rope_layout=layout, key_space=key_space,
+                                   workspace=workspace)
     out = out.cpu().numpy()
     worst = 0.0
     for s in range(w.n_seq):
@@ -110,6 +114,15 @@ def test_attention_over_a_compressed_cache():
     qpos = np.array(lengths, np.int64)            # the next token
     out = tri.tri_decode_attention(packed, torch.from_numpy(q).cuda(), torch.from_numpy(qpos).cuda(),
                                    rope_base=w.base, group=w.group, pos=res["pos_out"]).cpu().numpy()
+    # a caller-owned workspace (larger than needed), and no workspace: the same result to rounding
+    ws = torch.empty((1 << 22,), dtype=torch.uint8, device="cuda")
+    out_ws = tri.tri_decode_attention(packed, torch.from_numpy(q).cuda(), torch.from_numpy(qpos).cuda(),
+                                      rope_base=w.base, group=w.group, pos=res["pos_out"], workspace=ws).cpu().numpy()
+    out_one = tri.tri_decode_attention(packed, torch.from_numpy(q).cuda(), torch.from_numpy(qpos).cuda(),
+                                       rope_base=w.base, group=w.group, pos=res["pos_out"],
+                                       workspace=None).cpu().numpy()
+    assert np.array_equal(out_ws, out)
+    assert np.allclose(out_one, out, rtol=0, atol=1e-5 * float(np.abs(out).max()))
     kept = res["kept"].cpu().numpy()
     worst = 0.0
     for s in range(w.n_seq):
