@@ -192,8 +192,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_attention_kernel(con
       float a, c;
       key_band(cur, b, a, c);
       if constexpr (!POST) {   // u = k e^{-i (Q - p) theta}: then Re(q conj(k) e^{i..}) = Re(q conj(u))
-        double turns = dq * th[b];
-        turns -= __builtin_floor(turns);
+        const double turns = __builtin_amdgcn_fract(dq * th[b]);   // fraction of a turn, in [0, 1)
         const float cs = __builtin_amdgcn_cosf(float(turns)), sn = __builtin_amdgcn_sinf(float(turns));
         const float ur = fmaf(a, cs, c * sn);
         const float ui = fmaf(c, cs, -(a * sn));
@@ -206,13 +205,19 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_attention_kernel(con
 #pragma unroll
     for (int hh = 0; hh < GE; ++hh) {
       const float logit = live ? sum8d(part[hh]) * scale : -INFINITY;
-      const float m_new = fmaxf(m[hh], logit);
-      if (m_new == -INFINITY) continue;                 // nothing seen yet in this slot
-      const float keep = __expf(m[hh] - m_new), w = __expf(logit - m_new);
-      lsum[hh] = fmaf(lsum[hh], keep, w);
+      // a new running maximum rescales the slot's state (rare once a few keys have been seen,
+      // so the branch is usually skipped by the whole wave); e^{-inf} = 0 for an empty slot
+      if (logit > m[hh]) {
+        const float keep = __expf(m[hh] - logit);
+        lsum[hh] *= keep;
 #pragma unroll
-      for (int d = 0; d < 16; ++d) acc[hh][d] = fmaf(acc[hh][d], keep, w * value_dim(cur, d));
-      m[hh] = m_new;
+        for (int d = 0; d < 16; ++d) acc[hh][d] *= keep;
+        m[hh] = logit;
+      }
+      const float w = logit == -INFINITY ? 0.0f : __expf(logit - m[hh]);
+      lsum[hh] += w;
+#pragma unroll
+      for (int d = 0; d < 16; ++d) acc[hh][d] = fmaf(w, value_dim(cur, d), acc[hh][d]);
     }
   };
   // steps j0 = j_begin + 8 wave + 8 NW t; register buffers with the next steps' loads in
