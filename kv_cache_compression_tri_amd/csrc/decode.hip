@@ -26,27 +26,16 @@
 // caller's workspace and a second kernel merges the splits the same way.
 #include <algorithm>
 
+#include "device_util.h"
 #include "tri_internal.h"
 
 namespace tri {
 namespace {
 
-__device__ __forceinline__ float sum8d(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
-  return v;
-}
-
-
 constexpr int kDecodeWaves = 8;
 
-__device__ __forceinline__ float bf16w(uint32_t w, int hi) {
-  return __uint_as_float(hi ? (w & 0xFFFF0000u) : (w << 16));
-}
-__device__ __forceinline__ uint32_t wd(const uint4& v, int i) {
-  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
-}
+// bfloat16 half `hi` (0 or 1, a constant after unrolling) of a word, widened to float32
+__device__ __forceinline__ float bf16_half(uint32_t w, int hi) { return hi ? bf16_hi(w) : bf16_lo(w); }
 
 // One workgroup per (sequence, layer, KV head, pass, split): wave w takes every 8th step of 8
 // keys of the split and scores each key for up to GE query heads hq0.. of the group (the
@@ -150,27 +139,27 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_attention_kernel(con
   auto key_band = [&](const Step& st, int b, float& a, float& c) __attribute__((always_inline)) {
     if constexpr (BF16) {
       if constexpr (IL) {
-        const uint32_t w = wd(st.k[b >> 2], b & 3);
-        a = bf16w(w, 0);
-        c = bf16w(w, 1);
+        const uint32_t w = word(st.k[b >> 2], b & 3);
+        a = bf16_half(w, 0);
+        c = bf16_half(w, 1);
       } else {
-        const uint32_t wr = wd(st.k[0], b >> 1), wi = wd(st.k[1], b >> 1);
-        a = bf16w(wr, b & 1);
-        c = bf16w(wi, b & 1);
+        const uint32_t wr = word(st.k[0], b >> 1), wi = word(st.k[1], b >> 1);
+        a = bf16_half(wr, b & 1);
+        c = bf16_half(wi, b & 1);
       }
     } else {
       if constexpr (IL) {
-        a = __uint_as_float(wd(st.k[b >> 1], 2 * (b & 1)));
-        c = __uint_as_float(wd(st.k[b >> 1], 2 * (b & 1) + 1));
+        a = __uint_as_float(word(st.k[b >> 1], 2 * (b & 1)));
+        c = __uint_as_float(word(st.k[b >> 1], 2 * (b & 1) + 1));
       } else {
-        a = __uint_as_float(wd(st.k[b >> 2], b & 3));
-        c = __uint_as_float(wd(st.k[2 + (b >> 2)], b & 3));
+        a = __uint_as_float(word(st.k[b >> 2], b & 3));
+        c = __uint_as_float(word(st.k[2 + (b >> 2)], b & 3));
       }
     }
   };
   auto value_dim = [&](const Step& st, int d) __attribute__((always_inline)) -> float {
-    if constexpr (BF16) return bf16w(wd(st.v[d >> 3], (d & 7) >> 1), d & 1);
-    else return __uint_as_float(wd(st.v[d >> 2], d & 3));
+    if constexpr (BF16) return bf16_half(word(st.v[d >> 3], (d & 7) >> 1), d & 1);
+    else return __uint_as_float(word(st.v[d >> 2], d & 3));
   };
 
   float m[GE], lsum[GE], acc[GE][16];
@@ -204,7 +193,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_attention_kernel(con
     }
 #pragma unroll
     for (int hh = 0; hh < GE; ++hh) {
-      const float logit = live ? sum8d(part[hh]) * scale : -INFINITY;
+      const float logit = live ? sum8(part[hh]) * scale : -INFINITY;
       // a new running maximum rescales the slot's state (rare once a few keys have been seen,
       // so the branch is usually skipped by the whole wave); e^{-inf} = 0 for an empty slot
       if (logit > m[hh]) {

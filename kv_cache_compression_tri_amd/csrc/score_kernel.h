@@ -54,6 +54,7 @@
 // become W_f = c_f C_f e^{i Q theta_f} for every key of the unit and x_f = conj(k'_f); there is
 // no per-key rotation, no phase table and no chunk re-anchoring, and |k'_f| = |k_f|.
 #pragma once
+#include "device_util.h"
 #include "tri_internal.h"
 
 namespace tri {
@@ -78,16 +79,10 @@ struct Frag {
   uint4 d[DT == 0 ? 4 : (DT == 1 ? 2 : 1)];
 };
 
-__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
-  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
-}
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// (re, im) of band b (0..7) of the lane's fragment.
 // Signed byte i (0..3) of a word as float32 (exact; one SDWA conversion).
 __device__ __forceinline__ float i8_at(uint32_t w, int i) { return float(int8_t(w >> (8 * i))); }
 
+// (re, im) of band b (0..7) of the lane's fragment.
 template <int DT, bool IL>
 __device__ __forceinline__ void band_of(const Frag<DT>& fr, int b, float& re, float& im) {
   if constexpr (DT == 3) {
@@ -140,14 +135,6 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v)));
   const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v) >> 32));
   return int64_t((uint64_t(hi) << 32) | lo);
-}
-
-// Sum over the 8 lanes of a key (lanes 8k..8k+7): two quad swaps and a half-row mirror.
-__device__ __forceinline__ float sum8(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
-  return v;
 }
 
 // LDS phase table: entry (r, f), r < kChunk, holds (c, s) = e^{-i r theta_f} as float32.
