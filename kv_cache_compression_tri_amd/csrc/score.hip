@@ -1,11 +1,14 @@
 // Key scoring, pre-RoPE float32 / bfloat16 keys, and the dispatch over the instantiating
-// translation units (the kernel is in score_kernel.h).
+// translation units (the vector kernel is in score_kernel.h, the matrix-core one in
+// score_mfma.h).
 #include "score_kernel.h"
 
 namespace tri {
 
 hipError_t launch_score(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
                         bool post, bool mult, int grid, hipStream_t stream) {
+  if (score_mfma_applies(G_eff, dtype, post, mult, p.pos != nullptr, p.reduce_mean != 0))
+    return launch_score_mfma(p, interleaved, paged, grid, stream);
   if (p.pos && !post) return launch_score_pos(p, G_eff, dtype, interleaved, paged, grid, stream);
   if (mult) {
     if (dtype >= 2)

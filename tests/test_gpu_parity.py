@@ -136,6 +136,10 @@ SMALL_DENSE = {
                                    window=1, low_r_frac=0.5), [2049]),
     "g6_max_half_bf16_short": (dict(n_seq=3, n_layer=1, n_kvh=1, group=6, max_len=900, budget=64,
                                     window=16), [900, 1, 65]),
+    # G = 6..8 with bf16 keys run on the matrix-core kernel: several 256-key chunks, tails that
+    # are not a multiple of its 16-key step, interleaved layout
+    "g7_max_interleaved_bf16": (dict(n_seq=2, n_layer=2, n_kvh=1, group=7, layout="interleaved", max_len=2300,
+                                     budget=333, window=20), [2300, 1201]),
     # empty sequences between non-empty ones: the score grid divides only real keys
     "g4_max_half_bf16_empty_seqs": (dict(n_seq=5, n_layer=2, n_kvh=2, group=4, max_len=2600, budget=300,
                                          window=32), [0, 2600, 0, 0, 1031]),
@@ -184,6 +188,8 @@ def test_small_dense_parity(name):
     ([3000, 17, 4096, 900], "pre", dict(dtype="fp8")),
     ([1200, 4111, 64, 2000], "post", dict(dtype="fp8", layout="interleaved", group=5)),
     ([2500, 33, 4096, 1000], "pre", dict(dtype="int8", layout="interleaved", reduce="mean")),
+    ([3000, 17, 4096, 905], "pre", dict(group=7)),                       # matrix-core scoring, paged
+    ([1200, 4111, 64, 2001], "pre", dict(layout="interleaved", group=8)),
 ])
 def test_small_paged_parity(lengths, key_space, extra):
     w = W.scaled(W.WORKLOADS["paged_ragged64_bf16"], n_seq=4, n_layer=2, n_kvh=2, max_len=5120,
