@@ -404,6 +404,11 @@ def main():
         "alu": {
             "bound": "alu",
             "kernel": "score_kernel",
+            # bf16 keys before RoPE, additive, max over >= 6 heads: the head contraction runs on the
+            # bf16 matrix cores, so this vector-ALU figure then counts work the VALUs do not do
+            "head_contraction": ("mfma_bf16" if (w.dtype == "bf16" and args.key_space == "pre" and
+                                                 args.form == "additive" and not args.positions and
+                                                 w.reduce == "max" and w.group >= 6) else "valu"),
             "lane_ops_per_key": lane_ops,
             "achieved": alu_achieved,
             "peak": PEAK_VALU_TLANEOPS,
