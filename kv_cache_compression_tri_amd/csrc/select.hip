@@ -12,7 +12,9 @@
 // consecutive slots per lane; a unit of up to 32768 slots is read from memory once into
 // registers (2048 slots per wave), longer units re-read their scores on every sweep.  The threshold is
 // found by refining linear histograms instead of sorting:
-//   level 1: 2048 bins spanning [min, max] of the candidate keys;
+//   level 1: 2048 bins spanning [min, max] of the candidate keys, counted in four copies (lane
+//            l adds into copy l % 4, so lanes of one instruction that hit the same bin mostly
+//            hit different LDS words) and then folded;
 //   level k+1: 2048 sub-bins of the bin that holds the target rank;
 // until either the whole target bin is kept (its lower edge becomes the threshold: keep
 // key >= T) or the bins are single key values (at most three levels, because the key span
@@ -36,6 +38,7 @@ constexpr int kResident = 32768;              // slots a workgroup holds in regi
 constexpr int kBinBits = 11;
 constexpr int kBins = 1 << kBinBits;
 constexpr int kLevels = 3;                    // ceil(32 / kBinBits)
+constexpr int kSubHist = 4;                   // level 1: lane l adds into copy l % 4 (fewer same-bin conflicts)
 constexpr uint32_t kKeyNone = 0u;             // slot outside the wave's range
 constexpr uint32_t kKeyWindow = 0xFFFFFFFFu;  // recent-window slot, always kept
 
@@ -79,6 +82,7 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 template <int NW>
 struct SelShared {
   alignas(16) uint32_t hist[kLevels][kBins];
+  alignas(16) uint32_t sub[kSubHist * kBins];   // level 1: copy c (= lane % kSubHist) at c * kBins
   uint32_t wmin[NW], wmax[NW];
   uint32_t wties[NW], wkeep[NW];
   int32_t jstar;
@@ -233,6 +237,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void se
       sh.wmax[wave] = mx;
     }
     for (int i = tid; i < kLevels * kBins; i += kSelThreads) (&sh.hist[0][0])[i] = 0u;
+    for (int i = tid; i < kSubHist * kBins; i += kSelThreads) sh.sub[i] = 0u;
     __syncthreads();
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
@@ -249,13 +254,31 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void se
     int shift = bitlen > kBinBits ? bitlen - kBinBits : 0;
     for (int lev = 0; lev < kLevels; ++lev) {
       uint32_t* hist = sh.hist[lev];
-      sweep([&](int t, int) __attribute__((always_inline)) {
+      if (lev == 0) {
+        const uint32_t copy = uint32_t(lane & (kSubHist - 1)) * kBins;
+        sweep([&](int t, int) __attribute__((always_inline)) {
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) {
-          const uint32_t d = u[t][e] - base;
-          if (d <= span) atomicAdd(&hist[d >> shift], 1u);
+          for (int e = 0; e < kVec; ++e) {
+            const uint32_t d = u[t][e] - base;
+            if (d <= span) atomicAdd(&sh.sub[copy + (d >> shift)], 1u);
+          }
+        });
+        __syncthreads();
+        for (int i = tid; i < kBins; i += kSelThreads) {   // fold the copies
+          uint32_t v = 0;
+#pragma unroll
+          for (int c = 0; c < kSubHist; ++c) v += sh.sub[c * kBins + i];
+          hist[i] = v;
         }
-      });
+      } else {
+        sweep([&](int t, int) __attribute__((always_inline)) {
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) {
+            const uint32_t d = u[t][e] - base;
+            if (d <= span) atomicAdd(&hist[d >> shift], 1u);
+          }
+        });
+      }
       __syncthreads();
       uint32_t tbin, above, cnt;
       find_bin(hist, rank, lane, tbin, above, cnt);
