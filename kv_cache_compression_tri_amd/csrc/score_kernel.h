@@ -146,6 +146,71 @@ __device__ __forceinline__ int tab_slot(int r, int f) {
   return ((it * 4 + (b >> 1)) * 64 + kk * 8 + g) * 2 + (b & 1);   // float2 index
 }
 
+// Work division of the scoring kernels: the units' keys, in (sequence, layer, head) order and
+// in steps of KEYS keys (a unit of L keys has ceil(L / KEYS) steps), are split into one
+// contiguous, equal share per wave, so ragged lengths do not unbalance the grid.  Consecutive
+// steps of one unit form a segment: the weights carry over (rotated chunk by chunk) and the
+// loads stream without a break.  seq_len lives on the device, so each wave sums it itself.
+// body(s, u_in, st0, n_steps) runs for each segment of the wave's share: sequence s, unit u_in
+// of the sequence (layer * n_kvh + head), first step st0 and n_steps steps.
+template <int KEYS, typename Body>
+__device__ __forceinline__ void for_each_segment(const ScoreParams& P, int lane, int64_t w_id, int64_t n_waves,
+                                                 Body&& body) {
+  const int ups = P.n_layer * P.n_kvh;
+  auto unit_steps = [&](int sq) -> int64_t {
+    return (int64_t(min(max(P.seq_len[sq], 0), int(P.score_stride))) + KEYS - 1) / KEYS;
+  };
+  int64_t total = 0;
+  for (int s0 = 0; s0 < P.n_seq; s0 += 64) {
+    int64_t c = s0 + lane < P.n_seq ? unit_steps(s0 + lane) : 0;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
+    total += uniform64(c);
+  }
+  total *= ups;
+  const int64_t share = total / n_waves, extra = total % n_waves;
+  const int64_t g0 = w_id * share + min(w_id, extra);
+  const int64_t g1 = g0 + share + (w_id < extra ? 1 : 0);
+  // sequence holding step g0, and the global index of that sequence's first step
+  int s = 0;
+  int64_t seq_base = 0;
+  if (g0 < g1) {
+    for (int s0 = 0; s0 < P.n_seq; s0 += 64) {
+      const int64_t c = s0 + lane < P.n_seq ? unit_steps(s0 + lane) * ups : 0;
+      int64_t incl = c;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int64_t t = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += t;
+      }
+      const uint64_t hit = __ballot(seq_base + incl > g0);
+      if (hit) {
+        const int ln = __ffsll((unsigned long long)hit) - 1;
+        s = s0 + ln;
+        seq_base += uniform64(__shfl(incl - c, ln, 64));
+        break;
+      }
+      seq_base += uniform64(__shfl(incl, 63, 64));
+    }
+  }
+  int64_t gs = g0;
+  while (gs < g1 && s < P.n_seq) {
+    const int64_t spu = unit_steps(s);
+    const int64_t rel = gs - seq_base;
+    if (rel >= spu * ups) {            // past the end of sequence s (or s is empty)
+      seq_base += spu * ups;
+      ++s;
+      continue;
+    }
+    const int u_in = int(rel / spu);
+    const int st0 = int(rel - int64_t(u_in) * spu);
+    const int64_t seg_end = min(g1, seq_base + (int64_t(u_in) + 1) * spu);
+    const int seg_steps = int(seg_end - gs);
+    gs = seg_end;
+    body(s, u_in, st0, seg_steps);
+  }
+}
+
 template <int GE, int DT, bool IL, bool PAGED, bool POST, bool MULT, bool XP>
 __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScoreParams P) {
   // XP: pre-RoPE keys at explicit positions (P.pos): each key is rotated by its own phase,
@@ -214,63 +279,10 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
     off[3] = off[2] + 16;
   }
 
-  // Work division: the units' keys, in (sequence, layer, head) order and in 8-key steps
-  // (a unit of L keys has ceil(L / 8) steps), are split into one contiguous, equal share
-  // per wave, so ragged lengths do not unbalance the grid.  Consecutive steps of one unit
-  // form a segment: the weights carry over (rotated chunk by chunk) and the loads stream
-  // without a break.  seq_len lives on the device, so each wave sums it itself.
-  auto unit_steps = [&](int sq) -> int64_t {
-    return (int64_t(min(max(P.seq_len[sq], 0), int(P.score_stride))) + 7) >> 3;
-  };
-  int64_t total = 0;
-  for (int s0 = 0; s0 < P.n_seq; s0 += 64) {
-    int64_t c = s0 + lane < P.n_seq ? unit_steps(s0 + lane) : 0;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
-    total += uniform64(c);
-  }
-  total *= ups;
   const int64_t n_waves = int64_t(gridDim.x) * NW;
   const int64_t w_id = int64_t(blockIdx.x) * NW + wave;
-  const int64_t share = total / n_waves, extra = total % n_waves;
-  const int64_t g0 = w_id * share + min(w_id, extra);
-  const int64_t g1 = g0 + share + (w_id < extra ? 1 : 0);
-  // sequence holding step g0, and the global index of that sequence's first step
-  int s = 0;
-  int64_t seq_base = 0;
-  if (g0 < g1) {
-    for (int s0 = 0; s0 < P.n_seq; s0 += 64) {
-      const int64_t c = s0 + lane < P.n_seq ? unit_steps(s0 + lane) * ups : 0;
-      int64_t incl = c;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int64_t t = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += t;
-      }
-      const uint64_t hit = __ballot(seq_base + incl > g0);
-      if (hit) {
-        const int ln = __ffsll((unsigned long long)hit) - 1;
-        s = s0 + ln;
-        seq_base += uniform64(__shfl(incl - c, ln, 64));
-        break;
-      }
-      seq_base += uniform64(__shfl(incl, 63, 64));
-    }
-  }
-  int64_t gs = g0;
-  while (gs < g1 && s < P.n_seq) {
-    const int64_t spu = unit_steps(s);
-    const int64_t rel = gs - seq_base;
-    if (rel >= spu * ups) {            // past the end of sequence s (or s is empty)
-      seq_base += spu * ups;
-      ++s;
-      continue;
-    }
-    const int u_in = int(rel / spu);
-    const int st0 = int(rel - int64_t(u_in) * spu);
-    const int64_t seg_end = min(g1, seq_base + (int64_t(u_in) + 1) * spu);
-    const int seg_steps = int(seg_end - gs);
-    gs = seg_end;
+  for_each_segment<8>(P, lane, w_id, n_waves, [&](const int s, const int u_in, const int st0, const int seg_steps)
+                                                  __attribute__((always_inline)) {
     const int64_t unit = int64_t(s) * ups + u_in;
     const int l = u_in / P.n_kvh;
     const int h = u_in - l * P.n_kvh;
@@ -572,7 +584,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
         }
       }
     }
-  }
+  });
 }
 
 template <int GE, int DT, bool POST, bool MULT, bool XP>

@@ -152,58 +152,11 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_mfma_kernel(const Scor
     off[3] = km * ROW + 192 + 16 * q;
   }
 
-  // work division as in score_kernel.h, in 16-key steps
-  auto unit_steps = [&](int sq) -> int64_t {
-    return (int64_t(min(max(P.seq_len[sq], 0), int(P.score_stride))) + kMfKeys - 1) / kMfKeys;
-  };
-  int64_t total = 0;
-  for (int s0 = 0; s0 < P.n_seq; s0 += 64) {
-    int64_t c = s0 + lane < P.n_seq ? unit_steps(s0 + lane) : 0;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
-    total += uniform64(c);
-  }
-  total *= ups;
+  // work division shared with score_kernel.h, in 16-key steps
   const int64_t n_waves = int64_t(gridDim.x) * NW;
   const int64_t w_id = int64_t(blockIdx.x) * NW + wave;
-  const int64_t share = total / n_waves, extra = total % n_waves;
-  const int64_t g0 = w_id * share + min(w_id, extra);
-  const int64_t g1 = g0 + share + (w_id < extra ? 1 : 0);
-  int s = 0;
-  int64_t seq_base = 0;
-  if (g0 < g1) {
-    for (int s0 = 0; s0 < P.n_seq; s0 += 64) {
-      const int64_t c = s0 + lane < P.n_seq ? unit_steps(s0 + lane) * ups : 0;
-      int64_t incl = c;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int64_t t = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += t;
-      }
-      const uint64_t hit = __ballot(seq_base + incl > g0);
-      if (hit) {
-        const int ln = __ffsll((unsigned long long)hit) - 1;
-        s = s0 + ln;
-        seq_base += uniform64(__shfl(incl - c, ln, 64));
-        break;
-      }
-      seq_base += uniform64(__shfl(incl, 63, 64));
-    }
-  }
-  int64_t gs = g0;
-  while (gs < g1 && s < P.n_seq) {
-    const int64_t spu = unit_steps(s);
-    const int64_t rel = gs - seq_base;
-    if (rel >= spu * ups) {
-      seq_base += spu * ups;
-      ++s;
-      continue;
-    }
-    const int u_in = int(rel / spu);
-    const int st0 = int(rel - int64_t(u_in) * spu);
-    const int64_t seg_end = min(g1, seq_base + (int64_t(u_in) + 1) * spu);
-    const int n_steps = int(seg_end - gs);
-    gs = seg_end;
+  for_each_segment<kMfKeys>(P, lane, w_id, n_waves, [&](const int s, const int u_in, const int st0,
+                                                        const int n_steps) __attribute__((always_inline)) {
     const int64_t unit = int64_t(s) * ups + u_in;
     const int l = u_in / P.n_kvh;
     const int h = u_in - l * P.n_kvh;
@@ -364,7 +317,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_mfma_kernel(const Scor
         }
       }
     }
-  }
+  });
 }
 
 template <bool IL, bool PAGED>
