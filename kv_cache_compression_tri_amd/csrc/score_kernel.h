@@ -298,6 +298,9 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
     // paged: page of step n, read one step before the step's load is issued
     auto page_of = [&](int n) -> int32_t { return bt[(p0 + 8 * min(n, n_steps - 1)) >> 4]; };
     int32_t pg_next = PAGED ? page_of(0) : 0;   // widened only where it is used
+    // paged: bytes per page id (all layers and heads) and this unit's slice of a page
+    const uint64_t pg_bytes = uint64_t(P.n_layer) * uint64_t(P.n_kvh) * uint64_t(kPage * ROW);
+    const char* ubase = kbase + (int64_t(l) * P.n_kvh + h) * int64_t(kPage * ROW);
     Frag<DT> ring[PF];
     const int32_t* kpos = XP ? P.pos + unit * P.score_stride : nullptr;
     int32_t pring[XP ? PF : 1];   // XP: position of the lane's key, fetched with the key
@@ -308,9 +311,9 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
       if constexpr (XP) pring[sl] = (key0 + kk < p0 + nkeys) ? kpos[key0 + kk] : 0;
       const char* base;
       if constexpr (PAGED) {
-        const int64_t page = pg_next;
+        const int32_t page = pg_next;
         pg_next = page_of(n + 1);
-        base = kbase + ((((page * P.n_layer + l) * P.n_kvh + h) * kPage) + (key0 & 15)) * ROW;
+        base = ubase + uint64_t(uint32_t(page)) * pg_bytes + (key0 & 15) * ROW;
       } else {
         base = kbase + (unit * P.max_len + key0) * ROW;
       }

@@ -169,14 +169,16 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_mfma_kernel(const Scor
     const char* kbase = static_cast<const char*>(P.k);
     typedef __attribute__((address_space(4))) const int32_t* mf_const_i32_ptr;
     const mf_const_i32_ptr bt = PAGED ? (mf_const_i32_ptr)(P.block_table + int64_t(s) * P.max_pages) : nullptr;
+    // paged: bytes per page id (all layers and heads) and this unit's slice of a page
+    const uint64_t pg_bytes = uint64_t(P.n_layer) * uint64_t(P.n_kvh) * uint64_t(kPage * ROW);
+    const char* ubase = kbase + (int64_t(l) * P.n_kvh + h) * int64_t(kPage * ROW);
     uint4 ring[PF][4];
     auto load_step = [&](int n, int sl) __attribute__((always_inline)) {
       if (n >= n_steps) return;
       const int key0 = p0 + kMfKeys * n;
       const char* base;
       if constexpr (PAGED) {
-        const int64_t page = bt[key0 >> 4];
-        base = kbase + (((page * P.n_layer + l) * P.n_kvh + h) * kPage) * ROW;
+        base = ubase + uint64_t(uint32_t(bt[key0 >> 4])) * pg_bytes;
       } else {
         base = kbase + (unit * P.max_len + key0) * ROW;
       }
