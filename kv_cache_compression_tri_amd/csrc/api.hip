@@ -362,7 +362,8 @@ int tri_compact_kv(const tri_kv* kv, const int32_t* kept, const int32_t* kept_n,
     p.n_layer = kv->n_layer;
     p.n_kvh = kv->n_kvh;
     p.max_pages = kv->max_pages;
-    p.chunks_per_unit = (budget + 63) / 64;
+    const int copy_rows = tri::dense_copy_rows(elem_bytes(kv->dtype));
+    p.chunks_per_unit = (budget + copy_rows - 1) / copy_rows;
     const int64_t units = int64_t(kv->n_seq) * p.units_per_seq;
     if (!paged && units * p.chunks_per_unit > 0x7FFFFFFF) return fail(TRI_ENOTSUP, "grid too large");
     (void)hipGetLastError();

@@ -70,8 +70,13 @@ struct CompactParams {
   int32_t budget;
   int32_t units_per_seq;
   int32_t n_layer, n_kvh, max_pages;
-  int32_t chunks_per_unit;   // dense: ceil(budget / 64)
+  int32_t chunks_per_unit;   // dense: ceil(budget / dense_copy_rows(element bytes))
 };
+
+// Dense compaction: each thread of a kDenseCopyThreads-thread workgroup moves one 16-byte
+// piece of a kept row of K and of V, so a workgroup covers this many output rows.
+constexpr int kDenseCopyThreads = 128;
+constexpr int dense_copy_rows(int elem_bytes) { return kDenseCopyThreads * 16 / (kHeadDim * elem_bytes); }
 
 struct CalibParams {
   const void* q;
