@@ -250,6 +250,49 @@ def test_paged_in_place_every_row_moves():
     assert np.array_equal(bits(dw.k), ek) and np.array_equal(bits(dw.v), ev)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8", "int8"])
+@pytest.mark.parametrize("budget", [1, 7, 13, 33])
+@pytest.mark.parametrize("with_pos", [False, True])
+def test_dense_compaction_row_groups(dtype, budget, with_pos):
+    """Dense compaction of hand-made kept sets: budgets that leave every residue of the
+    kernel's 4-, 8- and 16-row groups, sequences shorter than the budget and an empty one;
+    K, V bit for bit, positions (slot ids or explicit positions) and new lengths."""
+    rng = np.random.default_rng(1000 * budget + len(dtype) + (7 if with_pos else 0))
+    lengths = [37, 5, 0, 100]
+    n_seq, n_layer, n_kvh, max_len = len(lengths), 2, 3, 100
+    shape = (n_seq, n_layer, n_kvh, max_len, 128)
+    raw = {"f32": (np.int32, torch.float32), "bf16": (np.int16, torch.bfloat16),
+           "fp8": (np.uint8, torch.float8_e4m3fn), "int8": (np.int8, torch.int8)}[dtype]
+    info = np.iinfo(raw[0])
+    kb = rng.integers(info.min, info.max, size=shape, dtype=raw[0], endpoint=True)
+    vb = rng.integers(info.min, info.max, size=shape, dtype=raw[0], endpoint=True)
+    k = torch.from_numpy(kb).cuda().view(raw[1])
+    v = torch.from_numpy(vb).cuda().view(raw[1])
+    pos = rng.integers(0, 1 << 20, size=(n_seq, n_layer, n_kvh, max_len), dtype=np.int32) if with_pos else None
+    kv = tri.KVCache.dense(k, v, torch.tensor(lengths, dtype=torch.int32, device="cuda"),
+                           pos=torch.from_numpy(pos).cuda() if with_pos else None)
+    kept = np.full((n_seq, n_layer, n_kvh, budget), -1, np.int32)
+    for s, L in enumerate(lengths):
+        n = min(L, budget)
+        for l in range(n_layer):
+            for h in range(n_kvh):
+                kept[s, l, h, :n] = np.sort(rng.choice(L, size=n, replace=False)) if n else []
+    kept_n = np.array([min(L, budget) for L in lengths], np.int32)
+    out = tri.tri_compact_kv(kv, torch.from_numpy(kept).cuda(), torch.from_numpy(kept_n).cuda(), budget)
+    torch.cuda.synchronize()
+    ko, vo, po, nl = bits(out["k_out"]), bits(out["v_out"]), bits(out["pos_out"]), bits(out["new_len"])
+    for s, L in enumerate(lengths):
+        n = min(L, budget)
+        assert nl[s] == n
+        for l in range(n_layer):
+            for h in range(n_kvh):
+                ek, ev, ep = oracle.compact_dense(kb[s, l, h], vb[s, l, h], kept[s, l, h, :n],
+                                                  pos=pos[s, l, h] if with_pos else None)
+                assert np.array_equal(ko[s, l, h, :n], ek), (s, l, h)
+                assert np.array_equal(vo[s, l, h, :n], ev), (s, l, h)
+                assert np.array_equal(po[s, l, h, :n], ep), (s, l, h)
+
+
 # ---------------------------------------------------------------------------------------
 # selection edge cases on hand-made scores
 # ---------------------------------------------------------------------------------------
