@@ -254,8 +254,8 @@ def test_paged_in_place_every_row_moves():
 @pytest.mark.parametrize("budget", [1, 7, 13, 33])
 @pytest.mark.parametrize("with_pos", [False, True])
 def test_dense_compaction_row_groups(dtype, budget, with_pos):
-    """Dense compaction of hand-made kept sets: budgets that leave every residue of the
-    kernel's 4-, 8- and 16-row groups, sequences shorter than the budget and an empty one;
+    """Dense compaction of hand-made kept sets: budgets that leave a partial last group for
+    each of the kernel's 4-, 8- and 16-row sizes, sequences shorter than the budget and an empty one;
     K, V bit for bit, positions (slot ids or explicit positions) and new lengths."""
     rng = np.random.default_rng(1000 * budget + len(dtype) + (7 if with_pos else 0))
     lengths = [37, 5, 0, 100]
