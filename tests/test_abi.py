@@ -169,6 +169,10 @@ def test_compact_validation():
     assert comp(paged, k_out=None, v_out=None, freed=FAKE) == _abi.TRI_EINVAL
     assert L.tri_compact_kv(ctypes.byref(paged), None, FAKE, 8, None, None, None, None, None, None,
                             None) == _abi.TRI_EINVAL
+    # the dense grid is units x ceil(budget / rows per workgroup) workgroups: 2^20 units with a
+    # budget of 2^20 slots exceed 2^31 - 1 and are refused before any launch
+    assert comp(_kv(n_layer=1 << 12, n_kvh=1 << 8), budget=1 << 20) == _abi.TRI_ENOTSUP
+    assert b"grid" in L.tri_last_error()
 
 
 def test_calibrate_validation():
