@@ -221,7 +221,9 @@ int tri_select_topb(const float *scores, const tri_kv *kv, int32_t budget, int32
  *            now in slot i (kv->pos gathered, or kept[i] when kv->pos == NULL).
  *   new_len: optional out int32 [n_seq], = kept_n.
  * kept must be ascending per unit (as written by tri_select_topb); the in-place order of
- * the paged path relies on kept[i] >= i. */
+ * the paged path relies on kept[i] >= i.  The dense path launches one workgroup per
+ * (unit, 4 / 8 / 16 output rows) for float32 / bf16 / 8-bit rows and returns TRI_ENOTSUP
+ * when that exceeds 2^31 - 1 workgroups. */
 int tri_compact_kv(const tri_kv *kv, const int32_t *kept, const int32_t *kept_n, int32_t budget,
                    void *k_out, void *v_out, int32_t *pos_out, int32_t *freed, int32_t *n_freed,
                    int32_t *new_len, void *stream);
