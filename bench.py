@@ -110,12 +110,11 @@ def _oracle_unit(job):
     unit = W.unit_index(w, s, l, h)
     L = int(hp.lengths[s])
     scale = float(hp.k_scale[l, h])
-    keys = synth.rows_as_float(w.seed, synth.TAG_K, unit, L, hp.mu_k[l, h], hp.sigma, w.sink, w.dtype,
-                               scale=scale)
-    vals = synth.rows(w.seed, synth.TAG_V, unit, L, np.zeros(128, np.float32), np.ones(128, np.float32),
-                      False, w.dtype)
     keys_raw = synth.rows(w.seed, synth.TAG_K, unit, L, hp.mu_k[l, h], hp.sigma, w.sink, w.dtype,
                           scale=scale)
+    keys = oracle.decode_stored(keys_raw, w.dtype, scale)
+    vals = synth.rows(w.seed, synth.TAG_V, unit, L, np.zeros(128, np.float32), np.ones(128, np.float32),
+                      False, w.dtype)
     center, mean_abs = oracle.unit_heads(hp.center, hp.mean_abs, l, h, w.group)
     t0 = time.perf_counter()
     sc = oracle.score_keys(keys, center, mean_abs, base=w.base, offsets=w.offsets, layout=w.layout,

@@ -112,8 +112,13 @@ typedef enum tri_score_form { TRI_SCORE_ADDITIVE = 0, TRI_SCORE_MULTIPLICATIVE =
  *   seq_len: [n_seq] int32 number of cached keys per sequence.
  *   pos:     optional [n_seq][n_layer][n_kvh][slots] int32 RoPE positions of the cached
  *            keys (slots = max_len dense, max_pages * page paged); NULL means the position
- *            of slot j is j.  tri_score_keys supports only pos == NULL (TRI_ENOTSUP
- *            otherwise); tri_compact_kv gathers pos when given.
+ *            of slot j is j.  A cache compacted before holds keys whose slots no longer
+ *            equal their positions, and the next compression must score them at pos:
+ *              tri_score_keys, pre-RoPE keys, additive form: each key is scored at pos[j];
+ *              tri_score_keys, pre-RoPE keys, multiplicative form: TRI_ENOTSUP;
+ *              tri_score_keys, TRI_KEYS_POST_ROPE: pos is not read (the cached keys
+ *                already carry their rotation);
+ *              tri_compact_kv: pos is gathered into pos_out.
  *   k_scale: optional device [n_layer][n_kvh] float32, dtype TRI_FP8_E4M3 or TRI_INT8 only
  *            (must be NULL otherwise): the key of head (l, h) is its decoded code times
  *            k_scale[l * n_kvh + h] (NULL = 1).  Scores are computed from the scaled keys;
@@ -177,7 +182,8 @@ int tri_calibrate_stats(const void *q, int32_t dtype, int64_t n, int32_t n_layer
  *           + sum_f (1 - R_f) m_f |k_f|
  *   score(j) = max_hq s_hq(j)  (TRI_REDUCE_MAX)   or   mean_hq s_hq(j)  (TRI_REDUCE_MEAN)
  *
- * with Q = query_pos[s] (int64; NULL means seq_len[s] - 1).  With cfg->key_space ==
+ * with Q = query_pos[s] (int64; NULL means seq_len[s] - 1) and p_j = kv->pos[...][j] when
+ * kv->pos is given (pre-RoPE keys, additive form), else p_j = j.  With cfg->key_space ==
  * TRI_KEYS_POST_ROPE the cached vector of slot j is k'_f = k_f e^{i j theta_f} (RoPE
  * applied at position j) and the score is that of k_f; since
  * conj(k_f) e^{-i p_j theta_f} = conj(k'_f), it is evaluated as
@@ -228,8 +234,6 @@ int tri_compact_kv(const tri_kv *kv, const int32_t *kept, const int32_t *kept_n,
                    void *k_out, void *v_out, int32_t *pos_out, int32_t *freed, int32_t *n_freed,
                    int32_t *new_len, void *stream);
 
-/* Text of the last failure on the calling thread ("" if none).  Owned by the library;
- * valid until the next call on this thread. */
 /* Attention of the newest token over a compressed cache: the consumer of the compaction
  * outputs.  After compression the kept keys are rotated by RoPE at their own positions and
  * read by standard attention ([Review] "Core Mechanism"; [DevTo] "Solving the Memory
@@ -263,6 +267,8 @@ int tri_decode_attention(const tri_kv *kv, int32_t layer0, int32_t n_layers, con
                          int32_t rope_layout, int32_t key_space, int32_t group, float *out, void *ws,
                          size_t *ws_bytes, void *stream);
 
+/* Text of the last failure on the calling thread ("" if none).  Owned by the library;
+ * valid until the next call on this thread. */
 const char *tri_last_error(void);
 
 /* ABI version of this header: major * 10000 + minor * 100 + patch. */

@@ -27,6 +27,7 @@ __all__ = [
     "tri_score_keys",
     "tri_select_topb",
     "tri_compact_kv",
+    "tri_decode_attention",
     "tri_version",
     "compress",
 ]

@@ -76,11 +76,6 @@ def f32_to_bf16_bits(x) -> np.ndarray:
     return r.astype(np.uint16)
 
 
-def bf16_bits_to_f32(b) -> np.ndarray:
-    """Exact widening of bfloat16 bit patterns to float32."""
-    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
-
-
 def f32_to_fp8_e4m3(x) -> np.ndarray:
     """OCP E4M3 codes of float32 values: round to nearest even on the float32 bits,
     subnormal steps of 2^-9 below 2^-6, saturation at +-448, NaN -> S.1111.111."""
@@ -111,21 +106,6 @@ def f32_to_int8(x) -> np.ndarray:
     return np.clip(np.rint(x), -127, 127).astype(np.int8)
 
 
-def fp8_e4m3_to_f32(c) -> np.ndarray:
-    """Exact float32 values of OCP E4M3 codes (built from their bit fields)."""
-    c = np.asarray(c, dtype=np.uint8).astype(np.uint32)
-    sign = (c & 0x80) << 24
-    e = (c >> 3) & 0xF
-    m = c & 7
-    # normal: float32 exponent e - 7 + 127, mantissa m in its top 3 bits
-    normal = sign | ((e + 120) << 23) | (m << 20)
-    out = normal.view(np.float32).copy()
-    sub = e == 0
-    out[sub] = (m[sub].astype(np.float32) * np.float32(2.0 ** -9)) * np.where(c[sub] & 0x80, -1.0, 1.0).astype(np.float32)
-    out[(c & 0x7F) == 0x7F] = np.nan
-    return out
-
-
 def rows(seed: int, tag: int, unit: int, n_rows: int, mu, sigma, sink: bool,
          dtype: str = "bf16", row_start: int = 0, scale: float = 1.0) -> np.ndarray:
     """Rows row_start .. row_start+n_rows-1 of one unit.
@@ -150,16 +130,3 @@ def rows(seed: int, tag: int, unit: int, n_rows: int, mu, sigma, sink: bool,
     if dtype == "int8":
         return f32_to_int8(x * np.float32(1.0 / scale))
     raise ValueError(f"unknown dtype {dtype!r}")
-
-
-def rows_as_float(seed, tag, unit, n_rows, mu, sigma, sink, dtype="bf16", row_start=0, scale=1.0):
-    """Same rows as ``rows`` but always as float32 values (bf16 widened exactly, fp8 codes
-    decoded exactly and multiplied by their scale; int8 codes times their scale)."""
-    r = rows(seed, tag, unit, n_rows, mu, sigma, sink, dtype, row_start, scale)
-    if dtype == "f32":
-        return r
-    if dtype == "fp8":
-        return fp8_e4m3_to_f32(r) * np.float32(scale)
-    if dtype == "int8":
-        return r.astype(np.float32) * np.float32(scale)
-    return bf16_bits_to_f32(r)

@@ -9,6 +9,8 @@ from .triattention import (  # noqa: F401
     rope_theta,
     rope_apply,
     decode_fp8_e4m3,
+    decode_bf16,
+    decode_stored,
     split_bands,
     concentration,
     score_keys,

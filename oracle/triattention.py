@@ -43,9 +43,29 @@ Scores are reduced over the query heads of a GQA group (max or mean), the top-B 
 each KV head are kept with the most recent window always kept, and the survivors are
 packed forward into dense or paged storage.
 
-Parity status: every function here is pinned by the CPU tests (exact-centre RoPE
-identity, R = 0 limit, hand values, invariants, brute-force top-B, calibration closed
-forms, compaction invariants and the pages' memory ratios).  None is "parity unpinned".
+Parity status: each public function is pinned by a CPU test against something other than
+itself (tests/test_oracle_pins.py, tests/test_oracle_golden.py; planted mistakes in
+tests/test_oracle_mutations.py must each fail one of them):
+  rope_theta, split_bands, score_keys (additive)   exact-centre identity against textbook
+        2x2 RoPE rotations, R = 0 limit, single-band hand values, invariants (shift,
+        scaling, mean fold, identical heads, zero key)
+  concentration            hand values, including the 0/0 band (read as 0)
+  unit_heads               hand values of the contiguous GQA groups, and a score of KV head 1
+                           that only its own query heads can produce
+  score_magnitude_bound    equality with the score where every band is phase-aligned at
+                           R = 1, hand values under max and mean with R < 1 and R > 1, and
+                           |score| <= bound on random units
+  score_keys (multiplicative)   hand value, aligned-phase closed form, the single-band
+                           identity with the additive series, scaling by the key norm
+  rope_apply               textbook rotation, inverse, post-RoPE keys score like pre-RoPE keys
+  decode_fp8_e4m3          values the E4M3 format fixes (subnormals, normals, 448, NaN)
+  decode_bf16, decode_stored   values the bfloat16 format fixes, and every one of the 65536
+                           patterns against torch's own bfloat16 widening; int8 codes
+  select_top_b             brute force over all subsets on tiny inputs, edge cases
+  compact_dense, compact_paged_sequence   bit copies, forward packing, freed pages
+  calibrate                closed forms (identical samples, rotating samples, scaling)
+  decode_attention         one key, equal logits, a 3:1 hand weighting, relative positions
+No function here is "parity unpinned".
 """
 
 from __future__ import annotations
@@ -54,6 +74,8 @@ import numpy as np
 
 __all__ = [
     "decode_fp8_e4m3",
+    "decode_bf16",
+    "decode_stored",
     "rope_theta",
     "rope_apply",
     "split_bands",
@@ -88,6 +110,34 @@ def decode_fp8_e4m3(codes) -> np.ndarray:
     out = sign * val
     out[(c & 0x7F) == 0x7F] = np.nan
     return out
+
+
+def decode_bf16(bits) -> np.ndarray:
+    """Exact float64 values of bfloat16 bit patterns (1 sign, 8 exponent bits with bias 127,
+    7 mantissa bits; exponent field 0 is subnormal, 255 is infinity or NaN)."""
+    b = np.asarray(bits).astype(np.int64) & 0xFFFF
+    sign = np.where(b & 0x8000, -1.0, 1.0)
+    e = (b >> 7) & 0xFF
+    m = (b & 0x7F).astype(np.float64)
+    with np.errstate(over="ignore"):
+        val = np.where(e == 0, m * 2.0 ** -133, (1.0 + m / 128.0) * np.exp2(e - 127.0))
+    val = np.where(e == 0xFF, np.where(m == 0, np.inf, np.nan), val)
+    return sign * val
+
+
+def decode_stored(raw, dtype: str, scale: float = 1.0) -> np.ndarray:
+    """The float64 values a cache stores: float32 as is, bfloat16 bits decoded, and 8-bit
+    codes (OCP E4M3 or two's-complement int8) decoded and multiplied by the head's scale
+    (stored key = true key / scale).  This is the key the score is defined on."""
+    if dtype == "f32":
+        return np.asarray(raw, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return decode_bf16(np.asarray(raw).view(np.uint16))
+    if dtype == "fp8":
+        return decode_fp8_e4m3(np.asarray(raw).view(np.uint8)) * np.float64(scale)
+    if dtype == "int8":
+        return np.asarray(raw).view(np.int8).astype(np.float64) * np.float64(scale)
+    raise ValueError(f"unknown cache dtype {dtype!r}")
 
 
 # ---------------------------------------------------------------------------------------
@@ -359,6 +409,9 @@ def unit_heads(center, mean_abs, layer: int, kv_head: int, group: int):
     center [n_layer, n_qh, F(,2)], mean_abs [n_layer, n_qh, F].  Query head h reads
     KV head h // group (contiguous GQA groups).
     """
+    n_qh = np.asarray(mean_abs).shape[1]
+    if group < 1 or kv_head < 0 or (kv_head + 1) * group > n_qh:
+        raise ValueError(f"KV head {kv_head} with {group} query heads each needs more than {n_qh} query heads")
     hs = slice(kv_head * group, (kv_head + 1) * group)
     return _as_complex(np.asarray(center)[layer, hs]), np.asarray(mean_abs, np.float64)[layer, hs]
 

@@ -28,8 +28,8 @@ BITS_VIEW = {"f32": np.int32, "bf16": np.int16, "fp8": np.uint8, "int8": np.int8
 
 
 def host_rows(w, hp, s, layer, kv_head, tag=synth.TAG_K, as_float=True):
-    """One unit's rows from the host generator: float32 values (fp8 keys decoded and
-    multiplied by their head's scale) or the raw stored elements."""
+    """One unit's rows from the host generator: the stored elements as the oracle decodes
+    them (float64; 8-bit key codes times their head's scale), or the raw stored elements."""
     unit = W.unit_index(w, s, layer, kv_head)
     L = int(hp.lengths[s])
     scale = 1.0
@@ -39,8 +39,8 @@ def host_rows(w, hp, s, layer, kv_head, tag=synth.TAG_K, as_float=True):
             scale = float(hp.k_scale[layer, kv_head])
     else:
         mu, sig, sink = np.zeros(w.head_dim, np.float32), np.ones(w.head_dim, np.float32), False
-    fn = synth.rows_as_float if as_float else synth.rows
-    return fn(w.seed, tag, unit, L, mu, sig, sink, w.dtype, scale=scale)
+    raw = synth.rows(w.seed, tag, unit, L, mu, sig, sink, w.dtype, scale=scale)
+    return oracle.decode_stored(raw, w.dtype, scale) if as_float else raw
 
 
 def host_bits(w, hp, s, layer, kv_head, tag=synth.TAG_K):

@@ -101,11 +101,6 @@ def test_score_keys_validation():
     assert _score(c, _kv(k=None))[0] == _abi.TRI_EINVAL
     assert _score(c, _kv(max_len=0))[0] == _abi.TRI_EINVAL
     assert _score(c, _kv(max_len=(1 << 20) + 1))[0] == _abi.TRI_ENOTSUP
-    assert _score(c, _kv(pos=FAKE.value), ws_query=True) == (_abi.TRI_OK, 0)   # keys at explicit positions
-    cmp, _omp = _cfg(form=_abi.TRI_SCORE_MULTIPLICATIVE)
-    assert _score(cmp, _kv(pos=FAKE.value))[0] == _abi.TRI_ENOTSUP
-    cpo, _opo = _cfg(key_space=_abi.TRI_KEYS_POST_ROPE, form=_abi.TRI_SCORE_MULTIPLICATIVE)
-    assert _score(cpo, _kv(pos=FAKE.value), ws_query=True) == (_abi.TRI_OK, 0)   # rotated keys need none
     assert _score(c, _kv(layout=_abi.TRI_PAGED, page=32))[0] == _abi.TRI_ENOTSUP
     assert _score(c, _kv(layout=_abi.TRI_PAGED, block_table=None))[0] == _abi.TRI_EINVAL
     assert _score(c, _kv(), center=None)[0] == _abi.TRI_EINVAL
@@ -123,6 +118,26 @@ def test_score_keys_validation():
     neg = (ctypes.c_int32 * 2)(1, -3)
     cc, _k = _cfg(n_offsets=2, offsets=ctypes.cast(neg, ctypes.POINTER(ctypes.c_int32)))
     assert _score(cc, _kv())[0] == _abi.TRI_EINVAL
+
+
+def test_score_keys_position_contract():
+    # tri.h, tri_kv.pos: scoring reads explicit key positions for pre-RoPE keys in the additive
+    # form, refuses them (TRI_ENOTSUP) in the multiplicative form, and does not need them for
+    # keys cached after RoPE (either form).  The workspace query validates without launching.
+    pre_add, _a = _cfg()
+    pre_mul, _b = _cfg(form=_abi.TRI_SCORE_MULTIPLICATIVE)
+    post_add, _c = _cfg(key_space=_abi.TRI_KEYS_POST_ROPE)
+    post_mul, _d = _cfg(key_space=_abi.TRI_KEYS_POST_ROPE, form=_abi.TRI_SCORE_MULTIPLICATIVE)
+    with_pos = dict(pos=FAKE.value)
+    assert _score(pre_add, _kv(**with_pos), ws_query=True) == (_abi.TRI_OK, 0)
+    assert _score(pre_mul, _kv(**with_pos), ws_query=True)[0] == _abi.TRI_ENOTSUP
+    assert _score(pre_mul, _kv(**with_pos))[0] == _abi.TRI_ENOTSUP
+    assert "multiplicative" in _abi.lib().tri_last_error().decode()
+    assert _score(post_add, _kv(**with_pos), ws_query=True) == (_abi.TRI_OK, 0)
+    assert _score(post_mul, _kv(**with_pos), ws_query=True) == (_abi.TRI_OK, 0)
+    for dt in (_abi.TRI_F32, _abi.TRI_FP8_E4M3, _abi.TRI_INT8):
+        assert _score(pre_add, _kv(dtype=dt, **with_pos), ws_query=True) == (_abi.TRI_OK, 0)
+        assert _score(pre_add, _kv(dtype=dt, layout=_abi.TRI_PAGED, **with_pos), ws_query=True) == (_abi.TRI_OK, 0)
 
 
 def test_score_keys_workspace_query_launches_nothing():

@@ -56,7 +56,7 @@ def unit_rows(w, hp, s, l, h, n, tag=synth.TAG_K):
 
 
 def as_float(bits, dtype):
-    return bits if dtype == "f32" else synth.bf16_bits_to_f32(bits)
+    return oracle.decode_stored(bits, dtype)
 
 
 # ---------------------------------------------------------------------------------------

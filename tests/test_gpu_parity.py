@@ -588,7 +588,7 @@ def test_zero_duplicated_and_nan_key_rows():
     sc_h, kept_h = sc.cpu().numpy()[0, 0], kept.cpu().numpy()[0, 0]
     k_out, v_out = bits(out["k_out"])[0, 0], bits(out["v_out"])[0, 0]
     for h in range(w.n_kvh):
-        keys = synth.bf16_bits_to_f32(raw[h])
+        keys = oracle.decode_stored(raw[h], "bf16")
         center_h, mean_abs_h = oracle.unit_heads(hp.center, hp.mean_abs, 0, h, w.group)
         orc = oracle.score_keys(keys, center_h, mean_abs_h, base=w.base, offsets=w.offsets)
         S = oracle.score_magnitude_bound(keys, center_h, mean_abs_h)
@@ -639,15 +639,15 @@ def test_post_rope_small_dense(dtype, layout, group, reduce):
                 post = oracle.rope_apply(pre, np.arange(L), base=w.base, layout=layout).astype(np.float32)
                 if dtype == "bf16":
                     raw = synth.f32_to_bf16_bits(post).view(np.int16)
-                    cached[(s, l, h)] = synth.bf16_bits_to_f32(raw.view(np.uint16))
+                    cached[(s, l, h)] = oracle.decode_stored(raw, "bf16")
                 elif dtype == "fp8":
                     sc_lh = np.float32(hp.k_scale[l, h])
                     raw = synth.f32_to_fp8_e4m3(post / sc_lh)
-                    cached[(s, l, h)] = synth.fp8_e4m3_to_f32(raw) * sc_lh
+                    cached[(s, l, h)] = oracle.decode_stored(raw, "fp8", sc_lh)
                 elif dtype == "int8":
                     sc_lh = np.float32(hp.k_scale[l, h])
                     raw = synth.f32_to_int8(post / sc_lh)
-                    cached[(s, l, h)] = raw.astype(np.float32) * sc_lh
+                    cached[(s, l, h)] = oracle.decode_stored(raw, "int8", sc_lh)
                 else:
                     raw = post.view(np.int32)
                     cached[(s, l, h)] = post
@@ -769,7 +769,7 @@ def test_multiplicative_zero_and_nan_key_rows():
     assert np.all(sc[[5, 77, 300]] == 0.0) and np.isnan(sc[400])
     ok = np.ones(600, bool)
     ok[[5, 77, 300, 400]] = False          # checked above; their bound S is 0
-    orc, S = P.oracle_scores(w, hp, 0, 0, 0, synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(keys)), "pre",
+    orc, S = P.oracle_scores(w, hp, 0, 0, 0, oracle.decode_stored(synth.f32_to_bf16_bits(keys), "bf16"), "pre",
                              "multiplicative")
     P.check_scores(sc[ok], orc[ok], S[ok])
 
@@ -916,7 +916,8 @@ def test_longest_supported_unit_sampled():
     worst = 0.0
     for r0 in [0, 4096, 131072 - 32, 524288 + 7, 1000000, L - 1024, L - 300]:
         n = min(256, L - r0)
-        rows = synth.rows_as_float(w.seed, synth.TAG_K, 0, n, hp.mu_k[0, 0], hp.sigma, w.sink, w.dtype, row_start=r0)
+        rows = oracle.decode_stored(synth.rows(w.seed, synth.TAG_K, 0, n, hp.mu_k[0, 0], hp.sigma, w.sink, w.dtype,
+                                               row_start=r0), w.dtype)
         pos = np.arange(r0, r0 + n)
         orc = oracle.score_keys(rows, center, mean_abs, base=w.base, offsets=w.offsets, key_pos=pos,
                                 query_pos=L - 1, layout=w.layout, reduce=w.reduce)

@@ -49,6 +49,9 @@ def _pin_calls():
         pins.test_p7_dense_rows_are_bit_copies,
         pins.test_p7_paged_forward_packing,
         pins.test_p10_fp8_e4m3_values_fixed_by_the_format,
+        pins.test_p10_bf16_values_fixed_by_the_format,
+        pins.test_p10_bf16_all_patterns_match_torch,
+        pins.test_p10_stored_keys_decode_with_their_scale,
         pins.test_p11_hand_value_two_bands,
         pins.test_p12_one_key_returns_its_value,
         pins.test_p12_equal_logits_average_the_values,
@@ -59,6 +62,16 @@ def _pin_calls():
         calls.append(lambda layout=layout: pins.test_p11_single_band_centre_matches_amplitude_series(layout))
         calls.append(lambda layout=layout: pins.test_p12_hand_weighting_three_to_one(layout))
         calls.append(lambda layout=layout: pins.test_p12_relative_positions_and_post_rope_keys(layout))
+    calls += [
+        pins.test_p13_kv_head_reads_its_contiguous_query_heads,
+        pins.test_p13_score_of_kv_head_one_hand_value,
+        pins.test_p13_bound_hand_values_two_heads,
+        pins.test_p13_band_without_query_energy_adds_nothing,
+    ]
+    for layout in ("half", "interleaved"):
+        for reduce in ("max", "mean"):
+            calls.append(lambda layout=layout, reduce=reduce:
+                         pins.test_p13_bound_is_reached_by_aligned_phases(layout, reduce))
     calls += [lambda t=t: pins.test_p5_select_matches_brute_force(t) for t in range(60)]
     with open(golden.GOLDEN) as fh:
         import json
@@ -191,6 +204,25 @@ def _fp8_no_subnormals(codes):
     return out
 
 
+def _bf16_bias_126(bits):
+    # slip: exponent bias off by one
+    return T.__dict__["_orig_decode_bf16"](bits) * 2.0
+
+
+def _bf16_mantissa_8bit(bits):
+    # slip: the 7-bit mantissa read as if it had 8 bits
+    b = np.asarray(bits).astype(np.int64) & 0xFFFF
+    e = (b >> 7) & 0xFF
+    m = (b & 0x7F).astype(np.float64)
+    val = np.where(e == 0, m * 2.0 ** -133, (1.0 + m / 256.0) * np.exp2(e - 127.0))
+    return np.where(b & 0x8000, -1.0, 1.0) * val
+
+
+def _stored_scale_divided(raw, dtype, scale=1.0):
+    # slip: the head's scale divides instead of multiplying
+    return T.__dict__["_orig_decode_stored"](raw, dtype, 1.0 / scale)
+
+
 def _calib_abs_of_mean(q, layout="half"):
     qb = T.split_bands(q, layout)
     c = qb.mean(axis=0)
@@ -232,6 +264,60 @@ def _l2_as_l1(bands):
     return np.sum(np.abs(bands), axis=-1)
 
 
+def _unit_heads_strided(center, mean_abs, layer, kv_head, group):
+    # slip: query heads of a KV head taken with a stride of n_kvh instead of contiguously
+    n_qh = np.asarray(mean_abs).shape[1]
+    hs = slice(kv_head, None, n_qh // group)
+    return T._as_complex(np.asarray(center)[layer, hs]), np.asarray(mean_abs, np.float64)[layer, hs]
+
+
+def _unit_heads_offset(center, mean_abs, layer, kv_head, group):
+    # slip: the group starts one KV head late
+    n_qh = np.asarray(mean_abs).shape[1]
+    k = min(kv_head + 1, n_qh // group - 1)
+    hs = slice(k * group, (k + 1) * group)
+    return T._as_complex(np.asarray(center)[layer, hs]), np.asarray(mean_abs, np.float64)[layer, hs]
+
+
+def _bound(kind):
+    def bound(keys, center, mean_abs, *, layout="half", reduce="max", form="additive"):
+        if form != "additive":
+            return T.__dict__["_orig_bound"](keys, center, mean_abs, layout=layout, reduce=reduce, form=form)
+        center = T._as_complex(center)
+        mean_abs = np.asarray(mean_abs, dtype=np.float64)
+        if center.ndim == 1:
+            center, mean_abs = center[None, :], mean_abs[None, :]
+        k_abs = np.abs(T.split_bands(np.asarray(keys, dtype=np.float64), layout))
+        heads = []
+        for h in range(center.shape[0]):
+            R = T.concentration(center[h], mean_abs[h])
+            if kind == "abs_dropped":
+                coef = np.abs(center[h]) + (1.0 - R) * mean_abs[h]
+            elif kind == "no_centre_term":
+                coef = np.abs((1.0 - R) * mean_abs[h])
+            else:
+                coef = np.abs(center[h]) + np.abs((1.0 - R) * mean_abs[h])
+            heads.append(np.sum(coef[None, :] * k_abs, axis=1))
+        heads = np.stack(heads, axis=0)
+        if kind == "summed_over_heads":
+            return heads.sum(axis=0)
+        if kind == "inflated":
+            return 2.0 * T._reduce_heads(heads, reduce)
+        return T._reduce_heads(heads, reduce)
+    return bound
+
+
+def _concentration(zero_over_zero):
+    def conc(center, mean_abs):
+        center = np.asarray(center, dtype=np.complex128)
+        mean_abs = np.asarray(mean_abs, dtype=np.float64)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            out = np.abs(center) / mean_abs
+        out[mean_abs == 0] = zero_over_zero
+        return out
+    return conc
+
+
 MUTATIONS = {
     "theta_exponent": ("rope_theta", _theta_wrong_exponent),
     "bands_pairing": ("split_bands", _bands_swapped),
@@ -259,6 +345,17 @@ MUTATIONS = {
     "mult_norm_l1": ("_l2_norm", _l2_as_l1),
     "attention_key_not_rotated": ("decode_attention", _attention_key_not_rotated),
     "attention_no_scale": ("decode_attention", _attention_no_scale),
+    "bf16_exponent_bias": ("decode_bf16", _bf16_bias_126),
+    "bf16_mantissa_width": ("decode_bf16", _bf16_mantissa_8bit),
+    "stored_scale_divided": ("decode_stored", _stored_scale_divided),
+    "gqa_strided_heads": ("unit_heads", _unit_heads_strided),
+    "gqa_group_offset": ("unit_heads", _unit_heads_offset),
+    "bound_abs_dropped": ("score_magnitude_bound", _bound("abs_dropped")),
+    "bound_summed_over_heads": ("score_magnitude_bound", _bound("summed_over_heads")),
+    "bound_inflated": ("score_magnitude_bound", _bound("inflated")),
+    "bound_no_centre_term": ("score_magnitude_bound", _bound("no_centre_term")),
+    "concentration_0_over_0_is_1": ("concentration", _concentration(1.0)),
+    "concentration_0_over_0_is_nan": ("concentration", _concentration(np.nan)),
 }
 
 
@@ -273,6 +370,9 @@ def test_mutation_is_caught(name, monkeypatch):
     monkeypatch.setitem(T.__dict__, "_orig_decode_fp8", T.decode_fp8_e4m3)
     monkeypatch.setitem(T.__dict__, "_orig_unit", T._trig_unit_term)
     monkeypatch.setitem(T.__dict__, "_orig_attn", T.decode_attention)
+    monkeypatch.setitem(T.__dict__, "_orig_bound", T.score_magnitude_bound)
+    monkeypatch.setitem(T.__dict__, "_orig_decode_bf16", T.decode_bf16)
+    monkeypatch.setitem(T.__dict__, "_orig_decode_stored", T.decode_stored)
     monkeypatch.setattr(T, attr, repl)
     if hasattr(oracle, attr):
         monkeypatch.setattr(oracle, attr, repl)

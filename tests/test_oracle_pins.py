@@ -11,12 +11,17 @@ Each test states what it pins.  Nothing here calls the HIP library.
   P7  compaction invariants
   P9  keys cached after RoPE: the oracle's rotation equals textbook RoPE, undoes itself,
       and scoring rotated keys equals scoring the pre-RoPE keys
-  P10 fp8 (OCP E4M3) key codes: values the format definition fixes
+  P10 fp8 (OCP E4M3) key codes: values the format definition fixes; bfloat16 patterns:
+      values the format fixes and all 65536 patterns against torch's widening; int8 codes
   P11 multiplicative form: hand value, aligned-phase closed form, the single-band
       identity with the amplitude series, and scaling by the key norm
   P12 attention over the compressed cache: one key returns its value, equal logits
       average the values, a hand-made 3:1 weighting, the relative-position property
       against textbook RoPE, and post-RoPE keys give the same result
+  P13 the statistics a KV head reads (contiguous GQA groups) and the magnitude bound S_j:
+      hand values for the group of KV head 1, equality s_j = S_j where every band is
+      phase-aligned at R = 1, hand values of S_j under max and mean, and a band with no
+      query energy (E|q_f| = E[q_f] = 0, concentration 0/0 read as 0)
 """
 
 import itertools
@@ -640,3 +645,164 @@ def test_p12_relative_positions_and_post_rope_keys(layout):
     post = oracle.decode_attention(q, k_post, v, base=base, key_pos=pos, query_pos=Q, layout=layout,
                                    key_space="post")
     assert np.allclose(out, post, atol=1e-9)
+
+
+# ---------------------------------------------------------------------------------------
+# P13 GQA mapping, the magnitude bound and the 0/0 band
+# ---------------------------------------------------------------------------------------
+
+def _stats_table(n_layer=2, n_qh=6, F=2):
+    """Statistics where query head q of layer l has centre (10 l + q + 1) on band 0 only
+    (0 elsewhere) and mean magnitude 2 (10 l + q + 1) on every band: every head is
+    told apart by its values."""
+    center = np.zeros((n_layer, n_qh, F, 2))
+    mean_abs = np.zeros((n_layer, n_qh, F))
+    for l in range(n_layer):
+        for q in range(n_qh):
+            center[l, q, 0, 0] = 10 * l + q + 1
+            mean_abs[l, q, :] = 2 * (10 * l + q + 1)
+    return center, mean_abs
+
+
+def test_p13_kv_head_reads_its_contiguous_query_heads():
+    # 6 query heads, G = 2: KV head h is read by query heads 2h and 2h + 1
+    center, mean_abs = _stats_table()
+    c, m = oracle.unit_heads(center, mean_abs, 1, 1, 2)
+    # layer 1, query heads 2 and 3: centres 13 and 14, magnitudes 26 and 28
+    np.testing.assert_array_equal(c, np.array([[13.0 + 0j, 0.0], [14.0 + 0j, 0.0]]))
+    np.testing.assert_array_equal(m, np.array([[26.0, 26.0], [28.0, 28.0]]))
+    c, m = oracle.unit_heads(center, mean_abs, 0, 1, 3)      # G = 3: heads 3, 4, 5 of layer 0
+    np.testing.assert_array_equal(c[:, 0].real, [4.0, 5.0, 6.0])
+    with pytest.raises(ValueError):                          # there is no KV head 2 at G = 3
+        oracle.unit_heads(center, mean_abs, 0, 2, 3)
+    c, m = oracle.unit_heads(center, mean_abs, 0, 0, 6)      # one KV head: all six
+    np.testing.assert_array_equal(c[:, 0].real, [1.0, 2.0, 3.0, 4.0, 5.0, 6.0])
+
+
+def test_p13_score_of_kv_head_one_hand_value():
+    # Only query heads 2 and 3 of layer 1 have a centre; every other head is all zeros (and
+    # E|q| = 0 there, so it adds nothing).  d = 4 (two bands, theta_0 = 1), key band 0 = 1,
+    # band 1 = 0, query at the key's position, one offset Delta = 1:
+    #   head 2: E q_0 = 3       -> 3 cos(1)
+    #   head 3: E q_0 = 5i      -> 5 cos(1 + pi/2) = -5 sin(1)
+    # both with E|q_0| = |E q_0| (R = 1, no norm term).
+    n_layer, n_qh, F, G = 2, 6, 2, 2
+    center = np.zeros((n_layer, n_qh, F, 2))
+    mean_abs = np.zeros((n_layer, n_qh, F))
+    center[1, 2, 0] = [3.0, 0.0]
+    center[1, 3, 0] = [0.0, 5.0]
+    mean_abs[1, 2, 0], mean_abs[1, 3, 0] = 3.0, 5.0
+    key = np.array([[1.0, 0.0, 0.0, 0.0]])
+    kw = dict(base=100.0, offsets=[1], key_pos=[0], query_pos=0)
+    got = {}
+    for h in range(n_qh // G):
+        c, m = oracle.unit_heads(center, mean_abs, 1, h, G)
+        got[h] = (oracle.score_keys(key, c, m, reduce="max", **kw)[0],
+                  oracle.score_keys(key, c, m, reduce="mean", **kw)[0])
+    assert abs(got[1][0] - 3.0 * math.cos(1.0)) < 1e-14
+    assert abs(got[1][1] - (3.0 * math.cos(1.0) - 5.0 * math.sin(1.0)) / 2.0) < 1e-14
+    assert got[0] == (0.0, 0.0) and got[2] == (0.0, 0.0)
+
+
+@pytest.mark.parametrize("layout", ["half", "interleaved"])
+@pytest.mark.parametrize("reduce", ["max", "mean"])
+def test_p13_bound_is_reached_by_aligned_phases(layout, reduce):
+    # R = 1 on every band (E|q_f| = |E q_f|: no norm term).  Choose each key band's phase so
+    # that d theta_f + arg E q_f - arg k_f = 0 at the one offset: every cosine is 1 and
+    # s_j = sum_f |E q_f| |k_f|, which is exactly S_j (the same for identical heads).
+    rng = np.random.default_rng(21)
+    d, F, L = 16, 8, 5
+    base, Q, delta = 300.0, 40, 3
+    cq = rng.standard_normal(F) + 1j * rng.standard_normal(F)
+    theta = np.array([base ** (-2.0 * f / d) for f in range(F)])
+    pos = np.array([0, 7, 19, 33, 40])
+    mags = rng.uniform(0.5, 2.0, (L, F))
+    kb = mags * np.exp(1j * ((Q - pos[:, None] + delta) * theta[None, :] + np.angle(cq)[None, :]))
+    keys = np.empty((L, d))
+    if layout == "half":
+        keys[:, :F], keys[:, F:] = kb.real, kb.imag
+    else:
+        keys[:, 0::2], keys[:, 1::2] = kb.real, kb.imag
+    center = np.stack([cq.real, cq.imag], -1)[None].repeat(2, axis=0)      # two identical heads
+    mean_abs = np.abs(cq)[None].repeat(2, axis=0)
+    s = oracle.score_keys(keys, center, mean_abs, base=base, offsets=[delta], key_pos=pos, query_pos=Q,
+                          layout=layout, reduce=reduce)
+    S = oracle.score_magnitude_bound(keys, center, mean_abs, layout=layout, reduce=reduce)
+    want = (mags * np.abs(cq)[None, :]).sum(axis=1)
+    np.testing.assert_allclose(S, want, rtol=1e-13, atol=0)
+    np.testing.assert_allclose(s, S, rtol=1e-12, atol=0)
+
+
+def test_p13_bound_hand_values_two_heads():
+    # d = 4: bands k_0 = 3, k_1 = 4i (|k| = 3, 4).  Coefficient of band f in S:
+    # |E q_f| + |(1 - R_f) E|q_f||.
+    #   head 0: E q = (1, 0),  E|q| = (2, 1)    R = (0.5, 0)  coef = (1 + 1,   0 + 1)   = (2, 1)
+    #   head 1: E q = (2i, 1), E|q| = (2, 0.5)  R = (1, 2)    coef = (2 + 0,   1 + 0.5) = (2, 1.5)
+    # S_head0 = 2*3 + 1*4 = 10, S_head1 = 2*3 + 1.5*4 = 12: max 12, mean 11.
+    keys = np.array([[3.0, 0.0, 0.0, 4.0]])
+    center = np.array([[[1.0, 0.0], [0.0, 0.0]], [[0.0, 2.0], [1.0, 0.0]]])
+    mean_abs = np.array([[2.0, 1.0], [2.0, 0.5]])
+    assert oracle.score_magnitude_bound(keys, center, mean_abs, reduce="max")[0] == pytest.approx(12.0, abs=1e-14)
+    assert oracle.score_magnitude_bound(keys, center, mean_abs, reduce="mean")[0] == pytest.approx(11.0, abs=1e-14)
+    # and the scores lie inside it (any offsets)
+    for reduce, S in (("max", 12.0), ("mean", 11.0)):
+        s = oracle.score_keys(keys, center, mean_abs, base=10.0, offsets=[1, 2, 5], reduce=reduce)
+        assert abs(s[0]) <= S
+
+
+def test_p13_band_without_query_energy_adds_nothing():
+    # concentration of a band with E|q_f| = 0 (and so E q_f = 0) is read as 0, and the band
+    # adds nothing to the score or to the bound.  d = 4: band 0 has E q = 0.6, E|q| = 2
+    # (R = 0.3); band 1 has neither.  k = (2i, 7 + 7i), query at the key, Delta = 5,
+    # theta_0 = 1: s = 0.6 * 2 cos(5 - pi/2) + (1 - 0.3) * 2 * 2 = 1.2 sin 5 + 2.8, and
+    # S = 2 (0.6 + 1.4) = 4.
+    np.testing.assert_array_equal(oracle.concentration(np.array([0.6 + 0j, 0j]), np.array([2.0, 0.0])),
+                                  [0.3, 0.0])
+    assert oracle.concentration(np.array([0j]), np.array([0.0]))[0] == 0.0
+    keys = np.array([[0.0, 7.0, 2.0, 7.0]])
+    center = np.array([[[0.6, 0.0], [0.0, 0.0]]])
+    mean_abs = np.array([[2.0, 0.0]])
+    s = oracle.score_keys(keys, center, mean_abs, base=10.0, offsets=[5], key_pos=[0], query_pos=0)
+    assert abs(s[0] - (1.2 * math.sin(5.0) + 2.8)) < 1e-14
+    S = oracle.score_magnitude_bound(keys, center, mean_abs)
+    assert abs(S[0] - 4.0) < 1e-14
+
+
+# ---------------------------------------------------------------------------------------
+# P10 (continued): bfloat16 patterns and the stored-key decoding
+# ---------------------------------------------------------------------------------------
+
+def test_p10_bf16_values_fixed_by_the_format():
+    dec = lambda b: float(oracle.decode_bf16(np.array([b], dtype=np.uint16))[0])
+    assert dec(0x3F80) == 1.0 and dec(0xBF80) == -1.0 and dec(0x4000) == 2.0
+    assert dec(0x3FC0) == 1.5 and dec(0x4049) == 3.140625 and dec(0x0000) == 0.0
+    assert dec(0x8000) == 0.0 and math.copysign(1.0, dec(0x8000)) == -1.0
+    assert dec(0x0001) == 2.0 ** -133                       # smallest subnormal
+    assert dec(0x007F) == 127 * 2.0 ** -133                 # largest subnormal
+    assert dec(0x0080) == 2.0 ** -126                       # smallest normal
+    assert dec(0x7F7F) == (2.0 - 2.0 ** -7) * 2.0 ** 127    # largest finite
+    assert dec(0x7F80) == math.inf and dec(0xFF80) == -math.inf
+    assert math.isnan(dec(0x7FC0)) and math.isnan(dec(0xFF81))
+
+
+def test_p10_bf16_all_patterns_match_torch():
+    torch = pytest.importorskip("torch")
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.decode_bf16(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_p10_stored_keys_decode_with_their_scale():
+    codes = np.array([0x38, 0xB8, 0x01, 0x7E], dtype=np.uint8)          # 1, -1, 2^-9, 448
+    np.testing.assert_array_equal(oracle.decode_stored(codes, "fp8", 0.5), [0.5, -0.5, 2.0 ** -10, 224.0])
+    i8 = np.array([-128, -127, -1, 0, 1, 127], dtype=np.int8)
+    np.testing.assert_array_equal(oracle.decode_stored(i8, "int8", 0.125),
+                                  [-16.0, -15.875, -0.125, 0.0, 0.125, 15.875])
+    bf = np.array([0x3F80, 0xC040], dtype=np.uint16)                     # 1, -3
+    np.testing.assert_array_equal(oracle.decode_stored(bf.view(np.int16), "bf16"), [1.0, -3.0])
+    f = np.array([0.1, -2.5], dtype=np.float32)
+    np.testing.assert_array_equal(oracle.decode_stored(f, "f32"), f.astype(np.float64))
