@@ -267,6 +267,22 @@ int tri_decode_attention(const tri_kv *kv, int32_t layer0, int32_t n_layers, con
                          int32_t rope_layout, int32_t key_space, int32_t group, float *out, void *ws,
                          size_t *ws_bytes, void *stream);
 
+/* tri_decode_attention without any allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, results and errors as tri_decode_attention with a workspace, except:
+ *   - the partial softmax states of a split shape go to a scratch array the library holds in
+ *     device memory, 8 MiB per GPU, until the process ends (it is set up on the first call
+ *     on each device); nothing is allocated or freed by the call;
+ *   - a shape whose split needs more than those 8 MiB (tri_decode_attention's workspace size
+ *     query returns the need) is refused with TRI_EWORKSPACE before anything is launched;
+ *   - every call on one GPU shares that GPU's scratch: calls that overlap on one GPU (other
+ *     streams or threads) race on it and must be serialised by the caller.  Each call writes
+ *     every scratch entry it reads, so nothing has to be cleared between calls. */
+int tri_decode_attention_noalloc(const tri_kv *kv, int32_t layer0, int32_t n_layers, const float *q,
+                                 const int64_t *query_pos, const int32_t *pos, int64_t pos_stride,
+                                 double rope_base, int32_t rope_layout, int32_t key_space, int32_t group,
+                                 float *out, void *stream);
+
 /* Text of the last failure on the calling thread ("" if none).  Owned by the library;
  * valid until the next call on this thread. */
 const char *tri_last_error(void);
@@ -274,7 +290,7 @@ const char *tri_last_error(void);
 /* ABI version of this header: major * 10000 + minor * 100 + patch. */
 int tri_version(void);
 
-#define TRI_VERSION 10600
+#define TRI_VERSION 10700
 
 #ifdef __cplusplus
 }

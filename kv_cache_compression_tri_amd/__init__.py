@@ -28,6 +28,7 @@ __all__ = [
     "tri_select_topb",
     "tri_compact_kv",
     "tri_decode_attention",
+    "tri_decode_attention_noalloc",
     "tri_version",
     "compress",
 ]
@@ -313,17 +314,10 @@ def tri_compact_kv(kv: KVCache, kept, kept_n, budget: int, k_out=None, v_out=Non
             "new_len": new_len}
 
 
-def tri_decode_attention(kv: KVCache, q, query_pos, *, rope_base: float, group: int, pos=None, layer0: int = 0,
-                         n_layers=None, rope_layout: str = "half", key_space: str = "pre", out=None, stream=None,
-                         workspace="auto"):
-    """Attention of the newest token over a (compressed) cache: keys rotated by RoPE at their
-    positions (pos, e.g. the compaction's pos_out [n_seq, n_layer, n_kvh, budget]; None = slot
-    index), softmax over kv.seq_len keys.  q: float32 [n_seq, n_layers, n_kvh * group, d]
-    pre-RoPE queries at query_pos (int64 [n_seq]).  Returns float32 out of q's shape.
-    workspace: "auto" (allocated here when the shape is split over several workgroups per
-    unit), None (one workgroup per unit, no workspace), or a device uint8 tensor."""
+def _attention_args(kv: KVCache, q, query_pos, rope_base, group, pos, layer0, n_layers, rope_layout, key_space,
+                    out, allocate_out):
+    """Checked arguments of the attention entry points, up to and including out."""
     torch = _torch()
-    L = _abi.lib()
     desc = kv.descriptor()
     n_layers = desc.n_layer - layer0 if n_layers is None else int(n_layers)
     shape_q = (kv.n_seq, n_layers, desc.n_kvh * int(group), desc.head_dim)
@@ -338,11 +332,29 @@ def tri_decode_attention(kv: KVCache, q, query_pos, *, rope_base: float, group: 
             raise ValueError("pos must be [n_seq, n_layer, n_kvh, stride]")
         pos_stride = int(pos.shape[3])
     if out is None:
+        if not allocate_out:
+            raise ValueError("out is required")
         out = torch.empty(shape_q, dtype=torch.float32, device=q.device)
     _dev(out, "out", torch.float32)
     _shape(out, "out", shape_q)
     args = (ctypes.byref(desc), int(layer0), n_layers, _ptr(q), _ptr(query_pos), _ptr(pos), pos_stride,
             float(rope_base), _LAYOUTS[rope_layout], _KEY_SPACES[key_space], int(group), _ptr(out))
+    return args, out, desc
+
+
+def tri_decode_attention(kv: KVCache, q, query_pos, *, rope_base: float, group: int, pos=None, layer0: int = 0,
+                         n_layers=None, rope_layout: str = "half", key_space: str = "pre", out=None, stream=None,
+                         workspace="auto"):
+    """Attention of the newest token over a (compressed) cache: keys rotated by RoPE at their
+    positions (pos, e.g. the compaction's pos_out [n_seq, n_layer, n_kvh, budget]; None = slot
+    index), softmax over kv.seq_len keys.  q: float32 [n_seq, n_layers, n_kvh * group, d]
+    pre-RoPE queries at query_pos (int64 [n_seq]).  Returns float32 out of q's shape.
+    workspace: "auto" (allocated here when the shape is split over several workgroups per
+    unit), None (one workgroup per unit, no workspace), or a device uint8 tensor."""
+    torch = _torch()
+    L = _abi.lib()
+    args, out, _desc = _attention_args(kv, q, query_pos, rope_base, group, pos, layer0, n_layers, rope_layout,
+                                       key_space, out, True)
     ws, nbytes, cap = None, None, ctypes.c_size_t(0)
     if workspace is not None:
         need = ctypes.c_size_t(0)
@@ -356,6 +368,18 @@ def tri_decode_attention(kv: KVCache, q, query_pos, *, rope_base: float, group: 
             cap.value = workspace.numel()
             ws, nbytes = _ptr(workspace), ctypes.byref(cap)
     _abi.check(L.tri_decode_attention(*args, ws, nbytes, _stream(stream)))
+    return out
+
+
+def tri_decode_attention_noalloc(kv: KVCache, q, query_pos, *, rope_base: float, group: int, out, pos=None,
+                                 layer0: int = 0, n_layers=None, rope_layout: str = "half", key_space: str = "pre",
+                                 stream=None):
+    """tri_decode_attention that allocates nothing: split shapes keep their partial results in
+    the library's static per-GPU scratch (8 MiB; larger needs raise TriError TRI_EWORKSPACE).
+    out must be given.  Calls that overlap on one GPU race on the scratch."""
+    args, out, _desc = _attention_args(kv, q, query_pos, rope_base, group, pos, layer0, n_layers, rope_layout,
+                                       key_space, out, False)
+    _abi.check(_abi.lib().tri_decode_attention_noalloc(*args, _stream(stream)))
     return out
 
 

@@ -25,6 +25,7 @@ EXPORTED = (
     "tri_last_error",
     "tri_version",
     "tri_decode_attention",
+    "tri_decode_attention_noalloc",
 )
 
 
@@ -95,8 +96,10 @@ def lib(path: str = LIB_PATH):
     L.tri_decode_attention.argtypes = [POINTER(TriKV), c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_int64,
                                        c_double, c_int32, c_int32, c_int32, c_void_p, c_void_p, POINTER(c_size_t),
                                        c_void_p]
+    L.tri_decode_attention_noalloc.argtypes = [POINTER(TriKV), c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                                               c_int64, c_double, c_int32, c_int32, c_int32, c_void_p, c_void_p]
     for name in ("tri_calibrate_stats", "tri_score_keys", "tri_select_topb", "tri_compact_kv", "tri_version",
-                 "tri_decode_attention"):
+                 "tri_decode_attention", "tri_decode_attention_noalloc"):
         getattr(L, name).restype = c_int
     _LIB = L
     return L

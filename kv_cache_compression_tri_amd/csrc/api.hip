@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 namespace {
@@ -95,6 +96,105 @@ int workspace(void* ws, size_t* ws_bytes, size_t need) {
   return 0;
 }
 
+// Validation and launch parameters of the attention consumer (shared by its two entry points).
+int decode_setup(const tri_kv* kv, int32_t layer0, int32_t n_layers, const float* q, const int64_t* query_pos,
+                 const int32_t* pos, int64_t pos_stride, double rope_base, int32_t rope_layout, int32_t key_space,
+                 int32_t group, float* out, tri::DecodeParams& p, int64_t& unit_passes) {
+  if (int rc = check_kv(kv, true)) return rc;
+  if (kv->dtype != TRI_F32 && kv->dtype != TRI_BF16)
+    return fail(TRI_ENOTSUP, "attention reads float32 or bfloat16 caches");
+  if (!kv->v) return fail(TRI_EINVAL, "v is NULL");
+  if (!q || !query_pos || !out) return fail(TRI_EINVAL, "q, query_pos and out must be non-NULL");
+  if (n_layers < 1 || layer0 < 0 || int64_t(layer0) + n_layers > kv->n_layer)
+    return fail(TRI_EINVAL, "layers [%d, %d) outside [0, %d)", layer0, layer0 + n_layers, kv->n_layer);
+  if (group < 1) return fail(TRI_EINVAL, "group must be >= 1");
+  if (group > tri::kMaxGroup) return fail(TRI_ENOTSUP, "group %d > %d", group, tri::kMaxGroup);
+  if (!std::isfinite(rope_base) || rope_base <= 0.0) return fail(TRI_EINVAL, "rope_base must be finite and > 0");
+  if (rope_layout != TRI_ROPE_HALF && rope_layout != TRI_ROPE_INTERLEAVED)
+    return fail(TRI_EINVAL, "unknown rope layout %d", rope_layout);
+  if (key_space != TRI_KEYS_PRE_ROPE && key_space != TRI_KEYS_POST_ROPE)
+    return fail(TRI_EINVAL, "unknown key space %d", key_space);
+  const int64_t slots = slots_of(kv);
+  if (pos && pos_stride < slots) return fail(TRI_EINVAL, "pos_stride %lld < %lld slots", (long long)pos_stride,
+                                             (long long)slots);
+  unit_passes = int64_t(kv->n_seq) * n_layers * kv->n_kvh *
+                ((group + tri::kDecodeHeadsPerPass - 1) / tri::kDecodeHeadsPerPass);
+  for (int f = 0; f < tri::kBands; ++f)
+    p.theta_turns[f] = std::pow(rope_base, -2.0 * f / double(tri::kHeadDim)) / (2.0 * M_PI);
+  p.k = kv->k;
+  p.v = kv->v;
+  p.seq_len = kv->seq_len;
+  p.block_table = kv->layout == TRI_PAGED ? kv->block_table : nullptr;
+  p.pos = pos;
+  p.query_pos = query_pos;
+  p.q = q;
+  p.out = out;
+  p.max_len = kv->max_len;
+  p.slots = slots;
+  p.pos_stride = pos ? pos_stride : 0;
+  p.n_seq = kv->n_seq;
+  p.n_layer = kv->n_layer;
+  p.n_kvh = kv->n_kvh;
+  p.group = group;
+  p.max_pages = kv->max_pages;
+  p.layer0 = layer0;
+  p.n_layers = n_layers;
+  return TRI_OK;
+}
+
+// Launch with n_split slot splits; their partial softmax states go to `parts_buf` (256-byte
+// aligned, decode_workspace_bytes(unit_passes, n_split) bytes) when n_split > 1.
+int decode_launch(const tri_kv* kv, tri::DecodeParams& p, int64_t unit_passes, int n_split, void* parts_buf,
+                  int32_t rope_layout, int32_t key_space, void* stream) {
+  if (unit_passes * n_split > 0x7FFFFFFF) return fail(TRI_ENOTSUP, "too many units");
+  p.n_split = n_split;
+  if (n_split > 1) {
+    p.split_len = ((p.slots + n_split - 1) / n_split + 63) / 64 * 64;
+    const int64_t parts = unit_passes * n_split * tri::kDecodeHeadsPerPass;
+    p.part_ml = static_cast<float*>(parts_buf);
+    p.part_acc = reinterpret_cast<float*>(static_cast<char*>(parts_buf) + ((parts * 2 * 4 + 255) / 256) * 256);
+  }
+  (void)hipGetLastError();
+  hipError_t e = tri::launch_decode_attention(p, kv->dtype == TRI_BF16, rope_layout == TRI_ROPE_INTERLEAVED,
+                                              kv->layout == TRI_PAGED, key_space == TRI_KEYS_POST_ROPE,
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TRI_OK : hip_fail(e, "attention launch");
+}
+
+// Static scratch of tri_decode_attention_noalloc: a file-scope device array, one copy per GPU,
+// held until the process ends.  In host code `scratch` names a host-side stand-in, so its
+// device address is looked up once per device (with that device current) and only that
+// address is passed to kernels.
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+int static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(TRI_ENOTSUP, "device %d: the static scratch covers devices 0..%d", dev,
+                                                 kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || reinterpret_cast<uintptr_t>(ptr) % 256 != 0)
+      return fail(TRI_EHIP, "static scratch of device %d is not 256-byte aligned", dev);
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return TRI_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -107,27 +207,13 @@ int tri_decode_attention(const tri_kv* kv, int32_t layer0, int32_t n_layers, con
                          size_t* ws_bytes, void* stream) {
   try {
     g_error.clear();
-    if (int rc = check_kv(kv, true)) return rc;
-    if (kv->dtype != TRI_F32 && kv->dtype != TRI_BF16)
-      return fail(TRI_ENOTSUP, "attention reads float32 or bfloat16 caches");
-    if (!kv->v) return fail(TRI_EINVAL, "v is NULL");
-    if (!q || !query_pos || !out) return fail(TRI_EINVAL, "q, query_pos and out must be non-NULL");
-    if (n_layers < 1 || layer0 < 0 || int64_t(layer0) + n_layers > kv->n_layer)
-      return fail(TRI_EINVAL, "layers [%d, %d) outside [0, %d)", layer0, layer0 + n_layers, kv->n_layer);
-    if (group < 1) return fail(TRI_EINVAL, "group must be >= 1");
-    if (group > tri::kMaxGroup) return fail(TRI_ENOTSUP, "group %d > %d", group, tri::kMaxGroup);
-    if (!std::isfinite(rope_base) || rope_base <= 0.0) return fail(TRI_EINVAL, "rope_base must be finite and > 0");
-    if (rope_layout != TRI_ROPE_HALF && rope_layout != TRI_ROPE_INTERLEAVED)
-      return fail(TRI_EINVAL, "unknown rope layout %d", rope_layout);
-    if (key_space != TRI_KEYS_PRE_ROPE && key_space != TRI_KEYS_POST_ROPE)
-      return fail(TRI_EINVAL, "unknown key space %d", key_space);
-    const int64_t slots = slots_of(kv);
-    if (pos && pos_stride < slots) return fail(TRI_EINVAL, "pos_stride %lld < %lld slots", (long long)pos_stride,
-                                               (long long)slots);
+    tri::DecodeParams p{};
+    int64_t unit_passes = 0;
+    if (int rc = decode_setup(kv, layer0, n_layers, q, query_pos, pos, pos_stride, rope_base, rope_layout,
+                              key_space, group, out, p, unit_passes))
+      return rc;
     // optional workspace: it lets few, long units split their slots over several workgroups
-    const int64_t unit_passes = int64_t(kv->n_seq) * n_layers * kv->n_kvh *
-                                ((group + tri::kDecodeHeadsPerPass - 1) / tri::kDecodeHeadsPerPass);
-    const int n_split = tri::decode_splits(unit_passes, slots);
+    const int n_split = tri::decode_splits(unit_passes, p.slots);
     const size_t need = size_t(tri::decode_workspace_bytes(unit_passes, n_split));
     if (ws_bytes && !ws) {
       *ws_bytes = need;
@@ -137,42 +223,39 @@ int tri_decode_attention(const tri_kv* kv, int32_t layer0, int32_t n_layers, con
     if (split && *ws_bytes < need)
       return fail(TRI_EWORKSPACE, "workspace of %zu bytes required (%zu given)", need, *ws_bytes);
     if (split && reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(TRI_EINVAL, "workspace must be 256-byte aligned");
-    if (unit_passes * (split ? n_split : 1) > 0x7FFFFFFF) return fail(TRI_ENOTSUP, "too many units");
-    tri::DecodeParams p{};
-    p.n_split = split ? n_split : 1;
-    if (split) {
-      p.split_len = ((slots + n_split - 1) / n_split + 63) / 64 * 64;
-      const int64_t parts = unit_passes * n_split * tri::kDecodeHeadsPerPass;
-      p.part_ml = static_cast<float*>(ws);
-      p.part_acc = reinterpret_cast<float*>(static_cast<char*>(ws) + ((parts * 2 * 4 + 255) / 256) * 256);
-    }
-    for (int f = 0; f < tri::kBands; ++f)
-      p.theta_turns[f] = std::pow(rope_base, -2.0 * f / double(tri::kHeadDim)) / (2.0 * M_PI);
-    p.k = kv->k;
-    p.v = kv->v;
-    p.seq_len = kv->seq_len;
-    p.block_table = kv->layout == TRI_PAGED ? kv->block_table : nullptr;
-    p.pos = pos;
-    p.query_pos = query_pos;
-    p.q = q;
-    p.out = out;
-    p.max_len = kv->max_len;
-    p.slots = slots;
-    p.pos_stride = pos ? pos_stride : 0;
-    p.n_seq = kv->n_seq;
-    p.n_layer = kv->n_layer;
-    p.n_kvh = kv->n_kvh;
-    p.group = group;
-    p.max_pages = kv->max_pages;
-    p.layer0 = layer0;
-    p.n_layers = n_layers;
-    (void)hipGetLastError();
-    hipError_t e = tri::launch_decode_attention(p, kv->dtype == TRI_BF16, rope_layout == TRI_ROPE_INTERLEAVED,
-                                                kv->layout == TRI_PAGED, key_space == TRI_KEYS_POST_ROPE,
-                                                static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? TRI_OK : hip_fail(e, "attention launch");
+    return decode_launch(kv, p, unit_passes, split ? n_split : 1, split ? ws : nullptr, rope_layout, key_space,
+                         stream);
   } catch (...) {
     return fail(TRI_EHIP, "unexpected host exception in tri_decode_attention");
+  }
+}
+
+int tri_decode_attention_noalloc(const tri_kv* kv, int32_t layer0, int32_t n_layers, const float* q,
+                                 const int64_t* query_pos, const int32_t* pos, int64_t pos_stride,
+                                 double rope_base, int32_t rope_layout, int32_t key_space, int32_t group,
+                                 float* out, void* stream) {
+  try {
+    g_error.clear();
+    tri::DecodeParams p{};
+    int64_t unit_passes = 0;
+    if (int rc = decode_setup(kv, layer0, n_layers, q, query_pos, pos, pos_stride, rope_base, rope_layout,
+                              key_space, group, out, p, unit_passes))
+      return rc;
+    // the split tri_decode_attention takes with a workspace, its partial results in the
+    // library's static scratch of this device
+    const int n_split = tri::decode_splits(unit_passes, p.slots);
+    const size_t need = size_t(tri::decode_workspace_bytes(unit_passes, n_split));
+    if (need > kStaticScratchBytes)
+      return fail(TRI_EWORKSPACE,
+                  "this shape splits its slots %d ways and needs %zu bytes of scratch; the static scratch "
+                  "holds %zu (call tri_decode_attention with a workspace, or without one)",
+                  n_split, need, kStaticScratchBytes);
+    void* scr = nullptr;
+    if (need > 0)
+      if (int rc = static_scratch(&scr)) return rc;
+    return decode_launch(kv, p, unit_passes, need > 0 ? n_split : 1, scr, rope_layout, key_space, stream);
+  } catch (...) {
+    return fail(TRI_EHIP, "unexpected host exception in tri_decode_attention_noalloc");
   }
 }
 

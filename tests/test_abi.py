@@ -311,3 +311,29 @@ def test_decode_attention_workspace():
     big = ctypes.c_size_t(1 << 20)
     assert att(_kv(), 4, ctypes.c_void_p(FAKE.value + 8), ctypes.byref(big)) == _abi.TRI_EINVAL
     assert "aligned" in L.tri_last_error().decode()
+
+
+def test_decode_attention_noalloc_validation():
+    # the no-allocation attention validates like tri_decode_attention, and refuses before any
+    # launch a shape whose slot split would need more than its 8 MiB static scratch
+    L = _abi.lib()
+
+    def att(kv=None, group=4, n_layers=2, base=1e6, ks=0):
+        kv = kv or _kv()
+        return L.tri_decode_attention_noalloc(ctypes.byref(kv), 0, n_layers, FAKE, FAKE, None, 0, base, 0, ks,
+                                              group, FAKE, None)
+    assert att(kv=_kv(dtype=_abi.TRI_FP8_E4M3)) == _abi.TRI_ENOTSUP
+    assert att(group=9) == _abi.TRI_ENOTSUP
+    assert att(group=0) == _abi.TRI_EINVAL
+    assert att(n_layers=3) == _abi.TRI_EINVAL
+    assert att(base=0.0) == _abi.TRI_EINVAL
+    assert att(ks=2) == _abi.TRI_EINVAL
+    assert att(kv=_kv(v=None)) == _abi.TRI_EINVAL
+    # 257 x 16 units of 2^20 slots: split 16 ways, about 137 MB of partial states
+    big = _kv(n_layer=257, n_kvh=16, max_len=1 << 20)
+    need = ctypes.c_size_t(0)
+    assert L.tri_decode_attention(ctypes.byref(big), 0, 257, FAKE, FAKE, None, 0, 1e6, 0, 0, 4, FAKE, None,
+                                  ctypes.byref(need), None) == _abi.TRI_OK
+    assert need.value > 8 << 20
+    assert att(kv=big, n_layers=257) == _abi.TRI_EWORKSPACE
+    assert "static scratch" in L.tri_last_error().decode()
