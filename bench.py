@@ -56,11 +56,12 @@ SCORE_SRC = os.path.join(ROOT, "kv_cache_compression_tri_amd", "csrc", "score_ke
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    # The score kernel is bound by the vector ALUs, whose clock ramps up over the first few
-    # hundred milliseconds of sustained load: the defaults time the steady state (300 warmup
-    # passes, then 1000 timed passes: about 0.2 s + 0.65 s on the 32K pass).
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=300)
+    # Defaults: 250 ms of untimed pre-roll passes (--preroll-ms), 10 warmup passes, then 200
+    # timed passes (about 0.12 s on the 32K pass).
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--preroll-ms", type=float, default=250.0,
+                    help="untimed passes for this long (wall ms) before the warmup passes (0 = none)")
     ap.add_argument("--workload", default=None, help="workload name (default: the 32K GQA pass)")
     ap.add_argument("--form", choices=("additive", "multiplicative"), default="additive",
                     help="score form: additive (default) or the phase-only series times the norms")
@@ -73,6 +74,8 @@ def parse():
     ap.add_argument("--cpu-units", type=int, default=0,
                     help="units for the oracle baseline (0 = two per host core, capped at 32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only the headline workload (skip the other stated workloads)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB mebibytes (calibrates HBM counters)")
     return ap.parse_args()
@@ -125,16 +128,45 @@ def _oracle_unit(job):
     return time.perf_counter() - t0, L
 
 
+def host_cpu():
+    """What the host says about its CPU: model string, family / model / stepping, core counts."""
+    info = {"model": platform.processor() or platform.machine(), "logical_cpus": os.cpu_count()}
+    try:
+        info["affinity_cpus"] = len(os.sched_getaffinity(0))
+    except AttributeError:
+        info["affinity_cpus"] = os.cpu_count()
+    fields = {}
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if ":" not in line:
+                    if fields:
+                        break                     # first processor block only
+                    continue
+                k, v = (x.strip() for x in line.split(":", 1))
+                fields.setdefault(k, v)
+    except OSError:
+        pass
+    if fields.get("model name"):
+        info["model"] = fields["model name"]
+    for k in ("vendor_id", "cpu family", "model", "stepping", "cpu MHz", "cache size", "cpu cores", "siblings"):
+        if k in fields:
+            info["cpuinfo_" + k.replace(" ", "_")] = fields[k]
+    return info
+
+
+# Worker processes of the oracle baseline: the host cores this GPU's share of the box gives
+# (16 per GPU); the host may show more.
+ORACLE_WORKERS_MAX = 16
+
+
 def cpu_baseline(name, n_units, key_space="pre", form="additive"):
     os.environ.setdefault("OMP_NUM_THREADS", "1")
     from kv_cache_compression_tri_amd.synth import workloads as W
     import numpy as np
     w = W.WORKLOADS[name]
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))
+    host = host_cpu()
+    cores = max(1, min(host["affinity_cpus"] or 1, ORACLE_WORKERS_MAX))
     if n_units <= 0:
         n_units = min(32, 2 * cores)
     rng = np.random.default_rng(2024)
@@ -150,15 +182,6 @@ def cpu_baseline(name, n_units, key_space="pre", form="additive"):
     keys = sum(r[1] for r in res)
     # rate over the oracle's own work, run on `workers` cores in parallel
     rate = keys / (busy / workers) / 1e9
-    cpu = platform.processor() or platform.machine()
-    try:
-        with open("/proc/cpuinfo") as fh:
-            for line in fh:
-                if line.startswith("model name"):
-                    cpu = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
     hp = W.make_params(w)
     pass_keys = int(np.sum(np.minimum(hp.lengths, w.max_len))) * w.n_layer * w.n_kvh
     return {
@@ -168,10 +191,12 @@ def cpu_baseline(name, n_units, key_space="pre", form="additive"):
         "kind": "oracle",
         "per_core_value": keys / busy / 1e9,
         "full_pass_s": pass_keys / (rate * 1e9),
+        "host": host,
         "sample": (f"{len(jobs)} random units of {name} ({keys} keys; score+select+compact per unit, "
-                   f"float64 numpy, one single-threaded process per core; wall {wall:.1f} s, "
-                   f"oracle time {busy:.1f} core-s) on {cpu}; full_pass_s extrapolates to all "
-                   f"{pass_keys} keys at this rate"),
+                   f"float64 numpy, one single-threaded process per core on {workers} of the host's "
+                   f"{host['logical_cpus']} logical CPUs ({host['affinity_cpus']} in this process's "
+                   f"affinity; 16 per GPU is this GPU's share); wall {wall:.1f} s, oracle time {busy:.1f} "
+                   f"core-s) on {host['model']}; full_pass_s extrapolates to all {pass_keys} keys at this rate"),
     }
 
 
@@ -237,40 +262,24 @@ def consumer(args, w, dw, kv, kept_n, new_len, k_out, v_out, pos_out, reps=20):
             "GBps": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(units are independent, so N GPUs would each run this pass on their share)",
-              file=sys.stderr)
-        return 2
+def measure(args, name, steps, warmup, key_space="pre", form="additive", positions=False, with_consumer=False,
+            preroll_ms=0.0):
+    """Build workload `name` in HBM, run untimed passes for preroll_ms of wall time, then
+    `warmup` untimed passes, then time exactly `steps` passes; returns the measurements (the
+    workload is freed before returning)."""
     import torch
-    if args.copy_probe:
-        moved, gbs = copy_bandwidth(args.copy_probe)
-        print(json.dumps({"copy_probe_bytes_read": moved // 2, "copy_probe_bytes_written": moved // 2,
-                          "copy_GBps": gbs}), flush=True)
-        return 0
     import kv_cache_compression_tri_amd as tri
     from kv_cache_compression_tri_amd.synth import device as SD
     from kv_cache_compression_tri_amd.synth import workloads as W
 
-    name = args.workload or W.BENCH_WORKLOAD
-    if name not in W.WORKLOADS:
-        print(f"unknown workload {name!r}; choose from {sorted(W.WORKLOADS)}", file=sys.stderr)
-        return 2
     w = W.WORKLOADS[name]
-    if not torch.cuda.is_available():
-        print("no GPU visible", file=sys.stderr)
-        return 1
-    torch.cuda.set_device(0)
     dw = SD.build(w)
     kv = dw.kv()
-    if args.positions:   # explicit positions (equal to the slot index, so the scores are unchanged)
+    if positions:   # explicit positions (equal to the slot index, so the scores are unchanged)
         n_slots = kv.slots
         kv.pos = torch.arange(n_slots, dtype=torch.int32, device=dw.k.device).expand(
             w.n_seq, w.n_layer, w.n_kvh, n_slots).contiguous()
     dev = dw.k.device
-    units = w.n_units
     lengths = [int(x) for x in dw.hp.lengths]
     keys_per_step = sum(lengths) * w.n_layer * w.n_kvh
     slots = kv.slots
@@ -295,8 +304,8 @@ def main():
         if ev is not None and ev[0] is not None:
             ev[0].record()
         tri.tri_score_keys(kv, dw.center, dw.mean_abs, rope_base=w.base, offsets=w.offsets, group=w.group,
-                           reduce=w.reduce, rope_layout=w.layout, scores=scores, key_space=args.key_space,
-                           form=args.form)
+                           reduce=w.reduce, rope_layout=w.layout, scores=scores, key_space=key_space,
+                           form=form)
         if ev is not None and ev[1] is not None:
             ev[1].record()
         tri.tri_select_topb(scores, kv, w.budget, w.window, kept=kept, kept_n=kept_n)
@@ -313,41 +322,56 @@ def main():
         if w.paged:
             SD.fill(w, dw.hp, dw.k, dw.v, dw.seq_len, dw.block_table)
 
-    for _ in range(args.warmup):
+    preroll = {"ms": 0.0, "passes": 0}
+    if preroll_ms > 0:
+        # Untimed clock pre-roll: under sustained load the GPU's clock first dips (the score
+        # kernel runs ~495 us for the first passes, ~575 us around passes 5-10, and settles near
+        # 470-480 us after ~40 passes of the 32K pass); passes run back to back until preroll_ms
+        # of wall time has passed, so that the timed passes see the steady state of a serving loop.
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < preroll_ms:
+            for _ in range(8):
+                regenerate()
+                step()
+                preroll["passes"] += 1
+            torch.cuda.synchronize()
+        preroll["ms"] = (time.perf_counter() - t0) * 1e3
+    for _ in range(warmup):
         regenerate()
         step()
     torch.cuda.synchronize()
     # Timed loop: the steps run back to back; the only events inside it bracket the score
     # kernel (its average launch duration for the roofline) and the whole loop.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] + [None, None] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] + [None, None] for _ in range(steps)]
     loop_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     if w.paged:
         ms_total = 0.0
-        for i in range(args.steps):
+        for i in range(steps):
             regenerate()
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             step(events[i])
             torch.cuda.synchronize()
             ms_total += (time.perf_counter() - t0) * 1e3
-        ms = ms_total / args.steps
+        ms = ms_total / steps
         loop_event_ms = None
     else:
         t0 = time.perf_counter()
         loop_ev[0].record()
-        for i in range(args.steps):
+        for i in range(steps):
             step(events[i])
         loop_ev[1].record()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        ms = (t1 - t0) * 1e3 / args.steps
-        loop_event_ms = loop_ev[0].elapsed_time(loop_ev[1]) / args.steps
-    score_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+        ms = (t1 - t0) * 1e3 / steps
+        loop_event_ms = loop_ev[0].elapsed_time(loop_ev[1]) / steps
+    score_ms = sum(e[0].elapsed_time(e[1]) for e in events) / steps
 
     # Breakdown loop (after the timed region, not part of the value): events between all
     # three kernels of each step, for the selection and compaction times.
-    n_bd = min(args.steps, 10)
+    n_bd = min(steps, 10)
     bd = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_bd)]
     for i in range(n_bd):
         regenerate()
@@ -361,6 +385,76 @@ def main():
     kept_rows = w.n_layer * w.n_kvh * sum(min(w.budget, L) for L in lengths)
     compact_bytes = kept_rows * w.head_dim * elt * 2 * 2 if compacts else 0   # K and V, read + write
     pass_bytes = score_bytes + compact_bytes
+    cons = None
+    if with_consumer and compacts and w.dtype in ("f32", "bf16"):
+        cons = consumer(args, w, dw, kv, kept_n, new_len, k_out, v_out, pos_out)
+    del dw, kv, scores, kept, kept_n, k_out, v_out, pos_out, new_len, freed, n_freed
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {
+        "w": w, "name": name, "steps": steps, "warmup": warmup, "ms": ms, "loop_event_ms": loop_event_ms,
+        "score_ms": score_ms, "select_ms": select_ms, "compact_ms": compact_ms, "step_ms": step_ms, "n_bd": n_bd,
+        "keys_per_step": keys_per_step, "score_bytes": score_bytes, "pass_bytes": pass_bytes,
+        "compacts": compacts, "consumer": cons, "preroll": preroll,
+    }
+
+
+def config_entry(m):
+    """Summary of one workload's measurement for the `configs` object."""
+    w = m["w"]
+    ms = m["ms"]
+    return {
+        "value": m["keys_per_step"] / (ms * 1e-3) / 1e9, "unit": "Gkeys/s", "ms_per_step": ms,
+        "steps": m["steps"], "warmup": m["warmup"],
+        "pass_hbm_frac": m["pass_bytes"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "score_kernel_hbm_frac": m["score_bytes"] / (m["score_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "score_ms": m["score_ms"], "select_ms": m["select_ms"], "compact_ms": m["compact_ms"],
+        "keys_per_step": m["keys_per_step"], "algorithmic_bytes": m["pass_bytes"],
+        "shape": {"n_seq": w.n_seq, "n_layer": w.n_layer, "n_kv_heads": w.n_kvh, "group": w.group,
+                  "context": w.max_len, "kv_dtype": w.dtype, "budget": w.budget, "window": w.window,
+                  "reduce": w.reduce, "layout": "paged" if w.paged else "dense"},
+    }
+
+
+# The pages' end-to-end figures at 32K-token generation: context only, never a target (they
+# need trained models and a serving stack; the pages do not state their hardware).
+PAGES_CONTEXT = {
+    "decode_throughput_vs_full_attention": 2.5,
+    "kv_memory_reduction": 10.7,
+    "setting": "32K-token generation, KV budget 3072, AIME25; hardware not stated on the pages "
+               "(a 24 GB RTX 4090 deployment is described); not comparable with this pass",
+}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(units are independent, so N GPUs would each run this pass on their share)",
+              file=sys.stderr)
+        return 2
+    import torch
+    if args.copy_probe:
+        moved, gbs = copy_bandwidth(args.copy_probe)
+        print(json.dumps({"copy_probe_bytes_read": moved // 2, "copy_probe_bytes_written": moved // 2,
+                          "copy_GBps": gbs}), flush=True)
+        return 0
+    from kv_cache_compression_tri_amd.synth import workloads as W
+
+    name = args.workload or W.BENCH_WORKLOAD
+    if name not in W.WORKLOADS:
+        print(f"unknown workload {name!r}; choose from {sorted(W.WORKLOADS)}", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    m = measure(args, name, args.steps, args.warmup, args.key_space, args.form, args.positions, args.consumer,
+                args.preroll_ms)
+    w = m["w"]
+    ms, score_ms = m["ms"], m["score_ms"]
+    keys_per_step, score_bytes, pass_bytes = m["keys_per_step"], m["score_bytes"], m["pass_bytes"]
+    step_ms = m["step_ms"]
     achieved = score_bytes / (score_ms * 1e-3) / 1e9
     lane_ops = score_lane_ops_per_key(1 if w.reduce == "mean" else w.group, args.key_space, args.form)
     alu_achieved = lane_ops * keys_per_step / (score_ms * 1e-3) / 1e12
@@ -380,12 +474,15 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
+        "clock_preroll": {"ms": m["preroll"]["ms"], "passes": m["preroll"]["passes"], "timed": False,
+                          "why": "untimed passes before the warmup so that the timed passes run at the "
+                                 "steady clock of sustained load (the clock dips over the first ~25 ms)"},
         "config": {
             "workload": name,
             "n_seq": w.n_seq, "n_layer": w.n_layer, "n_kv_heads": w.n_kvh, "group": w.group,
             "context": w.max_len, "head_dim": w.head_dim, "kv_dtype": w.dtype, "budget": w.budget,
             "window": w.window, "offsets": len(w.offsets), "reduce": w.reduce,
-            "layout": "paged" if w.paged else "dense", "compaction": compacts, "key_space": args.key_space,
+            "layout": "paged" if w.paged else "dense", "compaction": m["compacts"], "key_space": args.key_space,
             "form": args.form, "explicit_positions": bool(args.positions),
             "keys_per_step": keys_per_step, "parallelism": "single GPU",
         },
@@ -417,24 +514,35 @@ def main():
         "pass": {
             "algorithmic_bytes": pass_bytes,
             "hbm_frac": pass_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "score_ms": score_ms, "select_ms": select_ms, "compact_ms": compact_ms,
-            "loop_event_ms_per_step": loop_event_ms,
-            "breakdown_steps": n_bd,
+            "score_ms": score_ms, "select_ms": m["select_ms"], "compact_ms": m["compact_ms"],
+            "loop_event_ms_per_step": m["loop_event_ms"],
+            "breakdown_steps": m["n_bd"],
             "step_event_ms": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0],
                               "p90": step_ms[min(len(step_ms) - 1, int(0.9 * len(step_ms)))]},
             "algorithmic_GBps": pass_bytes / (ms * 1e-3) / 1e9,
         },
     }
-    cons = None
-    if args.consumer and compacts and w.dtype in ("f32", "bf16"):
-        cons = consumer(args, w, dw, kv, kept_n, new_len, k_out, v_out, pos_out)
-    del dw, kv, scores, kept, kept_n, k_out, v_out, pos_out, new_len, freed, n_freed
-    torch.cuda.empty_cache()
+    if m["consumer"] is not None:
+        line["consumer"] = m["consumer"]
+    # The other stated workloads, each timed in this run after the headline (same protocol:
+    # untimed warmup passes, then exactly the given number of timed passes; the paged pools are
+    # refilled before every pass, outside the timed region).  Their pass counts are capped so
+    # that the default run stays within a few minutes.
+    if not args.workload and not args.no_configs and args.key_space == "pre" and args.form == "additive" \
+            and not args.positions:
+        configs = {}
+        for other in W.STATED_WORKLOADS:
+            if other == name:
+                continue
+            paged = W.WORKLOADS[other].paged
+            k = min(args.steps, 20 if paged else 200)
+            wu = min(args.warmup, 5 if paged else 50)
+            configs[other] = config_entry(measure(args, other, max(k, 1), wu))
+        line["configs"] = configs
     _, copy_gbs = copy_bandwidth(1024)
     line["pass"]["copy_GBps"] = copy_gbs
     line["pass"]["frac_of_copy"] = pass_bytes / (ms * 1e-3) / 1e9 / copy_gbs
-    if cons is not None:
-        line["consumer"] = cons
+    line["context_from_pages"] = PAGES_CONTEXT
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(name, args.cpu_units, args.key_space, args.form)
     print(json.dumps(line), flush=True)
