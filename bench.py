@@ -50,7 +50,18 @@ def score_lane_ops_per_key(group_eff: int, key_space: str, form: str) -> int:
     return 64 * (rot + 3 + 3 * group_eff)
 METRIC = "Gkeys/s scored+selected+compacted at 32K ctx; % of HBM roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic.json")
-SCORE_SRC = os.path.join(ROOT, "kv_cache_compression_tri_amd", "csrc", "score_kernel.h")
+# the scoring kernels' sources (the matrix-core kernel includes the vector kernel's header); the
+# recorded traffic holds for the digest of both
+SCORE_SRCS = [os.path.join(ROOT, "kv_cache_compression_tri_amd", "csrc", f) for f in ("score_kernel.h", "score_mx.h")]
+
+
+def score_kernel_used(w, key_space: str, form: str, positions: bool) -> str:
+    """The scoring kernel the library launches for this pass: bfloat16 keys before RoPE at
+    consecutive positions, additive form, max over 4..8 heads take the matrix-core kernel."""
+    if (w.dtype == "bf16" and key_space == "pre" and form == "additive" and not positions and
+            w.reduce == "max" and 4 <= w.group <= 8):
+        return "score_mx_kernel"
+    return "score_kernel"
 
 
 def parse():
@@ -212,12 +223,15 @@ def recorded_traffic(name):
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)
-        with open(SCORE_SRC, "rb") as fh:
-            digest = hashlib.sha256(fh.read()).hexdigest()
+        h = hashlib.sha256()
+        for src in SCORE_SRCS:
+            with open(src, "rb") as fh:
+                h.update(fh.read())
+        digest = h.hexdigest()
     except (OSError, ValueError):
         return None
     entry = rec.get(name)
-    if not entry or entry.get("score_kernel_sha256") != digest:
+    if not entry or entry.get("score_sources_sha256") != digest:
         return None
     return entry.get("bytes_per_launch")
 
@@ -409,6 +423,7 @@ def config_entry(m):
         "pass_hbm_frac": m["pass_bytes"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "score_kernel_hbm_frac": m["score_bytes"] / (m["score_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "score_ms": m["score_ms"], "select_ms": m["select_ms"], "compact_ms": m["compact_ms"],
+        "score_kernel": score_kernel_used(w, "pre", "additive", False),
         "keys_per_step": m["keys_per_step"], "algorithmic_bytes": m["pass_bytes"],
         "shape": {"n_seq": w.n_seq, "n_layer": w.n_layer, "n_kv_heads": w.n_kvh, "group": w.group,
                   "context": w.max_len, "kv_dtype": w.dtype, "budget": w.budget, "window": w.window,
@@ -461,6 +476,7 @@ def main():
     value = keys_per_step / (ms * 1e-3) / 1e9
     traffic = recorded_traffic(name) if (args.key_space == "pre" and args.form == "additive"
                                          and not args.positions) else None
+    kernel = score_kernel_used(w, args.key_space, args.form, args.positions)
     line = {
         "metric": METRIC,
         "value": value,
@@ -488,7 +504,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "score_kernel",
+            "kernel": kernel,
             "achieved": achieved,
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
@@ -499,12 +515,10 @@ def main():
         },
         "alu": {
             "bound": "alu",
-            "kernel": "score_kernel",
-            # bf16 keys before RoPE, additive, max over >= 6 heads: the head contraction runs on the
-            # bf16 matrix cores, so this vector-ALU figure then counts work the VALUs do not do
-            "head_contraction": ("mfma_bf16" if (w.dtype == "bf16" and args.key_space == "pre" and
-                                                 args.form == "additive" and not args.positions and
-                                                 w.reduce == "max" and w.group >= 6) else "valu"),
+            "kernel": kernel,
+            # on the matrix-core kernel the head contraction runs on the bf16 matrix cores, so this
+            # vector-ALU figure then counts work the VALUs do not do
+            "head_contraction": "mfma_bf16" if kernel == "score_mx_kernel" else "valu",
             "lane_ops_per_key": lane_ops,
             "achieved": alu_achieved,
             "peak": PEAK_VALU_TLANEOPS,

@@ -304,11 +304,14 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
     Frag<DT> ring[PF];
     const int32_t* kpos = XP ? P.pos + unit * P.score_stride : nullptr;
     int32_t pring[XP ? PF : 1];   // XP: position of the lane's key, fetched with the key
+    // Loads of step n into ring slot sl.  They are issued whatever n is (past the segment's last
+    // step the range is empty: the loads return zeros and touch no memory), so that a ring
+    // register never merges with an older value under a branch; such a merge makes the compiler
+    // wait for every load in flight instead of the one step it needs.
     auto load_step = [&](int n, int sl) __attribute__((always_inline)) {
-      if (n >= n_steps) return;
       Frag<DT>& fr = ring[sl];
-      const int key0 = p0 + 8 * n;
-      if constexpr (XP) pring[sl] = (key0 + kk < p0 + nkeys) ? kpos[key0 + kk] : 0;
+      const int key0 = p0 + 8 * min(n, n_steps - 1);
+      if constexpr (XP) pring[sl] = (n < n_steps && key0 + kk < p0 + nkeys) ? kpos[key0 + kk] : 0;
       const char* base;
       if constexpr (PAGED) {
         const int32_t page = pg_next;
@@ -317,8 +320,10 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
       } else {
         base = kbase + (unit * P.max_len + key0) * ROW;
       }
+      const int rem = nkeys - 8 * n;
+      const int rows = __builtin_amdgcn_readfirstlane(n < n_steps ? (rem < 8 ? rem : 8) : 0);
       const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, min(8, nkeys - 8 * n) * ROW, 0x00020000);
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, rows * ROW, 0x00020000);
       if constexpr (B8 && !IL) {
         const uint2 re = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off[0], 0, kStreamPolicy));
         const uint2 im = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off[1], 0, kStreamPolicy));
@@ -479,8 +484,10 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
     float* out = P.scores + unit * P.score_stride + p0;
     const int lane_key = 8 * g + kk;   // key this lane stores within a group of 8 steps
     float keep = 0.0f;
-    int n = 0;
-    for (int c = 0; n < n_steps; ++c) {
+    // n0: first step of the current chunk; steps n0 + it >= n_steps of the last chunk compute
+    // nothing, but still issue their (empty) loads
+    for (int n0 = 0; n0 < n_steps; n0 += STEPS) {
+      const int c = n0 / STEPS;
       // The table is read-only, so its per-step reads are invariant across chunks; an opaque
       // base keeps them inside their step instead of being hoisted (and held in registers)
       // for all steps of the chunk.
@@ -500,12 +507,14 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
       }
 #pragma unroll
       for (int it = 0; it < STEPS; ++it) {
-        if (n < n_steps) {
+        const int n = n0 + it;
+        const bool live = n < n_steps;     // wave-uniform
+        float acc[GE];
+        float k2sum = 0.0f;   // multiplicative form: sum_f |k_f|^2 of the lane's bands
+        if (live) {
           Frag<DT>& cur = ring[it % PF];
-          float acc[GE];
 #pragma unroll
           for (int hh = 0; hh < GE; ++hh) acc[hh] = 0.0f;
-          float k2sum = 0.0f;   // multiplicative form: sum_f |k_f|^2 of the lane's bands
           if constexpr (POST) {
 #pragma unroll
             for (int b = 0; b < 8; ++b) {
@@ -568,8 +577,10 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
             }
           }
           }
-          // the slot is free again: fetch the step PF ahead into it
-          load_step(n + PF, it % PF);
+        }
+        // the slot is free again: fetch the step PF ahead into it
+        load_step(n + PF, it % PF);
+        if (live) {
           float sc = sum8(acc[0]);
 #pragma unroll
           for (int hh = 1; hh < GE; ++hh) sc = fmaxf(sc, sum8(acc[hh]));
@@ -581,10 +592,9 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
             // the scores are written once here and read once by the selection pass
             if (g <= (n & 7) && key < nkeys) __builtin_nontemporal_store(keep, out + key);
           }
-          ++n;
-          // keep each step's table reads and arithmetic inside its own step
-          __builtin_amdgcn_sched_barrier(0);
         }
+        // keep each step's table reads and arithmetic inside its own step
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   });

@@ -1,0 +1,389 @@
+// Key scoring with the head contraction on the bf16 matrix cores, weights as the row operand
+// (gfx950): bfloat16 keys before RoPE at consecutive positions, additive form, max over a group
+// of G query heads.
+//
+// It computes what the vector kernel in score_kernel.h computes (the same exact rewrite:
+// s_h(j) = sum_f Re(W_hf x_f) + N_hf |k_f|, x_f = e^{-i r theta_f} conj(k_f); "TriAttention:
+// Trigonometric KV Compression for Efficient Long Reasoning", sections "Core Mechanism" and "Key
+// Concepts", and the norm term of "TriAttention: How a Geometric Trick Cuts LLM Memory Use by 10x
+// Without Losing Accuracy", section "The Core Idea: Q/K Concentration in Pre-RoPE Space").
+// Per key the three real features of each band (Re x_f, Im x_f, |k_f|) are formed in float32 on
+// the vector ALUs; the contraction with the heads' weights is a 16-row x 16-key x 384 product on
+// v_mfma_f32_16x16x32_bf16 with an exact two-part split of both factors:
+//   - a feature x is x_hi + x_lo, x_hi = x with its low 16 bits cleared (a bfloat16), x_lo =
+//     x - x_hi rounded to the nearest bfloat16 (together 16 significand bits, relative error
+//     below 2^-16); a weight w is split the same way;
+//   - row 2h of the weight operand holds head h's w_hi, row 2h + 1 its w_lo (heads >= G are 0);
+//   - each group of 8 features is multiplied twice, with x_hi and with x_lo as the key operand,
+//     into one float32 accumulator, so rows 2h and 2h + 1 sum to (w_hi + w_lo)(x_hi + x_lo) up
+//     to the w_lo x_lo term (relative 2^-16 of the product).
+// The bf16 matrix cores run beside the vector ALUs when a wave interleaves its products with its
+// vector work (about 30 vector instructions per product hide it); a wave issues the two products
+// of each feature group as soon as that group is packed, and reduces a step's accumulator only
+// during the next step.
+//
+// Mapping: a wave step is 16 keys.  Lane l holds key m = l % 16 and bands 8q..8q+7 and
+// 32+8q..32+8q+7 (q = l / 16), four 16-byte pieces of the key's row; in the product it supplies column m
+// of the key operand (its own features, as 8 values of the k-range of lane group q) and row m of
+// the weight operand (the same bands' weights of head m / 2, part m % 2), and receives rows
+// 4q..4q+3 of column m: both parts of heads 2q and 2q + 1 of key m.  So the sum of the parts and
+// the max over a lane's two heads stay in the lane; the max over the lane groups is two swap
+// butterflies across rows of 16 and 32 lanes (v_permlane16_swap, v_permlane32_swap).  Scores of 4
+// steps are gathered so that each lane stores one of 64 consecutive keys.
+//
+// Key stream: in that layout 16 consecutive lanes hold 16 different keys, so loading it directly
+// would make every group of consecutive lanes read 16 bytes of 16 different rows.  Instead the
+// wave reads each step's 16 rows whole (16 consecutive lanes per 256-byte row, a plain streaming
+// pattern), two steps ahead, writes them to its own staging area in LDS and reads them back in
+// the product layout one step ahead of their use.  In the staging area 16-byte piece p of row r
+// sits in slot 16 r + (p xor r): the 16 lanes writing one row and the 16 lanes reading one piece
+// of 16 rows both hit 16 distinct slots modulo 16, so neither access has bank conflicts.  The
+// phase table, anchors, chunk re-anchoring and work division follow score_kernel.h; this kernel's
+// chunk is 224 offsets (14 steps), so that the table (112 KB) and the eight waves' staging rows
+// (32 KB) share the CU's 160 KB of LDS.
+#pragma once
+#include "score_kernel.h"   // for_each_segment, uniform64, kStreamPolicy
+
+namespace tri {
+namespace {
+
+typedef __bf16 mx_bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 mx_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float mx_f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t mx_u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMxKeys = 16;                 // keys per wave step
+constexpr int kMxSteps = 14;                // wave steps per chunk
+constexpr int kMxChunk = kMxSteps * kMxKeys;   // phase-table offsets (224)
+constexpr int kMxRow16 = 16;                // 16-byte slots per staged key row
+constexpr int kMxFeat = 48;                 // features per lane: 16 bands x (Re x, Im x, |k|)
+constexpr int kMxProducts = kMxFeat / 8;    // 16x16x32 products per operand part
+
+// band of local band j (0..15) of lane group q (0..3)
+__device__ __forceinline__ int mx_band(int q, int j) { return j < 8 ? 8 * q + j : 24 + 8 * q + j; }
+
+// float2 index of the phase table entry (r, f), r < kMxChunk: the 64 lanes of step r / 16 read
+// 64 consecutive 16-byte slots per instruction (instruction jj: the lane's local bands 2jj and
+// 2jj + 1)
+__device__ __forceinline__ int mx_tab_index(int r, int f) {
+  const int q = (f & 31) >> 3, j = (f & 7) + (f >= 32 ? 8 : 0);
+  const int it = r >> 4, m = r & 15;
+  return (((it * 8 + (j >> 1)) * 64) + m + 16 * q) * 2 + (j & 1);
+}
+
+// high part of x (low 16 bits cleared) as a float
+__device__ __forceinline__ float mx_hi(float x) { return __uint_as_float(__float_as_uint(x) & 0xFFFF0000u); }
+// packed bfloat16 pair: high parts of x0, x1 (one byte permute) / nearest of y0, y1
+__device__ __forceinline__ uint32_t mx_pack_hi(float x0, float x1) {
+  return __builtin_amdgcn_perm(__float_as_uint(x1), __float_as_uint(x0), 0x07060302u);
+}
+__device__ __forceinline__ uint32_t mx_pack_rne(float y0, float y1) {
+  const mx_bf16x2 v = {(__bf16)y0, (__bf16)y1};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// max with the lane 16 (permlane16) or 32 (permlane32) rows away: the swap of a value with
+// itself leaves the partner's value in one of the two results, the own value in the other
+__device__ __forceinline__ float mx_max_x16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float mx_max_x32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// The two operand parts of 8 features x[0..7]: high parts by truncation (one byte permute per
+// pair), remainders x - high (exact) rounded to the nearest bfloat16.
+__device__ __forceinline__ void mx_split8(const float (&x)[8], mx_u32x4& bh, mx_u32x4& bl) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float x0 = x[2 * e], x1 = x[2 * e + 1];
+    bh[e] = mx_pack_hi(x0, x1);
+    bl[e] = mx_pack_rne(x0 - mx_hi(x0), x1 - mx_hi(x1));
+  }
+}
+
+template <int G, bool IL, bool PAGED>
+__global__ __launch_bounds__(kScoreWaves * 64) void score_mx_kernel(const ScoreParams P) {
+  constexpr int NW = kScoreWaves;
+  constexpr int NT = NW * 64;
+  constexpr int STEPS = kMxSteps;               // wave steps per chunk
+  constexpr int PF = 2;                         // steps of loads in flight
+  constexpr int ROW = kHeadDim * 2;
+  static_assert(STEPS % 2 == 0 && STEPS % PF == 0, "chunk geometry");
+  static_assert(G >= 1 && G <= 8, "group");
+
+  __shared__ float4 tab[kMxChunk * kBands / 2];
+  __shared__ float2 stepc[kBands];             // e^{-i kMxChunk theta_f}
+  __shared__ float2 anc[NW][kBands];           // per-wave anchors
+  __shared__ uint4 stage[NW][kMxKeys * kMxRow16];   // per-wave staging rows of one step
+
+  const int tid = threadIdx.x;
+  {  // phase table: float64 recurrence per (band, run of offsets), rounded once
+    constexpr int RL = kMxChunk * kBands / NT;
+    const int f = tid & 63, run = tid >> 6;
+    const double th = P.theta[f];
+    double s1, c1, zr, zi;
+    sincos(-th, &s1, &c1);
+    sincos(-double(run * RL) * th, &zi, &zr);
+    float2* t2 = reinterpret_cast<float2*>(tab);
+    for (int m = 0; m < RL; ++m) {
+      t2[mx_tab_index(run * RL + m, f)] = make_float2(float(zr), float(zi));
+      const double nr = zr * c1 - zi * s1;
+      zi = zr * s1 + zi * c1;
+      zr = nr;
+    }
+    if (tid < kBands) {
+      double ss, cc;
+      sincos(-double(kMxChunk) * th, &ss, &cc);
+      stepc[tid] = make_float2(float(cc), float(ss));
+    }
+  }
+  __syncthreads();
+
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int km = lane & 15;       // key of the step (column), and weight row
+  const int q = lane >> 4;        // lane group: bands 8q..8q+7, 32+8q..32+8q+7
+  const int head = km >> 1;       // head of this lane's weight row
+  const bool lo_row = km & 1;     // the row holds the weights' remainders
+  const bool live_row = head < G;
+  // heads 2q and 2q + 1 of the lane's output rows: -inf drops a head past the group from the max
+  const float mask_a = (2 * q < G) ? 0.0f : -INFINITY;
+  const float mask_b = (2 * q + 1 < G) ? 0.0f : -INFINITY;
+  const int ups = P.n_layer * P.n_kvh;
+  const int n_qh = P.n_kvh * P.group;
+  // whole-row loads: load i, lane l reads 16-byte piece l % 16 of row 4i + l / 16
+  const int ld_p = lane & 15, ld_r = lane >> 4;
+  uint32_t off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) off[i] = (4 * i + ld_r) * ROW + 16 * ld_p;
+  // staging slots (16-byte units, piece p of row r at 16 r + (p xor r)) of the loaded pieces, and
+  // of the pieces this lane reads back: half split: pieces q, 4 + q, 8 + q, 12 + q of row km (re of
+  // bands 8q.., re of 32+8q.., im, im); interleaved: pieces 2q, 2q + 1, 8 + 2q, 9 + 2q
+  uint4* const st = stage[wave];
+  int st_w[4], st_r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * i + ld_r;
+    st_w[i] = r * kMxRow16 + (ld_p ^ r);
+    const int pc = IL ? (i < 2 ? 2 * q + i : 8 + 2 * q + (i - 2)) : 4 * i + q;
+    st_r[i] = km * kMxRow16 + (pc ^ km);
+  }
+  const int64_t n_waves = int64_t(gridDim.x) * NW;
+  const int64_t w_id = int64_t(blockIdx.x) * NW + wave;
+  for_each_segment<kMxKeys>(P, lane, w_id, n_waves, [&](const int s, const int u_in, const int st0,
+                                                        const int n_steps) __attribute__((always_inline)) {
+    const int64_t unit = int64_t(s) * ups + u_in;
+    const int l = u_in / P.n_kvh;
+    const int h = u_in - l * P.n_kvh;
+    const int L = min(max(P.seq_len[s], 0), int(P.score_stride));
+    const int p0 = kMxKeys * st0;                 // a multiple of 16: one page per step
+    const int nkeys = min(L - p0, kMxKeys * n_steps);
+    const int64_t Q = P.query_pos ? P.query_pos[s] : int64_t(L) - 1;
+
+    // ---- key stream ------------------------------------------------------------------
+    const char* kbase = static_cast<const char*>(P.k);
+    typedef __attribute__((address_space(4))) const int32_t* mx_const_i32_ptr;
+    const mx_const_i32_ptr bt = PAGED ? (mx_const_i32_ptr)(P.block_table + int64_t(s) * P.max_pages) : nullptr;
+    const uint64_t pg_bytes = uint64_t(P.n_layer) * uint64_t(P.n_kvh) * uint64_t(kPage * ROW);
+    const char* ubase = kbase + (int64_t(l) * P.n_kvh + h) * int64_t(kPage * ROW);
+    uint4 ring[PF][4];
+    // Loads of step n into ring slot sl.  They are issued whatever n is (past the segment's last
+    // step the range is empty: the loads return zeros and touch no memory), so that a ring
+    // register never merges with an older value under a branch; such a merge makes the compiler
+    // wait for every load in flight instead of the one step it needs.
+    auto load_step = [&](int n, int sl) __attribute__((always_inline)) {
+      const int nc = min(n, n_steps - 1);                    // a valid page-table entry
+      const int key0 = p0 + kMxKeys * nc;
+      const char* base;
+      if constexpr (PAGED) {
+        base = ubase + uint64_t(uint32_t(bt[key0 >> 4])) * pg_bytes;
+      } else {
+        base = kbase + (unit * P.max_len + key0) * ROW;
+      }
+      const int rem = nkeys - kMxKeys * n;
+      const int rows = __builtin_amdgcn_readfirstlane(n < n_steps ? (rem < kMxKeys ? rem : kMxKeys) : 0);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, rows * ROW, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        ring[sl][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], 0, kStreamPolicy));
+    };
+    // rows of a loaded step into the staging area, and back in the product layout (the wave's own
+    // area: LDS operations of one wave run in order, the fence keeps the compiler's order)
+    auto stage_write = [&](const uint4 (&r)[4]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[st_w[i]] = r[i];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    uint4 cur[4];                                  // the current step's pieces, product layout
+    auto stage_read = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cur[i] = st[st_r[i]];
+    };
+#pragma unroll
+    for (int i = 0; i < PF; ++i) load_step(i, i);
+    stage_write(ring[0]);                           // step 0 into the product layout
+    load_step(PF, 0);
+    stage_read();
+
+    // ---- weights of this lane's row: head `head` of the group (0 beyond G) ----------------
+    // feature order of a lane: Re x_j, Im x_j at 2j, 2j + 1 (products 0..3 take bands 4p..4p+3),
+    // |k_j| at 32 + j (products 4, 5); w[] multiplies the feature at the same index
+    float w[kMxFeat];
+    {
+      const int64_t hrow = int64_t(l) * n_qh + int64_t(h) * P.group + (live_row ? head : 0);
+      const float2* c2 = reinterpret_cast<const float2*>(P.center);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int64_t idx = hrow * kBands + mx_band(q, j);
+        const float2 c = live_row ? c2[idx] : make_float2(0.0f, 0.0f);
+        const float mm = live_row ? P.mean_abs[idx] : 0.0f;
+        w[2 * j] = c.x;
+        w[2 * j + 1] = c.y;
+        w[32 + j] = mm;
+      }
+    }
+    {  // anchor of this segment (float64), one band per lane
+      const double ang = double(Q - p0) * P.theta[lane];
+      double sa, ca;
+      sincos(ang, &sa, &ca);
+      const double cr = P.c_re[lane], ci = P.c_im[lane];
+      anc[wave][lane] = make_float2(float(cr * ca - ci * sa), float(cr * sa + ci * ca));
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {   // W = c A, N = m - |c| (a band with m = 0 has no norm term)
+      const float2 A = anc[wave][mx_band(q, j)];
+      const float cx = w[2 * j], cy = w[2 * j + 1], mm = w[32 + j];
+      w[2 * j] = cx * A.x - cy * A.y;
+      w[2 * j + 1] = -(cx * A.y + cy * A.x);
+      w[32 + j] = (mm > 0.0f) ? mm - __builtin_sqrtf(cx * cx + cy * cy) : 0.0f;
+    }
+    // the weight operands: the row's high parts, or its remainders
+    mx_u32x4 am[kMxProducts];
+    auto pack_weights = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int p = 0; p < kMxProducts; ++p)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float w0 = w[8 * p + 2 * e], w1 = w[8 * p + 2 * e + 1];
+          am[p][e] = lo_row ? mx_pack_rne(w0 - mx_hi(w0), w1 - mx_hi(w1)) : mx_pack_hi(w0, w1);
+        }
+    };
+    pack_weights();
+
+    float* out = P.scores + unit * P.score_stride + p0;
+    mx_f32x4 acc[2];
+    float keep = 0.0f;
+    // reduction of step n's accumulator (rows 4q..4q+3 of column km): the score of key km in
+    // every lane of the column; lane group q keeps the score of steps n = q mod 4, and after
+    // the fourth such step each lane stores one of 64 consecutive keys
+    auto finish = [&](const mx_f32x4& c, int n) __attribute__((always_inline)) {
+      const float a = c[0] + c[1] + mask_a;     // head 2q
+      const float b = c[2] + c[3] + mask_b;     // head 2q + 1
+      float t = __builtin_fmaxf(a, b);
+      t = mx_max_x16(t);
+      t = mx_max_x32(t);
+      if ((n & 3) == q) keep = t;
+      if ((n & 3) == 3 || n == n_steps - 1) {
+        const int key = kMxKeys * (n & ~3) + lane;
+        if (q <= (n & 3) && key < nkeys) __builtin_nontemporal_store(keep, out + key);
+      }
+    };
+    // n0: first step of the current chunk; steps n0 + it >= n_steps of the last chunk compute
+    // nothing, but still issue their (empty) loads
+    for (int n0 = 0; n0 < n_steps; n0 += STEPS) {
+      int tz = lane;
+      asm volatile("" : "+v"(tz));
+      if (n0 > 0) {  // next chunk: W <- W e^{-i kMxChunk theta_f}, then new weight operands
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float2 R = stepc[mx_band(q, j)];
+          const float a = w[2 * j], b = w[2 * j + 1];
+          w[2 * j] = fmaf(a, R.x, b * R.y);
+          w[2 * j + 1] = fmaf(b, R.x, -(a * R.y));
+        }
+        pack_weights();
+      }
+#pragma unroll
+      for (int it = 0; it < STEPS; ++it) {
+        const int n = n0 + it;
+        const bool live = n < n_steps;                        // wave-uniform
+        const float4* tp = tab + it * 8 * 64 + tz;
+        mx_f32x4& ac = acc[it & 1];
+        float kabs[16];
+        if (live) {
+          ac = mx_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {            // trig features of bands 4p..4p+3
+            float x[8];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+              const float4 t = tp[(2 * p + jj) * 64];
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                const int j = 4 * p + 2 * jj + e;
+                float a, b;
+                if constexpr (IL) {
+                  const uint32_t wv = word(cur[j >> 2], j & 3);
+                  a = bf16_lo(wv);
+                  b = bf16_hi(wv);
+                } else {
+                  const uint32_t wr = word(cur[j < 8 ? 0 : 1], (j & 7) >> 1);
+                  const uint32_t wi = word(cur[j < 8 ? 2 : 3], (j & 7) >> 1);
+                  a = (j & 1) ? bf16_hi(wr) : bf16_lo(wr);
+                  b = (j & 1) ? bf16_hi(wi) : bf16_lo(wi);
+                }
+                const float tc = e ? t.z : t.x, ts = e ? t.w : t.y;
+                x[4 * jj + 2 * e] = fmaf(tc, a, ts * b);           // Re(e^{-i r theta} conj(k))
+                x[4 * jj + 2 * e + 1] = fmaf(ts, a, -(tc * b));    // Im(...)
+                kabs[j] = __builtin_amdgcn_sqrtf(fmaf(a, a, b * b));
+              }
+            }
+            mx_u32x4 bh, bl;
+            mx_split8(x, bh, bl);
+            ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mx_bf16x8, am[p]),
+                                                          __builtin_bit_cast(mx_bf16x8, bh), ac, 0, 0, 0);
+            ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mx_bf16x8, am[p]),
+                                                          __builtin_bit_cast(mx_bf16x8, bl), ac, 0, 0, 0);
+          }
+        }
+        // the next step: its rows (loaded two steps ago) through the staging area into cur (free
+        // now: this step's features are formed), and its ring slot refilled
+        stage_write(ring[(it + 1) % PF]);
+        load_step(n + 1 + PF, (it + 1) % PF);
+        stage_read();
+        if (live) {
+#pragma unroll
+          for (int p = 4; p < 6; ++p) {            // |k| of bands 8(p - 4)..8(p - 4) + 7
+            mx_u32x4 bh, bl;
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = kabs[8 * (p - 4) + e];
+            mx_split8(x, bh, bl);
+            ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mx_bf16x8, am[p]),
+                                                          __builtin_bit_cast(mx_bf16x8, bh), ac, 0, 0, 0);
+            ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mx_bf16x8, am[p]),
+                                                          __builtin_bit_cast(mx_bf16x8, bl), ac, 0, 0, 0);
+          }
+          if (n > 0) finish(acc[(it & 1) ^ 1], n - 1);   // the previous step's products are done by now
+        }
+      }
+    }
+    if (n_steps > 0) finish(acc[(n_steps - 1) & 1], n_steps - 1);
+  });
+}
+
+template <int G, bool IL, bool PAGED>
+hipError_t launch_mx_case(const ScoreParams& p, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((score_mx_kernel<G, IL, PAGED>), dim3(grid), dim3(kScoreWaves * 64), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace tri

@@ -92,9 +92,11 @@ hipError_t launch_score(const ScoreParams& p, int G_eff, int dtype, bool interle
 hipError_t launch_score_pos(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged, int grid,
                             hipStream_t stream);
 // the matrix-core scoring kernel (bfloat16 keys before RoPE at consecutive positions,
-// additive form, max over 3..8 heads) and the shapes it takes
-bool score_mfma_applies(int G_eff, int dtype, bool post, bool mult, bool positions, bool reduce_mean);
-hipError_t launch_score_mfma(const ScoreParams& p, bool interleaved, bool paged, int grid, hipStream_t stream);
+// additive form, max over 4..8 heads) and the shapes it takes
+bool score_mx_applies(int G_eff, int dtype, bool post, bool mult, bool positions, bool reduce_mean);
+hipError_t launch_score_mx(const ScoreParams& p, int G_eff, bool interleaved, bool paged, int grid,
+                           hipStream_t stream);
+hipError_t launch_score_mx_paged(const ScoreParams& p, int G_eff, bool interleaved, int grid, hipStream_t stream);
 hipError_t launch_score_pos_8bit(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
                                  int grid, hipStream_t stream);
 hipError_t launch_score_mult(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,

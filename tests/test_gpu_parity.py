@@ -140,6 +140,14 @@ SMALL_DENSE = {
     # are not a multiple of its 16-key step, interleaved layout
     "g7_max_interleaved_bf16": (dict(n_seq=2, n_layer=2, n_kvh=1, group=7, layout="interleaved", max_len=2300,
                                      budget=333, window=20), [2300, 1201]),
+    # matrix-core scoring (G >= 4, bfloat16): lengths at its 224-key chunk, 16-key step and
+    # 64-key store-group boundaries, on either side of them
+    "g5_max_half_bf16_chunk_edges": (dict(n_seq=8, n_layer=1, n_kvh=2, group=5, max_len=1100, budget=100,
+                                          window=8), [223, 224, 225, 447, 448, 449, 1100, 1087]),
+    "g8_max_interleaved_bf16_step_edges": (dict(n_seq=8, n_layer=2, n_kvh=1, group=8, layout="interleaved",
+                                                max_len=320, budget=40, window=4), [1, 15, 16, 17, 63, 64, 65, 320]),
+    "g4_max_half_bf16_one_step": (dict(n_seq=3, n_layer=3, n_kvh=2, group=4, max_len=16, budget=9, window=2),
+                                  [16, 2, 9]),
     # empty sequences between non-empty ones: the score grid divides only real keys
     "g4_max_half_bf16_empty_seqs": (dict(n_seq=5, n_layer=2, n_kvh=2, group=4, max_len=2600, budget=300,
                                          window=32), [0, 2600, 0, 0, 1031]),
@@ -475,7 +483,10 @@ def test_full_gqa8b_batch16_16k_bf16():
 def test_full_long_128k_bf16():
     w = W.WORKLOADS["long_128k_bf16"]
     hp = W.make_params(w)
-    units = [0] + _low_r_units(w, hp, 1)
+    rng = np.random.default_rng(103)
+    # every unit spans many waves' shares; unit 0 starts a share, units 1 and the last start in
+    # the middle of one (the wave finishes the previous unit first)
+    units = [0, 1, w.n_units - 1] + _low_r_units(w, hp, 1) + [int(rng.integers(2, w.n_units - 1))]
     _full_dense("long_128k_bf16", units)
 
 
