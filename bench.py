@@ -87,6 +87,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="time only the headline workload (skip the other stated workloads)")
+    ap.add_argument("--fused", action="store_true",
+                    help="score and select in one launch (tri_score_select; dense f32/bf16 pre-RoPE caches of at "
+                         "most 32768 slots, additive form) instead of two; its time is reported as score_ms")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB mebibytes (calibrates HBM counters)")
     return ap.parse_args()
@@ -277,7 +280,7 @@ def consumer(args, w, dw, kv, kept_n, new_len, k_out, v_out, pos_out, reps=20):
 
 
 def measure(args, name, steps, warmup, key_space="pre", form="additive", positions=False, with_consumer=False,
-            preroll_ms=0.0):
+            preroll_ms=0.0, fused=False):
     """Build workload `name` in HBM, run untimed passes for preroll_ms of wall time, then
     `warmup` untimed passes, then time exactly `steps` passes; returns the measurements (the
     workload is freed before returning)."""
@@ -317,12 +320,18 @@ def measure(args, name, steps, warmup, key_space="pre", form="additive", positio
         # the selection and after the compaction (the breakdown loop); None entries are skipped
         if ev is not None and ev[0] is not None:
             ev[0].record()
-        tri.tri_score_keys(kv, dw.center, dw.mean_abs, rope_base=w.base, offsets=w.offsets, group=w.group,
-                           reduce=w.reduce, rope_layout=w.layout, scores=scores, key_space=key_space,
-                           form=form)
+        if fused:   # one launch scores and selects (its time is counted as the score kernel's)
+            tri.tri_score_select(kv, dw.center, dw.mean_abs, w.budget, w.window, rope_base=w.base,
+                                 offsets=w.offsets, group=w.group, reduce=w.reduce, rope_layout=w.layout,
+                                 kept=kept, kept_n=kept_n)
+        else:
+            tri.tri_score_keys(kv, dw.center, dw.mean_abs, rope_base=w.base, offsets=w.offsets, group=w.group,
+                               reduce=w.reduce, rope_layout=w.layout, scores=scores, key_space=key_space,
+                               form=form)
         if ev is not None and ev[1] is not None:
             ev[1].record()
-        tri.tri_select_topb(scores, kv, w.budget, w.window, kept=kept, kept_n=kept_n)
+        if not fused:
+            tri.tri_select_topb(scores, kv, w.budget, w.window, kept=kept, kept_n=kept_n)
         if ev is not None and ev[2] is not None:
             ev[2].record()
         if compacts:
@@ -464,8 +473,11 @@ def main():
         print("no GPU visible", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if args.fused and (args.key_space != "pre" or args.form != "additive" or args.positions):
+        print("--fused takes pre-RoPE keys at their slots in the additive form", file=sys.stderr)
+        return 2
     m = measure(args, name, args.steps, args.warmup, args.key_space, args.form, args.positions, args.consumer,
-                args.preroll_ms)
+                args.preroll_ms, fused=args.fused)
     w = m["w"]
     ms, score_ms = m["ms"], m["score_ms"]
     keys_per_step, score_bytes, pass_bytes = m["keys_per_step"], m["score_bytes"], m["pass_bytes"]
@@ -476,7 +488,7 @@ def main():
     value = keys_per_step / (ms * 1e-3) / 1e9
     traffic = recorded_traffic(name) if (args.key_space == "pre" and args.form == "additive"
                                          and not args.positions) else None
-    kernel = score_kernel_used(w, args.key_space, args.form, args.positions)
+    kernel = "score_select_kernel" if args.fused else score_kernel_used(w, args.key_space, args.form, args.positions)
     line = {
         "metric": METRIC,
         "value": value,
@@ -499,7 +511,7 @@ def main():
             "context": w.max_len, "head_dim": w.head_dim, "kv_dtype": w.dtype, "budget": w.budget,
             "window": w.window, "offsets": len(w.offsets), "reduce": w.reduce,
             "layout": "paged" if w.paged else "dense", "compaction": m["compacts"], "key_space": args.key_space,
-            "form": args.form, "explicit_positions": bool(args.positions),
+            "form": args.form, "explicit_positions": bool(args.positions), "fused_score_select": bool(args.fused),
             "keys_per_step": keys_per_step, "parallelism": "single GPU",
         },
         "roofline": {
@@ -543,7 +555,7 @@ def main():
     # refilled before every pass, outside the timed region).  Their pass counts are capped so
     # that the default run stays within a few minutes.
     if not args.workload and not args.no_configs and args.key_space == "pre" and args.form == "additive" \
-            and not args.positions:
+            and not args.positions and not args.fused:
         configs = {}
         for other in W.STATED_WORKLOADS:
             if other == name:

@@ -212,6 +212,21 @@ int tri_score_keys(const tri_score_cfg *cfg, const float *center, const float *m
 int tri_select_topb(const float *scores, const tri_kv *kv, int32_t budget, int32_t window,
                     int32_t *kept, int32_t *kept_n, void *ws, size_t *ws_bytes, void *stream);
 
+/* Scoring and selection in one launch ([Review] "Core Mechanism": every key is scored and
+ * only the top-scoring ones are kept), one workgroup per unit: the unit's scores stay in
+ * on-chip memory between the two steps instead of going to memory and back.  It computes
+ * exactly what tri_score_keys followed by tri_select_topb compute, for the cases it takes:
+ *   dense caches (kv->layout TRI_DENSE) of TRI_F32 or TRI_BF16 keys before RoPE
+ *   (cfg->key_space TRI_KEYS_PRE_ROPE) at their slot positions (kv->pos NULL), additive
+ *   form, kv->max_len <= 32768; anything else returns TRI_ENOTSUP.
+ * Arguments as for tri_score_keys and tri_select_topb; scores may be NULL (then no score is
+ * written) or, as for tri_score_keys, [n_seq][n_layer][n_kvh][max_len] float32 to receive
+ * them as well.  kept and kept_n as for tri_select_topb.  Needs no workspace. */
+int tri_score_select(const tri_score_cfg *cfg, const float *center, const float *mean_abs,
+                     const tri_kv *kv, const int64_t *query_pos, int32_t budget, int32_t window,
+                     float *scores, int32_t *kept, int32_t *kept_n, void *ws, size_t *ws_bytes,
+                     void *stream);
+
 /* Forward-packing compaction ([DevTo] "Solving the Memory Fragmentation Problem": the
  * survivors are moved into as few blocks as possible so that the emptied tail blocks can
  * be reclaimed).  Row kept[i] of each unit moves to slot i, i < kept_n[s] (bit copy).
@@ -290,7 +305,7 @@ const char *tri_last_error(void);
 /* ABI version of this header: major * 10000 + minor * 100 + patch. */
 int tri_version(void);
 
-#define TRI_VERSION 10700
+#define TRI_VERSION 10800
 
 #ifdef __cplusplus
 }

@@ -26,6 +26,7 @@ __all__ = [
     "tri_calibrate_stats",
     "tri_score_keys",
     "tri_select_topb",
+    "tri_score_select",
     "tri_compact_kv",
     "tri_decode_attention",
     "tri_decode_attention_noalloc",
@@ -263,6 +264,41 @@ def tri_select_topb(scores, kv: KVCache, budget: int, window: int, kept=None, ke
     _shape(kept_n, "kept_n", (kv.n_seq,))
     _abi.check(L.tri_select_topb(_ptr(scores), ctypes.byref(desc), int(budget), int(window), _ptr(kept),
                                  _ptr(kept_n), None, None, _stream(stream)))
+    return kept, kept_n
+
+
+def tri_score_select(kv: KVCache, center, mean_abs, budget: int, window: int, *, rope_base: float,
+                     offsets: Sequence[int], group: int, reduce: str = "max", rope_layout: str = "half",
+                     query_pos=None, scores=None, kept=None, kept_n=None, stream=None):
+    """Scoring and top-B selection in one launch (dense float32 / bfloat16 pre-RoPE caches of at
+    most 32768 slots, additive form); returns (kept, kept_n) as tri_select_topb does.  scores,
+    if given, also receives the scores (as from tri_score_keys); None writes none."""
+    torch = _torch()
+    L = _abi.lib()
+    desc = kv.descriptor()
+    _dev(center, "center", torch.float32)
+    _dev(mean_abs, "mean_abs", torch.float32)
+    _dev(query_pos, "query_pos", torch.int64)
+    _dev(scores, "scores", torch.float32)
+    if kept is None:
+        kept = torch.empty((kv.n_seq, desc.n_layer, desc.n_kvh, budget), dtype=torch.int32, device=kv.k.device)
+    if kept_n is None:
+        kept_n = torch.empty((kv.n_seq,), dtype=torch.int32, device=kv.k.device)
+    _dev(kept, "kept", torch.int32)
+    _dev(kept_n, "kept_n", torch.int32)
+    n_qh = desc.n_kvh * int(group)
+    _shape(center, "center", (desc.n_layer, n_qh, desc.head_dim // 2, 2))
+    _shape(mean_abs, "mean_abs", (desc.n_layer, n_qh, desc.head_dim // 2))
+    _shape(query_pos, "query_pos", (kv.n_seq,))
+    _shape(scores, "scores", (kv.n_seq, desc.n_layer, desc.n_kvh, kv.slots))
+    _shape(kept, "kept", (kv.n_seq, desc.n_layer, desc.n_kvh, int(budget)))
+    _shape(kept_n, "kept_n", (kv.n_seq,))
+    if mean_abs is None:
+        raise ValueError("mean_abs is required (additive form)")
+    cfg, _keep = _score_cfg(rope_base, offsets, group, reduce, rope_layout)
+    _abi.check(L.tri_score_select(ctypes.byref(cfg), _ptr(center), _ptr(mean_abs), ctypes.byref(desc),
+                                  _ptr(query_pos), int(budget), int(window), _ptr(scores), _ptr(kept),
+                                  _ptr(kept_n), None, None, _stream(stream)))
     return kept, kept_n
 
 

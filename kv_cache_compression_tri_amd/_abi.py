@@ -21,6 +21,7 @@ EXPORTED = (
     "tri_calibrate_stats",
     "tri_score_keys",
     "tri_select_topb",
+    "tri_score_select",
     "tri_compact_kv",
     "tri_last_error",
     "tri_version",
@@ -88,6 +89,8 @@ def lib(path: str = LIB_PATH):
                                  c_void_p, c_void_p, POINTER(c_size_t), c_void_p]
     L.tri_select_topb.argtypes = [c_void_p, POINTER(TriKV), c_int32, c_int32, c_void_p, c_void_p,
                                   c_void_p, POINTER(c_size_t), c_void_p]
+    L.tri_score_select.argtypes = [POINTER(TriScoreCfg), c_void_p, c_void_p, POINTER(TriKV), c_void_p, c_int32,
+                                   c_int32, c_void_p, c_void_p, c_void_p, c_void_p, POINTER(c_size_t), c_void_p]
     L.tri_compact_kv.argtypes = [POINTER(TriKV), c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
                                  c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
     L.tri_last_error.argtypes = []
@@ -98,7 +101,8 @@ def lib(path: str = LIB_PATH):
                                        c_void_p]
     L.tri_decode_attention_noalloc.argtypes = [POINTER(TriKV), c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                                c_int64, c_double, c_int32, c_int32, c_int32, c_void_p, c_void_p]
-    for name in ("tri_calibrate_stats", "tri_score_keys", "tri_select_topb", "tri_compact_kv", "tri_version",
+    for name in ("tri_calibrate_stats", "tri_score_keys", "tri_select_topb", "tri_score_select", "tri_compact_kv",
+                 "tri_version",
                  "tri_decode_attention", "tri_decode_attention_noalloc"):
         getattr(L, name).restype = c_int
     _LIB = L

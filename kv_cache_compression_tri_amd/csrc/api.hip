@@ -197,6 +197,91 @@ int static_scratch(void** out) {
 
 }  // namespace
 
+namespace {
+
+// Checks of a scoring configuration and the kernel parameters it gives (shared by
+// tri_score_keys and tri_score_select).  scores may be NULL here; each caller decides.
+int score_setup(const tri_score_cfg* cfg, const float* center, const float* mean_abs, const tri_kv* kv,
+                const int64_t* query_pos, float* scores, tri::ScoreParams& p) {
+  if (!cfg) return fail(TRI_EINVAL, "cfg is NULL");
+  if (int rc = check_kv(kv, true)) return rc;
+  if (!std::isfinite(cfg->rope_base) || cfg->rope_base <= 0.0)
+    return fail(TRI_EINVAL, "rope_base must be finite and > 0");
+  if (cfg->rope_layout != TRI_ROPE_HALF && cfg->rope_layout != TRI_ROPE_INTERLEAVED)
+    return fail(TRI_EINVAL, "unknown rope layout %d", cfg->rope_layout);
+  if (cfg->reduce != TRI_REDUCE_MAX && cfg->reduce != TRI_REDUCE_MEAN)
+    return fail(TRI_EINVAL, "unknown reduce %d", cfg->reduce);
+  if (cfg->key_space != TRI_KEYS_PRE_ROPE && cfg->key_space != TRI_KEYS_POST_ROPE)
+    return fail(TRI_EINVAL, "unknown key space %d", cfg->key_space);
+  if (cfg->form != TRI_SCORE_ADDITIVE && cfg->form != TRI_SCORE_MULTIPLICATIVE)
+    return fail(TRI_EINVAL, "unknown score form %d", cfg->form);
+  const bool mult = cfg->form == TRI_SCORE_MULTIPLICATIVE;
+  if (cfg->group < 1) return fail(TRI_EINVAL, "group must be >= 1");
+  if (cfg->group > tri::kMaxGroup) return fail(TRI_ENOTSUP, "group %d > %d", cfg->group, tri::kMaxGroup);
+  if (cfg->n_offsets < 1 || !cfg->offsets) return fail(TRI_EINVAL, "at least one offset is required");
+  if (cfg->n_offsets > tri::kMaxOffsets)
+    return fail(TRI_ENOTSUP, "%d offsets > %d", cfg->n_offsets, tri::kMaxOffsets);
+  for (int i = 0; i < cfg->n_offsets; ++i)
+    if (cfg->offsets[i] < 0) return fail(TRI_EINVAL, "offsets must be >= 0");
+  if (!center) return fail(TRI_EINVAL, "center must be non-NULL");
+  if (!mean_abs && !mult) return fail(TRI_EINVAL, "mean_abs must be non-NULL for the additive form");
+  // keys at explicit positions: pre-RoPE keys are rotated at them (additive form); keys cached
+  // after RoPE already carry their rotation, so their positions are not needed
+  if (kv->pos && mult && cfg->key_space == TRI_KEYS_PRE_ROPE)
+    return fail(TRI_ENOTSUP, "explicit key positions with the multiplicative form are not supported");
+
+  p = tri::ScoreParams{};
+  // theta_f = base^(-2f/d) and C_f = mean over offsets of e^{i Delta theta_f}, in float64
+  for (int f = 0; f < tri::kBands; ++f) {
+    const double th = std::pow(cfg->rope_base, -2.0 * f / double(tri::kHeadDim));
+    double cr = 0.0, ci = 0.0;
+    for (int i = 0; i < cfg->n_offsets; ++i) {
+      const double a = double(cfg->offsets[i]) * th;
+      cr += std::cos(a);
+      ci += std::sin(a);
+    }
+    p.theta[f] = th;
+    p.c_re[f] = cr / cfg->n_offsets;
+    p.c_im[f] = ci / cfg->n_offsets;
+  }
+  p.k = kv->k;
+  p.seq_len = kv->seq_len;
+  p.query_pos = query_pos;
+  p.block_table = kv->layout == TRI_PAGED ? kv->block_table : nullptr;
+  p.center = center;
+  p.mean_abs = mean_abs;
+  p.k_scale = kv->k_scale;
+  p.pos = cfg->key_space == TRI_KEYS_PRE_ROPE ? kv->pos : nullptr;
+  p.scores = scores;
+  p.max_len = kv->max_len;
+  p.score_stride = slots_of(kv);
+  p.n_layer = kv->n_layer;
+  p.n_kvh = kv->n_kvh;
+  p.group = cfg->group;
+  p.max_pages = kv->max_pages;
+  p.reduce_mean = cfg->reduce == TRI_REDUCE_MEAN;
+  p.n_seq = kv->n_seq;
+  return TRI_OK;
+}
+
+int select_setup(const tri_kv* kv, int32_t budget, int32_t window, int32_t* kept, int32_t* kept_n,
+                 tri::SelectParams& p) {
+  if (budget < 1) return fail(TRI_EINVAL, "budget must be >= 1");
+  if (window < 0) return fail(TRI_EINVAL, "window must be >= 0");
+  if (!kept || !kept_n) return fail(TRI_EINVAL, "kept and kept_n must be non-NULL");
+  p = tri::SelectParams{};
+  p.score_stride = slots_of(kv);
+  p.seq_len = kv->seq_len;
+  p.kept = kept;
+  p.kept_n = kept_n;
+  p.budget = budget;
+  p.window = window;
+  p.units_per_seq = kv->n_layer * kv->n_kvh;
+  return TRI_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* tri_last_error(void) { return g_error.c_str(); }
@@ -297,67 +382,13 @@ int tri_score_keys(const tri_score_cfg* cfg, const float* center, const float* m
                    size_t* ws_bytes, void* stream) {
   try {
     g_error.clear();
-    if (!cfg) return fail(TRI_EINVAL, "cfg is NULL");
-    if (int rc = check_kv(kv, true)) return rc;
-    if (!std::isfinite(cfg->rope_base) || cfg->rope_base <= 0.0)
-      return fail(TRI_EINVAL, "rope_base must be finite and > 0");
-    if (cfg->rope_layout != TRI_ROPE_HALF && cfg->rope_layout != TRI_ROPE_INTERLEAVED)
-      return fail(TRI_EINVAL, "unknown rope layout %d", cfg->rope_layout);
-    if (cfg->reduce != TRI_REDUCE_MAX && cfg->reduce != TRI_REDUCE_MEAN)
-      return fail(TRI_EINVAL, "unknown reduce %d", cfg->reduce);
-    if (cfg->key_space != TRI_KEYS_PRE_ROPE && cfg->key_space != TRI_KEYS_POST_ROPE)
-      return fail(TRI_EINVAL, "unknown key space %d", cfg->key_space);
-    if (cfg->form != TRI_SCORE_ADDITIVE && cfg->form != TRI_SCORE_MULTIPLICATIVE)
-      return fail(TRI_EINVAL, "unknown score form %d", cfg->form);
-    const bool mult = cfg->form == TRI_SCORE_MULTIPLICATIVE;
-    if (cfg->group < 1) return fail(TRI_EINVAL, "group must be >= 1");
-    if (cfg->group > tri::kMaxGroup) return fail(TRI_ENOTSUP, "group %d > %d", cfg->group, tri::kMaxGroup);
-    if (cfg->n_offsets < 1 || !cfg->offsets) return fail(TRI_EINVAL, "at least one offset is required");
-    if (cfg->n_offsets > tri::kMaxOffsets)
-      return fail(TRI_ENOTSUP, "%d offsets > %d", cfg->n_offsets, tri::kMaxOffsets);
-    for (int i = 0; i < cfg->n_offsets; ++i)
-      if (cfg->offsets[i] < 0) return fail(TRI_EINVAL, "offsets must be >= 0");
-    if (!center || !scores) return fail(TRI_EINVAL, "center and scores must be non-NULL");
-    if (!mean_abs && !mult) return fail(TRI_EINVAL, "mean_abs must be non-NULL for the additive form");
-    // keys at explicit positions: pre-RoPE keys are rotated at them (additive form); keys cached
-    // after RoPE already carry their rotation, so their positions are not needed
-    if (kv->pos && mult && cfg->key_space == TRI_KEYS_PRE_ROPE)
-      return fail(TRI_ENOTSUP, "explicit key positions with the multiplicative form are not supported");
+    tri::ScoreParams p;
+    if (int rc = score_setup(cfg, center, mean_abs, kv, query_pos, scores, p)) return rc;
+    if (!scores) return fail(TRI_EINVAL, "scores must be non-NULL");
     if (int rc = workspace(ws, ws_bytes, 0)) return rc > 0 ? TRI_OK : rc;
-
-    tri::ScoreParams p{};
-    // theta_f = base^(-2f/d) and C_f = mean over offsets of e^{i Delta theta_f}, in float64
-    for (int f = 0; f < tri::kBands; ++f) {
-      const double th = std::pow(cfg->rope_base, -2.0 * f / double(tri::kHeadDim));
-      double cr = 0.0, ci = 0.0;
-      for (int i = 0; i < cfg->n_offsets; ++i) {
-        const double a = double(cfg->offsets[i]) * th;
-        cr += std::cos(a);
-        ci += std::sin(a);
-      }
-      p.theta[f] = th;
-      p.c_re[f] = cr / cfg->n_offsets;
-      p.c_im[f] = ci / cfg->n_offsets;
-    }
-    const int64_t slots = slots_of(kv);
+    const bool mult = cfg->form == TRI_SCORE_MULTIPLICATIVE;
+    const int64_t slots = p.score_stride;
     const int64_t units = int64_t(kv->n_seq) * kv->n_layer * kv->n_kvh;
-    p.k = kv->k;
-    p.seq_len = kv->seq_len;
-    p.query_pos = query_pos;
-    p.block_table = kv->layout == TRI_PAGED ? kv->block_table : nullptr;
-    p.center = center;
-    p.mean_abs = mean_abs;
-    p.k_scale = kv->k_scale;
-    p.pos = cfg->key_space == TRI_KEYS_PRE_ROPE ? kv->pos : nullptr;
-    p.scores = scores;
-    p.max_len = kv->max_len;
-    p.score_stride = slots;
-    p.n_layer = kv->n_layer;
-    p.n_kvh = kv->n_kvh;
-    p.group = cfg->group;
-    p.max_pages = kv->max_pages;
-    p.reduce_mean = cfg->reduce == TRI_REDUCE_MEAN;
-    p.n_seq = kv->n_seq;
     // persistent grid: one workgroup per CU builds the 128 KB phase table once; fewer
     // workgroups when there are not kMinWaveSteps steps per wave even at full length
     const int64_t max_steps = units * ((slots + 7) / 8);
@@ -378,24 +409,47 @@ int tri_score_keys(const tri_score_cfg* cfg, const float* center, const float* m
   }
 }
 
+int tri_score_select(const tri_score_cfg* cfg, const float* center, const float* mean_abs, const tri_kv* kv,
+                     const int64_t* query_pos, int32_t budget, int32_t window, float* scores, int32_t* kept,
+                     int32_t* kept_n, void* ws, size_t* ws_bytes, void* stream) {
+  try {
+    g_error.clear();
+    tri::ScoreParams p;
+    tri::SelectParams sp;
+    if (int rc = score_setup(cfg, center, mean_abs, kv, query_pos, scores, p)) return rc;
+    if (int rc = select_setup(kv, budget, window, kept, kept_n, sp)) return rc;
+    if (kv->layout != TRI_DENSE) return fail(TRI_ENOTSUP, "fused scoring and selection takes dense caches only");
+    if (kv->dtype != TRI_F32 && kv->dtype != TRI_BF16)
+      return fail(TRI_ENOTSUP, "fused scoring and selection takes float32 or bfloat16 keys only");
+    if (cfg->key_space != TRI_KEYS_PRE_ROPE || cfg->form != TRI_SCORE_ADDITIVE || kv->pos)
+      return fail(TRI_ENOTSUP, "fused scoring and selection takes pre-RoPE keys at their slots, additive form");
+    if (p.score_stride > tri::kFuseMaxSlots)
+      return fail(TRI_ENOTSUP, "fused scoring and selection holds at most %d slots per unit (max_len %lld)",
+                  tri::kFuseMaxSlots, (long long)p.score_stride);
+    const int64_t units = int64_t(kv->n_seq) * kv->n_layer * kv->n_kvh;
+    if (units > 0x7FFFFFFF) return fail(TRI_ENOTSUP, "grid too large");
+    if (int rc = workspace(ws, ws_bytes, 0)) return rc > 0 ? TRI_OK : rc;
+    if (units == 0) return TRI_OK;
+    const int g_eff = p.reduce_mean ? 1 : cfg->group;
+    (void)hipGetLastError();
+    hipError_t e = tri::launch_score_select(p, sp, g_eff, kv->dtype, cfg->rope_layout == TRI_ROPE_INTERLEAVED,
+                                            units, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TRI_OK : hip_fail(e, "fused score/select launch");
+  } catch (...) {
+    return fail(TRI_EHIP, "unexpected host exception in tri_score_select");
+  }
+}
+
 int tri_select_topb(const float* scores, const tri_kv* kv, int32_t budget, int32_t window,
                     int32_t* kept, int32_t* kept_n, void* ws, size_t* ws_bytes, void* stream) {
   try {
     g_error.clear();
     if (int rc = check_kv(kv, false)) return rc;
-    if (budget < 1) return fail(TRI_EINVAL, "budget must be >= 1");
-    if (window < 0) return fail(TRI_EINVAL, "window must be >= 0");
-    if (!scores || !kept || !kept_n) return fail(TRI_EINVAL, "scores, kept and kept_n must be non-NULL");
+    tri::SelectParams p;
+    if (int rc = select_setup(kv, budget, window, kept, kept_n, p)) return rc;
+    if (!scores) return fail(TRI_EINVAL, "scores, kept and kept_n must be non-NULL");
     if (int rc = workspace(ws, ws_bytes, 0)) return rc > 0 ? TRI_OK : rc;
-    tri::SelectParams p{};
     p.scores = scores;
-    p.score_stride = slots_of(kv);
-    p.seq_len = kv->seq_len;
-    p.kept = kept;
-    p.kept_n = kept_n;
-    p.budget = budget;
-    p.window = window;
-    p.units_per_seq = kv->n_layer * kv->n_kvh;
     const int64_t units = int64_t(kv->n_seq) * p.units_per_seq;
     (void)hipGetLastError();
     hipError_t e = tri::launch_select(p, units, static_cast<hipStream_t>(stream));

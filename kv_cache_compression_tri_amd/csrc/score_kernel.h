@@ -55,6 +55,7 @@
 // no per-key rotation, no phase table and no chunk re-anchoring, and |k'_f| = |k_f|.
 #pragma once
 #include "device_util.h"
+#include "select_core.h"
 #include "tri_internal.h"
 
 namespace tri {
@@ -211,13 +212,35 @@ __device__ __forceinline__ void for_each_segment(const ScoreParams& P, int lane,
   }
 }
 
-template <int GE, int DT, bool IL, bool PAGED, bool POST, bool MULT, bool XP>
-__global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScoreParams P) {
+// Fused scoring and selection (FUSE): one workgroup per unit of at most kFuseMax slots scores
+// the unit into LDS, each wave an equal run of whole 64-key groups, and then selects its top B
+// from there (select_core.h), so the scores never go to memory.  The LDS is the phase table,
+// on a kFuseChunk-offset chunk (32 KB), and the unit's scores (128 KB): the CU's whole 160 KB,
+// so the anchors and the chunk step are kept in registers instead, and the selection lays its
+// histograms over the table and its level-1 copies over the scores once they are in registers.
+constexpr int kFuseMax = kFuseMaxSlots;
+constexpr int kFuseChunk = 64;
+
+// LDS of the scoring kernel besides the phase table.
+template <bool FUSE, int NW>
+struct ScoreSmem {
+  float2 stepc[kBands];        // e^{-i kChunk theta_f}
+  float2 anc[NW][kBands];      // per-wave anchors
+};
+template <int NW>
+struct ScoreSmem<true, NW> {
+  float sc[kFuseMax];          // the unit's scores
+};
+
+template <int GE, int DT, bool IL, bool PAGED, bool POST, bool MULT, bool XP, bool FUSE>
+__device__ __forceinline__ void score_impl(const ScoreParams& P, const SelectParams& SP) {
   // XP: pre-RoPE keys at explicit positions (P.pos): each key is rotated by its own phase,
   // formed like the anchor (float64 turns) and evaluated by v_cos / v_sin; no table
+  static_assert(!FUSE || (!PAGED && !POST && !MULT && !XP && DT <= 1), "fused: dense pre-RoPE additive f32/bf16");
   constexpr int NW = kScoreWaves;
   constexpr int NT = NW * 64;
-  constexpr int STEPS = kChunk / 8;            // 8 keys per wave step
+  constexpr int CH = FUSE ? kFuseChunk : kChunk;   // phase-table offsets
+  constexpr int STEPS = CH / 8;                // 8 keys per wave step
   constexpr int PF = GE <= 4 ? 4 : 2;          // steps of loads in flight
   constexpr int ESZ = DT == 0 ? 4 : (DT == 1 ? 2 : 1);
   constexpr bool B8 = DT >= 2;                 // one byte per element
@@ -225,14 +248,13 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
   static_assert(STEPS % PF == 0 && STEPS % 8 == 0, "chunk geometry");
 
   constexpr bool TABLE = !POST && !XP;          // consecutive positions: LDS phase table
-  __shared__ float4 tab[TABLE ? kChunk * kBands / 2 : 1];
-  __shared__ float2 stepc[kBands];             // e^{-i kChunk theta_f}
-  __shared__ float2 anc[NW][kBands];           // per-wave anchors
+  __shared__ float4 tab[TABLE ? CH * kBands / 2 : 1];
+  __shared__ __attribute__((aligned(16))) ScoreSmem<FUSE, NW> sm;
 
   const int tid = threadIdx.x;
   // ---- phase table: float64 recurrence per (band, run of offsets), rounded once -------
   if constexpr (TABLE) {
-    constexpr int RL = kChunk * kBands / NT;   // offsets per thread
+    constexpr int RL = CH * kBands / NT;       // offsets per thread
     const int f = tid & 63, run = tid >> 6;
     const double th = P.theta[f];
     double s1, c1, zr, zi;
@@ -245,10 +267,12 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
       zi = zr * s1 + zi * c1;
       zr = nr;
     }
-    if (tid < kBands) {
-      double ss, cc;
-      sincos(-double(kChunk) * th, &ss, &cc);
-      stepc[tid] = make_float2(float(cc), float(ss));
+    if constexpr (!FUSE) {
+      if (tid < kBands) {
+        double ss, cc;
+        sincos(-double(CH) * th, &ss, &cc);
+        sm.stepc[tid] = make_float2(float(cc), float(ss));
+      }
     }
   }
   __syncthreads();
@@ -257,6 +281,16 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kk = lane >> 3;   // key of the step
   const int g = lane & 7;     // band group
+  // FUSE: e^{-i CH theta_f} of the lane's 8 bands, in registers: lane f forms band f's (one
+  // float64 sincos per lane) and each lane reads its bands' across lanes
+  float2 sreg[FUSE ? 8 : 1];
+  if constexpr (FUSE) {
+    double ss, cc;
+    sincos(-double(CH) * P.theta[lane], &ss, &cc);
+    const float sx = float(cc), sy = float(ss);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) sreg[b] = make_float2(__shfl(sx, g * 8 + b, 64), __shfl(sy, g * 8 + b, 64));
+  }
   double th_turns[XP ? 8 : 1];   // XP: theta_f / (2 pi) of the lane's bands
   if constexpr (XP) {
 #pragma unroll
@@ -281,8 +315,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
 
   const int64_t n_waves = int64_t(gridDim.x) * NW;
   const int64_t w_id = int64_t(blockIdx.x) * NW + wave;
-  for_each_segment<8>(P, lane, w_id, n_waves, [&](const int s, const int u_in, const int st0, const int seg_steps)
-                                                  __attribute__((always_inline)) {
+  auto body = [&](const int s, const int u_in, const int st0, const int seg_steps) __attribute__((always_inline)) {
     const int64_t unit = int64_t(s) * ups + u_in;
     const int l = u_in / P.n_kvh;
     const int h = u_in - l * P.n_kvh;
@@ -388,14 +421,28 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
       }
     }
 
-    {  // anchor of this segment (float64), one band per lane; after RoPE the anchor is 0
+    // anchor of this segment (float64), one band per lane; after RoPE the anchor is 0.  Each
+    // lane reads its 8 bands' through LDS, or FUSE (no LDS to spare) across lanes
+    float2 areg[FUSE ? 8 : 1];
+    {
       const double ang = double((POST || XP) ? Q : Q - p0) * P.theta[lane];
       double sa, ca;
       sincos(ang, &sa, &ca);
       const double cr = P.c_re[lane], ci = P.c_im[lane];
-      anc[wave][lane] = make_float2(float(cr * ca - ci * sa), float(cr * sa + ci * ca));
+      const float ax = float(cr * ca - ci * sa), ay = float(cr * sa + ci * ca);
+      if constexpr (FUSE) {
+#pragma unroll
+        for (int b = 0; b < 8; ++b) areg[b] = make_float2(__shfl(ax, g * 8 + b, 64), __shfl(ay, g * 8 + b, 64));
+      } else {
+        sm.anc[wave][lane] = make_float2(ax, ay);
+        __builtin_amdgcn_wave_barrier();
+      }
     }
-    __builtin_amdgcn_wave_barrier();
+    // anchor of the lane's band b (0..7)
+    auto anchor = [&](int b) __attribute__((always_inline)) -> float2 {
+      if constexpr (FUSE) return areg[b];
+      else return sm.anc[wave][g * 8 + b];
+    };
 
     if constexpr (MULT) {
       // multiplicative form: the weight of band f is (c_f / |c_f|) ||c|| C_f A_f (a centre
@@ -410,7 +457,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
         const float cn = __builtin_sqrtf(sum8(c2));
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
-          const float2 c = cr[b], A = anc[wave][g * 8 + b];
+          const float2 c = cr[b], A = anchor(b);
           const float m = __builtin_sqrtf(c.x * c.x + c.y * c.y);
           const float sc = m > 0.0f ? cn / m : 0.0f;
           r[b] = sc * (c.x * A.x - c.y * A.y);
@@ -451,8 +498,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
     } else {
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const int f = g * 8 + b;
-      const float2 A = anc[wave][f];
+      const float2 A = anchor(b);
       if (P.reduce_mean) {   // group-mean centre (already averaged) times the anchor
         const float cx = wr[0][b], cy = wn[0][b];
         wr[0][b] = cx * A.x - cy * A.y;
@@ -496,7 +542,9 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
       if (TABLE && c > 0) {  // next chunk: W <- W e^{-i kChunk theta_f}
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
-          const float2 R = stepc[(tz & 7) * 8 + b];
+          float2 R;
+          if constexpr (FUSE) R = sreg[b];
+          else R = sm.stepc[(tz & 7) * 8 + b];
 #pragma unroll
           for (int hh = 0; hh < GE; ++hh) {
             const float a = wr[hh][b], q = wn[hh][b];
@@ -589,15 +637,57 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
           if ((it & 7) == 7 || n == n_steps - 1) {
             // lane (kk, g) holds the score of step (n & ~7) + g, key kk
             const int key = 8 * (n & ~7) + lane_key;
-            // the scores are written once here and read once by the selection pass
-            if (g <= (n & 7) && key < nkeys) __builtin_nontemporal_store(keep, out + key);
+            // the scores are written once here and read once by the selection pass (FUSE: into
+            // LDS, and to memory only if asked for)
+            if (g <= (n & 7) && key < nkeys) {
+              if constexpr (FUSE) {
+                sm.sc[p0 + key] = keep;
+                if (P.scores) __builtin_nontemporal_store(keep, out + key);
+              } else {
+                __builtin_nontemporal_store(keep, out + key);
+              }
+            }
           }
         }
         // keep each step's table reads and arithmetic inside its own step
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-  });
+  };
+  if constexpr (FUSE) {
+    // one unit per workgroup: wave w scores steps [w S, (w + 1) S) of it, S a multiple of 8
+    // (whole 64-key store groups); then the workgroup selects from the scores in LDS
+    const int64_t unit = blockIdx.x;
+    const int s = int(unit / ups), u_in = int(unit - int64_t(s) * ups);
+    const int L = min(max(P.seq_len[s], 0), int(P.score_stride));
+    const int steps = (L + 7) / 8;
+    const int share = (steps + 8 * NW - 1) / (8 * NW) * 8;
+    const int st0 = wave * share;
+    const int n = min(share, steps - st0);
+    if (n > 0) body(s, u_in, st0, n);
+    __syncthreads();
+    // the selection's state over LDS the scoring has finished with: histograms and per-wave
+    // partials over the phase table, level-1 copies over the scores (select_unit reads the
+    // scores into registers and synchronises before it writes those)
+    static_assert(sizeof(tab) >= kLevels * kBins * 4 + sizeof(SelSmall<NW>), "table region too small");
+    static_assert(sizeof(sm) >= kSubHist * kBins * 4, "score region too small");
+    const SelLds<NW> S{reinterpret_cast<uint32_t(*)[kBins]>(tab), reinterpret_cast<uint32_t*>(sm.sc),
+                       reinterpret_cast<SelSmall<NW>*>(reinterpret_cast<char*>(tab) + kLevels * kBins * 4)};
+    select_unit<NT, kFuseMax, false, true>(SP, unit, S, sm.sc);
+  } else {
+    for_each_segment<8>(P, lane, w_id, n_waves, body);
+  }
+}
+
+template <int GE, int DT, bool IL, bool PAGED, bool POST, bool MULT, bool XP>
+__global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScoreParams P) {
+  score_impl<GE, DT, IL, PAGED, POST, MULT, XP, false>(P, SelectParams{});
+}
+
+// scoring and selection of one unit per workgroup (FUSE above)
+template <int GE, int DT, bool IL>
+__global__ __launch_bounds__(kScoreWaves * 64) void score_select_kernel(const ScoreParams P, const SelectParams S) {
+  score_impl<GE, DT, IL, false, false, false, false, true>(P, S);
 }
 
 template <int GE, int DT, bool POST, bool MULT, bool XP>

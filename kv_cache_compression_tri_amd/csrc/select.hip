@@ -1,369 +1,17 @@
-// Top-B selection kernel of the TriAttention compression pass (gfx950).
-//
-// Per unit (one workgroup): keep the last W' = min(window, budget) slots, then the best
-// budget - W' of the remaining candidates ranked by (score descending, slot ascending), and
-// write the kept slots in ascending order ("TriAttention: Trigonometric KV Compression for
-// Efficient Long Reasoning", section "Core Mechanism": only the top-scoring keys are kept;
-// "TriAttention: trigonometric KV cache compression for long reasoning", section "The KV
-// budget is a runtime knob ...": the budget bounds the whole kept cache).
-//
-// Scores map to order-preserving 32-bit keys (NaN and -inf to the lowest candidate key, -0
-// to +0).  Each wave of a 1024-thread workgroup owns a contiguous range of slots, four
-// consecutive slots per lane; a unit of up to 32768 slots is read from memory once into
-// registers (2048 slots per wave), longer units re-read their scores on every sweep.  The threshold is
-// found by refining linear histograms instead of sorting:
-//   level 1: 2048 bins spanning [min, max] of the candidate keys, counted in four copies (lane
-//            l adds into copy l % 4, so lanes of one instruction that hit the same bin mostly
-//            hit different LDS words) and then folded;
-//   level k+1: 2048 sub-bins of the bin that holds the target rank;
-// until either the whole target bin is kept (its lower edge becomes the threshold: keep
-// key >= T) or the bins are single key values (at most three levels, because the key span
-// has 32 bits and each level resolves 11).  In the second case only some of the keys equal
-// to the threshold are kept: the lowest slots among them, found with one more sweep.
-// The ordered write counts the kept slots per wave, turns the counts into offsets, and
-// writes each wave's kept slots in order from ballots (mbcnt ranks), without a sort.
-#include "tri_internal.h"
+// Top-B selection kernel of the TriAttention compression pass (gfx950): one workgroup per
+// unit; the selection itself is in select_core.h.
+#include "select_core.h"
 
 namespace tri {
 namespace {
 
-// Workgroup sizes: a unit that fits in registers (up to kResident slots) uses kResThreads
-// threads holding kResident / kResThreads keys each; longer units stream their scores
-// with kStreamThreads threads.
-constexpr int kResThreads = 1024;
-constexpr int kStreamThreads = 1024;
-constexpr int kVec = 4;                       // consecutive slots per lane in a tile
-constexpr int kTile = 64 * kVec;              // slots per wave tile
-constexpr int kResident = 32768;              // slots a workgroup holds in registers
-constexpr int kBinBits = 11;
-constexpr int kBins = 1 << kBinBits;
-constexpr int kLevels = 3;                    // ceil(32 / kBinBits)
-constexpr int kSubHist = 4;                   // level 1: lane l adds into copy l % 4 (fewer same-bin conflicts)
-constexpr uint32_t kKeyNone = 0u;             // slot outside the wave's range
-constexpr uint32_t kKeyWindow = 0xFFFFFFFFu;  // recent-window slot, always kept
-
-// Candidate keys lie in [0x007FFFFF, 0xFF800000], strictly between the two sentinels.
-__device__ __forceinline__ uint32_t order_key(uint32_t b) {
-  const float x = __uint_as_float(b);
-  if (b == 0x80000000u) b = 0u;                              // -0 ranks as +0
-  const uint32_t k = b ^ (uint32_t(int32_t(b) >> 31) | 0x80000000u);
-  return x != x ? 0x007FFFFFu : k;                           // NaN ranks as -inf
-}
-
-// acc + number of set bits of m in lanes below this one
-__device__ __forceinline__ uint32_t mbcnt(uint64_t m, uint32_t acc) {
-  return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), acc));
-}
-
-// Inclusive prefix sum over the 64 lanes: row shifts inside 16-lane rows, then row
-// broadcasts of lane 15 and lane 31 into the rows above.
-__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
-  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x111, 0xF, 0xF, true));   // row_shr:1
-  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x112, 0xF, 0xF, true));   // row_shr:2
-  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x114, 0xF, 0xF, true));   // row_shr:4
-  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x118, 0xF, 0xF, true));   // row_shr:8
-  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x142, 0xA, 0xF, false));  // row_bcast:15
-  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x143, 0xC, 0xF, false));  // row_bcast:31
-  return v;
-}
-
-__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = min(v, uint32_t(__shfl_xor(int(v), d, 64)));
-  return v;
-}
-
-__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = max(v, uint32_t(__shfl_xor(int(v), d, 64)));
-  return v;
-}
-
-template <int NW>
-struct SelShared {
-  alignas(16) uint32_t hist[kLevels][kBins];
-  alignas(16) uint32_t sub[kSubHist * kBins];   // level 1: copy c (= lane % kSubHist) at c * kBins
-  uint32_t wmin[NW], wmax[NW];
-  uint32_t wties[NW], wkeep[NW];
-  int32_t jstar;
-};
-
-// The bin holding the rank-th largest (1-based) histogram entry, the number of entries in
-// higher bins and in the bin itself.  Every lane of the calling wave gets the same result.
-// Lane l first sums bins [kBins - 32(l+1), kBins - 32l), so lanes ascending walk the bins
-// descending; the 16-byte reads are rotated per lane to spread them over the LDS banks.
-__device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t rank, int lane, uint32_t& tbin,
-                                         uint32_t& above, uint32_t& cnt) {
-  const uint4* hv = reinterpret_cast<const uint4*>(hist + kBins - 32 * (lane + 1));
-  uint32_t lsum = 0;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint4 q = hv[(c + lane) & 7];
-    lsum += (q.x + q.y) + (q.z + q.w);
-  }
-  const uint32_t incl = wave_incl_sum(lsum);
-  const uint64_t hit = __ballot(incl >= rank);
-  const int fl = hit ? __ffsll((unsigned long long)hit) - 1 : 63;
-  const uint32_t abv = uint32_t(__builtin_amdgcn_readlane(int(incl - lsum), fl));
-  const int top = kBins - 1 - 32 * fl;
-  const uint32_t v = lane < 32 ? hist[top - lane] : 0u;
-  const uint32_t incl2 = abv + wave_incl_sum(v);
-  const uint64_t hit2 = __ballot(lane < 32 && incl2 >= rank);
-  const int k = hit2 ? __ffsll((unsigned long long)hit2) - 1 : 31;
-  cnt = uint32_t(__builtin_amdgcn_readlane(int(v), k));
-  above = uint32_t(__builtin_amdgcn_readlane(int(incl2), k)) - cnt;
-  tbin = uint32_t(top - k);
-}
-
 template <bool kStream, int NT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(const SelectParams P) {
-  constexpr int kSelThreads = NT;
-  constexpr int kSelWaves = NT / 64;
-  constexpr int kBatchTiles = kResident / (NT * kVec);   // tiles of keys a wave holds in registers
-  __shared__ SelShared<kSelWaves> sh;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t unit = blockIdx.x;
-  const int s = int(unit / P.units_per_seq);
-  const int L = min(max(P.seq_len[s], 0), int(P.score_stride));
-  const int B = P.budget;
-  const float* sc = P.scores + unit * P.score_stride;
-  int32_t* out = P.kept + unit * int64_t(B);
-
-  if (tid == 0 && unit % P.units_per_seq == 0) P.kept_n[s] = min(L, B);
-  if (L <= B) {
-    for (int i = tid; i < B; i += kSelThreads) out[i] = i < L ? i : -1;
-    return;
-  }
-  const int w = min(P.window, B);
-  const int ncand = L - w;                 // >= 1 because L > B >= w
-  const uint32_t need = uint32_t(B - w);   // candidates to keep
-
-  // this wave's slots [r0, r1), in tiles of 64 lanes x 4 consecutive slots
-  const int per_wave = (L + kSelWaves * kTile - 1) / (kSelWaves * kTile) * kTile;
-  const int r0 = min(L, wave * per_wave), r1 = min(L, r0 + per_wave);
-  const int n_tiles = (r1 - r0 + kTile - 1) / kTile;
-  const int cand_end = min(r1, ncand);
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sc), (short)0, L * 4, 0x00020000);
-
-  uint32_t u[kBatchTiles][kVec];
-  // raw scores of the tiles from t0 into r (no waiting here: the loads stay in flight)
-  auto issue = [&](int t0, uint32_t (&r)[kBatchTiles][kVec]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int t = 0; t < kBatchTiles; ++t) {
-      if (t0 + t < n_tiles) {
-        const int j = r0 + (t0 + t) * kTile + lane * kVec;
-        const uint4 q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, j * 4, 0, 0));
-        r[t][0] = q.x;
-        r[t][1] = q.y;
-        r[t][2] = q.z;
-        r[t][3] = q.w;
-      }
-    }
-  };
-  // scores in u -> order keys, with the window and padding sentinels
-  auto to_keys = [&](int t0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int t = 0; t < kBatchTiles; ++t) {
-      const int jt = r0 + (t0 + t) * kTile;
-      if (t0 + t < n_tiles) {
-        if (jt + kTile <= cand_end) {
-#pragma unroll
-          for (int e = 0; e < kVec; ++e) u[t][e] = order_key(u[t][e]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < kVec; ++e) {
-            const int j = jt + lane * kVec + e;
-            u[t][e] = j >= r1 ? kKeyNone : j >= ncand ? kKeyWindow : order_key(u[t][e]);
-          }
-        }
-      }
-    }
-  };
-  // body(t, jt) runs for every tile of the wave with keys u[t][*] of slots jt + 4*lane + e;
-  // the scheduling barrier keeps the tiles in order so that ballots do not pile up in SGPRs.
-  // Streaming: the next batch's loads are issued into a second buffer before the current
-  // batch is processed, so their latency overlaps the work instead of stalling each batch.
-  auto sweep = [&](auto&& body) __attribute__((always_inline)) {
-    if constexpr (kStream) {
-      uint32_t nxt[kBatchTiles][kVec];
-      issue(0, nxt);
-      for (int t0 = 0; t0 < n_tiles; t0 += kBatchTiles) {
-#pragma unroll
-        for (int t = 0; t < kBatchTiles; ++t)
-#pragma unroll
-          for (int e = 0; e < kVec; ++e) u[t][e] = nxt[t][e];
-        to_keys(t0);
-        if (t0 + kBatchTiles < n_tiles) issue(t0 + kBatchTiles, nxt);
-#pragma unroll
-        for (int t = 0; t < kBatchTiles; ++t) {
-          if (t0 + t < n_tiles) body(t, r0 + (t0 + t) * kTile);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < kBatchTiles; ++t) {
-        if (t < n_tiles) body(t, r0 + t * kTile);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  };
-  if constexpr (!kStream) {
-    issue(0, u);
-    to_keys(0);
-  }
-
-  // kept: key > tau, or key == tau and slot <= jstar (jstar = -1 when all ties at tau are
-  // kept, i.e. the threshold is key >= tau + 1)
-  uint32_t tau = kKeyWindow - 1u;
-  int jstar = -1;
-  bool partial = false;
-  if (need > 0) {
-    // ---- range of the candidate keys (sentinels wrap out of the min and the max) --------
-    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-    sweep([&](int t, int) __attribute__((always_inline)) {
-#pragma unroll
-      for (int e = 0; e < kVec; ++e) {
-        mn = min(mn, u[t][e] - 1u);
-        mx = max(mx, u[t][e] + 1u);
-      }
-    });
-    mn = wave_min(mn);
-    mx = wave_max(mx);
-    if (lane == 0) {
-      sh.wmin[wave] = mn;
-      sh.wmax[wave] = mx;
-    }
-    for (int i = tid; i < kLevels * kBins; i += kSelThreads) (&sh.hist[0][0])[i] = 0u;
-    for (int i = tid; i < kSubHist * kBins; i += kSelThreads) sh.sub[i] = 0u;
-    __syncthreads();
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-#pragma unroll
-    for (int i = 0; i < kSelWaves; ++i) {
-      lo = min(lo, sh.wmin[i]);
-      hi = max(hi, sh.wmax[i]);
-    }
-    lo += 1u;
-    hi -= 1u;
-
-    // ---- histogram refinement ------------------------------------------------------------
-    uint32_t base = lo, span = hi - lo, rank = need;   // in range: key - base <= span
-    const int bitlen = 32 - __clz(int(span));
-    int shift = bitlen > kBinBits ? bitlen - kBinBits : 0;
-    for (int lev = 0; lev < kLevels; ++lev) {
-      uint32_t* hist = sh.hist[lev];
-      if (lev == 0) {
-        const uint32_t copy = uint32_t(lane & (kSubHist - 1)) * kBins;
-        sweep([&](int t, int) __attribute__((always_inline)) {
-#pragma unroll
-          for (int e = 0; e < kVec; ++e) {
-            const uint32_t d = u[t][e] - base;
-            if (d <= span) atomicAdd(&sh.sub[copy + (d >> shift)], 1u);
-          }
-        });
-        __syncthreads();
-        for (int i = tid; i < kBins; i += kSelThreads) {   // fold the copies
-          uint32_t v = 0;
-#pragma unroll
-          for (int c = 0; c < kSubHist; ++c) v += sh.sub[c * kBins + i];
-          hist[i] = v;
-        }
-      } else {
-        sweep([&](int t, int) __attribute__((always_inline)) {
-#pragma unroll
-          for (int e = 0; e < kVec; ++e) {
-            const uint32_t d = u[t][e] - base;
-            if (d <= span) atomicAdd(&hist[d >> shift], 1u);
-          }
-        });
-      }
-      __syncthreads();
-      uint32_t tbin, above, cnt;
-      find_bin(hist, rank, lane, tbin, above, cnt);
-      rank -= above;
-      const uint32_t edge = base + (tbin << shift);
-      if (rank == cnt) {             // the whole bin is kept
-        tau = edge - 1u;
-        break;
-      }
-      if (shift == 0) {              // keys equal to edge: only the first `rank` are kept
-        tau = edge;
-        partial = true;
-        break;
-      }
-      base = edge;
-      span = (1u << shift) - 1u;
-      shift = shift > kBinBits ? shift - kBinBits : 0;
-    }
-
-    if (partial) {
-      // ---- slot of the rank-th key equal to tau, in slot order -------------------------
-      uint32_t ct = 0;
-      sweep([&](int t, int) __attribute__((always_inline)) {
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) ct += uint32_t(__popcll(__ballot(u[t][e] == tau)));
-      });
-      if (lane == 0) sh.wties[wave] = ct;
-      __syncthreads();
-      uint32_t run = 0;
-      for (int i = 0; i < wave; ++i) run += sh.wties[i];
-      if (run < rank && rank <= run + ct) {
-        sweep([&](int t, int jt) __attribute__((always_inline)) {
-          uint64_t m[kVec];
-#pragma unroll
-          for (int e = 0; e < kVec; ++e) m[e] = __ballot(u[t][e] == tau);
-          uint32_t r = run;
-#pragma unroll
-          for (int e = 0; e < kVec; ++e) r = mbcnt(m[e], r);
-#pragma unroll
-          for (int e = 0; e < kVec; ++e) {
-            const bool f = u[t][e] == tau;
-            if (f && r == rank - 1u) sh.jstar = jt + lane * kVec + e;
-            r += f ? 1u : 0u;
-          }
-#pragma unroll
-          for (int e = 0; e < kVec; ++e) run += uint32_t(__popcll(m[e]));
-        });
-      }
-      __syncthreads();
-      jstar = sh.jstar;
-    }
-  }
-
-  // ---- ordered write --------------------------------------------------------------------
-  auto keep = [&](uint32_t k, int j) __attribute__((always_inline)) {
-    return k > tau || (k == tau && j <= jstar);
-  };
-  uint32_t ck = 0;
-  sweep([&](int t, int jt) __attribute__((always_inline)) {
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) ck += uint32_t(__popcll(__ballot(keep(u[t][e], jt + lane * kVec + e))));
-  });
-  if (lane == 0) sh.wkeep[wave] = ck;
-  __syncthreads();
-  uint32_t run = 0;
-  for (int i = 0; i < wave; ++i) run += sh.wkeep[i];
-  sweep([&](int t, int jt) __attribute__((always_inline)) {
-    bool f[kVec];
-    uint64_t m[kVec];
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) {
-      f[e] = keep(u[t][e], jt + lane * kVec + e);
-      m[e] = __ballot(f[e]);
-    }
-    uint32_t r = run;
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) r = mbcnt(m[e], r);
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) {
-      if (f[e] && r < uint32_t(B)) out[r] = jt + lane * kVec + e;
-      r += f[e] ? 1u : 0u;
-    }
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) run += uint32_t(__popcll(m[e]));
-  });
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kLevels][kBins];   // read as 16-byte pieces
+  __shared__ uint32_t sub[kSubHist * kBins];
+  __shared__ SelSmall<NT / 64> sm;
+  const SelLds<NT / 64> S{hist, sub, &sm};
+  select_unit<NT, kResident, kStream, false>(P, blockIdx.x, S, nullptr);
 }
 
 }  // namespace

@@ -337,3 +337,37 @@ def test_decode_attention_noalloc_validation():
     assert need.value > 8 << 20
     assert att(kv=big, n_layers=257) == _abi.TRI_EWORKSPACE
     assert "static scratch" in L.tri_last_error().decode()
+
+
+def test_score_select_validation():
+    # tri.h, tri_score_select: dense float32 / bfloat16 caches of pre-RoPE keys at their slots,
+    # additive form, at most 32768 slots; everything else is refused before any launch.  The
+    # workspace query validates without launching and needs 0 bytes.
+    L = _abi.lib()
+
+    def call(cfg_over=None, kv=None, budget=64, window=8, kept=FAKE, mean_abs=FAKE, scores=None, query=True):
+        cfg, _offs = _cfg(**(cfg_over or {}))
+        kv = kv or _kv()
+        size = ctypes.c_size_t(123)
+        rc = L.tri_score_select(ctypes.byref(cfg), FAKE, mean_abs, ctypes.byref(kv), None, budget, window, scores,
+                                kept, FAKE, None, ctypes.byref(size) if query else None, None)
+        return rc, size.value
+
+    assert call() == (_abi.TRI_OK, 0)
+    assert call(kv=_kv(dtype=_abi.TRI_F32)) == (_abi.TRI_OK, 0)
+    assert call(scores=FAKE) == (_abi.TRI_OK, 0)
+    assert call(kv=_kv(max_len=32768)) == (_abi.TRI_OK, 0)
+    assert call(kv=_kv(max_len=32769))[0] == _abi.TRI_ENOTSUP
+    assert "32768" in L.tri_last_error().decode()
+    assert call(kv=_kv(layout=_abi.TRI_PAGED))[0] == _abi.TRI_ENOTSUP
+    for dt in (_abi.TRI_FP8_E4M3, _abi.TRI_INT8):
+        assert call(kv=_kv(dtype=dt))[0] == _abi.TRI_ENOTSUP
+    assert call(cfg_over=dict(key_space=_abi.TRI_KEYS_POST_ROPE))[0] == _abi.TRI_ENOTSUP
+    assert call(cfg_over=dict(form=_abi.TRI_SCORE_MULTIPLICATIVE))[0] == _abi.TRI_ENOTSUP
+    assert call(kv=_kv(pos=FAKE.value))[0] == _abi.TRI_ENOTSUP
+    assert call(cfg_over=dict(group=9))[0] == _abi.TRI_ENOTSUP
+    assert call(budget=0)[0] == _abi.TRI_EINVAL
+    assert call(window=-1)[0] == _abi.TRI_EINVAL
+    assert call(kept=None)[0] == _abi.TRI_EINVAL
+    assert call(mean_abs=None)[0] == _abi.TRI_EINVAL
+    assert call(query=False, kv=_kv(layout=_abi.TRI_PAGED))[0] == _abi.TRI_ENOTSUP

@@ -1,0 +1,127 @@
+"""GPU parity of the fused scoring + selection entry point (tri_score_select).
+
+Two checks, through the C ABI:
+- exact: the kept slots of the fused launch equal those tri_select_topb picks from the
+  scores the fused launch itself wrote (the same selection, once over LDS, once over memory);
+- against the float64 oracle: those scores within the score tolerance and the kept set valid
+  up to ties within it (parity.py), for every unit of the small cases and sampled units of the
+  full-size 32K (288 units) and batch-16 (4608 units) workloads.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_tri_amd as tri
+from kv_cache_compression_tri_amd.synth import device as SD
+from kv_cache_compression_tri_amd.synth import workloads as W
+
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def fused(dw, with_scores=True):
+    w = dw.w
+    kv = dw.kv()
+    scores = None
+    if with_scores:
+        scores = torch.full((w.n_seq, w.n_layer, w.n_kvh, kv.slots), float("nan"), dtype=torch.float32,
+                            device=dw.k.device)
+    kept, kept_n = tri.tri_score_select(kv, dw.center, dw.mean_abs, w.budget, w.window, rope_base=w.base,
+                                        offsets=w.offsets, group=w.group, reduce=w.reduce, rope_layout=w.layout,
+                                        scores=scores)
+    torch.cuda.synchronize()
+    return kv, scores, kept, kept_n
+
+
+def check_against_select(dw, kv, scores, kept, kept_n):
+    """The fused selection equals the standalone one on the fused launch's own scores."""
+    w = dw.w
+    k2, n2 = tri.tri_select_topb(scores, kv, w.budget, w.window)
+    torch.cuda.synchronize()
+    assert torch.equal(kept, k2), "fused kept slots differ from tri_select_topb on the same scores"
+    assert torch.equal(kept_n, n2)
+
+
+def check_unit(dw, s, l, h, sc, kp, kn):
+    w, hp = dw.w, dw.hp
+    L = int(hp.lengths[s])
+    keys = P.host_rows(w, hp, s, l, h)
+    orc, S = P.oracle_scores(w, hp, s, l, h, keys)
+    worst, _ = P.check_scores(sc[:L], orc, S)
+    P.check_kept(kp, sc, orc, S, L, w.budget, w.window)
+    assert kn == min(L, w.budget)
+    return worst
+
+
+BASE = W.WORKLOADS["gqa8b_32k_bf16"]
+SMALL = {
+    # max over 4 heads, ragged lengths around the 64-key groups and the per-wave shares
+    "g4_max_half_bf16": (dict(n_seq=4, n_layer=2, n_kvh=2, group=4, max_len=3000, budget=500, window=64),
+                         [3000, 1777, 513, 64]),
+    # mean over the group (one effective head), interleaved pairs
+    "g4_mean_interleaved_bf16": (dict(n_seq=2, n_layer=2, n_kvh=2, group=4, reduce="mean", layout="interleaved",
+                                      max_len=2100, budget=333, window=32), [2100, 1000]),
+    # float32 keys, G = 1; lengths at and below the budget, a single key, an empty sequence
+    "g1_max_half_f32": (dict(n_seq=5, n_layer=1, n_kvh=2, group=1, dtype="f32", max_len=1200, budget=256,
+                             window=16, base=1e4, offsets=W.geometric_offsets(10)), [1200, 256, 100, 1, 0]),
+    # G = 8, window larger than the budget, low-concentration heads
+    "g8_max_interleaved_bf16": (dict(n_seq=1, n_layer=2, n_kvh=2, group=8, layout="interleaved", max_len=1500,
+                                     budget=200, window=300, low_r_frac=0.5), [1500]),
+    # the largest unit the fused launch takes: 32768 slots, and one that is one 8-key step short
+    "g2_max_half_bf16_max_len": (dict(n_seq=2, n_layer=1, n_kvh=1, group=2, max_len=32768, budget=2048,
+                                      window=128), [32768, 32761]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_fused_small(name):
+    over, lengths = SMALL[name]
+    w = W.scaled(BASE, name=name, **over)
+    log(f"fused small {name}: {over} lengths={lengths}")
+    dw = SD.build(w, hp=W.make_params(w, lengths=lengths))
+    kv, scores, kept, kept_n = fused(dw)
+    check_against_select(dw, kv, scores, kept, kept_n)
+    sc, kp, kn = scores.cpu().numpy(), kept.cpu().numpy(), kept_n.cpu().numpy()
+    worst = 0.0
+    for s in range(w.n_seq):
+        for l in range(w.n_layer):
+            for h in range(w.n_kvh):
+                worst = max(worst, check_unit(dw, s, l, h, sc[s, l, h], kp[s, l, h], kn[s]))
+    # without a score buffer the kept slots are the same
+    _, _, kept2, kept_n2 = fused(dw, with_scores=False)
+    assert torch.equal(kept, kept2) and torch.equal(kept_n, kept_n2)
+    log(f"  max score error / bound = {worst:.3e}")
+
+
+@pytest.mark.parametrize("name,units", [
+    ("gqa8b_32k_bf16", [0, 1, 287, 150]),
+    ("gqa8b_batch16_16k_bf16", [0, 4607, 2000]),
+])
+def test_fused_full_size(name, units):
+    w = W.WORKLOADS[name]
+    log(f"fused full size {name}")
+    dw = SD.build(w)
+    kv, scores, kept, kept_n = fused(dw)
+    check_against_select(dw, kv, scores, kept, kept_n)
+    worst = 0.0
+    for u in units:
+        s, l, h = W.unit_coords(w, u)
+        log(f"  unit {u} (seq {s}, layer {l}, head {h})")
+        worst = max(worst, check_unit(dw, s, l, h, scores[s, l, h].cpu().numpy(), kept[s, l, h].cpu().numpy(),
+                                      int(kept_n[s].item())))
+    log(f"  max score error / bound = {worst:.3e}")
