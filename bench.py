@@ -55,6 +55,31 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic.json")
 SCORE_SRCS = [os.path.join(ROOT, "kv_cache_compression_tri_amd", "csrc", f) for f in ("score_kernel.h", "score_mx.h")]
 
 
+def fused_applies(w, key_space: str = "pre", form: str = "additive", positions: bool = False) -> bool:
+    """tri_score_select takes float32/bf16 caches of pre-RoPE keys at their slots, additive form,
+    at most 32768 slots per unit."""
+    slots = w.max_pages * 16 if w.paged else w.max_len
+    return (w.dtype in ("f32", "bf16") and key_space == "pre" and form == "additive" and not positions
+            and slots <= 32768)
+
+
+def use_fused(mode: str, w, n_cu: int, key_space="pre", form="additive", positions=False) -> bool:
+    """Whether a pass scores and selects in one launch.  auto: where the fused launch measured
+    faster than the two launches.  It saves writing the scores and reading them back, which costs
+    most when scoring is bound by the key stream (one effective head: the mean reduction or
+    G = 1), and a workgroup per unit only balances when every CU gets many units (at the 32K
+    pass, 288 units on 256 CUs, 32 CUs score two whole units)."""
+    ok = fused_applies(w, key_space, form, positions)
+    if mode == "on":
+        if not ok:
+            raise SystemExit(f"--fused on: {w.name} is not a case tri_score_select takes")
+        return True
+    if mode == "off" or not ok:
+        return False
+    g_eff = 1 if w.reduce == "mean" else w.group
+    return g_eff == 1 and w.n_units >= 8 * n_cu
+
+
 def score_kernel_used(w, key_space: str, form: str, positions: bool) -> str:
     """The scoring kernel the library launches for this pass: bfloat16 keys before RoPE at
     consecutive positions, additive form, max over 4..8 heads take the matrix-core kernel."""
@@ -87,9 +112,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="time only the headline workload (skip the other stated workloads)")
-    ap.add_argument("--fused", action="store_true",
-                    help="score and select in one launch (tri_score_select; dense f32/bf16 pre-RoPE caches of at "
-                         "most 32768 slots, additive form) instead of two; its time is reported as score_ms")
+    ap.add_argument("--fused", choices=("auto", "on", "off"), default="auto",
+                    help="score and select in one launch (tri_score_select; f32/bf16 pre-RoPE caches of at most "
+                         "32768 slots, additive form) instead of two, its time reported as score_ms: on, off, or "
+                         "auto (default: where it measured faster, one effective head and at least 8 units per CU)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB mebibytes (calibrates HBM counters)")
     return ap.parse_args()
@@ -422,7 +448,7 @@ def measure(args, name, steps, warmup, key_space="pre", form="additive", positio
     }
 
 
-def config_entry(m):
+def config_entry(m, fused=False):
     """Summary of one workload's measurement for the `configs` object."""
     w = m["w"]
     ms = m["ms"]
@@ -432,7 +458,8 @@ def config_entry(m):
         "pass_hbm_frac": m["pass_bytes"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "score_kernel_hbm_frac": m["score_bytes"] / (m["score_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "score_ms": m["score_ms"], "select_ms": m["select_ms"], "compact_ms": m["compact_ms"],
-        "score_kernel": score_kernel_used(w, "pre", "additive", False),
+        "score_kernel": "score_select_kernel" if fused else score_kernel_used(w, "pre", "additive", False),
+        "fused_score_select": fused,
         "keys_per_step": m["keys_per_step"], "algorithmic_bytes": m["pass_bytes"],
         "shape": {"n_seq": w.n_seq, "n_layer": w.n_layer, "n_kv_heads": w.n_kvh, "group": w.group,
                   "context": w.max_len, "kv_dtype": w.dtype, "budget": w.budget, "window": w.window,
@@ -473,11 +500,10 @@ def main():
         print("no GPU visible", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
-    if args.fused and (args.key_space != "pre" or args.form != "additive" or args.positions):
-        print("--fused takes pre-RoPE keys at their slots in the additive form", file=sys.stderr)
-        return 2
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    fused = use_fused(args.fused, W.WORKLOADS[name], n_cu, args.key_space, args.form, args.positions)
     m = measure(args, name, args.steps, args.warmup, args.key_space, args.form, args.positions, args.consumer,
-                args.preroll_ms, fused=args.fused)
+                args.preroll_ms, fused=fused)
     w = m["w"]
     ms, score_ms = m["ms"], m["score_ms"]
     keys_per_step, score_bytes, pass_bytes = m["keys_per_step"], m["score_bytes"], m["pass_bytes"]
@@ -488,7 +514,7 @@ def main():
     value = keys_per_step / (ms * 1e-3) / 1e9
     traffic = recorded_traffic(name) if (args.key_space == "pre" and args.form == "additive"
                                          and not args.positions) else None
-    kernel = "score_select_kernel" if args.fused else score_kernel_used(w, args.key_space, args.form, args.positions)
+    kernel = "score_select_kernel" if fused else score_kernel_used(w, args.key_space, args.form, args.positions)
     line = {
         "metric": METRIC,
         "value": value,
@@ -511,7 +537,7 @@ def main():
             "context": w.max_len, "head_dim": w.head_dim, "kv_dtype": w.dtype, "budget": w.budget,
             "window": w.window, "offsets": len(w.offsets), "reduce": w.reduce,
             "layout": "paged" if w.paged else "dense", "compaction": m["compacts"], "key_space": args.key_space,
-            "form": args.form, "explicit_positions": bool(args.positions), "fused_score_select": bool(args.fused),
+            "form": args.form, "explicit_positions": bool(args.positions), "fused_score_select": fused,
             "keys_per_step": keys_per_step, "parallelism": "single GPU",
         },
         "roofline": {
@@ -555,7 +581,7 @@ def main():
     # refilled before every pass, outside the timed region).  Their pass counts are capped so
     # that the default run stays within a few minutes.
     if not args.workload and not args.no_configs and args.key_space == "pre" and args.form == "additive" \
-            and not args.positions and not args.fused:
+            and not args.positions and args.fused != "on":
         configs = {}
         for other in W.STATED_WORKLOADS:
             if other == name:
@@ -563,7 +589,8 @@ def main():
             paged = W.WORKLOADS[other].paged
             k = min(args.steps, 20 if paged else 200)
             wu = min(args.warmup, 5 if paged else 50)
-            configs[other] = config_entry(measure(args, other, max(k, 1), wu))
+            fo = use_fused(args.fused, W.WORKLOADS[other], n_cu)
+            configs[other] = config_entry(measure(args, other, max(k, 1), wu, fused=fo), fo)
         line["configs"] = configs
     _, copy_gbs = copy_bandwidth(1024)
     line["pass"]["copy_GBps"] = copy_gbs

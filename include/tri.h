@@ -216,12 +216,13 @@ int tri_select_topb(const float *scores, const tri_kv *kv, int32_t budget, int32
  * only the top-scoring ones are kept), one workgroup per unit: the unit's scores stay in
  * on-chip memory between the two steps instead of going to memory and back.  It computes
  * exactly what tri_score_keys followed by tri_select_topb compute, for the cases it takes:
- *   dense caches (kv->layout TRI_DENSE) of TRI_F32 or TRI_BF16 keys before RoPE
- *   (cfg->key_space TRI_KEYS_PRE_ROPE) at their slot positions (kv->pos NULL), additive
- *   form, kv->max_len <= 32768; anything else returns TRI_ENOTSUP.
+ *   dense or paged caches of TRI_F32 or TRI_BF16 keys before RoPE (cfg->key_space
+ *   TRI_KEYS_PRE_ROPE) at their slot positions (kv->pos NULL), additive form, at most 32768
+ *   slots per unit (dense: max_len; paged: max_pages * page); anything else returns
+ *   TRI_ENOTSUP.
  * Arguments as for tri_score_keys and tri_select_topb; scores may be NULL (then no score is
- * written) or, as for tri_score_keys, [n_seq][n_layer][n_kvh][max_len] float32 to receive
- * them as well.  kept and kept_n as for tri_select_topb.  Needs no workspace. */
+ * written) or, as for tri_score_keys, [n_seq][n_layer][n_kvh][slots] float32 to receive them
+ * as well.  kept and kept_n as for tri_select_topb.  Needs no workspace. */
 int tri_score_select(const tri_score_cfg *cfg, const float *center, const float *mean_abs,
                      const tri_kv *kv, const int64_t *query_pos, int32_t budget, int32_t window,
                      float *scores, int32_t *kept, int32_t *kept_n, void *ws, size_t *ws_bytes,

@@ -270,8 +270,8 @@ def tri_select_topb(scores, kv: KVCache, budget: int, window: int, kept=None, ke
 def tri_score_select(kv: KVCache, center, mean_abs, budget: int, window: int, *, rope_base: float,
                      offsets: Sequence[int], group: int, reduce: str = "max", rope_layout: str = "half",
                      query_pos=None, scores=None, kept=None, kept_n=None, stream=None):
-    """Scoring and top-B selection in one launch (dense float32 / bfloat16 pre-RoPE caches of at
-    most 32768 slots, additive form); returns (kept, kept_n) as tri_select_topb does.  scores,
+    """Scoring and top-B selection in one launch (dense or paged float32 / bfloat16 pre-RoPE caches
+    of at most 32768 slots, additive form); returns (kept, kept_n) as tri_select_topb does.  scores,
     if given, also receives the scores (as from tri_score_keys); None writes none."""
     torch = _torch()
     L = _abi.lib()

@@ -418,13 +418,12 @@ int tri_score_select(const tri_score_cfg* cfg, const float* center, const float*
     tri::SelectParams sp;
     if (int rc = score_setup(cfg, center, mean_abs, kv, query_pos, scores, p)) return rc;
     if (int rc = select_setup(kv, budget, window, kept, kept_n, sp)) return rc;
-    if (kv->layout != TRI_DENSE) return fail(TRI_ENOTSUP, "fused scoring and selection takes dense caches only");
     if (kv->dtype != TRI_F32 && kv->dtype != TRI_BF16)
       return fail(TRI_ENOTSUP, "fused scoring and selection takes float32 or bfloat16 keys only");
     if (cfg->key_space != TRI_KEYS_PRE_ROPE || cfg->form != TRI_SCORE_ADDITIVE || kv->pos)
       return fail(TRI_ENOTSUP, "fused scoring and selection takes pre-RoPE keys at their slots, additive form");
     if (p.score_stride > tri::kFuseMaxSlots)
-      return fail(TRI_ENOTSUP, "fused scoring and selection holds at most %d slots per unit (max_len %lld)",
+      return fail(TRI_ENOTSUP, "fused scoring and selection holds at most %d slots per unit (%lld)",
                   tri::kFuseMaxSlots, (long long)p.score_stride);
     const int64_t units = int64_t(kv->n_seq) * kv->n_layer * kv->n_kvh;
     if (units > 0x7FFFFFFF) return fail(TRI_ENOTSUP, "grid too large");
@@ -433,7 +432,7 @@ int tri_score_select(const tri_score_cfg* cfg, const float* center, const float*
     const int g_eff = p.reduce_mean ? 1 : cfg->group;
     (void)hipGetLastError();
     hipError_t e = tri::launch_score_select(p, sp, g_eff, kv->dtype, cfg->rope_layout == TRI_ROPE_INTERLEAVED,
-                                            units, static_cast<hipStream_t>(stream));
+                                            kv->layout == TRI_PAGED, units, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TRI_OK : hip_fail(e, "fused score/select launch");
   } catch (...) {
     return fail(TRI_EHIP, "unexpected host exception in tri_score_select");

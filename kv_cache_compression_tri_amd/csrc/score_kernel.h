@@ -212,7 +212,8 @@ __device__ __forceinline__ void for_each_segment(const ScoreParams& P, int lane,
   }
 }
 
-// Fused scoring and selection (FUSE): one workgroup per unit of at most kFuseMax slots scores
+// Fused scoring and selection (FUSE; dense or paged caches): one workgroup per unit of at most
+// kFuseMax slots scores
 // the unit into LDS, each wave an equal run of whole 64-key groups, and then selects its top B
 // from there (select_core.h), so the scores never go to memory.  The LDS is the phase table,
 // on a kFuseChunk-offset chunk (32 KB), and the unit's scores (128 KB): the CU's whole 160 KB,
@@ -236,7 +237,7 @@ template <int GE, int DT, bool IL, bool PAGED, bool POST, bool MULT, bool XP, bo
 __device__ __forceinline__ void score_impl(const ScoreParams& P, const SelectParams& SP) {
   // XP: pre-RoPE keys at explicit positions (P.pos): each key is rotated by its own phase,
   // formed like the anchor (float64 turns) and evaluated by v_cos / v_sin; no table
-  static_assert(!FUSE || (!PAGED && !POST && !MULT && !XP && DT <= 1), "fused: dense pre-RoPE additive f32/bf16");
+  static_assert(!FUSE || (!POST && !MULT && !XP && DT <= 1), "fused: pre-RoPE additive f32/bf16");
   constexpr int NW = kScoreWaves;
   constexpr int NT = NW * 64;
   constexpr int CH = FUSE ? kFuseChunk : kChunk;   // phase-table offsets
@@ -685,9 +686,9 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(const ScorePara
 }
 
 // scoring and selection of one unit per workgroup (FUSE above)
-template <int GE, int DT, bool IL>
+template <int GE, int DT, bool IL, bool PAGED>
 __global__ __launch_bounds__(kScoreWaves * 64) void score_select_kernel(const ScoreParams P, const SelectParams S) {
-  score_impl<GE, DT, IL, false, false, false, false, true>(P, S);
+  score_impl<GE, DT, IL, PAGED, false, false, false, true>(P, S);
 }
 
 template <int GE, int DT, bool POST, bool MULT, bool XP>

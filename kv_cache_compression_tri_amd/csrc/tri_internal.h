@@ -91,13 +91,17 @@ hipError_t launch_score(const ScoreParams& p, int G_eff, int dtype, bool interle
                         bool post, bool mult, int grid, hipStream_t stream);
 hipError_t launch_score_pos(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged, int grid,
                             hipStream_t stream);
-// fused scoring and selection, one workgroup per unit of at most kFuseMaxSlots slots (dense
-// float32 / bfloat16 keys before RoPE at their slots, additive form)
+// fused scoring and selection, one workgroup per unit of at most kFuseMaxSlots slots (float32 /
+// bfloat16 keys before RoPE at their slots, additive form; dense or paged)
 constexpr int kFuseMaxSlots = 32768;
 hipError_t launch_score_select(const ScoreParams& p, const SelectParams& s, int G_eff, int dtype, bool interleaved,
-                               int64_t units, hipStream_t stream);
+                               bool paged, int64_t units, hipStream_t stream);
 hipError_t launch_score_select_f32(const ScoreParams& p, const SelectParams& s, int G_eff, bool interleaved,
                                    int64_t units, hipStream_t stream);
+hipError_t launch_score_select_bf16_paged(const ScoreParams& p, const SelectParams& s, int G_eff, bool interleaved,
+                                          int64_t units, hipStream_t stream);
+hipError_t launch_score_select_f32_paged(const ScoreParams& p, const SelectParams& s, int G_eff, bool interleaved,
+                                         int64_t units, hipStream_t stream);
 // the matrix-core scoring kernel (bfloat16 keys before RoPE at consecutive positions,
 // additive form, max over 4..8 heads) and the shapes it takes
 bool score_mx_applies(int G_eff, int dtype, bool post, bool mult, bool positions, bool reduce_mean);

@@ -340,8 +340,8 @@ def test_decode_attention_noalloc_validation():
 
 
 def test_score_select_validation():
-    # tri.h, tri_score_select: dense float32 / bfloat16 caches of pre-RoPE keys at their slots,
-    # additive form, at most 32768 slots; everything else is refused before any launch.  The
+    # tri.h, tri_score_select: dense or paged float32 / bfloat16 caches of pre-RoPE keys at their
+    # slots, additive form, at most 32768 slots; everything else is refused before any launch.  The
     # workspace query validates without launching and needs 0 bytes.
     L = _abi.lib()
 
@@ -359,7 +359,9 @@ def test_score_select_validation():
     assert call(kv=_kv(max_len=32768)) == (_abi.TRI_OK, 0)
     assert call(kv=_kv(max_len=32769))[0] == _abi.TRI_ENOTSUP
     assert "32768" in L.tri_last_error().decode()
-    assert call(kv=_kv(layout=_abi.TRI_PAGED))[0] == _abi.TRI_ENOTSUP
+    assert call(kv=_kv(layout=_abi.TRI_PAGED)) == (_abi.TRI_OK, 0)
+    assert call(kv=_kv(layout=_abi.TRI_PAGED, max_pages=2048)) == (_abi.TRI_OK, 0)
+    assert call(kv=_kv(layout=_abi.TRI_PAGED, max_pages=2049))[0] == _abi.TRI_ENOTSUP
     for dt in (_abi.TRI_FP8_E4M3, _abi.TRI_INT8):
         assert call(kv=_kv(dtype=dt))[0] == _abi.TRI_ENOTSUP
     assert call(cfg_over=dict(key_space=_abi.TRI_KEYS_POST_ROPE))[0] == _abi.TRI_ENOTSUP
@@ -370,4 +372,4 @@ def test_score_select_validation():
     assert call(window=-1)[0] == _abi.TRI_EINVAL
     assert call(kept=None)[0] == _abi.TRI_EINVAL
     assert call(mean_abs=None)[0] == _abi.TRI_EINVAL
-    assert call(query=False, kv=_kv(layout=_abi.TRI_PAGED))[0] == _abi.TRI_ENOTSUP
+    assert call(query=False, kv=_kv(dtype=_abi.TRI_INT8))[0] == _abi.TRI_ENOTSUP

@@ -4,8 +4,9 @@ Two checks, through the C ABI:
 - exact: the kept slots of the fused launch equal those tri_select_topb picks from the
   scores the fused launch itself wrote (the same selection, once over LDS, once over memory);
 - against the float64 oracle: those scores within the score tolerance and the kept set valid
-  up to ties within it (parity.py), for every unit of the small cases and sampled units of the
-  full-size 32K (288 units) and batch-16 (4608 units) workloads.
+  up to ties within it (parity.py), for every unit of the small dense and paged cases and
+  sampled units of the full-size 32K (288 units), batch-16 (4608 units) and paged 64-sequence
+  (18432 units) workloads.
 """
 
 import numpy as np
@@ -108,9 +109,30 @@ def test_fused_small(name):
     log(f"  max score error / bound = {worst:.3e}")
 
 
+@pytest.mark.parametrize("lengths,extra", [
+    ([5000, 70, 1300, 1024], {}),                                            # bf16, max over 4 heads
+    ([2222, 4000, 1, 513], dict(dtype="f32", layout="interleaved", group=2)),
+    ([700, 4100, 1500, 33], dict(layout="interleaved", group=3, reduce="mean")),
+    ([5120, 5105, 17, 4096], dict(group=8, window=0)),
+])
+def test_fused_small_paged(lengths, extra):
+    w = W.scaled(W.WORKLOADS["paged_ragged64_bf16"], n_seq=4, n_layer=2, n_kvh=2, max_len=5120,
+                 len_range=(16, 5120), **extra)
+    log(f"fused small paged lengths={lengths} {extra}")
+    dw = SD.build(w, hp=W.make_params(w, lengths=lengths))
+    kv, scores, kept, kept_n = fused(dw)
+    check_against_select(dw, kv, scores, kept, kept_n)
+    sc, kp, kn = scores.cpu().numpy(), kept.cpu().numpy(), kept_n.cpu().numpy()
+    for s in range(w.n_seq):
+        for l in range(w.n_layer):
+            for h in range(w.n_kvh):
+                check_unit(dw, s, l, h, sc[s, l, h], kp[s, l, h], kn[s])
+
+
 @pytest.mark.parametrize("name,units", [
     ("gqa8b_32k_bf16", [0, 1, 287, 150]),
     ("gqa8b_batch16_16k_bf16", [0, 4607, 2000]),
+    ("paged_ragged64_bf16", [0, 18431, 9000]),
 ])
 def test_fused_full_size(name, units):
     w = W.WORKLOADS[name]
