@@ -341,6 +341,9 @@ def measure(args, name, steps, warmup, key_space="pre", form="additive", positio
         v_out = torch.empty_like(k_out) if dw.v is not None else None
         freed = n_freed = None
 
+    # the selection's workspace (units longer than 32768 slots: two-stage selection), allocated once
+    sel_ws = tri.select_workspace(scores, kv, w.budget, w.window, kept, kept_n)
+
     def step(ev=None):
         # ev: events recorded before the score kernel and after it (the timed loop), plus after
         # the selection and after the compaction (the breakdown loop); None entries are skipped
@@ -357,7 +360,7 @@ def measure(args, name, steps, warmup, key_space="pre", form="additive", positio
         if ev is not None and ev[1] is not None:
             ev[1].record()
         if not fused:
-            tri.tri_select_topb(scores, kv, w.budget, w.window, kept=kept, kept_n=kept_n)
+            tri.tri_select_topb(scores, kv, w.budget, w.window, kept=kept, kept_n=kept_n, workspace=sel_ws)
         if ev is not None and ev[2] is not None:
             ev[2].record()
         if compacts:

@@ -208,7 +208,12 @@ int tri_score_keys(const tri_score_cfg *cfg, const float *center, const float *m
  *   kept:   out int32 [n_seq][n_layer][n_kvh][budget], kept slots in ascending order;
  *           entries past the kept count are set to -1
  *   kept_n: out int32 [n_seq], min(budget, seq_len[s]) (same for every unit of s)
- * Needs no workspace. */
+ * Workspace (optional): ws == NULL with ws_bytes != NULL stores the size that lets units of
+ * more than 32768 slots be selected in two stages over many workgroups (0 when that does not
+ * apply: shorter units, or budget - min(window, budget) too large for it); given a
+ * workspace of that size, the call uses it, and returns TRI_EWORKSPACE if it is smaller.
+ * Without one (ws_bytes == NULL) every unit is selected by one workgroup.  The result is
+ * the same either way. */
 int tri_select_topb(const float *scores, const tri_kv *kv, int32_t budget, int32_t window,
                     int32_t *kept, int32_t *kept_n, void *ws, size_t *ws_bytes, void *stream);
 

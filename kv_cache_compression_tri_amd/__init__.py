@@ -26,6 +26,7 @@ __all__ = [
     "tri_calibrate_stats",
     "tri_score_keys",
     "tri_select_topb",
+    "select_workspace",
     "tri_score_select",
     "tri_compact_kv",
     "tri_decode_attention",
@@ -247,8 +248,24 @@ def tri_score_keys(kv: KVCache, center, mean_abs, *, rope_base: float, offsets: 
     return scores
 
 
-def tri_select_topb(scores, kv: KVCache, budget: int, window: int, kept=None, kept_n=None, stream=None):
-    """Top-B per unit; returns (kept int32 [n_seq, n_layer, n_kvh, budget], kept_n int32 [n_seq])."""
+def select_workspace(scores, kv: KVCache, budget: int, window: int, kept, kept_n):
+    """The workspace tri_select_topb can use for these buffers (a device uint8 tensor), or None
+    when it needs none: allocate once and pass it to every call of a loop."""
+    torch = _torch()
+    L = _abi.lib()
+    desc = kv.descriptor()
+    need = ctypes.c_size_t(0)
+    _abi.check(L.tri_select_topb(_ptr(scores), ctypes.byref(desc), int(budget), int(window), _ptr(kept),
+                                 _ptr(kept_n), None, ctypes.byref(need), None))
+    return torch.empty((need.value,), dtype=torch.uint8, device=scores.device) if need.value else None
+
+
+def tri_select_topb(scores, kv: KVCache, budget: int, window: int, kept=None, kept_n=None, stream=None,
+                    workspace="auto"):
+    """Top-B per unit; returns (kept int32 [n_seq, n_layer, n_kvh, budget], kept_n int32 [n_seq]).
+
+    workspace: "auto" (allocated here when units longer than 32768 slots can be selected in two
+    stages over many workgroups), None (one workgroup per unit), or a device uint8 tensor."""
     torch = _torch()
     L = _abi.lib()
     desc = kv.descriptor()
@@ -262,8 +279,21 @@ def tri_select_topb(scores, kv: KVCache, budget: int, window: int, kept=None, ke
     _shape(scores, "scores", (kv.n_seq, desc.n_layer, desc.n_kvh, kv.slots))
     _shape(kept, "kept", (kv.n_seq, desc.n_layer, desc.n_kvh, int(budget)))
     _shape(kept_n, "kept_n", (kv.n_seq,))
+    ws, nbytes, cap = None, None, ctypes.c_size_t(0)
+    if workspace is not None:
+        need = ctypes.c_size_t(0)
+        _abi.check(L.tri_select_topb(_ptr(scores), ctypes.byref(desc), int(budget), int(window), _ptr(kept),
+                                     _ptr(kept_n), None, ctypes.byref(need), _stream(stream)))
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError("workspace must be 'auto', None or a device uint8 tensor")
+            workspace = (torch.empty((need.value,), dtype=torch.uint8, device=scores.device) if need.value else None)
+        if workspace is not None:
+            _dev(workspace, "workspace", torch.uint8)
+            cap.value = workspace.numel()
+            ws, nbytes = _ptr(workspace), ctypes.byref(cap)
     _abi.check(L.tri_select_topb(_ptr(scores), ctypes.byref(desc), int(budget), int(window), _ptr(kept),
-                                 _ptr(kept_n), None, None, _stream(stream)))
+                                 _ptr(kept_n), ws, nbytes, _stream(stream)))
     return kept, kept_n
 
 

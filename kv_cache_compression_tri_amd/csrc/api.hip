@@ -447,11 +447,21 @@ int tri_select_topb(const float* scores, const tri_kv* kv, int32_t budget, int32
     tri::SelectParams p;
     if (int rc = select_setup(kv, budget, window, kept, kept_n, p)) return rc;
     if (!scores) return fail(TRI_EINVAL, "scores, kept and kept_n must be non-NULL");
-    if (int rc = workspace(ws, ws_bytes, 0)) return rc > 0 ? TRI_OK : rc;
     p.scores = scores;
     const int64_t units = int64_t(kv->n_seq) * p.units_per_seq;
+    // optional workspace: units longer than 32768 slots are then selected by the two-stage
+    // tournament instead of one workgroup each
+    const size_t need = tri::select_workspace_bytes(p, units);
+    if (ws_bytes && !ws) {
+      *ws_bytes = need;
+      return TRI_OK;
+    }
+    const bool tour = ws && ws_bytes && need > 0;
+    if (tour && *ws_bytes < need)
+      return fail(TRI_EWORKSPACE, "workspace of %zu bytes required (%zu given)", need, *ws_bytes);
+    if (tour && units * ((p.score_stride + 32767) / 32768) > 0x7FFFFFFF) return fail(TRI_ENOTSUP, "grid too large");
     (void)hipGetLastError();
-    hipError_t e = tri::launch_select(p, units, static_cast<hipStream_t>(stream));
+    hipError_t e = tri::launch_select(p, units, tour ? ws : nullptr, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TRI_OK : hip_fail(e, "select launch");
   } catch (...) {
     return fail(TRI_EHIP, "unexpected host exception in tri_select_topb");

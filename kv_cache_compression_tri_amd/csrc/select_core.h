@@ -15,7 +15,8 @@
 // found by refining linear histograms instead of sorting:
 //   level 1: 2048 bins spanning [min, max] of the candidate keys, counted in four copies (lane
 //            l adds into copy l % 4, so lanes of one instruction that hit the same bin mostly
-//            hit different LDS words) and then folded;
+//            hit different LDS words; a lane adds a run of its slots in one bin at once) and
+//            then folded;
 //   level k+1: 2048 sub-bins of the bin that holds the target rank;
 // until either the whole target bin is kept (its lower edge becomes the threshold: keep
 // key >= T) or the bins are single key values (at most three levels, because the key span
@@ -126,13 +127,24 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t rank, in
   tbin = uint32_t(top - k);
 }
 
-// Selection of one unit by a workgroup of NT threads, whose lanes hold up to kCap slots in
-// registers (kCap / NT per lane); longer units (kStream) re-read their scores on every sweep.
-// The scores come from global memory (P.scores), or, with kLds, from lds_sc (the unit's
-// score_stride slots, already in LDS and complete: the caller synchronises first).
-template <int NT, int kCap, bool kStream, bool kLds>
-__device__ __forceinline__ void select_unit(const SelectParams& P, const int64_t unit, const SelLds<NT / 64>& S,
-                                            const float* lds_sc) {
+// One selection: L values (scores, or with kKeysIn order keys already), keep the last
+// min(window, B) positions and the best B - min(window, B) others; write the kept positions
+// ascending.
+struct SelJob {
+  const void* in;            // the L values (global memory; with kLds the LDS argument instead)
+  int L, B, window;
+  int32_t* out;              // B entries: kept positions ascending, -1 past the kept count
+  uint32_t* out_key;         // optional: the kept positions' order keys, in the same order
+  const int32_t* pos_map;    // optional: write pos_map[j] instead of base + j
+  int32_t base;              // added to the written positions (without pos_map)
+  int32_t* kept_n;           // optional: receives min(L, B)
+};
+
+// Selection by a workgroup of NT threads, whose lanes hold up to kCap values in registers
+// (kCap / NT per lane); longer inputs (kStream) are re-read on every sweep.  With kLds the
+// values are lds_sc (already in LDS and complete: the caller synchronises first).
+template <int NT, int kCap, bool kStream, bool kLds, bool kKeysIn = false>
+__device__ __forceinline__ void select_job(const SelJob& J, const SelLds<NT / 64>& S, const float* lds_sc) {
   constexpr int kSelThreads = NT;
   constexpr int kSelWaves = NT / 64;
   constexpr int kBatchTiles = kCap / (NT * kVec);   // tiles of keys a wave holds in registers
@@ -140,18 +152,26 @@ __device__ __forceinline__ void select_unit(const SelectParams& P, const int64_t
   static_assert(!(kStream && kLds), "LDS-resident scores are never streamed");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int s = int(unit / P.units_per_seq);
-  const int L = min(max(P.seq_len[s], 0), int(P.score_stride));
-  const int B = P.budget;
-  const float* sc = kLds ? nullptr : P.scores + unit * P.score_stride;
-  int32_t* out = P.kept + unit * int64_t(B);
+  const int L = J.L;
+  const int B = J.B;
+  const float* sc = kLds ? nullptr : static_cast<const float*>(J.in);
+  int32_t* out = J.out;
+  auto position = [&](int j) __attribute__((always_inline)) -> int32_t {
+    return J.pos_map ? J.pos_map[j] : J.base + j;
+  };
 
-  if (tid == 0 && unit % P.units_per_seq == 0) P.kept_n[s] = min(L, B);
+  if (tid == 0 && J.kept_n) *J.kept_n = min(L, B);
   if (L <= B) {
-    for (int i = tid; i < B; i += kSelThreads) out[i] = i < L ? i : -1;
+    for (int i = tid; i < B; i += kSelThreads) {
+      out[i] = i < L ? position(i) : -1;
+      if (J.out_key && i < L) {
+        const uint32_t raw = kLds ? __float_as_uint(lds_sc[i]) : __float_as_uint(sc[i]);
+        J.out_key[i] = kKeysIn ? raw : order_key(raw);
+      }
+    }
     return;
   }
-  const int w = min(P.window, B);
+  const int w = min(J.window, B);
   const int ncand = L - w;                 // >= 1 because L > B >= w
   const uint32_t need = uint32_t(B - w);   // candidates to keep
 
@@ -191,12 +211,12 @@ __device__ __forceinline__ void select_unit(const SelectParams& P, const int64_t
       if (t0 + t < n_tiles) {
         if (jt + kTile <= cand_end) {
 #pragma unroll
-          for (int e = 0; e < kVec; ++e) u[t][e] = order_key(u[t][e]);
+          for (int e = 0; e < kVec; ++e) u[t][e] = kKeysIn ? u[t][e] : order_key(u[t][e]);
         } else {
 #pragma unroll
           for (int e = 0; e < kVec; ++e) {
             const int j = jt + lane * kVec + e;
-            u[t][e] = j >= r1 ? kKeyNone : j >= ncand ? kKeyWindow : order_key(u[t][e]);
+            u[t][e] = j >= r1 ? kKeyNone : j >= ncand ? kKeyWindow : kKeysIn ? u[t][e] : order_key(u[t][e]);
           }
         }
       }
@@ -281,11 +301,23 @@ __device__ __forceinline__ void select_unit(const SelectParams& P, const int64_t
       if (lev == 0) {
         const uint32_t copy = uint32_t(lane & (kSubHist - 1)) * kBins;
         sweep([&](int t, int) __attribute__((always_inline)) {
+          // a lane's 4 consecutive slots often share a bin: runs of equal bins add once
+          uint32_t pb = 0xFFFFFFFFu, pc = 0;
 #pragma unroll
           for (int e = 0; e < kVec; ++e) {
             const uint32_t d = u[t][e] - base;
-            if (d <= span) atomicAdd(&S.sub[copy + (d >> shift)], 1u);
+            if (d <= span) {
+              const uint32_t b = d >> shift;
+              if (b == pb) {
+                ++pc;
+              } else {
+                if (pc) atomicAdd(&S.sub[copy + pb], pc);
+                pb = b;
+                pc = 1;
+              }
+            }
           }
+          if (pc) atomicAdd(&S.sub[copy + pb], pc);
         });
         __syncthreads();
         for (int i = tid; i < kBins; i += kSelThreads) {   // fold the copies
@@ -382,12 +414,33 @@ __device__ __forceinline__ void select_unit(const SelectParams& P, const int64_t
     for (int e = 0; e < kVec; ++e) r = mbcnt(m[e], r);
 #pragma unroll
     for (int e = 0; e < kVec; ++e) {
-      if (f[e] && r < uint32_t(B)) out[r] = jt + lane * kVec + e;
+      if (f[e] && r < uint32_t(B)) {
+        out[r] = position(jt + lane * kVec + e);
+        if (J.out_key) J.out_key[r] = u[t][e];
+      }
       r += f[e] ? 1u : 0u;
     }
 #pragma unroll
     for (int e = 0; e < kVec; ++e) run += uint32_t(__popcll(m[e]));
   });
+}
+
+// Selection of unit `unit` of a SelectParams launch (its scores, length, budget and window).
+template <int NT, int kCap, bool kStream, bool kLds>
+__device__ __forceinline__ void select_unit(const SelectParams& P, const int64_t unit, const SelLds<NT / 64>& S,
+                                            const float* lds_sc) {
+  const int s = int(unit / P.units_per_seq);
+  SelJob J;
+  J.in = kLds ? nullptr : P.scores + unit * P.score_stride;
+  J.L = min(max(P.seq_len[s], 0), int(P.score_stride));
+  J.B = P.budget;
+  J.window = P.window;
+  J.out = P.kept + unit * int64_t(P.budget);
+  J.out_key = nullptr;
+  J.pos_map = nullptr;
+  J.base = 0;
+  J.kept_n = unit % P.units_per_seq == 0 ? P.kept_n + s : nullptr;
+  select_job<NT, kCap, kStream, kLds>(J, S, lds_sc);
 }
 
 }  // namespace

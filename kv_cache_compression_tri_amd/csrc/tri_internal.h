@@ -164,7 +164,10 @@ int64_t decode_workspace_bytes(int64_t unit_passes, int n_split);
 hipError_t launch_decode_attention(const DecodeParams& p, bool bf16, bool interleaved, bool paged, bool post,
                                    hipStream_t stream);
 
-hipError_t launch_select(const SelectParams& p, int64_t n_units, hipStream_t stream);
+// selection; with a workspace of select_workspace_bytes (> 0 only for units longer than the
+// register-resident capacity), the two-stage tournament, otherwise one workgroup per unit
+size_t select_workspace_bytes(const SelectParams& p, int64_t n_units);
+hipError_t launch_select(const SelectParams& p, int64_t n_units, void* ws, hipStream_t stream);
 hipError_t launch_compact(const CompactParams& p, int64_t n_units, int elem_bytes, bool paged,
                           bool with_v, hipStream_t stream);
 hipError_t launch_calib(const CalibParams& p, bool bf16, bool interleaved, hipStream_t stream);

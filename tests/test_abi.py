@@ -373,3 +373,30 @@ def test_score_select_validation():
     assert call(kept=None)[0] == _abi.TRI_EINVAL
     assert call(mean_abs=None)[0] == _abi.TRI_EINVAL
     assert call(query=False, kv=_kv(dtype=_abi.TRI_INT8))[0] == _abi.TRI_ENOTSUP
+
+
+def test_select_workspace_query():
+    # tri.h, tri_select_topb: the optional workspace lets units of more than 32768 slots be
+    # selected in two stages; its size is units x runs x (budget - min(window, budget)) x 8
+    # bytes while runs x that <= 32768, else 0 (and 0 for shorter units).
+    L = _abi.lib()
+
+    def need(kv, budget, window):
+        size = ctypes.c_size_t(123)
+        rc = L.tri_select_topb(FAKE, ctypes.byref(kv), budget, window, FAKE, FAKE, None, ctypes.byref(size), None)
+        assert rc == _abi.TRI_OK
+        return size.value
+
+    units = 1 * 2 * 2
+    assert need(_kv(max_len=4096), 2048, 128) == 0
+    assert need(_kv(max_len=32768), 2048, 128) == 0
+    assert need(_kv(max_len=131072), 4096, 256) == units * 4 * 3840 * 8
+    assert need(_kv(max_len=32769), 2048, 128) == units * 2 * 1920 * 8
+    assert need(_kv(max_len=131072), 8200, 8) == units * 4 * 8192 * 8
+    assert need(_kv(max_len=131072), 8201, 8) == 0                  # 4 runs x 8193 > 32768
+    assert need(_kv(max_len=131072), 2048, 2048) == 0               # the window is the budget
+    assert need(_kv(layout=_abi.TRI_PAGED, max_pages=4096), 1024, 128) == units * 2 * 896 * 8
+    # a workspace smaller than needed is refused
+    size = ctypes.c_size_t(100)
+    assert L.tri_select_topb(FAKE, ctypes.byref(_kv(max_len=131072)), 4096, 256, FAKE, FAKE, FAKE,
+                             ctypes.byref(size), None) == _abi.TRI_EWORKSPACE

@@ -314,15 +314,18 @@ def _select_case(scores_list, budget, window):
     lengths = torch.tensor([len(x) for x in scores_list], dtype=torch.int32, device="cuda")
     k = torch.empty((n_seq, 1, 1, max_len, 128), dtype=torch.bfloat16, device="cuda")
     kv = tri.KVCache.dense(k, None, lengths)
-    kept, kept_n = tri.tri_select_topb(torch.from_numpy(sc).cuda(), kv, budget, window)
-    kept, kept_n = kept.cpu().numpy(), kept_n.cpu().numpy()
-    for i, x in enumerate(scores_list):
-        L = len(x)
-        want = oracle.select_top_b(np.asarray(x, np.float64), L, budget, window)
-        n = min(L, budget)
-        assert kept_n[i] == n
-        assert np.array_equal(kept[i, 0, 0, :n], want), f"case {i} (L={L}, B={budget}, W={window})"
-        assert np.all(kept[i, 0, 0, n:] == -1)
+    dsc = torch.from_numpy(sc).cuda()
+    # both ways: with the workspace (units over 32768 slots: two-stage selection) and without
+    for ws in ("auto", None):
+        kept, kept_n = tri.tri_select_topb(dsc, kv, budget, window, workspace=ws)
+        kept, kept_n = kept.cpu().numpy(), kept_n.cpu().numpy()
+        for i, x in enumerate(scores_list):
+            L = len(x)
+            want = oracle.select_top_b(np.asarray(x, np.float64), L, budget, window)
+            n = min(L, budget)
+            assert kept_n[i] == n
+            assert np.array_equal(kept[i, 0, 0, :n], want), f"case {i} (L={L}, B={budget}, W={window}, ws={ws})"
+            assert np.all(kept[i, 0, 0, n:] == -1)
 
 
 def test_select_edge_cases():
@@ -375,6 +378,32 @@ def test_select_long_unit_multiple_segments():
     y = rng.integers(0, 50, 70001).astype(np.float32)
     log("select long units (140000, 70001), B=5000 W=256")
     _select_case([x, y], 5000, 256)
+
+
+def test_select_two_stage_runs():
+    # units over 32768 slots with a workspace: each run of 32768 candidates keeps its best B',
+    # then the unit keeps its best B' of those; lengths around the runs' edges, ties across
+    # runs, special values, units at or below the budget and at the register capacity
+    rng = np.random.default_rng(8)
+    special = rng.standard_normal(65553).astype(np.float32)
+    special[rng.choice(65553, 3000, replace=False)] = np.nan
+    special[rng.choice(65553, 3000, replace=False)] = -np.inf
+    special[rng.choice(65553, 500, replace=False)] = np.inf
+    special[rng.choice(65553, 2000, replace=False)] = -0.0
+    ties = np.full(98310, 0.75, np.float32)
+    ties[rng.choice(98310, 20000, replace=False)] = 2.0
+    cases = [
+        rng.standard_normal(131072).astype(np.float32),
+        rng.integers(0, 40, 32769).astype(np.float32),                # 1 candidate in the second run
+        rng.standard_normal(500).astype(np.float32),                  # L <= B
+        rng.standard_normal(32768).astype(np.float32),                # one run
+        special,
+        ties,                                                         # ties across three runs
+        np.zeros(0, np.float32),                                      # empty
+    ]
+    for budget, window in ((3840, 256), (1000, 0), (4097, 4096), (8200, 8), (8201, 8), (2048, 2048)):
+        log(f"two-stage selection B={budget} W={window}")
+        _select_case(cases, budget, window)
 
 
 # ---------------------------------------------------------------------------------------
