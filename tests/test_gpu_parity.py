@@ -977,19 +977,25 @@ def test_longest_supported_unit_sampled():
 
 # ---------------------------------------------------------------------------------------
 # the three calls captured in a HIP graph: the library allocates nothing and issues no
-# memsets, so a captured pass replays to the eager results
+# memsets, so a captured pass replays to the eager results (also with scoring and selection
+# in one launch, and with the two-stage selection of units over 32768 slots, whose
+# workspace is allocated before the capture)
 # ---------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("paged", [False, True])
-def test_graph_capture_replays_match_eager(paged):
+@pytest.mark.parametrize("mode", ["dense", "paged", "fused", "long"])
+def test_graph_capture_replays_match_eager(mode):
+    paged = mode == "paged"
     if paged:
         w = W.scaled(W.WORKLOADS["paged_ragged64_bf16"], name="graph_paged", n_seq=3, n_layer=2, n_kvh=2,
                      max_len=3000, len_range=(16, 3000), budget=512, window=32)
         lengths = [3000, 700, 2049]
+    elif mode == "long":
+        w = W.scaled(BASE, name="graph_long", n_seq=2, n_layer=1, n_kvh=2, max_len=40000, budget=2048, window=64)
+        lengths = [40000, 33000]
     else:
         w = W.scaled(BASE, name="graph_dense", n_seq=2, n_layer=2, n_kvh=2, max_len=2500, budget=400, window=32)
         lengths = [2500, 1333]
-    log(f"graph capture, {'paged (in place)' if paged else 'dense'} lengths={lengths}")
+    log(f"graph capture, {mode} lengths={lengths}")
     dw = SD.build(w, hp=W.make_params(w, lengths=lengths))
     kv = dw.kv()
     dev = dw.k.device
@@ -1008,10 +1014,19 @@ def test_graph_capture_replays_match_eager(paged):
         v_out = torch.empty_like(k_out)
         freed = n_freed = None
 
+    sel_ws = tri.select_workspace(scores, kv, w.budget, w.window, kept, kept_n)
+    assert (sel_ws is not None) == (mode == "long")
+
     def one_pass(stream):
-        tri.tri_score_keys(kv, dw.center, dw.mean_abs, rope_base=w.base, offsets=w.offsets, group=w.group,
-                           reduce=w.reduce, scores=scores, stream=stream)
-        tri.tri_select_topb(scores, kv, w.budget, w.window, kept=kept, kept_n=kept_n, stream=stream)
+        if mode == "fused":
+            tri.tri_score_select(kv, dw.center, dw.mean_abs, w.budget, w.window, rope_base=w.base,
+                                 offsets=w.offsets, group=w.group, reduce=w.reduce, scores=scores, kept=kept,
+                                 kept_n=kept_n, stream=stream)
+        else:
+            tri.tri_score_keys(kv, dw.center, dw.mean_abs, rope_base=w.base, offsets=w.offsets, group=w.group,
+                               reduce=w.reduce, scores=scores, stream=stream)
+            tri.tri_select_topb(scores, kv, w.budget, w.window, kept=kept, kept_n=kept_n, stream=stream,
+                                workspace=sel_ws)
         tri.tri_compact_kv(kv, kept, kept_n, w.budget, k_out=k_out, v_out=v_out, pos_out=pos_out, freed=freed,
                            n_freed=n_freed, new_len=new_len, stream=stream)
 
