@@ -311,7 +311,7 @@ const char *tri_last_error(void);
 /* ABI version of this header: major * 10000 + minor * 100 + patch. */
 int tri_version(void);
 
-#define TRI_VERSION 10800
+#define TRI_VERSION 10900
 
 #ifdef __cplusplus
 }
