@@ -1,7 +1,8 @@
 // Key-scoring kernel of the TriAttention compression pass (gfx950), shared by the
 // translation units that instantiate it (score.hip / score_post.hip: pre-RoPE keys / keys
 // cached after RoPE, float32 or bfloat16; score_8bit.hip / score_post_8bit.hip: fp8 and
-// int8 codes; score_*mult*.hip: the same for the multiplicative form).
+// int8 codes; score_*mult*.hip: the same for the multiplicative form; score_pos*.hip: keys
+// at explicit positions; score_select*.hip: scoring fused with the selection, FUSE below).
 //
 // What it computes (per unit = sequence s, layer l, KV head h; key slot j at position p_j;
 // query heads hq of the group with centre c_f = E[q_f] and m_f = E|q_f|):

@@ -136,7 +136,7 @@ SMALL_DENSE = {
                                    window=1, low_r_frac=0.5), [2049]),
     "g6_max_half_bf16_short": (dict(n_seq=3, n_layer=1, n_kvh=1, group=6, max_len=900, budget=64,
                                     window=16), [900, 1, 65]),
-    # G = 6..8 with bf16 keys run on the matrix-core kernel: several 256-key chunks, tails that
+    # G = 4..8 with bf16 keys run on the matrix-core kernel: several 224-key chunks, tails that
     # are not a multiple of its 16-key step, interleaved layout
     "g7_max_interleaved_bf16": (dict(n_seq=2, n_layer=2, n_kvh=1, group=7, layout="interleaved", max_len=2300,
                                      budget=333, window=20), [2300, 1201]),
