@@ -68,7 +68,9 @@ def use_fused(mode: str, w, n_cu: int, key_space="pre", form="additive", positio
     faster than the two launches.  It saves writing the scores and reading them back, which costs
     most when scoring is bound by the key stream (one effective head: the mean reduction or
     G = 1), and a workgroup per unit only balances when every CU gets many units (at the 32K
-    pass, 288 units on 256 CUs, 32 CUs score two whole units)."""
+    pass, 288 units on 256 CUs, 32 CUs score two whole units) or when the units are so few and
+    short that the two-launch path gives each at most one workgroup too (the 2K single-head
+    pass: one launch less and a smaller phase table)."""
     ok = fused_applies(w, key_space, form, positions)
     if mode == "on":
         if not ok:
@@ -77,7 +79,13 @@ def use_fused(mode: str, w, n_cu: int, key_space="pre", form="additive", positio
     if mode == "off" or not ok:
         return False
     g_eff = 1 if w.reduce == "mean" else w.group
-    return g_eff == 1 and w.n_units >= 8 * n_cu
+    if g_eff == 1 and w.n_units >= 8 * n_cu:         # many units per CU, bound by the key stream
+        return True
+    # few short units: the persistent scoring grid would give no unit more than one workgroup
+    # either (one per 256 8-key steps, at most one per CU), and every unit gets its own CU
+    slots = w.max_pages * 16 if w.paged else w.max_len
+    grid = min(n_cu, -(-w.n_units * (-(-slots // 8)) // (32 * 8)))
+    return grid <= w.n_units <= n_cu
 
 
 def score_kernel_used(w, key_space: str, form: str, positions: bool) -> str:
