@@ -1,5 +1,6 @@
-// Top-B selection kernel of the TriAttention compression pass (gfx950): one workgroup per
-// unit; the selection itself is in select_core.h.
+// Top-B selection kernels of the TriAttention compression pass (gfx950): one workgroup per
+// unit, or, for units longer than the register capacity and a caller's workspace, two stages
+// over many workgroups (below); the selection itself is in select_core.h.
 #include <algorithm>
 
 #include "select_core.h"

@@ -10,9 +10,10 @@
 //
 // Scores map to order-preserving 32-bit keys (NaN and -inf to the lowest candidate key, -0
 // to +0).  Each wave of a 1024-thread workgroup owns a contiguous range of slots, four
-// consecutive slots per lane; a unit of up to 32768 slots is read from memory once into
-// registers (2048 slots per wave), longer units re-read their scores on every sweep.  The threshold is
-// found by refining linear histograms instead of sorting:
+// consecutive slots per lane; up to 32768 values are read from memory (or LDS) once into
+// registers (2048 per wave), longer inputs are re-read on every sweep (select.hip can instead
+// split them into register-resident runs).  The threshold is found by refining linear
+// histograms instead of sorting:
 //   level 1: 2048 bins spanning [min, max] of the candidate keys, counted in four copies (lane
 //            l adds into copy l % 4, so lanes of one instruction that hit the same bin mostly
 //            hit different LDS words; a lane adds a run of its slots in one bin at once) and
