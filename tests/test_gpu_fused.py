@@ -147,3 +147,36 @@ def test_fused_full_size(name, units):
         worst = max(worst, check_unit(dw, s, l, h, scores[s, l, h].cpu().numpy(), kept[s, l, h].cpu().numpy(),
                                       int(kept_n[s].item())))
     log(f"  max score error / bound = {worst:.3e}")
+
+
+def test_fused_explicit_query_positions():
+    # the newest query ahead of the cache and behind it (query_pos given), max over 4 heads and
+    # the mean over them
+    import oracle
+    for reduce in ("max", "mean"):
+        w = W.scaled(BASE, name=f"fused_qpos_{reduce}", n_seq=3, n_layer=1, n_kvh=2, group=4, reduce=reduce,
+                     max_len=1500, budget=256, window=16)
+        lengths = [1500, 900, 1200]
+        qpos = [1500 + 3000, 950, 700]
+        hp = W.make_params(w, lengths=lengths)
+        log(f"fused, explicit query positions {qpos} (lengths {lengths}), reduce {reduce}")
+        dw = SD.build(w, hp=hp)
+        kv = dw.kv()
+        q = torch.tensor(qpos, dtype=torch.int64, device="cuda")
+        scores = torch.full((w.n_seq, w.n_layer, w.n_kvh, kv.slots), float("nan"), device="cuda")
+        kept, kept_n = tri.tri_score_select(kv, dw.center, dw.mean_abs, w.budget, w.window, rope_base=w.base,
+                                            offsets=w.offsets, group=w.group, reduce=w.reduce, query_pos=q,
+                                            scores=scores)
+        torch.cuda.synchronize()
+        check_against_select(dw, kv, scores, kept, kept_n)
+        sc, kp = scores.cpu().numpy(), kept.cpu().numpy()
+        for s in range(w.n_seq):
+            L = lengths[s]
+            for h in range(w.n_kvh):
+                keys = P.host_rows(w, hp, s, 0, h)
+                center, mean_abs = oracle.unit_heads(hp.center, hp.mean_abs, 0, h, w.group)
+                orc = oracle.score_keys(keys, center, mean_abs, base=w.base, offsets=w.offsets, query_pos=qpos[s],
+                                        layout=w.layout, reduce=w.reduce)
+                S = oracle.score_magnitude_bound(keys, center, mean_abs, layout=w.layout, reduce=w.reduce)
+                P.check_scores(sc[s, 0, h, :L], orc, S)
+                P.check_kept(kp[s, 0, h], sc[s, 0, h], orc, S, L, w.budget, w.window)
