@@ -243,6 +243,8 @@ int main(void) {
          offsetof(tri_score_cfg, key_space), offsetof(tri_score_cfg, form));
   printf("%d %d %d\n", tri_version(), tri_score_keys(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL),
          TRI_VERSION);
+  printf("%d %d\n", tri_score_select(NULL, NULL, NULL, NULL, NULL, 1, 0, NULL, NULL, NULL, NULL, NULL, NULL),
+         tri_select_topb(NULL, NULL, 1, 0, NULL, NULL, NULL, NULL, NULL));
   return 0;
 }
 ''')
@@ -261,6 +263,7 @@ int main(void) {
                         ctypes.sizeof(C)]
     assert lines[1] == [C.offsets.offset, C.group.offset, C.key_space.offset, C.form.offset]
     assert lines[2][0] == lines[2][2] and lines[2][1] == _abi.TRI_EINVAL
+    assert lines[3] == [_abi.TRI_EINVAL, _abi.TRI_EINVAL]
 
 
 def test_decode_attention_validation():
