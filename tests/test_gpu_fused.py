@@ -180,3 +180,44 @@ def test_fused_explicit_query_positions():
                 S = oracle.score_magnitude_bound(keys, center, mean_abs, layout=w.layout, reduce=w.reduce)
                 P.check_scores(sc[s, 0, h, :L], orc, S)
                 P.check_kept(kp[s, 0, h], sc[s, 0, h], orc, S, L, w.budget, w.window)
+
+
+def _fused_random_case(seed):
+    rng = np.random.default_rng(2000 + seed)
+    paged = bool(rng.integers(2))
+    over = dict(name=f"fmix{seed}", n_seq=int(rng.integers(1, 4)), n_layer=int(rng.integers(1, 3)),
+                n_kvh=int(rng.integers(1, 3)), group=int(rng.integers(1, 9)), dtype=["f32", "bf16"][rng.integers(2)],
+                layout=["half", "interleaved"][rng.integers(2)], reduce=["max", "mean"][rng.integers(2)],
+                max_len=int(rng.integers(300, 2600)), budget=int(16 * rng.integers(2, 40)),
+                window=int(rng.integers(0, 200)), base=float([1e4, 5e5, 1e6][rng.integers(3)]),
+                offsets=W.geometric_offsets(int(rng.integers(0, 15))), seed=int(80 + seed),
+                low_r_frac=float(rng.uniform(0, 0.5)), sink=bool(rng.integers(2)))
+    if paged:
+        w = W.scaled(W.WORKLOADS["paged_ragged64_bf16"], len_range=(1, over["max_len"]), **over)
+    else:
+        w = W.scaled(BASE, **over)
+    lengths = [int(x) for x in rng.integers(0, w.max_len + 1, w.n_seq)]
+    lengths[int(rng.integers(w.n_seq))] = w.max_len
+    return w, lengths
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_fused_random_option_mix(seed):
+    w, lengths = _fused_random_case(seed)
+    log(f"fused mix {seed}: {w.dtype} {'paged' if w.paged else 'dense'} {w.layout} G={w.group} {w.reduce} "
+        f"B={w.budget} W={w.window} |D|={len(w.offsets)} base={w.base:g} lengths={lengths}")
+    dw = SD.build(w, hp=W.make_params(w, lengths=lengths))
+    kv, scores, kept, kept_n = fused(dw)
+    check_against_select(dw, kv, scores, kept, kept_n)
+    sc, kp, kn = scores.cpu().numpy(), kept.cpu().numpy(), kept_n.cpu().numpy()
+    for s in range(w.n_seq):
+        L = lengths[s]
+        for l in range(w.n_layer):
+            for h in range(w.n_kvh):
+                keys = P.host_rows(w, dw.hp, s, l, h)
+                orc, S = P.oracle_scores(w, dw.hp, s, l, h, keys)
+                live = S > 0
+                P.check_scores(sc[s, l, h, :L][live], orc[live], S[live])
+                assert np.all(sc[s, l, h, :L][~live] == 0.0)
+                P.check_kept(kp[s, l, h], sc[s, l, h], orc, S, L, w.budget, w.window)
+                assert kn[s] == min(L, w.budget)
