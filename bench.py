@@ -465,7 +465,7 @@ def config_entry(m, fused=False):
     ms = m["ms"]
     return {
         "value": m["keys_per_step"] / (ms * 1e-3) / 1e9, "unit": "Gkeys/s", "ms_per_step": ms,
-        "steps": m["steps"], "warmup": m["warmup"],
+        "steps": m["steps"], "warmup": m["warmup"], "clock_preroll_ms": round(m["preroll"]["ms"], 1),
         "pass_hbm_frac": m["pass_bytes"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "score_kernel_hbm_frac": m["score_bytes"] / (m["score_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "score_ms": m["score_ms"], "select_ms": m["select_ms"], "compact_ms": m["compact_ms"],
@@ -587,10 +587,10 @@ def main():
     }
     if m["consumer"] is not None:
         line["consumer"] = m["consumer"]
-    # The other stated workloads, each timed in this run after the headline (same protocol:
-    # untimed warmup passes, then exactly the given number of timed passes; the paged pools are
-    # refilled before every pass, outside the timed region).  Their pass counts are capped so
-    # that the default run stays within a few minutes.
+    # The other stated workloads, each timed in this run after the headline (same protocol: the
+    # untimed clock pre-roll and warmup passes, then exactly the given number of timed passes;
+    # the paged pools are refilled before every pass, outside the timed region).  Their pass
+    # counts are capped so that the default run stays within a few minutes.
     if not args.workload and not args.no_configs and args.key_space == "pre" and args.form == "additive" \
             and not args.positions and args.fused != "on":
         configs = {}
@@ -601,7 +601,7 @@ def main():
             k = min(args.steps, 20 if paged else 200)
             wu = min(args.warmup, 5 if paged else 50)
             fo = use_fused(args.fused, W.WORKLOADS[other], n_cu)
-            configs[other] = config_entry(measure(args, other, max(k, 1), wu, fused=fo), fo)
+            configs[other] = config_entry(measure(args, other, max(k, 1), wu, preroll_ms=args.preroll_ms, fused=fo), fo)
         line["configs"] = configs
     _, copy_gbs = copy_bandwidth(1024)
     line["pass"]["copy_GBps"] = copy_gbs
