@@ -24,6 +24,8 @@ __all__ = [
     "KVCache",
     "TriError",
     "tri_calibrate_stats",
+    "save_stats",
+    "load_stats",
     "tri_score_keys",
     "tri_select_topb",
     "select_workspace",
@@ -197,6 +199,42 @@ def tri_calibrate_stats(q, rope_layout: str = "half", center=None, mean_abs=None
     _abi.check(L.tri_calibrate_stats(_ptr(q), _dtype_code(q), n, n_layer, n_qh, d, _LAYOUTS[rope_layout],
                                      _ptr(center), _ptr(mean_abs), None, None, _stream(stream)))
     return center, mean_abs
+
+
+def save_stats(path, center, mean_abs, *, rope_base: float, rope_layout: str = "half"):
+    """Write calibration statistics to an .npz file (arrays and their RoPE settings only; the
+    statistics belong to one model and its RoPE base and pair layout: "TriAttention:
+    trigonometric KV cache compression for long reasoning", section "Calibration statistics are
+    tied to a specific model")."""
+    import numpy as np
+    if rope_layout not in _LAYOUTS:
+        raise ValueError(f"unknown rope layout {rope_layout!r}")
+    c = center.detach().float().cpu().numpy()
+    m = mean_abs.detach().float().cpu().numpy()
+    if c.ndim != 4 or c.shape[-1] != 2 or m.shape != c.shape[:3]:
+        raise ValueError("center must be [n_layer, n_qh, F, 2] and mean_abs [n_layer, n_qh, F]")
+    np.savez(path, center=c, mean_abs=m, rope_base=np.float64(rope_base), head_dim=np.int64(2 * c.shape[2]),
+             rope_layout=np.str_(rope_layout))
+
+
+def load_stats(path, *, device="cuda", rope_base=None, rope_layout=None, n_layer=None, n_qh=None):
+    """Read statistics written by save_stats: (center, mean_abs, rope_base, rope_layout), the
+    arrays as float32 tensors on `device`.  Any of rope_base, rope_layout, n_layer, n_qh given
+    must match the file (ValueError otherwise): statistics of another model or RoPE setting
+    would pick the wrong keys without any other error."""
+    import numpy as np
+    torch = _torch()
+    with np.load(path, allow_pickle=False) as f:
+        c, m = f["center"], f["mean_abs"]
+        base, layout, hd = float(f["rope_base"]), str(f["rope_layout"]), int(f["head_dim"])
+    if c.ndim != 4 or c.shape[-1] != 2 or m.shape != c.shape[:3] or hd != 2 * c.shape[2]:
+        raise ValueError(f"{path}: malformed statistics (center {c.shape}, mean_abs {m.shape}, head_dim {hd})")
+    for name, want, got in (("rope_base", rope_base, base), ("rope_layout", rope_layout, layout),
+                            ("n_layer", n_layer, c.shape[0]), ("n_qh", n_qh, c.shape[1])):
+        if want is not None and want != got:
+            raise ValueError(f"{path}: statistics have {name} {got!r}, expected {want!r}")
+    return (torch.from_numpy(np.ascontiguousarray(c, np.float32)).to(device),
+            torch.from_numpy(np.ascontiguousarray(m, np.float32)).to(device), base, layout)
 
 
 _KEY_SPACES = {"pre": _abi.TRI_KEYS_PRE_ROPE, "post": _abi.TRI_KEYS_POST_ROPE}
