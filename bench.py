@@ -294,8 +294,10 @@ def consumer(args, w, dw, kv, kept_n, new_len, k_out, v_out, pos_out, reps=20):
     q = torch.from_numpy(rng.standard_normal((w.n_seq, w.n_layer, w.n_qh, w.head_dim)).astype(np.float32)).cuda()
     qpos = dw.seq_len.to(torch.int64)
     out = torch.empty_like(q)
-    run = lambda: tri.tri_decode_attention(cache, q, qpos, rope_base=w.base, group=w.group, pos=pos,
-                                           rope_layout=w.layout, key_space=args.key_space, out=out)
+    # the entry point without allocation: the same kernels and split as with a workspace, and
+    # one library call per attention (no workspace query or allocation on the host)
+    run = lambda: tri.tri_decode_attention_noalloc(cache, q, qpos, rope_base=w.base, group=w.group, pos=pos,
+                                                   rope_layout=w.layout, key_space=args.key_space, out=out)
     for _ in range(3):
         run()
     torch.cuda.synchronize()

@@ -276,10 +276,11 @@ int tri_compact_kv(const tri_kv *kv, const int32_t *kept, const int32_t *kept_n,
  *               softmax_j((R(Q) q) . (R(p_j) k_j) / sqrt(head_dim)) weighted sum of v_j over
  *               the seq_len[s] cached keys (zeros when there are none).
  *   ws, ws_bytes: optional workspace (convention above).  Without one (ws_bytes == NULL)
- *               each (sequence, layer, KV head) is one workgroup.  With one, shapes with few
- *               units split their slots over several workgroups and merge the partial softmax
- *               states in a second kernel; the size query returns 0 when the shape is not
- *               split.  A workspace smaller than the query's answer: TRI_EWORKSPACE.  The
+ *               each (sequence, layer, KV head) is one workgroup.  With one, shapes with
+ *               fewer than 1024 (sequence, layer, KV head, pass of 4 heads) groups split their
+ *               slots over 2-16 workgroups (a power of two, >= 128 slots each) and merge the
+ *               partial softmax states in a second kernel; the size query returns 0 when the
+ *               shape is not split, and never more than 4.3 MB.  A workspace smaller than the query's answer: TRI_EWORKSPACE.  The
  *               results of the two paths agree to float32 rounding (the summation order
  *               differs).
  * Errors as for the other calls. */
@@ -295,7 +296,8 @@ int tri_decode_attention(const tri_kv *kv, int32_t layer0, int32_t n_layers, con
  *     device memory, 8 MiB per GPU, until the process ends (it is set up on the first call
  *     on each device); nothing is allocated or freed by the call;
  *   - a shape whose split needs more than those 8 MiB (tri_decode_attention's workspace size
- *     query returns the need) is refused with TRI_EWORKSPACE before anything is launched;
+ *     query returns the need) is refused with TRI_EWORKSPACE before anything is launched; the
+ *     split rule above keeps every need under 4.3 MB, so this is a guard;
  *   - every call on one GPU shares that GPU's scratch: calls that overlap on one GPU (other
  *     streams or threads) race on it and must be serialised by the caller.  Each call writes
  *     every scratch entry it reads, so nothing has to be cleared between calls. */

@@ -479,7 +479,8 @@ def tri_decode_attention_noalloc(kv: KVCache, q, query_pos, *, rope_base: float,
                                  layer0: int = 0, n_layers=None, rope_layout: str = "half", key_space: str = "pre",
                                  stream=None):
     """tri_decode_attention that allocates nothing: split shapes keep their partial results in
-    the library's static per-GPU scratch (8 MiB; larger needs raise TriError TRI_EWORKSPACE).
+    the library's static per-GPU scratch (8 MiB; the split rule keeps every need under 4.3 MB,
+    and a larger one would raise TriError TRI_EWORKSPACE).
     out must be given.  Calls that overlap on one GPU race on the scratch."""
     args, out, _desc = _attention_args(kv, q, query_pos, rope_base, group, pos, layer0, n_layers, rope_layout,
                                        key_space, out, False)

@@ -143,18 +143,17 @@ struct DecodeParams {
   // n_split == 1: one workgroup writes out directly (no workspace).
   int32_t n_split;
   int64_t split_len;            // multiple of 64
-  float* part_ml;               // [units * n_pass][n_split][4][2]   (running max, sum)
+  float* part_ml;               // [units * n_pass][n_split][4][2]   (reference max, base 2; sum)
   float* part_acc;              // [units * n_pass][n_split][4][128] (unnormalised value sums)
 };
-// Slot splits for the attention kernel.  Its workgroups hold more than 128 VGPRs per lane,
-// so a CU runs one at a time and the kernel takes ceil(groups / kDecodeCUs) rounds.  The
-// split count minimises rounds x (per-workgroup cost + slots per split), plus the merge
-// kernel when split; costs in slot-equivalents, fitted to same-process timings on MI355X
-// (256 CUs): about 190 slots of fixed work per workgroup, about 260 for the merge.
+// Slot splits for the attention kernel.  A CU holds four of its (bfloat16) workgroups at once;
+// the kernel streams best with several per CU, so groups are split (a power of two ways)
+// until every CU has kDecodeMinGroupsPerCU of them, keeping kDecodeMinSplitLen slots or more
+// per split (fitted to same-process timings on MI355X, 256 CUs).  The partial states then
+// stay under 2 * 4 * 256 groups x 4 heads x 520 bytes (4.3 MB).
 constexpr int kDecodeCUs = 256;
-constexpr int kDecodeGroupCost = 192;
-constexpr int kDecodeMergeCost = 256;
-constexpr int kDecodeMinSplitLen = 64;
+constexpr int kDecodeMinGroupsPerCU = 4;
+constexpr int kDecodeMinSplitLen = 128;
 constexpr int kDecodeMaxSplits = 16;
 constexpr int kDecodeHeadsPerPass = 4;
 // slot splits the attention kernel uses for this many (sequence, layer, KV head, pass)

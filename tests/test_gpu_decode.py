@@ -68,8 +68,8 @@ def as_float(bits, dtype):
                                                           ("bf16", "interleaved", "post", 2),
                                                           ("f32", "half", "post", 8)])
 def test_attention_dense(dtype, layout, key_space, group, workspace):
-    # workspace "auto": the units split their 1300 slots over 10-16 workgroups each (splits past
-    # a unit's length, and a unit with no keys, included); None: one workgroup per unit
+    # workspace "auto": the units split their 1300 slots over 8 workgroups each (splits past a
+    # unit's length, and a unit with no keys, included); None: one workgroup per unit
     w = W.scaled(W.WORKLOADS["gqa8b_32k_bf16"], name="att", n_seq=3, n_layer=2, n_kvh=2, group=group, dtype=dtype,
                  layout=layout, max_len=1300)
     lengths = [1300, 517, 0]

@@ -4,8 +4,9 @@ tri_decode_attention_noalloc keeps the partial softmax states of a split shape i
 library's static per-GPU scratch instead of a caller workspace.  Two calls in a row over the
 same scratch, the second on a smaller input with another split count (and a third that is
 not split at all), must each equal tri_decode_attention with a workspace bit for bit (the
-same kernels and the same split), and agree with the oracle.  A shape whose split would
-need more than the scratch is refused before any launch (tests/test_abi.py).
+same kernels and the same split), and agree with the oracle.  The split rule keeps the
+partial states of every shape under the scratch (tests/test_abi.py checks the bound); a
+larger need would be refused before any launch.
 """
 
 import ctypes
@@ -77,7 +78,7 @@ def test_noalloc_equals_the_workspace_entry_point_on_consecutive_calls():
         # 4 unit passes of 4000 slots: split 16 ways
         dict(name="noalloc_a", n_layer=2, n_kvh=2, group=4, dtype="bf16", layout="half", key_space="pre",
              max_len=4000, lengths=[4000], seed=71),
-        # smaller: 2 units, 2 passes each (G = 7), 700 slots (split 10 ways), float32 interleaved,
+        # smaller: 2 units, 2 passes each (G = 7), 700 slots (split 4 ways), float32 interleaved,
         # post-RoPE keys
         dict(name="noalloc_b", n_layer=1, n_kvh=2, group=7, dtype="f32", layout="interleaved", key_space="post",
              max_len=700, lengths=[700], seed=72),
