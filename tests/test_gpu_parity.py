@@ -431,6 +431,36 @@ def test_calibration_parity(dtype, layout):
 # full-size workloads, sampled units
 # ---------------------------------------------------------------------------------------
 
+ATT_TOL = 2e-3     # |out_gpu - out_oracle| <= ATT_TOL * max_j |v_j| (per query head)
+
+
+def _check_consumer(w, hp, cache, kept, picks, pos, seed):
+    """Attention of a new query of every sequence over the cache the pass compressed, as
+    bench.py times it (the no-allocation entry point: the same kernels and slot split as with a
+    workspace), against the oracle on sampled (sequence, layer, KV head) units."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((w.n_seq, w.n_layer, w.n_qh, w.head_dim)).astype(np.float32)
+    qpos = np.asarray(hp.lengths, np.int64)                 # the next token of each sequence
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    tri.tri_decode_attention_noalloc(cache, torch.from_numpy(q).cuda(), torch.from_numpy(qpos).cuda(),
+                                     rope_base=w.base, group=w.group, pos=pos, rope_layout=w.layout, out=out)
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got)), "non-finite attention output"
+    g = w.group
+    worst = 0.0
+    for s, l, h in picks:
+        n = min(int(hp.lengths[s]), w.budget)
+        kk = kept[s, l, h, :n]
+        k = P.host_rows(w, hp, s, l, h)[kk]
+        v = P.host_rows(w, hp, s, l, h, tag=synth.TAG_V)[kk]
+        want = oracle.decode_attention(q[s, l, h * g:(h + 1) * g], k, v, base=w.base, key_pos=kk,
+                                       query_pos=int(qpos[s]), layout=w.layout)
+        err = float(np.abs(got[s, l, h * g:(h + 1) * g] - want).max()) / max(float(np.abs(v).max()), 1e-30)
+        assert err <= ATT_TOL, f"attention (seq {s}, layer {l}, head {h}): error {err:.3e} of max |v|"
+        worst = max(worst, err)
+    log(f"  attention over the compressed cache, {len(picks)} sampled units: max error / max|v| = {worst:.3e}")
+
+
 def _full_dense(name, units, key_space="pre"):
     w = W.WORKLOADS[name]
     log(f"full size {name}: building")
@@ -438,6 +468,11 @@ def _full_dense(name, units, key_space="pre"):
     log(f"full size {name}: running the pass (keys {key_space}-RoPE)")
     scores, kept, kept_n, out = run_pass(dw, key_space)
     kn = kept_n.cpu().numpy()
+    if out["v_out"] is not None and key_space == "pre" and w.dtype in ("f32", "bf16"):
+        log(f"full size {name}: attention over the compressed cache")
+        cache = tri.KVCache.dense(out["k_out"], out["v_out"], out["new_len"])
+        _check_consumer(w, dw.hp, cache, kept.cpu().numpy(), [W.unit_coords(w, u) for u in units],
+                        out["pos_out"], seed=200 + len(units))
     worst = 0.0
     for u in units:
         s, l, h = W.unit_coords(w, u)
@@ -560,6 +595,13 @@ def test_full_paged_ragged64_bf16():
         assert np.array_equal(packed_v, hv[kp_h[:n]])
         want_freed = hp.block_table[s, -(-n // 16): -(-L // 16)]
         assert nf[s] == len(want_freed) and np.array_equal(freed[s, : nf[s]], want_freed)
+    # attention over the pool packed in place, with the kept keys' positions at the pool's slot
+    # stride (as bench.py runs it)
+    log("full size paged_ragged64_bf16: attention over the compressed cache")
+    pos = torch.zeros((w.n_seq, w.n_layer, w.n_kvh, dw.kv().slots), dtype=torch.int32, device="cuda")
+    pos[..., :w.budget] = out["pos_out"]
+    cache = tri.KVCache.paged(dw.k, dw.v, dw.block_table, out["new_len"], pos=pos)
+    _check_consumer(w, hp, cache, kept.cpu().numpy(), picks, pos, seed=210)
     # freed-page accounting over the whole batch
     total_before = int(sum(-(-int(L) // 16) for L in hp.lengths))
     total_after = int(sum(-(-min(int(L), w.budget) // 16) for L in hp.lengths))
