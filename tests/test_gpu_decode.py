@@ -98,6 +98,44 @@ def test_attention_dense(dtype, layout, key_space, group, workspace):
     log(f"  max attention error / max|v| = {worst:.3e}")
 
 
+@pytest.mark.parametrize("workspace", ["auto", None])
+@pytest.mark.parametrize("dtype,layout,key_space,group", [("f32", "interleaved", "pre", 3),
+                                                          ("bf16", "interleaved", "post", 8),
+                                                          ("f32", "half", "post", 5), ("bf16", "half", "pre", 6)])
+def test_attention_paged(dtype, layout, key_space, group, workspace):
+    # a paged pool (pages at a random permutation of the pool), positions = slots; lengths
+    # that end inside a page, one page, and no keys; with the workspace the units split their
+    # slots (splits past a unit's length included), without it one workgroup per unit
+    w = W.scaled(W.WORKLOADS["paged_ragged64_bf16"], name="att_paged", n_seq=4, n_layer=2, n_kvh=2, group=group,
+                 dtype=dtype, layout=layout, max_len=1300, len_range=(1, 1300))
+    lengths = [1300, 517, 0, 16]
+    hp = W.make_params(w, lengths=lengths)
+    log(f"attention paged {dtype} {layout} keys {key_space}-RoPE G={group} lengths={lengths} workspace={workspace}")
+    dw = SD.build(w, hp=hp)
+    kv = dw.kv()
+    assert kv.layout == "paged"
+    rng = np.random.default_rng(63)
+    n_qh = w.n_kvh * group
+    q = rng.standard_normal((w.n_seq, w.n_layer, n_qh, 128)).astype(np.float32)
+    qpos = np.array([1300 + 7, 517 + 300, 5, 16], np.int64)
+    out = tri.tri_decode_attention(kv, torch.from_numpy(q).cuda(), torch.from_numpy(qpos).cuda(),
+                                   rope_base=w.base, group=group, rope_layout=layout, key_space=key_space,
+                                   workspace=workspace)
+    out = out.cpu().numpy()
+    worst = 0.0
+    for s in range(w.n_seq):
+        L = lengths[s]
+        for l in range(w.n_layer):
+            for h in range(w.n_kvh):
+                k = as_float(unit_rows(w, hp, s, l, h, L), dtype)
+                v = as_float(unit_rows(w, hp, s, l, h, L, synth.TAG_V), dtype)
+                want = oracle.decode_attention(q[s, l, h * group:(h + 1) * group], k, v, base=w.base,
+                                               key_pos=np.arange(L), query_pos=int(qpos[s]), layout=layout,
+                                               key_space=key_space)
+                worst = max(worst, check_attention(out[s, l, h * group:(h + 1) * group], want, v))
+    log(f"  max attention error / max|v| = {worst:.3e}")
+
+
 def test_attention_over_a_compressed_cache():
     # compress a dense cache, then attend over k_out / v_out with the kept keys' positions
     w = W.scaled(W.WORKLOADS["gqa8b_32k_bf16"], name="att_comp", n_seq=2, n_layer=2, n_kvh=2, max_len=3000,
