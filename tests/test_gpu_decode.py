@@ -136,6 +136,58 @@ def test_attention_paged(dtype, layout, key_space, group, workspace):
     log(f"  max attention error / max|v| = {worst:.3e}")
 
 
+@pytest.mark.parametrize("paged,group", [(False, 4), (True, 7)])
+def test_noalloc_attention_under_graph_capture(paged, group):
+    # the no-allocation entry point captured in a HIP graph (its intended caller); every replay,
+    # after eager calls that reuse the static scratch with other queries, equals the eager call
+    name = "paged_ragged64_bf16" if paged else "gqa8b_32k_bf16"
+    extra = dict(len_range=(1, 3000)) if paged else {}
+    w = W.scaled(W.WORKLOADS[name], name="att_graph", n_seq=2, n_layer=2, n_kvh=2, group=group, max_len=3000,
+                 **extra)
+    lengths = [3000, 1111]
+    hp = W.make_params(w, lengths=lengths)
+    log(f"no-allocation attention under graph capture, paged={paged} G={group} lengths={lengths}")
+    dw = SD.build(w, hp=hp)
+    kv = dw.kv()
+    rng = np.random.default_rng(64)
+    n_qh = w.n_kvh * group
+    q = torch.from_numpy(rng.standard_normal((w.n_seq, w.n_layer, n_qh, 128)).astype(np.float32)).cuda()
+    q_other = torch.from_numpy(rng.standard_normal((w.n_seq, w.n_layer, n_qh, 128)).astype(np.float32)).cuda()
+    qpos = torch.tensor([3000 + 5, 1111], dtype=torch.int64, device="cuda")
+    out = torch.empty_like(q)
+    out_other = torch.empty_like(q)
+
+    def call(stream, qq, oo):
+        tri.tri_decode_attention_noalloc(kv, qq, qpos, rope_base=w.base, group=group, out=oo, stream=stream)
+
+    call(None, q, out)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            call(side, q, out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        call(None, q_other, out_other)     # eager work that rewrites the static scratch
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), f"replay {rep} differs from the eager call"
+    # and the eager result itself against the oracle on one unit per sequence
+    got = ref.cpu().numpy()
+    for s, L in enumerate(lengths):
+        k = as_float(unit_rows(w, hp, s, 1, 1, L), w.dtype)
+        v = as_float(unit_rows(w, hp, s, 1, 1, L, synth.TAG_V), w.dtype)
+        want = oracle.decode_attention(q.cpu().numpy()[s, 1, group:2 * group], k, v, base=w.base,
+                                       key_pos=np.arange(L), query_pos=int(qpos[s]), layout=w.layout)
+        check_attention(got[s, 1, group:2 * group], want, v)
+
+
 def test_attention_over_a_compressed_cache():
     # compress a dense cache, then attend over k_out / v_out with the kept keys' positions
     w = W.scaled(W.WORKLOADS["gqa8b_32k_bf16"], name="att_comp", n_seq=2, n_layer=2, n_kvh=2, max_len=3000,
