@@ -112,7 +112,9 @@ def parse():
     ap.add_argument("--positions", action="store_true",
                     help="give the cache explicit key positions (slot index), scored without the phase table")
     ap.add_argument("--consumer", action="store_true",
-                    help="also time attention of a new token over the compressed cache (tri_decode_attention)")
+                    help="time attention of a new token over the compressed cache (the default; kept for scripts)")
+    ap.add_argument("--no-consumer", action="store_true",
+                    help="skip timing attention over the compressed cache after each workload's timed passes")
     ap.add_argument("--key-space", choices=("pre", "post"), default="pre",
                     help="score the cache as pre-RoPE keys (default) or as keys already rotated by RoPE")
     ap.add_argument("--cpu-units", type=int, default=0,
@@ -477,6 +479,7 @@ def config_entry(m, fused=False):
         "shape": {"n_seq": w.n_seq, "n_layer": w.n_layer, "n_kv_heads": w.n_kvh, "group": w.group,
                   "context": w.max_len, "kv_dtype": w.dtype, "budget": w.budget, "window": w.window,
                   "reduce": w.reduce, "layout": "paged" if w.paged else "dense"},
+        **({"consumer": m["consumer"]} if m["consumer"] is not None else {}),
     }
 
 
@@ -515,7 +518,7 @@ def main():
     torch.cuda.set_device(0)
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     fused = use_fused(args.fused, W.WORKLOADS[name], n_cu, args.key_space, args.form, args.positions)
-    m = measure(args, name, args.steps, args.warmup, args.key_space, args.form, args.positions, args.consumer,
+    m = measure(args, name, args.steps, args.warmup, args.key_space, args.form, args.positions, not args.no_consumer,
                 args.preroll_ms, fused=fused)
     w = m["w"]
     ms, score_ms = m["ms"], m["score_ms"]
@@ -603,7 +606,8 @@ def main():
             k = min(args.steps, 20 if paged else 200)
             wu = min(args.warmup, 5 if paged else 50)
             fo = use_fused(args.fused, W.WORKLOADS[other], n_cu)
-            configs[other] = config_entry(measure(args, other, max(k, 1), wu, preroll_ms=args.preroll_ms, fused=fo), fo)
+            configs[other] = config_entry(measure(args, other, max(k, 1), wu, with_consumer=not args.no_consumer,
+                                                  preroll_ms=args.preroll_ms, fused=fo), fo)
         line["configs"] = configs
     _, copy_gbs = copy_bandwidth(1024)
     line["pass"]["copy_GBps"] = copy_gbs
