@@ -1,6 +1,7 @@
 """Summarize a rocprofv3 kernel-trace database of one bench.py run as markdown: per-kernel
-statistics, with the pass kernels (scoring, selection, compaction) attributed to the workload
-whose scoring kernel ran last (bench.py times one workload after another).
+statistics, with the pass kernels (scoring, selection, compaction) and the attention calls over
+the compressed cache attributed to the workload whose scoring kernel ran last (bench.py times
+one workload after another).
 
     python -m kv_cache_compression_tri_amd.profsum RESULTS_DB TITLE "COMMAND" [NOTE]
 """
@@ -18,7 +19,7 @@ PHASES = {
     "tri::score_mx_kernel<7, false, false>": "long_128k_bf16",
     "tri::score_mx_kernel<4, false, true>": "paged_ragged64_bf16",
 }
-PASS_PREFIXES = ("tri::score", "tri::select", "tri::compact")
+PASS_PREFIXES = ("tri::score", "tri::select", "tri::compact", "tri::decode")   # decode: the consumer calls
 
 
 def short(name: str) -> str:
