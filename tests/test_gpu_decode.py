@@ -188,6 +188,57 @@ def test_noalloc_attention_under_graph_capture(paged, group):
         check_attention(got[s, 1, group:2 * group], want, v)
 
 
+@pytest.mark.parametrize("paged", [False, True])
+def test_attention_over_a_layer_slice(paged):
+    # one layer at a time (as a decode loop calls it) and a slice of two layers: queries and
+    # outputs cover only the slice, keys, values and positions are read at the absolute layer;
+    # explicit positions (not the slot index), with and without the split workspace, and the
+    # no-allocation entry point
+    name = "paged_ragged64_bf16" if paged else "gqa8b_32k_bf16"
+    extra = dict(len_range=(1, 1500)) if paged else {}
+    w = W.scaled(W.WORKLOADS[name], name="att_slice", n_seq=2, n_layer=3, n_kvh=2, group=4, max_len=1500, **extra)
+    lengths = [1500, 611]
+    hp = W.make_params(w, lengths=lengths)
+    log(f"attention over layer slices, paged={paged} lengths={lengths}")
+    dw = SD.build(w, hp=hp)
+    kv0 = dw.kv()
+    slots = kv0.slots
+    rng = np.random.default_rng(65)
+    # strictly increasing positions with gaps, as a compacted cache holds them
+    pos_h = np.zeros((w.n_seq, w.n_layer, w.n_kvh, slots), np.int32)
+    for s, L in enumerate(lengths):
+        for l in range(w.n_layer):
+            for h in range(w.n_kvh):
+                pos_h[s, l, h, :L] = np.cumsum(rng.integers(1, 9, size=L))
+    pos = torch.from_numpy(pos_h).cuda()
+    kv = tri.KVCache.paged(dw.k, dw.v, dw.block_table, dw.seq_len, pos=pos) if paged else \
+        tri.KVCache.dense(dw.k, dw.v, dw.seq_len, pos=pos)
+    qpos = torch.from_numpy(np.array([int(pos_h[s, :, :, max(L - 1, 0)].max()) + 3 for s, L in enumerate(lengths)],
+                                     np.int64)).cuda()
+    n_qh = w.n_kvh * w.group
+    for layer0, n_layers in ((2, 1), (0, 1), (1, 2)):
+        q = rng.standard_normal((w.n_seq, n_layers, n_qh, 128)).astype(np.float32)
+        qd = torch.from_numpy(q).cuda()
+        outs = {ws: tri.tri_decode_attention(kv, qd, qpos, rope_base=w.base, group=w.group, pos=pos, layer0=layer0,
+                                             n_layers=n_layers, workspace=ws).cpu().numpy() for ws in ("auto", None)}
+        out_na = torch.empty_like(qd)
+        tri.tri_decode_attention_noalloc(kv, qd, qpos, rope_base=w.base, group=w.group, pos=pos, layer0=layer0,
+                                         n_layers=n_layers, out=out_na)
+        assert np.array_equal(out_na.cpu().numpy(), outs["auto"])   # same kernels, same split
+        worst = 0.0
+        for s, L in enumerate(lengths):
+            for lr in range(n_layers):
+                l = layer0 + lr
+                for h in range(w.n_kvh):
+                    k = as_float(unit_rows(w, hp, s, l, h, L), w.dtype)
+                    v = as_float(unit_rows(w, hp, s, l, h, L, synth.TAG_V), w.dtype)
+                    want = oracle.decode_attention(q[s, lr, h * w.group:(h + 1) * w.group], k, v, base=w.base,
+                                                   key_pos=pos_h[s, l, h, :L], query_pos=int(qpos[s]))
+                    for ws, out in outs.items():
+                        worst = max(worst, check_attention(out[s, lr, h * w.group:(h + 1) * w.group], want, v))
+        log(f"  layers [{layer0}, {layer0 + n_layers}): max attention error / max|v| = {worst:.3e}")
+
+
 def test_attention_over_a_compressed_cache():
     # compress a dense cache, then attend over k_out / v_out with the kept keys' positions
     w = W.scaled(W.WORKLOADS["gqa8b_32k_bf16"], name="att_comp", n_seq=2, n_layer=2, n_kvh=2, max_len=3000,
