@@ -562,6 +562,18 @@ def test_full_paged_ragged64_bf16():
     rng = np.random.default_rng(102)
     seqs = [int(np.argmin(hp.lengths)), int(np.argmax(hp.lengths))] + [int(x) for x in rng.choice(w.n_seq, 2, replace=False)]
     picks = [(s, int(rng.integers(w.n_layer)), int(rng.integers(w.n_kvh))) for s in seqs]
+    # units where a wave's share of the scoring grid starts inside the unit: the matrix-core kernel
+    # runs one 8-wave workgroup per CU and splits the 16-key steps of all units, in (sequence,
+    # layer, head) order, into equal shares (the first total % waves shares one step longer)
+    unit_steps = np.repeat((hp.lengths.astype(np.int64) + 15) // 16, w.n_layer * w.n_kvh)
+    ends = np.cumsum(unit_steps)
+    n_waves = torch.cuda.get_device_properties(0).multi_processor_count * 8
+    share, extra = divmod(int(ends[-1]), n_waves)
+    for wv in (n_waves // 3, n_waves // 2, (2 * n_waves) // 3):
+        g0 = wv * share + min(wv, extra)
+        u = int(np.searchsorted(ends, g0, side="right"))
+        if g0 > (ends[u - 1] if u else 0):           # the share starts after the unit's first step
+            picks.append(W.unit_coords(w, u))
     # the pool is compacted in place: the oracle's rows come from the host generator
     pk = dw.k
     for s, l, h in picks[:2]:
