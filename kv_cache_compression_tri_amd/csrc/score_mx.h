@@ -27,9 +27,12 @@
 // of the key operand (its own features, as 8 values of the k-range of lane group q) and row m of
 // the weight operand (the same bands' weights of head m / 2, part m % 2), and receives rows
 // 4q..4q+3 of column m: both parts of heads 2q and 2q + 1 of key m.  So the sum of the parts and
-// the max over a lane's two heads stay in the lane; the max over the lane groups is two swap
-// butterflies across rows of 16 and 32 lanes (v_permlane16_swap, v_permlane32_swap).  Scores of 4
-// steps are gathered so that each lane stores one of 64 consecutive keys.
+// the max over a lane's two heads stay in the lane (a step's accumulator starts at -inf in the
+// rows of heads past the group); the max over the four lane groups is taken for two steps at
+// once: a swap of the 32-lane halves between the two steps' values (v_permlane32_swap) and a
+// swap of 16-lane rows within the result (v_permlane16_swap) leave the even step's scores in
+// rows 0 and 1 and the odd step's in rows 2 and 3.  Two such pairs give each lane one of 64
+// consecutive keys to store.
 //
 // Key stream: in that layout 16 consecutive lanes hold 16 different keys, so loading it directly
 // would make every group of consecutive lanes read 16 bytes of 16 different rows.  Instead the
@@ -80,17 +83,6 @@ __device__ __forceinline__ uint32_t mx_pack_hi(float x0, float x1) {
 __device__ __forceinline__ uint32_t mx_pack_rne(float y0, float y1) {
   const mx_bf16x2 v = {(__bf16)y0, (__bf16)y1};
   return __builtin_bit_cast(uint32_t, v);
-}
-
-// max with the lane 16 (permlane16) or 32 (permlane32) rows away: the swap of a value with
-// itself leaves the partner's value in one of the two results, the own value in the other
-__device__ __forceinline__ float mx_max_x16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float mx_max_x32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // The two operand parts of 8 features x[0..7]: high parts by truncation (one byte permute per
@@ -152,6 +144,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_mx_kernel(const ScoreP
   // heads 2q and 2q + 1 of the lane's output rows: -inf drops a head past the group from the max
   const float mask_a = (2 * q < G) ? 0.0f : -INFINITY;
   const float mask_b = (2 * q + 1 < G) ? 0.0f : -INFINITY;
+  const mx_f32x4 init = {mask_a, 0.0f, mask_b, 0.0f};   // a step's accumulator before its products
   const int ups = P.n_layer * P.n_kvh;
   const int n_qh = P.n_kvh * P.group;
   // whole-row loads: load i, lane l reads 16-byte piece l % 16 of row 4i + l / 16
@@ -279,21 +272,32 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_mx_kernel(const ScoreP
 
     float* out = P.scores + unit * P.score_stride + p0;
     mx_f32x4 acc[2];
-    float keep = 0.0f;
-    // reduction of step n's accumulator (rows 4q..4q+3 of column km): the score of key km in
-    // every lane of the column; lane group q keeps the score of steps n = q mod 4, and after
-    // the fourth such step each lane stores one of 64 consecutive keys
-    auto finish = [&](const mx_f32x4& c, int n) __attribute__((always_inline)) {
-      const float a = c[0] + c[1] + mask_a;     // head 2q
-      const float b = c[2] + c[3] + mask_b;     // head 2q + 1
-      float t = __builtin_fmaxf(a, b);
-      t = mx_max_x16(t);
-      t = mx_max_x32(t);
-      if ((n & 3) == q) keep = t;
-      if ((n & 3) == 3 || n == n_steps - 1) {
-        const int key = kMxKeys * (n & ~3) + lane;
-        if (q <= (n & 3) && key < nkeys) __builtin_nontemporal_store(keep, out + key);
+    float te = 0.0f, pa = 0.0f;      // the even step of a pair; the first pair of a 4-step group
+    // lane (q, km) stores key km of step so of each 4-step group, so = 0, 2, 1, 3 for q = 0..3
+    const int so = ((q & 1) << 1) | (q >> 1);
+    // reduction of step n's accumulator (rows 4q..4q+3 of column km; the initial value drops
+    // heads past the group): the lane's two heads' maximum, then, for a pair of steps at once,
+    // the maximum over the four lane groups by a 32-lane swap of the two steps' values and a
+    // 16-lane swap of the result (rows 0, 1 then hold the even step's scores, rows 2, 3 the odd
+    // one's); every second pair completes a group of 64 consecutive keys, one per lane
+    auto finish = [&](const mx_f32x4& c, int n, bool last) __attribute__((always_inline)) {
+      const float t = __builtin_fmaxf(c[0] + c[1], c[2] + c[3]);
+      if ((n & 1) == 0 && !last) {
+        te = t;
+        return;
       }
+      const float e = (n & 1) ? te : t;   // an even last step pairs with itself
+      const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(e), __float_as_uint(t), false, false);
+      const float a = __builtin_fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+      const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+      const float pr = __builtin_fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
+      if ((n & 2) == 0) {
+        pa = pr;
+        if (!last) return;
+      }
+      const float v = (q & 1) ? pr : pa;
+      const int key = kMxKeys * ((n & ~3) + so) + km;
+      if (so <= (n & 3) && key < nkeys) __builtin_nontemporal_store(v, out + key);
     };
     // n0: first step of the current chunk; steps n0 + it >= n_steps of the last chunk compute
     // nothing, but still issue their (empty) loads
@@ -318,7 +322,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_mx_kernel(const ScoreP
         mx_f32x4& ac = acc[it & 1];
         float kabs[16];
         if (live) {
-          ac = mx_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          ac = init;
 #pragma unroll
           for (int p = 0; p < 4; ++p) {            // trig features of bands 4p..4p+3
             float x[8];
@@ -371,11 +375,11 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_mx_kernel(const ScoreP
             ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mx_bf16x8, am[p]),
                                                           __builtin_bit_cast(mx_bf16x8, bl), ac, 0, 0, 0);
           }
-          if (n > 0) finish(acc[(it & 1) ^ 1], n - 1);   // the previous step's products are done by now
+          if (n > 0) finish(acc[(it & 1) ^ 1], n - 1, false);   // the previous step's products are done by now
         }
       }
     }
-    if (n_steps > 0) finish(acc[(n_steps - 1) & 1], n_steps - 1);
+    if (n_steps > 0) finish(acc[(n_steps - 1) & 1], n_steps - 1, true);
   });
 }
 
