@@ -66,7 +66,7 @@ def as_float(bits, dtype):
 @pytest.mark.parametrize("workspace", ["auto", None])
 @pytest.mark.parametrize("dtype,layout,key_space,group", [("bf16", "half", "pre", 4), ("f32", "interleaved", "pre", 7),
                                                           ("bf16", "interleaved", "post", 2),
-                                                          ("f32", "half", "post", 8)])
+                                                          ("f32", "half", "post", 8), ("bf16", "half", "pre", 1)])
 def test_attention_dense(dtype, layout, key_space, group, workspace):
     # workspace "auto": the units split their 1300 slots over 8 workgroups each (splits past a
     # unit's length, and a unit with no keys, included); None: one workgroup per unit
