@@ -89,9 +89,10 @@ def use_fused(mode: str, w, n_cu: int, key_space="pre", form="additive", positio
 
 
 def score_kernel_used(w, key_space: str, form: str, positions: bool) -> str:
-    """The scoring kernel the library launches for this pass: bfloat16 keys before RoPE at
-    consecutive positions, additive form, max over 4..8 heads take the matrix-core kernel."""
-    if (w.dtype == "bf16" and key_space == "pre" and form == "additive" and not positions and
+    """The scoring kernel the library launches for this pass: bfloat16 keys, additive form, max
+    over 4..8 heads take the matrix-core kernel (keys before RoPE at consecutive positions, or
+    cached after RoPE, whose positions are not read)."""
+    if (w.dtype == "bf16" and form == "additive" and (key_space == "post" or not positions) and
             w.reduce == "max" and 4 <= w.group <= 8):
         return "score_mx_kernel"
     return "score_kernel"

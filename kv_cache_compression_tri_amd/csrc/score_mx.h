@@ -1,6 +1,6 @@
 // Key scoring with the head contraction on the bf16 matrix cores, weights as the row operand
-// (gfx950): bfloat16 keys before RoPE at consecutive positions, additive form, max over a group
-// of G query heads.
+// (gfx950): bfloat16 keys before RoPE at consecutive positions, or cached after RoPE (POST),
+// additive form, max over a group of G query heads.
 //
 // It computes what the vector kernel in score_kernel.h computes (the same exact rewrite:
 // s_h(j) = sum_f Re(W_hf x_f) + N_hf |k_f|, x_f = e^{-i r theta_f} conj(k_f); "TriAttention:
@@ -44,6 +44,13 @@
 // phase table, anchors, chunk re-anchoring and work division follow score_kernel.h; this kernel's
 // chunk is 224 offsets (14 steps), so that the table (112 KB) and the eight waves' staging rows
 // (32 KB) share the CU's 160 KB of LDS.
+//
+// Keys cached after RoPE (POST): k'_f = k_f e^{i p_j theta_f}, so x_f = conj(k'_f) and the weights
+// are anchored at Q once per segment (W_f = c_f C_f e^{i Q theta_f}); there is no phase table and
+// no re-anchoring.  Re(W x) = Re W Re k' + Im W Im k' is linear in the raw key, whose bfloat16
+// values are exact operands: the four trig products per step take the four staged 16-byte pieces
+// of the lane's row as they are (one product each, the weight rows still split in two parts),
+// and only |k_f| is formed and split on the vector ALUs.
 #pragma once
 #include "score_kernel.h"   // for_each_segment, uniform64, kStreamPolicy
 
@@ -96,23 +103,33 @@ __device__ __forceinline__ void mx_split8(const float (&x)[8], mx_u32x4& bh, mx_
   }
 }
 
-template <int G, bool IL, bool PAGED>
+// Weight index (into w[]: Re W at 2j, -Im W at 2j + 1) that multiplies element e of raw key piece
+// p (0..3) in the product of keys cached after RoPE, and the sign it takes there: the half split's
+// pieces hold the real parts of local bands 0..7, 8..15, then their imaginary parts; the
+// interleaved pieces hold (re, im) of local bands 4p..4p+3.
+__device__ __forceinline__ constexpr int mx_post_index(bool il, int p, int e) {
+  return il ? 2 * (4 * p + (e >> 1)) + (e & 1) : 2 * ((p & 1) * 8 + e) + (p >> 1);
+}
+
+template <int G, bool IL, bool PAGED, bool POST>
 __global__ __launch_bounds__(kScoreWaves * 64) void score_mx_kernel(const ScoreParams P) {
   constexpr int NW = kScoreWaves;
   constexpr int NT = NW * 64;
-  constexpr int STEPS = kMxSteps;               // wave steps per chunk
-  constexpr int PF = 2;                         // steps of loads in flight
+  // wave steps per chunk (keys after RoPE have no table: there the chunk is only the unrolled
+  // loop), and steps of loads in flight (3 or 4 steps for keys after RoPE measured the same)
+  constexpr int STEPS = kMxSteps;
+  constexpr int PF = 2;
   constexpr int ROW = kHeadDim * 2;
   static_assert(STEPS % 2 == 0 && STEPS % PF == 0, "chunk geometry");
   static_assert(G >= 1 && G <= 8, "group");
 
-  __shared__ float4 tab[kMxChunk * kBands / 2];
+  __shared__ float4 tab[POST ? 1 : kMxChunk * kBands / 2];   // keys after RoPE need no table
   __shared__ float2 stepc[kBands];             // e^{-i kMxChunk theta_f}
   __shared__ float2 anc[NW][kBands];           // per-wave anchors
   __shared__ uint4 stage[NW][kMxKeys * kMxRow16];   // per-wave staging rows of one step
 
   const int tid = threadIdx.x;
-  {  // phase table: float64 recurrence per (band, run of offsets), rounded once
+  if constexpr (!POST) {  // phase table: float64 recurrence per (band, run of offsets), rounded once
     constexpr int RL = kMxChunk * kBands / NT;
     const int f = tid & 63, run = tid >> 6;
     const double th = P.theta[f];
@@ -241,8 +258,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_mx_kernel(const ScoreP
         w[32 + j] = mm;
       }
     }
-    {  // anchor of this segment (float64), one band per lane
-      const double ang = double(Q - p0) * P.theta[lane];
+    {  // anchor of this segment (float64), one band per lane; after RoPE the key carries its own phase
+      const double ang = double(POST ? Q : Q - p0) * P.theta[lane];
       double sa, ca;
       sincos(ang, &sa, &ca);
       const double cr = P.c_re[lane], ci = P.c_im[lane];
@@ -264,7 +281,14 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_mx_kernel(const ScoreP
       for (int p = 0; p < kMxProducts; ++p)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float w0 = w[8 * p + 2 * e], w1 = w[8 * p + 2 * e + 1];
+          // keys after RoPE: the trig products take the raw key pieces, so their weights follow the
+          // pieces' element order, Re W for a real part and Im W (= -w[2j + 1]) for an imaginary one
+          float w0 = w[8 * p + 2 * e], w1 = w[8 * p + 2 * e + 1];
+          if (POST && p < 4) {
+            const int i0 = mx_post_index(IL, p, 2 * e), i1 = mx_post_index(IL, p, 2 * e + 1);
+            w0 = (i0 & 1) ? -w[i0] : w[i0];
+            w1 = (i1 & 1) ? -w[i1] : w[i1];
+          }
           am[p][e] = lo_row ? mx_pack_rne(w0 - mx_hi(w0), w1 - mx_hi(w1)) : mx_pack_hi(w0, w1);
         }
     };
@@ -304,7 +328,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_mx_kernel(const ScoreP
     for (int n0 = 0; n0 < n_steps; n0 += STEPS) {
       int tz = lane;
       asm volatile("" : "+v"(tz));
-      if (n0 > 0) {  // next chunk: W <- W e^{-i kMxChunk theta_f}, then new weight operands
+      if (!POST && n0 > 0) {  // next chunk: W <- W e^{-i kMxChunk theta_f}, then new weight operands
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const float2 R = stepc[mx_band(q, j)];
@@ -321,7 +345,31 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_mx_kernel(const ScoreP
         const float4* tp = tab + it * 8 * 64 + tz;
         mx_f32x4& ac = acc[it & 1];
         float kabs[16];
-        if (live) {
+        if (POST && live) {
+          // keys after RoPE: x_f = conj(k'_f), so Re(W x) = Re W Re k' + Im W Im k' and the trig
+          // products take the raw bfloat16 pieces (exact) as the key operand, one product per piece;
+          // |k_f| = |k'_f| from the same words
+          ac = init;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            float a, b;
+            if constexpr (IL) {
+              const uint32_t wv = word(cur[j >> 2], j & 3);
+              a = bf16_lo(wv);
+              b = bf16_hi(wv);
+            } else {
+              const uint32_t wr = word(cur[j < 8 ? 0 : 1], (j & 7) >> 1);
+              const uint32_t wi = word(cur[j < 8 ? 2 : 3], (j & 7) >> 1);
+              a = (j & 1) ? bf16_hi(wr) : bf16_lo(wr);
+              b = (j & 1) ? bf16_hi(wi) : bf16_lo(wi);
+            }
+            kabs[j] = __builtin_amdgcn_sqrtf(fmaf(a, a, b * b));
+          }
+#pragma unroll
+          for (int p = 0; p < 4; ++p)
+            ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mx_bf16x8, am[p]),
+                                                          __builtin_bit_cast(mx_bf16x8, cur[p]), ac, 0, 0, 0);
+        } else if (!POST && live) {
           ac = init;
 #pragma unroll
           for (int p = 0; p < 4; ++p) {            // trig features of bands 4p..4p+3
@@ -383,9 +431,9 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_mx_kernel(const ScoreP
   });
 }
 
-template <int G, bool IL, bool PAGED>
+template <int G, bool IL, bool PAGED, bool POST>
 hipError_t launch_mx_case(const ScoreParams& p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((score_mx_kernel<G, IL, PAGED>), dim3(grid), dim3(kScoreWaves * 64), 0, st, p);
+  hipLaunchKernelGGL((score_mx_kernel<G, IL, PAGED, POST>), dim3(grid), dim3(kScoreWaves * 64), 0, st, p);
   return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
 // Key scoring on the bf16 matrix cores (kernel in score_mx.h): bfloat16 keys before RoPE at
-// consecutive positions, additive form, max over 4..8 query heads per KV head.  Dense caches
+// consecutive positions or cached after RoPE, additive form, max over 4..8 query heads per KV
+// head.  Dense caches
 // here, paged ones in score_mx_paged.hip (two translation units so they compile in parallel).
 #include "score_mx.h"
 
@@ -9,21 +10,28 @@ namespace tri {
 // the 32K pass's scoring (36 x 8 units of 32768 bfloat16 keys; group statistics of that
 // workload, G changed), vector / matrix cores: G = 3 0.456 / 0.474 ms, G = 4 0.482 / 0.478,
 // G = 5 0.540 / 0.475, G = 6 0.600 / 0.478; the 128K pass (G = 7) 0.981 / 0.754 ms; the paged
-// pass of 64 sequences (G = 4) 20.30 / 19.84 ms.  So it takes G >= 4.
+// pass of 64 sequences (G = 4) 20.30 / 19.84 ms.  So it takes G >= 4.  Keys cached after RoPE
+// (no rotation; the trig products take the raw keys), same measure on two boxes: G = 2
+// 0.407 / 0.433 ms, G = 3 0.385 / 0.437, G = 4 0.423 / 0.429 and 0.448 / 0.438, G = 5
+// 0.490 / 0.438, G = 6 0.513 / 0.440, 128K 0.823 / 0.629 and 0.847 / 0.677 ms, paged 16.79 /
+// 15.17 and 17.70 / 16.82 ms: the same rule.
 constexpr int kMxMinGroup = 4;
 
 bool score_mx_applies(int G_eff, int dtype, bool post, bool mult, bool positions, bool reduce_mean) {
-  return dtype == 1 && !post && !mult && !positions && !reduce_mean && G_eff >= kMxMinGroup &&
+  // keys cached after RoPE carry their positions, so explicit positions are not read for them
+  return dtype == 1 && !mult && !reduce_mean && (post || !positions) && G_eff >= kMxMinGroup &&
          G_eff <= kMaxGroup;
 }
 
-hipError_t launch_score_mx(const ScoreParams& p, int G_eff, bool interleaved, bool paged, int grid,
+hipError_t launch_score_mx(const ScoreParams& p, int G_eff, bool interleaved, bool paged, bool post, int grid,
                            hipStream_t stream) {
+  if (post) return paged ? launch_score_mx_post_paged(p, G_eff, interleaved, grid, stream)
+                         : launch_score_mx_post(p, G_eff, interleaved, grid, stream);
   if (paged) return launch_score_mx_paged(p, G_eff, interleaved, grid, stream);
 #define TRI_MX_CASE(GG)                                                                   \
   case GG:                                                                                \
-    return interleaved ? launch_mx_case<GG, true, false>(p, grid, stream)                 \
-                       : launch_mx_case<GG, false, false>(p, grid, stream);
+    return interleaved ? launch_mx_case<GG, true, false, false>(p, grid, stream)                 \
+                       : launch_mx_case<GG, false, false, false>(p, grid, stream);
   switch (G_eff) {
     TRI_MX_CASE(4)
     TRI_MX_CASE(5)

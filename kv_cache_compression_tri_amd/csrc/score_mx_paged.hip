@@ -7,8 +7,8 @@ namespace tri {
 hipError_t launch_score_mx_paged(const ScoreParams& p, int G_eff, bool interleaved, int grid, hipStream_t stream) {
 #define TRI_MX_CASE(GG)                                                                   \
   case GG:                                                                                \
-    return interleaved ? launch_mx_case<GG, true, true>(p, grid, stream)                  \
-                       : launch_mx_case<GG, false, true>(p, grid, stream);
+    return interleaved ? launch_mx_case<GG, true, true, false>(p, grid, stream)                  \
+                       : launch_mx_case<GG, false, true, false>(p, grid, stream);
   switch (G_eff) {
     TRI_MX_CASE(4)
     TRI_MX_CASE(5)

@@ -183,6 +183,36 @@ def test_small_dense_parity(name):
     log(f"  max score error / bound = {worst:.3e}")
 
 
+# bfloat16 caches read as keys cached after RoPE, max over G >= 4 heads: the matrix-core kernel
+# with the raw keys as the trig products' operand, at the step, store-group and chunk edges
+# above; and G = 2, 3 (the vector kernel)
+POST_MX = ["g4_max_half_bf16", "g8_max_bf16", "g5_max_half_bf16_lowR", "g6_max_half_bf16_short",
+           "g7_max_interleaved_bf16", "g5_max_half_bf16_chunk_edges", "g8_max_interleaved_bf16_step_edges",
+           "g4_max_half_bf16_one_step", "g4_max_half_bf16_empty_seqs"]
+POST_MX_EXTRA = {
+    "g2_max_half_bf16": (dict(n_seq=2, n_layer=2, n_kvh=2, group=2, max_len=1700, budget=300, window=16),
+                         [1700, 1041]),
+    "g3_max_interleaved_bf16": (dict(n_seq=3, n_layer=1, n_kvh=2, group=3, layout="interleaved", max_len=700,
+                                     budget=90, window=0), [700, 17, 241]),
+}
+
+
+@pytest.mark.parametrize("name", POST_MX + sorted(POST_MX_EXTRA))
+def test_small_dense_parity_post_rope(name):
+    over, lengths = SMALL_DENSE[name] if name in SMALL_DENSE else POST_MX_EXTRA[name]
+    w = W.scaled(BASE, name=name + "_post", **over)
+    log(f"small dense post-RoPE {name}: {over} lengths={lengths}")
+    dw = SD.build(w, hp=W.make_params(w, lengths=lengths))
+    sc, kept, kept_n, out = host_outputs(*run_pass(dw, "post"))
+    worst = 0.0
+    for s in range(w.n_seq):
+        for l in range(w.n_layer):
+            for h in range(w.n_kvh):
+                e, _ = check_dense_unit(dw, s, l, h, sc, kept, kept_n, out, "post")
+                worst = max(worst, e)
+    log(f"  max score error / bound = {worst:.3e}")
+
+
 # ---------------------------------------------------------------------------------------
 # small paged case: every unit, in-place packing, freed pages
 # ---------------------------------------------------------------------------------------
@@ -198,6 +228,8 @@ def test_small_dense_parity(name):
     ([2500, 33, 4096, 1000], "pre", dict(dtype="int8", layout="interleaved", reduce="mean")),
     ([3000, 17, 4096, 905], "pre", dict(group=7)),                       # matrix-core scoring, paged
     ([1200, 4111, 64, 2001], "pre", dict(layout="interleaved", group=8)),
+    ([1200, 4111, 64, 2001], "post", dict(layout="interleaved", group=8)),   # matrix cores, keys after RoPE
+    ([333, 4096, 17, 1600], "post", dict(group=2)),                         # vector kernel, keys after RoPE
 ])
 def test_small_paged_parity(lengths, key_space, extra):
     w = W.scaled(W.WORKLOADS["paged_ragged64_bf16"], n_seq=4, n_layer=2, n_kvh=2, max_len=5120,
@@ -776,6 +808,15 @@ def test_full_gqa8b_32k_bf16_post_rope():
     rng = np.random.default_rng(105)
     units = [0, w.n_units - 1] + _low_r_units(w, hp, 1) + [int(x) for x in rng.choice(w.n_units, 1, replace=False)]
     _full_dense("gqa8b_32k_bf16", units, key_space="post")
+
+
+def test_full_long_128k_bf16_post_rope():
+    # the 128K cache read as a post-RoPE cache: G = 7 on the matrix cores, raw keys in the products
+    w = W.WORKLOADS["long_128k_bf16"]
+    hp = W.make_params(w)
+    rng = np.random.default_rng(107)
+    units = [1, w.n_units - 1] + _low_r_units(w, hp, 1) + [int(rng.integers(2, w.n_units - 1))]
+    _full_dense("long_128k_bf16", units, key_space="post")
 
 
 def test_full_gqa8b_32k_fp8():
