@@ -89,12 +89,15 @@ def use_fused(mode: str, w, n_cu: int, key_space="pre", form="additive", positio
 
 
 def score_kernel_used(w, key_space: str, form: str, positions: bool) -> str:
-    """The scoring kernel the library launches for this pass: bfloat16 keys, additive form, max
-    over 4..8 heads take the matrix-core kernel (keys before RoPE at consecutive positions, or
-    cached after RoPE, whose positions are not read)."""
-    if (w.dtype == "bf16" and form == "additive" and (key_space == "post" or not positions) and
-            w.reduce == "max" and 4 <= w.group <= 8):
-        return "score_mx_kernel"
+    """The scoring kernel the library launches for this pass: the additive form with the max over
+    the group takes the matrix-core kernel for bfloat16 keys at 4..8 heads (before RoPE at
+    consecutive positions, or cached after RoPE, whose positions are not read) and for 8-bit keys
+    cached after RoPE at 2..8 heads."""
+    if form == "additive" and w.reduce == "max":
+        if w.dtype == "bf16" and (key_space == "post" or not positions) and 4 <= w.group <= 8:
+            return "score_mx_kernel"
+        if w.dtype in ("fp8", "int8") and key_space == "post" and 2 <= w.group <= 8:
+            return "score_mx_kernel"
     return "score_kernel"
 
 

@@ -24,7 +24,7 @@ LIBS = {
         "dir": os.path.join(PKG, "csrc"),
         "sources": ["api.hip", "score.hip", "score_post.hip", "score_8bit.hip", "score_post_8bit.hip",
                     "score_mult.hip", "score_post_mult.hip", "score_mult_8bit.hip", "score_post_mult_8bit.hip",
-                    "score_pos.hip", "score_pos_8bit.hip", "score_mx.hip", "score_mx_paged.hip", "score_mx_post.hip", "score_mx_post_paged.hip", "score_select.hip", "score_select_f32.hip",
+                    "score_pos.hip", "score_pos_8bit.hip", "score_mx.hip", "score_mx_paged.hip", "score_mx_post.hip", "score_mx_post_paged.hip", "score_mx_post_8bit.hip", "score_select.hip", "score_select_f32.hip",
                     "score_select_paged.hip", "score_select_f32_paged.hip",
                     "select.hip", "compact.hip", "calib.hip", "decode.hip"],
         "includes": [os.path.join(ROOT, "include"), os.path.join(PKG, "csrc")],

@@ -8,7 +8,7 @@ namespace tri {
 hipError_t launch_score(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
                         bool post, bool mult, int grid, hipStream_t stream) {
   if (score_mx_applies(G_eff, dtype, post, mult, p.pos != nullptr, p.reduce_mean != 0))
-    return launch_score_mx(p, G_eff, interleaved, paged, post, grid, stream);
+    return launch_score_mx(p, G_eff, dtype, interleaved, paged, post, grid, stream);
   if (p.pos && !post) return launch_score_pos(p, G_eff, dtype, interleaved, paged, grid, stream);
   if (mult) {
     if (dtype >= 2)

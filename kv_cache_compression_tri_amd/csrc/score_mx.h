@@ -111,22 +111,65 @@ __device__ __forceinline__ constexpr int mx_post_index(bool il, int p, int e) {
   return il ? 2 * (4 * p + (e >> 1)) + (e & 1) : 2 * ((p & 1) * 8 + e) + (p >> 1);
 }
 
-template <int G, bool IL, bool PAGED, bool POST>
+// (re, im) of local bands 0..15 of a lane's 8-bit key piece words cw(0..7), exactly (DT 2: OCP E4M3
+// codes, two per conversion; DT 3: int8 codes): half split, words 0..3 hold the real codes of local
+// bands 0..15 and words 4..7 the imaginary ones; interleaved, word k holds (re, im) of local bands
+// 2k and 2k + 1
+template <int DT, bool IL, typename CW>
+__device__ __forceinline__ void mx_decode8(const CW& cw, float (&re)[16], float (&im)[16]) {
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    if constexpr (DT == 2) {
+      if constexpr (IL) {
+        const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(int(cw(j >> 1)), false);
+        const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(int(cw(j >> 1)), true);
+        re[j] = a[0]; im[j] = a[1]; re[j + 1] = b[0]; im[j + 1] = b[1];
+      } else {
+        const bool hi = (j & 2) != 0;
+        const auto a = hi ? __builtin_amdgcn_cvt_pk_f32_fp8(int(cw(j >> 2)), true)
+                          : __builtin_amdgcn_cvt_pk_f32_fp8(int(cw(j >> 2)), false);
+        const auto b = hi ? __builtin_amdgcn_cvt_pk_f32_fp8(int(cw(4 + (j >> 2))), true)
+                          : __builtin_amdgcn_cvt_pk_f32_fp8(int(cw(4 + (j >> 2))), false);
+        re[j] = a[0]; re[j + 1] = a[1]; im[j] = b[0]; im[j + 1] = b[1];
+      }
+    } else {
+      if constexpr (IL) {
+        const uint32_t w = cw(j >> 1);
+        re[j] = float(int8_t(w)); im[j] = float(int8_t(w >> 8));
+        re[j + 1] = float(int8_t(w >> 16)); im[j + 1] = float(int8_t(w >> 24));
+      } else {
+        const uint32_t wr = cw(j >> 2), wi = cw(4 + (j >> 2));
+        const int sh = 8 * (j & 3);
+        re[j] = float(int8_t(wr >> sh)); re[j + 1] = float(int8_t(wr >> (sh + 8)));
+        im[j] = float(int8_t(wi >> sh)); im[j + 1] = float(int8_t(wi >> (sh + 8)));
+      }
+    }
+  }
+}
+
+template <int G, bool IL, bool PAGED, bool POST, int DT = 1>
 __global__ __launch_bounds__(kScoreWaves * 64) void score_mx_kernel(const ScoreParams P) {
   constexpr int NW = kScoreWaves;
   constexpr int NT = NW * 64;
   // wave steps per chunk (keys after RoPE have no table: there the chunk is only the unrolled
-  // loop), and steps of loads in flight (3 or 4 steps for keys after RoPE measured the same)
+  // loop), and steps of loads in flight (3 or 4 steps for keys after RoPE measured the same, and so
+  // did 8 for 8-bit keys and 12 waves per CU)
   constexpr int STEPS = kMxSteps;
   constexpr int PF = 2;
-  constexpr int ROW = kHeadDim * 2;
+  // DT 1: bfloat16 keys; DT 2 / 3: fp8 (OCP E4M3) / int8 codes, keys cached after RoPE only.  An
+  // 8-bit row is 128 bytes: 8 pieces of 16 bytes, loaded in 2 instructions per step instead of 4.
+  static_assert(DT == 1 || (POST && (DT == 2 || DT == 3)), "8-bit keys: after RoPE");
+  constexpr bool E8 = DT != 1;
+  constexpr int ROW = kHeadDim * (E8 ? 1 : 2);
+  constexpr int NLD = E8 ? 2 : 4;               // 16-byte load instructions per step
+  constexpr int RPC = E8 ? 8 : kMxRow16;        // 16-byte pieces per row
   static_assert(STEPS % 2 == 0 && STEPS % PF == 0, "chunk geometry");
   static_assert(G >= 1 && G <= 8, "group");
 
   __shared__ float4 tab[POST ? 1 : kMxChunk * kBands / 2];   // keys after RoPE need no table
   __shared__ float2 stepc[kBands];             // e^{-i kMxChunk theta_f}
   __shared__ float2 anc[NW][kBands];           // per-wave anchors
-  __shared__ uint4 stage[NW][kMxKeys * kMxRow16];   // per-wave staging rows of one step
+  __shared__ uint4 stage[NW][kMxKeys * RPC];        // per-wave staging rows of one step
 
   const int tid = threadIdx.x;
   if constexpr (!POST) {  // phase table: float64 recurrence per (band, run of offsets), rounded once
@@ -164,22 +207,34 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_mx_kernel(const ScoreP
   const mx_f32x4 init = {mask_a, 0.0f, mask_b, 0.0f};   // a step's accumulator before its products
   const int ups = P.n_layer * P.n_kvh;
   const int n_qh = P.n_kvh * P.group;
-  // whole-row loads: load i, lane l reads 16-byte piece l % 16 of row 4i + l / 16
-  const int ld_p = lane & 15, ld_r = lane >> 4;
-  uint32_t off[4];
+  // whole-row loads: load i, lane l reads 16-byte piece l % 16 of row 4i + l / 16 (8-bit rows:
+  // piece l % 8 of row 8i + l / 8)
+  const int ld_p = lane & (RPC - 1), ld_r = lane / RPC;
+  uint32_t off[NLD];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) off[i] = (4 * i + ld_r) * ROW + 16 * ld_p;
-  // staging slots (16-byte units, piece p of row r at 16 r + (p xor r)) of the loaded pieces, and
-  // of the pieces this lane reads back: half split: pieces q, 4 + q, 8 + q, 12 + q of row km (re of
-  // bands 8q.., re of 32+8q.., im, im); interleaved: pieces 2q, 2q + 1, 8 + 2q, 9 + 2q
+  for (int i = 0; i < NLD; ++i) off[i] = ((64 / RPC) * i + ld_r) * ROW + 16 * ld_p;
+  // staging slots (16-byte units, piece p of row r at 16 r + (p xor r); 8-bit rows: 8 r +
+  // (p xor (r mod 8))) of the loaded pieces, and of the pieces this lane reads back: half split:
+  // pieces q, 4 + q, 8 + q, 12 + q of row km (re of bands 8q.., re of 32+8q.., im, im);
+  // interleaved: pieces 2q, 2q + 1, 8 + 2q, 9 + 2q.  8-bit rows: half split, the 8-byte halves q % 2
+  // of pieces 2i + q / 2 (the same bands' codes), as 8-byte units; interleaved, pieces q and 4 + q
   uint4* const st = stage[wave];
-  int st_w[4], st_r[4];
+  int st_w[NLD], st_r[4];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int r = (64 / RPC) * i + ld_r;
+    st_w[i] = r * RPC + (ld_p ^ (r & (RPC - 1)));
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = 4 * i + ld_r;
-    st_w[i] = r * kMxRow16 + (ld_p ^ r);
-    const int pc = IL ? (i < 2 ? 2 * q + i : 8 + 2 * q + (i - 2)) : 4 * i + q;
-    st_r[i] = km * kMxRow16 + (pc ^ km);
+    if constexpr (E8) {
+      const int pc = IL ? (i == 0 ? q : 4 + q) : 2 * i + (q >> 1);
+      const int slot = km * RPC + (pc ^ (km & (RPC - 1)));
+      st_r[i] = IL ? slot : 2 * slot + (q & 1);
+    } else {
+      const int pc = IL ? (i < 2 ? 2 * q + i : 8 + 2 * q + (i - 2)) : 4 * i + q;
+      st_r[i] = km * kMxRow16 + (pc ^ km);
+    }
   }
   const int64_t n_waves = int64_t(gridDim.x) * NW;
   const int64_t w_id = int64_t(blockIdx.x) * NW + wave;
@@ -199,7 +254,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_mx_kernel(const ScoreP
     const mx_const_i32_ptr bt = PAGED ? (mx_const_i32_ptr)(P.block_table + int64_t(s) * P.max_pages) : nullptr;
     const uint64_t pg_bytes = uint64_t(P.n_layer) * uint64_t(P.n_kvh) * uint64_t(kPage * ROW);
     const char* ubase = kbase + (int64_t(l) * P.n_kvh + h) * int64_t(kPage * ROW);
-    uint4 ring[PF][4];
+    uint4 ring[PF][NLD];
     // Loads of step n into ring slot sl.  They are issued whatever n is (past the segment's last
     // step the range is empty: the loads return zeros and touch no memory), so that a ring
     // register never merges with an older value under a branch; such a merge makes the compiler
@@ -218,22 +273,40 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_mx_kernel(const ScoreP
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, rows * ROW, 0x00020000);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NLD; ++i)
         ring[sl][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], 0, kStreamPolicy));
     };
     // rows of a loaded step into the staging area, and back in the product layout (the wave's own
     // area: LDS operations of one wave run in order, the fence keeps the compiler's order)
-    auto stage_write = [&](const uint4 (&r)[4]) __attribute__((always_inline)) {
+    auto stage_write = [&](const uint4 (&r)[NLD]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st[st_w[i]] = r[i];
+      for (int i = 0; i < NLD; ++i) st[st_w[i]] = r[i];
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
     uint4 cur[4];                                  // the current step's pieces, product layout
     auto stage_read = [&]() __attribute__((always_inline)) {
+      if constexpr (E8 && IL) {                    // 8-bit: the lane's 32 bytes in cur[0], cur[1]
+        cur[0] = st[st_r[0]];
+        cur[1] = st[st_r[1]];
+      } else if constexpr (E8) {
+        const uint2* st2 = reinterpret_cast<const uint2*>(st);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cur[i] = st[st_r[i]];
+        for (int i = 0; i < 4; ++i) {
+          const uint2 v = st2[st_r[i]];
+          if (i & 1) {
+            cur[i >> 1].z = v.x;
+            cur[i >> 1].w = v.y;
+          } else {
+            cur[i >> 1].x = v.x;
+            cur[i >> 1].y = v.y;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cur[i] = st[st_r[i]];
+      }
     };
 #pragma unroll
     for (int i = 0; i < PF; ++i) load_step(i, i);
@@ -273,6 +346,13 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_mx_kernel(const ScoreP
       w[2 * j] = cx * A.x - cy * A.y;
       w[2 * j + 1] = -(cx * A.y + cy * A.x);
       w[32 + j] = (mm > 0.0f) ? mm - __builtin_sqrtf(cx * cx + cy * cy) : 0.0f;
+    }
+    if constexpr (E8) {
+      if (P.k_scale) {   // stored key = true key / scale: both terms are linear in the key
+        const float ks = P.k_scale[int64_t(l) * P.n_kvh + h];
+#pragma unroll
+        for (int i = 0; i < kMxFeat; ++i) w[i] *= ks;
+      }
     }
     // the weight operands: the row's high parts, or its remainders
     mx_u32x4 am[kMxProducts];
@@ -345,7 +425,27 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_mx_kernel(const ScoreP
         const float4* tp = tab + it * 8 * 64 + tz;
         mx_f32x4& ac = acc[it & 1];
         float kabs[16];
-        if (POST && live) {
+        if (E8 && live) {
+          // 8-bit keys after RoPE: the codes' values (exact in float32, and in bfloat16: at most 8
+          // significant bits) give |k_f| and, packed as bfloat16 in the raw pieces' element order,
+          // the trig products' key operand
+          ac = init;
+          float re[16], im[16];
+          mx_decode8<DT, IL>([&](int k) { return word(cur[k >> 2], k & 3); }, re, im);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) kabs[j] = __builtin_amdgcn_sqrtf(fmaf(re[j], re[j], im[j] * im[j]));
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            mx_u32x4 bk;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i0 = mx_post_index(IL, p, 2 * e), i1 = mx_post_index(IL, p, 2 * e + 1);
+              bk[e] = mx_pack_hi((i0 & 1) ? im[i0 >> 1] : re[i0 >> 1], (i1 & 1) ? im[i1 >> 1] : re[i1 >> 1]);
+            }
+            ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mx_bf16x8, am[p]),
+                                                          __builtin_bit_cast(mx_bf16x8, bk), ac, 0, 0, 0);
+          }
+        } else if (!E8 && POST && live) {
           // keys after RoPE: x_f = conj(k'_f), so Re(W x) = Re W Re k' + Im W Im k' and the trig
           // products take the raw bfloat16 pieces (exact) as the key operand, one product per piece;
           // |k_f| = |k'_f| from the same words
@@ -431,9 +531,9 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_mx_kernel(const ScoreP
   });
 }
 
-template <int G, bool IL, bool PAGED, bool POST>
+template <int G, bool IL, bool PAGED, bool POST, int DT = 1>
 hipError_t launch_mx_case(const ScoreParams& p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((score_mx_kernel<G, IL, PAGED, POST>), dim3(grid), dim3(kScoreWaves * 64), 0, st, p);
+  hipLaunchKernelGGL((score_mx_kernel<G, IL, PAGED, POST, DT>), dim3(grid), dim3(kScoreWaves * 64), 0, st, p);
   return hipGetLastError();
 }
 

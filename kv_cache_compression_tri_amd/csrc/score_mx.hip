@@ -17,14 +17,23 @@ namespace tri {
 // 15.17 and 17.70 / 16.82 ms: the same rule.
 constexpr int kMxMinGroup = 4;
 
+// 8-bit keys cached after RoPE (fp8 / int8 caches of the 32K pass's shape, same measure): the
+// vector kernel takes G = 2 0.292, G = 3 0.312, G = 4 0.361 / 0.371 (fp8 / int8), G = 7 0.512 ms,
+// this kernel 0.25-0.26 ms at every G (4: 0.252 / 0.256, 7: 0.254), so it takes G >= 2.
+constexpr int kMxMinGroup8 = 2;
+
 bool score_mx_applies(int G_eff, int dtype, bool post, bool mult, bool positions, bool reduce_mean) {
-  // keys cached after RoPE carry their positions, so explicit positions are not read for them
-  return dtype == 1 && !mult && !reduce_mean && (post || !positions) && G_eff >= kMxMinGroup &&
-         G_eff <= kMaxGroup;
+  // keys cached after RoPE carry their positions, so explicit positions are not read for them; 8-bit
+  // keys take this kernel only after RoPE (before RoPE their rotation and split cost what the
+  // products save)
+  if (mult || reduce_mean || G_eff > kMaxGroup) return false;
+  if (dtype == 2 || dtype == 3) return post && G_eff >= kMxMinGroup8;
+  return dtype == 1 && (post || !positions) && G_eff >= kMxMinGroup;
 }
 
-hipError_t launch_score_mx(const ScoreParams& p, int G_eff, bool interleaved, bool paged, bool post, int grid,
-                           hipStream_t stream) {
+hipError_t launch_score_mx(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged, bool post,
+                           int grid, hipStream_t stream) {
+  if (dtype != 1) return launch_score_mx_post_8bit(p, G_eff, dtype, interleaved, paged, grid, stream);
   if (post) return paged ? launch_score_mx_post_paged(p, G_eff, interleaved, grid, stream)
                          : launch_score_mx_post(p, G_eff, interleaved, grid, stream);
   if (paged) return launch_score_mx_paged(p, G_eff, interleaved, grid, stream);

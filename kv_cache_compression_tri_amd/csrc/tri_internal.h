@@ -105,12 +105,14 @@ hipError_t launch_score_select_f32_paged(const ScoreParams& p, const SelectParam
 // the matrix-core scoring kernel (bfloat16 keys, additive form, max over the group's heads;
 // before RoPE at consecutive positions, or cached after RoPE) and the shapes it takes
 bool score_mx_applies(int G_eff, int dtype, bool post, bool mult, bool positions, bool reduce_mean);
-hipError_t launch_score_mx(const ScoreParams& p, int G_eff, bool interleaved, bool paged, bool post, int grid,
-                           hipStream_t stream);
+hipError_t launch_score_mx(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged, bool post,
+                           int grid, hipStream_t stream);
 hipError_t launch_score_mx_paged(const ScoreParams& p, int G_eff, bool interleaved, int grid, hipStream_t stream);
 hipError_t launch_score_mx_post(const ScoreParams& p, int G_eff, bool interleaved, int grid, hipStream_t stream);
 hipError_t launch_score_mx_post_paged(const ScoreParams& p, int G_eff, bool interleaved, int grid,
                                       hipStream_t stream);
+hipError_t launch_score_mx_post_8bit(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
+                                     int grid, hipStream_t stream);
 hipError_t launch_score_pos_8bit(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,
                                  int grid, hipStream_t stream);
 hipError_t launch_score_mult(const ScoreParams& p, int G_eff, int dtype, bool interleaved, bool paged,

@@ -12,12 +12,12 @@ import sys
 
 # scoring-kernel names of the stated workloads, as bench.py launches them by default
 PHASES = {
-    "tri::score_mx_kernel<4, false, false, false>": "gqa8b_32k_bf16",
+    "tri::score_mx_kernel<4, false, false, false, 1>": "gqa8b_32k_bf16",
     "tri::score_kernel<1, 0, false, false, false, false, false>": "single_head_2k_f32",
     "tri::score_select_kernel<1, 0, false, false>": "single_head_2k_f32",
     "tri::score_select_kernel<1, 1, false, false>": "gqa8b_batch16_16k_bf16",
-    "tri::score_mx_kernel<7, false, false, false>": "long_128k_bf16",
-    "tri::score_mx_kernel<4, false, true, false>": "paged_ragged64_bf16",
+    "tri::score_mx_kernel<7, false, false, false, 1>": "long_128k_bf16",
+    "tri::score_mx_kernel<4, false, true, false, 1>": "paged_ragged64_bf16",
 }
 PASS_PREFIXES = ("tri::score", "tri::select", "tri::compact", "tri::decode")   # decode: the consumer calls
 

@@ -183,17 +183,33 @@ def test_small_dense_parity(name):
     log(f"  max score error / bound = {worst:.3e}")
 
 
-# bfloat16 caches read as keys cached after RoPE, max over G >= 4 heads: the matrix-core kernel
-# with the raw keys as the trig products' operand, at the step, store-group and chunk edges
-# above; and G = 2, 3 (the vector kernel)
+# bfloat16, fp8 and int8 caches read as keys cached after RoPE, max over G >= 4 heads: the
+# matrix-core kernel with the raw keys (8-bit: their values packed as bfloat16) as the trig
+# products' operand, at the step, store-group and chunk edges above and with per-head key scales
+# (8-bit keys from G = 2); and bfloat16 at G = 2, 3 (the vector kernel)
 POST_MX = ["g4_max_half_bf16", "g8_max_bf16", "g5_max_half_bf16_lowR", "g6_max_half_bf16_short",
            "g7_max_interleaved_bf16", "g5_max_half_bf16_chunk_edges", "g8_max_interleaved_bf16_step_edges",
-           "g4_max_half_bf16_one_step", "g4_max_half_bf16_empty_seqs"]
+           "g4_max_half_bf16_one_step", "g4_max_half_bf16_empty_seqs", "g4_max_half_fp8",
+           "g8_max_interleaved_fp8", "g4_max_half_int8", "g7_max_interleaved_int8"]
 POST_MX_EXTRA = {
     "g2_max_half_bf16": (dict(n_seq=2, n_layer=2, n_kvh=2, group=2, max_len=1700, budget=300, window=16),
                          [1700, 1041]),
     "g3_max_interleaved_bf16": (dict(n_seq=3, n_layer=1, n_kvh=2, group=3, layout="interleaved", max_len=700,
                                      budget=90, window=0), [700, 17, 241]),
+    "g5_max_half_fp8_step_edges": (dict(n_seq=8, n_layer=2, n_kvh=1, group=5, dtype="fp8", max_len=320,
+                                        budget=40, window=4), [1, 15, 16, 17, 63, 64, 65, 320]),
+    "g6_max_interleaved_fp8_chunk_edges": (dict(n_seq=8, n_layer=1, n_kvh=2, group=6, dtype="fp8",
+                                                layout="interleaved", max_len=1100, budget=100, window=8),
+                                           [223, 224, 225, 447, 448, 449, 1100, 1087]),
+    "g8_max_half_int8_step_edges": (dict(n_seq=8, n_layer=1, n_kvh=2, group=8, dtype="int8", max_len=320,
+                                         budget=40, window=0), [1, 15, 16, 17, 63, 64, 65, 320]),
+    "g2_max_half_fp8": (dict(n_seq=2, n_layer=2, n_kvh=2, group=2, dtype="fp8", max_len=1700, budget=300,
+                             window=16), [1700, 1041]),
+    "g3_max_interleaved_int8": (dict(n_seq=3, n_layer=1, n_kvh=2, group=3, dtype="int8", layout="interleaved",
+                                     max_len=700, budget=90, window=0), [700, 17, 241]),
+    "g5_max_interleaved_int8_empty_seqs": (dict(n_seq=5, n_layer=2, n_kvh=2, group=5, dtype="int8",
+                                                layout="interleaved", max_len=2600, budget=300, window=32),
+                                           [0, 2600, 0, 0, 1031]),
 }
 
 
@@ -230,6 +246,9 @@ def test_small_dense_parity_post_rope(name):
     ([1200, 4111, 64, 2001], "pre", dict(layout="interleaved", group=8)),
     ([1200, 4111, 64, 2001], "post", dict(layout="interleaved", group=8)),   # matrix cores, keys after RoPE
     ([333, 4096, 17, 1600], "post", dict(group=2)),                         # vector kernel, keys after RoPE
+    ([2500, 33, 4096, 1000], "post", dict(dtype="int8")),                   # matrix cores, 8-bit after RoPE
+    ([1025, 4096, 16, 2047], "post", dict(dtype="fp8", group=7)),
+    ([700, 4100, 1500, 33], "post", dict(dtype="int8", layout="interleaved", group=3)),
 ])
 def test_small_paged_parity(lengths, key_space, extra):
     w = W.scaled(W.WORKLOADS["paged_ragged64_bf16"], n_seq=4, n_layer=2, n_kvh=2, max_len=5120,
@@ -808,6 +827,16 @@ def test_full_gqa8b_32k_bf16_post_rope():
     rng = np.random.default_rng(105)
     units = [0, w.n_units - 1] + _low_r_units(w, hp, 1) + [int(x) for x in rng.choice(w.n_units, 1, replace=False)]
     _full_dense("gqa8b_32k_bf16", units, key_space="post")
+
+
+@pytest.mark.parametrize("name", ["gqa8b_32k_fp8", "gqa8b_32k_int8"])
+def test_full_gqa8b_32k_8bit_post_rope(name):
+    # the full-size 8-bit caches read as post-RoPE caches: matrix cores, codes times per-head scales
+    w = W.WORKLOADS[name]
+    hp = W.make_params(w)
+    rng = np.random.default_rng(109)
+    units = [0, w.n_units - 1] + _low_r_units(w, hp, 1) + [int(x) for x in rng.choice(w.n_units, 1, replace=False)]
+    _full_dense(name, units, key_space="post")
 
 
 def test_full_long_128k_bf16_post_rope():
