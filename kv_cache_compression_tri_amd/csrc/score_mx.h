@@ -214,7 +214,9 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_mx_kernel(const ScoreP
 #pragma unroll
   for (int i = 0; i < NLD; ++i) off[i] = ((64 / RPC) * i + ld_r) * ROW + 16 * ld_p;
   // staging slots (16-byte units, piece p of row r at 16 r + (p xor r); 8-bit rows: 8 r +
-  // (p xor (r mod 8))) of the loaded pieces, and of the pieces this lane reads back: half split:
+  // (p xor (r / 2)), so that the 16 rows read back at one piece or 8-byte half fall on 16 distinct
+  // bank groups: r / 2 and r mod 2 tell them apart) of the loaded pieces, and of the pieces this
+  // lane reads back: half split:
   // pieces q, 4 + q, 8 + q, 12 + q of row km (re of bands 8q.., re of 32+8q.., im, im);
   // interleaved: pieces 2q, 2q + 1, 8 + 2q, 9 + 2q.  8-bit rows: half split, the 8-byte halves q % 2
   // of pieces 2i + q / 2 (the same bands' codes), as 8-byte units; interleaved, pieces q and 4 + q
@@ -223,13 +225,13 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_mx_kernel(const ScoreP
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
     const int r = (64 / RPC) * i + ld_r;
-    st_w[i] = r * RPC + (ld_p ^ (r & (RPC - 1)));
+    st_w[i] = r * RPC + (ld_p ^ (E8 ? r >> 1 : r));
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if constexpr (E8) {
       const int pc = IL ? (i == 0 ? q : 4 + q) : 2 * i + (q >> 1);
-      const int slot = km * RPC + (pc ^ (km & (RPC - 1)));
+      const int slot = km * RPC + (pc ^ (km >> 1));
       st_r[i] = IL ? slot : 2 * slot + (q & 1);
     } else {
       const int pc = IL ? (i < 2 ? 2 * q + i : 8 + 2 * q + (i - 2)) : 4 * i + q;
