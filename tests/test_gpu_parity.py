@@ -829,6 +829,35 @@ def test_full_gqa8b_32k_bf16_post_rope():
     _full_dense("gqa8b_32k_bf16", units, key_space="post")
 
 
+@pytest.mark.parametrize("dtype,layout,group,key_space", [("fp8", "half", 4, "post"), ("int8", "interleaved", 3, "post"),
+                                                           ("fp8", "interleaved", 4, "pre"), ("int8", "half", 6, "pre")])
+def test_8bit_without_key_scales(dtype, layout, group, key_space):
+    # 8-bit codes passed without per-head scales: each key is its codes' values (scale 1); post-RoPE
+    # max takes the matrix-core kernel, pre-RoPE the vector kernel
+    w = W.scaled(BASE, name="noscale", n_seq=2, n_layer=2, n_kvh=2, group=group, dtype=dtype, layout=layout,
+                 max_len=1300, budget=200, window=16)
+    lengths = [1300, 517]
+    hp = W.make_params(w, lengths=lengths)
+    log(f"8-bit keys without scales: {dtype} {layout} G={group} keys {key_space}-RoPE")
+    dw = SD.build(w, hp=hp)
+    kv = tri.KVCache.dense(dw.k, dw.v, dw.seq_len)
+    sc = tri.tri_score_keys(kv, dw.center, dw.mean_abs, rope_base=w.base, offsets=w.offsets, group=w.group,
+                            reduce=w.reduce, rope_layout=w.layout, key_space=key_space)
+    torch.cuda.synchronize()
+    sc = sc.cpu().numpy()
+    worst = 0.0
+    for s in range(w.n_seq):
+        L = lengths[s]
+        for l in range(w.n_layer):
+            for h in range(w.n_kvh):
+                codes = P.host_rows(w, hp, s, l, h, as_float=False)
+                keys = oracle.decode_stored(codes, dtype, 1.0)
+                orc, S = P.oracle_scores(w, hp, s, l, h, keys, key_space)
+                e, _ = P.check_scores(sc[s, l, h, :L], orc, S)
+                worst = max(worst, e)
+    log(f"  max score error / bound = {worst:.3e}")
+
+
 @pytest.mark.parametrize("name", ["gqa8b_32k_fp8", "gqa8b_32k_int8"])
 def test_full_gqa8b_32k_8bit_post_rope(name):
     # the full-size 8-bit caches read as post-RoPE caches: matrix cores, codes times per-head scales
