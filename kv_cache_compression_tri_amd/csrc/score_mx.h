@@ -1,6 +1,6 @@
 // Key scoring with the head contraction on the bf16 matrix cores, weights as the row operand
-// (gfx950): bfloat16 keys before RoPE at consecutive positions, or cached after RoPE (POST),
-// additive form, max over a group of G query heads.
+// (gfx950): bfloat16 keys before RoPE at consecutive positions, or bfloat16, fp8 and int8 keys
+// cached after RoPE (POST; DT = 1, 2, 3), additive form, max over a group of G query heads.
 //
 // It computes what the vector kernel in score_kernel.h computes (the same exact rewrite:
 // s_h(j) = sum_f Re(W_hf x_f) + N_hf |k_f|, x_f = e^{-i r theta_f} conj(k_f); "TriAttention:
@@ -50,7 +50,10 @@
 // no re-anchoring.  Re(W x) = Re W Re k' + Im W Im k' is linear in the raw key, whose bfloat16
 // values are exact operands: the four trig products per step take the four staged 16-byte pieces
 // of the lane's row as they are (one product each, the weight rows still split in two parts),
-// and only |k_f| is formed and split on the vector ALUs.
+// and only |k_f| is formed and split on the vector ALUs.  8-bit keys (fp8 OCP E4M3, int8; a row is
+// 128 bytes, loaded in two 16-byte instructions per lane and step) are converted exactly to float32
+// for |k_f| and packed as bfloat16 for the products (their values have at most 8 significant bits);
+// a per-(layer, KV head) key scale multiplies the weights once per segment.
 #pragma once
 #include "score_kernel.h"   // for_each_segment, uniform64, kStreamPolicy
 
@@ -103,10 +106,11 @@ __device__ __forceinline__ void mx_split8(const float (&x)[8], mx_u32x4& bh, mx_
   }
 }
 
-// Weight index (into w[]: Re W at 2j, -Im W at 2j + 1) that multiplies element e of raw key piece
-// p (0..3) in the product of keys cached after RoPE, and the sign it takes there: the half split's
-// pieces hold the real parts of local bands 0..7, 8..15, then their imaginary parts; the
-// interleaved pieces hold (re, im) of local bands 4p..4p+3.
+// Index into w[] (Re W of local band j at 2j, -Im W at 2j + 1) of the weight that multiplies element
+// e of raw key piece p (0..3) in the products of keys cached after RoPE; an odd index (an imaginary
+// part) takes the weight negated.  The half split's pieces hold the real parts of local bands 0..7
+// and 8..15, then their imaginary parts; the interleaved pieces hold (re, im) of local bands
+// 4p..4p+3.
 __device__ __forceinline__ constexpr int mx_post_index(bool il, int p, int e) {
   return il ? 2 * (4 * p + (e >> 1)) + (e & 1) : 2 * ((p & 1) * 8 + e) + (p >> 1);
 }
@@ -213,13 +217,13 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_mx_kernel(const ScoreP
   uint32_t off[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) off[i] = ((64 / RPC) * i + ld_r) * ROW + 16 * ld_p;
-  // staging slots (16-byte units, piece p of row r at 16 r + (p xor r); 8-bit rows: 8 r +
-  // (p xor (r / 2)), so that the 16 rows read back at one piece or 8-byte half fall on 16 distinct
-  // bank groups: r / 2 and r mod 2 tell them apart) of the loaded pieces, and of the pieces this
-  // lane reads back: half split:
-  // pieces q, 4 + q, 8 + q, 12 + q of row km (re of bands 8q.., re of 32+8q.., im, im);
-  // interleaved: pieces 2q, 2q + 1, 8 + 2q, 9 + 2q.  8-bit rows: half split, the 8-byte halves q % 2
-  // of pieces 2i + q / 2 (the same bands' codes), as 8-byte units; interleaved, pieces q and 4 + q
+  // Staging slots, in 16-byte units: piece p of row r sits at 16 r + (p xor r); for 8-bit rows at
+  // 8 r + (p xor (r / 2)), so that the 16 rows read back at one piece or 8-byte half fall on 16
+  // distinct bank groups (r / 2 and r mod 2 tell them apart).  st_w: the slots of the loaded pieces.
+  // st_r: the pieces this lane reads back, from row km.  Half split: pieces q, 4 + q, 8 + q, 12 + q
+  // (re of bands 8q.., re of 32+8q.., im, im); interleaved: pieces 2q, 2q + 1, 8 + 2q, 9 + 2q.
+  // 8-bit rows, half split: the 8-byte halves q % 2 of pieces 2i + q / 2 (the same bands' codes),
+  // indexed in 8-byte units; interleaved: pieces q and 4 + q.
   uint4* const st = stage[wave];
   int st_w[NLD], st_r[4];
 #pragma unroll
